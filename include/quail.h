@@ -1,0 +1,284 @@
+/*
+ * quail.h -- C ABI of the MI355X (gfx950) AI.IF join-prefill library.
+ *
+ * The library evaluates AI.IF predicates by prefill only: every shared anchor
+ * row's KV is computed once per layer, many suffix rows attend to it through
+ * cascade attention (suffix->anchor cross-attention plus causal suffix
+ * self-attention, merged by LSE rescaling), and the last suffix position emits
+ * one token from a head cut to 8 vocabulary columns, which becomes a boolean.
+ *
+ * Pages this interface follows (cited by title and section):
+ *  [pt] "Motor de inferência Quail atinge 1 bilhão de tokens por minuto por
+ *       GPU", section "Como funciona": the query-aware KV cache (the plan is
+ *       known, so accesses are predictable and eviction has no regret), zero
+ *       decode (one token from the final prefill pass), simplified cascade
+ *       attention with LSE rescaling, and the output head cut to 8 options.
+ *  [fa] "Quail: یک میلیارد توکن در دقیقه روی یک GPU", body and key points:
+ *       the AI.IF join example, the engine sees the whole plan, the last
+ *       prefill pass predicts one token, the head keeps 8 columns, model
+ *       qwen3-4b-fp8 on one GPU.
+ *  [it] "Quail, il motore di inferenza che supera il miliardo di token al
+ *       minuto su una H100": filter = one model call per row, naive join =
+ *       one call per row pair; KV regret.
+ *
+ * Conventions (all functions):
+ *  - "dev" pointers are device (HBM) addresses on the current HIP device;
+ *    "host" pointers are ordinary host memory. Tensors are row-major and
+ *    contiguous. bf16 is passed as uint16_t bit patterns, fp8 as uint8_t OCP
+ *    E4M3 codes (bias 7, max 448, S.1111.111 = NaN).
+ *  - The caller owns every device buffer (weights, tokens, outputs, the KV
+ *    pool and the workspace). The library never allocates or frees device
+ *    memory. It keeps a small pinned host staging area for per-call metadata.
+ *  - Host arrays are read before the call returns. Device inputs must stay
+ *    valid until the stream reaches the enqueued work.
+ *  - Every compute call only enqueues work on `stream` (a hipStream_t; NULL =
+ *    the default stream). Nothing waits for the GPU.
+ *  - Errors are all-or-nothing: every condition the host can detect (bad
+ *    sizes, non-monotone offsets, lengths out of range, a stale handle, a full
+ *    pool, an unsupported shape) returns before anything is enqueued, and
+ *    quail_last_error() describes it. A failing HIP launch returns
+ *    QUAIL_E_HIP; work enqueued before it in the same call may have run.
+ *  - A context is not thread-safe and assumes one stream order: use one
+ *    context per stream.
+ */
+#ifndef QUAIL_H
+#define QUAIL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t quail_status;
+#define QUAIL_OK              0
+#define QUAIL_E_INVAL        (-1)   /* malformed argument */
+#define QUAIL_E_NOMEM        (-2)   /* KV pool or workspace too small */
+#define QUAIL_E_STALE        (-3)   /* anchor handle released or used up */
+#define QUAIL_E_HIP          (-4)   /* HIP runtime / launch failure */
+#define QUAIL_E_UNSUPPORTED  (-5)   /* shape the kernels do not cover */
+
+#define QUAIL_DTYPE_F32       0
+#define QUAIL_DTYPE_BF16      1
+#define QUAIL_DTYPE_FP8_E4M3  2
+
+typedef struct quail_ctx quail_ctx;
+typedef void* quail_stream;                      /* hipStream_t */
+
+/* Anchor handle: (generation << 32) | slot. QUAIL_NO_ANCHOR marks a filter
+ * row (a suffix with no anchor: anchor length 0). */
+typedef int64_t quail_anchor;
+#define QUAIL_NO_ANCHOR ((quail_anchor)-1)
+
+/* Model shape. Supported by the kernels: head_dim == 128; hidden,
+ * intermediate multiples of 64; n_q_heads a multiple of n_kv_heads with
+ * group size 1, 2, 4 or 8. kv_dtype is QUAIL_DTYPE_BF16 or
+ * QUAIL_DTYPE_FP8_E4M3 (anchor KV stored as E4M3 codes of k/k_scale and
+ * v/v_scale, saturating, round-to-nearest-even). RoPE is rotate-half with
+ * inverse frequency rope_theta^(-2i/head_dim); RMSNorm is
+ * x / sqrt(mean(x^2) + rms_eps) * gamma. Positions: anchor tokens 0..La-1,
+ * suffix token j at La + j; La + Ls must not exceed max_anchor_len +
+ * max_suffix_len. */
+typedef struct {
+    int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, vocab;
+    float rope_theta, rms_eps;
+    int32_t kv_dtype;
+    float k_scale, v_scale;
+    int32_t max_anchor_len, max_suffix_len;
+} quail_model_config;
+
+/* One layer's weights (all dev). fp8 matrices are [out, in] E4M3 codes with
+ * one bf16 scale per output row: W_eff[o][i] = decode(code[o][i]) * scale[o].
+ * w_qkv rows: q (n_q_heads*head_dim), then k, then v (n_kv_heads*head_dim
+ * each). w_gate_up rows: gate (intermediate), then up (intermediate). */
+typedef struct {
+    const uint16_t *attn_norm, *mlp_norm;              /* bf16 [hidden] */
+    const uint8_t  *w_qkv, *w_o, *w_gate_up, *w_down;  /* fp8 [out, in] */
+    const uint16_t *s_qkv, *s_o, *s_gate_up, *s_down;  /* bf16 [out] */
+} quail_layer_weights;
+
+typedef struct {
+    const uint16_t *embed;                 /* dev bf16 [vocab, hidden] */
+    const quail_layer_weights *layers;     /* host array [n_layers] */
+    const uint16_t *final_norm;            /* dev bf16 [hidden] */
+    const uint16_t *head8;                 /* dev bf16 [hidden, 8] */
+} quail_weights;
+
+/* ---- library ------------------------------------------------------------ */
+const char*  quail_version(void);
+/* Message of the last failing call on this thread ("" if none). */
+const char*  quail_last_error(void);
+
+/* ---- sizing --------------------------------------------------------------- */
+/* Pool bytes one anchor of `anchor_len` tokens occupies: layers x {K,V} x
+ * kv heads x ceil(anchor_len/64)*64 tokens x head_dim x (2 B bf16 | 1 B fp8),
+ * rounded up to 256 B. Slab layout [layer][K|V][kv_head][token][head_dim]. */
+quail_status quail_anchor_bytes(const quail_model_config* cfg, int32_t anchor_len, size_t* out);
+
+/* Workspace bytes a context needs for batches of up to `max_batch_tokens`
+ * tokens (activations, per-batch metadata, the RoPE table). */
+quail_status quail_workspace_bytes(const quail_model_config* cfg, int32_t max_batch_tokens,
+                                   size_t* out);
+
+/* ---- plan (a1) ------------------------------------------------------------ */
+/* Orders pairs for anchor-KV reuse ([pt] "Como funciona", query-aware KV
+ * cache bullet; [it] the Modal-blog quote on ordering requests to cache and
+ * evict KV): pairs are stably sorted by anchor index (filter rows,
+ * pair_anchor < 0, last), then cut greedily into steps that fit both
+ * `max_batch_tokens` suffix tokens and `pool_bytes` of distinct anchor slabs.
+ * Under prefill-at-first-use and evict-after-last-use, the bytes resident
+ * during a step are the slabs of the distinct anchors it touches.
+ * Inputs (host): anchor_len[n_anchors], pair_anchor[n_pairs] (-1 = filter
+ * row), pair_len[n_pairs]. Outputs (host): pair_order[n_pairs],
+ * step_bounds[n_pairs + 1] (step s is pair_order[step_bounds[s] ..
+ * step_bounds[s+1]) ), *n_steps, *peak_bytes (largest step residency).
+ * E_INVAL for a pair length outside [1, max_batch_tokens] or an anchor index
+ * out of range; E_NOMEM if one slab exceeds pool_bytes. Touches no GPU. */
+quail_status quail_plan_build(const quail_model_config* cfg, size_t pool_bytes,
+                              int32_t max_batch_tokens,
+                              int32_t n_anchors, const int32_t* anchor_len,
+                              int32_t n_pairs, const int32_t* pair_anchor, const int32_t* pair_len,
+                              int32_t* pair_order, int32_t* step_bounds, int32_t* n_steps,
+                              size_t* peak_bytes);
+
+/* ---- context -------------------------------------------------------------- */
+/* Borrows the weights (they must outlive the context), the KV pool (dev,
+ * pool_bytes, 256-B aligned) and the workspace (dev, at least
+ * quail_workspace_bytes(cfg, max_batch_tokens)). Touches no GPU. */
+quail_status quail_ctx_create(const quail_model_config* cfg, const quail_weights* w,
+                              void* kv_pool, size_t pool_bytes,
+                              void* workspace, size_t ws_bytes, int32_t max_batch_tokens,
+                              quail_ctx** out);
+quail_status quail_ctx_destroy(quail_ctx* ctx);
+
+/* ---- anchor prefill + KV writer (a2, a3, a9) -------------------------------- */
+/* Runs the decoder stack over each anchor's tokens (positions 0..La-1) and
+ * stores every layer's post-RoPE K and its V in a pool slab carved for the
+ * anchor: the anchor's KV is computed once and reused by all of its pairs
+ * ([pt] "Como funciona", cascade-attention bullet; [it] ordering requests to
+ * reuse KV). Anchor self-attention is causal and reads the stored (for fp8,
+ * decoded) K/V.
+ * tokens: dev int32, anchors packed back to back; offsets: host [n+1],
+ * non-decreasing, anchor a = tokens[offsets[a] .. offsets[a+1]), length in
+ * [1, min(max_anchor_len, max_batch_tokens)]. n_uses: host [n], the number of
+ * pairs that will read the anchor (0 = never prefilled; its handle is
+ * QUAIL_NO_ANCHOR). anchor_ids: host [n] caller row ids or NULL; an id that
+ * was prefilled and evicted before counts its tokens as regret.
+ * out: host [n] handles. E_NOMEM (nothing enqueued, nothing kept) when the
+ * pool cannot hold all n slabs at once. */
+quail_status quail_anchor_prefill(quail_ctx* ctx, int32_t n, const int32_t* tokens,
+                                  const int32_t* offsets, const int32_t* n_uses,
+                                  const int64_t* anchor_ids, quail_anchor* out,
+                                  quail_stream stream);
+
+/* Gives up an anchor before its declared uses are spent (its slab is freed;
+ * later use returns E_STALE). */
+quail_status quail_anchor_release(quail_ctx* ctx, quail_anchor handle);
+
+/* Device addresses of an anchor's K and V for one layer ([kv_head][La_pad]
+ * [head_dim], bf16 or fp8 per kv_dtype) and its lengths. For tests/tools. */
+quail_status quail_anchor_kv(const quail_ctx* ctx, quail_anchor handle, int32_t layer,
+                             void** k, void** v, int32_t* anchor_len, int32_t* padded_len);
+
+/* ---- join prefill (a2, a4-a7) --------------------------------------------- */
+/* For each pair i: suffix tokens tokens[offsets[i] .. offsets[i+1]) (dev
+ * int32; host offsets [n+1], non-decreasing, lengths in [1,
+ * min(max_suffix_len, max_batch_tokens)]) at positions La + j after anchor
+ * pair_anchor[i] (host handle, or QUAIL_NO_ANCHOR for a filter row). Runs the
+ * decoder stack: RMSNorm, W8A16 QKV + RoPE, cascade attention against the
+ * anchor's stored KV ([pt] "Como funciona": the suffix attends to the anchor,
+ * then to itself, merged by LSE rescaling), O projection + residual,
+ * RMSNorm, SwiGLU MLP + residual. Writes the last position's hidden state to
+ * h_last (dev bf16 [n, hidden], caller order) and, if h_all is not NULL, every
+ * position's final hidden state to h_all (dev bf16 [offsets[n], hidden]).
+ * Pairs may come in any order; each pair spends one use of its anchor and an
+ * anchor whose uses reach 0 is evicted (its slab is reused in stream order).
+ * E_STALE if a handle is stale or used more often than declared. */
+quail_status quail_join_prefill(quail_ctx* ctx, int32_t n, const quail_anchor* pair_anchor,
+                                const int32_t* tokens, const int32_t* offsets,
+                                uint16_t* h_last, uint16_t* h_all, quail_stream stream);
+
+/* ---- 8-column head + boolean (a8) ----------------------------------------- */
+/* z = bf16(RMSNorm(h_last; final_norm)); logits = z . head8 (fp32 [n, 8]);
+ * token = first maximum; decision = (true_mask >> token) & 1 ([pt] "Como
+ * funciona", zero-decode bullet and the 8-option head; [fa] key points).
+ * h_last dev bf16 [n, hidden]; logits dev f32 [n, 8]; token, decision dev u8
+ * [n]. Any output pointer may be NULL except decision. */
+quail_status quail_head8(quail_ctx* ctx, int32_t n, const uint16_t* h_last, uint8_t true_mask,
+                         float* logits, uint8_t* token, uint8_t* decision, quail_stream stream);
+
+/* Context-free fp32 head without a norm: logits = x . w8 for x dev f32
+ * [n, hidden], w8 dev f32 [hidden, 8]. */
+quail_status quail_head8_f32(int32_t n, int32_t hidden, const float* x, const float* w8,
+                             uint8_t true_mask, float* logits, uint8_t* token,
+                             uint8_t* decision, quail_stream stream);
+
+/* ---- whole join (a1-a9 in one call) --------------------------------------- */
+/* Runs a join end to end: builds the plan (quail_plan_build order and steps),
+ * prefills each anchor just before its first step, runs each step's pairs,
+ * evicts each anchor after its last step, and applies the head.
+ * a_tokens dev int32 + a_offsets host [n_anchors+1]; pair_anchor host
+ * [n_pairs] anchor index or -1; s_tokens dev int32 + s_offsets host
+ * [n_pairs+1]. Outputs (dev, caller pair order): logits f32 [n_pairs, 8]
+ * (nullable), token u8 (nullable), decision u8 [n_pairs]. */
+quail_status quail_join_run(quail_ctx* ctx, int32_t n_anchors, const int32_t* a_tokens,
+                            const int32_t* a_offsets, int32_t n_pairs,
+                            const int32_t* pair_anchor, const int32_t* s_tokens,
+                            const int32_t* s_offsets, uint8_t true_mask, float* logits,
+                            uint8_t* token, uint8_t* decision, quail_stream stream);
+
+/* Residency counters: bytes resident now and at peak, anchors prefilled,
+ * anchors evicted, regret tokens (anchor tokens prefilled again after an
+ * eviction). Any pointer may be NULL. */
+quail_status quail_pool_stats(const quail_ctx* ctx, size_t* resident, size_t* peak,
+                              int64_t* prefills, int64_t* evictions, int64_t* regret_tokens);
+
+/* ---- cascade attention on given Q/K/V (a5) --------------------------------- */
+/* [pt] "Como funciona", cascade-attention bullet: each suffix's queries
+ * attend to all of its anchor's keys (cross partial, no mask) and causally to
+ * its own keys (self partial, diagonal included); the partials are merged by
+ * LSE rescaling. Softmax scale sm_scale; query head h reads KV head
+ * h / (hq / hkv).
+ * dtype: QUAIL_DTYPE_F32 (head_dim 64 or 128) or QUAIL_DTYPE_BF16 (head_dim
+ * 128). ak, av: dev [sum La, hkv, d]; a_off: host [n_anchors+1]. q: dev
+ * [sum Ls, hq, d]; k, v: dev [sum Ls, hkv, d]; s_off: host [n_suffix+1];
+ * s_anchor: host [n_suffix] anchor index or -1 (no anchor). Suffixes of one
+ * anchor are processed together; any order is accepted.
+ * out: dev [sum Ls, hq, d] (dtype); lse: dev f32 [sum Ls, hq] natural-log
+ * LSE of the merged row, or NULL. workspace: dev, at least
+ * quail_cascade_workspace_bytes(...). */
+quail_status quail_cascade_workspace_bytes(int32_t n_anchors, const int32_t* a_off,
+                                           int32_t n_suffix, const int32_t* s_off,
+                                           size_t* out);
+quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t d, float sm_scale,
+                                int32_t n_anchors, const void* ak, const void* av,
+                                const int32_t* a_off, int32_t n_suffix, const int32_t* s_anchor,
+                                const void* q, const void* k, const void* v, const int32_t* s_off,
+                                void* out, float* lse, void* workspace, size_t ws_bytes,
+                                quail_stream stream);
+
+/* ---- W8A16 GEMM (the projections of a4, a6, a7) ----------------------------- */
+/* y[m][n] = bf16( scale[n] * sum_k x[m][k] * decode(w[n][k]) ), fp32
+ * accumulation. x dev bf16 [M, K] (row stride K); w dev fp8 [N, K]; scale dev
+ * bf16 [N]; y dev bf16 [M, N]. K a multiple of 64, N a multiple of 128 ([it]
+ * "Qwen3 4B FP8": FP8 weights, bf16 activations). */
+quail_status quail_gemm_w8a16(int32_t M, int32_t N, int32_t K, const uint16_t* x,
+                              const uint8_t* w, const uint16_t* scale, uint16_t* y,
+                              quail_stream stream);
+
+/* ---- E4M3 codec of the fp8 KV store -------------------------------------- */
+/* codes[i] = E4M3(x[i] / scale): saturate to +-448, round to nearest, ties to
+ * the even code (the KV writer's quantiser for anchor K/V held as fp8; the
+ * configuration "fp8 KV ~58 GB resident" of the multi-join workload).
+ * x dev f32 [n]; codes dev u8 [n]. */
+quail_status quail_fp8_e4m3_encode(int64_t n, const float* x, float scale, uint8_t* codes,
+                                   quail_stream stream);
+/* x[i] = decode(codes[i]) * scale (exact decode; NaN codes give NaN). */
+quail_status quail_fp8_e4m3_decode(int64_t n, const uint8_t* codes, float scale, float* x,
+                                   quail_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QUAIL_H */

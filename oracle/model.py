@@ -116,6 +116,7 @@ def decoder_layer(h, pos, W: LayerWeights, shape, mode="contract", fp8_kv_upto=0
     q = _bf(rope(q, pos, shape.rope_theta), mode)
     k = _bf(rope(k, pos, shape.rope_theta), mode)
     v = _bf(v, mode)
+    k_pre, v_pre = k, v          # the values an fp8 store quantises
     if fp8_kv_upto > 0:
         n = fp8_kv_upto
         k = k.copy()
@@ -129,7 +130,7 @@ def decoder_layer(h, pos, W: LayerWeights, shape, mode="contract", fp8_kv_upto=0
     m = _bf(silu(u @ W.w_gate.T) * (u @ W.w_up.T), mode)
     h = _bf(h + m @ W.w_down.T, mode)
     if return_kv:
-        return h, k, v
+        return h, (k, v, k_pre, v_pre)
     return h
 
 
@@ -149,8 +150,8 @@ def forward_tokens(tokens, weights, shape, mode="contract", fp8_kv_upto=0,
         W = layers[l] if layers is not None else LayerWeights(weights["layers"][l], shape, dtype)
         out = decoder_layer(h, pos, W, shape, mode, fp8_kv_upto, return_kv=return_kv)
         if return_kv:
-            h, k, v = out
-            kvs.append((k, v))
+            h, kv = out
+            kvs.append(kv)          # (k, v, k before fp8 storage, v before fp8 storage)
         else:
             h = out
     return (h, kvs) if return_kv else h

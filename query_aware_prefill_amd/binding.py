@@ -1,0 +1,291 @@
+"""Thin ctypes binding of libquail.so (include/quail.h).
+
+Argument marshalling only: torch tensors are passed as device pointers, host
+arrays as ctypes buffers, torch streams as hipStream_t handles. Every step of
+the prefill path runs inside the library's HIP kernels; this module computes
+nothing. It fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libquail.so")
+_lib = None
+
+OK, E_INVAL, E_NOMEM, E_STALE, E_HIP, E_UNSUPPORTED = 0, -1, -2, -3, -4, -5
+DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
+NO_ANCHOR = -1
+
+_STATUS = {E_INVAL: "E_INVAL", E_NOMEM: "E_NOMEM", E_STALE: "E_STALE", E_HIP: "E_HIP",
+           E_UNSUPPORTED: "E_UNSUPPORTED"}
+
+
+class QuailError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class ModelConfig(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("hidden", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("intermediate", C.c_int32),
+                ("vocab", C.c_int32), ("rope_theta", C.c_float), ("rms_eps", C.c_float),
+                ("kv_dtype", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float),
+                ("max_anchor_len", C.c_int32), ("max_suffix_len", C.c_int32)]
+
+
+class LayerWeights(C.Structure):
+    _fields_ = [("attn_norm", C.c_void_p), ("mlp_norm", C.c_void_p),
+                ("w_qkv", C.c_void_p), ("w_o", C.c_void_p), ("w_gate_up", C.c_void_p),
+                ("w_down", C.c_void_p), ("s_qkv", C.c_void_p), ("s_o", C.c_void_p),
+                ("s_gate_up", C.c_void_p), ("s_down", C.c_void_p)]
+
+
+class Weights(C.Structure):
+    _fields_ = [("embed", C.c_void_p), ("layers", C.POINTER(LayerWeights)),
+                ("final_norm", C.c_void_p), ("head8", C.c_void_p)]
+
+
+_i32p = C.POINTER(C.c_int32)
+_i64p = C.POINTER(C.c_int64)
+_szp = C.POINTER(C.c_size_t)
+_vp = C.c_void_p
+
+_SIGS = {
+    "quail_version": ([], C.c_char_p),
+    "quail_last_error": ([], C.c_char_p),
+    "quail_anchor_bytes": ([C.POINTER(ModelConfig), C.c_int32, _szp], C.c_int32),
+    "quail_workspace_bytes": ([C.POINTER(ModelConfig), C.c_int32, _szp], C.c_int32),
+    "quail_plan_build": ([C.POINTER(ModelConfig), C.c_size_t, C.c_int32, C.c_int32, _i32p, C.c_int32,
+                          _i32p, _i32p, _i32p, _i32p, _i32p, _szp], C.c_int32),
+    "quail_ctx_create": ([C.POINTER(ModelConfig), C.POINTER(Weights), _vp, C.c_size_t, _vp, C.c_size_t,
+                          C.c_int32, C.POINTER(_vp)], C.c_int32),
+    "quail_ctx_destroy": ([_vp], C.c_int32),
+    "quail_anchor_prefill": ([_vp, C.c_int32, _vp, _i32p, _i32p, _i64p, _i64p, _vp], C.c_int32),
+    "quail_anchor_release": ([_vp, C.c_int64], C.c_int32),
+    "quail_anchor_kv": ([_vp, C.c_int64, C.c_int32, C.POINTER(_vp), C.POINTER(_vp), _i32p, _i32p],
+                        C.c_int32),
+    "quail_join_prefill": ([_vp, C.c_int32, _i64p, _vp, _i32p, _vp, _vp, _vp], C.c_int32),
+    "quail_head8": ([_vp, C.c_int32, _vp, C.c_uint8, _vp, _vp, _vp, _vp], C.c_int32),
+    "quail_head8_f32": ([C.c_int32, C.c_int32, _vp, _vp, C.c_uint8, _vp, _vp, _vp, _vp], C.c_int32),
+    "quail_join_run": ([_vp, C.c_int32, _vp, _i32p, C.c_int32, _i32p, _vp, _i32p, C.c_uint8, _vp, _vp,
+                        _vp, _vp], C.c_int32),
+    "quail_pool_stats": ([_vp, _szp, _szp, _i64p, _i64p, _i64p], C.c_int32),
+    "quail_cascade_workspace_bytes": ([C.c_int32, _i32p, C.c_int32, _i32p, _szp], C.c_int32),
+    "quail_cascade_attn": ([C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_float, C.c_int32, _vp, _vp,
+                            _i32p, C.c_int32, _i32p, _vp, _vp, _vp, _i32p, _vp, _vp, _vp, C.c_size_t,
+                            _vp], C.c_int32),
+    "quail_gemm_w8a16": ([C.c_int32, C.c_int32, C.c_int32, _vp, _vp, _vp, _vp, _vp], C.c_int32),
+    "quail_fp8_e4m3_encode": ([C.c_int64, _vp, C.c_float, _vp, _vp], C.c_int32),
+    "quail_fp8_e4m3_decode": ([C.c_int64, _vp, C.c_float, _vp, _vp], C.c_int32),
+}
+
+EXPORTS = tuple(_SIGS)
+
+
+def load(path: str = _LIB_PATH):
+    """Load libquail.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m query_aware_prefill_amd.build` (there is no fallback)")
+    lib = C.CDLL(path)
+    for name, (args, res) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(st):
+    if st != OK:
+        raise QuailError(st, load().quail_last_error().decode())
+
+
+# ---- marshalling helpers ------------------------------------------------------
+def _i32(a):
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(_i32p)
+
+
+def _i64(a):
+    a = np.ascontiguousarray(a, dtype=np.int64)
+    return a, a.ctypes.data_as(_i64p)
+
+
+def dptr(t):
+    """Device pointer of a contiguous torch CUDA tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def stream_handle(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+# ---- library calls (same names as the C ABI) -----------------------------------
+def quail_version() -> str:
+    return load().quail_version().decode()
+
+
+def quail_anchor_bytes(cfg: ModelConfig, anchor_len: int) -> int:
+    out = C.c_size_t()
+    _check(load().quail_anchor_bytes(C.byref(cfg), anchor_len, C.byref(out)))
+    return out.value
+
+
+def quail_workspace_bytes(cfg: ModelConfig, max_batch_tokens: int) -> int:
+    out = C.c_size_t()
+    _check(load().quail_workspace_bytes(C.byref(cfg), max_batch_tokens, C.byref(out)))
+    return out.value
+
+
+def quail_plan_build(cfg: ModelConfig, pool_bytes: int, max_batch_tokens: int, anchor_len,
+                     pair_anchor, pair_len):
+    al, alp = _i32(anchor_len)
+    pa, pap = _i32(pair_anchor)
+    pl, plp = _i32(pair_len)
+    n = len(pa)
+    order, op = _i32(np.zeros(n, np.int32))
+    bounds, bp = _i32(np.zeros(n + 1, np.int32))
+    nsteps = C.c_int32()
+    peak = C.c_size_t()
+    _check(load().quail_plan_build(C.byref(cfg), pool_bytes, max_batch_tokens, len(al), alp, n, pap,
+                                   plp, op, bp, C.byref(nsteps), C.byref(peak)))
+    return order, bounds[: nsteps.value + 1].copy(), peak.value
+
+
+class Context:
+    """Owns a quail_ctx; device buffers (weights, pool, workspace) are torch
+    tensors held by the caller and borrowed here."""
+
+    def __init__(self, cfg: ModelConfig, weights: Weights, kv_pool, workspace, max_batch_tokens: int):
+        self.cfg = cfg
+        self._weights = weights       # keep the ctypes struct (and its layer array) alive
+        self._pool = kv_pool
+        self._ws = workspace
+        h = C.c_void_p()
+        _check(load().quail_ctx_create(C.byref(cfg), C.byref(weights), dptr(kv_pool),
+                                       kv_pool.numel() * kv_pool.element_size() if kv_pool is not None else 0,
+                                       dptr(workspace), workspace.numel() * workspace.element_size(),
+                                       max_batch_tokens, C.byref(h)))
+        self.handle = h
+
+    def close(self):
+        if self.handle:
+            load().quail_ctx_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def quail_anchor_prefill(ctx: Context, tokens, offsets, n_uses, anchor_ids=None, stream=None):
+    off, offp = _i32(offsets)
+    nu, nup = _i32(n_uses)
+    n = len(off) - 1
+    out, outp = _i64(np.zeros(n, np.int64))
+    ids, idsp = (None, None) if anchor_ids is None else _i64(anchor_ids)
+    _check(load().quail_anchor_prefill(ctx.handle, n, dptr(tokens), offp, nup, idsp, outp,
+                                       stream_handle(stream)))
+    return out
+
+
+def quail_anchor_release(ctx: Context, handle: int):
+    _check(load().quail_anchor_release(ctx.handle, int(handle)))
+
+
+def quail_anchor_kv(ctx: Context, handle: int, layer: int):
+    k, v = C.c_void_p(), C.c_void_p()
+    la, lp = C.c_int32(), C.c_int32()
+    _check(load().quail_anchor_kv(ctx.handle, int(handle), layer, C.byref(k), C.byref(v),
+                                  C.byref(la), C.byref(lp)))
+    return k.value, v.value, la.value, lp.value
+
+
+def quail_join_prefill(ctx: Context, pair_anchor, tokens, offsets, h_last, h_all=None, stream=None):
+    pa, pap = _i64(pair_anchor)
+    off, offp = _i32(offsets)
+    _check(load().quail_join_prefill(ctx.handle, len(pa), pap, dptr(tokens), offp, dptr(h_last),
+                                     dptr(h_all), stream_handle(stream)))
+
+
+def quail_head8(ctx: Context, h_last, true_mask, logits, token, decision, stream=None):
+    _check(load().quail_head8(ctx.handle, h_last.shape[0], dptr(h_last), true_mask, dptr(logits),
+                              dptr(token), dptr(decision), stream_handle(stream)))
+
+
+def quail_head8_f32(x, w8, true_mask, logits, token, decision, stream=None):
+    _check(load().quail_head8_f32(x.shape[0], x.shape[1], dptr(x), dptr(w8), true_mask, dptr(logits),
+                                  dptr(token), dptr(decision), stream_handle(stream)))
+
+
+def quail_join_run(ctx: Context, a_tokens, a_offsets, pair_anchor, s_tokens, s_offsets, true_mask,
+                   logits, token, decision, stream=None):
+    ao, aop = _i32(a_offsets)
+    pa, pap = _i32(pair_anchor)
+    so, sop = _i32(s_offsets)
+    _check(load().quail_join_run(ctx.handle, len(ao) - 1, dptr(a_tokens), aop, len(pa), pap,
+                                 dptr(s_tokens), sop, true_mask, dptr(logits), dptr(token),
+                                 dptr(decision), stream_handle(stream)))
+
+
+def quail_pool_stats(ctx: Context) -> dict:
+    r, p = C.c_size_t(), C.c_size_t()
+    pf, ev, rg = C.c_int64(), C.c_int64(), C.c_int64()
+    _check(load().quail_pool_stats(ctx.handle, C.byref(r), C.byref(p), C.byref(pf), C.byref(ev),
+                                   C.byref(rg)))
+    return dict(resident=r.value, peak=p.value, prefills=pf.value, evictions=ev.value,
+                regret_tokens=rg.value)
+
+
+def quail_cascade_workspace_bytes(a_off, s_off) -> int:
+    ao, aop = _i32(a_off)
+    so, sop = _i32(s_off)
+    out = C.c_size_t()
+    _check(load().quail_cascade_workspace_bytes(max(len(ao) - 1, 0), aop, len(so) - 1, sop,
+                                                C.byref(out)))
+    return out.value
+
+
+def quail_cascade_attn(dtype, hq, hkv, d, sm_scale, ak, av, a_off, s_anchor, q, k, v, s_off, out,
+                       lse=None, workspace=None, stream=None):
+    ao, aop = _i32(a_off)
+    sa, sap = _i32(s_anchor)
+    so, sop = _i32(s_off)
+    _check(load().quail_cascade_attn(dtype, hq, hkv, d, sm_scale, max(len(ao) - 1, 0), dptr(ak),
+                                     dptr(av), aop, len(sa), sap, dptr(q), dptr(k), dptr(v), sop,
+                                     dptr(out), dptr(lse), dptr(workspace),
+                                     workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                     stream_handle(stream)))
+
+
+def quail_gemm_w8a16(x, w, scale, y, stream=None):
+    M, K = x.shape
+    N = w.shape[0]
+    _check(load().quail_gemm_w8a16(M, N, K, dptr(x), dptr(w), dptr(scale), dptr(y),
+                                   stream_handle(stream)))
+
+
+def quail_fp8_e4m3_encode(x, scale, codes, stream=None):
+    _check(load().quail_fp8_e4m3_encode(x.numel(), dptr(x), scale, dptr(codes), stream_handle(stream)))
+
+
+def quail_fp8_e4m3_decode(codes, scale, x, stream=None):
+    _check(load().quail_fp8_e4m3_decode(codes.numel(), dptr(codes), scale, dptr(x), stream_handle(stream)))

@@ -1,0 +1,416 @@
+// Cascade attention for AI.IF join prefill on gfx950.
+//
+// [pt] "Como funciona", simplified cascade attention: each suffix token
+// attends to every key of its anchor (cross-attention), then causally to the
+// keys of its own suffix, and the two softmax partials are combined by LSE
+// rescaling. The same kernel runs the anchor's own causal attention (no
+// cross part; the "self" keys are the anchor's stored slab).
+//
+// bf16 kernel (head_dim 128)
+// --------------------------
+// One workgroup = one tile of query tokens x one KV head g. Its NW waves cover
+// the G query heads of g (GQA group) x NW/G groups of 32 tokens; every wave
+// reads the same K/V tiles from LDS. Per 64-key tile each wave computes
+//   S^T = K . Q^T      (v_mfma_f32_32x32x16_bf16, A = K rows, B = Q rows)
+// so that each lane owns ONE query row (lane % 32) and 32 of the tile's keys:
+// the row max and row sum are per-lane scalars, combined with the partner
+// lane (lane ^ 32) by one exchange. Then
+//   O^T += V^T . P^T   (A = V^T rows from a transposed LDS tile, B = P)
+// where P comes straight from the S^T accumulator registers in the k-slot
+// order the MFMA expects; V^T is read with the same key permutation.
+// The cross keys and the self keys form one sequence of tiles with one online
+// softmax: rescaling the running cross accumulator by exp(m_cross - m) when
+// the self keys arrive is exactly the LSE merge of the two partials
+// (O = e^(L_c - L) O_c + e^(L_s - L) O_s with L = logaddexp(L_c, L_s)).
+//
+// fp32 kernel (head_dim 64 or 128)
+// --------------------------------
+// One wave per (query token, query head); computes the cross partial (O_c,
+// L_c) and the self partial (O_s, L_s) separately and merges them with the
+// LSE formula. Used for the fp32 configuration, where accuracy, not speed,
+// is the point.
+#include "device_common.h"
+#include "quail_internal.h"
+
+namespace quail {
+
+constexpr int KSTR = kHeadDim + 8;   // K tile row stride in LDS (u16): 272 B
+constexpr int VSTR = kKeyTile + 4;   // V^T tile row stride in LDS (u16): 136 B
+
+struct TileView {
+  const uint8_t* k;       // byte pointer to (row 0, head g)
+  const uint8_t* v;
+  int64_t tok_bytes;      // bytes between tokens
+  int32_t kbase;          // first key index of the tile
+  int32_t len;            // valid rows of the source
+  int32_t fp8;
+};
+
+// Register prefetch of one K/V tile. K: KC chunks of 8 elements per thread.
+// V: one 4-key x 8-dim block per thread (threads < 256).
+template <int NT>
+struct TileRegs {
+  static constexpr int KC = (kKeyTile * kHeadDim / 8) / NT;
+  uint4 k[KC];
+  uint4 v[4];
+};
+
+template <int NT>
+__device__ __forceinline__ void load_tile(TileRegs<NT>& r, const TileView& t, int tid) {
+  const int esz = t.fp8 ? 1 : 2;
+#pragma unroll
+  for (int i = 0; i < TileRegs<NT>::KC; ++i) {
+    const int chunk = tid + i * NT;
+    const int row = chunk >> 4;            // 16 chunks of 8 dims per row
+    const int c8 = chunk & 15;
+    const int key = t.kbase + row;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (key < t.len) {
+      const uint8_t* p = t.k + (int64_t)key * t.tok_bytes + c8 * 8 * esz;
+      if (t.fp8) {
+        uint2 w = *reinterpret_cast<const uint2*>(p);
+        val = make_uint4(w.x, w.y, 0, 0);
+      } else {
+        val = *reinterpret_cast<const uint4*>(p);
+      }
+    }
+    r.k[i] = val;
+  }
+  if (NT <= 256 || tid < 256) {
+    const int blk = tid & 255;             // 16 key groups x 16 dim chunks
+    const int kg = blk >> 4;
+    const int c8 = blk & 15;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = t.kbase + kg * 4 + j;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (key < t.len) {
+        const uint8_t* p = t.v + (int64_t)key * t.tok_bytes + c8 * 8 * esz;
+        if (t.fp8) {
+          uint2 w = *reinterpret_cast<const uint2*>(p);
+          val = make_uint4(w.x, w.y, 0, 0);
+        } else {
+          val = *reinterpret_cast<const uint4*>(p);
+        }
+      }
+      r.v[j] = val;
+    }
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void store_tile(const TileRegs<NT>& r, int fp8, float ks, float vs,
+                                           uint16_t* Ks, uint16_t* Vt, int tid) {
+#pragma unroll
+  for (int i = 0; i < TileRegs<NT>::KC; ++i) {
+    const int chunk = tid + i * NT;
+    const int row = chunk >> 4;
+    const int c8 = chunk & 15;
+    uint4 val = r.k[i];
+    if (fp8) {
+      uint32_t a, b, c, d;
+      fp8x4_to_bf16x4_scaled(val.x, ks, a, b);
+      fp8x4_to_bf16x4_scaled(val.y, ks, c, d);
+      val = make_uint4(a, b, c, d);
+    }
+    *reinterpret_cast<uint4*>(Ks + row * KSTR + c8 * 8) = val;
+  }
+  if (NT <= 256 || tid < 256) {
+    const int blk = tid & 255;
+    const int kg = blk >> 4;
+    const int c8 = blk & 15;
+    uint32_t w[4][4];   // w[j] = 8 bf16 of key kg*4+j, packed in 4 words
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint4 val = r.v[j];
+      if (fp8) {
+        uint32_t a, b, c, d;
+        fp8x4_to_bf16x4_scaled(val.x, vs, a, b);
+        fp8x4_to_bf16x4_scaled(val.y, vs, c, d);
+        val = make_uint4(a, b, c, d);
+      }
+      w[j][0] = val.x; w[j][1] = val.y; w[j][2] = val.z; w[j][3] = val.w;
+    }
+    // transpose: dim c8*8 + e, keys kg*4 .. kg*4+3
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int word = e >> 1;
+      const int sh = (e & 1) * 16;
+      uint32_t k0 = (w[0][word] >> sh) & 0xFFFFu;
+      uint32_t k1 = (w[1][word] >> sh) & 0xFFFFu;
+      uint32_t k2 = (w[2][word] >> sh) & 0xFFFFu;
+      uint32_t k3 = (w[3][word] >> sh) & 0xFFFFu;
+      uint2 out = make_uint2(k0 | (k1 << 16), k2 | (k3 << 16));
+      *reinterpret_cast<uint2*>(Vt + (c8 * 8 + e) * VSTR + kg * 4) = out;
+    }
+  }
+}
+
+template <int G>
+__global__ void __launch_bounds__(64 * (G >= 4 ? G : 4))
+attn_bf16_kernel(AttnParams p) {
+  constexpr int NW = G >= 4 ? G : 4;     // waves per workgroup
+  constexpr int NT = 64 * NW;
+  constexpr int TOKG = NW / G;           // token groups of 32
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kKeyTile * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[kHeadDim * VSTR];
+
+  const int64_t total = (int64_t)p.n_tiles * p.hkv;
+  const int64_t wid = xcd_remap(blockIdx.x, total);
+  if (wid < 0) return;
+  const int g = (int)(wid / p.n_tiles);            // kv head (slow index)
+  const AttnTile tile = p.tiles[wid % p.n_tiles];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int head = g * G + (wave % G);
+  const int tg = wave / G;
+  const int qrow = tg * kQRows + l32;              // offset from tile.q0
+  const bool row_ok = qrow < tile.nq;
+  const int64_t tok = (int64_t)tile.q0 + qrow;
+
+  // Q fragments: B operand, lane holds query row l32, dims ks*16 + hi*8 .. +7
+  bf16x8_t qf[8];
+  {
+    const uint16_t* qp = p.q + tok * p.q_stride + head * kHeadDim + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
+      qf[ks] = bitcast<bf16x8_t>(u);
+    }
+  }
+  const int seg_lo = row_ok ? p.seg_lo[tok] : 0x7FFFFFFF;
+  const int self_q = tile.self_qbase + qrow;       // self-key index of this query
+
+  KVSrc cs{}, ss{};
+  int n_ct = 0, n_st = 0;
+  if (tile.cross >= 0) { cs = p.srcs[tile.cross]; n_ct = (cs.len + kKeyTile - 1) / kKeyTile; }
+  if (tile.self >= 0) {
+    ss = p.srcs[tile.self];
+    const int self_end = tile.self_qbase + tile.nq;
+    n_st = (self_end - tile.self_k0 + kKeyTile - 1) / kKeyTile;
+    if (n_st < 0) n_st = 0;
+  }
+  const int n_tiles = n_ct + n_st;
+
+  auto view = [&](int it) {
+    TileView t;
+    const KVSrc& s = it < n_ct ? cs : ss;
+    const int esz = s.fp8 ? 1 : 2;
+    t.k = reinterpret_cast<const uint8_t*>(s.k) + (int64_t)g * s.head_stride * esz;
+    t.v = reinterpret_cast<const uint8_t*>(s.v) + (int64_t)g * s.head_stride * esz;
+    t.tok_bytes = s.tok_stride * esz;
+    t.kbase = it < n_ct ? it * kKeyTile : tile.self_k0 + (it - n_ct) * kKeyTile;
+    t.len = s.len;
+    t.fp8 = s.fp8;
+    return t;
+  };
+
+  f32x16_t o[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[cb][r] = 0.0f;
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+
+  TileRegs<NT> regs;
+  if (n_tiles > 0) load_tile<NT>(regs, view(0), tid);
+
+  for (int it = 0; it < n_tiles; ++it) {
+    const bool is_cross = it < n_ct;
+    const int fp8 = is_cross ? cs.fp8 : ss.fp8;
+    const int kbase = is_cross ? it * kKeyTile : tile.self_k0 + (it - n_ct) * kKeyTile;
+    __syncthreads();
+    store_tile<NT>(regs, fp8, p.k_scale, p.v_scale, Ks, Vt, tid);
+    __syncthreads();
+    if (it + 1 < n_tiles) load_tile<NT>(regs, view(it + 1), tid);
+
+    // S^T for two 32-key blocks
+    f32x16_t s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+      const uint16_t* kp = Ks + (kb * 32 + l32) * KSTR + hi * 8;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        bf16x8_t a = bitcast<bf16x8_t>(*reinterpret_cast<const uint4*>(kp + ks * 16));
+        s[kb] = mfma_32x32x16(a, qf[ks], s[kb]);
+      }
+    }
+    // scale into the log2 domain and mask; key of (kb, r) = kb*32 + (r/4)*8 + hi*4 + r%4
+    const bool need_mask = is_cross ? (kbase + kKeyTile > cs.len) : true;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[kb][r] * p.scale_log2;
+        if (need_mask) {
+          const int key = kbase + kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+          const bool vis = is_cross ? (key < cs.len) : (key >= seg_lo && key <= self_q);
+          x = vis ? x : -INFINITY;
+        }
+        s[kb][r] = x;
+        mt = fmaxf(mt, x);
+      }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[cb][r] *= alpha;
+
+    // P (bf16) as the B operand: k-step (kb, sp) takes regs 8*sp .. 8*sp+7
+    bf16x8_t pb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = exp2f(s[kb][sp * 8 + 2 * e] - m_use);
+          const float p1 = exp2f(s[kb][sp * 8 + 2 * e + 1] - m_use);
+          l_run += p0 + p1;
+          w[e] = pack_bf16x2(p0, p1);
+        }
+        pb[kb][sp] = bitcast<bf16x8_t>(make_uint4(w[0], w[1], w[2], w[3]));
+      }
+    }
+    // O^T += V^T . P^T ; A lane: dim row cb*32 + l32, keys kb*32 + sp*16 + hi*4 + {0..3, 8..11}
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const uint16_t* vp = Vt + (cb * 32 + l32) * VSTR + hi * 4;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+          const uint2 lo = *reinterpret_cast<const uint2*>(vp + kb * 32 + sp * 16);
+          const uint2 hi2 = *reinterpret_cast<const uint2*>(vp + kb * 32 + sp * 16 + 8);
+          bf16x8_t a = bitcast<bf16x8_t>(make_uint4(lo.x, lo.y, hi2.x, hi2.y));
+          o[cb] = mfma_32x32x16(a, pb[kb][sp], o[cb]);
+        }
+      }
+    }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (!row_ok) return;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  uint16_t* op = p.out + tok * p.o_stride + head * kHeadDim + hi * 4;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      uint2 w;
+      w.x = pack_bf16x2(o[cb][rg * 4 + 0] * inv, o[cb][rg * 4 + 1] * inv);
+      w.y = pack_bf16x2(o[cb][rg * 4 + 2] * inv, o[cb][rg * 4 + 3] * inv);
+      *reinterpret_cast<uint2*>(op + cb * 32 + rg * 8) = w;
+    }
+  }
+  if (p.lse != nullptr && hi == 0) {
+    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+    const float L = l_tot > 0.0f ? (m_use + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    p.lse[tok * p.hq + head] = L;
+  }
+}
+
+hipError_t launch_attn_bf16(const AttnParams& p, int group, hipStream_t s) {
+  if (p.n_tiles == 0) return hipSuccess;
+  const int64_t total = (int64_t)p.n_tiles * p.hkv;
+  const int64_t grid = (total + 7) / 8 * 8;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  switch (group) {
+    case 1: attn_bf16_kernel<1><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p); break;
+    case 2: attn_bf16_kernel<2><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p); break;
+    case 4: attn_bf16_kernel<4><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p); break;
+    case 8: attn_bf16_kernel<8><<<dim3((unsigned)grid), dim3(512), 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// fp32 path: one wave per (token, head); explicit partials + LSE merge.
+// ----------------------------------------------------------------------------
+struct Partial {
+  float m, l;
+  float acc[2];
+};
+
+__device__ __forceinline__ void partial_scan(const float* kp, const float* vp, int64_t tstride,
+                                             int k0, int k1, const float (&q)[2], int nd,
+                                             float scale, int lane, Partial& st) {
+  st.m = -INFINITY;
+  st.l = 0.0f;
+  st.acc[0] = st.acc[1] = 0.0f;
+  for (int j = k0; j < k1; ++j) {
+    const float* kr = kp + (int64_t)j * tstride;
+    float part = 0.0f;
+    for (int e = 0; e < nd; ++e) part += q[e] * kr[lane + 64 * e];
+    const float sc = wave_sum(part) * scale;
+    const float mn = fmaxf(st.m, sc);
+    const float a = expf(st.m - mn);
+    const float pj = expf(sc - mn);
+    st.l = st.l * a + pj;
+    const float* vr = vp + (int64_t)j * tstride;
+    for (int e = 0; e < nd; ++e) st.acc[e] = st.acc[e] * a + pj * vr[lane + 64 * e];
+    st.m = mn;
+  }
+}
+
+__global__ void __launch_bounds__(256) attn_f32_kernel(AttnF32Params p) {
+  const int wave = (int)(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  if (wave >= p.n_tok * p.hq) return;
+  const int t = wave / p.hq;
+  const int h = wave % p.hq;
+  const int g = h / (p.hq / p.hkv);
+  const int nd = p.d / 64;
+  float q[2] = {0.0f, 0.0f};
+  for (int e = 0; e < nd; ++e) q[e] = p.q[((int64_t)t * p.hq + h) * p.d + lane + 64 * e];
+  const int64_t kvs = (int64_t)p.hkv * p.d;
+
+  Partial cr, sf;
+  const int a = p.tok_anchor[t];
+  if (a >= 0) {
+    partial_scan(p.ak + (int64_t)g * p.d, p.av + (int64_t)g * p.d, kvs, p.a_off[a],
+                 p.a_off[a + 1], q, nd, p.scale, lane, cr);
+  } else {
+    cr.m = -INFINITY; cr.l = 0.0f; cr.acc[0] = cr.acc[1] = 0.0f;
+  }
+  partial_scan(p.k + (int64_t)g * p.d, p.v + (int64_t)g * p.d, kvs, p.tok_seg[t], t + 1, q, nd,
+               p.scale, lane, sf);
+  // partial results: O_i = acc_i / l_i, L_i = m_i + log l_i; merge by LSE
+  const float Lc = cr.l > 0.0f ? cr.m + logf(cr.l) : -INFINITY;
+  const float Ls = sf.l > 0.0f ? sf.m + logf(sf.l) : -INFINITY;
+  const float mx = fmaxf(Lc, Ls);
+  const float L = mx + logf(expf(Lc - mx) + expf(Ls - mx));
+  const float wc = cr.l > 0.0f ? expf(Lc - L) : 0.0f;
+  const float ws = sf.l > 0.0f ? expf(Ls - L) : 0.0f;
+  for (int e = 0; e < nd; ++e) {
+    const float oc = cr.l > 0.0f ? cr.acc[e] / cr.l : 0.0f;
+    const float os = sf.l > 0.0f ? sf.acc[e] / sf.l : 0.0f;
+    p.out[((int64_t)t * p.hq + h) * p.d + lane + 64 * e] = wc * oc + ws * os;
+  }
+  if (p.lse != nullptr && lane == 0) p.lse[(int64_t)t * p.hq + h] = L;
+}
+
+hipError_t launch_attn_f32(const AttnF32Params& p, hipStream_t s) {
+  const int64_t waves = (int64_t)p.n_tok * p.hq;
+  if (waves == 0) return hipSuccess;
+  attn_f32_kernel<<<dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace quail

@@ -1,0 +1,106 @@
+// Device helpers shared by the gfx950 kernels: number formats, MFMA, lane ops.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace quail {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// float -> bf16 bits, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// Two OCP E4M3 codes (byte 0/1 of the selected 16-bit half of w) -> two
+// floats, exact (gfx950 decodes OCP E4M3).
+template <bool HI>
+__device__ __forceinline__ f32x2_t fp8x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+}
+
+// Four E4M3 codes in a 32-bit word -> four bf16 packed in two words, exact
+// (every E4M3 value is a bf16 value).
+__device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  f32x2_t a = fp8x2_to_f32<false>(w);
+  f32x2_t b = fp8x2_to_f32<true>(w);
+  lo = (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xFFFF0000u);
+  hi = (__float_as_uint(b[0]) >> 16) | (__float_as_uint(b[1]) & 0xFFFF0000u);
+}
+
+// Four E4M3 codes, decoded and multiplied by `scale`, rounded to bf16.
+__device__ __forceinline__ void fp8x4_to_bf16x4_scaled(uint32_t w, float scale, uint32_t& lo,
+                                                       uint32_t& hi) {
+  f32x2_t a = fp8x2_to_f32<false>(w);
+  f32x2_t b = fp8x2_to_f32<true>(w);
+  lo = pack_bf16x2(a[0] * scale, a[1] * scale);
+  hi = pack_bf16x2(b[0] * scale, b[1] * scale);
+}
+
+// float -> OCP E4M3 code: saturate to +-448, round to nearest, ties to even.
+// Normal range (|x| >= 2^-6): round the binary32 mantissa to 3 bits in the
+// integer domain (carries move into the exponent) and rebias 127 -> 7.
+// Subnormal range: the code is the integer nearest to |x| * 2^9 (ties even);
+// 8 there is the smallest normal, which is code 8 as well.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  uint32_t b = __float_as_uint(x);
+  uint32_t sign = (b >> 24) & 0x80u;
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return sign | 0x7Fu;     // NaN
+  float a = fminf(fabsf(x), 448.0f);
+  uint32_t code;
+  if (a >= 0.015625f) {
+    uint32_t u = __float_as_uint(a);
+    u += 0x7FFFFu + ((u >> 20) & 1u);
+    code = (u >> 20) - (120u << 3);
+  } else {
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ T bitcast(const uint4& u) {
+  static_assert(sizeof(T) == 16, "16-byte cast");
+  return __builtin_bit_cast(T, u);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Workgroup id remapped so that each of the 8 XCDs (which receive workgroups
+// round-robin) processes one contiguous range of logical ids. Returns -1 for
+// the padding ids of a grid rounded up to a multiple of 8.
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t total) {
+  const int64_t per = (total + 7) / 8;
+  const int64_t logical = (bid % 8) * per + bid / 8;
+  return logical < total ? logical : -1;
+}
+
+}  // namespace quail

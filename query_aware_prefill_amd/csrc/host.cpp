@@ -1,0 +1,1171 @@
+// Host runtime of the AI.IF join-prefill library: argument validation and the
+// error model, the plan builder, the anchor-KV residency manager, per-batch
+// metadata, and the layer loop that enqueues the gfx950 kernels.
+//
+// [pt] "Como funciona": the engine knows the whole plan, so it can predict KV
+// accesses and evict with no regret; each anchor's KV is computed once and the
+// suffixes reach it through cascade attention; prefill only, one token from
+// the final pass through an 8-column head. [it]/[pl]: the vLLM baseline lost
+// time to host overhead (the CPU planning while the GPU waited) and to KV
+// regret. Hence: plans are built once, in C++, before any launch; each batch
+// is a fixed sequence of large launches with no host synchronisation inside
+// the layer loop; per-batch metadata goes to the device in one pinned copy.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <numeric>
+#include <string>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "../../include/quail.h"
+#include "quail_internal.h"
+
+using namespace quail;
+
+// ---------------------------------------------------------------------------
+// errors
+// ---------------------------------------------------------------------------
+namespace {
+
+thread_local std::string g_err;
+
+quail_status fail(quail_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define HIP_TRY(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess)                                                               \
+      return fail(QUAIL_E_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));          \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------------------
+// pinned staging for host -> device metadata copies (stream ordered)
+// ---------------------------------------------------------------------------
+class Stager {
+ public:
+  ~Stager() {
+    for (auto& s : slots_) {
+      if (s.ev) { hipEventSynchronize(s.ev); hipEventDestroy(s.ev); }
+      if (s.buf) hipHostFree(s.buf);
+    }
+  }
+  // Copies `bytes` from host memory `src` to device `dst` on `stream`; `src`
+  // may be reused as soon as this returns.
+  hipError_t copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+    if (bytes == 0) return hipSuccess;
+    std::lock_guard<std::mutex> lk(mu_);
+    if (slots_.empty()) slots_.resize(4);
+    Slot& s = slots_[next_];
+    next_ = (next_ + 1) % slots_.size();
+    hipError_t e;
+    if (s.ev) {
+      e = hipEventSynchronize(s.ev);       // the previous copy out of this slot is done
+      if (e != hipSuccess) return e;
+    } else {
+      e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
+      if (e != hipSuccess) return e;
+    }
+    if (s.cap < bytes) {
+      if (s.buf) hipHostFree(s.buf);
+      s.buf = nullptr;
+      s.cap = 0;
+      e = hipHostMalloc(&s.buf, align_up(bytes, 1 << 20), hipHostMallocDefault);
+      if (e != hipSuccess) return e;
+      s.cap = align_up(bytes, 1 << 20);
+    }
+    std::memcpy(s.buf, src, bytes);
+    e = hipMemcpyAsync(dst, s.buf, bytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return e;
+    return hipEventRecord(s.ev, stream);
+  }
+
+ private:
+  struct Slot { void* buf = nullptr; size_t cap = 0; hipEvent_t ev = nullptr; };
+  std::vector<Slot> slots_;
+  size_t next_ = 0;
+  std::mutex mu_;
+};
+
+Stager& stager() {
+  static Stager* s = new Stager();   // process lifetime (freed by the runtime at exit)
+  return *s;
+}
+
+// Host-side blob of device metadata arrays, laid out back to back (256-B
+// aligned), copied with one staged copy; returns device pointers.
+class Blob {
+ public:
+  template <typename T>
+  size_t add(const std::vector<T>& v) {
+    size_t off = align_up(bytes_.size());
+    bytes_.resize(off + align_up(v.size() * sizeof(T)));
+    if (!v.empty()) std::memcpy(bytes_.data() + off, v.data(), v.size() * sizeof(T));
+    return off;
+  }
+  size_t size() const { return bytes_.size(); }
+  const uint8_t* data() const { return bytes_.data(); }
+  void clear() { bytes_.clear(); }
+
+ private:
+  std::vector<uint8_t> bytes_;
+};
+
+int group_tokens(int G) {   // query tokens per attention tile for GQA group size G
+  const int nw = G >= 4 ? G : 4;
+  return kQRows * (nw / G);
+}
+
+bool valid_group(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
+
+quail_status check_cfg(const quail_model_config* c) {
+  if (!c) return fail(QUAIL_E_INVAL, "config is NULL");
+  if (c->n_layers <= 0 || c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
+      c->head_dim <= 0 || c->intermediate <= 0 || c->vocab <= 0)
+    return fail(QUAIL_E_INVAL, "config sizes must be positive");
+  if (c->max_anchor_len < 0 || c->max_suffix_len <= 0)
+    return fail(QUAIL_E_INVAL, "max_anchor_len >= 0 and max_suffix_len > 0 required");
+  if (!(c->rms_eps >= 0.0f) || !(c->rope_theta > 0.0f))
+    return fail(QUAIL_E_INVAL, "rms_eps >= 0 and rope_theta > 0 required");
+  if (c->head_dim != kHeadDim)
+    return fail(QUAIL_E_UNSUPPORTED, "head_dim %d (the kernels take 128)", c->head_dim);
+  if (c->hidden % 64 || c->intermediate % 64)
+    return fail(QUAIL_E_UNSUPPORTED, "hidden and intermediate must be multiples of 64");
+  if (c->n_q_heads % c->n_kv_heads || !valid_group(c->n_q_heads / c->n_kv_heads))
+    return fail(QUAIL_E_UNSUPPORTED, "GQA group size must be 1, 2, 4 or 8");
+  if (c->kv_dtype != QUAIL_DTYPE_BF16 && c->kv_dtype != QUAIL_DTYPE_FP8_E4M3)
+    return fail(QUAIL_E_UNSUPPORTED, "kv_dtype must be BF16 or FP8_E4M3");
+  if (c->kv_dtype == QUAIL_DTYPE_FP8_E4M3 && !(c->k_scale > 0.0f && c->v_scale > 0.0f))
+    return fail(QUAIL_E_INVAL, "fp8 KV needs positive k_scale and v_scale");
+  return QUAIL_OK;
+}
+
+size_t kv_elem_bytes(const quail_model_config& c) {
+  return c.kv_dtype == QUAIL_DTYPE_FP8_E4M3 ? 1 : 2;
+}
+
+int32_t pad_len(int32_t la) { return (la + kKeyTile - 1) / kKeyTile * kKeyTile; }
+
+size_t slab_bytes(const quail_model_config& c, int32_t la) {
+  return align_up((size_t)c.n_layers * 2 * c.n_kv_heads * (size_t)pad_len(la) * c.head_dim *
+                  kv_elem_bytes(c));
+}
+
+int32_t max_pos(const quail_model_config& c) { return c.max_anchor_len + c.max_suffix_len; }
+
+// Workspace carve for a context.
+struct WsLayout {
+  size_t rope, h, u, q, k, v, o, m, hlast, meta, total;
+  size_t meta_cap;
+};
+
+size_t meta_capacity(int32_t T) {
+  // tok_src, pos, seg_lo, kv_lapad, last_idx, out_idx (int32), kv_row (int64),
+  // tiles (<= T + 64), srcs (<= T + 2), plus alignment slack
+  return align_up((size_t)T * 4) * 6 + align_up((size_t)T * 8) +
+         align_up((size_t)(T + 64) * sizeof(AttnTile)) + align_up((size_t)(T + 2) * sizeof(KVSrc)) +
+         16 * kAlign;
+}
+
+WsLayout ws_layout(const quail_model_config& c, int32_t T) {
+  WsLayout w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  const size_t Tt = (size_t)T;
+  w.rope = take((size_t)max_pos(c) * (c.head_dim / 2) * sizeof(float2));
+  w.h = take(Tt * c.hidden * 2);
+  w.u = take(Tt * c.hidden * 2);
+  w.q = take(Tt * c.n_q_heads * c.head_dim * 2);
+  w.k = take(Tt * c.n_kv_heads * c.head_dim * 2);
+  w.v = take(Tt * c.n_kv_heads * c.head_dim * 2);
+  w.o = take(Tt * c.n_q_heads * c.head_dim * 2);
+  w.m = take(Tt * c.intermediate * 2);
+  w.hlast = take(Tt * c.hidden * 2);
+  w.meta_cap = meta_capacity(T);
+  w.meta = take(w.meta_cap);
+  w.total = off;
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// plan builder (shared by quail_plan_build and quail_join_run)
+// ---------------------------------------------------------------------------
+struct Plan {
+  std::vector<int32_t> order, bounds;
+  size_t peak = 0;
+};
+
+quail_status build_plan(const std::vector<size_t>& slab, int32_t n_pairs, const int32_t* pair_anchor,
+                        const int32_t* pair_len, size_t pool_bytes, int32_t max_batch_tokens,
+                        Plan& out) {
+  const int32_t na = (int32_t)slab.size();
+  for (int32_t i = 0; i < n_pairs; ++i) {
+    const int32_t a = pair_anchor[i];
+    if (a >= na || a < -1) return fail(QUAIL_E_INVAL, "pair %d: anchor index %d out of range", i, a);
+    if (pair_len[i] <= 0 || pair_len[i] > max_batch_tokens)
+      return fail(QUAIL_E_INVAL, "pair %d: length %d outside [1, %d]", i, pair_len[i], max_batch_tokens);
+    if (a >= 0 && slab[a] > pool_bytes)
+      return fail(QUAIL_E_NOMEM, "anchor %d: slab of %zu B exceeds the pool (%zu B)", a, slab[a],
+                  pool_bytes);
+  }
+  out.order.resize(n_pairs);
+  std::iota(out.order.begin(), out.order.end(), 0);
+  auto key = [&](int32_t i) -> int64_t { return pair_anchor[i] < 0 ? INT64_MAX : pair_anchor[i]; };
+  std::stable_sort(out.order.begin(), out.order.end(),
+                   [&](int32_t x, int32_t y) { return key(x) < key(y); });
+  out.bounds.assign(1, 0);
+  out.peak = 0;
+  int64_t tokens = 0;
+  size_t bytes = 0;
+  std::unordered_set<int32_t> anchors;
+  for (int32_t pos = 0; pos < n_pairs; ++pos) {
+    const int32_t i = out.order[pos];
+    const int32_t a = pair_anchor[i];
+    const int32_t L = pair_len[i];
+    size_t add = (a >= 0 && !anchors.count(a)) ? slab[a] : 0;
+    if (pos > out.bounds.back() && (tokens + L > max_batch_tokens || bytes + add > pool_bytes)) {
+      out.peak = std::max(out.peak, bytes);
+      out.bounds.push_back(pos);
+      tokens = 0;
+      bytes = 0;
+      anchors.clear();
+      add = a >= 0 ? slab[a] : 0;
+    }
+    tokens += L;
+    if (a >= 0 && !anchors.count(a)) {
+      anchors.insert(a);
+      bytes += add;
+    }
+  }
+  if (n_pairs > 0) {
+    out.peak = std::max(out.peak, bytes);
+    out.bounds.push_back(n_pairs);
+  }
+  return QUAIL_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// context
+// ---------------------------------------------------------------------------
+struct quail_ctx {
+  quail_model_config cfg;
+  quail_weights w;
+  std::vector<quail_layer_weights> layers;
+  uint8_t* pool = nullptr;
+  size_t pool_bytes = 0;
+  uint8_t* ws = nullptr;
+  size_t ws_bytes = 0;
+  int32_t T = 0;                      // max batch tokens
+  WsLayout L{};
+  bool rope_ready = false;
+
+  // residency
+  struct Slot {
+    bool live = false;
+    uint32_t gen = 0;
+    size_t off = 0, bytes = 0;
+    int32_t len = 0, lapad = 0;
+    int64_t uses = 0;
+  };
+  std::vector<Slot> slots;
+  std::vector<int32_t> free_slots;
+  std::vector<std::pair<size_t, size_t>> free_list;   // (offset, size), sorted by offset
+  size_t resident = 0, peak = 0;
+  int64_t prefills = 0, evictions = 0, regret = 0;
+  std::unordered_set<int64_t> seen_ids;
+
+  Blob blob;
+
+  bool alloc(size_t bytes, size_t& off) {
+    for (size_t i = 0; i < free_list.size(); ++i) {
+      if (free_list[i].second >= bytes) {
+        off = free_list[i].first;
+        free_list[i].first += bytes;
+        free_list[i].second -= bytes;
+        if (free_list[i].second == 0) free_list.erase(free_list.begin() + i);
+        return true;
+      }
+    }
+    return false;
+  }
+  void release(size_t off, size_t bytes) {
+    auto it = std::lower_bound(free_list.begin(), free_list.end(), std::make_pair(off, (size_t)0));
+    it = free_list.insert(it, {off, bytes});
+    size_t i = it - free_list.begin();
+    if (i + 1 < free_list.size() && free_list[i].first + free_list[i].second == free_list[i + 1].first) {
+      free_list[i].second += free_list[i + 1].second;
+      free_list.erase(free_list.begin() + i + 1);
+    }
+    if (i > 0 && free_list[i - 1].first + free_list[i - 1].second == free_list[i].first) {
+      free_list[i - 1].second += free_list[i].second;
+      free_list.erase(free_list.begin() + i);
+    }
+  }
+  Slot* lookup(quail_anchor h) {
+    if (h < 0) return nullptr;
+    const uint32_t slot = (uint32_t)(h & 0xFFFFFFFF);
+    const uint32_t gen = (uint32_t)((uint64_t)h >> 32);
+    if (slot >= slots.size()) return nullptr;
+    Slot& s = slots[slot];
+    if (!s.live || s.gen != gen) return nullptr;
+    return &s;
+  }
+  void evict(int32_t slot) {
+    Slot& s = slots[slot];
+    release(s.off, s.bytes);
+    resident -= s.bytes;
+    s.live = false;
+    s.gen++;
+    free_slots.push_back(slot);
+    evictions++;
+  }
+};
+
+namespace {
+
+template <typename T>
+T* ws_ptr(quail_ctx* c, size_t off) { return reinterpret_cast<T*>(c->ws + off); }
+
+quail_status ensure_rope(quail_ctx* c, hipStream_t s) {
+  if (c->rope_ready) return QUAIL_OK;
+  const int P = max_pos(c->cfg);
+  const int half = c->cfg.head_dim / 2;
+  std::vector<float2> tab((size_t)P * half);
+  for (int p = 0; p < P; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double inv = std::pow((double)c->cfg.rope_theta, -2.0 * i / c->cfg.head_dim);
+      const double ang = (double)p * inv;
+      tab[(size_t)p * half + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+    }
+  HIP_TRY(stager().copy(c->ws + c->L.rope, tab.data(), tab.size() * sizeof(float2), s));
+  c->rope_ready = true;
+  return QUAIL_OK;
+}
+
+// One batch of token rows through the decoder stack.
+struct Batch {
+  bool anchor_mode = false;
+  int32_t n_tok = 0;
+  std::vector<int32_t> tok_src, pos, seg_lo, kv_lapad;
+  std::vector<int64_t> kv_row;
+  std::vector<AttnTile> tiles;
+  std::vector<KVSrc> srcs;
+  std::vector<int64_t> src_layer_stride;   // per src, elements per layer
+  // outputs
+  std::vector<int32_t> last_row, last_dst;  // h_last: row -> destination row
+  std::vector<int32_t> all_dst;             // h_all: internal row -> caller token row
+};
+
+// The layer-stride of a KV source is folded in by patching the srcs per layer.
+quail_status run_batch(quail_ctx* c, const Batch& b, const int32_t* tokens, uint16_t* h_last,
+                       uint16_t* h_all, hipStream_t s) {
+  const quail_model_config& cf = c->cfg;
+  const int H = cf.hidden, Hq = cf.n_q_heads, Hkv = cf.n_kv_heads, I = cf.intermediate;
+  const int G = Hq / Hkv;
+  const int n = b.n_tok;
+  if (n == 0) return QUAIL_OK;
+
+  // metadata blob: per-layer src tables are laid out back to back
+  Blob& bl = c->blob;
+  bl.clear();
+  const size_t o_tok = bl.add(b.tok_src), o_pos = bl.add(b.pos), o_seg = bl.add(b.seg_lo);
+  const size_t o_lap = bl.add(b.kv_lapad), o_row = bl.add(b.kv_row), o_til = bl.add(b.tiles);
+  const size_t o_ldst = bl.add(b.last_row), o_ldd = bl.add(b.last_dst), o_all = bl.add(b.all_dst);
+  const int nl_attn = b.anchor_mode ? cf.n_layers - 1 : cf.n_layers;
+  std::vector<KVSrc> srcs_all;
+  srcs_all.reserve((size_t)std::max(nl_attn, 1) * b.srcs.size());
+  for (int l = 0; l < std::max(nl_attn, 1); ++l)
+    for (size_t i = 0; i < b.srcs.size(); ++i) {
+      KVSrc x = b.srcs[i];
+      const size_t esz = x.fp8 ? 1 : 2;
+      x.k = reinterpret_cast<const uint8_t*>(x.k) + (size_t)l * b.src_layer_stride[i] * esz;
+      x.v = reinterpret_cast<const uint8_t*>(x.v) + (size_t)l * b.src_layer_stride[i] * esz;
+      srcs_all.push_back(x);
+    }
+  const size_t o_src = bl.add(srcs_all);
+  if (bl.size() > c->L.meta_cap)
+    return fail(QUAIL_E_NOMEM, "batch metadata (%zu B) exceeds its workspace region", bl.size());
+  uint8_t* md = c->ws + c->L.meta;
+  HIP_TRY(stager().copy(md, bl.data(), bl.size(), s));
+
+  auto dp = [&](size_t off) { return md + off; };
+  const int32_t* d_tok = reinterpret_cast<const int32_t*>(dp(o_tok));
+  const int32_t* d_pos = reinterpret_cast<const int32_t*>(dp(o_pos));
+  const int32_t* d_seg = reinterpret_cast<const int32_t*>(dp(o_seg));
+  const int32_t* d_lap = reinterpret_cast<const int32_t*>(dp(o_lap));
+  const int64_t* d_row = reinterpret_cast<const int64_t*>(dp(o_row));
+  const AttnTile* d_til = reinterpret_cast<const AttnTile*>(dp(o_til));
+  const KVSrc* d_src = reinterpret_cast<const KVSrc*>(dp(o_src));
+
+  uint16_t* hbuf = ws_ptr<uint16_t>(c, c->L.h);
+  uint16_t* ubuf = ws_ptr<uint16_t>(c, c->L.u);
+  uint16_t* qbuf = ws_ptr<uint16_t>(c, c->L.q);
+  uint16_t* kbuf = ws_ptr<uint16_t>(c, c->L.k);
+  uint16_t* vbuf = ws_ptr<uint16_t>(c, c->L.v);
+  uint16_t* obuf = ws_ptr<uint16_t>(c, c->L.o);
+  uint16_t* mbuf = ws_ptr<uint16_t>(c, c->L.m);
+  const float2* rope = ws_ptr<const float2>(c, c->L.rope);
+
+  HIP_TRY(launch_embed(tokens, d_tok, c->w.embed, hbuf, n, H, s));
+  for (int l = 0; l < cf.n_layers; ++l) {
+    const quail_layer_weights& lw = c->layers[l];
+    NormParams np{};
+    np.x = hbuf; np.ldx = H; np.gamma = lw.attn_norm; np.y = ubuf; np.ldy = H;
+    np.rows = n; np.H = H; np.eps = cf.rms_eps;
+    HIP_TRY(launch_rmsnorm(np, s));
+
+    GemmParams gp{};
+    gp.A = ubuf; gp.lda = H; gp.B = lw.w_qkv; gp.scale = lw.s_qkv;
+    gp.M = n; gp.N = (Hq + 2 * Hkv) * kHeadDim; gp.K = H;
+    gp.hq = Hq; gp.hkv = Hkv; gp.rope = rope; gp.pos = d_pos; gp.q_out = qbuf;
+    gp.layer = l;
+    if (b.anchor_mode) {
+      gp.kv_mode = 1; gp.pool = c->pool; gp.kv_row = d_row; gp.kv_lapad = d_lap;
+      gp.kv_fp8 = cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3;
+      gp.k_inv_scale = 1.0f / cf.k_scale; gp.v_inv_scale = 1.0f / cf.v_scale;
+    } else {
+      gp.kv_mode = 0; gp.k_out = kbuf; gp.v_out = vbuf;
+    }
+    HIP_TRY(launch_gemm(gp, EPI_QKV, s));
+    if (b.anchor_mode && l == cf.n_layers - 1) break;   // last layer: K/V is all an anchor needs
+
+    AttnParams ap{};
+    ap.tiles = d_til; ap.n_tiles = (int32_t)b.tiles.size();
+    ap.srcs = d_src + (size_t)l * b.srcs.size();
+    ap.seg_lo = d_seg; ap.q = qbuf; ap.q_stride = (int64_t)Hq * kHeadDim;
+    ap.out = obuf; ap.o_stride = (int64_t)Hq * kHeadDim; ap.lse = nullptr;
+    ap.hq = Hq; ap.hkv = Hkv;
+    ap.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)kHeadDim));
+    ap.k_scale = cf.k_scale; ap.v_scale = cf.v_scale;
+    HIP_TRY(launch_attn_bf16(ap, G, s));
+
+    GemmParams go{};
+    go.A = obuf; go.lda = (int64_t)Hq * kHeadDim; go.B = lw.w_o; go.scale = lw.s_o;
+    go.M = n; go.N = H; go.K = Hq * kHeadDim; go.Y = hbuf; go.ldy = H;
+    HIP_TRY(launch_gemm(go, EPI_RESID, s));
+
+    np.gamma = lw.mlp_norm;
+    HIP_TRY(launch_rmsnorm(np, s));
+
+    GemmParams gg{};
+    gg.A = ubuf; gg.lda = H; gg.B = lw.w_gate_up; gg.scale = lw.s_gate_up;
+    gg.M = n; gg.N = I; gg.K = H; gg.Y = mbuf; gg.ldy = I; gg.inter = I;
+    HIP_TRY(launch_gemm(gg, EPI_SWIGLU, s));
+
+    GemmParams gd{};
+    gd.A = mbuf; gd.lda = I; gd.B = lw.w_down; gd.scale = lw.s_down;
+    gd.M = n; gd.N = H; gd.K = I; gd.Y = hbuf; gd.ldy = H;
+    HIP_TRY(launch_gemm(gd, EPI_RESID, s));
+  }
+  if (!b.anchor_mode) {
+    if (h_last && !b.last_row.empty()) {
+      // h_last[last_dst[i]] = h[last_row[i]]
+      HIP_TRY(launch_copy_rows(hbuf, H, reinterpret_cast<const int32_t*>(dp(o_ldst)), h_last, H,
+                               reinterpret_cast<const int32_t*>(dp(o_ldd)),
+                               (int32_t)b.last_row.size(), H, s));
+    }
+    if (h_all) {
+      HIP_TRY(launch_copy_rows(hbuf, H, nullptr, h_all, H,
+                               reinterpret_cast<const int32_t*>(dp(o_all)), n, H, s));
+    }
+  }
+  return QUAIL_OK;
+}
+
+quail_status check_offsets(int32_t n, const int32_t* off, int32_t lo, int32_t hi, const char* what) {
+  if (n < 0) return fail(QUAIL_E_INVAL, "%s: negative count", what);
+  if (n > 0 && !off) return fail(QUAIL_E_INVAL, "%s: offsets are NULL", what);
+  if (n > 0 && off[0] < 0) return fail(QUAIL_E_INVAL, "%s: offsets[0] < 0", what);
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t len = (int64_t)off[i + 1] - off[i];
+    if (len < lo || len > hi)
+      return fail(QUAIL_E_INVAL, "%s %d: length %lld outside [%d, %d]", what, i, (long long)len, lo, hi);
+  }
+  return QUAIL_OK;
+}
+
+hipStream_t as_stream(quail_stream s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Anchor prefill core: anchor a = tokens[starts[a] .. starts[a] + lens[a]).
+quail_status anchor_core(quail_ctx* c, int32_t n, const int32_t* tokens, const int32_t* starts,
+                         const int32_t* lens, const int32_t* n_uses, const int64_t* anchor_ids,
+                         quail_anchor* out, hipStream_t s) {
+  if (!n_uses || !out) return fail(QUAIL_E_INVAL, "n_uses and out are required");
+  if (!tokens) return fail(QUAIL_E_INVAL, "tokens is NULL");
+  for (int32_t a = 0; a < n; ++a)
+    if (n_uses[a] < 0) return fail(QUAIL_E_INVAL, "anchor %d: negative use count", a);
+  // carve all slabs first (all or nothing)
+  std::vector<std::pair<size_t, size_t>> got;
+  std::vector<int32_t> slot_of(n, -1);
+  for (int32_t a = 0; a < n; ++a) {
+    if (n_uses[a] == 0) continue;
+    const size_t bytes = slab_bytes(c->cfg, lens[a]);
+    size_t off;
+    if (!c->alloc(bytes, off)) {
+      for (auto& g : got) c->release(g.first, g.second);
+      return fail(QUAIL_E_NOMEM, "KV pool cannot hold the %d new anchor slabs", n);
+    }
+    got.push_back({off, bytes});
+  }
+  size_t gi = 0;
+  for (int32_t a = 0; a < n; ++a) {
+    if (n_uses[a] == 0) { out[a] = QUAIL_NO_ANCHOR; continue; }
+    int32_t slot;
+    if (!c->free_slots.empty()) { slot = c->free_slots.back(); c->free_slots.pop_back(); }
+    else { slot = (int32_t)c->slots.size(); c->slots.emplace_back(); }
+    quail_ctx::Slot& sl = c->slots[slot];
+    sl.live = true;
+    sl.off = got[gi].first;
+    sl.bytes = got[gi].second;
+    ++gi;
+    sl.len = lens[a];
+    sl.lapad = pad_len(sl.len);
+    sl.uses = n_uses[a];
+    slot_of[a] = slot;
+    out[a] = ((int64_t)sl.gen << 32) | (uint32_t)slot;
+    c->resident += sl.bytes;
+    c->prefills++;
+    if (anchor_ids) {
+      if (c->seen_ids.count(anchor_ids[a])) c->regret += sl.len;
+      else c->seen_ids.insert(anchor_ids[a]);
+    }
+  }
+  c->peak = std::max(c->peak, c->resident);
+
+  if (quail_status st = ensure_rope(c, s)) return st;
+  const quail_model_config& cf = c->cfg;
+  const int G = cf.n_q_heads / cf.n_kv_heads;
+  const int TQ = group_tokens(G);
+  const size_t esz = kv_elem_bytes(cf);
+  // batches of whole anchors up to T tokens
+  int32_t a0 = 0;
+  while (a0 < n) {
+    Batch b;
+    b.anchor_mode = true;
+    int32_t a1 = a0;
+    int32_t tok = 0;
+    while (a1 < n && (n_uses[a1] == 0 || tok + lens[a1] <= c->T)) {
+      if (n_uses[a1] > 0) tok += lens[a1];
+      ++a1;
+    }
+    for (int32_t a = a0; a < a1; ++a) {
+      if (n_uses[a] == 0) continue;
+      const quail_ctx::Slot& sl = c->slots[slot_of[a]];
+      const int32_t r0 = b.n_tok;
+      const int32_t src = (int32_t)b.srcs.size();
+      KVSrc ks{};
+      ks.k = c->pool + sl.off;
+      ks.v = c->pool + sl.off + (size_t)cf.n_kv_heads * sl.lapad * kHeadDim * esz;
+      ks.tok_stride = kHeadDim;
+      ks.head_stride = (int64_t)sl.lapad * kHeadDim;
+      ks.len = sl.len;
+      ks.fp8 = cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3;
+      b.srcs.push_back(ks);
+      b.src_layer_stride.push_back((int64_t)2 * cf.n_kv_heads * sl.lapad * kHeadDim);
+      for (int32_t t = 0; t < sl.len; ++t) {
+        b.tok_src.push_back(starts[a] + t);
+        b.pos.push_back(t);
+        b.seg_lo.push_back(0);
+        b.kv_row.push_back((int64_t)(sl.off / esz) + (int64_t)t * kHeadDim);
+        b.kv_lapad.push_back(sl.lapad);
+      }
+      for (int32_t t0 = 0; t0 < sl.len; t0 += TQ) {
+        AttnTile tl{};
+        tl.q0 = r0 + t0;
+        tl.nq = std::min(TQ, sl.len - t0);
+        tl.cross = -1;
+        tl.self = src;
+        tl.self_qbase = t0;
+        tl.self_k0 = 0;
+        b.tiles.push_back(tl);
+      }
+      b.n_tok += sl.len;
+    }
+    if (quail_status st = run_batch(c, b, tokens, nullptr, nullptr, s)) return st;
+    a0 = a1;
+  }
+  return QUAIL_OK;
+}
+
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+const char* quail_version(void) { return "quail-mi355x 0.1 (gfx950)"; }
+
+const char* quail_last_error(void) { return g_err.c_str(); }
+
+quail_status quail_anchor_bytes(const quail_model_config* cfg, int32_t anchor_len, size_t* out) {
+  if (quail_status st = check_cfg(cfg)) return st;
+  if (!out || anchor_len < 1) return fail(QUAIL_E_INVAL, "anchor_len >= 1 and out required");
+  *out = slab_bytes(*cfg, anchor_len);
+  return QUAIL_OK;
+}
+
+quail_status quail_workspace_bytes(const quail_model_config* cfg, int32_t max_batch_tokens,
+                                   size_t* out) {
+  if (quail_status st = check_cfg(cfg)) return st;
+  if (!out || max_batch_tokens < 1) return fail(QUAIL_E_INVAL, "max_batch_tokens >= 1 and out required");
+  *out = ws_layout(*cfg, max_batch_tokens).total;
+  return QUAIL_OK;
+}
+
+quail_status quail_plan_build(const quail_model_config* cfg, size_t pool_bytes, int32_t max_batch_tokens,
+                              int32_t n_anchors, const int32_t* anchor_len, int32_t n_pairs,
+                              const int32_t* pair_anchor, const int32_t* pair_len, int32_t* pair_order,
+                              int32_t* step_bounds, int32_t* n_steps, size_t* peak_bytes) {
+  if (quail_status st = check_cfg(cfg)) return st;
+  if (n_anchors < 0 || n_pairs < 0 || max_batch_tokens < 1)
+    return fail(QUAIL_E_INVAL, "negative count or max_batch_tokens < 1");
+  if ((n_anchors > 0 && !anchor_len) || (n_pairs > 0 && (!pair_anchor || !pair_len || !pair_order)) ||
+      !step_bounds || !n_steps)
+    return fail(QUAIL_E_INVAL, "NULL array");
+  std::vector<size_t> slab(n_anchors);
+  for (int32_t a = 0; a < n_anchors; ++a) {
+    if (anchor_len[a] < 1) return fail(QUAIL_E_INVAL, "anchor %d: length %d < 1", a, anchor_len[a]);
+    slab[a] = slab_bytes(*cfg, anchor_len[a]);
+  }
+  Plan p;
+  if (quail_status st = build_plan(slab, n_pairs, pair_anchor, pair_len, pool_bytes, max_batch_tokens, p))
+    return st;
+  std::copy(p.order.begin(), p.order.end(), pair_order);
+  std::copy(p.bounds.begin(), p.bounds.end(), step_bounds);
+  *n_steps = (int32_t)p.bounds.size() - 1;
+  if (peak_bytes) *peak_bytes = p.peak;
+  return QUAIL_OK;
+}
+
+quail_status quail_ctx_create(const quail_model_config* cfg, const quail_weights* w, void* kv_pool,
+                              size_t pool_bytes, void* workspace, size_t ws_bytes,
+                              int32_t max_batch_tokens, quail_ctx** out) {
+  if (quail_status st = check_cfg(cfg)) return st;
+  if (!w || !out) return fail(QUAIL_E_INVAL, "weights and out are required");
+  if (max_batch_tokens < 1) return fail(QUAIL_E_INVAL, "max_batch_tokens must be >= 1");
+  if (!w->embed || !w->layers || !w->head8) return fail(QUAIL_E_INVAL, "weights incomplete");
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const quail_layer_weights& x = w->layers[l];
+    if (!x.attn_norm || !x.mlp_norm || !x.w_qkv || !x.w_o || !x.w_gate_up || !x.w_down || !x.s_qkv ||
+        !x.s_o || !x.s_gate_up || !x.s_down)
+      return fail(QUAIL_E_INVAL, "layer %d weights incomplete", l);
+  }
+  if (pool_bytes > 0 && (!kv_pool || reinterpret_cast<uintptr_t>(kv_pool) % kAlign))
+    return fail(QUAIL_E_INVAL, "kv_pool must be non-NULL and 256-B aligned");
+  WsLayout L = ws_layout(*cfg, max_batch_tokens);
+  if (!workspace || ws_bytes < L.total)
+    return fail(QUAIL_E_NOMEM, "workspace of %zu B < %zu B needed", ws_bytes, L.total);
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(QUAIL_E_INVAL, "workspace must be 256-B aligned");
+  quail_ctx* c = new quail_ctx();
+  c->cfg = *cfg;
+  c->w = *w;
+  c->layers.assign(w->layers, w->layers + cfg->n_layers);
+  c->w.layers = c->layers.data();
+  c->pool = static_cast<uint8_t*>(kv_pool);
+  c->pool_bytes = pool_bytes / kAlign * kAlign;
+  c->ws = static_cast<uint8_t*>(workspace);
+  c->ws_bytes = ws_bytes;
+  c->T = max_batch_tokens;
+  c->L = L;
+  if (c->pool_bytes) c->free_list.push_back({0, c->pool_bytes});
+  *out = c;
+  return QUAIL_OK;
+}
+
+quail_status quail_ctx_destroy(quail_ctx* ctx) {
+  delete ctx;
+  return QUAIL_OK;
+}
+
+quail_status quail_pool_stats(const quail_ctx* c, size_t* resident, size_t* peak, int64_t* prefills,
+                              int64_t* evictions, int64_t* regret_tokens) {
+  if (!c) return fail(QUAIL_E_INVAL, "ctx is NULL");
+  if (resident) *resident = c->resident;
+  if (peak) *peak = c->peak;
+  if (prefills) *prefills = c->prefills;
+  if (evictions) *evictions = c->evictions;
+  if (regret_tokens) *regret_tokens = c->regret;
+  return QUAIL_OK;
+}
+
+quail_status quail_anchor_release(quail_ctx* c, quail_anchor h) {
+  if (!c) return fail(QUAIL_E_INVAL, "ctx is NULL");
+  quail_ctx::Slot* s = c->lookup(h);
+  if (!s) return fail(QUAIL_E_STALE, "anchor handle %lld is stale", (long long)h);
+  c->evict((int32_t)(h & 0xFFFFFFFF));
+  return QUAIL_OK;
+}
+
+quail_status quail_anchor_kv(const quail_ctx* cc, quail_anchor h, int32_t layer, void** k, void** v,
+                             int32_t* anchor_len, int32_t* padded_len) {
+  quail_ctx* c = const_cast<quail_ctx*>(cc);
+  if (!c) return fail(QUAIL_E_INVAL, "ctx is NULL");
+  quail_ctx::Slot* s = c->lookup(h);
+  if (!s) return fail(QUAIL_E_STALE, "anchor handle %lld is stale", (long long)h);
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(QUAIL_E_INVAL, "layer %d out of range", layer);
+  const size_t esz = kv_elem_bytes(c->cfg);
+  const size_t per = (size_t)c->cfg.n_kv_heads * s->lapad * c->cfg.head_dim * esz;
+  uint8_t* base = c->pool + s->off + (size_t)layer * 2 * per;
+  if (k) *k = base;
+  if (v) *v = base + per;
+  if (anchor_len) *anchor_len = s->len;
+  if (padded_len) *padded_len = s->lapad;
+  return QUAIL_OK;
+}
+
+quail_status quail_anchor_prefill(quail_ctx* c, int32_t n, const int32_t* tokens, const int32_t* offsets,
+                                  const int32_t* n_uses, const int64_t* anchor_ids, quail_anchor* out,
+                                  quail_stream stream) {
+  if (!c) return fail(QUAIL_E_INVAL, "ctx is NULL");
+  if (n == 0) return QUAIL_OK;
+  const int32_t maxlen = std::min(c->cfg.max_anchor_len, c->T);
+  if (quail_status st = check_offsets(n, offsets, 1, maxlen, "anchor")) return st;
+  std::vector<int32_t> starts(offsets, offsets + n), lens(n);
+  for (int32_t a = 0; a < n; ++a) lens[a] = offsets[a + 1] - offsets[a];
+  return anchor_core(c, n, tokens, starts.data(), lens.data(), n_uses, anchor_ids, out,
+                     as_stream(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Join prefill core: pair i = tokens[starts[i] .. starts[i] + lens[i]) after
+// anchor ha[i]; its last hidden row goes to h_last row dst_row[i] (i if NULL);
+// with h_all, row (starts[i] + t) of h_all receives position t. Pairs are
+// grouped by anchor internally (stable).
+quail_status join_core(quail_ctx* c, int32_t n, const quail_anchor* ha, const int32_t* tokens,
+                       const int32_t* starts, const int32_t* lens, uint16_t* h_last,
+                       const int32_t* dst_row, uint16_t* h_all, hipStream_t s) {
+  const quail_model_config& cf = c->cfg;
+  if (!ha || !tokens) return fail(QUAIL_E_INVAL, "pair_anchor and tokens are required");
+  // validate handles and use counts
+  std::unordered_map<int32_t, int64_t> need;
+  std::vector<int32_t> slot(n, -1);
+  for (int32_t i = 0; i < n; ++i) {
+    if (ha[i] == QUAIL_NO_ANCHOR) continue;
+    quail_ctx::Slot* sl = c->lookup(ha[i]);
+    if (!sl) return fail(QUAIL_E_STALE, "pair %d: anchor handle %lld is stale", i, (long long)ha[i]);
+    slot[i] = (int32_t)(ha[i] & 0xFFFFFFFF);
+    if (++need[slot[i]] > sl->uses)
+      return fail(QUAIL_E_STALE, "pair %d: anchor used more often than its declared %lld uses", i,
+                  (long long)sl->uses);
+    if (sl->len + lens[i] > max_pos(cf))
+      return fail(QUAIL_E_INVAL, "pair %d: anchor + suffix exceeds the position range", i);
+  }
+  if (quail_status st = ensure_rope(c, s)) return st;
+  std::vector<int32_t> order(n);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+    const int64_t kx = slot[x] < 0 ? INT64_MAX : slot[x], ky = slot[y] < 0 ? INT64_MAX : slot[y];
+    return kx < ky;
+  });
+  const int G = cf.n_q_heads / cf.n_kv_heads;
+  const int TQ = group_tokens(G);
+  const size_t esz = kv_elem_bytes(cf);
+  int32_t p0 = 0;
+  while (p0 < n) {
+    Batch b;
+    b.anchor_mode = false;
+    int32_t p1 = p0, tok = 0;
+    while (p1 < n && tok + lens[order[p1]] <= c->T) {
+      tok += lens[order[p1]];
+      ++p1;
+    }
+    // source 0: this batch's suffix K/V (token-major, reused every layer)
+    KVSrc self{};
+    self.k = ws_ptr<uint16_t>(c, c->L.k);
+    self.v = ws_ptr<uint16_t>(c, c->L.v);
+    self.tok_stride = (int64_t)cf.n_kv_heads * kHeadDim;
+    self.head_stride = kHeadDim;
+    self.len = tok;
+    self.fp8 = 0;
+    b.srcs.push_back(self);
+    b.src_layer_stride.push_back(0);
+    std::unordered_map<int32_t, int32_t> src_of_slot;
+    int32_t i = p0;
+    while (i < p1) {
+      // a run of pairs with the same anchor
+      int32_t j = i;
+      while (j < p1 && slot[order[j]] == slot[order[i]]) ++j;
+      int32_t cross = -1, la = 0;
+      if (slot[order[i]] >= 0) {
+        const quail_ctx::Slot& sl = c->slots[slot[order[i]]];
+        la = sl.len;
+        auto it = src_of_slot.find(slot[order[i]]);
+        if (it == src_of_slot.end()) {
+          KVSrc ks{};
+          ks.k = c->pool + sl.off;
+          ks.v = c->pool + sl.off + (size_t)cf.n_kv_heads * sl.lapad * kHeadDim * esz;
+          ks.tok_stride = kHeadDim;
+          ks.head_stride = (int64_t)sl.lapad * kHeadDim;
+          ks.len = sl.len;
+          ks.fp8 = cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3;
+          cross = (int32_t)b.srcs.size();
+          b.srcs.push_back(ks);
+          b.src_layer_stride.push_back((int64_t)2 * cf.n_kv_heads * sl.lapad * kHeadDim);
+          src_of_slot[slot[order[i]]] = cross;
+        } else {
+          cross = it->second;
+        }
+      }
+      const int32_t g0 = b.n_tok;
+      for (int32_t k = i; k < j; ++k) {
+        const int32_t pi = order[k];
+        const int32_t len = lens[pi];
+        const int32_t r0 = b.n_tok;
+        for (int32_t t = 0; t < len; ++t) {
+          b.tok_src.push_back(starts[pi] + t);
+          b.pos.push_back(la + t);
+          b.seg_lo.push_back(r0);
+          b.all_dst.push_back(starts[pi] + t);
+        }
+        b.last_row.push_back(r0 + len - 1);
+        b.last_dst.push_back(dst_row ? dst_row[pi] : pi);
+        b.n_tok += len;
+      }
+      for (int32_t t0 = g0; t0 < b.n_tok; t0 += TQ) {
+        AttnTile tl{};
+        tl.q0 = t0;
+        tl.nq = std::min(TQ, b.n_tok - t0);
+        tl.cross = cross;
+        tl.self = 0;
+        tl.self_qbase = t0;
+        tl.self_k0 = b.seg_lo[t0];
+        b.tiles.push_back(tl);
+      }
+      i = j;
+    }
+    if (quail_status st = run_batch(c, b, tokens, h_last, h_all, s)) return st;
+    p0 = p1;
+  }
+  // spend uses; evict anchors at their last use (stream-ordered reuse)
+  for (auto& kv : need) {
+    quail_ctx::Slot& sl = c->slots[kv.first];
+    sl.uses -= kv.second;
+    if (sl.uses == 0) c->evict(kv.first);
+  }
+  return QUAIL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+quail_status quail_join_prefill(quail_ctx* c, int32_t n, const quail_anchor* pair_anchor,
+                                const int32_t* tokens, const int32_t* offsets, uint16_t* h_last,
+                                uint16_t* h_all, quail_stream stream) {
+  if (!c) return fail(QUAIL_E_INVAL, "ctx is NULL");
+  if (n == 0) return QUAIL_OK;
+  if (!h_last) return fail(QUAIL_E_INVAL, "h_last is required");
+  const int32_t maxlen = std::min(c->cfg.max_suffix_len, c->T);
+  if (quail_status st = check_offsets(n, offsets, 1, maxlen, "pair")) return st;
+  std::vector<int32_t> starts(offsets, offsets + n), lens(n);
+  for (int32_t i = 0; i < n; ++i) lens[i] = offsets[i + 1] - offsets[i];
+  return join_core(c, n, pair_anchor, tokens, starts.data(), lens.data(), h_last, nullptr, h_all,
+                   as_stream(stream));
+}
+
+quail_status quail_head8(quail_ctx* c, int32_t n, const uint16_t* h_last, uint8_t true_mask,
+                         float* logits, uint8_t* token, uint8_t* decision, quail_stream stream) {
+  if (!c) return fail(QUAIL_E_INVAL, "ctx is NULL");
+  if (n < 0) return fail(QUAIL_E_INVAL, "negative n");
+  if (n == 0) return QUAIL_OK;
+  if (!h_last || !decision) return fail(QUAIL_E_INVAL, "h_last and decision are required");
+  Head8Params p{};
+  p.h = h_last; p.ldh = c->cfg.hidden; p.gamma = c->w.final_norm; p.w8 = c->w.head8;
+  p.logits = logits; p.token = token; p.decision = decision;
+  p.rows = n; p.H = c->cfg.hidden; p.eps = c->cfg.rms_eps; p.true_mask = true_mask;
+  HIP_TRY(launch_head8(p, as_stream(stream)));
+  return QUAIL_OK;
+}
+
+quail_status quail_head8_f32(int32_t n, int32_t hidden, const float* x, const float* w8,
+                             uint8_t true_mask, float* logits, uint8_t* token, uint8_t* decision,
+                             quail_stream stream) {
+  if (n < 0 || hidden <= 0) return fail(QUAIL_E_INVAL, "n >= 0 and hidden > 0 required");
+  if (n == 0) return QUAIL_OK;
+  if (!x || !w8 || !decision) return fail(QUAIL_E_INVAL, "x, w8 and decision are required");
+  HIP_TRY(launch_head8_f32(n, hidden, x, w8, true_mask, logits, token, decision, as_stream(stream)));
+  return QUAIL_OK;
+}
+
+quail_status quail_join_run(quail_ctx* c, int32_t n_anchors, const int32_t* a_tokens,
+                            const int32_t* a_offsets, int32_t n_pairs, const int32_t* pair_anchor,
+                            const int32_t* s_tokens, const int32_t* s_offsets, uint8_t true_mask,
+                            float* logits, uint8_t* token, uint8_t* decision, quail_stream stream) {
+  if (!c) return fail(QUAIL_E_INVAL, "ctx is NULL");
+  if (n_pairs == 0) return QUAIL_OK;
+  if (!decision) return fail(QUAIL_E_INVAL, "decision is required");
+  const int32_t amax = std::min(c->cfg.max_anchor_len, c->T);
+  if (quail_status st = check_offsets(n_anchors, a_offsets, 1, amax, "anchor")) return st;
+  if (quail_status st = check_offsets(n_pairs, s_offsets, 1, std::min(c->cfg.max_suffix_len, c->T), "pair"))
+    return st;
+  if (!pair_anchor) return fail(QUAIL_E_INVAL, "pair_anchor is NULL");
+  std::vector<size_t> slab(n_anchors);
+  std::vector<int32_t> alen(n_anchors), plen(n_pairs);
+  for (int32_t a = 0; a < n_anchors; ++a) {
+    alen[a] = a_offsets[a + 1] - a_offsets[a];
+    slab[a] = slab_bytes(c->cfg, alen[a]);
+  }
+  for (int32_t i = 0; i < n_pairs; ++i) plen[i] = s_offsets[i + 1] - s_offsets[i];
+  // the plan is built against the largest free block of the pool now
+  size_t free_bytes = 0;
+  for (auto& f : c->free_list) free_bytes = std::max(free_bytes, f.second);
+  Plan plan;
+  if (quail_status st = build_plan(slab, n_pairs, pair_anchor, plen.data(), free_bytes, c->T, plan))
+    return st;
+  std::vector<int32_t> uses(n_anchors, 0);
+  for (int32_t i = 0; i < n_pairs; ++i)
+    if (pair_anchor[i] >= 0) uses[pair_anchor[i]]++;
+  // anchors in order of first use along the plan
+  std::vector<int32_t> first_use;
+  {
+    std::vector<char> seen(n_anchors, 0);
+    for (int32_t k = 0; k < n_pairs; ++k) {
+      const int32_t a = pair_anchor[plan.order[k]];
+      if (a >= 0 && !seen[a]) { seen[a] = 1; first_use.push_back(a); }
+    }
+  }
+  std::vector<quail_anchor> handle(n_anchors, QUAIL_NO_ANCHOR);
+  size_t next_fresh = 0;                      // next anchor (in first-use order) to prefill
+  hipStream_t s = as_stream(stream);
+  uint16_t* hl = ws_ptr<uint16_t>(c, c->L.hlast);
+  for (size_t st = 0; st + 1 < plan.bounds.size(); ++st) {
+    const int32_t b0 = plan.bounds[st], b1 = plan.bounds[st + 1];
+    // Prefill the anchors this step needs; batch later steps' anchors with
+    // them (up to one batch of tokens and half the free pool) so anchor
+    // prefill runs as few, large launches.
+    bool need = false;
+    for (int32_t k = b0; k < b1 && !need; ++k) {
+      const int32_t a = pair_anchor[plan.order[k]];
+      need = a >= 0 && handle[a] == QUAIL_NO_ANCHOR;
+    }
+    if (need) {
+      size_t fb = 0;
+      for (auto& f : c->free_list) fb = std::max(fb, f.second);
+      std::vector<int32_t> batch, st_, ln, nu;
+      std::vector<int64_t> ids;
+      int64_t tok = 0;
+      size_t bytes = 0;
+      // every anchor of this step is taken; later ones while they fit
+      std::vector<char> in_step(n_anchors, 0);
+      for (int32_t k = b0; k < b1; ++k)
+        if (pair_anchor[plan.order[k]] >= 0) in_step[pair_anchor[plan.order[k]]] = 1;
+      while (next_fresh < first_use.size()) {
+        const int32_t a = first_use[next_fresh];
+        const bool must = in_step[a];
+        if (!must && (tok + alen[a] > c->T || bytes + slab[a] > fb / 2)) break;
+        batch.push_back(a);
+        st_.push_back(a_offsets[a]);
+        ln.push_back(alen[a]);
+        nu.push_back(uses[a]);
+        ids.push_back(a);
+        tok += alen[a];
+        bytes += slab[a];
+        ++next_fresh;
+      }
+      std::vector<quail_anchor> hnd(batch.size());
+      if (quail_status r = anchor_core(c, (int32_t)batch.size(), a_tokens, st_.data(), ln.data(), nu.data(),
+                                       ids.data(), hnd.data(), s))
+        return r;
+      for (size_t f = 0; f < batch.size(); ++f) handle[batch[f]] = hnd[f];
+    }
+    const int32_t np = b1 - b0;
+    std::vector<quail_anchor> ha(np);
+    std::vector<int32_t> starts(np), lens(np), dst(np), outmap(np);
+    for (int32_t k = 0; k < np; ++k) {
+      const int32_t pi = plan.order[b0 + k];
+      ha[k] = pair_anchor[pi] >= 0 ? handle[pair_anchor[pi]] : QUAIL_NO_ANCHOR;
+      starts[k] = s_offsets[pi];
+      lens[k] = plen[pi];
+      dst[k] = k;
+      outmap[k] = pi;
+    }
+    if (quail_status r = join_core(c, np, ha.data(), s_tokens, starts.data(), lens.data(), hl, dst.data(),
+                                   nullptr, s))
+      return r;
+    // head on this step's last rows, written to the caller's pair slots (the
+    // map goes to the metadata region; stream order protects earlier readers)
+    Blob& bl = c->blob;
+    bl.clear();
+    bl.add(outmap);
+    uint8_t* md = c->ws + c->L.meta;
+    HIP_TRY(stager().copy(md, bl.data(), bl.size(), s));
+    Head8Params p{};
+    p.h = hl; p.ldh = c->cfg.hidden; p.gamma = c->w.final_norm; p.w8 = c->w.head8;
+    p.out_map = reinterpret_cast<const int32_t*>(md);
+    p.logits = logits; p.token = token; p.decision = decision;
+    p.rows = np; p.H = c->cfg.hidden; p.eps = c->cfg.rms_eps; p.true_mask = true_mask;
+    HIP_TRY(launch_head8(p, s));
+  }
+  return QUAIL_OK;
+}
+
+// ---- cascade attention on given Q/K/V ---------------------------------------
+quail_status quail_cascade_workspace_bytes(int32_t n_anchors, const int32_t* a_off, int32_t n_suffix,
+                                           const int32_t* s_off, size_t* out) {
+  if (n_anchors < 0 || n_suffix < 0 || !out) return fail(QUAIL_E_INVAL, "bad arguments");
+  if (n_suffix > 0 && !s_off) return fail(QUAIL_E_INVAL, "s_off is NULL");
+  if (n_anchors > 0 && !a_off) return fail(QUAIL_E_INVAL, "a_off is NULL");
+  const int64_t T = n_suffix > 0 ? s_off[n_suffix] : 0;
+  // seg_lo + tok_anchor (int32 per token), a_off copy, tiles (<= T + n_suffix),
+  // srcs (n_anchors + 1)
+  *out = align_up((size_t)T * 4) * 2 + align_up((size_t)(n_anchors + 1) * 4) +
+         align_up((size_t)(T + n_suffix + 1) * sizeof(AttnTile)) +
+         align_up((size_t)(n_anchors + 1) * sizeof(KVSrc)) + 8 * kAlign;
+  return QUAIL_OK;
+}
+
+quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t d, float sm_scale,
+                                int32_t n_anchors, const void* ak, const void* av, const int32_t* a_off,
+                                int32_t n_suffix, const int32_t* s_anchor, const void* q, const void* k,
+                                const void* v, const int32_t* s_off, void* out, float* lse,
+                                void* workspace, size_t ws_bytes, quail_stream stream) {
+  if (dtype != QUAIL_DTYPE_F32 && dtype != QUAIL_DTYPE_BF16)
+    return fail(QUAIL_E_UNSUPPORTED, "dtype must be F32 or BF16");
+  if (hq <= 0 || hkv <= 0 || hq % hkv) return fail(QUAIL_E_INVAL, "hq must be a positive multiple of hkv");
+  const int G = hq / hkv;
+  if (dtype == QUAIL_DTYPE_BF16 && (d != kHeadDim || !valid_group(G)))
+    return fail(QUAIL_E_UNSUPPORTED, "bf16 path: head_dim 128 and GQA group 1, 2, 4 or 8");
+  if (dtype == QUAIL_DTYPE_F32 && d != 64 && d != 128)
+    return fail(QUAIL_E_UNSUPPORTED, "fp32 path: head_dim 64 or 128");
+  if (!(sm_scale > 0.0f)) return fail(QUAIL_E_INVAL, "sm_scale must be positive");
+  if (n_suffix < 0 || n_anchors < 0) return fail(QUAIL_E_INVAL, "negative count");
+  if (n_suffix == 0) return QUAIL_OK;
+  if (quail_status st = check_offsets(n_suffix, s_off, 1, INT32_MAX, "suffix")) return st;
+  if (n_anchors > 0)
+    if (quail_status st = check_offsets(n_anchors, a_off, 1, INT32_MAX, "anchor")) return st;
+  if (!s_anchor || !q || !k || !v || !out) return fail(QUAIL_E_INVAL, "NULL argument");
+  for (int32_t s = 0; s < n_suffix; ++s)
+    if (s_anchor[s] < -1 || s_anchor[s] >= n_anchors)
+      return fail(QUAIL_E_INVAL, "suffix %d: anchor %d out of range", s, s_anchor[s]);
+  if (n_anchors > 0 && (!ak || !av)) return fail(QUAIL_E_INVAL, "anchor K/V are NULL");
+  size_t need = 0;
+  quail_cascade_workspace_bytes(n_anchors, a_off, n_suffix, s_off, &need);
+  if (!workspace || ws_bytes < need) return fail(QUAIL_E_NOMEM, "workspace %zu B < %zu B", ws_bytes, need);
+
+  const int32_t T = s_off[n_suffix];
+  hipStream_t st = as_stream(stream);
+  std::vector<int32_t> seg(T), tok_anchor(T);
+  for (int32_t s = 0; s < n_suffix; ++s)
+    for (int32_t t = s_off[s]; t < s_off[s + 1]; ++t) { seg[t] = s_off[s]; tok_anchor[t] = s_anchor[s]; }
+  Blob bl;
+  const size_t o_seg = bl.add(seg);
+  if (dtype == QUAIL_DTYPE_F32) {
+    const size_t o_ta = bl.add(tok_anchor);
+    std::vector<int32_t> ao(a_off, a_off + (n_anchors > 0 ? n_anchors + 1 : 0));
+    if (ao.empty()) ao.push_back(0);
+    const size_t o_ao = bl.add(ao);
+    uint8_t* md = static_cast<uint8_t*>(workspace);
+    HIP_TRY(stager().copy(md, bl.data(), bl.size(), st));
+    AttnF32Params p{};
+    p.ak = static_cast<const float*>(ak); p.av = static_cast<const float*>(av);
+    p.a_off = reinterpret_cast<const int32_t*>(md + o_ao);
+    p.q = static_cast<const float*>(q); p.k = static_cast<const float*>(k); p.v = static_cast<const float*>(v);
+    p.tok_anchor = reinterpret_cast<const int32_t*>(md + o_ta);
+    p.tok_seg = reinterpret_cast<const int32_t*>(md + o_seg);
+    p.out = static_cast<float*>(out); p.lse = lse;
+    p.n_tok = T; p.hq = hq; p.hkv = hkv; p.d = d; p.scale = sm_scale;
+    HIP_TRY(launch_attn_f32(p, st));
+    return QUAIL_OK;
+  }
+  const int TQ = group_tokens(G);
+  std::vector<KVSrc> srcs;
+  KVSrc self{};
+  self.k = k; self.v = v; self.tok_stride = (int64_t)hkv * d; self.head_stride = d; self.len = T; self.fp8 = 0;
+  srcs.push_back(self);
+  for (int32_t a = 0; a < n_anchors; ++a) {
+    KVSrc x{};
+    x.k = static_cast<const uint16_t*>(ak) + (int64_t)a_off[a] * hkv * d;
+    x.v = static_cast<const uint16_t*>(av) + (int64_t)a_off[a] * hkv * d;
+    x.tok_stride = (int64_t)hkv * d; x.head_stride = d; x.len = a_off[a + 1] - a_off[a]; x.fp8 = 0;
+    srcs.push_back(x);
+  }
+  std::vector<AttnTile> tiles;
+  int32_t s0 = 0;
+  while (s0 < n_suffix) {
+    int32_t s1 = s0 + 1;
+    while (s1 < n_suffix && s_anchor[s1] == s_anchor[s0]) ++s1;
+    const int32_t t_end = s_off[s1];
+    for (int32_t t0 = s_off[s0]; t0 < t_end; t0 += TQ) {
+      AttnTile tl{};
+      tl.q0 = t0; tl.nq = std::min(TQ, t_end - t0);
+      tl.cross = s_anchor[s0] >= 0 ? 1 + s_anchor[s0] : -1;
+      tl.self = 0; tl.self_qbase = t0; tl.self_k0 = seg[t0];
+      tiles.push_back(tl);
+    }
+    s0 = s1;
+  }
+  const size_t o_til = bl.add(tiles);
+  const size_t o_src = bl.add(srcs);
+  if (bl.size() > ws_bytes) return fail(QUAIL_E_NOMEM, "workspace too small for tiles");
+  uint8_t* md = static_cast<uint8_t*>(workspace);
+  HIP_TRY(stager().copy(md, bl.data(), bl.size(), st));
+  AttnParams p{};
+  p.tiles = reinterpret_cast<const AttnTile*>(md + o_til);
+  p.n_tiles = (int32_t)tiles.size();
+  p.srcs = reinterpret_cast<const KVSrc*>(md + o_src);
+  p.seg_lo = reinterpret_cast<const int32_t*>(md + o_seg);
+  p.q = static_cast<const uint16_t*>(q); p.q_stride = (int64_t)hq * d;
+  p.out = static_cast<uint16_t*>(out); p.o_stride = (int64_t)hq * d;
+  p.lse = lse; p.hq = hq; p.hkv = hkv;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  p.k_scale = 1.0f; p.v_scale = 1.0f;
+  HIP_TRY(launch_attn_bf16(p, G, st));
+  return QUAIL_OK;
+}
+
+quail_status quail_gemm_w8a16(int32_t M, int32_t N, int32_t K, const uint16_t* x, const uint8_t* w,
+                              const uint16_t* scale, uint16_t* y, quail_stream stream) {
+  if (M < 0 || N <= 0 || K <= 0) return fail(QUAIL_E_INVAL, "M >= 0, N > 0, K > 0 required");
+  if (K % 64 || N % 128) return fail(QUAIL_E_UNSUPPORTED, "K must be a multiple of 64 and N of 128");
+  if (M == 0) return QUAIL_OK;
+  if (!x || !w || !scale || !y) return fail(QUAIL_E_INVAL, "NULL argument");
+  GemmParams p{};
+  p.A = x; p.lda = K; p.B = w; p.scale = scale; p.M = M; p.N = N; p.K = K; p.Y = y; p.ldy = N;
+  HIP_TRY(launch_gemm(p, EPI_STORE, as_stream(stream)));
+  return QUAIL_OK;
+}
+
+quail_status quail_fp8_e4m3_encode(int64_t n, const float* x, float scale, uint8_t* codes,
+                                   quail_stream stream) {
+  if (n < 0 || !(scale > 0.0f)) return fail(QUAIL_E_INVAL, "n >= 0 and scale > 0 required");
+  if (n == 0) return QUAIL_OK;
+  if (!x || !codes) return fail(QUAIL_E_INVAL, "NULL argument");
+  HIP_TRY(launch_fp8_encode(n, x, 1.0f / scale, codes, as_stream(stream)));
+  return QUAIL_OK;
+}
+
+quail_status quail_fp8_e4m3_decode(int64_t n, const uint8_t* codes, float scale, float* x,
+                                   quail_stream stream) {
+  if (n < 0) return fail(QUAIL_E_INVAL, "n >= 0 required");
+  if (n == 0) return QUAIL_OK;
+  if (!x || !codes) return fail(QUAIL_E_INVAL, "NULL argument");
+  HIP_TRY(launch_fp8_decode(n, codes, scale, x, as_stream(stream)));
+  return QUAIL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,206 @@
+// Memory-bound kernels of the prefill path on gfx950: embedding gather,
+// RMSNorm, last-row gather, the 8-column head with its argmax/boolean, and the
+// E4M3 codec used by the fp8 KV store. All are one wave per row with 16-byte
+// vector accesses; rows are independent.
+#include "device_common.h"
+#include "quail_internal.h"
+
+namespace quail {
+
+// h[r] = embed[tokens[tok_map ? tok_map[r] : r]]
+__global__ void __launch_bounds__(256) embed_kernel(const int32_t* tokens, const int32_t* tok_map,
+                                                    const uint16_t* embed, uint16_t* h,
+                                                    int32_t rows, int32_t H) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  const int src = tok_map ? tok_map[r] : r;
+  const int64_t tok = tokens[src];
+  const uint4* s = reinterpret_cast<const uint4*>(embed + tok * H);
+  uint4* d = reinterpret_cast<uint4*>(h + (int64_t)r * H);
+  for (int c = lane; c < H / 8; c += 64) d[c] = s[c];
+}
+
+hipError_t launch_embed(const int32_t* tokens, const int32_t* tok_map, const uint16_t* embed,
+                        uint16_t* h, int32_t rows, int32_t H, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  embed_kernel<<<dim3((rows + 3) / 4), dim3(256), 0, s>>>(tokens, tok_map, embed, h, rows, H);
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256) copy_rows_kernel(const uint16_t* src, int64_t lds,
+                                                        const int32_t* src_idx, uint16_t* dst,
+                                                        int64_t ldd, const int32_t* dst_idx,
+                                                        int32_t rows, int32_t H) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  const int64_t sr = src_idx ? src_idx[r] : r;
+  const int64_t dr = dst_idx ? dst_idx[r] : r;
+  const uint4* s = reinterpret_cast<const uint4*>(src + sr * lds);
+  uint4* d = reinterpret_cast<uint4*>(dst + dr * ldd);
+  for (int c = lane; c < H / 8; c += 64) d[c] = s[c];
+}
+
+hipError_t launch_copy_rows(const uint16_t* src, int64_t lds, const int32_t* src_idx,
+                            uint16_t* dst, int64_t ldd, const int32_t* dst_idx, int32_t rows,
+                            int32_t H, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  copy_rows_kernel<<<dim3((rows + 3) / 4), dim3(256), 0, s>>>(src, lds, src_idx, dst, ldd,
+                                                              dst_idx, rows, H);
+  return hipGetLastError();
+}
+
+// y = bf16(x / sqrt(mean(x^2) + eps) * gamma)
+__global__ void __launch_bounds__(256) rmsnorm_kernel(NormParams p) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= p.rows) return;
+  const int src = p.row_map ? p.row_map[r] : r;
+  const uint4* x = reinterpret_cast<const uint4*>(p.x + (int64_t)src * p.ldx);
+  const int nc = p.H / 8;
+  float ss = 0.0f;
+  for (int c = lane; c < nc; c += 64) {
+    const uint4 u = x[c];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = bf16_bits_to_f32(w[i] & 0xFFFF), b = bf16_bits_to_f32(w[i] >> 16);
+      ss += a * a + b * b;
+    }
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)p.H + p.eps);
+  uint4* y = reinterpret_cast<uint4*>(p.y + (int64_t)r * p.ldy);
+  const uint4* gm = reinterpret_cast<const uint4*>(p.gamma);
+  for (int c = lane; c < nc; c += 64) {
+    const uint4 u = x[c];
+    const uint4 gg = gm ? gm[c] : make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = bf16_bits_to_f32(w[i] & 0xFFFF) * inv * bf16_bits_to_f32(gw[i] & 0xFFFF);
+      const float b = bf16_bits_to_f32(w[i] >> 16) * inv * bf16_bits_to_f32(gw[i] >> 16);
+      o[i] = pack_bf16x2(a, b);
+    }
+    y[c] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s) {
+  if (p.rows == 0) return hipSuccess;
+  rmsnorm_kernel<<<dim3((p.rows + 3) / 4), dim3(256), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+// Argmax (first maximum), boolean and store for one row's 8 logits (lane 0).
+__device__ __forceinline__ void head8_finish(const float (&lg)[8], uint32_t true_mask, int out,
+                                             float* logits, uint8_t* token, uint8_t* decision) {
+  int best = 0;
+#pragma unroll
+  for (int j = 1; j < 8; ++j)
+    if (lg[j] > lg[best]) best = j;
+  if (logits) {
+    float4* lp = reinterpret_cast<float4*>(logits + (int64_t)out * 8);
+    lp[0] = make_float4(lg[0], lg[1], lg[2], lg[3]);
+    lp[1] = make_float4(lg[4], lg[5], lg[6], lg[7]);
+  }
+  if (token) token[out] = (uint8_t)best;
+  decision[out] = (uint8_t)((true_mask >> best) & 1u);
+}
+
+// z = bf16(RMSNorm(h_row; gamma)); logits = z . w8 (fp32); argmax; boolean.
+__global__ void __launch_bounds__(256) head8_kernel(Head8Params p) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= p.rows) return;
+  const int src = p.row_map ? p.row_map[r] : r;
+  const uint16_t* x = p.h + (int64_t)src * p.ldh;
+  float inv = 1.0f;
+  if (p.gamma) {
+    float ss = 0.0f;
+    for (int i = lane; i < p.H; i += 64) {
+      const float a = bf16_bits_to_f32(x[i]);
+      ss += a * a;
+    }
+    ss = wave_sum(ss);
+    inv = 1.0f / sqrtf(ss / (float)p.H + p.eps);
+  }
+  float lg[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int i = lane; i < p.H; i += 64) {
+    float z = bf16_bits_to_f32(x[i]);
+    if (p.gamma) z = bf16_bits_to_f32(f32_to_bf16_bits(z * inv * bf16_bits_to_f32(p.gamma[i])));
+    const uint4 w = *reinterpret_cast<const uint4*>(p.w8 + (int64_t)i * 8);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lg[2 * j] += z * bf16_bits_to_f32(ww[j] & 0xFFFF);
+      lg[2 * j + 1] += z * bf16_bits_to_f32(ww[j] >> 16);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) lg[j] = wave_sum(lg[j]);
+  if (lane == 0)
+    head8_finish(lg, p.true_mask, p.out_map ? p.out_map[r] : r, p.logits, p.token, p.decision);
+}
+
+hipError_t launch_head8(const Head8Params& p, hipStream_t s) {
+  if (p.rows == 0) return hipSuccess;
+  head8_kernel<<<dim3((p.rows + 3) / 4), dim3(256), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256) head8_f32_kernel(int32_t n, int32_t H, const float* x,
+                                                        const float* w8, uint32_t true_mask,
+                                                        float* logits, uint8_t* token,
+                                                        uint8_t* decision) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= n) return;
+  float lg[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int i = lane; i < H; i += 64) {
+    const float z = x[(int64_t)r * H + i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lg[j] += z * w8[(int64_t)i * 8 + j];
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) lg[j] = wave_sum(lg[j]);
+  if (lane == 0) head8_finish(lg, true_mask, r, logits, token, decision);
+}
+
+hipError_t launch_head8_f32(int32_t n, int32_t H, const float* x, const float* w8,
+                            uint32_t true_mask, float* logits, uint8_t* token,
+                            uint8_t* decision, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  head8_f32_kernel<<<dim3((n + 3) / 4), dim3(256), 0, s>>>(n, H, x, w8, true_mask, logits, token,
+                                                          decision);
+  return hipGetLastError();
+}
+
+__global__ void fp8_encode_kernel(int64_t n, const float* x, float inv_scale, uint8_t* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = (uint8_t)f32_to_e4m3(x[i] * inv_scale);
+}
+
+__global__ void fp8_decode_kernel(int64_t n, const uint8_t* codes, float scale, float* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = fp8x2_to_f32<false>((uint32_t)codes[i])[0] * scale;
+}
+
+hipError_t launch_fp8_encode(int64_t n, const float* x, float inv_scale, uint8_t* out,
+                             hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  fp8_encode_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(n, x, inv_scale, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_decode(int64_t n, const uint8_t* codes, float scale, float* out,
+                             hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  fp8_decode_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(n, codes, scale, out);
+  return hipGetLastError();
+}
+
+}  // namespace quail

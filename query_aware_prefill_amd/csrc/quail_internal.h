@@ -1,0 +1,135 @@
+// Internal declarations shared by the HIP kernels and the host runtime.
+// Nothing here is part of the public C ABI (include/quail.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace quail {
+
+constexpr int kHeadDim = 128;   // head_dim of the MFMA attention and QKV epilogue
+constexpr int kKeyTile = 64;    // keys per attention tile; slab rows are padded to this
+constexpr int kQRows = 32;      // query tokens per wave in the attention kernel
+
+// A key/value source for attention. Element (token t, kv head g, dim c) of K
+// lives at k + t*tok_stride + g*head_stride + c; likewise V.
+struct KVSrc {
+  const void* k;
+  const void* v;
+  int64_t tok_stride;     // elements
+  int64_t head_stride;    // elements
+  int32_t len;            // valid tokens (rows >= len read as zero)
+  int32_t fp8;            // 1: OCP E4M3 codes (decoded, times k_scale / v_scale)
+};
+
+// One attention work item: query tokens [q0, q0+nq) against
+//   - every key of source `cross` (no mask), then
+//   - keys [self_k0, self_qbase + row] of source `self` (causal), where row is
+//     the query's offset from q0, and keys below seg_lo[q0 + row] are hidden.
+// Either source may be -1 (absent).
+struct AttnTile {
+  int32_t q0, nq;
+  int32_t cross;
+  int32_t self;
+  int32_t self_qbase;
+  int32_t self_k0;
+};
+
+struct AttnParams {
+  const AttnTile* tiles;
+  int32_t n_tiles;
+  const KVSrc* srcs;
+  const int32_t* seg_lo;    // [tokens] first visible self key of each query token
+  const uint16_t* q;        // bf16 [tokens][q_stride], head h at h*128
+  int64_t q_stride;
+  uint16_t* out;            // bf16 [tokens][o_stride]
+  int64_t o_stride;
+  float* lse;               // f32 [tokens][hq] or null
+  int32_t hq, hkv;
+  float scale_log2;         // softmax scale * log2(e)
+  float k_scale, v_scale;   // fp8 dequantisation scales
+};
+
+// fp32 reference-precision cascade (small head dims, explicit two partials + merge)
+struct AttnF32Params {
+  const float* ak; const float* av;      // [sum La][hkv][d]
+  const int32_t* a_off;                  // [n_anchors+1] (device)
+  const float* q; const float* k; const float* v;   // [sum Ls][h][d]
+  const int32_t* tok_anchor;             // [tokens] anchor index or -1
+  const int32_t* tok_seg;                // [tokens] first token of the token's suffix
+  float* out; float* lse;
+  int32_t n_tok, hq, hkv, d;
+  float scale;
+};
+
+enum GemmEpi : int32_t {
+  EPI_STORE = 0,    // y = bf16(acc * scale)
+  EPI_RESID = 1,    // y = bf16(y + acc * scale)           (residual add in place)
+  EPI_SWIGLU = 2,   // y[n] = bf16(silu(g) * u), g from row n, u from row n + inter
+  EPI_QKV = 3,      // RoPE on q/k heads, q -> q_out, k/v -> suffix buffers or slabs
+};
+
+struct GemmParams {
+  const uint16_t* A; int64_t lda;        // bf16 [M][K]
+  const uint8_t* B;                      // fp8 [N_rows][K]
+  const uint16_t* scale;                 // bf16 [N_rows]
+  int32_t M, N, K;                       // N = output columns
+  uint16_t* Y; int64_t ldy;              // STORE / RESID / SWIGLU output
+  int32_t inter;                         // SWIGLU: up rows start at `inter`
+  // QKV epilogue
+  int32_t hq, hkv;
+  const float2* rope;                    // [max_pos][64] (cos, sin)
+  const int32_t* pos;                    // [M] RoPE position of each row
+  uint16_t* q_out;                       // [M][hq*128]
+  int32_t kv_mode;                       // 0: suffix buffers, 1: anchor slabs
+  uint16_t* k_out; uint16_t* v_out;      // kv_mode 0: [M][hkv][128]
+  void* pool;                            // kv_mode 1: slab pool base
+  const int64_t* kv_row;                 // kv_mode 1: [M] element offset of (slab, token)
+  const int32_t* kv_lapad;               // kv_mode 1: [M] padded anchor length
+  int32_t layer;
+  int32_t kv_fp8;                        // slabs hold E4M3 codes
+  float k_inv_scale, v_inv_scale;
+};
+
+struct NormParams {
+  const uint16_t* x; int64_t ldx;
+  const uint16_t* gamma;                 // bf16 [H] (null: gain 1)
+  uint16_t* y; int64_t ldy;
+  const int32_t* row_map;                // optional: y row r reads x row row_map[r]
+  int32_t rows, H;
+  float eps;
+};
+
+struct Head8Params {
+  const uint16_t* h; int64_t ldh;        // bf16 rows
+  const int32_t* row_map;                // optional: row r reads h row row_map[r]
+  const uint16_t* gamma;                 // final norm (bf16 [H]) or null
+  const uint16_t* w8;                    // bf16 [H][8]
+  const int32_t* out_map;                // optional: output slot of row r
+  float* logits; uint8_t* token; uint8_t* decision;
+  int32_t rows, H;
+  float eps;
+  uint32_t true_mask;
+};
+
+// ---- launchers (return the launch's hipError_t) ----
+hipError_t launch_attn_bf16(const AttnParams& p, int group, hipStream_t s);
+hipError_t launch_attn_f32(const AttnF32Params& p, hipStream_t s);
+hipError_t launch_gemm(const GemmParams& p, GemmEpi epi, hipStream_t s);
+hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s);
+hipError_t launch_embed(const int32_t* tokens, const int32_t* tok_map, const uint16_t* embed,
+                        uint16_t* h, int32_t rows, int32_t H, hipStream_t s);
+// dst[dst_idx ? dst_idx[r] : r] = src[src_idx ? src_idx[r] : r], bf16 rows of H
+hipError_t launch_copy_rows(const uint16_t* src, int64_t lds, const int32_t* src_idx,
+                            uint16_t* dst, int64_t ldd, const int32_t* dst_idx, int32_t rows,
+                            int32_t H, hipStream_t s);
+hipError_t launch_head8(const Head8Params& p, hipStream_t s);
+hipError_t launch_head8_f32(int32_t n, int32_t H, const float* x, const float* w8,
+                            uint32_t true_mask, float* logits, uint8_t* token,
+                            uint8_t* decision, hipStream_t s);
+hipError_t launch_fp8_encode(int64_t n, const float* x, float inv_scale, uint8_t* out,
+                             hipStream_t s);
+hipError_t launch_fp8_decode(int64_t n, const uint8_t* codes, float scale, float* out,
+                             hipStream_t s);
+
+}  // namespace quail

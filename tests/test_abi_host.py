@@ -1,0 +1,205 @@
+"""CPU tests of the C-ABI library: it loads, exports every function quail.h
+declares, and its host logic (sizing, plan builder, validation and error
+model) matches the oracle -- no GPU call is made here."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import plan as OP
+from query_aware_prefill_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "quail.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|quail_status)\s+(quail_\w+)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load()
+    names = _declared()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(B.EXPORTS) == names
+    assert B.quail_version().startswith("quail-mi355x")
+
+
+def _cfg(layers=36, fp8=False, **kw):
+    d = dict(n_layers=layers, hidden=2560, n_q_heads=32, n_kv_heads=8, head_dim=128,
+             intermediate=9728, vocab=151936, rope_theta=1e6, rms_eps=1e-6,
+             kv_dtype=B.DTYPE_FP8_E4M3 if fp8 else B.DTYPE_BF16, k_scale=1.0, v_scale=1.0,
+             max_anchor_len=2048, max_suffix_len=256)
+    d.update(kw)
+    return B.ModelConfig(**d)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_anchor_bytes_matches_oracle_slab(fp8):
+    cfg = _cfg(fp8=fp8)
+    for la in (1, 63, 64, 65, 768, 1024, 2048):
+        assert B.quail_anchor_bytes(cfg, la) == OP.slab_bytes(la, 36, 8, 128, 1 if fp8 else 2)
+    # 1024 anchors of 768 tokens: 57.98 GB in fp8 (twice that in bf16)
+    assert B.quail_anchor_bytes(cfg, 768) * 1024 == 36 * 2 * 8 * 768 * 128 * 1024 * (1 if fp8 else 2)
+
+
+def test_workspace_bytes_grows_with_batch():
+    cfg = _cfg()
+    a = B.quail_workspace_bytes(cfg, 1024)
+    b = B.quail_workspace_bytes(cfg, 2048)
+    assert b > a > 1024 * 2560 * 2 * 8
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_plan_build_matches_oracle(seed):
+    r = np.random.default_rng(100 + seed)
+    cfg = _cfg(layers=2, n_kv_heads=2, n_q_heads=4, hidden=256, intermediate=384)
+    na = int(r.integers(1, 9))
+    a_len = r.integers(1, 300, na).astype(np.int32)
+    slab = np.array([OP.slab_bytes(x, 2, 2, 128, 2) for x in a_len])
+    n = int(r.integers(0, 60))
+    pa = r.integers(-1, na, n).astype(np.int32)
+    pl = r.integers(1, 64, n).astype(np.int32)
+    pool = int(slab.max() * r.integers(1, 4))
+    mbt = int(r.integers(64, 300))
+    ref = OP.plan_reference(slab, pa, pl, pool, mbt)
+    order, bounds, peak = B.quail_plan_build(cfg, pool, mbt, a_len, pa, pl)
+    assert np.array_equal(order, ref["order"])
+    assert np.array_equal(bounds, ref["step_bounds"])
+    assert peak == ref["peak"]
+
+
+def test_plan_build_errors():
+    cfg = _cfg(layers=1)
+    slab = B.quail_anchor_bytes(cfg, 100)
+    with pytest.raises(B.QuailError) as e:
+        B.quail_plan_build(cfg, slab - 1, 64, [100], [0], [5])
+    assert e.value.status == B.E_NOMEM
+    with pytest.raises(B.QuailError) as e:
+        B.quail_plan_build(cfg, slab, 64, [100], [0], [65])
+    assert e.value.status == B.E_INVAL
+    with pytest.raises(B.QuailError) as e:
+        B.quail_plan_build(cfg, slab, 64, [100], [1], [5])
+    assert e.value.status == B.E_INVAL
+
+
+def test_config_validation():
+    lib = B.load()
+    out = C.c_size_t()
+    bad = _cfg(head_dim=64)
+    assert lib.quail_workspace_bytes(C.byref(bad), 16, C.byref(out)) == B.E_UNSUPPORTED
+    bad = _cfg(n_q_heads=24)     # group size 3
+    assert lib.quail_workspace_bytes(C.byref(bad), 16, C.byref(out)) == B.E_UNSUPPORTED
+    bad = _cfg(hidden=2500)
+    assert lib.quail_workspace_bytes(C.byref(bad), 16, C.byref(out)) == B.E_UNSUPPORTED
+    bad = _cfg(n_layers=0)
+    assert lib.quail_workspace_bytes(C.byref(bad), 16, C.byref(out)) == B.E_INVAL
+    assert b"positive" in lib.quail_last_error()
+
+
+class _FakeCtx:
+    """A context over fake (never dereferenced) device addresses: every call
+    below must fail in host validation before touching the GPU."""
+
+    def __init__(self, pool_bytes, layers=2, mbt=256):
+        self.lib = B.load()
+        self.cfg = _cfg(layers=layers, n_kv_heads=2, n_q_heads=4, hidden=256, intermediate=384,
+                        max_anchor_len=512, max_suffix_len=128)
+        fake = 0x7F0000000000
+        self.lw = (B.LayerWeights * layers)()
+        for i in range(layers):
+            for f, _ in B.LayerWeights._fields_:
+                setattr(self.lw[i], f, fake)
+        self.w = B.Weights(embed=fake, layers=C.cast(self.lw, C.POINTER(B.LayerWeights)),
+                           final_norm=fake, head8=fake)
+        ws = B.quail_workspace_bytes(self.cfg, mbt)
+        h = C.c_void_p()
+        st = self.lib.quail_ctx_create(C.byref(self.cfg), C.byref(self.w), fake, pool_bytes, fake, ws,
+                                       mbt, C.byref(h))
+        assert st == 0, self.lib.quail_last_error()
+        self.h = h
+
+    def close(self):
+        self.lib.quail_ctx_destroy(self.h)
+
+
+def _i32(a):
+    a = np.ascontiguousarray(a, np.int32)
+    return a, a.ctypes.data_as(C.POINTER(C.c_int32))
+
+
+def _i64(a):
+    a = np.ascontiguousarray(a, np.int64)
+    return a, a.ctypes.data_as(C.POINTER(C.c_int64))
+
+
+def test_anchor_prefill_pool_too_small_is_nomem_and_keeps_nothing():
+    cfg_slab = OP.slab_bytes(100, 2, 2, 128, 2)
+    fc = _FakeCtx(pool_bytes=cfg_slab + cfg_slab // 2)
+    off, offp = _i32([0, 100, 200])
+    nu, nup = _i32([3, 4])
+    out, outp = _i64([0, 0])
+    st = fc.lib.quail_anchor_prefill(fc.h, 2, 0x7F0000000000, offp, nup, None, outp, None)
+    assert st == B.E_NOMEM
+    r, p = C.c_size_t(), C.c_size_t()
+    pf, ev, rg = C.c_int64(), C.c_int64(), C.c_int64()
+    fc.lib.quail_pool_stats(fc.h, C.byref(r), C.byref(p), C.byref(pf), C.byref(ev), C.byref(rg))
+    assert r.value == 0 and pf.value == 0
+    fc.close()
+
+
+def test_anchor_prefill_rejects_bad_offsets():
+    fc = _FakeCtx(pool_bytes=1 << 26)
+    nu, nup = _i32([1, 1])
+    out, outp = _i64([0, 0])
+    for offs in ([0, 10, 5], [0, 0, 10], [0, 10, 10 + 513], [-1, 5, 10]):
+        off, offp = _i32(offs)
+        st = fc.lib.quail_anchor_prefill(fc.h, 2, 0x7F0000000000, offp, nup, None, outp, None)
+        assert st == B.E_INVAL, offs
+    fc.close()
+
+
+def test_join_with_stale_handle_is_stale():
+    fc = _FakeCtx(pool_bytes=1 << 26)
+    for h in (5, (3 << 32) | 0, 0):
+        ha, hap = _i64([h])
+        off, offp = _i32([0, 4])
+        st = fc.lib.quail_join_prefill(fc.h, 1, hap, 0x7F0000000000, offp, 0x7F0000000000, None, None)
+        assert st == B.E_STALE
+        assert fc.lib.quail_anchor_release(fc.h, h) == B.E_STALE
+    fc.close()
+
+
+def test_join_rejects_bad_suffix_lengths():
+    fc = _FakeCtx(pool_bytes=1 << 26)
+    ha, hap = _i64([B.NO_ANCHOR, B.NO_ANCHOR])
+    for offs in ([0, 0, 4], [0, 129, 130], [0, 4, 2]):
+        off, offp = _i32(offs)
+        st = fc.lib.quail_join_prefill(fc.h, 2, hap, 0x7F0000000000, offp, 0x7F0000000000, None, None)
+        assert st == B.E_INVAL, offs
+    fc.close()
+
+
+def test_cascade_attn_argument_checks():
+    lib = B.load()
+    so, sop = _i32([0, 4])
+    sa, sap = _i32([0])
+    ao, aop = _i32([0, 8])
+    ws = C.c_size_t()
+    assert lib.quail_cascade_workspace_bytes(1, aop, 1, sop, C.byref(ws)) == 0
+    fake = 0x7F0000000000
+    # head_dim 64 is fp32-only
+    assert lib.quail_cascade_attn(B.DTYPE_BF16, 4, 2, 64, 0.1, 1, fake, fake, aop, 1, sap, fake, fake,
+                                  fake, sop, fake, None, fake, ws.value, None) == B.E_UNSUPPORTED
+    # anchor index out of range
+    sa2, sap2 = _i32([3])
+    assert lib.quail_cascade_attn(B.DTYPE_BF16, 4, 2, 128, 0.1, 1, fake, fake, aop, 1, sap2, fake, fake,
+                                  fake, sop, fake, None, fake, ws.value, None) == B.E_INVAL
+    # workspace too small
+    assert lib.quail_cascade_attn(B.DTYPE_BF16, 4, 2, 128, 0.1, 1, fake, fake, aop, 1, sap, fake, fake,
+                                  fake, sop, fake, None, fake, 16, None) == B.E_NOMEM

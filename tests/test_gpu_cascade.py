@@ -1,0 +1,161 @@
+"""GPU parity of cascade attention (cross + self partials merged by LSE)
+against the oracle's monolithic causal attention over [anchor ‖ suffix]:
+the fp32 configuration (1 anchor x 64 + 8 suffixes x 32, 4q/2kv x 64),
+ragged bf16 edge cases, the Qwen3-shaped bf16 configuration reduced, and
+that configuration at full size (256 anchors x 64 suffixes) on sampled
+suffixes in the benchmark's launch configuration."""
+import math
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as OA, model as OM
+from tests.gpu_util import bf16_f64, decisions_agree, rel_inf, say, u16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    import torch
+    assert torch.cuda.is_available()
+    from query_aware_prefill_amd import binding
+    binding.load()
+    return binding
+
+
+def _run(B, case, lse=True):
+    import torch
+    from query_aware_prefill_amd.device import to_device
+    f32 = case["dtype"] == "f32"
+    dev = {k: to_device(case[k]) for k in ("ak", "av", "q", "k", "v")}
+    T = int(case["s_off"][-1])
+    out = torch.empty((T, case["hq"], case["d"]), dtype=torch.float32 if f32 else torch.int16,
+                      device="cuda")
+    lse_t = torch.empty((T, case["hq"]), dtype=torch.float32, device="cuda") if lse else None
+    wsb = B.quail_cascade_workspace_bytes(case["a_off"], case["s_off"])
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    B.quail_cascade_attn(B.DTYPE_F32 if f32 else B.DTYPE_BF16, case["hq"], case["hkv"], case["d"],
+                         case["sm_scale"], dev["ak"], dev["av"], case["a_off"], case["s_anchor"],
+                         dev["q"], dev["k"], dev["v"], case["s_off"], out, lse_t, ws)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().astype(np.float64) if f32 else bf16_f64(u16(out))
+    return o, (lse_t.cpu().numpy().astype(np.float64) if lse else None)
+
+
+def test_c0_fp32_cascade_and_head(B):
+    import torch
+    say("C0 fp32 cascade")
+    case = W.c0_case(0)
+    o, lse = _run(B, case)
+    ref_o, ref_l = OA.cascade_case_reference(case, mode="monolithic")
+    assert np.max(np.abs(o - ref_o)) <= 1e-3
+    assert np.max(np.abs(lse - ref_l)) <= 1e-3
+    # cascade form of the oracle agrees with its monolithic form
+    c_o, _ = OA.cascade_case_reference(case, mode="cascade")
+    assert np.max(np.abs(c_o - ref_o)) < 1e-12
+    # 8-column head on each suffix's last position (flattened 4 x 64 output)
+    last = case["s_off"][1:] - 1
+    x = o[last].reshape(len(last), 256).astype(np.float32)
+    logits = torch.empty((len(last), 8), dtype=torch.float32, device="cuda")
+    tok = torch.empty(len(last), dtype=torch.uint8, device="cuda")
+    dec = torch.empty(len(last), dtype=torch.uint8, device="cuda")
+    B.quail_head8_f32(torch.from_numpy(x).cuda(), torch.from_numpy(case["w8"]).cuda(),
+                      case["true_mask"], logits, tok, dec)
+    torch.cuda.synchronize()
+    ref_logits = ref_o[last].reshape(len(last), 256) @ case["w8"].astype(np.float64)
+    rt, rd, rm = OM.decide(ref_logits, case["true_mask"])
+    assert np.max(np.abs(logits.cpu().numpy() - ref_logits)) <= 1e-3
+    ok, n_sure = decisions_agree(dec.cpu().numpy(), rd, rm, 1e-3)
+    assert ok and n_sure >= 6
+
+
+def test_fp32_head_dim_128_and_no_anchor_rows(B):
+    say("fp32 d=128 with filter rows")
+    case = W.cascade_case(3, [40, 7], [0, -1, 1, 0, -1], [5, 1, 33, 2, 17], hq=4, hkv=1, d=128,
+                          dtype="f32", cfg_id=9)
+    o, lse = _run(B, case)
+    ref_o, ref_l = OA.cascade_case_reference(case)
+    assert np.max(np.abs(o - ref_o)) <= 1e-3
+    assert np.max(np.abs(lse - ref_l)) <= 1e-3
+
+
+BF16_CASES = [
+    # (a_len, s_anchor, s_len, hq, hkv)
+    ([64], [0] * 3, [32, 32, 32], 4, 1),
+    ([1], [0, 0], [1, 2], 4, 1),
+    ([65, 63], [0, 1, 0, 1], [33, 31, 1, 100], 8, 2),
+    ([200], [0] * 5, [7, 64, 65, 3, 128], 32, 8),
+    ([130, 5], [-1, 0, -1, 1, 1], [9, 40, 1, 96, 32], 4, 2),
+    ([77, 300], [1, 0, 1, 1], [50, 20, 70, 2], 8, 8),
+    ([512], [0, 0], [128, 64], 16, 2),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(BF16_CASES)))
+def test_bf16_ragged_cases(B, ci):
+    a_len, s_anchor, s_len, hq, hkv = BF16_CASES[ci]
+    say("bf16 case", ci, a_len, s_len, hq, hkv)
+    case = W.cascade_case(ci, a_len, s_anchor, s_len, hq=hq, hkv=hkv, d=128, dtype="bf16", cfg_id=11)
+    o, lse = _run(B, case)
+    ref_o, ref_l = OA.cascade_case_reference(case)
+    for s in range(len(s_len)):
+        sl = slice(case["s_off"][s], case["s_off"][s + 1])
+        err = rel_inf(o[sl], ref_o[sl])
+        assert err <= 2e-2, (s, err)
+    assert np.max(np.abs(lse - ref_l)) <= 1e-3 + 1e-4 * np.max(np.abs(ref_l))
+
+
+def test_c1_reduced_full_length_ranges(B):
+    """4 anchors of U{512..2048} x 8 suffixes of U{32..128}, 32q/8kv x 128."""
+    say("C1 reduced")
+    case = W.c1_case(seed=1, n_anchors=4, per_anchor=8)
+    o, lse = _run(B, case)
+    ref_o, ref_l = OA.cascade_case_reference(case)
+    worst = 0.0
+    for s in range(len(case["s_len"])):
+        sl = slice(case["s_off"][s], case["s_off"][s + 1])
+        worst = max(worst, rel_inf(o[sl], ref_o[sl]))
+    say("  worst rel err", worst)
+    assert worst <= 2e-2
+    assert np.max(np.abs(lse - ref_l)) <= 1e-3 + 1e-4 * np.max(np.abs(ref_l))
+
+
+def test_c1_full_size_sampled(B):
+    """The full configuration (256 anchors x 64 suffixes, 1.31M suffix tokens,
+    32q/8kv x 128) in one launch, as the benchmark runs it; 12 sampled
+    suffixes (first and last of the batch included) are checked against the
+    oracle."""
+    import torch
+    say("C1 full size: generating on device")
+    case = W.c1_device(seed=1)
+    T = int(case["s_off"][-1])
+    out = torch.empty((T, 32, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, 32), dtype=torch.float32, device="cuda")
+    wsb = B.quail_cascade_workspace_bytes(case["a_off"], case["s_off"])
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    say("C1 full size: launch")
+    B.quail_cascade_attn(B.DTYPE_BF16, 32, 8, 128, case["sm_scale"], case["ak"], case["av"],
+                         case["a_off"], case["s_anchor"], case["q"], case["k"], case["v"],
+                         case["s_off"], out, lse, ws)
+    torch.cuda.synchronize()
+    say("C1 full size: oracle on samples")
+    r = np.random.default_rng(5)
+    n_suf = len(case["s_len"])
+    picks = sorted({0, n_suf - 1, *r.choice(n_suf, 10, replace=False).tolist()})
+
+    def host(t):
+        return t.float().cpu().numpy().astype(np.float64)
+
+    for s in picks:
+        t0, t1 = int(case["s_off"][s]), int(case["s_off"][s + 1])
+        a = int(case["s_anchor"][s])
+        a0, a1 = int(case["a_off"][a]), int(case["a_off"][a + 1])
+        ro, rl = OA.monolithic_pair_attention(host(case["q"][t0:t1]), host(case["ak"][a0:a1]),
+                                              host(case["av"][a0:a1]), host(case["k"][t0:t1]),
+                                              host(case["v"][t0:t1]), case["sm_scale"])
+        err = rel_inf(host(out[t0:t1]), ro)
+        lerr = float(np.max(np.abs(host(lse[t0:t1]) - rl)))
+        say("  suffix", s, "rel", err, "lse", lerr)
+        assert err <= 2e-2 and lerr <= 1e-2

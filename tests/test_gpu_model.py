@@ -1,0 +1,215 @@
+"""GPU parity of the model path against the oracle's per-pair monolithic
+forward: anchor prefill + KV writer (slab contents), join prefill (last and
+all hidden rows), the 8-column head and its booleans, residency counters and
+handle errors, the whole-join entry point, the fp8 KV store, and one
+Qwen3-4B-shaped decoder layer."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import codecs, model as OM
+from tests.gpu_util import bf16_f64, decisions_agree, rel_inf, say, u16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    import torch
+    assert torch.cuda.is_available()
+    from query_aware_prefill_amd import binding
+    binding.load()
+    return binding
+
+
+def _slab(ctx, handle, layer, B, shape):
+    """Read one layer's K and V of an anchor back from the pool tensor."""
+    kp, vp, la, lap = B.quail_anchor_kv(ctx, handle, layer)
+    pool = ctx._pool
+    esz = 1 if shape.kv_fp8 else 2
+    n = shape.n_kv_heads * lap * shape.head_dim * esz
+    out = []
+    for p in (kp, vp):
+        off = p - pool.data_ptr()
+        raw = pool[off:off + n].cpu().numpy()
+        if esz == 2:
+            vals = bf16_f64(raw.view(np.uint16))
+        else:
+            vals = codecs.e4m3_decode(raw) * (shape.k_scale if p == kp else shape.v_scale)
+        out.append(vals.reshape(shape.n_kv_heads, lap, shape.head_dim)[:, :la].transpose(1, 0, 2))
+    return out
+
+
+def _fp8_codes_valid(got, stored, pre):
+    """An fp8 store decides a code from a float: where the GPU's and the
+    oracle's pre-quantisation values straddle a rounding midpoint the codes
+    may differ by one step. Every stored value must be one of the two E4M3
+    values bracketing the oracle's pre-quantisation value, and nearly all
+    must equal the oracle's code."""
+    codes = np.arange(127, dtype=np.uint8)
+    grid = codecs.e4m3_decode(codes)                       # non-negative values
+    a = np.minimum(np.abs(pre), 448.0)
+    i = np.clip(np.searchsorted(grid, a), 1, 126)
+    lo, hi = grid[i - 1], grid[i]
+    ok = (np.abs(got) == lo) | (np.abs(got) == hi) | (got == 0)
+    assert np.all(ok | (np.abs(got - stored) == 0)), np.flatnonzero(~ok)[:5]
+    assert np.mean(got == stored) >= 0.99
+
+
+def _setup(shape, seed, a_len, pairs, B, pool_bytes=None, mbt=512):
+    import torch
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    wts = W.model_weights(shape, seed)
+    pa = [p[0] for p in pairs]
+    sl = [p[1] for p in pairs]
+    case = W.join_case(seed, shape.vocab, a_len, pa, sl, cfg_id=20)
+    dm = DeviceModel(shape, wts, max_anchor_len=1024, max_suffix_len=256)
+    if pool_bytes is None:
+        pool_bytes = sum(B.quail_anchor_bytes(dm.cfg, x) for x in a_len) + 4096
+    ctx = dm.context(pool_bytes, mbt)
+    return wts, case, dm, ctx, to_device(case["a_tok"]), to_device(case["s_tok"])
+
+
+@pytest.mark.parametrize("kv_fp8", [False, True])
+def test_tiny_model_anchor_join_head(B, kv_fp8):
+    import torch
+    shape = W.tiny_shape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                         intermediate=384, vocab=512, kv_fp8=kv_fp8)
+    a_len = [1, 70, 130]
+    pairs = [(1, 5), (0, 3), (1, 33), (-1, 7), (2, 17), (1, 64), (0, 1), (-1, 2)]
+    wts, case, dm, ctx, a_tok, s_tok = _setup(shape, 3, a_len, pairs, B)
+    uses = np.bincount([p[0] for p in pairs if p[0] >= 0], minlength=3)
+    say("tiny model: anchor prefill", "fp8" if kv_fp8 else "bf16")
+    handles = B.quail_anchor_prefill(ctx, a_tok, case["a_off"], uses, anchor_ids=np.arange(3))
+    torch.cuda.synchronize()
+    # KV writer: the slab holds the oracle's per-layer post-RoPE K and V
+    for a in range(3):
+        toks = case["a_tok"][case["a_off"][a]:case["a_off"][a + 1]]
+        _, kv = OM.forward_tokens(toks, wts, shape, return_kv=True,
+                                  fp8_kv_upto=len(toks) if kv_fp8 else 0)
+        for l in range(shape.n_layers):
+            k, v = _slab(ctx, handles[a], l, B, shape)
+            if not kv_fp8:
+                assert rel_inf(k, kv[l][0]) <= 2e-2, (a, l, "K")
+                assert rel_inf(v, kv[l][1]) <= 2e-2, (a, l, "V")
+            else:
+                for got, stored, pre in ((k, kv[l][0], kv[l][2]), (v, kv[l][1], kv[l][3])):
+                    _fp8_codes_valid(got, stored, pre)
+    say("tiny model: join prefill")
+    n = len(pairs)
+    T = int(case["s_off"][-1])
+    h_last = torch.empty((n, shape.hidden), dtype=torch.int16, device="cuda")
+    h_all = torch.empty((T, shape.hidden), dtype=torch.int16, device="cuda")
+    pair_handles = [handles[a] if a >= 0 else B.NO_ANCHOR for a, _ in pairs]
+    B.quail_join_prefill(ctx, pair_handles, s_tok, case["s_off"], h_last, h_all)
+    logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+    tok = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+    B.quail_head8(ctx, h_last, 0x0F, logits, tok, dec)
+    torch.cuda.synchronize()
+    hl, ha = bf16_f64(u16(h_last)), bf16_f64(u16(h_all))
+    ref_logits, ref_dec, ref_margin = [], [], []
+    for i, (a, L) in enumerate(pairs):
+        at = case["a_tok"][case["a_off"][a]:case["a_off"][a + 1]] if a >= 0 else []
+        st = case["s_tok"][case["s_off"][i]:case["s_off"][i + 1]]
+        ref = OM.forward_pair(at, st, wts, shape, true_mask=0x0F)
+        assert rel_inf(hl[i], ref["h_last"]) <= 2e-2, (i, rel_inf(hl[i], ref["h_last"]))
+        assert rel_inf(ha[case["s_off"][i]:case["s_off"][i + 1]], ref["h"][len(at):]) <= 2e-2
+        ref_logits.append(ref["logits"]); ref_dec.append(ref["decision"]); ref_margin.append(ref["margin"])
+    ref_logits = np.array(ref_logits)
+    assert rel_inf(logits.cpu().numpy(), ref_logits) <= 2e-2
+    tau = 2e-2 * np.max(np.abs(ref_logits))
+    ok, n_sure = decisions_agree(dec.cpu().numpy(), ref_dec, ref_margin, tau)
+    assert ok
+    st = B.quail_pool_stats(ctx)
+    assert st["prefills"] == 3 and st["evictions"] == 3 and st["regret_tokens"] == 0
+    assert st["resident"] == 0 and st["peak"] > 0
+    with pytest.raises(B.QuailError) as e:
+        B.quail_join_prefill(ctx, [handles[1]], s_tok, case["s_off"][:2], h_last)
+    assert e.value.status == B.E_STALE
+
+
+def test_release_and_regret_counting(B):
+    import torch
+    shape = W.tiny_shape(n_layers=1, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                         intermediate=384, vocab=512)
+    wts, case, dm, ctx, a_tok, s_tok = _setup(shape, 4, [50], [(0, 4)], B)
+    say("release + regret")
+    h = B.quail_anchor_prefill(ctx, a_tok, case["a_off"], [2], anchor_ids=[77])
+    B.quail_anchor_release(ctx, h[0])
+    with pytest.raises(B.QuailError) as e:
+        B.quail_anchor_release(ctx, h[0])
+    assert e.value.status == B.E_STALE
+    h2 = B.quail_anchor_prefill(ctx, a_tok, case["a_off"], [1], anchor_ids=[77])
+    h_last = torch.empty((1, shape.hidden), dtype=torch.int16, device="cuda")
+    B.quail_join_prefill(ctx, [h2[0]], s_tok, case["s_off"], h_last)
+    torch.cuda.synchronize()
+    st = B.quail_pool_stats(ctx)
+    assert st["prefills"] == 2 and st["evictions"] == 2 and st["regret_tokens"] == 50
+
+
+def test_join_run_end_to_end(B):
+    """Multi-join shaped: 6 anchors, 5 rows probing 3 anchors each (in row
+    order, unsorted), 2 filter rows; plan + prefill + join + head in one call."""
+    import torch
+    from query_aware_prefill_amd.device import to_device
+    shape = W.tiny_shape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                         intermediate=384, vocab=512)
+    r = np.random.default_rng(8)
+    a_len = r.integers(20, 120, 6).tolist()
+    pairs = []
+    for row in range(5):
+        L = int(r.integers(2, 40))
+        for a in r.choice(6, 3, replace=False):
+            pairs.append((int(a), L))
+    pairs += [(-1, 9), (-1, 3)]
+    # small batch budget so the plan has several steps
+    wts, case, dm, ctx, a_tok, s_tok = _setup(shape, 5, a_len, pairs, B, mbt=128)
+    n = len(pairs)
+    logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+    tok = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+    say("join_run", n, "pairs")
+    B.quail_join_run(ctx, a_tok, case["a_off"], case["pair_anchor"], s_tok, case["s_off"], 0x0F,
+                     logits, tok, dec)
+    torch.cuda.synchronize()
+    ref_logits, ref_dec, ref_margin = [], [], []
+    for i, (a, L) in enumerate(pairs):
+        at = case["a_tok"][case["a_off"][a]:case["a_off"][a + 1]] if a >= 0 else []
+        st = case["s_tok"][case["s_off"][i]:case["s_off"][i + 1]]
+        ref = OM.forward_pair(at, st, wts, shape, true_mask=0x0F)
+        ref_logits.append(ref["logits"]); ref_dec.append(ref["decision"]); ref_margin.append(ref["margin"])
+    ref_logits = np.array(ref_logits)
+    assert rel_inf(logits.cpu().numpy(), ref_logits) <= 2e-2
+    ok, _ = decisions_agree(dec.cpu().numpy(), ref_dec, ref_margin, 2e-2 * np.max(np.abs(ref_logits)))
+    assert ok
+    st = B.quail_pool_stats(ctx)
+    used = len({a for a, _ in pairs if a >= 0})
+    assert st["prefills"] == used and st["evictions"] == used and st["regret_tokens"] == 0
+
+
+def test_qwen3_shaped_layer(B):
+    """One decoder layer with the Qwen3-4B shapes (hidden 2560, 32q/8kv x 128,
+    SwiGLU 9728, RoPE theta 1e6, fp8 weights): 2 anchors x 1024 tokens, two
+    64-token suffixes each, against the oracle on every suffix position."""
+    import torch
+    shape = W.ModelShape(n_layers=1, hidden=2560, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                         intermediate=9728, vocab=4096)
+    pairs = [(0, 64), (1, 64), (0, 64), (1, 64)]
+    wts, case, dm, ctx, a_tok, s_tok = _setup(shape, 6, [1024, 1024], pairs, B, mbt=2048)
+    say("qwen3 layer: prefill + join")
+    handles = B.quail_anchor_prefill(ctx, a_tok, case["a_off"], [2, 2])
+    T = int(case["s_off"][-1])
+    h_last = torch.empty((4, shape.hidden), dtype=torch.int16, device="cuda")
+    h_all = torch.empty((T, shape.hidden), dtype=torch.int16, device="cuda")
+    B.quail_join_prefill(ctx, [handles[a] for a, _ in pairs], s_tok, case["s_off"], h_last, h_all)
+    torch.cuda.synchronize()
+    ha = bf16_f64(u16(h_all))
+    for i in (0, 1):
+        a = pairs[i][0]
+        at = case["a_tok"][case["a_off"][a]:case["a_off"][a + 1]]
+        st = case["s_tok"][case["s_off"][i]:case["s_off"][i + 1]]
+        h = OM.forward_tokens(np.concatenate([at, st]), wts, shape)
+        err = rel_inf(ha[case["s_off"][i]:case["s_off"][i + 1]], h[len(at):])
+        say("  pair", i, "rel", err)
+        assert err <= 2e-2

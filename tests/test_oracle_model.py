@@ -168,8 +168,11 @@ def test_fp8_kv_applies_to_anchor_positions_only():
     wts = W.model_weights(shape, 7)
     lw = M.LayerWeights(wts["layers"][0], shape)
     h = M.embed(np.arange(10), wts)
-    _, k, v = M.decoder_layer(h, np.arange(10), lw, shape, "contract", fp8_kv_upto=6, return_kv=True)
-    _, k0, v0 = M.decoder_layer(h, np.arange(10), lw, shape, "contract", fp8_kv_upto=0, return_kv=True)
+    _, (k, v, kp, vp) = M.decoder_layer(h, np.arange(10), lw, shape, "contract", fp8_kv_upto=6,
+                                        return_kv=True)
+    _, (k0, v0, _, _) = M.decoder_layer(h, np.arange(10), lw, shape, "contract", fp8_kv_upto=0,
+                                        return_kv=True)
+    assert np.array_equal(kp, k0) and np.array_equal(vp, v0)
     assert np.array_equal(k[6:], k0[6:]) and np.array_equal(v[6:], v0[6:])
     assert np.array_equal(k[:6], codecs.e4m3_roundtrip(k0[:6]))
     assert not np.array_equal(k[:6], k0[:6])

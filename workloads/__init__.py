@@ -126,17 +126,27 @@ _FP8_EXP_P = _FP8_EXP_P / _FP8_EXP_P.sum()
 _FP8_EXP_CDF = np.cumsum(_FP8_EXP_P)
 
 
+# exponent field for each 16-bit uniform draw (inverse CDF as a lookup table)
+_FP8_EXP_TABLE = np.minimum(
+    np.searchsorted(_FP8_EXP_CDF, (np.arange(1 << 16) + 0.5) / (1 << 16), side="right"),
+    15).astype(np.uint8)
+
+
 def draw_fp8_codes(rng: np.random.Generator, shape) -> np.ndarray:
-    """OCP E4M3 codes drawn field by field; never a NaN code (S.1111.111)."""
+    """OCP E4M3 codes drawn field by field from one 32-bit draw per code:
+    bits 0..15 pick the exponent field through the histogram above, bits
+    16..18 the mantissa, bit 19 the sign; never a NaN code (S.1111.111)."""
     n = int(np.prod(shape))
-    u = rng.random(n, dtype=np.float64)
-    e = np.searchsorted(_FP8_EXP_CDF, u, side="right").astype(np.uint8)
-    e = np.minimum(e, 15)
-    bits = rng.integers(0, 1 << 16, size=n, dtype=np.uint32)
-    m = (bits & 7).astype(np.uint8)
-    m = np.where(e == 15, np.minimum(m, 6), m).astype(np.uint8)
-    s = ((bits >> 3) & 1).astype(np.uint8)
-    return ((s << 7) | (e << 3) | m).astype(np.uint8).reshape(shape)
+    out = np.empty(n, np.uint8)
+    step = 1 << 24
+    for i in range(0, n, step):
+        bits = rng.integers(0, 1 << 32, size=min(step, n - i), dtype=np.uint32)
+        e = _FP8_EXP_TABLE[bits & 0xFFFF]
+        m = ((bits >> 16) & 7).astype(np.uint8)
+        m = np.where(e == 15, np.minimum(m, 6), m).astype(np.uint8)
+        s = ((bits >> 19) & 1).astype(np.uint8)
+        out[i:i + len(bits)] = (s << 7) | (e << 3) | m
+    return out.reshape(shape)
 
 
 # RMS of the magnitudes drawn by draw_fp8_codes (about 100); used only to pick
