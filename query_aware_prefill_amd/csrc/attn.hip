@@ -55,45 +55,46 @@ struct TileRegs {
   uint4 v[4];
 };
 
+// Rows at or beyond the source length are clamped to its last row: their
+// scores are masked to -inf and their P is 0, so only finiteness matters, and
+// the loads stay unconditional (no wait per load).
 template <int NT>
 __device__ __forceinline__ void load_tile(TileRegs<NT>& r, const TileView& t, int tid) {
-  const int esz = t.fp8 ? 1 : 2;
+  if (t.fp8) {
 #pragma unroll
-  for (int i = 0; i < TileRegs<NT>::KC; ++i) {
-    const int chunk = tid + i * NT;
-    const int row = chunk >> 4;            // 16 chunks of 8 dims per row
-    const int c8 = chunk & 15;
-    const int key = t.kbase + row;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (key < t.len) {
-      const uint8_t* p = t.k + (int64_t)key * t.tok_bytes + c8 * 8 * esz;
-      if (t.fp8) {
-        uint2 w = *reinterpret_cast<const uint2*>(p);
-        val = make_uint4(w.x, w.y, 0, 0);
-      } else {
-        val = *reinterpret_cast<const uint4*>(p);
-      }
+    for (int i = 0; i < TileRegs<NT>::KC; ++i) {
+      const int chunk = tid + i * NT;
+      const int key = min(t.kbase + (chunk >> 4), t.len - 1);
+      const uint2 w = *reinterpret_cast<const uint2*>(t.k + (int64_t)key * t.tok_bytes + (chunk & 15) * 8);
+      r.k[i] = make_uint4(w.x, w.y, 0, 0);
     }
-    r.k[i] = val;
+  } else {
+#pragma unroll
+    for (int i = 0; i < TileRegs<NT>::KC; ++i) {
+      const int chunk = tid + i * NT;
+      const int key = min(t.kbase + (chunk >> 4), t.len - 1);
+      r.k[i] = *reinterpret_cast<const uint4*>(t.k + (int64_t)key * t.tok_bytes + (chunk & 15) * 16);
+    }
   }
   if (NT <= 256 || tid < 256) {
-    const int blk = tid & 255;             // 16 key groups x 16 dim chunks
-    const int kg = blk >> 4;
-    const int c8 = blk & 15;
+    // V block: 4 keys x 8 dims; key groups run fastest across lanes so that
+    // the transposed LDS writes of 16 lanes form one contiguous 128-B row
+    const int blk = tid & 255;
+    const int kg = blk & 15;
+    const int c8 = blk >> 4;
+    if (t.fp8) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = t.kbase + kg * 4 + j;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (key < t.len) {
-        const uint8_t* p = t.v + (int64_t)key * t.tok_bytes + c8 * 8 * esz;
-        if (t.fp8) {
-          uint2 w = *reinterpret_cast<const uint2*>(p);
-          val = make_uint4(w.x, w.y, 0, 0);
-        } else {
-          val = *reinterpret_cast<const uint4*>(p);
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int key = min(t.kbase + kg * 4 + j, t.len - 1);
+        const uint2 w = *reinterpret_cast<const uint2*>(t.v + (int64_t)key * t.tok_bytes + c8 * 8);
+        r.v[j] = make_uint4(w.x, w.y, 0, 0);
       }
-      r.v[j] = val;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = min(t.kbase + kg * 4 + j, t.len - 1);
+        r.v[j] = *reinterpret_cast<const uint4*>(t.v + (int64_t)key * t.tok_bytes + c8 * 16);
+      }
     }
   }
 }
@@ -117,8 +118,8 @@ __device__ __forceinline__ void store_tile(const TileRegs<NT>& r, int fp8, float
   }
   if (NT <= 256 || tid < 256) {
     const int blk = tid & 255;
-    const int kg = blk >> 4;
-    const int c8 = blk & 15;
+    const int kg = blk & 15;
+    const int c8 = blk >> 4;
     uint32_t w[4][4];   // w[j] = 8 bf16 of key kg*4+j, packed in 4 words
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -134,13 +135,12 @@ __device__ __forceinline__ void store_tile(const TileRegs<NT>& r, int fp8, float
     // transpose: dim c8*8 + e, keys kg*4 .. kg*4+3
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
+      // bytes of the low (e even) or high (e odd) halves of two words
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
       const int word = e >> 1;
-      const int sh = (e & 1) * 16;
-      uint32_t k0 = (w[0][word] >> sh) & 0xFFFFu;
-      uint32_t k1 = (w[1][word] >> sh) & 0xFFFFu;
-      uint32_t k2 = (w[2][word] >> sh) & 0xFFFFu;
-      uint32_t k3 = (w[3][word] >> sh) & 0xFFFFu;
-      uint2 out = make_uint2(k0 | (k1 << 16), k2 | (k3 << 16));
+      uint2 out;
+      out.x = __builtin_amdgcn_perm(w[1][word], w[0][word], sel);
+      out.y = __builtin_amdgcn_perm(w[3][word], w[2][word], sel);
       *reinterpret_cast<uint2*>(Vt + (c8 * 8 + e) * VSTR + kg * 4) = out;
     }
   }
@@ -242,33 +242,42 @@ attn_bf16_kernel(AttnParams p) {
         s[kb] = mfma_32x32x16(a, qf[ks], s[kb]);
       }
     }
-    // scale into the log2 domain and mask; key of (kb, r) = kb*32 + (r/4)*8 + hi*4 + r%4
+    // Mask (key of (kb, r) = kbase + kb*32 + (r/4)*8 + hi*4 + r%4), then the
+    // row max of this tile over both lanes of the row (scores are raw here;
+    // the softmax scale is folded into the exponent below).
     const bool need_mask = is_cross ? (kbase + kKeyTile > cs.len) : true;
+    if (need_mask) {
+      const int lo = is_cross ? 0 : seg_lo;
+      const int hi_k = is_cross ? cs.len - 1 : self_q;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kbase + kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+          s[kb][r] = (key >= lo && key <= hi_k) ? s[kb][r] : -INFINITY;
+        }
+    }
     float mt = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[kb][r] * p.scale_log2;
-        if (need_mask) {
-          const int key = kbase + kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-          const bool vis = is_cross ? (key < cs.len) : (key >= seg_lo && key <= self_q);
-          x = vis ? x : -INFINITY;
-        }
-        s[kb][r] = x;
-        mt = fmaxf(mt, x);
-      }
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * p.scale_log2;
+    // Lazy rescale: the running reference m_run moves only when a row's max
+    // exceeds it by more than 8 (log2 units), so P stays below 2^8 and the
+    // O accumulator is rescaled only on those (rare, wave-uniform) tiles.
+    // The final O / l and the LSE are exact for any reference.
+    if (__ballot(mt > m_run + 8.0f) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first visible tile
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[cb][r] *= alpha;
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[cb][r] *= alpha;
+    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
 
     // P (bf16) as the B operand: k-step (kb, sp) takes regs 8*sp .. 8*sp+7
     bf16x8_t pb[2][2];
@@ -279,8 +288,8 @@ attn_bf16_kernel(AttnParams p) {
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = exp2f(s[kb][sp * 8 + 2 * e] - m_use);
-          const float p1 = exp2f(s[kb][sp * 8 + 2 * e + 1] - m_use);
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][sp * 8 + 2 * e], p.scale_log2, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][sp * 8 + 2 * e + 1], p.scale_log2, -m_use));
           l_run += p0 + p1;
           w[e] = pack_bf16x2(p0, p1);
         }
@@ -325,16 +334,249 @@ attn_bf16_kernel(AttnParams p) {
   }
 }
 
-hipError_t launch_attn_bf16(const AttnParams& p, int group, hipStream_t s) {
+// ----------------------------------------------------------------------------
+// bf16-only kernel with direct HBM->LDS loads (both key sources bf16).
+//
+// K and V tiles are copied from HBM straight into LDS by global_load_lds
+// (16 B per lane, no staging registers), double-buffered: the copy of tile
+// i+1 is in flight while tile i is computed. Rows are 256 B; each row's 16-B
+// chunks are XOR-swizzled so that the MFMA operand reads are free of bank
+// conflicts. V stays in its natural [key][dim] layout and the transposed A
+// operand of O^T += V^T P^T comes from ds_read_tr16_b64: within a 16-lane
+// block, lane 4a+b receives element b of the rows addressed by lanes a, a+4,
+// a+8, a+12; pointing lane s at V[K0 + s/4][D0 + 4(s%4)] hands lane j the four
+// keys K0..K0+3 of dim D0 + j.
+// ----------------------------------------------------------------------------
+constexpr int kRowElems = kHeadDim;                 // 128 bf16 = 256 B per key row
+constexpr int kTileElems = kKeyTile * kRowElems;    // 8192 bf16 = 16 KB
+
+__device__ __forceinline__ int swz_k(int key, int chunk) { return chunk ^ (key & 7); }
+__device__ __forceinline__ int swz_v(int key, int chunk) { return chunk ^ ((key & 3) << 1); }
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ v4i16_t lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (v4i16_t __attribute__((address_space(3)))*)(__attribute__((address_space(3))) char*)p);
+}
+
+// Issue the direct copies of one 64-key tile (K and V) of kv head g into the
+// LDS stage `kd`/`vd`. Each wave copies 16/NW 1-KB slices (4 rows each) of K
+// and of V; rows at or past the source length are clamped (masked later).
+template <int NW>
+__device__ __forceinline__ void issue_tile(const KVSrc& src, int g, int kbase, uint16_t* kd,
+                                           uint16_t* vd, int wave, int lane) {
+  constexpr int PER_WAVE = 16 / NW;
+  const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(src.k) + (int64_t)g * src.head_stride * 2;
+  const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(src.v) + (int64_t)g * src.head_stride * 2;
+  const int64_t tb = src.tok_stride * 2;
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int slice = wave * PER_WAVE + i;          // 4 rows per slice
+    const int row = slice * 4 + (lane >> 4);
+    const int key = min(kbase + row, src.len - 1);
+    const int slot = lane & 15;
+    __builtin_amdgcn_global_load_lds(kb8 + key * tb + swz_k(row, slot) * 16,
+                                     (lds_void_t*)(kd + slice * 4 * kRowElems), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vb8 + key * tb + swz_v(row, slot) * 16,
+                                     (lds_void_t*)(vd + slice * 4 * kRowElems), 16, 0, 0);
+  }
+}
+
+template <int G>
+__global__ void __launch_bounds__(64 * (G >= 4 ? G : 4), 2)
+attn_direct_kernel(AttnParams p) {
+  constexpr int NW = G >= 4 ? G : 4;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][kTileElems];   // [stage][K,V]
+
+  const int64_t total = (int64_t)p.n_tiles * p.hkv;
+  const int64_t wid = xcd_remap(blockIdx.x, total);
+  if (wid < 0) return;
+  const int g = (int)(wid / p.n_tiles);
+  const AttnTile tile = p.tiles[wid % p.n_tiles];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int head = g * G + (wave % G);
+  const int tg = wave / G;
+  const int qrow = tg * kQRows + l32;
+  const bool row_ok = qrow < tile.nq;
+  const int64_t tok = (int64_t)tile.q0 + qrow;
+
+  KVSrc cs{}, ss{};
+  int n_ct = 0, n_st = 0;
+  if (tile.cross >= 0) { cs = p.srcs[tile.cross]; n_ct = (cs.len + kKeyTile - 1) / kKeyTile; }
+  if (tile.self >= 0) {
+    ss = p.srcs[tile.self];
+    n_st = max(0, (tile.self_qbase + tile.nq - tile.self_k0 + kKeyTile - 1) / kKeyTile);
+  }
+  const int n_tiles = n_ct + n_st;
+  auto src_of = [&](int it) -> const KVSrc& { return it < n_ct ? cs : ss; };
+  auto kbase_of = [&](int it) { return it < n_ct ? it * kKeyTile : tile.self_k0 + (it - n_ct) * kKeyTile; };
+
+  if (n_tiles > 0) issue_tile<NW>(src_of(0), g, kbase_of(0), lds[0][0], lds[0][1], wave, lane);
+
+  bf16x8_t qf[8];
+  {
+    const uint16_t* qp = p.q + tok * p.q_stride + head * kHeadDim + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
+      qf[ks] = bitcast<bf16x8_t>(u);
+    }
+  }
+  const int seg_lo = row_ok ? p.seg_lo[tok] : 0x7FFFFFFF;
+  const int self_q = tile.self_qbase + qrow;
+
+  f32x16_t o[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[cb][r] = 0.0f;
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+
+  // tr-read addressing (per lane, fixed): block B = lane/16, j = lane%16
+  const int trB = lane >> 4, trj = lane & 15;
+  const int tr_key_off = trj >> 2;                    // + K0
+  const int tr_d0 = 16 * (trB & 1) + 4 * (trj & 3);   // + cb*32
+
+  for (int it = 0; it < n_tiles; ++it) {
+    const int st = it & 1;
+    const bool is_cross = it < n_ct;
+    const int kbase = kbase_of(it);
+    // One barrier per tile. Its fence waits for this wave's outstanding
+    // copies (those of tile it) and the barrier then guarantees (a) every
+    // wave's copies of tile it have landed and (b) every wave has finished
+    // reading stage st^1 in the previous iteration, so it may be refilled.
+    __syncthreads();
+    if (it + 1 < n_tiles)
+      issue_tile<NW>(src_of(it + 1), g, kbase_of(it + 1), lds[st ^ 1][0], lds[st ^ 1][1], wave, lane);
+    const uint16_t* Kt = lds[st][0];
+    const uint16_t* Vt = lds[st][1];
+
+    f32x16_t s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+      const int key = kb * 32 + l32;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const uint16_t* a_p = Kt + key * kRowElems + swz_k(key, ks * 2 + hi) * 8;
+        bf16x8_t a = bitcast<bf16x8_t>(*reinterpret_cast<const uint4*>(a_p));
+        s[kb] = mfma_32x32x16(a, qf[ks], s[kb]);
+      }
+    }
+    const bool need_mask = is_cross ? (kbase + kKeyTile > cs.len) : true;
+    if (need_mask) {
+      const int lo = is_cross ? 0 : seg_lo;
+      const int hi_k = is_cross ? cs.len - 1 : self_q;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kbase + kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+          s[kb][r] = (key >= lo && key <= hi_k) ? s[kb][r] : -INFINITY;
+        }
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * p.scale_log2;
+    if (__ballot(mt > m_run + 8.0f) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[cb][r] *= alpha;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+
+    bf16x8_t pb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][sp * 8 + 2 * e], p.scale_log2, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][sp * 8 + 2 * e + 1], p.scale_log2, -m_use));
+          l_run += p0 + p1;
+          w[e] = pack_bf16x2(p0, p1);
+        }
+        pb[kb][sp] = bitcast<bf16x8_t>(make_uint4(w[0], w[1], w[2], w[3]));
+      }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int d0 = cb * 32 + tr_d0;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+          const int k0 = kb * 32 + sp * 16 + hi * 4 + tr_key_off;
+          const int k1 = k0 + 8;
+          const v4i16_t lo4 = lds_read_tr16(Vt + k0 * kRowElems + swz_v(k0, d0 >> 3) * 8 + (d0 & 7));
+          const v4i16_t hi4 = lds_read_tr16(Vt + k1 * kRowElems + swz_v(k1, d0 >> 3) * 8 + (d0 & 7));
+          const uint2 a_lo = __builtin_bit_cast(uint2, lo4);
+          const uint2 a_hi = __builtin_bit_cast(uint2, hi4);
+          bf16x8_t a = bitcast<bf16x8_t>(make_uint4(a_lo.x, a_lo.y, a_hi.x, a_hi.y));
+          o[cb] = mfma_32x32x16(a, pb[kb][sp], o[cb]);
+        }
+    }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (!row_ok) return;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  uint16_t* op = p.out + tok * p.o_stride + head * kHeadDim + hi * 4;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      uint2 w;
+      w.x = pack_bf16x2(o[cb][rg * 4 + 0] * inv, o[cb][rg * 4 + 1] * inv);
+      w.y = pack_bf16x2(o[cb][rg * 4 + 2] * inv, o[cb][rg * 4 + 3] * inv);
+      *reinterpret_cast<uint2*>(op + cb * 32 + rg * 8) = w;
+    }
+  if (p.lse != nullptr && hi == 0) {
+    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+    const float L = l_tot > 0.0f ? (m_use + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    p.lse[tok * p.hq + head] = L;
+  }
+}
+
+hipError_t launch_attn_bf16(const AttnParams& p, int group, bool any_fp8, hipStream_t s) {
   if (p.n_tiles == 0) return hipSuccess;
   const int64_t total = (int64_t)p.n_tiles * p.hkv;
   const int64_t grid = (total + 7) / 8 * 8;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 gr((unsigned)grid);
+  if (!any_fp8) {
+    switch (group) {
+      case 1: attn_direct_kernel<1><<<gr, dim3(256), 0, s>>>(p); break;
+      case 2: attn_direct_kernel<2><<<gr, dim3(256), 0, s>>>(p); break;
+      case 4: attn_direct_kernel<4><<<gr, dim3(256), 0, s>>>(p); break;
+      case 8: attn_direct_kernel<8><<<gr, dim3(512), 0, s>>>(p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (group) {
-    case 1: attn_bf16_kernel<1><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p); break;
-    case 2: attn_bf16_kernel<2><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p); break;
-    case 4: attn_bf16_kernel<4><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p); break;
-    case 8: attn_bf16_kernel<8><<<dim3((unsigned)grid), dim3(512), 0, s>>>(p); break;
+    case 1: attn_bf16_kernel<1><<<gr, dim3(256), 0, s>>>(p); break;
+    case 2: attn_bf16_kernel<2><<<gr, dim3(256), 0, s>>>(p); break;
+    case 4: attn_bf16_kernel<4><<<gr, dim3(256), 0, s>>>(p); break;
+    case 8: attn_bf16_kernel<8><<<gr, dim3(512), 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

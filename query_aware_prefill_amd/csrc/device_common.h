@@ -11,15 +11,15 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-// float -> bf16 bits, round to nearest, ties to even (inputs are finite).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two floats -> two bf16 (round to nearest, ties to even) packed in a word:
+// one v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  return pack_bf16x2(x, 0.0f) & 0xFFFFu;
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {

@@ -456,7 +456,7 @@ quail_status run_batch(quail_ctx* c, const Batch& b, const int32_t* tokens, uint
     ap.hq = Hq; ap.hkv = Hkv;
     ap.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)kHeadDim));
     ap.k_scale = cf.k_scale; ap.v_scale = cf.v_scale;
-    HIP_TRY(launch_attn_bf16(ap, G, s));
+    HIP_TRY(launch_attn_bf16(ap, G, cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3, s));
 
     GemmParams go{};
     go.A = obuf; go.lda = (int64_t)Hq * kHeadDim; go.B = lw.w_o; go.scale = lw.s_o;
@@ -1134,7 +1134,7 @@ quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t 
   p.lse = lse; p.hq = hq; p.hkv = hkv;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
   p.k_scale = 1.0f; p.v_scale = 1.0f;
-  HIP_TRY(launch_attn_bf16(p, G, st));
+  HIP_TRY(launch_attn_bf16(p, G, false, st));
   return QUAIL_OK;
 }
 

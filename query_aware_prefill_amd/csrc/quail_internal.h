@@ -113,7 +113,9 @@ struct Head8Params {
 };
 
 // ---- launchers (return the launch's hipError_t) ----
-hipError_t launch_attn_bf16(const AttnParams& p, int group, hipStream_t s);
+// any_fp8: some key source of this launch holds E4M3 codes (register-staged
+// kernel); otherwise the direct HBM->LDS kernel runs.
+hipError_t launch_attn_bf16(const AttnParams& p, int group, bool any_fp8, hipStream_t s);
 hipError_t launch_attn_f32(const AttnF32Params& p, hipStream_t s);
 hipError_t launch_gemm(const GemmParams& p, GemmEpi epi, hipStream_t s);
 hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s);
