@@ -21,6 +21,16 @@ Reported:
              on a time-bounded sample of the same pairs, scaled to tokens/min.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Secondary measurements (not the headline line; each prints its own JSON):
+  --workload gemm    the four W8A16 projection shapes of the Qwen3-4B layer
+                     (QKV 6144x2560, O 2560x4096, gate/up 19456x2560, down
+                     2560x9728) at M = 65536 tokens, TFLOP/s against the bf16
+                     MFMA peak.
+  --workload layer   one decoder layer of the Qwen3-4B shape, random-init fp8
+                     weights: 16 anchors x 1024 tokens, 512 suffixes x 64
+                     tokens per anchor, run end to end by quail_join_run
+                     (plan, anchor prefill + KV writer, join prefill, head).
 """
 from __future__ import annotations
 
@@ -94,6 +104,90 @@ def cpu_baseline(case, budget_s=15.0):
                       f"({logical} logical / {computed} suffix tokens in {spent:.1f} s of oracle compute)"}
 
 
+def bench_gemm(args):
+    import torch
+    import workloads as W
+    from query_aware_prefill_amd import binding as B
+    from query_aware_prefill_amd.device import to_device
+    B.load()
+    M = 65536
+    r = np.random.default_rng(0)
+    out = {"metric": "W8A16 GEMM TFLOP/s", "unit": "TFLOP/s", "M": M, "shapes": {}}
+    x_full = torch.randn((M, 9728), device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    for name, (N, K) in {"qkv": (6144, 2560), "o": (2560, 4096), "gate_up": (19456, 2560),
+                         "down": (2560, 9728)}.items():
+        x = x_full[:, :K].contiguous()
+        w = to_device(W.draw_fp8_codes(r, (N, K)))
+        sc = to_device(W.bf16_bits_from_f32((0.0002 * (1 + r.random(N))).astype(np.float32)))
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        for _ in range(args.warmup):
+            B.quail_gemm_w8a16(x, w, sc, y)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record()
+            B.quail_gemm_w8a16(x, w, sc, y)
+            b.record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        out["shapes"][name] = {"N": N, "K": K, "ms": ms, "tflops": tf, "frac": tf / PEAK_BF16_TFLOPS}
+        log(f"gemm {name} {M}x{N}x{K}: {ms:.3f} ms, {tf:.1f} TFLOP/s")
+    print(json.dumps(out), flush=True)
+
+
+def bench_layer(args):
+    import torch
+    import workloads as W
+    from query_aware_prefill_amd import binding as B
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    B.load()
+    shape = W.ModelShape(n_layers=1, hidden=2560, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                         intermediate=9728, vocab=W.QWEN3_4B.vocab)
+    log("generating one layer of random-init weights")
+    wts = W.model_weights(shape, 0)
+    case = W.c2_case(seed=2)
+    n_pairs = len(case["pair_anchor"])
+    dm = DeviceModel(shape, wts, max_anchor_len=1024, max_suffix_len=64)
+    T = 65536
+    pool = 16 * B.quail_anchor_bytes(dm.cfg, 1024) + (1 << 20)
+    ctx = dm.context(pool, T)
+    a_tok, s_tok = to_device(case["a_tok"]), to_device(case["s_tok"])
+    logits = torch.empty((n_pairs, 8), dtype=torch.float32, device="cuda")
+    dec = torch.empty(n_pairs, dtype=torch.uint8, device="cuda")
+
+    def step():
+        B.quail_join_run(ctx, a_tok, case["a_off"], case["pair_anchor"], s_tok, case["s_off"], 0x0F,
+                         logits, None, dec)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    anchor_tok = int(np.sum(case["a_len"]))
+    suffix_tok = int(np.sum(case["s_len"]))
+    logical = int(np.sum(case["a_len"][case["pair_anchor"]]) + suffix_tok)
+    # executed algorithmic work: suffix tokens run the whole layer (201.85
+    # MFLOP/token of projections); with one layer, the anchors' last layer only
+    # needs its K/V, i.e. the QKV projection (31.46 MFLOP/token).
+    gemm_flops = 201_850_880.0 * suffix_tok + 31_457_280.0 * anchor_tok
+    attn_flops = 16384.0 * (np.sum(case["s_len"] * case["a_len"][case["pair_anchor"]]) +
+                            np.sum(case["s_len"] * (case["s_len"] + 1) / 2))
+    st = B.quail_pool_stats(ctx)
+    res = {"metric": "decoder-layer join prefill", "unit": "tokens/min", "ms_per_step": ms,
+           "logical_tokens_per_min": logical / (ms * 1e-3) * 60, "computed_tokens_per_min":
+           (anchor_tok + suffix_tok) / (ms * 1e-3) * 60, "pairs": n_pairs,
+           "algorithmic_tflops": (gemm_flops + attn_flops) / (ms * 1e-3) / 1e12,
+           "pool": st}
+    log(f"layer: {ms:.2f} ms/step, {res['algorithmic_tflops']:.1f} TFLOP/s algorithmic")
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,12 +195,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--workload", choices=["cascade", "gemm", "layer"], default="cascade")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(pairs grouped by anchor shard across GPUs with no communication but the "
               "1-byte decisions; see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "gemm":
+        return bench_gemm(args)
+    if args.workload == "layer":
+        return bench_layer(args)
 
     import torch
     import workloads as W

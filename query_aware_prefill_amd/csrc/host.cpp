@@ -292,6 +292,7 @@ struct quail_ctx {
   size_t resident = 0, peak = 0;
   int64_t prefills = 0, evictions = 0, regret = 0;
   std::unordered_set<int64_t> seen_ids;
+  int64_t run_serial = 0;            // quail_join_run calls (namespaces their anchor ids)
 
   Blob blob;
 
@@ -951,6 +952,9 @@ quail_status quail_join_run(quail_ctx* c, int32_t n_anchors, const int32_t* a_to
   }
   std::vector<quail_anchor> handle(n_anchors, QUAIL_NO_ANCHOR);
   size_t next_fresh = 0;                      // next anchor (in first-use order) to prefill
+  // anchor ids are this call's anchor indices, namespaced by the call, so that
+  // regret counts re-prefills within one plan only
+  const int64_t id_base = (++c->run_serial) << 32;
   hipStream_t s = as_stream(stream);
   uint16_t* hl = ws_ptr<uint16_t>(c, c->L.hlast);
   for (size_t st = 0; st + 1 < plan.bounds.size(); ++st) {
@@ -982,7 +986,7 @@ quail_status quail_join_run(quail_ctx* c, int32_t n_anchors, const int32_t* a_to
         st_.push_back(a_offsets[a]);
         ln.push_back(alen[a]);
         nu.push_back(uses[a]);
-        ids.push_back(a);
+        ids.push_back(id_base | a);
         tok += alen[a];
         bytes += slab[a];
         ++next_fresh;

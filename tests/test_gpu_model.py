@@ -189,6 +189,14 @@ def test_join_run_end_to_end(B):
     st = B.quail_pool_stats(ctx)
     used = len({a for a, _ in pairs if a >= 0})
     assert st["prefills"] == used and st["evictions"] == used and st["regret_tokens"] == 0
+    # a second, identical query on the same context is a new plan: no regret
+    dec2 = torch.empty(n, dtype=torch.uint8, device="cuda")
+    B.quail_join_run(ctx, a_tok, case["a_off"], case["pair_anchor"], s_tok, case["s_off"], 0x0F,
+                     None, None, dec2)
+    torch.cuda.synchronize()
+    assert np.array_equal(dec2.cpu().numpy(), dec.cpu().numpy())
+    st = B.quail_pool_stats(ctx)
+    assert st["prefills"] == 2 * used and st["regret_tokens"] == 0 and st["resident"] == 0
 
 
 def test_qwen3_shaped_layer(B):
