@@ -27,6 +27,8 @@ Secondary measurements (not the headline line; each prints its own JSON):
                      (QKV 6144x2560, O 2560x4096, gate/up 19456x2560, down
                      2560x9728) at M = 65536 tokens, TFLOP/s against the bf16
                      MFMA peak.
+  --workload copy    a plain 4 GiB device-to-device copy (read 4 GiB, write
+                     4 GiB): the calibration kernel for the HBM byte counters.
   --workload layer   one decoder layer of the Qwen3-4B shape, random-init fp8
                      weights: 16 anchors x 1024 tokens, 512 suffixes x 64
                      tokens per anchor, run end to end by quail_join_run
@@ -53,6 +55,31 @@ METRIC = "prefill tokens/min per GPU on join workload; cascade-attn TFLOP/s vs M
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cascade_attn_c1_hbm_traffic.txt")
+KERNEL_SOURCES = ["query_aware_prefill_amd/csrc/attn.hip", "query_aware_prefill_amd/csrc/device_common.h",
+                  "query_aware_prefill_amd/csrc/quail_internal.h"]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernel sources have changed since the counters were taken."""
+    import hashlib
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+        h = hashlib.sha256()
+        for f in KERNEL_SOURCES:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest() != kv.get("kernel_sources_sha256"):
+            return None
+        return float(kv["traffic_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def algorithmic_flops(a_len, s_anchor, s_len, hq=32, d=128):
@@ -132,9 +159,44 @@ def bench_gemm(args):
         torch.cuda.synchronize()
         ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
         tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-        out["shapes"][name] = {"N": N, "K": K, "ms": ms, "tflops": tf, "frac": tf / PEAK_BF16_TFLOPS}
-        log(f"gemm {name} {M}x{N}x{K}: {ms:.3f} ms, {tf:.1f} TFLOP/s")
+        # context only: the vendor library's plain bf16 GEMM of the same shape
+        # (bf16 weights; not the W8A16 operation measured above)
+        wb = torch.randn((N, K), device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        for _ in range(args.warmup):
+            torch.matmul(x, wb.t())
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True); t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(args.steps):
+            torch.matmul(x, wb.t())
+        t1.record()
+        torch.cuda.synchronize()
+        ref_ms = t0.elapsed_time(t1) / args.steps
+        del wb
+        out["shapes"][name] = {"N": N, "K": K, "ms": ms, "tflops": tf, "frac": tf / PEAK_BF16_TFLOPS,
+                               "torch_bf16_matmul_tflops": 2.0 * M * N * K / (ref_ms * 1e-3) / 1e12}
+        log(f"gemm {name} {M}x{N}x{K}: {ms:.3f} ms, {tf:.1f} TFLOP/s "
+            f"(torch bf16 matmul {out['shapes'][name]['torch_bf16_matmul_tflops']:.1f})")
     print(json.dumps(out), flush=True)
+
+
+def bench_copy(args):
+    import torch
+    n = 4 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    print(json.dumps({"metric": "device copy", "bytes_read": n, "bytes_written": n, "ms": ms,
+                      "GB/s": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
 def bench_layer(args):
@@ -195,7 +257,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--workload", choices=["cascade", "gemm", "layer"], default="cascade")
+    ap.add_argument("--workload", choices=["cascade", "gemm", "layer", "copy"], default="cascade")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -207,6 +269,8 @@ def main():
         return bench_gemm(args)
     if args.workload == "layer":
         return bench_layer(args)
+    if args.workload == "copy":
+        return bench_copy(args)
 
     import torch
     import workloads as W
@@ -282,8 +346,8 @@ def main():
         },
         "roofline": {
             "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-            "kernel": "quail::attn_bf16_kernel<4>", "flops_per_launch": flops,
+            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
+            "kernel": "quail::attn_direct_kernel<4>", "flops_per_launch": flops,
             "launch_ms": kernel_ms,
             "algorithmic_bytes_per_launch": algorithmic_bytes(a_len, s_len),
         },

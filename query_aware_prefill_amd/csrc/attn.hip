@@ -338,7 +338,9 @@ attn_bf16_kernel(AttnParams p) {
 // bf16-only kernel with direct HBM->LDS loads (both key sources bf16).
 //
 // K and V tiles are copied from HBM straight into LDS by global_load_lds
-// (16 B per lane, no staging registers), double-buffered: the copy of tile
+// (16 B per lane, no staging registers; issued as inline asm so the compiler
+// does not make the operand reads wait for copies in flight), double-buffered:
+// the copy of tile
 // i+1 is in flight while tile i is computed. Rows are 256 B; each row's 16-B
 // chunks are XOR-swizzled so that the MFMA operand reads are free of bank
 // conflicts. V stays in its natural [key][dim] layout and the transposed A
@@ -377,10 +379,8 @@ __device__ __forceinline__ void issue_tile(const KVSrc& src, int g, int kbase, u
     const int row = slice * 4 + (lane >> 4);
     const int key = min(kbase + row, src.len - 1);
     const int slot = lane & 15;
-    __builtin_amdgcn_global_load_lds(kb8 + key * tb + swz_k(row, slot) * 16,
-                                     (lds_void_t*)(kd + slice * 4 * kRowElems), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vb8 + key * tb + swz_v(row, slot) * 16,
-                                     (lds_void_t*)(vd + slice * 4 * kRowElems), 16, 0, 0);
+    copy16_to_lds(kb8 + key * tb + swz_k(row, slot) * 16, kd + slice * 4 * kRowElems);
+    copy16_to_lds(vb8 + key * tb + swz_v(row, slot) * 16, vd + slice * 4 * kRowElems);
   }
 }
 

@@ -94,6 +94,33 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane i writes
+// lds_base + 16*i (gfx950 global_load_lds_dwordx4; lds_base is wave-uniform).
+// Issued through inline asm so that the compiler does not treat every later
+// LDS read as a possible alias of the copy and wait for all copies in flight;
+// callers wait explicitly (s_waitcnt vmcnt) before the barrier that publishes
+// the data.
+__device__ __forceinline__ void copy16_to_lds(const void* gptr, const void* lds_base) {
+  // the low 32 bits of a generic pointer into LDS are its LDS offset (no null
+  // check needed: lds_base always points into a __shared__ array)
+  const uint32_t lds = (uint32_t)reinterpret_cast<uintptr_t>(lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Workgroup id remapped so that each of the 8 XCDs (which receive workgroups
 // round-robin) processes one contiguous range of logical ids. Returns -1 for
 // the padding ids of a grid rounded up to a multiple of 8.
