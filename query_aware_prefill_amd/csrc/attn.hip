@@ -347,13 +347,19 @@ attn_bf16_kernel(AttnParams p) {
 // operand of O^T += V^T P^T comes from ds_read_tr16_b64: within a 16-lane
 // block, lane 4a+b receives element b of the rows addressed by lanes a, a+4,
 // a+8, a+12; pointing lane s at V[K0 + s/4][D0 + 4(s%4)] hands lane j the four
-// keys K0..K0+3 of dim D0 + j.
+// keys K0..K0+3 of dim D0 + j. Swizzles are chosen for gfx950's 64-bank LDS
+// (measured: with a 32-bank layout half of all LDS cycles were conflicts).
 // ----------------------------------------------------------------------------
 constexpr int kRowElems = kHeadDim;                 // 128 bf16 = 256 B per key row
 constexpr int kTileElems = kKeyTile * kRowElems;    // 8192 bf16 = 16 KB
 
-__device__ __forceinline__ int swz_k(int key, int chunk) { return chunk ^ (key & 7); }
-__device__ __forceinline__ int swz_v(int key, int chunk) { return chunk ^ ((key & 3) << 1); }
+// LDS serves 64 banks x 4 B per cycle: 16 lanes of a 16-B read, 32 lanes of an
+// 8-B read. K: the 16 rows one ds_read_b128 cycle touches (same chunk) land
+// on 16 distinct chunks. V: one ds_read_tr16_b64 cycle reads 4 consecutive
+// rows x 64 B (4 chunks); shifting each row's chunks by 4*(row % 4) puts the
+// four rows on disjoint 64-B bank groups.
+__device__ __forceinline__ int swz_k(int key, int chunk) { return chunk ^ (key & 15); }
+__device__ __forceinline__ int swz_v(int key, int chunk) { return chunk ^ ((key & 3) << 2); }
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -384,10 +390,14 @@ __device__ __forceinline__ void issue_tile(const KVSrc& src, int g, int kbase, u
   }
 }
 
-template <int G>
-__global__ void __launch_bounds__(64 * (G >= 4 ? G : 4), 2)
+// QB = 32-row query blocks per wave. QB = 2 makes every K/V fragment read from
+// LDS feed two MFMAs (half the LDS traffic per FLOP) at the cost of one wave
+// per SIMD; QB = 1 keeps two workgroups per CU.
+template <int G, int QB>
+__global__ void __launch_bounds__(64 * (G >= 4 ? G : 4), QB == 1 ? 2 : 1)
 attn_direct_kernel(AttnParams p) {
   constexpr int NW = G >= 4 ? G : 4;
+  constexpr int ROWS = kQRows * QB;                   // query tokens per wave
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][kTileElems];   // [stage][K,V]
 
   const int64_t total = (int64_t)p.n_tiles * p.hkv;
@@ -403,9 +413,6 @@ attn_direct_kernel(AttnParams p) {
   const int hi = lane >> 5;
   const int head = g * G + (wave % G);
   const int tg = wave / G;
-  const int qrow = tg * kQRows + l32;
-  const bool row_ok = qrow < tile.nq;
-  const int64_t tok = (int64_t)tile.q0 + qrow;
 
   KVSrc cs{}, ss{};
   int n_ct = 0, n_st = 0;
@@ -420,30 +427,40 @@ attn_direct_kernel(AttnParams p) {
 
   if (n_tiles > 0) issue_tile<NW>(src_of(0), g, kbase_of(0), lds[0][0], lds[0][1], wave, lane);
 
-  bf16x8_t qf[8];
-  {
-    const uint16_t* qp = p.q + tok * p.q_stride + head * kHeadDim + hi * 8;
+  // per 32-row block: query row of this lane
+  int qrow[QB], seg_lo[QB], self_q[QB];
+  bool row_ok[QB];
+  int64_t tok[QB];
+  bf16x8_t qf[QB][8];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    qrow[qb] = tg * ROWS + qb * kQRows + l32;
+    row_ok[qb] = qrow[qb] < tile.nq;
+    tok[qb] = (int64_t)tile.q0 + qrow[qb];
+    const uint16_t* qp = p.q + tok[qb] * p.q_stride + head * kHeadDim + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
-      qf[ks] = bitcast<bf16x8_t>(u);
+      uint4 u = row_ok[qb] ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
+      qf[qb][ks] = bitcast<bf16x8_t>(u);
     }
+    seg_lo[qb] = row_ok[qb] ? p.seg_lo[tok[qb]] : 0x7FFFFFFF;
+    self_q[qb] = tile.self_qbase + qrow[qb];
   }
-  const int seg_lo = row_ok ? p.seg_lo[tok] : 0x7FFFFFFF;
-  const int self_q = tile.self_qbase + qrow;
 
-  f32x16_t o[4];
+  f32x16_t o[QB][4];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[cb][r] = 0.0f;
-  float m_run = -INFINITY;
-  float l_run = 0.0f;
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[qb][cb][r] = 0.0f;
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.0f; }
 
-  // tr-read addressing (per lane, fixed): block B = lane/16, j = lane%16
   const int trB = lane >> 4, trj = lane & 15;
-  const int tr_key_off = trj >> 2;                    // + K0
-  const int tr_d0 = 16 * (trB & 1) + 4 * (trj & 3);   // + cb*32
+  const int tr_key_off = trj >> 2;
+  const int tr_d0 = 16 * (trB & 1) + 4 * (trj & 3);
 
   for (int it = 0; it < n_tiles; ++it) {
     const int st = it & 1;
@@ -459,64 +476,72 @@ attn_direct_kernel(AttnParams p) {
     const uint16_t* Kt = lds[st][0];
     const uint16_t* Vt = lds[st][1];
 
-    f32x16_t s[2];
+    f32x16_t s[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
       const int key = kb * 32 + l32;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const uint16_t* a_p = Kt + key * kRowElems + swz_k(key, ks * 2 + hi) * 8;
-        bf16x8_t a = bitcast<bf16x8_t>(*reinterpret_cast<const uint4*>(a_p));
-        s[kb] = mfma_32x32x16(a, qf[ks], s[kb]);
+        const bf16x8_t a = bitcast<bf16x8_t>(*reinterpret_cast<const uint4*>(a_p));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma_32x32x16(a, qf[qb][ks], s[qb][kb]);
       }
     }
     const bool need_mask = is_cross ? (kbase + kKeyTile > cs.len) : true;
-    if (need_mask) {
-      const int lo = is_cross ? 0 : seg_lo;
-      const int hi_k = is_cross ? cs.len - 1 : self_q;
+    bf16x8_t pb[QB][2][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (need_mask) {
+        const int lo = is_cross ? 0 : seg_lo[qb];
+        const int hi_k = is_cross ? cs.len - 1 : self_q[qb];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kbase + kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+            s[qb][kb][r] = (key >= lo && key <= hi_k) ? s[qb][kb][r] : -INFINITY;
+          }
+      }
+      float mt = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kbase + kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-          s[kb][r] = (key >= lo && key <= hi_k) ? s[kb][r] : -INFINITY;
-        }
-    }
-    float mt = -INFINITY;
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[qb][kb][r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * p.scale_log2;
+      // lazy rescale (see the register-staged kernel)
+      if (__ballot(mt > m_run[qb] + 8.0f) != 0) {
+        const float m_new = fmaxf(m_run[qb], mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * p.scale_log2;
-    if (__ballot(mt > m_run + 8.0f) != 0) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[cb][r] *= alpha;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-
-    bf16x8_t pb[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int sp = 0; sp < 2; ++sp) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][sp * 8 + 2 * e], p.scale_log2, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][sp * 8 + 2 * e + 1], p.scale_log2, -m_use));
-          l_run += p0 + p1;
-          w[e] = pack_bf16x2(p0, p1);
-        }
-        pb[kb][sp] = bitcast<bf16x8_t>(make_uint4(w[0], w[1], w[2], w[3]));
+          for (int r = 0; r < 16; ++r) o[qb][cb][r] *= alpha;
       }
+      const float m_use = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][sp * 8 + 2 * e], p.scale_log2, -m_use));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][sp * 8 + 2 * e + 1], p.scale_log2, -m_use));
+            l_run[qb] += p0 + p1;
+            w[e] = pack_bf16x2(p0, p1);
+          }
+          pb[qb][kb][sp] = bitcast<bf16x8_t>(make_uint4(w[0], w[1], w[2], w[3]));
+        }
+    }
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       const int d0 = cb * 32 + tr_d0;
@@ -530,30 +555,44 @@ attn_direct_kernel(AttnParams p) {
           const v4i16_t hi4 = lds_read_tr16(Vt + k1 * kRowElems + swz_v(k1, d0 >> 3) * 8 + (d0 & 7));
           const uint2 a_lo = __builtin_bit_cast(uint2, lo4);
           const uint2 a_hi = __builtin_bit_cast(uint2, hi4);
-          bf16x8_t a = bitcast<bf16x8_t>(make_uint4(a_lo.x, a_lo.y, a_hi.x, a_hi.y));
-          o[cb] = mfma_32x32x16(a, pb[kb][sp], o[cb]);
+          const bf16x8_t a = bitcast<bf16x8_t>(make_uint4(a_lo.x, a_lo.y, a_hi.x, a_hi.y));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) o[qb][cb] = mfma_32x32x16(a, pb[qb][kb][sp], o[qb][cb]);
         }
     }
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (!row_ok) return;
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  uint16_t* op = p.out + tok * p.o_stride + head * kHeadDim + hi * 4;
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
+    if (!row_ok[qb]) continue;
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    uint16_t* op = p.out + tok[qb] * p.o_stride + head * kHeadDim + hi * 4;
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      uint2 w;
-      w.x = pack_bf16x2(o[cb][rg * 4 + 0] * inv, o[cb][rg * 4 + 1] * inv);
-      w.y = pack_bf16x2(o[cb][rg * 4 + 2] * inv, o[cb][rg * 4 + 3] * inv);
-      *reinterpret_cast<uint2*>(op + cb * 32 + rg * 8) = w;
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        uint2 w;
+        w.x = pack_bf16x2(o[qb][cb][rg * 4 + 0] * inv, o[qb][cb][rg * 4 + 1] * inv);
+        w.y = pack_bf16x2(o[qb][cb][rg * 4 + 2] * inv, o[qb][cb][rg * 4 + 3] * inv);
+        *reinterpret_cast<uint2*>(op + cb * 32 + rg * 8) = w;
+      }
+    if (p.lse != nullptr && hi == 0) {
+      const float m_use = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
+      const float L = l_tot > 0.0f ? (m_use + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+      p.lse[tok[qb] * p.hq + head] = L;
     }
-  if (p.lse != nullptr && hi == 0) {
-    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-    const float L = l_tot > 0.0f ? (m_use + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-    p.lse[tok * p.hq + head] = L;
   }
+}
+
+int attn_rows_per_wave(int group, bool any_fp8) {
+  static const int qb = [] {
+    const char* e = getenv("QUAIL_ATTN_QB");
+    return (e && atoi(e) == 2) ? 2 : 1;
+  }();
+  // fp8 sources use the register-staged kernel; 8-wave workgroups keep QB = 1
+  // (two 32-row blocks would not fit the register file at 512 threads)
+  return (any_fp8 || group == 8) ? kQRows : kQRows * qb;
 }
 
 hipError_t launch_attn_bf16(const AttnParams& p, int group, bool any_fp8, hipStream_t s) {
@@ -563,11 +602,15 @@ hipError_t launch_attn_bf16(const AttnParams& p, int group, bool any_fp8, hipStr
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 gr((unsigned)grid);
   if (!any_fp8) {
+    const bool two = attn_rows_per_wave(group, false) == 2 * kQRows;
     switch (group) {
-      case 1: attn_direct_kernel<1><<<gr, dim3(256), 0, s>>>(p); break;
-      case 2: attn_direct_kernel<2><<<gr, dim3(256), 0, s>>>(p); break;
-      case 4: attn_direct_kernel<4><<<gr, dim3(256), 0, s>>>(p); break;
-      case 8: attn_direct_kernel<8><<<gr, dim3(512), 0, s>>>(p); break;
+      case 1: two ? attn_direct_kernel<1, 2><<<gr, dim3(256), 0, s>>>(p)
+                  : attn_direct_kernel<1, 1><<<gr, dim3(256), 0, s>>>(p); break;
+      case 2: two ? attn_direct_kernel<2, 2><<<gr, dim3(256), 0, s>>>(p)
+                  : attn_direct_kernel<2, 1><<<gr, dim3(256), 0, s>>>(p); break;
+      case 4: two ? attn_direct_kernel<4, 2><<<gr, dim3(256), 0, s>>>(p)
+                  : attn_direct_kernel<4, 1><<<gr, dim3(256), 0, s>>>(p); break;
+      case 8: attn_direct_kernel<8, 1><<<gr, dim3(512), 0, s>>>(p); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

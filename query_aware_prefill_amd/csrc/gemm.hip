@@ -8,9 +8,9 @@
 // bf16 MFMA with fp32 accumulation; the row scale is applied in the epilogue:
 //   y[m][n] = scale[n] * sum_k x[m][k] * decode(w[n][k]).
 //
-// Tiling (see gemm_pipe_kernel): 256 tokens x 256 output columns x 64 k per
-// workgroup step, each wave owning a strip of tokens x 128 columns. The MFMA
-// computes the transposed product
+// Tiling (see gemm_direct_kernel): 256 tokens x 256 output columns x 64 k per
+// workgroup step, each wave owning 64 tokens x 128 columns. The MFMA computes
+// the transposed product
 // D = W_tile . X_tile^T (v_mfma_f32_32x32x16_bf16), so each lane owns one
 // token row and 16 output columns per 32-column block: a whole 128-column
 // head lives in one wave, the RoPE pair (i, i + 64) sits in one lane, and the
@@ -169,193 +169,48 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const f32x16_t (&a
 }
 
 // ----------------------------------------------------------------------------
-// Pipelined variant: activations copied HBM->LDS with global_load_lds (no
-// staging registers), fp8 weights staged through registers and decoded once per
-// workgroup, both double-buffered in LDS with one barrier per k-step. LDS rows
-// are 128 B (64 k values); their 16-B chunks are XOR-swizzled by row so the
-// MFMA operand reads (eight rows per LDS cycle, same chunk) hit distinct banks.
-// Workgroup tile BM x BN, WM x WN waves; each wave owns BM/WM rows x 128
-// columns, so the RoPE pair (i, i+64) of a head and the gate/up pair of the
-// SwiGLU tile stay inside one lane.
+// The GEMM kernel: both operands copied HBM->LDS by global_load_lds (issued
+// as inline asm so the compiler does not make the operand reads wait for
+// copies in flight), fp8 weight codes kept as codes in LDS (half the bytes)
+// and decoded after each read with v_cvt_scalef32_pk_bf16_fp8 (exact, scale
+// 1). k-steps of 64 over 3 LDS stages; the copies of step k+2 are in flight
+// while step k computes. Each step starts with an explicit wait for this
+// step's copies and a raw s_barrier (a fenced __syncthreads would wait for all
+// copies in flight).
+//
+// k order inside a step: the MFMA k-slots may take any permutation of k as
+// long as both operands use the same one. Here MFMA t of pair j (k-substep
+// 2j+t), lane group h (= lane / 32), element e holds k = 32j + 16h + 8t + e,
+// so that one 16-B read of a weight row gives a lane the codes of two
+// MFMAs.
+//
+// LDS (64 banks x 4 B per cycle; a 16-B read serves 16 lanes per cycle): A
+// rows are 128 B, chunk ^= (row/2) % 8; B rows are 64 B, chunk ^= (row/4) % 4;
+// the 16 rows one read cycle touches then hit 16 distinct chunks.
 // ----------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ int swz8(int row, int chunk) { return chunk ^ (row & 7); }
-
-template <int EPI, int BM, int BN, int WM, int WN>
-__global__ void __launch_bounds__(64 * WM * WN)
-gemm_pipe_kernel(GemmParams p) {
-  constexpr int NW = WM * WN;
-  constexpr int NT = 64 * NW;
-  constexpr int MW = BM / WM;                 // rows per wave
-  constexpr int MB = MW / 32;                 // 32-row MFMA blocks per wave
-  static_assert(BN / WN == 128, "each wave owns 128 columns");
-  constexpr int A_ELEMS = BM * 64;            // one stage of A (bf16)
-  constexpr int B_ELEMS = BN * 64;            // one stage of B (decoded bf16)
-  constexpr int A_SLICES = BM / 8;            // 1-KB copies (8 rows) per stage
-  constexpr int A_PER_WAVE = A_SLICES / NW;
-  constexpr int B_CHUNKS = BN * 4 / NT;       // 16-code chunks per thread per stage
-  static_assert(A_SLICES % NW == 0 && (BN * 4) % NT == 0, "tile/thread split");
-  __shared__ __attribute__((aligned(1024))) uint16_t As[2][A_ELEMS];
-  __shared__ __attribute__((aligned(1024))) uint16_t Bs[2][B_ELEMS];
-
-  const int n_tn = (EPI == EPI_SWIGLU) ? p.N / (BN / 2) : p.N / BN;
-  const int n_tm = (p.M + BM - 1) / BM;
-  const int64_t total = (int64_t)n_tn * n_tm;
-  const int64_t wid = xcd_remap(blockIdx.x, total);
-  if (wid < 0) return;
-  const int tm = (int)(wid / n_tn);
-  const int tn = (int)(wid % n_tn);
-  const int m0 = tm * BM;
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
-  const int wm = wave % WM;
-  const int wn = wave / WM;
-
-  // weight row held in B-tile row r
-  auto wrow = [&](int r) -> int {
-    if (EPI == EPI_SWIGLU) {
-      const int pr = r >> 7, j = r & 63;
-      const int base = tn * (BN / 2) + pr * 64 + j;
-      return (r & 64) ? p.inter + base : base;
-    }
-    return tn * BN + r;
-  };
-
-  auto issue_a = [&](int k0, uint16_t* dst) {
-#pragma unroll
-    for (int i = 0; i < A_PER_WAVE; ++i) {
-      const int slice = wave * A_PER_WAVE + i;
-      const int row = slice * 8 + (lane >> 3);
-      const int m = min(m0 + row, p.M - 1);
-      const int chunk = swz8(row, lane & 7);
-      __builtin_amdgcn_global_load_lds(p.A + (int64_t)m * p.lda + k0 + chunk * 8,
-                                       (lds_void_t*)(dst + slice * 8 * 64), 16, 0, 0);
-    }
-  };
-  uint4 rb[B_CHUNKS];
-  auto load_b = [&](int k0) {
-#pragma unroll
-    for (int j = 0; j < B_CHUNKS; ++j) {
-      const int c = tid + NT * j;
-      rb[j] = *reinterpret_cast<const uint4*>(p.B + (int64_t)wrow(c >> 2) * p.K + k0 + (c & 3) * 16);
-    }
-  };
-  auto store_b = [&](uint16_t* dst) {
-#pragma unroll
-    for (int j = 0; j < B_CHUNKS; ++j) {
-      const int c = tid + NT * j;
-      const int row = c >> 2;
-      uint32_t w[8];
-      fp8x4_to_bf16x4(rb[j].x, w[0], w[1]);
-      fp8x4_to_bf16x4(rb[j].y, w[2], w[3]);
-      fp8x4_to_bf16x4(rb[j].z, w[4], w[5]);
-      fp8x4_to_bf16x4(rb[j].w, w[6], w[7]);
-      uint16_t* rp = dst + row * 64;
-      *reinterpret_cast<uint4*>(rp + swz8(row, (c & 3) * 2) * 8) = make_uint4(w[0], w[1], w[2], w[3]);
-      *reinterpret_cast<uint4*>(rp + swz8(row, (c & 3) * 2 + 1) * 8) = make_uint4(w[4], w[5], w[6], w[7]);
-    }
-  };
-
-  f32x16_t acc[MB][4];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
-
-  const int nk = p.K / 64;
-  issue_a(0, As[0]);
-  load_b(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    store_b(Bs[st]);          // stage st was last read two steps ago (fenced by the last barrier)
-    // The fence of this barrier waits for this wave's copies of A(kt) and the
-    // loads of B; the barrier then makes both stages st visible to all waves
-    // and retires every read of stage st^1.
-    __syncthreads();
-    if (kt + 1 < nk) {
-      issue_a((kt + 1) * 64, As[st ^ 1]);
-      load_b((kt + 1) * 64);
-    }
-    const uint16_t* Ap = As[st];
-    const uint16_t* Bp = Bs[st];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8_t af[MB], bfr[4];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int row = wm * MW + mb * 32 + l32;
-        af[mb] = bitcast<bf16x8_t>(*reinterpret_cast<const uint4*>(Ap + row * 64 + swz8(row, kk * 2 + hi) * 8));
-      }
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int row = wn * 128 + nb * 32 + l32;
-        bfr[nb] = bitcast<bf16x8_t>(*reinterpret_cast<const uint4*>(Bp + row * 64 + swz8(row, kk * 2 + hi) * 8));
-      }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma_32x32x16(bfr[nb], af[mb], acc[mb][nb]);
-    }
-  }
-
-  // epilogue: the wave's 128 columns start at column n_base (STORE/RESID/QKV)
-  // or, for SWIGLU, output column o_base (gate rows) / o_base + inter (up rows)
-  const int n_base = tn * BN + wn * 128;
-  const int o_base = tn * (BN / 2) + wn * 64;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int m = m0 + wm * MW + mb * 32 + l32;
-    if (m >= p.M) continue;
-    epilogue<EPI>(p, acc[mb], m, n_base, o_base, hi);
-  }
-}
-
-// ----------------------------------------------------------------------------
-// Deep-pipelined variant (the default): both operands copied HBM->LDS by
-// global_load_lds, the fp8 weights kept as codes in LDS and decoded right after
-// each read with v_cvt_scalef32_pk_bf16_fp8 (exact, scale 1). k-steps of BK
-// over STAGES LDS stages; the copies of step k+STAGES-1 are in flight while
-// step k computes. Each step begins with an explicit wait for this step's
-// copies only and a raw s_barrier (a fenced __syncthreads would wait for all
-// copies in flight). LDS rows are XOR-swizzled in 16-B chunks so that the
-// operand reads of one LDS cycle spread over the banks.
-// ----------------------------------------------------------------------------
-template <int BK> __device__ __forceinline__ int swz_a(int row, int chunk) {
-  return BK == 64 ? (chunk ^ (row & 7)) : (chunk ^ ((row >> 1) & 3));
-}
-template <int BK> __device__ __forceinline__ int swz_b(int row, int chunk) {
-  return BK == 64 ? (chunk ^ ((row >> 1) & 3)) : (chunk ^ ((row >> 2) & 1));
-}
+__device__ __forceinline__ int swz_a(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+__device__ __forceinline__ int swz_b(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
 // 8 E4M3 codes -> 8 bf16 (exact)
-__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint2 w) {
-  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false);
-  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true);
-  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false);
-  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true);
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
   return bitcast<bf16x8_t>(make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
                                       __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)));
 }
 
-template <int EPI, int BM, int BN, int WM, int WN, int BK, int STAGES>
+template <int EPI, int BM, int BN, int WM, int WN>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_direct_kernel(GemmParams p) {
   constexpr int NW = WM * WN;
   constexpr int MW = BM / WM;
   constexpr int MB = MW / 32;
-  constexpr int KK = BK / 16;                      // MFMA k-substeps per step
-  constexpr int A_ROW = BK * 2, B_ROW = BK;        // bytes per LDS row
+  constexpr int STAGES = 3;
+  constexpr int A_ROW = 128, B_ROW = 64;           // bytes per LDS row (k = 64)
   constexpr int A_BYTES = BM * A_ROW, B_BYTES = BN * B_ROW;
-  constexpr int A_RPC = 1024 / A_ROW, B_RPC = 1024 / B_ROW;   // rows per 1-KB copy
-  constexpr int A_CPR = A_ROW / 16, B_CPR = B_ROW / 16;       // 16-B chunks per row
-  constexpr int A_PW = A_BYTES / 1024 / NW, B_PW = B_BYTES / 1024 / NW;
+  constexpr int A_PW = A_BYTES / 1024 / NW, B_PW = B_BYTES / 1024 / NW;   // 1-KB copies per wave
   constexpr int CPW = A_PW + B_PW;
   static_assert(BN / WN == 128, "each wave owns 128 columns");
   static_assert((A_BYTES / 1024) % NW == 0 && (B_BYTES / 1024) % NW == 0, "copy split");
@@ -386,25 +241,26 @@ gemm_direct_kernel(GemmParams p) {
     }
     return tn * BN + r;
   };
+  // per-lane copy sources: A copies are 8 rows x 128 B, B copies 16 rows x 64 B
   const uint8_t* a_src[A_PW];
   const uint8_t* b_src[B_PW];
 #pragma unroll
   for (int i = 0; i < A_PW; ++i) {
-    const int row = (wave * A_PW + i) * A_RPC + lane / A_CPR;
+    const int row = (wave * A_PW + i) * 8 + (lane >> 3);
     const int m = min(m0 + row, p.M - 1);
-    a_src[i] = reinterpret_cast<const uint8_t*>(p.A + (int64_t)m * p.lda) + swz_a<BK>(row, lane % A_CPR) * 16;
+    a_src[i] = reinterpret_cast<const uint8_t*>(p.A + (int64_t)m * p.lda) + swz_a(row, lane & 7) * 16;
   }
 #pragma unroll
   for (int i = 0; i < B_PW; ++i) {
-    const int row = (wave * B_PW + i) * B_RPC + lane / B_CPR;
-    b_src[i] = p.B + (int64_t)wrow(row) * p.K + swz_b<BK>(row, lane % B_CPR) * 16;
+    const int row = (wave * B_PW + i) * 16 + (lane >> 2);
+    b_src[i] = p.B + (int64_t)wrow(row) * p.K + swz_b(row, lane & 3) * 16;
   }
   auto issue = [&](int kt) {
     uint8_t* st = smem[kt % STAGES];
 #pragma unroll
-    for (int i = 0; i < A_PW; ++i) copy16_to_lds(a_src[i] + kt * BK * 2, st + (wave * A_PW + i) * 1024);
+    for (int i = 0; i < A_PW; ++i) copy16_to_lds(a_src[i] + kt * 128, st + (wave * A_PW + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < B_PW; ++i) copy16_to_lds(b_src[i] + kt * BK, st + A_BYTES + (wave * B_PW + i) * 1024);
+    for (int i = 0; i < B_PW; ++i) copy16_to_lds(b_src[i] + kt * 64, st + A_BYTES + (wave * B_PW + i) * 1024);
   };
 
   f32x16_t acc[MB][4];
@@ -415,44 +271,41 @@ gemm_direct_kernel(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
 
-  const int nk = p.K / BK;
+  const int nk = p.K / 64;
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < nk) issue(s);
   for (int kt = 0; kt < nk; ++kt) {
-    const int after = min(STAGES - 2, nk - 1 - kt);    // copies issued after step kt's
-    if (after >= 2) wait_vmcnt<2 * CPW>();
-    else if (after == 1) wait_vmcnt<CPW>();
+    if (kt + 1 < nk) wait_vmcnt<CPW>();      // the copies of step kt+1 may stay in flight
     else wait_vmcnt<0>();
-    raw_barrier();               // step kt landed everywhere; stage (kt-1)%STAGES is free
+    raw_barrier();                           // step kt landed everywhere; stage (kt-1)%3 is free
     if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
     const uint8_t* st = smem[kt % STAGES];
-    // all operand reads of the step first, then the MFMAs
-    uint4 ar[KK][MB];
-    uint2 br[KK][4];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int row = wm * MW + mb * 32 + l32;
-        ar[kk][mb] = *reinterpret_cast<const uint4*>(st + row * A_ROW + swz_a<BK>(row, kk * 2 + hi) * 16);
-      }
+    for (int j = 0; j < 2; ++j) {            // pairs of MFMA k-substeps
+      uint4 bw[4];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         const int row = wn * 128 + nb * 32 + l32;
-        br[kk][nb] = *reinterpret_cast<const uint2*>(st + A_BYTES + row * B_ROW + swz_b<BK>(row, kk) * 16 + hi * 8);
+        bw[nb] = *reinterpret_cast<const uint4*>(st + A_BYTES + row * B_ROW + swz_b(row, 2 * j + hi) * 16);
       }
-    }
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      bf16x8_t bfr[4];
+      for (int t = 0; t < 2; ++t) {
+        bf16x8_t af[MB], bfr[4];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) bfr[nb] = fp8x8_to_bf16x8(br[kk][nb]);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb) {
+          const int row = wm * MW + mb * 32 + l32;
+          af[mb] = bitcast<bf16x8_t>(
+              *reinterpret_cast<const uint4*>(st + row * A_ROW + swz_a(row, 4 * j + 2 * hi + t) * 16));
+        }
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = mfma_32x32x16(bfr[nb], bitcast<bf16x8_t>(ar[kk][mb]), acc[mb][nb]);
+          bfr[nb] = t == 0 ? fp8x8_to_bf16x8(bw[nb].x, bw[nb].y) : fp8x8_to_bf16x8(bw[nb].z, bw[nb].w);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma_32x32x16(bfr[nb], af[mb], acc[mb][nb]);
+      }
     }
   }
 
@@ -468,32 +321,18 @@ gemm_direct_kernel(GemmParams p) {
 
 hipError_t launch_gemm(const GemmParams& p, GemmEpi epi, hipStream_t s) {
   if (p.M == 0) return hipSuccess;
-  // tile configuration: 0 = 256x128 (4 waves), 1 = 256x256 (8 waves of 64x128),
-  // 2 = 256x256 (4 waves of 128x128); direct pipelines: 3 = 8 waves, k-steps of
-  // 32 over 4 stages, 4 = 8 waves, k-steps of 64 over 3 stages, 5 = 4 waves of
-  // 128x128, k-steps of 64 over 3 stages. QUAIL_GEMM_TILE overrides the default.
-  static int cfg = [] {
-    const char* e = getenv("QUAIL_GEMM_TILE");
-    return e ? atoi(e) : 4;
-  }();
-  // a 256-column tile needs N % 256 == 0 (SWIGLU: 128 output columns per tile)
-  const bool wide_ok = (epi == EPI_SWIGLU) ? (p.N % 128 == 0) : (p.N % 256 == 0);
-  const int c = wide_ok ? cfg : 0;
-  const int bn = c == 0 ? 128 : 256;
+  // 256x256 tiles (8 waves of 64 rows x 128 columns) when the columns allow
+  // (SWIGLU: 128 output columns per tile), else 256x128 (4 waves)
+  const bool wide = (epi == EPI_SWIGLU) ? (p.N % 128 == 0) : (p.N % 256 == 0);
+  const int bn = wide ? 256 : 128;
   const int n_tn = (epi == EPI_SWIGLU) ? p.N / (bn / 2) : p.N / bn;
   const int64_t total = (int64_t)n_tn * ((p.M + 255) / 256);
   const int64_t grid = (total + 7) / 8 * 8;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 g((unsigned)grid);
 #define QUAIL_GEMM_LAUNCH(E)                                                              \
-  switch (c) {                                                                            \
-    case 0: gemm_pipe_kernel<E, 256, 128, 4, 1><<<g, dim3(256), 0, s>>>(p); break;        \
-    case 1: gemm_pipe_kernel<E, 256, 256, 4, 2><<<g, dim3(512), 0, s>>>(p); break;        \
-    case 2: gemm_pipe_kernel<E, 256, 256, 2, 2><<<g, dim3(256), 0, s>>>(p); break;        \
-    case 3: gemm_direct_kernel<E, 256, 256, 4, 2, 32, 4><<<g, dim3(512), 0, s>>>(p); break; \
-    case 4: gemm_direct_kernel<E, 256, 256, 4, 2, 64, 3><<<g, dim3(512), 0, s>>>(p); break; \
-    default: gemm_direct_kernel<E, 256, 256, 2, 2, 64, 3><<<g, dim3(256), 0, s>>>(p); break; \
-  }
+  if (wide) gemm_direct_kernel<E, 256, 256, 4, 2><<<g, dim3(512), 0, s>>>(p);             \
+  else gemm_direct_kernel<E, 256, 128, 4, 1><<<g, dim3(256), 0, s>>>(p);
   switch (epi) {
     case EPI_STORE: QUAIL_GEMM_LAUNCH(EPI_STORE); break;
     case EPI_RESID: QUAIL_GEMM_LAUNCH(EPI_RESID); break;

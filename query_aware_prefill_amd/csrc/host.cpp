@@ -128,9 +128,11 @@ class Blob {
   std::vector<uint8_t> bytes_;
 };
 
-int group_tokens(int G) {   // query tokens per attention tile for GQA group size G
+// query tokens per attention tile for GQA group size G (the kernel's waves
+// cover the G heads x (waves / G) token groups)
+int group_tokens(int G, bool any_fp8) {
   const int nw = G >= 4 ? G : 4;
-  return kQRows * (nw / G);
+  return attn_rows_per_wave(G, any_fp8) * (nw / G);
 }
 
 bool valid_group(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
@@ -555,7 +557,7 @@ quail_status anchor_core(quail_ctx* c, int32_t n, const int32_t* tokens, const i
   if (quail_status st = ensure_rope(c, s)) return st;
   const quail_model_config& cf = c->cfg;
   const int G = cf.n_q_heads / cf.n_kv_heads;
-  const int TQ = group_tokens(G);
+  const int TQ = group_tokens(G, cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3);
   const size_t esz = kv_elem_bytes(cf);
   // batches of whole anchors up to T tokens
   int32_t a0 = 0;
@@ -784,7 +786,7 @@ quail_status join_core(quail_ctx* c, int32_t n, const quail_anchor* ha, const in
     return kx < ky;
   });
   const int G = cf.n_q_heads / cf.n_kv_heads;
-  const int TQ = group_tokens(G);
+  const int TQ = group_tokens(G, cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3);
   const size_t esz = kv_elem_bytes(cf);
   int32_t p0 = 0;
   while (p0 < n) {
@@ -1096,7 +1098,7 @@ quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t 
     HIP_TRY(launch_attn_f32(p, st));
     return QUAIL_OK;
   }
-  const int TQ = group_tokens(G);
+  const int TQ = group_tokens(G, false);
   std::vector<KVSrc> srcs;
   KVSrc self{};
   self.k = k; self.v = v; self.tok_stride = (int64_t)hkv * d; self.head_stride = d; self.len = T; self.fp8 = 0;

@@ -116,6 +116,8 @@ struct Head8Params {
 // any_fp8: some key source of this launch holds E4M3 codes (register-staged
 // kernel); otherwise the direct HBM->LDS kernel runs.
 hipError_t launch_attn_bf16(const AttnParams& p, int group, bool any_fp8, hipStream_t s);
+// Query tokens one wave of that launch covers (tiles hold (waves / group) of these).
+int attn_rows_per_wave(int group, bool any_fp8);
 hipError_t launch_attn_f32(const AttnF32Params& p, hipStream_t s);
 hipError_t launch_gemm(const GemmParams& p, GemmEpi epi, hipStream_t s);
 hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s);
