@@ -369,36 +369,69 @@ __device__ __forceinline__ v4i16_t lds_read_tr16(const uint16_t* p) {
       (v4i16_t __attribute__((address_space(3)))*)(__attribute__((address_space(3))) char*)p);
 }
 
-// Issue the direct copies of one 64-key tile (K and V) of kv head g into the
-// LDS stage `kd`/`vd`. Each wave copies 16/NW 1-KB slices (4 rows each) of K
-// and of V; rows at or past the source length are clamped (masked later).
+// Per-lane constants of the direct copies. Each wave copies 16/NW 1-KB slices
+// (4 rows of 256 B) of a K or V tile; lane L writes 16-B slot L % 16 of row
+// slice*4 + L/16 and so reads the chunk that the swizzle puts in that slot.
 template <int NW>
-__device__ __forceinline__ void issue_tile(const KVSrc& src, int g, int kbase, uint16_t* kd,
-                                           uint16_t* vd, int wave, int lane) {
-  constexpr int PER_WAVE = 16 / NW;
-  const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(src.k) + (int64_t)g * src.head_stride * 2;
-  const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(src.v) + (int64_t)g * src.head_stride * 2;
-  const int64_t tb = src.tok_stride * 2;
+struct CopyLanes {
+  static constexpr int PER_WAVE = 16 / NW;
+  uint32_t row[PER_WAVE];                   // tile row copied by this lane
+  uint32_t koff[PER_WAVE], voff[PER_WAVE];  // byte offset of its chunk within the row
+  uint32_t lds[PER_WAVE];                   // LDS byte offset of the slice (wave-uniform)
+};
+
+template <int NW>
+__device__ __forceinline__ CopyLanes<NW> copy_lanes(int wave, int lane) {
+  CopyLanes<NW> c;
 #pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int slice = wave * PER_WAVE + i;          // 4 rows per slice
-    const int row = slice * 4 + (lane >> 4);
-    const int key = min(kbase + row, src.len - 1);
-    const int slot = lane & 15;
-    copy16_to_lds(kb8 + key * tb + swz_k(row, slot) * 16, kd + slice * 4 * kRowElems);
-    copy16_to_lds(vb8 + key * tb + swz_v(row, slot) * 16, vd + slice * 4 * kRowElems);
+  for (int i = 0; i < CopyLanes<NW>::PER_WAVE; ++i) {
+    const int slice = wave * CopyLanes<NW>::PER_WAVE + i;
+    c.row[i] = slice * 4 + (lane >> 4);
+    c.koff[i] = swz_k(c.row[i], lane & 15) * 16;
+    c.voff[i] = swz_v(c.row[i], lane & 15) * 16;
+    c.lds[i] = slice * 4 * kRowElems * 2;
+  }
+  return c;
+}
+
+// Issue the direct copies of one 64-key K (IS_V = false) or V tile of kv head
+// g into the LDS slot at byte address `dst`. Rows at or past the source length
+// are clamped to its last row (their scores are masked); full tiles skip the
+// clamp. Per-lane offsets are 24-bit products (token strides are bounded on
+// the host).
+template <int NW, bool IS_V>
+__device__ __forceinline__ void issue_copy(const KVSrc& src, int g, int kbase, uint32_t dst,
+                                           const CopyLanes<NW>& cl) {
+  const uint32_t tb = (uint32_t)src.tok_stride * 2u;
+  const int64_t base = ((int64_t)g * src.head_stride + (int64_t)kbase * src.tok_stride) * 2;
+  const uint8_t* b8 = reinterpret_cast<const uint8_t*>(IS_V ? src.v : src.k) + base;
+  const bool full = kbase + kKeyTile <= src.len;
+  const uint32_t last = (uint32_t)max(src.len - 1 - kbase, 0);
+#pragma unroll
+  for (int i = 0; i < CopyLanes<NW>::PER_WAVE; ++i) {
+    const uint32_t r = full ? cl.row[i] : min(cl.row[i], last);
+    copy16_to_lds_off(b8, __umul24(r, tb) + (IS_V ? cl.voff[i] : cl.koff[i]), dst + cl.lds[i]);
   }
 }
 
-// QB = 32-row query blocks per wave. QB = 2 makes every K/V fragment read from
-// LDS feed two MFMAs (half the LDS traffic per FLOP) at the cost of one wave
-// per SIMD; QB = 1 keeps two workgroups per CU.
-template <int G, int QB>
-__global__ void __launch_bounds__(64 * (G >= 4 ? G : 4), QB == 1 ? 2 : 1)
+template <bool B>
+struct MaskTag { static constexpr bool value = B; };
+
+// Software pipeline over the key tiles: while the softmax of tile j (exp,
+// bf16 packing, row sums) runs on the VALU, the S MFMAs of tile j+1 are in
+// flight, and the PV MFMAs of tile j overlap the masking and row max of tile
+// j+1. K and V have two LDS slots each; at step j the copies of K(j+2) and
+// V(j+1) are issued into the slots that step j-1 finished reading, so one
+// barrier per tile suffices.
+// Full cross tiles and the masked tiles (the ragged end of the cross keys,
+// all self tiles) are handled by separate instantiations of the step, so the
+// unmasked step carries no mask code.
+template <int G>
+__global__ void __launch_bounds__(64 * (G >= 4 ? G : 4), 2)
 attn_direct_kernel(AttnParams p) {
   constexpr int NW = G >= 4 ? G : 4;
-  constexpr int ROWS = kQRows * QB;                   // query tokens per wave
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][kTileElems];   // [stage][K,V]
+  constexpr uint32_t kSlotBytes = kTileElems * 2;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][kTileElems];   // [K,V][slot]
 
   const int64_t total = (int64_t)p.n_tiles * p.hkv;
   const int64_t wid = xcd_remap(blockIdx.x, total);
@@ -407,193 +440,253 @@ attn_direct_kernel(AttnParams p) {
   const AttnTile tile = p.tiles[wid % p.n_tiles];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const int head = g * G + (wave % G);
   const int tg = wave / G;
+  const int qrow = tg * kQRows + l32;
+  const bool row_ok = qrow < tile.nq;
+  const int64_t tok = (int64_t)tile.q0 + qrow;
 
   KVSrc cs{}, ss{};
-  int n_ct = 0, n_st = 0;
-  if (tile.cross >= 0) { cs = p.srcs[tile.cross]; n_ct = (cs.len + kKeyTile - 1) / kKeyTile; }
+  int n_ct = 0, n_st = 0, n_full = 0;
+  if (tile.cross >= 0) {
+    cs = p.srcs[tile.cross];
+    n_ct = (cs.len + kKeyTile - 1) / kKeyTile;
+    n_full = cs.len / kKeyTile;
+  }
   if (tile.self >= 0) {
     ss = p.srcs[tile.self];
     n_st = max(0, (tile.self_qbase + tile.nq - tile.self_k0 + kKeyTile - 1) / kKeyTile);
   }
   const int n_tiles = n_ct + n_st;
-  auto src_of = [&](int it) -> const KVSrc& { return it < n_ct ? cs : ss; };
-  auto kbase_of = [&](int it) { return it < n_ct ? it * kKeyTile : tile.self_k0 + (it - n_ct) * kKeyTile; };
-
-  if (n_tiles > 0) issue_tile<NW>(src_of(0), g, kbase_of(0), lds[0][0], lds[0][1], wave, lane);
-
-  // per 32-row block: query row of this lane
-  int qrow[QB], seg_lo[QB], self_q[QB];
-  bool row_ok[QB];
-  int64_t tok[QB];
-  bf16x8_t qf[QB][8];
+  if (n_tiles == 0) {
+    // no visible key: zero output, LSE -inf
+    if (row_ok) {
+      uint16_t* op = p.out + tok * p.o_stride + head * kHeadDim + hi * 4;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    qrow[qb] = tg * ROWS + qb * kQRows + l32;
-    row_ok[qb] = qrow[qb] < tile.nq;
-    tok[qb] = (int64_t)tile.q0 + qrow[qb];
-    const uint16_t* qp = p.q + tok[qb] * p.q_stride + head * kHeadDim + hi * 8;
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) *reinterpret_cast<uint2*>(op + cb * 32 + rg * 8) = make_uint2(0, 0);
+      if (p.lse != nullptr && hi == 0) p.lse[tok * p.hq + head] = -INFINITY;
+    }
+    return;
+  }
+  auto src_of = [&](int j) -> const KVSrc& { return j < n_ct ? cs : ss; };
+  auto kbase_of = [&](int j) { return j < n_ct ? j * kKeyTile : tile.self_k0 + (j - n_ct) * kKeyTile; };
+
+  const uint32_t lds_k0 = lds_addr_of(&lds[0][0][0]);
+  const uint32_t lds_v0 = lds_addr_of(&lds[1][0][0]);
+  const CopyLanes<NW> cl = copy_lanes<NW>(wave, lane);
+  issue_copy<NW, false>(src_of(0), g, kbase_of(0), lds_k0, cl);
+  issue_copy<NW, true>(src_of(0), g, kbase_of(0), lds_v0, cl);
+  if (n_tiles > 1) issue_copy<NW, false>(src_of(1), g, kbase_of(1), lds_k0 + kSlotBytes, cl);
+
+  // Q fragments: B operand, lane holds query row l32, dims ks*16 + hi*8 .. +7
+  bf16x8_t qf[8];
+  {
+    const uint16_t* qp = p.q + tok * p.q_stride + head * kHeadDim + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      uint4 u = row_ok[qb] ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
-      qf[qb][ks] = bitcast<bf16x8_t>(u);
+      uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
+      qf[ks] = bitcast<bf16x8_t>(u);
     }
-    seg_lo[qb] = row_ok[qb] ? p.seg_lo[tok[qb]] : 0x7FFFFFFF;
-    self_q[qb] = tile.self_qbase + qrow[qb];
+  }
+  const int seg_lo = row_ok ? p.seg_lo[tok] : 0;
+  const int self_q = row_ok ? tile.self_qbase + qrow : -1;
+
+  // per-lane LDS element offsets of the operand reads within a slot
+  // K (A of S^T): key row kb*32 + l32, 16-B chunk swz_k(key, ks*2 + hi); the
+  // kb term is a constant row offset.
+  uint32_t k_off[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) k_off[ks] = l32 * kRowElems + swz_k(l32, ks * 2 + hi) * 8;
+  // V^T (A of O^T) through ds_read_tr16_b64: within each 16-lane block lane j
+  // points at key (j / 4) of a 4-key group and dims 4*(j % 4) .. +3 of a
+  // 16-dim half; the 4-key groups start at multiples of 4, so the swizzle
+  // term depends on the lane only and the key-group terms are constant rows.
+  const int trj = lane & 15;
+  const int tr_key = hi * 4 + (trj >> 2);
+  const int tr_d0 = 16 * ((lane >> 4) & 1) + 4 * (trj & 3);
+  uint32_t v_off[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int d0 = cb * 32 + tr_d0;
+    v_off[cb] = tr_key * kRowElems + swz_v(tr_key, d0 >> 3) * 8 + (d0 & 7);
   }
 
-  f32x16_t o[QB][4];
+  f32x16_t o[4];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+  for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[qb][cb][r] = 0.0f;
-  float m_run[QB], l_run[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.0f; }
+    for (int r = 0; r < 16; ++r) o[cb][r] = 0.0f;
+  // Running reference of the online softmax (log2 units). Finite start value:
+  // the first visible score always triggers a rescale (alpha = 0), and rows
+  // with no visible key keep P = 0.
+  float m_run = -1e30f;
+  float l_run = 0.0f;
 
-  const int trB = lane >> 4, trj = lane & 15;
-  const int tr_key_off = trj >> 2;
-  const int tr_d0 = 16 * (trB & 1) + 4 * (trj & 3);
-
-  for (int it = 0; it < n_tiles; ++it) {
-    const int st = it & 1;
-    const bool is_cross = it < n_ct;
-    const int kbase = kbase_of(it);
-    // One barrier per tile. Its fence waits for this wave's outstanding
-    // copies (those of tile it) and the barrier then guarantees (a) every
-    // wave's copies of tile it have landed and (b) every wave has finished
-    // reading stage st^1 in the previous iteration, so it may be refilled.
-    __syncthreads();
-    if (it + 1 < n_tiles)
-      issue_tile<NW>(src_of(it + 1), g, kbase_of(it + 1), lds[st ^ 1][0], lds[st ^ 1][1], wave, lane);
-    const uint16_t* Kt = lds[st][0];
-    const uint16_t* Vt = lds[st][1];
-
-    f32x16_t s[QB][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.0f;
+  // S^T = K . Q^T of the tile in K slot `slot` (two 32-key halves)
+  auto scores = [&](int slot, f32x16_t (&s)[2]) {
+    const uint16_t* Kt = lds[0][slot];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int key = kb * 32 + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const uint16_t* a_p = Kt + key * kRowElems + swz_k(key, ks * 2 + hi) * 8;
-        const bf16x8_t a = bitcast<bf16x8_t>(*reinterpret_cast<const uint4*>(a_p));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma_32x32x16(a, qf[qb][ks], s[qb][kb]);
+        const bf16x8_t a = bitcast<bf16x8_t>(
+            *reinterpret_cast<const uint4*>(Kt + k_off[ks] + kb * 32 * kRowElems));
+        s[kb] = mfma_32x32x16(a, qf[ks], s[kb]);
       }
     }
-    const bool need_mask = is_cross ? (kbase + kKeyTile > cs.len) : true;
-    bf16x8_t pb[QB][2][2];
+  };
+  // mask tile j: visible keys of this row are [lo, hi_k]; the key of (kb, r)
+  // is kbase + kb*32 + hi*4 + (r/4)*8 + r%4 (unsigned range test)
+  auto mask = [&](int j, f32x16_t (&s)[2]) {
+    const bool cross = j < n_ct;
+    const int lo = cross ? 0 : seg_lo;
+    const int hi_k = cross ? cs.len - 1 : self_q;
+    const uint32_t range = (uint32_t)(hi_k - lo);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      if (need_mask) {
-        const int lo = is_cross ? 0 : seg_lo[qb];
-        const int hi_k = is_cross ? cs.len - 1 : self_q[qb];
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint32_t x = (uint32_t)(kbase_of(j) + kb * 32 + hi * 4 - lo);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kbase + kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-            s[qb][kb][r] = (key >= lo && key <= hi_k) ? s[qb][kb][r] : -INFINITY;
-          }
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t c = (uint32_t)((r >> 2) * 8 + (r & 3));
+        s[kb][r] = (x + c <= range) ? s[kb][r] : -INFINITY;
       }
-      float mt = -INFINITY;
+    }
+  };
+  // row max of a tile (both lanes of the row), log2 units
+  auto row_max = [&](const f32x16_t (&s)[2]) {
+    float m0 = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int r = 1; r < 16; ++r) m0 = fmaxf(m0, fmaxf(s[0][r], s[1][r]));
+    return xor32_max(m0) * p.scale_log2;
+  };
+  // Lazy rescale: the running reference m_run moves only when a row's max
+  // exceeds it by more than 8 (log2 units), so P stays below 2^8 and O is
+  // rescaled only on those (rare, wave-uniform) occasions. O / l and the LSE
+  // are exact for any reference.
+  auto rescale = [&](float mt) {
+    if (__ballot(mt > m_run + 8.0f) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[qb][kb][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * p.scale_log2;
-      // lazy rescale (see the register-staged kernel)
-      if (__ballot(mt > m_run[qb] + 8.0f) != 0) {
-        const float m_new = fmaxf(m_run[qb], mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-        m_run[qb] = m_new;
-        l_run[qb] *= alpha;
+      for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
+        for (int r = 0; r < 16; ++r) o[cb][r] *= alpha;
+    }
+  };
+  // P = 2^(s*scale - m_run) in bf16 as the B operand: k-step (kb, sp) takes
+  // regs 8*sp .. 8*sp+7 of half kb; the row sum adds the fp32 values
+  auto probs = [&](const f32x16_t (&s)[2], bf16x8_t (&pb)[2][2]) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[qb][cb][r] *= alpha;
-      }
-      const float m_use = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int sp = 0; sp < 2; ++sp) {
+        uint32_t w[4];
 #pragma unroll
-        for (int sp = 0; sp < 2; ++sp) {
-          uint32_t w[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][sp * 8 + 2 * e], p.scale_log2, -m_use));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][sp * 8 + 2 * e + 1], p.scale_log2, -m_use));
-            l_run[qb] += p0 + p1;
-            w[e] = pack_bf16x2(p0, p1);
-          }
-          pb[qb][kb][sp] = bitcast<bf16x8_t>(make_uint4(w[0], w[1], w[2], w[3]));
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][sp * 8 + 2 * e], p.scale_log2, -m_run));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][sp * 8 + 2 * e + 1], p.scale_log2, -m_run));
+          l_run += p0 + p1;
+          w[e] = pack_bf16x2(p0, p1);
         }
-    }
+        pb[kb][sp] = bitcast<bf16x8_t>(make_uint4(w[0], w[1], w[2], w[3]));
+      }
+  };
+  // O^T += V^T . P^T with the tile in V slot `slot`; A lane: dim row
+  // cb*32 + l32, keys kb*32 + sp*16 + hi*4 + {0..3, 8..11}
+  auto pv = [&](int slot, const bf16x8_t (&pb)[2][2]) {
+    const uint16_t* Vt = lds[1][slot];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      const int d0 = cb * 32 + tr_d0;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
-        for (int sp = 0; sp < 2; ++sp) {
-          const int k0 = kb * 32 + sp * 16 + hi * 4 + tr_key_off;
-          const int k1 = k0 + 8;
-          const v4i16_t lo4 = lds_read_tr16(Vt + k0 * kRowElems + swz_v(k0, d0 >> 3) * 8 + (d0 & 7));
-          const v4i16_t hi4 = lds_read_tr16(Vt + k1 * kRowElems + swz_v(k1, d0 >> 3) * 8 + (d0 & 7));
-          const uint2 a_lo = __builtin_bit_cast(uint2, lo4);
-          const uint2 a_hi = __builtin_bit_cast(uint2, hi4);
-          const bf16x8_t a = bitcast<bf16x8_t>(make_uint4(a_lo.x, a_lo.y, a_hi.x, a_hi.y));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) o[qb][cb] = mfma_32x32x16(a, pb[qb][kb][sp], o[qb][cb]);
+        for (int cb = 0; cb < 4; ++cb) {
+          const uint16_t* vp = Vt + v_off[cb] + (kb * 32 + sp * 16) * kRowElems;
+          const uint2 a_lo = __builtin_bit_cast(uint2, lds_read_tr16(vp));
+          const uint2 a_hi = __builtin_bit_cast(uint2, lds_read_tr16(vp + 8 * kRowElems));
+          o[cb] = mfma_32x32x16(bitcast<bf16x8_t>(make_uint4(a_lo.x, a_lo.y, a_hi.x, a_hi.y)),
+                                pb[kb][sp], o[cb]);
         }
-    }
+  };
+
+  // The copies are inline asm, invisible to the compiler's wait-count
+  // tracking, and a workgroup barrier's fence does not wait for them: every
+  // barrier that publishes copied tiles is preceded by an explicit wait for
+  // all of this wave's copies in flight.
+  auto publish = [&]() {
+    wait_vmcnt<0>();
+    __syncthreads();
+  };
+
+  // prologue: scores of tile 0
+  f32x16_t s_cur[2];
+  publish();
+  scores(0, s_cur);
+  if (n_full == 0) mask(0, s_cur);
+  rescale(row_max(s_cur));
+
+  // step j: issue K(j+2), V(j+1); S(j+1) with P(j); PV(j) with mask/max of j+1
+  auto step = [&](int j, auto tag) {
+    constexpr bool MASK_NEXT = decltype(tag)::value;
+    // Waits for this wave's copies of K(j+1) and V(j); the barrier then
+    // makes every wave's copies visible and guarantees that step j-1 (which
+    // read K(j) and V(j-1)) is finished everywhere.
+    publish();
+    if (j + 2 < n_tiles) issue_copy<NW, false>(src_of(j + 2), g, kbase_of(j + 2), lds_k0 + (j & 1) * kSlotBytes, cl);
+    issue_copy<NW, true>(src_of(j + 1), g, kbase_of(j + 1), lds_v0 + ((j + 1) & 1) * kSlotBytes, cl);
+    bf16x8_t pb[2][2];
+    probs(s_cur, pb);
+    f32x16_t s_nxt[2];
+    scores((j + 1) & 1, s_nxt);
+    pv(j & 1, pb);
+    if constexpr (MASK_NEXT) mask(j + 1, s_nxt);
+    const float mt = row_max(s_nxt);
+    rescale(mt);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+  };
+  int j = 0;
+  for (; j + 1 < n_full; ++j) step(j, MaskTag<false>{});
+  for (; j + 1 < n_tiles; ++j) step(j, MaskTag<true>{});
+  // epilogue: the last tile's PV (its V copy was issued by the last step, or
+  // by the prologue)
+  {
+    publish();
+    bf16x8_t pb[2][2];
+    probs(s_cur, pb);
+    pv(j & 1, pb);
   }
 
+  const float l_tot = xor32_sum(l_run);
+  if (!row_ok) return;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  uint16_t* op = p.out + tok * p.o_stride + head * kHeadDim + hi * 4;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
-    if (!row_ok[qb]) continue;
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    uint16_t* op = p.out + tok[qb] * p.o_stride + head * kHeadDim + hi * 4;
+  for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        uint2 w;
-        w.x = pack_bf16x2(o[qb][cb][rg * 4 + 0] * inv, o[qb][cb][rg * 4 + 1] * inv);
-        w.y = pack_bf16x2(o[qb][cb][rg * 4 + 2] * inv, o[qb][cb][rg * 4 + 3] * inv);
-        *reinterpret_cast<uint2*>(op + cb * 32 + rg * 8) = w;
-      }
-    if (p.lse != nullptr && hi == 0) {
-      const float m_use = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
-      const float L = l_tot > 0.0f ? (m_use + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-      p.lse[tok[qb] * p.hq + head] = L;
+    for (int rg = 0; rg < 4; ++rg) {
+      uint2 w;
+      w.x = pack_bf16x2(o[cb][rg * 4 + 0] * inv, o[cb][rg * 4 + 1] * inv);
+      w.y = pack_bf16x2(o[cb][rg * 4 + 2] * inv, o[cb][rg * 4 + 3] * inv);
+      *reinterpret_cast<uint2*>(op + cb * 32 + rg * 8) = w;
     }
+  if (p.lse != nullptr && hi == 0) {
+    const float L = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    p.lse[tok * p.hq + head] = L;
   }
 }
 
-int attn_rows_per_wave(int group, bool any_fp8) {
-  static const int qb = [] {
-    const char* e = getenv("QUAIL_ATTN_QB");
-    return (e && atoi(e) == 2) ? 2 : 1;
-  }();
-  // fp8 sources use the register-staged kernel; 8-wave workgroups keep QB = 1
-  // (two 32-row blocks would not fit the register file at 512 threads)
-  return (any_fp8 || group == 8) ? kQRows : kQRows * qb;
-}
+int attn_rows_per_wave(int, bool) { return kQRows; }
 
 hipError_t launch_attn_bf16(const AttnParams& p, int group, bool any_fp8, hipStream_t s) {
   if (p.n_tiles == 0) return hipSuccess;
@@ -602,15 +695,11 @@ hipError_t launch_attn_bf16(const AttnParams& p, int group, bool any_fp8, hipStr
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 gr((unsigned)grid);
   if (!any_fp8) {
-    const bool two = attn_rows_per_wave(group, false) == 2 * kQRows;
     switch (group) {
-      case 1: two ? attn_direct_kernel<1, 2><<<gr, dim3(256), 0, s>>>(p)
-                  : attn_direct_kernel<1, 1><<<gr, dim3(256), 0, s>>>(p); break;
-      case 2: two ? attn_direct_kernel<2, 2><<<gr, dim3(256), 0, s>>>(p)
-                  : attn_direct_kernel<2, 1><<<gr, dim3(256), 0, s>>>(p); break;
-      case 4: two ? attn_direct_kernel<4, 2><<<gr, dim3(256), 0, s>>>(p)
-                  : attn_direct_kernel<4, 1><<<gr, dim3(256), 0, s>>>(p); break;
-      case 8: attn_direct_kernel<8, 1><<<gr, dim3(512), 0, s>>>(p); break;
+      case 1: attn_direct_kernel<1><<<gr, dim3(256), 0, s>>>(p); break;
+      case 2: attn_direct_kernel<2><<<gr, dim3(256), 0, s>>>(p); break;
+      case 4: attn_direct_kernel<4><<<gr, dim3(256), 0, s>>>(p); break;
+      case 8: attn_direct_kernel<8><<<gr, dim3(512), 0, s>>>(p); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

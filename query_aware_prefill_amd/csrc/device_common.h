@@ -110,6 +110,32 @@ __device__ __forceinline__ void copy16_to_lds(const void* gptr, const void* lds_
                : "memory", "m0");
 }
 
+// Same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset (the saddr form: no 64-bit address arithmetic per lane).
+// `lds_addr` is the wave-uniform LDS byte address of the 1-KB destination.
+__device__ __forceinline__ void copy16_to_lds_off(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ object (low 32 bits of its generic pointer)
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>(p);
+}
+
+// max / sum of x over lanes l and l ^ 32 (v_permlane32_swap: exchanges the
+// two 32-lane halves, no LDS round trip)
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");

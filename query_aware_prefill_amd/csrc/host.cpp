@@ -137,6 +137,12 @@ int group_tokens(int G, bool any_fp8) {
 
 bool valid_group(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
 
+// KV token strides are at most n_kv_heads * 128 elements. The attention
+// kernel forms per-lane tile offsets as 24-bit products (row < 64 times the
+// stride in bytes), which needs strides below 2^24 bytes; 4096 heads give at
+// most 1 MB per token.
+constexpr int kMaxKVHeads = 4096;
+
 quail_status check_cfg(const quail_model_config* c) {
   if (!c) return fail(QUAIL_E_INVAL, "config is NULL");
   if (c->n_layers <= 0 || c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
@@ -152,6 +158,8 @@ quail_status check_cfg(const quail_model_config* c) {
     return fail(QUAIL_E_UNSUPPORTED, "hidden and intermediate must be multiples of 64");
   if (c->n_q_heads % c->n_kv_heads || !valid_group(c->n_q_heads / c->n_kv_heads))
     return fail(QUAIL_E_UNSUPPORTED, "GQA group size must be 1, 2, 4 or 8");
+  if (c->n_kv_heads > kMaxKVHeads)
+    return fail(QUAIL_E_UNSUPPORTED, "n_kv_heads %d (at most %d)", c->n_kv_heads, kMaxKVHeads);
   if (c->kv_dtype != QUAIL_DTYPE_BF16 && c->kv_dtype != QUAIL_DTYPE_FP8_E4M3)
     return fail(QUAIL_E_UNSUPPORTED, "kv_dtype must be BF16 or FP8_E4M3");
   if (c->kv_dtype == QUAIL_DTYPE_FP8_E4M3 && !(c->k_scale > 0.0f && c->v_scale > 0.0f))
@@ -1053,6 +1061,7 @@ quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t 
   if (dtype != QUAIL_DTYPE_F32 && dtype != QUAIL_DTYPE_BF16)
     return fail(QUAIL_E_UNSUPPORTED, "dtype must be F32 or BF16");
   if (hq <= 0 || hkv <= 0 || hq % hkv) return fail(QUAIL_E_INVAL, "hq must be a positive multiple of hkv");
+  if (hkv > kMaxKVHeads) return fail(QUAIL_E_UNSUPPORTED, "hkv %d (at most %d)", hkv, kMaxKVHeads);
   const int G = hq / hkv;
   if (dtype == QUAIL_DTYPE_BF16 && (d != kHeadDim || !valid_group(G)))
     return fail(QUAIL_E_UNSUPPORTED, "bf16 path: head_dim 128 and GQA group 1, 2, 4 or 8");
