@@ -29,6 +29,11 @@ Secondary measurements (not the headline line; each prints its own JSON):
                      MFMA peak.
   --workload copy    a plain 4 GiB device-to-device copy (read 4 GiB, write
                      4 GiB): the calibration kernel for the HBM byte counters.
+  --workload stream  anchor-KV streaming sweep: 1024 anchors of 768 tokens
+                     (bf16 K/V of one layer, 3.2 GB resident), each read by
+                     one suffix of S tokens, S in {1, 4, 16, 64, 256}; anchor
+                     KV bytes per launch / launch time against 8 TB/s, and
+                     TFLOP/s (the intensity is 4*S FLOP per KV byte).
   --workload layer   one decoder layer of the Qwen3-4B shape, random-init fp8
                      weights: 16 anchors x 1024 tokens, 512 suffixes x 64
                      tokens per anchor, run end to end by quail_join_run
@@ -199,6 +204,51 @@ def bench_copy(args):
                       "GB/s": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
+def bench_stream(args):
+    import torch
+    import workloads as W
+    from query_aware_prefill_amd import binding as B
+    B.load()
+    out = {"metric": "anchor-KV streaming (cascade attention, bf16 KV)", "unit": "GB/s",
+           "peak_GBs": HBM_PEAK_GBS, "anchors": 1024, "anchor_len": 768, "points": []}
+    for S in (1, 4, 16, 64, 256):
+        a_len, s_anchor, s_len = W.stream_lengths(S)
+        case = W.cascade_device(7, a_len, s_anchor, s_len)
+        T = int(case["s_off"][-1])
+        o = torch.empty((T, 32, 128), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(B.quail_cascade_workspace_bytes(case["a_off"], case["s_off"]),
+                         dtype=torch.uint8, device="cuda")
+        stream = torch.cuda.current_stream()
+
+        def step():
+            B.quail_cascade_attn(B.DTYPE_BF16, 32, 8, 128, case["sm_scale"], case["ak"], case["av"],
+                                 case["a_off"], s_anchor, case["q"], case["k"], case["v"],
+                                 case["s_off"], o, None, ws, stream=stream)
+
+        for _ in range(max(args.warmup, 1)):
+            step()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for a, b in ev:
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        kv_bytes = 2.0 * float(np.sum(a_len)) * 8 * 128 * 2
+        cross, self_ = algorithmic_flops(a_len, s_anchor, s_len)
+        pt = {"S": S, "ms": ms, "anchor_kv_bytes": kv_bytes, "GB/s": kv_bytes / (ms * 1e-3) / 1e9,
+              "frac_hbm": kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+              "tflops": (cross + self_) / (ms * 1e-3) / 1e12}
+        out["points"].append(pt)
+        log(f"stream S={S}: {ms:.3f} ms, {pt['GB/s']:.0f} GB/s ({pt['frac_hbm']:.2f} of HBM), "
+            f"{pt['tflops']:.1f} TFLOP/s")
+        del case, o, ws
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
 def bench_layer(args):
     import torch
     import workloads as W
@@ -257,7 +307,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--workload", choices=["cascade", "gemm", "layer", "copy"], default="cascade")
+    ap.add_argument("--workload", choices=["cascade", "gemm", "layer", "copy", "stream"],
+                    default="cascade")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -271,6 +322,8 @@ def main():
         return bench_layer(args)
     if args.workload == "copy":
         return bench_copy(args)
+    if args.workload == "stream":
+        return bench_stream(args)
 
     import torch
     import workloads as W
@@ -347,7 +400,7 @@ def main():
         "roofline": {
             "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
-            "kernel": "quail::attn_direct_kernel<4>", "flops_per_launch": flops,
+            "kernel": "quail::attn_direct_kernel<4, 1>", "flops_per_launch": flops,
             "launch_ms": kernel_ms,
             "algorithmic_bytes_per_launch": algorithmic_bytes(a_len, s_len),
         },

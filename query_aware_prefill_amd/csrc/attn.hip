@@ -394,25 +394,34 @@ __device__ __forceinline__ CopyLanes<NW> copy_lanes(int wave, int lane) {
   return c;
 }
 
-// Issue the direct copies of one 64-key K (IS_V = false) or V tile of kv head
-// g into the LDS slot at byte address `dst`. Rows at or past the source length
-// are clamped to its last row (their scores are masked); full tiles skip the
-// clamp. Per-lane offsets are 24-bit products (token strides are bounded on
-// the host).
+// The direct copies of one 64-key K (IS_V = false) or V tile of kv head g
+// into the LDS slot at byte address `dst`: PER_WAVE 1-KB slices per wave.
+// Rows at or
+// past the source length are clamped to its last row (their scores are
+// masked); full tiles skip the clamp. Per-lane offsets are 24-bit products
+// (token strides are bounded on the host).
 template <int NW, bool IS_V>
-__device__ __forceinline__ void issue_copy(const KVSrc& src, int g, int kbase, uint32_t dst,
-                                           const CopyLanes<NW>& cl) {
-  const uint32_t tb = (uint32_t)src.tok_stride * 2u;
-  const int64_t base = ((int64_t)g * src.head_stride + (int64_t)kbase * src.tok_stride) * 2;
-  const uint8_t* b8 = reinterpret_cast<const uint8_t*>(IS_V ? src.v : src.k) + base;
-  const bool full = kbase + kKeyTile <= src.len;
-  const uint32_t last = (uint32_t)max(src.len - 1 - kbase, 0);
-#pragma unroll
-  for (int i = 0; i < CopyLanes<NW>::PER_WAVE; ++i) {
+struct TileCopy {
+  const uint8_t* b8;
+  uint32_t tb, last, dst;
+  bool full;
+  __device__ __forceinline__ TileCopy(const KVSrc& src, int g, int kbase, uint32_t dst_) {
+    tb = (uint32_t)src.tok_stride * 2u;
+    const int64_t base = ((int64_t)g * src.head_stride + (int64_t)kbase * src.tok_stride) * 2;
+    b8 = reinterpret_cast<const uint8_t*>(IS_V ? src.v : src.k) + base;
+    full = kbase + kKeyTile <= src.len;
+    last = (uint32_t)max(src.len - 1 - kbase, 0);
+    dst = dst_;
+  }
+  __device__ __forceinline__ void issue(int i, const CopyLanes<NW>& cl) const {
     const uint32_t r = full ? cl.row[i] : min(cl.row[i], last);
     copy16_to_lds_off(b8, __umul24(r, tb) + (IS_V ? cl.voff[i] : cl.koff[i]), dst + cl.lds[i]);
   }
-}
+  __device__ __forceinline__ void issue_all(const CopyLanes<NW>& cl) const {
+#pragma unroll
+    for (int i = 0; i < CopyLanes<NW>::PER_WAVE; ++i) issue(i, cl);
+  }
+};
 
 template <bool B>
 struct MaskTag { static constexpr bool value = B; };
@@ -426,10 +435,15 @@ struct MaskTag { static constexpr bool value = B; };
 // Full cross tiles and the masked tiles (the ragged end of the cross keys,
 // all self tiles) are handled by separate instantiations of the step, so the
 // unmasked step carries no mask code.
-template <int G>
-__global__ void __launch_bounds__(64 * (G >= 4 ? G : 4), 2)
+// Token groups of 32 rows per workgroup: the workgroup's waves cover the G
+// query heads of one kv head x (waves / G) token groups and share every K/V
+// tile copied into LDS.
+constexpr int kAttnTokenGroups = 1;
+
+template <int G, int TG>
+__global__ void __launch_bounds__(64 * (G >= 4 ? G : 4) * TG, TG == 1 ? 2 : 1)
 attn_direct_kernel(AttnParams p) {
-  constexpr int NW = G >= 4 ? G : 4;
+  constexpr int NW = (G >= 4 ? G : 4) * TG;
   constexpr uint32_t kSlotBytes = kTileElems * 2;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][kTileElems];   // [K,V][slot]
 
@@ -480,9 +494,9 @@ attn_direct_kernel(AttnParams p) {
   const uint32_t lds_k0 = lds_addr_of(&lds[0][0][0]);
   const uint32_t lds_v0 = lds_addr_of(&lds[1][0][0]);
   const CopyLanes<NW> cl = copy_lanes<NW>(wave, lane);
-  issue_copy<NW, false>(src_of(0), g, kbase_of(0), lds_k0, cl);
-  issue_copy<NW, true>(src_of(0), g, kbase_of(0), lds_v0, cl);
-  if (n_tiles > 1) issue_copy<NW, false>(src_of(1), g, kbase_of(1), lds_k0 + kSlotBytes, cl);
+  TileCopy<NW, false>(src_of(0), g, kbase_of(0), lds_k0).issue_all(cl);
+  TileCopy<NW, true>(src_of(0), g, kbase_of(0), lds_v0).issue_all(cl);
+  if (n_tiles > 1) TileCopy<NW, false>(src_of(1), g, kbase_of(1), lds_k0 + kSlotBytes).issue_all(cl);
 
   // Q fragments: B operand, lane holds query row l32, dims ks*16 + hi*8 .. +7
   bf16x8_t qf[8];
@@ -528,8 +542,9 @@ attn_direct_kernel(AttnParams p) {
   float m_run = -1e30f;
   float l_run = 0.0f;
 
-  // S^T = K . Q^T of the tile in K slot `slot` (two 32-key halves)
-  auto scores = [&](int slot, f32x16_t (&s)[2]) {
+  // S^T = K . Q^T of the tile in K slot `slot` (two 32-key halves); hook(m)
+  // runs after the m-th of the 16 MFMAs
+  auto scores = [&](int slot, f32x16_t (&s)[2], auto hook) {
     const uint16_t* Kt = lds[0][slot];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -540,6 +555,7 @@ attn_direct_kernel(AttnParams p) {
         const bf16x8_t a = bitcast<bf16x8_t>(
             *reinterpret_cast<const uint4*>(Kt + k_off[ks] + kb * 32 * kRowElems));
         s[kb] = mfma_32x32x16(a, qf[ks], s[kb]);
+        hook(kb * 8 + ks);
       }
     }
   };
@@ -603,7 +619,7 @@ attn_direct_kernel(AttnParams p) {
   };
   // O^T += V^T . P^T with the tile in V slot `slot`; A lane: dim row
   // cb*32 + l32, keys kb*32 + sp*16 + hi*4 + {0..3, 8..11}
-  auto pv = [&](int slot, const bf16x8_t (&pb)[2][2]) {
+  auto pv = [&](int slot, const bf16x8_t (&pb)[2][2], auto hook) {
     const uint16_t* Vt = lds[1][slot];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -616,8 +632,10 @@ attn_direct_kernel(AttnParams p) {
           const uint2 a_hi = __builtin_bit_cast(uint2, lds_read_tr16(vp + 8 * kRowElems));
           o[cb] = mfma_32x32x16(bitcast<bf16x8_t>(make_uint4(a_lo.x, a_lo.y, a_hi.x, a_hi.y)),
                                 pb[kb][sp], o[cb]);
+          hook(kb * 8 + sp * 4 + cb);
         }
   };
+  auto no_hook = [](int) {};
 
   // The copies are inline asm, invisible to the compiler's wait-count
   // tracking, and a workgroup barrier's fence does not wait for them: every
@@ -631,7 +649,7 @@ attn_direct_kernel(AttnParams p) {
   // prologue: scores of tile 0
   f32x16_t s_cur[2];
   publish();
-  scores(0, s_cur);
+  scores(0, s_cur, no_hook);
   if (n_full == 0) mask(0, s_cur);
   rescale(row_max(s_cur));
 
@@ -642,13 +660,15 @@ attn_direct_kernel(AttnParams p) {
     // makes every wave's copies visible and guarantees that step j-1 (which
     // read K(j) and V(j-1)) is finished everywhere.
     publish();
-    if (j + 2 < n_tiles) issue_copy<NW, false>(src_of(j + 2), g, kbase_of(j + 2), lds_k0 + (j & 1) * kSlotBytes, cl);
-    issue_copy<NW, true>(src_of(j + 1), g, kbase_of(j + 1), lds_v0 + ((j + 1) & 1) * kSlotBytes, cl);
+    // K(j+2) into the K slot of tile j, V(j+1) into the V slot of tile j-1
+    if (j + 2 < n_tiles)
+      TileCopy<NW, false>(src_of(j + 2), g, kbase_of(j + 2), lds_k0 + (j & 1) * kSlotBytes).issue_all(cl);
+    TileCopy<NW, true>(src_of(j + 1), g, kbase_of(j + 1), lds_v0 + ((j + 1) & 1) * kSlotBytes).issue_all(cl);
     bf16x8_t pb[2][2];
     probs(s_cur, pb);
     f32x16_t s_nxt[2];
-    scores((j + 1) & 1, s_nxt);
-    pv(j & 1, pb);
+    scores((j + 1) & 1, s_nxt, no_hook);
+    pv(j & 1, pb, no_hook);
     if constexpr (MASK_NEXT) mask(j + 1, s_nxt);
     const float mt = row_max(s_nxt);
     rescale(mt);
@@ -664,7 +684,7 @@ attn_direct_kernel(AttnParams p) {
     publish();
     bf16x8_t pb[2][2];
     probs(s_cur, pb);
-    pv(j & 1, pb);
+    pv(j & 1, pb, no_hook);
   }
 
   const float l_tot = xor32_sum(l_run);
@@ -686,7 +706,13 @@ attn_direct_kernel(AttnParams p) {
   }
 }
 
-int attn_rows_per_wave(int, bool) { return kQRows; }
+static int direct_token_groups(int group) { return group == 8 ? 1 : kAttnTokenGroups; }
+
+int attn_tile_tokens(int group, bool any_fp8) {
+  const int nw = group >= 4 ? group : 4;
+  const int tg = any_fp8 ? 1 : direct_token_groups(group);
+  return kQRows * nw * tg / group;
+}
 
 hipError_t launch_attn_bf16(const AttnParams& p, int group, bool any_fp8, hipStream_t s) {
   if (p.n_tiles == 0) return hipSuccess;
@@ -695,11 +721,12 @@ hipError_t launch_attn_bf16(const AttnParams& p, int group, bool any_fp8, hipStr
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 gr((unsigned)grid);
   if (!any_fp8) {
+    constexpr int TG = kAttnTokenGroups;
     switch (group) {
-      case 1: attn_direct_kernel<1><<<gr, dim3(256), 0, s>>>(p); break;
-      case 2: attn_direct_kernel<2><<<gr, dim3(256), 0, s>>>(p); break;
-      case 4: attn_direct_kernel<4><<<gr, dim3(256), 0, s>>>(p); break;
-      case 8: attn_direct_kernel<8><<<gr, dim3(512), 0, s>>>(p); break;
+      case 1: attn_direct_kernel<1, TG><<<gr, dim3(256 * TG), 0, s>>>(p); break;
+      case 2: attn_direct_kernel<2, TG><<<gr, dim3(256 * TG), 0, s>>>(p); break;
+      case 4: attn_direct_kernel<4, TG><<<gr, dim3(256 * TG), 0, s>>>(p); break;
+      case 8: attn_direct_kernel<8, 1><<<gr, dim3(512), 0, s>>>(p); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

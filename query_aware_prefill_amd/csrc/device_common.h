@@ -96,6 +96,9 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // 16 bytes per lane from global memory straight into LDS: lane i writes
 // lds_base + 16*i (gfx950 global_load_lds_dwordx4; lds_base is wave-uniform).
+// An LDS-DMA load that reads M0 right after an SALU write of M0 needs one
+// wait state on this generation, hence the s_nop inside the asm (the
+// compiler's hazard recognizer does not look into inline asm).
 // Issued through inline asm so that the compiler does not treat every later
 // LDS read as a possible alias of the copy and wait for all copies in flight;
 // callers wait explicitly (s_waitcnt vmcnt) before the barrier that publishes
@@ -104,7 +107,7 @@ __device__ __forceinline__ void copy16_to_lds(const void* gptr, const void* lds_
   // the low 32 bits of a generic pointer into LDS are its LDS offset (no null
   // check needed: lds_base always points into a __shared__ array)
   const uint32_t lds = (uint32_t)reinterpret_cast<uintptr_t>(lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
@@ -114,7 +117,7 @@ __device__ __forceinline__ void copy16_to_lds(const void* gptr, const void* lds_
 // byte offset (the saddr form: no 64-bit address arithmetic per lane).
 // `lds_addr` is the wave-uniform LDS byte address of the 1-KB destination.
 __device__ __forceinline__ void copy16_to_lds_off(const void* sbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(lds_addr)
                : "memory", "m0");

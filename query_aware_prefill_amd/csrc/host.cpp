@@ -128,12 +128,8 @@ class Blob {
   std::vector<uint8_t> bytes_;
 };
 
-// query tokens per attention tile for GQA group size G (the kernel's waves
-// cover the G heads x (waves / G) token groups)
-int group_tokens(int G, bool any_fp8) {
-  const int nw = G >= 4 ? G : 4;
-  return attn_rows_per_wave(G, any_fp8) * (nw / G);
-}
+// query tokens per attention tile for GQA group size G
+int group_tokens(int G, bool any_fp8) { return attn_tile_tokens(G, any_fp8); }
 
 bool valid_group(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
 

@@ -117,7 +117,8 @@ struct Head8Params {
 // kernel); otherwise the direct HBM->LDS kernel runs.
 hipError_t launch_attn_bf16(const AttnParams& p, int group, bool any_fp8, hipStream_t s);
 // Query tokens one wave of that launch covers (tiles hold (waves / group) of these).
-int attn_rows_per_wave(int group, bool any_fp8);
+// query tokens per attention tile (one workgroup) for GQA group size `group`
+int attn_tile_tokens(int group, bool any_fp8);
 hipError_t launch_attn_f32(const AttnF32Params& p, hipStream_t s);
 hipError_t launch_gemm(const GemmParams& p, GemmEpi epi, hipStream_t s);
 hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s);

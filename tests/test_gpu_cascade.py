@@ -107,6 +107,22 @@ def test_bf16_ragged_cases(B, ci):
     assert np.max(np.abs(lse - ref_l)) <= 1e-3 + 1e-4 * np.max(np.abs(ref_l))
 
 
+@pytest.mark.parametrize("S", [1, 4, 33])
+def test_stream_shape(B, S):
+    """Anchor-KV streaming shape: 768-token anchors, each read by one suffix
+    of S tokens (one query tile per anchor, mostly empty rows at small S)."""
+    a_len, s_anchor, s_len = W.stream_lengths(S, n_anchors=5)
+    say("stream shape S =", S)
+    case = W.cascade_case(40 + S, a_len, s_anchor, s_len, hq=32, hkv=8, d=128, dtype="bf16", cfg_id=12)
+    o, lse = _run(B, case)
+    ref_o, ref_l = OA.cascade_case_reference(case)
+    for s in range(len(s_len)):
+        sl = slice(case["s_off"][s], case["s_off"][s + 1])
+        err = rel_inf(o[sl], ref_o[sl])
+        assert err <= 2e-2, (s, err)
+    assert np.max(np.abs(lse - ref_l)) <= 1e-3 + 1e-4 * np.max(np.abs(ref_l))
+
+
 def test_c1_reduced_full_length_ranges(B):
     """4 anchors of U{512..2048} x 8 suffixes of U{32..128}, 32q/8kv x 128."""
     say("C1 reduced")

@@ -290,13 +290,14 @@ def c1_case(seed: int = 1, n_anchors: int = 256, per_anchor: int = 64,
                         dtype="bf16", cfg_id=1)
 
 
-def c1_device(seed: int = 1, device="cuda", n_anchors: int = 256,
-              per_anchor: int = 64, la_range=(512, 2048), ls_range=(32, 128)):
-    """Full-size C1 drawn directly in device memory with torch's seeded
-    generator (N(0,1) float32 draws converted to bf16). Same lengths as
-    ``c1_case``; values differ (different generator)."""
+def cascade_device(seed, a_len, s_anchor, s_len, device="cuda", hq=32, hkv=8, d=128):
+    """A bf16 cascade-attention case drawn directly in device memory with
+    torch's seeded generator (N(0,1) float32 draws converted to bf16); the
+    arrays and keys are those of ``cascade_case``."""
     import torch
-    a_len, s_anchor, s_len = c1_lengths(seed, n_anchors, per_anchor, la_range, ls_range)
+    a_len = np.asarray(a_len, np.int32)
+    s_anchor = np.asarray(s_anchor, np.int32)
+    s_len = np.asarray(s_len, np.int32)
     a_off = np.zeros(len(a_len) + 1, np.int32)
     a_off[1:] = np.cumsum(a_len)
     s_off = np.zeros(len(s_len) + 1, np.int32)
@@ -316,11 +317,30 @@ def c1_device(seed: int = 1, device="cuda", n_anchors: int = 256,
         return out
 
     TA, TS = int(a_off[-1]), int(s_off[-1])
-    ak = draw((TA, 8, 128)); av = draw((TA, 8, 128))
-    q = draw((TS, 32, 128)); k = draw((TS, 8, 128)); v = draw((TS, 8, 128))
+    ak = draw((TA, hkv, d)); av = draw((TA, hkv, d))
+    q = draw((TS, hq, d)); k = draw((TS, hkv, d)); v = draw((TS, hkv, d))
     return dict(a_len=a_len, a_off=a_off, s_anchor=s_anchor, s_len=s_len,
-                s_off=s_off, ak=ak, av=av, q=q, k=k, v=v, hq=32, hkv=8, d=128,
-                dtype="bf16", sm_scale=1.0 / math.sqrt(128))
+                s_off=s_off, ak=ak, av=av, q=q, k=k, v=v, hq=hq, hkv=hkv, d=d,
+                dtype="bf16", sm_scale=1.0 / math.sqrt(d))
+
+
+def c1_device(seed: int = 1, device="cuda", n_anchors: int = 256,
+              per_anchor: int = 64, la_range=(512, 2048), ls_range=(32, 128)):
+    """Full-size C1 drawn directly in device memory (see ``cascade_device``).
+    Same lengths as ``c1_case``; values differ (different generator)."""
+    a_len, s_anchor, s_len = c1_lengths(seed, n_anchors, per_anchor, la_range, ls_range)
+    return cascade_device(seed, a_len, s_anchor, s_len, device)
+
+
+def stream_lengths(S: int, n_anchors: int = 1024, la: int = 768):
+    """Anchor-KV streaming shape of the multi-join configuration: n_anchors
+    anchors of la tokens (the resident KV), each read by one suffix of S
+    tokens, so the attention intensity grows with S (4*S FLOP per bf16 KV
+    byte)."""
+    a_len = np.full(n_anchors, la, np.int32)
+    s_anchor = np.arange(n_anchors, dtype=np.int32)
+    s_len = np.full(n_anchors, S, np.int32)
+    return a_len, s_anchor, s_len
 
 
 # ----------------------------------------------------------------------------
