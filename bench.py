@@ -34,6 +34,18 @@ Secondary measurements (not the headline line; each prints its own JSON):
                      one suffix of S tokens, S in {1, 4, 16, 64, 256}; anchor
                      KV bytes per launch / launch time against 8 TB/s, and
                      TFLOP/s (the intensity is 4*S FLOP per KV byte).
+  --workload join36 | filter36 | multijoin36
+                     end to end on the 36-layer Qwen3-4B-shaped stack with
+                     random-init fp8 weights (quail_join_run: plan, anchor
+                     prefill + KV writer, join prefill, 8-column head):
+                     join36 = 64 anchors x 1024 tokens, 2048 suffixes of 64
+                     tokens each; filter36 = 10,000 rows of lognormal lengths
+                     200..2000, no anchor; multijoin36 = 1024 anchors x 768
+                     tokens with fp8 KV, rows of U{48..256} tokens each probing
+                     51 anchors (--rows selects how many of the 5,000 rows).
+                     Logical and computed tokens/min; the oracle leg runs the
+                     per-pair definition on a few sampled pairs and compares
+                     logits and decisions.
   --workload layer   one decoder layer of the Qwen3-4B shape, random-init fp8
                      weights: 16 anchors x 1024 tokens, 512 suffixes x 64
                      tokens per anchor, run end to end by quail_join_run
@@ -249,6 +261,137 @@ def bench_stream(args):
     print(json.dumps(out), flush=True)
 
 
+def cpu_baseline_e2e(wd, shape, pairs, gpu_logits, true_mask, budget_s):
+    """Oracle leg of the end-to-end modes: the per-pair definition (monolithic
+    causal forward over [anchor | suffix], head at the last position), fp32
+    with the contract's bf16 rounding points, on pairs taken in the given
+    (random) order until the time budget is spent; logits and decisions are
+    compared with the GPU's. Dequantising the weights is setup, not timed."""
+    import torch
+    import workloads as W
+    from oracle import model as OM
+    t0 = time.perf_counter()
+    wh = W.weights_to_host(wd)
+    layers = [OM.LayerWeights(lw, shape, np.float32) for lw in wh["layers"]]
+    setup = time.perf_counter() - t0
+    spent, logical, done = 0.0, 0, 0
+    worst, agree, decided = 0.0, 0, 0
+    for i, a_tok, s_tok in pairs:
+        c0 = time.perf_counter()
+        r = OM.forward_pair(a_tok, s_tok, wh, shape, true_mask, mode="contract", dtype=np.float32,
+                            layers=layers)
+        spent += time.perf_counter() - c0
+        done += 1
+        logical += len(a_tok) + len(s_tok)
+        g = gpu_logits[i]
+        ref = np.asarray(r["logits"], np.float64)
+        worst = max(worst, float(np.max(np.abs(g - ref)) / max(np.max(np.abs(ref)), 1e-30)))
+        tau = 2e-2 * float(np.max(np.abs(ref)))
+        if abs(r["margin"]) > tau:
+            decided += 1
+            gk = int(np.argmax(g))
+            agree += int(((true_mask >> gk) & 1) == r["decision"])
+        if spent >= budget_s:
+            break
+    return {"value": logical / spent * 60.0, "unit": "tokens/min", "cores": int(torch.get_num_threads()),
+            "kind": "oracle",
+            "sample": f"{done} pairs drawn at random from the workload, full 36-layer forward of "
+                      f"[anchor | suffix] in float32 with the bf16 rounding points "
+                      f"({logical} logical tokens in {spent:.1f} s; weight dequantisation "
+                      f"{setup:.1f} s not timed)",
+            "check": {"pairs": done, "max_rel_logit_err": worst, "decisions_beyond_tau": decided,
+                      "decisions_agree": agree}}
+
+
+def bench_e2e(args):
+    import torch
+    import workloads as W
+    from query_aware_prefill_amd import binding as B
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    B.load()
+    kind = args.workload
+    shape = W.QWEN3_4B
+    if kind == "multijoin36":
+        shape = W.ModelShape(**{**shape.__dict__, "kv_fp8": True})
+    log(f"{kind}: generating the workload")
+    if kind == "join36":
+        case = W.c3b_case()
+        a_len, a_off, a_tok = case["a_len"], case["a_off"], case["a_tok"]
+        pair_anchor, s_off, s_tok = case["pair_anchor"], case["s_off"], case["s_tok"]
+        desc = "join: 64 anchors x 1024 tokens, 2048 suffixes of 64 tokens per anchor (131,072 pairs)"
+    elif kind == "filter36":
+        case = W.c3a_case()
+        a_len, a_off = case["a_len"], case["a_off"]
+        a_tok = case["a_tok"] if len(case["a_tok"]) else np.zeros(1, np.int32)
+        pair_anchor, s_off, s_tok = case["pair_anchor"], case["s_off"], case["s_tok"]
+        desc = "filter: 10,000 rows, lognormal lengths 200..2000, no anchor"
+    else:
+        case = W.c4_case()
+        rows = min(args.rows, len(case["row_len"]))
+        keep = case["pair_row"] < rows
+        a_len, a_off, a_tok = case["a_len"], case["a_off"], case["a_tok"]
+        pair_anchor = case["pair_anchor"][keep]
+        prow = case["pair_row"][keep]
+        plen = case["row_len"][prow]
+        s_off = np.zeros(len(prow) + 1, np.int64)
+        s_off[1:] = np.cumsum(plen)
+        s_tok = np.concatenate([case["row_tok"][case["row_off"][r]:case["row_off"][r + 1]] for r in prow])
+        s_off = s_off.astype(np.int32)
+        desc = (f"multi-join: 1024 anchors x 768 tokens (fp8 KV), {rows} of the 5,000 rows of "
+                f"U{{48..256}} tokens, 51 anchors per row ({len(prow)} pairs)")
+    s_len = np.diff(s_off).astype(np.int64)
+    log(f"{kind}: {len(pair_anchor)} pairs, {int(np.sum(s_len))} suffix tokens; weights on device")
+    wd = W.model_weights_device(shape, 0)
+    max_a = int(np.max(a_len)) if len(a_len) else 0
+    dm = DeviceModel(shape, wd, max_anchor_len=max(max_a, 1), max_suffix_len=int(np.max(s_len)))
+    T = 65536
+    used = np.unique(pair_anchor[pair_anchor >= 0])
+    pool = sum(B.quail_anchor_bytes(dm.cfg, int(a_len[a])) for a in used) + (1 << 20) if len(used) else 1 << 20
+    pool = min(pool, 96 << 30)
+    ctx = dm.context(pool, T)
+    a_tok_d, s_tok_d = to_device(a_tok.astype(np.int32)), to_device(s_tok.astype(np.int32))
+    n = len(pair_anchor)
+    logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+    dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+    log(f"{kind}: pool {pool / 2**30:.2f} GiB; running")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    B.quail_join_run(ctx, a_tok_d, a_off, pair_anchor, s_tok_d, s_off, 0x0F, logits, None, dec)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0
+    la = np.where(pair_anchor >= 0, a_len[np.maximum(pair_anchor, 0)] if len(a_len) else 0, 0).astype(np.int64)
+    suffix_tok = int(np.sum(s_len))
+    anchor_tok = int(np.sum(a_len[used])) if len(used) else 0
+    logical = int(np.sum(la) + suffix_tok)
+    st = B.quail_pool_stats(ctx)
+    # executed GEMM work: every suffix token runs all 36 layers (201.85 MFLOP
+    # per token per layer); anchors run 35 full layers and the last layer's
+    # QKV projection only (their last-layer output is not needed)
+    gemm = 201_850_880.0 * suffix_tok * shape.n_layers + anchor_tok * (
+        201_850_880.0 * (shape.n_layers - 1) + 31_457_280.0)
+    attn = 16384.0 * shape.n_layers * float(np.sum(s_len * la) + np.sum(s_len * (s_len + 1) / 2))
+    attn += 16384.0 * (shape.n_layers - 1) * float(sum(int(a_len[a]) * (int(a_len[a]) + 1) / 2 for a in used))
+    res = {"metric": "end-to-end prefill tokens/min (36-layer stack)", "workload": desc, "unit": "tokens/min",
+           "ms": ms, "pairs": int(n), "logical_tokens": logical, "computed_tokens": suffix_tok + anchor_tok,
+           "logical_tokens_per_min": logical / (ms * 1e-3) * 60.0,
+           "computed_tokens_per_min": (suffix_tok + anchor_tok) / (ms * 1e-3) * 60.0,
+           "algorithmic_tflops": (gemm + attn) / (ms * 1e-3) / 1e12, "pool": st,
+           "weights": "random init on device (W ~ N(0, 0.02), per-row bf16 scales, E4M3 codes)"}
+    log(f"{kind}: {ms / 1000:.2f} s, {res['logical_tokens_per_min'] / 1e9:.3f} G logical tok/min, "
+        f"{res['algorithmic_tflops']:.1f} TFLOP/s")
+    if not args.no_cpu_baseline:
+        lg = logits.cpu().numpy().astype(np.float64)
+        order = np.random.default_rng(0).permutation(n)[:16]
+        pairs = []
+        for i in order:
+            a = int(pair_anchor[i])
+            at = a_tok[a_off[a]:a_off[a + 1]] if a >= 0 else np.zeros(0, np.int32)
+            pairs.append((int(i), at, s_tok[s_off[i]:s_off[i + 1]]))
+        log(f"{kind}: oracle leg")
+        res["cpu_baseline"] = cpu_baseline_e2e(wd, shape, pairs, lg, 0x0F, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
 def bench_layer(args):
     import torch
     import workloads as W
@@ -307,8 +450,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--workload", choices=["cascade", "gemm", "layer", "copy", "stream"],
-                    default="cascade")
+    ap.add_argument("--workload", choices=["cascade", "gemm", "layer", "copy", "stream", "join36",
+                                           "filter36", "multijoin36"], default="cascade")
+    ap.add_argument("--rows", type=int, default=625, help="multijoin36: rows of the 5,000 used")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -324,6 +468,8 @@ def main():
         return bench_copy(args)
     if args.workload == "stream":
         return bench_stream(args)
+    if args.workload in ("join36", "filter36", "multijoin36"):
+        return bench_e2e(args)
 
     import torch
     import workloads as W

@@ -9,10 +9,12 @@ import numpy as np
 from . import binding as B
 
 
-def to_device(a: np.ndarray, device="cuda"):
+def to_device(a, device="cuda"):
     """Copy a numpy array to the device byte for byte (uint16 is carried as
-    int16, since both are raw bf16 bits here)."""
+    int16, since both are raw bf16 bits here); device tensors pass through."""
     import torch
+    if isinstance(a, torch.Tensor):
+        return a.to(device).contiguous()
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         a = a.view(np.int16)

@@ -203,6 +203,56 @@ def model_weights(shape: ModelShape, seed: int = 0, with_layers=True) -> dict:
     return w
 
 
+def model_weights_device(shape: ModelShape, seed: int = 0, device="cuda") -> dict:
+    """Random-init weights drawn directly in device memory with torch's seeded
+    generator (for full-size models, whose host generation takes minutes).
+    Same keys and formats as ``model_weights`` (bf16 as int16 bits, fp8 as
+    uint8 OCP E4M3 codes); values differ. Projection weights follow the recipe
+    W ~ N(0, 0.02), per-row scale = bf16(max|W_row| / 448), codes = the E4M3
+    rounding of W / scale (clamped to +-448 first)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(7_000_003 * seed + 11)
+    H, I = shape.hidden, shape.intermediate
+
+    def bf16(shape_, std=1.0, mean=0.0):
+        x = torch.randn(shape_, generator=g, device=device, dtype=torch.float32) * std + mean
+        return x.to(torch.bfloat16).view(torch.int16)
+
+    def fp8_rows(n_out, n_in):
+        codes = torch.empty((n_out, n_in), dtype=torch.uint8, device=device)
+        scales = torch.empty(n_out, dtype=torch.int16, device=device)
+        step = max(1, (1 << 26) // n_in)
+        for r0 in range(0, n_out, step):
+            r1 = min(n_out, r0 + step)
+            w = torch.randn((r1 - r0, n_in), generator=g, device=device, dtype=torch.float32) * 0.02
+            sc = (w.abs().amax(dim=1) / 448.0).to(torch.bfloat16)
+            q = (w / sc.float()[:, None]).clamp_(-448.0, 448.0)
+            codes[r0:r1] = q.to(torch.float8_e4m3fn).view(torch.uint8)
+            scales[r0:r1] = sc.view(torch.int16)
+        return codes, scales
+
+    w = {"embed": bf16((shape.vocab, H)), "final_norm": bf16((H,), 0.1, 1.0),
+         "head8": bf16((H, 8), 0.02), "layers": []}
+    for _ in range(shape.n_layers):
+        lw = {"attn_norm": bf16((H,), 0.1, 1.0), "mlp_norm": bf16((H,), 0.1, 1.0)}
+        for name, (n_out, n_in) in (("qkv", (shape.qkv_dim, H)), ("o", (H, shape.q_dim)),
+                                     ("gate_up", (2 * I, H)), ("down", (H, I))):
+            lw["w_" + name], lw["s_" + name] = fp8_rows(n_out, n_in)
+        w["layers"].append(lw)
+    return w
+
+
+def weights_to_host(w: dict) -> dict:
+    """Host copy (numpy, bf16 as uint16 bits) of device weights."""
+    def h(t):
+        a = t.cpu().numpy()
+        return a.view(np.uint16) if a.dtype == np.int16 else a
+    out = {k: h(v) for k, v in w.items() if k != "layers"}
+    out["layers"] = [{k: h(v) for k, v in lw.items()} for lw in w["layers"]]
+    return out
+
+
 def full_head(shape: ModelShape, seed: int = 0, vocab=None) -> np.ndarray:
     """A full unembedding [hidden, vocab] (bf16) for head-restriction checks."""
     V = vocab or shape.vocab
