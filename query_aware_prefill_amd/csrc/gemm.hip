@@ -33,6 +33,9 @@
 
 namespace quail {
 
+// token tiles per workgroup group (see the grouped order in gemm_direct_kernel)
+constexpr int kGemmGroupM = 4;
+
 // silu(g) = g / (1 + e^-g): v_exp_f32 (2^x) and v_rcp_f32, each about 1 ulp,
 // far below the bf16 rounding of the product that follows
 __device__ __forceinline__ float silu_f(float g) {
@@ -221,8 +224,16 @@ gemm_direct_kernel(GemmParams p) {
   const int64_t total = (int64_t)n_tn * n_tm;
   const int64_t wid = xcd_remap(blockIdx.x, total);
   if (wid < 0) return;
-  const int tm = (int)(wid / n_tn);
-  const int tn = (int)(wid % n_tn);
+  // Grouped order: logical ids sweep kGemmGroupM token tiles x all column
+  // tiles, column-major inside the group, so the workgroups that run at the
+  // same time on one XCD share both their activation rows and their weight
+  // rows through that XCD's L2.
+  const int64_t per_group = (int64_t)kGemmGroupM * n_tn;
+  const int64_t grp = wid / per_group;
+  const int64_t rem = wid % per_group;
+  const int gm_rows = (int)min<int64_t>(kGemmGroupM, n_tm - grp * kGemmGroupM);
+  const int tm = (int)(grp * kGemmGroupM + rem % gm_rows);
+  const int tn = (int)(rem / gm_rows);
   const int m0 = tm * BM;
 
   const int tid = threadIdx.x;
