@@ -426,24 +426,234 @@ struct TileCopy {
 template <bool B>
 struct MaskTag { static constexpr bool value = B; };
 
+// The key tiles one workgroup visits: first the cross tiles of its anchor
+// source (the last one ragged), then the self tiles from self_k0 up to its
+// last query. Tiles j >= n_full need masking.
+struct TileSeq {
+  KVSrc cs{}, ss{};
+  int n_ct = 0, n_st = 0, n_full = 0, n_tiles = 0, self_k0 = 0;
+  __device__ __forceinline__ TileSeq(const AttnParams& p, const AttnTile& tile) {
+    if (tile.cross >= 0) {
+      cs = p.srcs[tile.cross];
+      n_ct = (cs.len + kKeyTile - 1) / kKeyTile;
+      n_full = cs.len / kKeyTile;
+    }
+    if (tile.self >= 0) {
+      ss = p.srcs[tile.self];
+      n_st = max(0, (tile.self_qbase + tile.nq - tile.self_k0 + kKeyTile - 1) / kKeyTile);
+    }
+    n_tiles = n_ct + n_st;
+    self_k0 = tile.self_k0;
+  }
+  __device__ __forceinline__ const KVSrc& src(int j) const { return j < n_ct ? cs : ss; }
+  __device__ __forceinline__ int kbase(int j) const { return j < n_ct ? j * kKeyTile : self_k0 + (j - n_ct) * kKeyTile; }
+};
+
+// One wave's share of the bf16 MFMA attention: 32 query rows of one head
+// (lane % 32 owns row l32; the two lanes of a row split its keys), the
+// operand-read offsets into a K / V tile in LDS, the O^T accumulator and the
+// online-softmax state.
+struct WaveAttn {
+  bf16x8_t qf[8];       // Q as the B operand: dims ks*16 + hi*8 .. +7
+  f32x16_t o[4];
+  float m_run, l_run, scale_log2;
+  int lane, hi, lo_self, hi_self;
+
+  // LDS element offset of the K operand (A of S^T) for k-step ks: key row
+  // l32, 16-B chunk swz_k(l32, ks*2 + hi); the 32-key half is a constant row
+  // offset. Formed where used (a few VALU ops next to the MFMAs) rather than
+  // kept in registers across the loop.
+  __device__ __forceinline__ uint32_t k_off(int ks) const {
+    const int l32 = lane & 31;
+    return l32 * kRowElems + swz_k(l32, ks * 2 + hi) * 8;
+  }
+  // LDS element offset of the V^T operand (A of O^T, read with
+  // ds_read_tr16_b64) for 32-dim block cb: within each 16-lane block lane j
+  // points at key (j / 4) of a 4-key group and dims 4*(j % 4) .. +3 of a
+  // 16-dim half; the 4-key groups start at multiples of 4, so the swizzle
+  // term depends on the lane only and the key-group terms are constant rows.
+  __device__ __forceinline__ uint32_t v_off(int cb) const {
+    const int trj = lane & 15;
+    const int tr_key = hi * 4 + (trj >> 2);
+    const int d0 = cb * 32 + 16 * ((lane >> 4) & 1) + 4 * (trj & 3);
+    return tr_key * kRowElems + swz_v(tr_key, d0 >> 3) * 8 + (d0 & 7);
+  }
+
+  __device__ __forceinline__ void init(const AttnParams& p, const AttnTile& tile, int64_t tok,
+                                       bool row_ok, int qrow, int head, int lane_) {
+    lane = lane_;
+    hi = lane >> 5;
+    const uint16_t* qp = p.q + tok * p.q_stride + head * kHeadDim + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
+      qf[ks] = bitcast<bf16x8_t>(u);
+    }
+    // self keys visible to this row: [first key of its segment, its own key]
+    lo_self = row_ok ? p.seg_lo[tok] : 0;
+    hi_self = row_ok ? tile.self_qbase + qrow : -1;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[cb][r] = 0.0f;
+    // running reference of the online softmax (log2 units); finite start:
+    // the first visible score always triggers a rescale (alpha = 0), and
+    // rows with no visible key keep P = 0
+    m_run = -1e30f;
+    l_run = 0.0f;
+    scale_log2 = p.scale_log2;
+  }
+
+  // S^T = K . Q^T of the tile at Kt (two 32-key halves)
+  __device__ __forceinline__ void scores(const uint16_t* Kt, f32x16_t (&s)[2]) const {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8_t a = bitcast<bf16x8_t>(
+            *reinterpret_cast<const uint4*>(Kt + k_off(ks) + kb * 32 * kRowElems));
+        s[kb] = mfma_32x32x16(a, qf[ks], s[kb]);
+      }
+    }
+  }
+
+  // mask a tile starting at key kbase: visible keys are [0, cross_len) for a
+  // cross tile, [lo_self, hi_self] for a self tile; the key of (kb, r) is
+  // kbase + kb*32 + hi*4 + (r/4)*8 + r%4 (unsigned range test)
+  __device__ __forceinline__ void mask(f32x16_t (&s)[2], int kbase, bool cross, int cross_len) const {
+    const int lo = cross ? 0 : lo_self;
+    const int hk = cross ? cross_len - 1 : hi_self;
+    const uint32_t range = (uint32_t)(hk - lo);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint32_t x = (uint32_t)(kbase + kb * 32 + hi * 4 - lo);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t c = (uint32_t)((r >> 2) * 8 + (r & 3));
+        s[kb][r] = (x + c <= range) ? s[kb][r] : -INFINITY;
+      }
+    }
+  }
+
+  // row max of a tile over both lanes of the row, log2 units
+  __device__ __forceinline__ float row_max(const f32x16_t (&s)[2]) const {
+    float m0 = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) m0 = fmaxf(m0, fmaxf(s[0][r], s[1][r]));
+    return xor32_max(m0) * scale_log2;
+  }
+
+  // Lazy rescale: the running reference moves only when a row's max exceeds
+  // it by more than 8 (log2 units), so P stays below 2^8 and O is rescaled
+  // only on those (rare, wave-uniform) occasions. O / l and the LSE are exact
+  // for any reference.
+  __device__ __forceinline__ void rescale(float mt) {
+    if (__ballot(mt > m_run + 8.0f) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[cb][r] *= alpha;
+    }
+  }
+
+  // P = 2^(s*scale - m_run) in bf16 as the B operand: k-step (kb, sp) takes
+  // regs 8*sp .. 8*sp+7 of half kb; the row sum adds the fp32 values
+  __device__ __forceinline__ void probs(const f32x16_t (&s)[2], bf16x8_t (&pb)[2][2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][sp * 8 + 2 * e], scale_log2, -m_run));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][sp * 8 + 2 * e + 1], scale_log2, -m_run));
+          l_run += p0 + p1;
+          w[e] = pack_bf16x2(p0, p1);
+        }
+        pb[kb][sp] = bitcast<bf16x8_t>(make_uint4(w[0], w[1], w[2], w[3]));
+      }
+  }
+
+  // O^T += V^T . P^T with the tile at Vt; A lane: dim row cb*32 + l32, keys
+  // kb*32 + sp*16 + hi*4 + {0..3, 8..11}
+  __device__ __forceinline__ void pv(const uint16_t* Vt, const bf16x8_t (&pb)[2][2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          const uint16_t* vp = Vt + v_off(cb) + (kb * 32 + sp * 16) * kRowElems;
+          const uint2 a_lo = __builtin_bit_cast(uint2, lds_read_tr16(vp));
+          const uint2 a_hi = __builtin_bit_cast(uint2, lds_read_tr16(vp + 8 * kRowElems));
+          o[cb] = mfma_32x32x16(bitcast<bf16x8_t>(make_uint4(a_lo.x, a_lo.y, a_hi.x, a_hi.y)),
+                                pb[kb][sp], o[cb]);
+        }
+  }
+
+  // O / l as bf16 and the natural-log LSE (-inf without a visible key)
+  __device__ __forceinline__ void store(const AttnParams& p, int64_t tok, bool row_ok, int head) const {
+    const float l_tot = xor32_sum(l_run);
+    if (!row_ok) return;
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    uint16_t* op = p.out + tok * p.o_stride + head * kHeadDim + hi * 4;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        uint2 w;
+        w.x = pack_bf16x2(o[cb][rg * 4 + 0] * inv, o[cb][rg * 4 + 1] * inv);
+        w.y = pack_bf16x2(o[cb][rg * 4 + 2] * inv, o[cb][rg * 4 + 3] * inv);
+        *reinterpret_cast<uint2*>(op + cb * 32 + rg * 8) = w;
+      }
+    if (p.lse != nullptr && hi == 0) {
+      const float L = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+      p.lse[tok * p.hq + head] = L;
+    }
+  }
+};
+
+// rows of a tile with no visible key at all: zero output, LSE -inf
+__device__ __forceinline__ void store_empty(const AttnParams& p, int64_t tok, bool row_ok, int head, int hi) {
+  if (!row_ok) return;
+  uint16_t* op = p.out + tok * p.o_stride + head * kHeadDim + hi * 4;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) *reinterpret_cast<uint2*>(op + cb * 32 + rg * 8) = make_uint2(0, 0);
+  if (p.lse != nullptr && hi == 0) p.lse[tok * p.hq + head] = -INFINITY;
+}
+
+// Every barrier that publishes copied tiles: the copies are inline asm,
+// invisible to the compiler's wait-count tracking, and a workgroup barrier's
+// fence does not wait for them, so the issuing wave waits for all of its
+// copies in flight first.
+__device__ __forceinline__ void publish() {
+  wait_vmcnt<0>();
+  __syncthreads();
+}
+
 // Software pipeline over the key tiles: while the softmax of tile j (exp,
 // bf16 packing, row sums) runs on the VALU, the S MFMAs of tile j+1 are in
 // flight, and the PV MFMAs of tile j overlap the masking and row max of tile
 // j+1. K and V have two LDS slots each; at step j the copies of K(j+2) and
 // V(j+1) are issued into the slots that step j-1 finished reading, so one
-// barrier per tile suffices.
-// Full cross tiles and the masked tiles (the ragged end of the cross keys,
-// all self tiles) are handled by separate instantiations of the step, so the
-// unmasked step carries no mask code.
-// Token groups of 32 rows per workgroup: the workgroup's waves cover the G
-// query heads of one kv head x (waves / G) token groups and share every K/V
-// tile copied into LDS.
-constexpr int kAttnTokenGroups = 1;
-
-template <int G, int TG>
-__global__ void __launch_bounds__(64 * (G >= 4 ? G : 4) * TG, TG == 1 ? 2 : 1)
+// barrier per tile suffices. Full cross tiles and the masked tiles (the
+// ragged end of the cross keys, all self tiles) are handled by separate
+// instantiations of the step, so the unmasked step carries no mask code.
+// One workgroup: the G query heads of one kv head x (waves / G) groups of 32
+// query tokens, all sharing every K/V tile copied into LDS.
+template <int G>
+__global__ void __launch_bounds__(64 * (G >= 4 ? G : 4), 2)
 attn_direct_kernel(AttnParams p) {
-  constexpr int NW = (G >= 4 ? G : 4) * TG;
+  constexpr int NW = G >= 4 ? G : 4;
   constexpr uint32_t kSlotBytes = kTileElems * 2;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][kTileElems];   // [K,V][slot]
 
@@ -456,263 +666,68 @@ attn_direct_kernel(AttnParams p) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
   const int head = g * G + (wave % G);
-  const int tg = wave / G;
-  const int qrow = tg * kQRows + l32;
+  const int qrow = (wave / G) * kQRows + (lane & 31);
   const bool row_ok = qrow < tile.nq;
   const int64_t tok = (int64_t)tile.q0 + qrow;
 
-  KVSrc cs{}, ss{};
-  int n_ct = 0, n_st = 0, n_full = 0;
-  if (tile.cross >= 0) {
-    cs = p.srcs[tile.cross];
-    n_ct = (cs.len + kKeyTile - 1) / kKeyTile;
-    n_full = cs.len / kKeyTile;
-  }
-  if (tile.self >= 0) {
-    ss = p.srcs[tile.self];
-    n_st = max(0, (tile.self_qbase + tile.nq - tile.self_k0 + kKeyTile - 1) / kKeyTile);
-  }
-  const int n_tiles = n_ct + n_st;
-  if (n_tiles == 0) {
-    // no visible key: zero output, LSE -inf
-    if (row_ok) {
-      uint16_t* op = p.out + tok * p.o_stride + head * kHeadDim + hi * 4;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) *reinterpret_cast<uint2*>(op + cb * 32 + rg * 8) = make_uint2(0, 0);
-      if (p.lse != nullptr && hi == 0) p.lse[tok * p.hq + head] = -INFINITY;
-    }
+  const TileSeq ts(p, tile);
+  if (ts.n_tiles == 0) {
+    store_empty(p, tok, row_ok, head, lane >> 5);
     return;
   }
-  auto src_of = [&](int j) -> const KVSrc& { return j < n_ct ? cs : ss; };
-  auto kbase_of = [&](int j) { return j < n_ct ? j * kKeyTile : tile.self_k0 + (j - n_ct) * kKeyTile; };
-
   const uint32_t lds_k0 = lds_addr_of(&lds[0][0][0]);
   const uint32_t lds_v0 = lds_addr_of(&lds[1][0][0]);
   const CopyLanes<NW> cl = copy_lanes<NW>(wave, lane);
-  TileCopy<NW, false>(src_of(0), g, kbase_of(0), lds_k0).issue_all(cl);
-  TileCopy<NW, true>(src_of(0), g, kbase_of(0), lds_v0).issue_all(cl);
-  if (n_tiles > 1) TileCopy<NW, false>(src_of(1), g, kbase_of(1), lds_k0 + kSlotBytes).issue_all(cl);
+  TileCopy<NW, false>(ts.src(0), g, ts.kbase(0), lds_k0).issue_all(cl);
+  TileCopy<NW, true>(ts.src(0), g, ts.kbase(0), lds_v0).issue_all(cl);
+  if (ts.n_tiles > 1) TileCopy<NW, false>(ts.src(1), g, ts.kbase(1), lds_k0 + kSlotBytes).issue_all(cl);
 
-  // Q fragments: B operand, lane holds query row l32, dims ks*16 + hi*8 .. +7
-  bf16x8_t qf[8];
-  {
-    const uint16_t* qp = p.q + tok * p.q_stride + head * kHeadDim + hi * 8;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
-      qf[ks] = bitcast<bf16x8_t>(u);
-    }
-  }
-  const int seg_lo = row_ok ? p.seg_lo[tok] : 0;
-  const int self_q = row_ok ? tile.self_qbase + qrow : -1;
-
-  // per-lane LDS element offsets of the operand reads within a slot
-  // K (A of S^T): key row kb*32 + l32, 16-B chunk swz_k(key, ks*2 + hi); the
-  // kb term is a constant row offset.
-  uint32_t k_off[8];
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) k_off[ks] = l32 * kRowElems + swz_k(l32, ks * 2 + hi) * 8;
-  // V^T (A of O^T) through ds_read_tr16_b64: within each 16-lane block lane j
-  // points at key (j / 4) of a 4-key group and dims 4*(j % 4) .. +3 of a
-  // 16-dim half; the 4-key groups start at multiples of 4, so the swizzle
-  // term depends on the lane only and the key-group terms are constant rows.
-  const int trj = lane & 15;
-  const int tr_key = hi * 4 + (trj >> 2);
-  const int tr_d0 = 16 * ((lane >> 4) & 1) + 4 * (trj & 3);
-  uint32_t v_off[4];
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    const int d0 = cb * 32 + tr_d0;
-    v_off[cb] = tr_key * kRowElems + swz_v(tr_key, d0 >> 3) * 8 + (d0 & 7);
-  }
-
-  f32x16_t o[4];
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[cb][r] = 0.0f;
-  // Running reference of the online softmax (log2 units). Finite start value:
-  // the first visible score always triggers a rescale (alpha = 0), and rows
-  // with no visible key keep P = 0.
-  float m_run = -1e30f;
-  float l_run = 0.0f;
-
-  // S^T = K . Q^T of the tile in K slot `slot` (two 32-key halves); hook(m)
-  // runs after the m-th of the 16 MFMAs
-  auto scores = [&](int slot, f32x16_t (&s)[2], auto hook) {
-    const uint16_t* Kt = lds[0][slot];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8_t a = bitcast<bf16x8_t>(
-            *reinterpret_cast<const uint4*>(Kt + k_off[ks] + kb * 32 * kRowElems));
-        s[kb] = mfma_32x32x16(a, qf[ks], s[kb]);
-        hook(kb * 8 + ks);
-      }
-    }
-  };
-  // mask tile j: visible keys of this row are [lo, hi_k]; the key of (kb, r)
-  // is kbase + kb*32 + hi*4 + (r/4)*8 + r%4 (unsigned range test)
-  auto mask = [&](int j, f32x16_t (&s)[2]) {
-    const bool cross = j < n_ct;
-    const int lo = cross ? 0 : seg_lo;
-    const int hi_k = cross ? cs.len - 1 : self_q;
-    const uint32_t range = (uint32_t)(hi_k - lo);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const uint32_t x = (uint32_t)(kbase_of(j) + kb * 32 + hi * 4 - lo);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t c = (uint32_t)((r >> 2) * 8 + (r & 3));
-        s[kb][r] = (x + c <= range) ? s[kb][r] : -INFINITY;
-      }
-    }
-  };
-  // row max of a tile (both lanes of the row), log2 units
-  auto row_max = [&](const f32x16_t (&s)[2]) {
-    float m0 = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) m0 = fmaxf(m0, fmaxf(s[0][r], s[1][r]));
-    return xor32_max(m0) * p.scale_log2;
-  };
-  // Lazy rescale: the running reference m_run moves only when a row's max
-  // exceeds it by more than 8 (log2 units), so P stays below 2^8 and O is
-  // rescaled only on those (rare, wave-uniform) occasions. O / l and the LSE
-  // are exact for any reference.
-  auto rescale = [&](float mt) {
-    if (__ballot(mt > m_run + 8.0f) != 0) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[cb][r] *= alpha;
-    }
-  };
-  // P = 2^(s*scale - m_run) in bf16 as the B operand: k-step (kb, sp) takes
-  // regs 8*sp .. 8*sp+7 of half kb; the row sum adds the fp32 values
-  auto probs = [&](const f32x16_t (&s)[2], bf16x8_t (&pb)[2][2]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int sp = 0; sp < 2; ++sp) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][sp * 8 + 2 * e], p.scale_log2, -m_run));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][sp * 8 + 2 * e + 1], p.scale_log2, -m_run));
-          l_run += p0 + p1;
-          w[e] = pack_bf16x2(p0, p1);
-        }
-        pb[kb][sp] = bitcast<bf16x8_t>(make_uint4(w[0], w[1], w[2], w[3]));
-      }
-  };
-  // O^T += V^T . P^T with the tile in V slot `slot`; A lane: dim row
-  // cb*32 + l32, keys kb*32 + sp*16 + hi*4 + {0..3, 8..11}
-  auto pv = [&](int slot, const bf16x8_t (&pb)[2][2], auto hook) {
-    const uint16_t* Vt = lds[1][slot];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int sp = 0; sp < 2; ++sp)
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          const uint16_t* vp = Vt + v_off[cb] + (kb * 32 + sp * 16) * kRowElems;
-          const uint2 a_lo = __builtin_bit_cast(uint2, lds_read_tr16(vp));
-          const uint2 a_hi = __builtin_bit_cast(uint2, lds_read_tr16(vp + 8 * kRowElems));
-          o[cb] = mfma_32x32x16(bitcast<bf16x8_t>(make_uint4(a_lo.x, a_lo.y, a_hi.x, a_hi.y)),
-                                pb[kb][sp], o[cb]);
-          hook(kb * 8 + sp * 4 + cb);
-        }
-  };
-  auto no_hook = [](int) {};
-
-  // The copies are inline asm, invisible to the compiler's wait-count
-  // tracking, and a workgroup barrier's fence does not wait for them: every
-  // barrier that publishes copied tiles is preceded by an explicit wait for
-  // all of this wave's copies in flight.
-  auto publish = [&]() {
-    wait_vmcnt<0>();
-    __syncthreads();
-  };
+  WaveAttn w;
+  w.init(p, tile, tok, row_ok, qrow, head, lane);
 
   // prologue: scores of tile 0
   f32x16_t s_cur[2];
   publish();
-  scores(0, s_cur, no_hook);
-  if (n_full == 0) mask(0, s_cur);
-  rescale(row_max(s_cur));
+  w.scores(lds[0][0], s_cur);
+  if (ts.n_full == 0) w.mask(s_cur, ts.kbase(0), 0 < ts.n_ct, ts.cs.len);
+  w.rescale(w.row_max(s_cur));
 
   // step j: issue K(j+2), V(j+1); S(j+1) with P(j); PV(j) with mask/max of j+1
   auto step = [&](int j, auto tag) {
     constexpr bool MASK_NEXT = decltype(tag)::value;
-    // Waits for this wave's copies of K(j+1) and V(j); the barrier then
-    // makes every wave's copies visible and guarantees that step j-1 (which
-    // read K(j) and V(j-1)) is finished everywhere.
+    // waits for this wave's copies of K(j+1) and V(j); the barrier then makes
+    // every wave's copies visible and guarantees that step j-1 (which read
+    // K(j) and V(j-1)) is finished everywhere
     publish();
-    // K(j+2) into the K slot of tile j, V(j+1) into the V slot of tile j-1
-    if (j + 2 < n_tiles)
-      TileCopy<NW, false>(src_of(j + 2), g, kbase_of(j + 2), lds_k0 + (j & 1) * kSlotBytes).issue_all(cl);
-    TileCopy<NW, true>(src_of(j + 1), g, kbase_of(j + 1), lds_v0 + ((j + 1) & 1) * kSlotBytes).issue_all(cl);
+    if (j + 2 < ts.n_tiles)
+      TileCopy<NW, false>(ts.src(j + 2), g, ts.kbase(j + 2), lds_k0 + (j & 1) * kSlotBytes).issue_all(cl);
+    TileCopy<NW, true>(ts.src(j + 1), g, ts.kbase(j + 1), lds_v0 + ((j + 1) & 1) * kSlotBytes).issue_all(cl);
     bf16x8_t pb[2][2];
-    probs(s_cur, pb);
+    w.probs(s_cur, pb);
     f32x16_t s_nxt[2];
-    scores((j + 1) & 1, s_nxt, no_hook);
-    pv(j & 1, pb, no_hook);
-    if constexpr (MASK_NEXT) mask(j + 1, s_nxt);
-    const float mt = row_max(s_nxt);
-    rescale(mt);
+    w.scores(lds[0][(j + 1) & 1], s_nxt);
+    w.pv(lds[1][j & 1], pb);
+    if constexpr (MASK_NEXT) w.mask(s_nxt, ts.kbase(j + 1), j + 1 < ts.n_ct, ts.cs.len);
+    w.rescale(w.row_max(s_nxt));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
   };
   int j = 0;
-  for (; j + 1 < n_full; ++j) step(j, MaskTag<false>{});
-  for (; j + 1 < n_tiles; ++j) step(j, MaskTag<true>{});
+  for (; j + 1 < ts.n_full; ++j) step(j, MaskTag<false>{});
+  for (; j + 1 < ts.n_tiles; ++j) step(j, MaskTag<true>{});
   // epilogue: the last tile's PV (its V copy was issued by the last step, or
   // by the prologue)
   {
     publish();
     bf16x8_t pb[2][2];
-    probs(s_cur, pb);
-    pv(j & 1, pb, no_hook);
+    w.probs(s_cur, pb);
+    w.pv(lds[1][j & 1], pb);
   }
-
-  const float l_tot = xor32_sum(l_run);
-  if (!row_ok) return;
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  uint16_t* op = p.out + tok * p.o_stride + head * kHeadDim + hi * 4;
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      uint2 w;
-      w.x = pack_bf16x2(o[cb][rg * 4 + 0] * inv, o[cb][rg * 4 + 1] * inv);
-      w.y = pack_bf16x2(o[cb][rg * 4 + 2] * inv, o[cb][rg * 4 + 3] * inv);
-      *reinterpret_cast<uint2*>(op + cb * 32 + rg * 8) = w;
-    }
-  if (p.lse != nullptr && hi == 0) {
-    const float L = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-    p.lse[tok * p.hq + head] = L;
-  }
+  w.store(p, tok, row_ok, head);
 }
 
-static int direct_token_groups(int group) { return group == 8 ? 1 : kAttnTokenGroups; }
-
-int attn_tile_tokens(int group, bool any_fp8) {
-  const int nw = group >= 4 ? group : 4;
-  const int tg = any_fp8 ? 1 : direct_token_groups(group);
-  return kQRows * nw * tg / group;
-}
+int attn_tile_tokens(int group, bool) { return kQRows * (group >= 4 ? group : 4) / group; }
 
 hipError_t launch_attn_bf16(const AttnParams& p, int group, bool any_fp8, hipStream_t s) {
   if (p.n_tiles == 0) return hipSuccess;
@@ -721,12 +736,11 @@ hipError_t launch_attn_bf16(const AttnParams& p, int group, bool any_fp8, hipStr
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 gr((unsigned)grid);
   if (!any_fp8) {
-    constexpr int TG = kAttnTokenGroups;
     switch (group) {
-      case 1: attn_direct_kernel<1, TG><<<gr, dim3(256 * TG), 0, s>>>(p); break;
-      case 2: attn_direct_kernel<2, TG><<<gr, dim3(256 * TG), 0, s>>>(p); break;
-      case 4: attn_direct_kernel<4, TG><<<gr, dim3(256 * TG), 0, s>>>(p); break;
-      case 8: attn_direct_kernel<8, 1><<<gr, dim3(512), 0, s>>>(p); break;
+      case 1: attn_direct_kernel<1><<<gr, dim3(256), 0, s>>>(p); break;
+      case 2: attn_direct_kernel<2><<<gr, dim3(256), 0, s>>>(p); break;
+      case 4: attn_direct_kernel<4><<<gr, dim3(256), 0, s>>>(p); break;
+      case 8: attn_direct_kernel<8><<<gr, dim3(512), 0, s>>>(p); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
