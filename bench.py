@@ -30,10 +30,11 @@ Secondary measurements (not the headline line; each prints its own JSON):
   --workload copy    a plain 4 GiB device-to-device copy (read 4 GiB, write
                      4 GiB): the calibration kernel for the HBM byte counters.
   --workload stream  anchor-KV streaming sweep: 1024 anchors of 768 tokens
-                     (bf16 K/V of one layer, 3.2 GB resident), each read by
-                     one suffix of S tokens, S in {1, 4, 16, 64, 256}; anchor
-                     KV bytes per launch / launch time against 8 TB/s, and
-                     TFLOP/s (the intensity is 4*S FLOP per KV byte).
+                     (K/V of one layer: bf16, 3.2 GB, or E4M3 codes, 1.6 GB),
+                     each read by one suffix of S tokens, S in {1, 4, 16, 64,
+                     256}; anchor KV bytes per launch / launch time against
+                     8 TB/s, and TFLOP/s (4*S FLOP per bf16 KV byte, 8*S per
+                     E4M3 byte).
   --workload join36 | filter36 | multijoin36
                      end to end on the 36-layer Qwen3-4B-shaped stack with
                      random-init fp8 weights (quail_join_run: plan, anchor
@@ -221,43 +222,45 @@ def bench_stream(args):
     import workloads as W
     from query_aware_prefill_amd import binding as B
     B.load()
-    out = {"metric": "anchor-KV streaming (cascade attention, bf16 KV)", "unit": "GB/s",
+    out = {"metric": "anchor-KV streaming (cascade attention)", "unit": "GB/s",
            "peak_GBs": HBM_PEAK_GBS, "anchors": 1024, "anchor_len": 768, "points": []}
-    for S in (1, 4, 16, 64, 256):
-        a_len, s_anchor, s_len = W.stream_lengths(S)
-        case = W.cascade_device(7, a_len, s_anchor, s_len)
-        T = int(case["s_off"][-1])
-        o = torch.empty((T, 32, 128), dtype=torch.bfloat16, device="cuda")
-        ws = torch.empty(B.quail_cascade_workspace_bytes(case["a_off"], case["s_off"]),
-                         dtype=torch.uint8, device="cuda")
-        stream = torch.cuda.current_stream()
+    for kv, dtype, esz in (("bf16", B.DTYPE_BF16, 2), ("e4m3", B.DTYPE_FP8_E4M3, 1)):
+        for S in (1, 4, 16, 64, 256):
+            a_len, s_anchor, s_len = W.stream_lengths(S)
+            case = W.cascade_device(7, a_len, s_anchor, s_len, anchor_kv=kv)
+            T = int(case["s_off"][-1])
+            o = torch.empty((T, 32, 128), dtype=torch.bfloat16, device="cuda")
+            ws = torch.empty(B.quail_cascade_workspace_bytes(case["a_off"], case["s_off"]),
+                             dtype=torch.uint8, device="cuda")
+            stream = torch.cuda.current_stream()
 
-        def step():
-            B.quail_cascade_attn(B.DTYPE_BF16, 32, 8, 128, case["sm_scale"], case["ak"], case["av"],
-                                 case["a_off"], s_anchor, case["q"], case["k"], case["v"],
-                                 case["s_off"], o, None, ws, stream=stream)
+            def step():
+                B.quail_cascade_attn(dtype, 32, 8, 128, case["sm_scale"], case["ak"], case["av"],
+                                     case["a_off"], s_anchor, case["q"], case["k"], case["v"],
+                                     case["s_off"], o, None, ws, stream=stream)
 
-        for _ in range(max(args.warmup, 1)):
-            step()
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-        for a, b in ev:
-            a.record(stream)
-            step()
-            b.record(stream)
-        torch.cuda.synchronize()
-        ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
-        kv_bytes = 2.0 * float(np.sum(a_len)) * 8 * 128 * 2
-        cross, self_ = algorithmic_flops(a_len, s_anchor, s_len)
-        pt = {"S": S, "ms": ms, "anchor_kv_bytes": kv_bytes, "GB/s": kv_bytes / (ms * 1e-3) / 1e9,
-              "frac_hbm": kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-              "tflops": (cross + self_) / (ms * 1e-3) / 1e12}
-        out["points"].append(pt)
-        log(f"stream S={S}: {ms:.3f} ms, {pt['GB/s']:.0f} GB/s ({pt['frac_hbm']:.2f} of HBM), "
-            f"{pt['tflops']:.1f} TFLOP/s")
-        del case, o, ws
-        torch.cuda.empty_cache()
+            for _ in range(max(args.warmup, 1)):
+                step()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+            for a, b in ev:
+                a.record(stream)
+                step()
+                b.record(stream)
+            torch.cuda.synchronize()
+            ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+            kv_bytes = 2.0 * float(np.sum(a_len)) * 8 * 128 * esz
+            cross, self_ = algorithmic_flops(a_len, s_anchor, s_len)
+            pt = {"kv": kv, "S": S, "ms": ms, "anchor_kv_bytes": kv_bytes,
+                  "GB/s": kv_bytes / (ms * 1e-3) / 1e9,
+                  "frac_hbm": kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                  "tflops": (cross + self_) / (ms * 1e-3) / 1e12}
+            out["points"].append(pt)
+            log(f"stream {kv} S={S}: {ms:.3f} ms, {pt['GB/s']:.0f} GB/s ({pt['frac_hbm']:.2f} of HBM), "
+                f"{pt['tflops']:.1f} TFLOP/s")
+            del case, o, ws
+            torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 
 

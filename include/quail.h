@@ -240,12 +240,15 @@ quail_status quail_pool_stats(const quail_ctx* ctx, size_t* resident, size_t* pe
  * its own keys (self partial, diagonal included); the partials are merged by
  * LSE rescaling. Softmax scale sm_scale; query head h reads KV head
  * h / (hq / hkv).
- * dtype: QUAIL_DTYPE_F32 (head_dim 64 or 128) or QUAIL_DTYPE_BF16 (head_dim
- * 128). ak, av: dev [sum La, hkv, d]; a_off: host [n_anchors+1]. q: dev
+ * dtype: QUAIL_DTYPE_F32 (head_dim 64 or 128), QUAIL_DTYPE_BF16 (head_dim
+ * 128), or QUAIL_DTYPE_FP8_E4M3: bf16 q, k, v and out with the anchor K/V
+ * given as OCP E4M3 codes (one byte per element, value = the decoded code,
+ * unit scale: the resident-KV format of the multi-join configuration).
+ * ak, av: dev [sum La, hkv, d]; a_off: host [n_anchors+1]. q: dev
  * [sum Ls, hq, d]; k, v: dev [sum Ls, hkv, d]; s_off: host [n_suffix+1];
  * s_anchor: host [n_suffix] anchor index or -1 (no anchor). Suffixes of one
  * anchor are processed together; any order is accepted.
- * out: dev [sum Ls, hq, d] (dtype); lse: dev f32 [sum Ls, hq] natural-log
+ * out: dev [sum Ls, hq, d] (f32 or bf16); lse: dev f32 [sum Ls, hq] natural-log
  * LSE of the merged row, or NULL. workspace: dev, at least
  * quail_cascade_workspace_bytes(...). */
 quail_status quail_cascade_workspace_bytes(int32_t n_anchors, const int32_t* a_off,

@@ -175,10 +175,11 @@ attn_bf16_kernel(AttnParams p) {
   // Q fragments: B operand, lane holds query row l32, dims ks*16 + hi*8 .. +7
   bf16x8_t qf[8];
   {
-    const uint16_t* qp = p.q + tok * p.q_stride + head * kHeadDim + hi * 8;
+    const uint16_t* qp = p.q + tok * p.q_stride + head * kHeadDim + hi * 16;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
+      const int d = 32 * (ks >> 1) + 8 * (ks & 1);
+      uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qp + d) : make_uint4(0, 0, 0, 0);
       qf[ks] = bitcast<bf16x8_t>(u);
     }
   }
@@ -335,91 +336,114 @@ attn_bf16_kernel(AttnParams p) {
 }
 
 // ----------------------------------------------------------------------------
-// bf16-only kernel with direct HBM->LDS loads (both key sources bf16).
+// Kernel with direct HBM->LDS copies; K/V tiles in bf16 or as E4M3 codes.
 //
 // K and V tiles are copied from HBM straight into LDS by global_load_lds
 // (16 B per lane, no staging registers; issued as inline asm so the compiler
-// does not make the operand reads wait for copies in flight), double-buffered:
-// the copy of tile
-// i+1 is in flight while tile i is computed. Rows are 256 B; each row's 16-B
-// chunks are XOR-swizzled so that the MFMA operand reads are free of bank
-// conflicts. V stays in its natural [key][dim] layout and the transposed A
-// operand of O^T += V^T P^T comes from ds_read_tr16_b64: within a 16-lane
-// block, lane 4a+b receives element b of the rows addressed by lanes a, a+4,
-// a+8, a+12; pointing lane s at V[K0 + s/4][D0 + 4(s%4)] hands lane j the four
-// keys K0..K0+3 of dim D0 + j. Swizzles are chosen for gfx950's 64-bank LDS
-// (measured: with a 32-bank layout half of all LDS cycles were conflicts).
+// does not make the operand reads wait for copies in flight). bf16 rows are
+// 256 B, E4M3 rows 128 B (decoded to bf16 after each LDS read, exactly:
+// every E4M3 value is a bf16 value); each row's 16-B chunks are XOR-swizzled
+// so that the MFMA operand reads are free of bank conflicts on gfx950's
+// 64-bank LDS. V stays in its natural [key][dim] layout and the transposed A
+// operand of O^T += V^T P^T comes from the LDS transpose reads:
+//   ds_read_tr16_b64: within a 16-lane block, pointing lane s at
+//     V[K0 + s/4][D0 + 4(s%4)] hands lane j the keys K0..K0+3 of dim D0 + j;
+//   ds_read_tr8_b64: pointing lane s at V[K0 + s/2][D0 + 8(s%2)] hands lane j
+//     the keys K0..K0+7 of dim D0 + j.
+// Key order inside a 32-key half: S^T row r holds key pi(r), pi swapping bits
+// 2 and 3, so that the P values a lane holds for one MFMA k-step are 8
+// consecutive keys (what one tr8 read, or two tr16 reads, deliver for V^T).
+// Dim order of the S^T k-steps: k-step 2t+u, lane half hi, slot e holds dim
+// 32t + 16hi + 8u + e, so one 16-B read of an E4M3 K row serves two k-steps.
 // ----------------------------------------------------------------------------
 constexpr int kRowElems = kHeadDim;                 // 128 bf16 = 256 B per key row
 constexpr int kTileElems = kKeyTile * kRowElems;    // 8192 bf16 = 16 KB
 
-// LDS serves 64 banks x 4 B per cycle: 16 lanes of a 16-B read, 32 lanes of an
-// 8-B read. K: the 16 rows one ds_read_b128 cycle touches (same chunk) land
-// on 16 distinct chunks. V: one ds_read_tr16_b64 cycle reads 4 consecutive
-// rows x 64 B (4 chunks); shifting each row's chunks by 4*(row % 4) puts the
+// LDS serves 64 banks x 4 B per cycle: 16 lanes of a 16-B read, 32 lanes of
+// an 8-B read.
+// bf16 K (16 chunks per row): the 16 rows one ds_read_b128 cycle touches
+// (same chunk) land on 16 distinct chunks. bf16 V: one tr16 cycle reads 4
+// consecutive rows x 64 B; shifting each row's chunks by 4*(row % 4) puts the
 // four rows on disjoint 64-B bank groups.
 __device__ __forceinline__ int swz_k(int key, int chunk) { return chunk ^ (key & 15); }
 __device__ __forceinline__ int swz_v(int key, int chunk) { return chunk ^ ((key & 3) << 2); }
+// E4M3 K (8 chunks per 128-B row, two rows per 256-B bank cycle): the 16
+// rows of a cycle pair up by parity and (row / 2) % 8 spreads each parity
+// over the 8 chunk positions. E4M3 V: one tr8 cycle reads 8 consecutive rows
+// x two 16-B chunks; (row / 2) % 4 moves the same-parity rows onto disjoint
+// chunk pairs.
+__device__ __forceinline__ int swz8_k(int key, int chunk) { return chunk ^ ((key >> 1) & 7); }
+__device__ __forceinline__ int swz8_v(int key, int chunk) { return chunk ^ (((key >> 1) & 3) << 1); }
+
+// S^T row -> key offset inside a 32-key half (and back: pi is an involution)
+__device__ __forceinline__ int key_pi(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
+typedef int v2i32_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ v4i16_t lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (v4i16_t __attribute__((address_space(3)))*)(__attribute__((address_space(3))) char*)p);
 }
-
-// Per-lane constants of the direct copies. Each wave copies 16/NW 1-KB slices
-// (4 rows of 256 B) of a K or V tile; lane L writes 16-B slot L % 16 of row
-// slice*4 + L/16 and so reads the chunk that the swizzle puts in that slot.
-template <int NW>
-struct CopyLanes {
-  static constexpr int PER_WAVE = 16 / NW;
-  uint32_t row[PER_WAVE];                   // tile row copied by this lane
-  uint32_t koff[PER_WAVE], voff[PER_WAVE];  // byte offset of its chunk within the row
-  uint32_t lds[PER_WAVE];                   // LDS byte offset of the slice (wave-uniform)
-};
-
-template <int NW>
-__device__ __forceinline__ CopyLanes<NW> copy_lanes(int wave, int lane) {
-  CopyLanes<NW> c;
-#pragma unroll
-  for (int i = 0; i < CopyLanes<NW>::PER_WAVE; ++i) {
-    const int slice = wave * CopyLanes<NW>::PER_WAVE + i;
-    c.row[i] = slice * 4 + (lane >> 4);
-    c.koff[i] = swz_k(c.row[i], lane & 15) * 16;
-    c.voff[i] = swz_v(c.row[i], lane & 15) * 16;
-    c.lds[i] = slice * 4 * kRowElems * 2;
-  }
-  return c;
+__device__ __forceinline__ v2i32_t lds_read_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (v2i32_t __attribute__((address_space(3)))*)(__attribute__((address_space(3))) char*)p);
 }
 
-// The direct copies of one 64-key K (IS_V = false) or V tile of kv head g
-// into the LDS slot at byte address `dst`: PER_WAVE 1-KB slices per wave.
-// Rows at or
-// past the source length are clamped to its last row (their scores are
-// masked); full tiles skip the clamp. Per-lane offsets are 24-bit products
-// (token strides are bounded on the host).
+// 8 E4M3 codes (two words) -> 8 bf16, exact
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bitcast<bf16x8_t>(make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                                      __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)));
+}
+
+// The direct copies of one 64-key K (IS_V = false) or V tile of kv head g into
+// the LDS slot at byte address `dst`, by wave `wave` of NW: 1-KB slices of 4
+// bf16 rows or 8 E4M3 rows; lane L writes 16-B slot L % (16 or 8) of its row
+// and reads the chunk the swizzle puts there. Rows at or past the source
+// length are clamped to its last row (their scores are masked); full tiles
+// skip the clamp. Per-lane offsets are 24-bit products (token strides are
+// bounded on the host).
 template <int NW, bool IS_V>
 struct TileCopy {
   const uint8_t* b8;
   uint32_t tb, last, dst;
-  bool full;
+  bool full, fp8;
   __device__ __forceinline__ TileCopy(const KVSrc& src, int g, int kbase, uint32_t dst_) {
-    tb = (uint32_t)src.tok_stride * 2u;
-    const int64_t base = ((int64_t)g * src.head_stride + (int64_t)kbase * src.tok_stride) * 2;
+    fp8 = uniform(src.fp8) != 0;
+    const int sh = fp8 ? 0 : 1;                  // log2 of the element size
+    tb = (uint32_t)src.tok_stride << sh;
+    const int64_t base = ((int64_t)g * src.head_stride + (int64_t)kbase * src.tok_stride) << sh;
     b8 = reinterpret_cast<const uint8_t*>(IS_V ? src.v : src.k) + base;
     full = kbase + kKeyTile <= src.len;
     last = (uint32_t)max(src.len - 1 - kbase, 0);
     dst = dst_;
   }
-  __device__ __forceinline__ void issue(int i, const CopyLanes<NW>& cl) const {
-    const uint32_t r = full ? cl.row[i] : min(cl.row[i], last);
-    copy16_to_lds_off(b8, __umul24(r, tb) + (IS_V ? cl.voff[i] : cl.koff[i]), dst + cl.lds[i]);
-  }
-  __device__ __forceinline__ void issue_all(const CopyLanes<NW>& cl) const {
+  __device__ __forceinline__ void issue_all(int wave, int lane) const {
+    if (!fp8) {
+      constexpr int PER = 16 / NW;
 #pragma unroll
-    for (int i = 0; i < CopyLanes<NW>::PER_WAVE; ++i) issue(i, cl);
+      for (int i = 0; i < PER; ++i) {
+        const int slice = wave * PER + i;
+        const uint32_t row = slice * 4 + (lane >> 4);
+        const uint32_t off = (IS_V ? swz_v(row, lane & 15) : swz_k(row, lane & 15)) * 16;
+        const uint32_t r = full ? row : min(row, last);
+        copy16_to_lds_off(b8, __umul24(r, tb) + off, dst + slice * 1024);
+      }
+    } else {
+      constexpr int PER = 8 / NW;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int slice = wave * PER + i;
+        const uint32_t row = slice * 8 + (lane >> 3);
+        const uint32_t off = (IS_V ? swz8_v(row, lane & 7) : swz8_k(row, lane & 7)) * 16;
+        const uint32_t r = full ? row : min(row, last);
+        copy16_to_lds_off(b8, __umul24(r, tb) + off, dst + slice * 1024);
+      }
+    }
   }
 };
 
@@ -450,43 +474,25 @@ struct TileSeq {
 };
 
 // One wave's share of the bf16 MFMA attention: 32 query rows of one head
-// (lane % 32 owns row l32; the two lanes of a row split its keys), the
-// operand-read offsets into a K / V tile in LDS, the O^T accumulator and the
-// online-softmax state.
+// (lane % 32 owns row l32; the two lanes of a row split its keys), the O^T
+// accumulator and the online-softmax state. Operand offsets into the LDS
+// tiles are formed where used (a few VALU ops next to the MFMAs) rather than
+// kept in registers across the loop.
 struct WaveAttn {
-  bf16x8_t qf[8];       // Q as the B operand: dims ks*16 + hi*8 .. +7
+  bf16x8_t qf[8];       // Q as the B operand of k-step 2t+u: dims 32t + 16hi + 8u .. +7
   f32x16_t o[4];
   float m_run, l_run, scale_log2;
   int lane, hi, lo_self, hi_self;
-
-  // LDS element offset of the K operand (A of S^T) for k-step ks: key row
-  // l32, 16-B chunk swz_k(l32, ks*2 + hi); the 32-key half is a constant row
-  // offset. Formed where used (a few VALU ops next to the MFMAs) rather than
-  // kept in registers across the loop.
-  __device__ __forceinline__ uint32_t k_off(int ks) const {
-    const int l32 = lane & 31;
-    return l32 * kRowElems + swz_k(l32, ks * 2 + hi) * 8;
-  }
-  // LDS element offset of the V^T operand (A of O^T, read with
-  // ds_read_tr16_b64) for 32-dim block cb: within each 16-lane block lane j
-  // points at key (j / 4) of a 4-key group and dims 4*(j % 4) .. +3 of a
-  // 16-dim half; the 4-key groups start at multiples of 4, so the swizzle
-  // term depends on the lane only and the key-group terms are constant rows.
-  __device__ __forceinline__ uint32_t v_off(int cb) const {
-    const int trj = lane & 15;
-    const int tr_key = hi * 4 + (trj >> 2);
-    const int d0 = cb * 32 + 16 * ((lane >> 4) & 1) + 4 * (trj & 3);
-    return tr_key * kRowElems + swz_v(tr_key, d0 >> 3) * 8 + (d0 & 7);
-  }
 
   __device__ __forceinline__ void init(const AttnParams& p, const AttnTile& tile, int64_t tok,
                                        bool row_ok, int qrow, int head, int lane_) {
     lane = lane_;
     hi = lane >> 5;
-    const uint16_t* qp = p.q + tok * p.q_stride + head * kHeadDim + hi * 8;
+    const uint16_t* qp = p.q + tok * p.q_stride + head * kHeadDim + hi * 16;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
+      const int d = 32 * (ks >> 1) + 8 * (ks & 1);
+      uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qp + d) : make_uint4(0, 0, 0, 0);
       qf[ks] = bitcast<bf16x8_t>(u);
     }
     // self keys visible to this row: [first key of its segment, its own key]
@@ -504,34 +510,55 @@ struct WaveAttn {
     scale_log2 = p.scale_log2;
   }
 
-  // S^T = K . Q^T of the tile at Kt (two 32-key halves)
+  // S^T = K . Q^T of the tile at Kt (two 32-key halves); lane l32 reads key
+  // row pi(l32) of each half
+  template <bool FP8>
   __device__ __forceinline__ void scores(const uint16_t* Kt, f32x16_t (&s)[2]) const {
+    const int krow = key_pi(lane & 31);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+    if constexpr (!FP8) {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8_t a = bitcast<bf16x8_t>(
-            *reinterpret_cast<const uint4*>(Kt + k_off(ks) + kb * 32 * kRowElems));
-        s[kb] = mfma_32x32x16(a, qf[ks], s[kb]);
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = kb * 32 + krow;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const int chunk = 4 * (ks >> 1) + 2 * hi + (ks & 1);
+          const bf16x8_t a = bitcast<bf16x8_t>(
+              *reinterpret_cast<const uint4*>(Kt + row * kRowElems + swz_k(row, chunk) * 8));
+          s[kb] = mfma_32x32x16(a, qf[ks], s[kb]);
+        }
+      }
+    } else {
+      const uint8_t* K8 = reinterpret_cast<const uint8_t*>(Kt);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = kb * 32 + krow;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint4 c = *reinterpret_cast<const uint4*>(K8 + row * 128 + swz8_k(row, 2 * t + hi) * 16);
+          s[kb] = mfma_32x32x16(e4m3x8_to_bf16x8(c.x, c.y), qf[2 * t], s[kb]);
+          s[kb] = mfma_32x32x16(e4m3x8_to_bf16x8(c.z, c.w), qf[2 * t + 1], s[kb]);
+        }
       }
     }
   }
 
   // mask a tile starting at key kbase: visible keys are [0, cross_len) for a
-  // cross tile, [lo_self, hi_self] for a self tile; the key of (kb, r) is
-  // kbase + kb*32 + hi*4 + (r/4)*8 + r%4 (unsigned range test)
+  // cross tile, [lo_self, hi_self] for a self tile; register i of half kb
+  // holds key kbase + kb*32 + 16*(i/8) + 8*hi + i%8 (unsigned range test)
   __device__ __forceinline__ void mask(f32x16_t (&s)[2], int kbase, bool cross, int cross_len) const {
     const int lo = cross ? 0 : lo_self;
     const int hk = cross ? cross_len - 1 : hi_self;
     const uint32_t range = (uint32_t)(hk - lo);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const uint32_t x = (uint32_t)(kbase + kb * 32 + hi * 4 - lo);
+      const uint32_t x = (uint32_t)(kbase + kb * 32 + hi * 8 - lo);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const uint32_t c = (uint32_t)((r >> 2) * 8 + (r & 3));
+        const uint32_t c = (uint32_t)(16 * (r >> 3) + (r & 7));
         s[kb][r] = (x + c <= range) ? s[kb][r] : -INFINITY;
       }
     }
@@ -563,7 +590,8 @@ struct WaveAttn {
   }
 
   // P = 2^(s*scale - m_run) in bf16 as the B operand: k-step (kb, sp) takes
-  // regs 8*sp .. 8*sp+7 of half kb; the row sum adds the fp32 values
+  // regs 8*sp .. 8*sp+7 of half kb, i.e. keys kb*32 + 16sp + 8hi + 0..7; the
+  // row sum adds the fp32 values
   __device__ __forceinline__ void probs(const f32x16_t (&s)[2], bf16x8_t (&pb)[2][2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -582,20 +610,47 @@ struct WaveAttn {
   }
 
   // O^T += V^T . P^T with the tile at Vt; A lane: dim row cb*32 + l32, keys
-  // kb*32 + sp*16 + hi*4 + {0..3, 8..11}
+  // kb*32 + 16sp + 8hi + 0..7. The 16-lane block (lane / 16) covers dims
+  // cb*32 + 16*(block % 2) .. +15 and keys +8 for blocks 2, 3.
+  template <bool FP8>
   __device__ __forceinline__ void pv(const uint16_t* Vt, const bf16x8_t (&pb)[2][2]) {
+    const int s16 = lane & 15;
+    const int dhalf = (lane >> 4) & 1;
+    if constexpr (!FP8) {
+      // two tr16 reads: keys +0..3 and +4..7; lane s16 points at key
+      // s16 / 4 of the group and dims 4*(s16 % 4) .. +3 of the 16-dim half
+      const int key0 = hi * 8 + (s16 >> 2);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int sp = 0; sp < 2; ++sp)
+        for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          const uint16_t* vp = Vt + v_off(cb) + (kb * 32 + sp * 16) * kRowElems;
-          const uint2 a_lo = __builtin_bit_cast(uint2, lds_read_tr16(vp));
-          const uint2 a_hi = __builtin_bit_cast(uint2, lds_read_tr16(vp + 8 * kRowElems));
-          o[cb] = mfma_32x32x16(bitcast<bf16x8_t>(make_uint4(a_lo.x, a_lo.y, a_hi.x, a_hi.y)),
-                                pb[kb][sp], o[cb]);
-        }
+          for (int cb = 0; cb < 4; ++cb) {
+            const int key = kb * 32 + sp * 16 + key0;
+            const int d0 = cb * 32 + 16 * dhalf + 4 * (s16 & 3);
+            const uint16_t* vp = Vt + key * kRowElems + swz_v(key, d0 >> 3) * 8 + (d0 & 7);
+            const uint2 a_lo = __builtin_bit_cast(uint2, lds_read_tr16(vp));
+            const uint2 a_hi = __builtin_bit_cast(uint2, lds_read_tr16(vp + 4 * kRowElems));
+            o[cb] = mfma_32x32x16(bitcast<bf16x8_t>(make_uint4(a_lo.x, a_lo.y, a_hi.x, a_hi.y)),
+                                  pb[kb][sp], o[cb]);
+          }
+    } else {
+      // one tr8 read: lane s16 points at key s16 / 2 of the 8-key group and
+      // dims 8*(s16 % 2) .. +7 of the 16-dim half
+      const uint8_t* V8 = reinterpret_cast<const uint8_t*>(Vt);
+      const int key0 = hi * 8 + (s16 >> 1);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            const int key = kb * 32 + sp * 16 + key0;
+            const uint8_t* vp = V8 + key * 128 + swz8_v(key, 2 * cb + dhalf) * 16 + 8 * (s16 & 1);
+            const v2i32_t c = lds_read_tr8(vp);
+            o[cb] = mfma_32x32x16(e4m3x8_to_bf16x8((uint32_t)c.x, (uint32_t)c.y), pb[kb][sp], o[cb]);
+          }
+    }
   }
 
   // O / l as bf16 and the natural-log LSE (-inf without a visible key)
@@ -645,12 +700,13 @@ __device__ __forceinline__ void publish() {
 // flight, and the PV MFMAs of tile j overlap the masking and row max of tile
 // j+1. K and V have two LDS slots each; at step j the copies of K(j+2) and
 // V(j+1) are issued into the slots that step j-1 finished reading, so one
-// barrier per tile suffices. Full cross tiles and the masked tiles (the
-// ragged end of the cross keys, all self tiles) are handled by separate
-// instantiations of the step, so the unmasked step carries no mask code.
+// barrier per tile suffices. The step is instantiated per tile format (FC:
+// cross tiles are E4M3 codes, FS: self tiles are) and per masking need, so
+// that no MFMA accumulator crosses a runtime branch: full cross tiles, the
+// remaining (ragged) cross tiles, the cross -> self transition, self tiles.
 // One workgroup: the G query heads of one kv head x (waves / G) groups of 32
 // query tokens, all sharing every K/V tile copied into LDS.
-template <int G>
+template <int G, bool FC, bool FS>
 __global__ void __launch_bounds__(64 * (G >= 4 ? G : 4), 2)
 attn_direct_kernel(AttnParams p) {
   constexpr int NW = G >= 4 ? G : 4;
@@ -678,10 +734,9 @@ attn_direct_kernel(AttnParams p) {
   }
   const uint32_t lds_k0 = lds_addr_of(&lds[0][0][0]);
   const uint32_t lds_v0 = lds_addr_of(&lds[1][0][0]);
-  const CopyLanes<NW> cl = copy_lanes<NW>(wave, lane);
-  TileCopy<NW, false>(ts.src(0), g, ts.kbase(0), lds_k0).issue_all(cl);
-  TileCopy<NW, true>(ts.src(0), g, ts.kbase(0), lds_v0).issue_all(cl);
-  if (ts.n_tiles > 1) TileCopy<NW, false>(ts.src(1), g, ts.kbase(1), lds_k0 + kSlotBytes).issue_all(cl);
+  TileCopy<NW, false>(ts.src(0), g, ts.kbase(0), lds_k0).issue_all(wave, lane);
+  TileCopy<NW, true>(ts.src(0), g, ts.kbase(0), lds_v0).issue_all(wave, lane);
+  if (ts.n_tiles > 1) TileCopy<NW, false>(ts.src(1), g, ts.kbase(1), lds_k0 + kSlotBytes).issue_all(wave, lane);
 
   WaveAttn w;
   w.init(p, tile, tok, row_ok, qrow, head, lane);
@@ -689,61 +744,85 @@ attn_direct_kernel(AttnParams p) {
   // prologue: scores of tile 0
   f32x16_t s_cur[2];
   publish();
-  w.scores(lds[0][0], s_cur);
+  if (ts.n_ct > 0) w.scores<FC>(lds[0][0], s_cur);
+  else w.scores<FS>(lds[0][0], s_cur);
   if (ts.n_full == 0) w.mask(s_cur, ts.kbase(0), 0 < ts.n_ct, ts.cs.len);
   w.rescale(w.row_max(s_cur));
 
-  // step j: issue K(j+2), V(j+1); S(j+1) with P(j); PV(j) with mask/max of j+1
-  auto step = [&](int j, auto tag) {
-    constexpr bool MASK_NEXT = decltype(tag)::value;
+  // step j: issue K(j+2), V(j+1); S(j+1) with P(j); PV(j) with mask/max of
+  // j+1. PV_FP8 / S_FP8: formats of tiles j and j+1.
+  auto step = [&](int j, auto pv_tag, auto s_tag, auto mask_tag) {
+    constexpr bool PV_FP8 = decltype(pv_tag)::value;
+    constexpr bool S_FP8 = decltype(s_tag)::value;
+    constexpr bool MASK_NEXT = decltype(mask_tag)::value;
     // waits for this wave's copies of K(j+1) and V(j); the barrier then makes
     // every wave's copies visible and guarantees that step j-1 (which read
     // K(j) and V(j-1)) is finished everywhere
     publish();
     if (j + 2 < ts.n_tiles)
-      TileCopy<NW, false>(ts.src(j + 2), g, ts.kbase(j + 2), lds_k0 + (j & 1) * kSlotBytes).issue_all(cl);
-    TileCopy<NW, true>(ts.src(j + 1), g, ts.kbase(j + 1), lds_v0 + ((j + 1) & 1) * kSlotBytes).issue_all(cl);
+      TileCopy<NW, false>(ts.src(j + 2), g, ts.kbase(j + 2), lds_k0 + (j & 1) * kSlotBytes).issue_all(wave, lane);
+    TileCopy<NW, true>(ts.src(j + 1), g, ts.kbase(j + 1), lds_v0 + ((j + 1) & 1) * kSlotBytes).issue_all(wave, lane);
     bf16x8_t pb[2][2];
     w.probs(s_cur, pb);
     f32x16_t s_nxt[2];
-    w.scores(lds[0][(j + 1) & 1], s_nxt);
-    w.pv(lds[1][j & 1], pb);
+    w.scores<S_FP8>(lds[0][(j + 1) & 1], s_nxt);
+    w.pv<PV_FP8>(lds[1][j & 1], pb);
     if constexpr (MASK_NEXT) w.mask(s_nxt, ts.kbase(j + 1), j + 1 < ts.n_ct, ts.cs.len);
     w.rescale(w.row_max(s_nxt));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
   };
+  using C8 = MaskTag<FC>;
+  using S8 = MaskTag<FS>;
   int j = 0;
-  for (; j + 1 < ts.n_full; ++j) step(j, MaskTag<false>{});
-  for (; j + 1 < ts.n_tiles; ++j) step(j, MaskTag<true>{});
+  for (; j + 1 < ts.n_full; ++j) step(j, C8{}, C8{}, MaskTag<false>{});
+  for (; j + 1 < ts.n_ct; ++j) step(j, C8{}, C8{}, MaskTag<true>{});
+  if (j + 1 < ts.n_tiles && j < ts.n_ct) {
+    step(j, C8{}, S8{}, MaskTag<true>{});
+    ++j;
+  }
+  for (; j + 1 < ts.n_tiles; ++j) step(j, S8{}, S8{}, MaskTag<true>{});
   // epilogue: the last tile's PV (its V copy was issued by the last step, or
   // by the prologue)
   {
     publish();
     bf16x8_t pb[2][2];
     w.probs(s_cur, pb);
-    w.pv(lds[1][j & 1], pb);
+    if (j < ts.n_ct) w.pv<FC>(lds[1][j & 1], pb);
+    else w.pv<FS>(lds[1][j & 1], pb);
   }
   w.store(p, tok, row_ok, head);
 }
 
 int attn_tile_tokens(int group, bool) { return kQRows * (group >= 4 ? group : 4) / group; }
 
-hipError_t launch_attn_bf16(const AttnParams& p, int group, bool any_fp8, hipStream_t s) {
+template <bool FC, bool FS>
+static hipError_t launch_direct(const AttnParams& p, int group, dim3 gr, hipStream_t s) {
+  switch (group) {
+    case 1: attn_direct_kernel<1, FC, FS><<<gr, dim3(256), 0, s>>>(p); break;
+    case 2: attn_direct_kernel<2, FC, FS><<<gr, dim3(256), 0, s>>>(p); break;
+    case 4: attn_direct_kernel<4, FC, FS><<<gr, dim3(256), 0, s>>>(p); break;
+    case 8: attn_direct_kernel<8, FC, FS><<<gr, dim3(512), 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16(const AttnParams& p, int group, bool fp8_cross, bool fp8_self, hipStream_t s) {
   if (p.n_tiles == 0) return hipSuccess;
   const int64_t total = (int64_t)p.n_tiles * p.hkv;
   const int64_t grid = (total + 7) / 8 * 8;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 gr((unsigned)grid);
-  if (!any_fp8) {
-    switch (group) {
-      case 1: attn_direct_kernel<1><<<gr, dim3(256), 0, s>>>(p); break;
-      case 2: attn_direct_kernel<2><<<gr, dim3(256), 0, s>>>(p); break;
-      case 4: attn_direct_kernel<4><<<gr, dim3(256), 0, s>>>(p); break;
-      case 8: attn_direct_kernel<8><<<gr, dim3(512), 0, s>>>(p); break;
-      default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+  const bool any_fp8 = fp8_cross || fp8_self;
+  // E4M3 sources with unit scales are read by the direct kernel (decoded after
+  // each LDS read); other scales take the register-staged kernel, which
+  // applies them while staging
+  if (!any_fp8 || (p.k_scale == 1.0f && p.v_scale == 1.0f)) {
+    if (fp8_cross && fp8_self) return launch_direct<true, true>(p, group, gr, s);
+    if (fp8_cross) return launch_direct<true, false>(p, group, gr, s);
+    if (fp8_self) return launch_direct<false, true>(p, group, gr, s);
+    return launch_direct<false, false>(p, group, gr, s);
   }
   switch (group) {
     case 1: attn_bf16_kernel<1><<<gr, dim3(256), 0, s>>>(p); break;

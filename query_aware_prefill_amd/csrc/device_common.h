@@ -117,11 +117,22 @@ __device__ __forceinline__ void copy16_to_lds(const void* gptr, const void* lds_
 // byte offset (the saddr form: no 64-bit address arithmetic per lane).
 // `lds_addr` is the wave-uniform LDS byte address of the 1-KB destination.
 __device__ __forceinline__ void copy16_to_lds_off(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  // both operands are wave-uniform; readfirstlane makes that explicit to the
+  // compiler (a no-op for values already in SGPRs)
+  // (readfirstlane returns a signed int: each half goes through uint32_t so
+  // that widening never sign-extends into the other half)
+  const uint64_t a = reinterpret_cast<uint64_t>(sbase);
+  const uint32_t a_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const uint32_t a_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t sa = ((uint64_t)a_hi << 32) | (uint64_t)a_lo;
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "v"(voff), "s"(reinterpret_cast<const void*>(sa)), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory", "m0");
 }
+
+// a wave-uniform value as such (v_readfirstlane; free for values in SGPRs)
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // LDS byte address of a __shared__ object (low 32 bits of its generic pointer)
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {

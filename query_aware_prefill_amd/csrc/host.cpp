@@ -463,7 +463,10 @@ quail_status run_batch(quail_ctx* c, const Batch& b, const int32_t* tokens, uint
     ap.hq = Hq; ap.hkv = Hkv;
     ap.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)kHeadDim));
     ap.k_scale = cf.k_scale; ap.v_scale = cf.v_scale;
-    HIP_TRY(launch_attn_bf16(ap, G, cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3, s));
+    // anchor batches attend over their own slab (self source); join batches
+    // read the anchor slab as the cross source and bf16 suffix K/V as self
+    const bool slab_fp8 = cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3;
+    HIP_TRY(launch_attn_bf16(ap, G, !b.anchor_mode && slab_fp8, b.anchor_mode && slab_fp8, s));
 
     GemmParams go{};
     go.A = obuf; go.lda = (int64_t)Hq * kHeadDim; go.B = lw.w_o; go.scale = lw.s_o;
@@ -1054,13 +1057,13 @@ quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t 
                                 int32_t n_suffix, const int32_t* s_anchor, const void* q, const void* k,
                                 const void* v, const int32_t* s_off, void* out, float* lse,
                                 void* workspace, size_t ws_bytes, quail_stream stream) {
-  if (dtype != QUAIL_DTYPE_F32 && dtype != QUAIL_DTYPE_BF16)
-    return fail(QUAIL_E_UNSUPPORTED, "dtype must be F32 or BF16");
+  if (dtype != QUAIL_DTYPE_F32 && dtype != QUAIL_DTYPE_BF16 && dtype != QUAIL_DTYPE_FP8_E4M3)
+    return fail(QUAIL_E_UNSUPPORTED, "dtype must be F32, BF16 or FP8_E4M3");
   if (hq <= 0 || hkv <= 0 || hq % hkv) return fail(QUAIL_E_INVAL, "hq must be a positive multiple of hkv");
   if (hkv > kMaxKVHeads) return fail(QUAIL_E_UNSUPPORTED, "hkv %d (at most %d)", hkv, kMaxKVHeads);
   const int G = hq / hkv;
-  if (dtype == QUAIL_DTYPE_BF16 && (d != kHeadDim || !valid_group(G)))
-    return fail(QUAIL_E_UNSUPPORTED, "bf16 path: head_dim 128 and GQA group 1, 2, 4 or 8");
+  if (dtype != QUAIL_DTYPE_F32 && (d != kHeadDim || !valid_group(G)))
+    return fail(QUAIL_E_UNSUPPORTED, "bf16 / E4M3 path: head_dim 128 and GQA group 1, 2, 4 or 8");
   if (dtype == QUAIL_DTYPE_F32 && d != 64 && d != 128)
     return fail(QUAIL_E_UNSUPPORTED, "fp32 path: head_dim 64 or 128");
   if (!(sm_scale > 0.0f)) return fail(QUAIL_E_INVAL, "sm_scale must be positive");
@@ -1108,11 +1111,15 @@ quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t 
   KVSrc self{};
   self.k = k; self.v = v; self.tok_stride = (int64_t)hkv * d; self.head_stride = d; self.len = T; self.fp8 = 0;
   srcs.push_back(self);
+  // anchor K/V: bf16, or E4M3 codes (1 byte per element) for dtype FP8_E4M3
+  const bool a_fp8 = dtype == QUAIL_DTYPE_FP8_E4M3;
+  const int64_t a_esz = a_fp8 ? 1 : 2;
   for (int32_t a = 0; a < n_anchors; ++a) {
     KVSrc x{};
-    x.k = static_cast<const uint16_t*>(ak) + (int64_t)a_off[a] * hkv * d;
-    x.v = static_cast<const uint16_t*>(av) + (int64_t)a_off[a] * hkv * d;
-    x.tok_stride = (int64_t)hkv * d; x.head_stride = d; x.len = a_off[a + 1] - a_off[a]; x.fp8 = 0;
+    x.k = static_cast<const uint8_t*>(ak) + (int64_t)a_off[a] * hkv * d * a_esz;
+    x.v = static_cast<const uint8_t*>(av) + (int64_t)a_off[a] * hkv * d * a_esz;
+    x.tok_stride = (int64_t)hkv * d; x.head_stride = d; x.len = a_off[a + 1] - a_off[a];
+    x.fp8 = a_fp8 ? 1 : 0;
     srcs.push_back(x);
   }
   std::vector<AttnTile> tiles;
@@ -1145,7 +1152,7 @@ quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t 
   p.lse = lse; p.hq = hq; p.hkv = hkv;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
   p.k_scale = 1.0f; p.v_scale = 1.0f;
-  HIP_TRY(launch_attn_bf16(p, G, false, st));
+  HIP_TRY(launch_attn_bf16(p, G, a_fp8, false, st));
   return QUAIL_OK;
 }
 

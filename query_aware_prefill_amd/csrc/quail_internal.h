@@ -113,10 +113,10 @@ struct Head8Params {
 };
 
 // ---- launchers (return the launch's hipError_t) ----
-// any_fp8: some key source of this launch holds E4M3 codes (register-staged
-// kernel); otherwise the direct HBM->LDS kernel runs.
-hipError_t launch_attn_bf16(const AttnParams& p, int group, bool any_fp8, hipStream_t s);
-// Query tokens one wave of that launch covers (tiles hold (waves / group) of these).
+// fp8_cross / fp8_self: the cross (anchor) / self key sources of this launch
+// hold E4M3 codes. With unit k/v scales every combination runs the direct
+// HBM->LDS kernel; other scales take the register-staged kernel.
+hipError_t launch_attn_bf16(const AttnParams& p, int group, bool fp8_cross, bool fp8_self, hipStream_t s);
 // query tokens per attention tile (one workgroup) for GQA group size `group`
 int attn_tile_tokens(int group, bool any_fp8);
 hipError_t launch_attn_f32(const AttnF32Params& p, hipStream_t s);

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from oracle import attention as OA, model as OM
+from oracle import attention as OA, codecs as OC, model as OM
 from tests.gpu_util import bf16_f64, decisions_agree, rel_inf, say, u16
 
 pytestmark = pytest.mark.gpu
@@ -116,6 +116,58 @@ def test_stream_shape(B, S):
     case = W.cascade_case(40 + S, a_len, s_anchor, s_len, hq=32, hkv=8, d=128, dtype="bf16", cfg_id=12)
     o, lse = _run(B, case)
     ref_o, ref_l = OA.cascade_case_reference(case)
+    for s in range(len(s_len)):
+        sl = slice(case["s_off"][s], case["s_off"][s + 1])
+        err = rel_inf(o[sl], ref_o[sl])
+        assert err <= 2e-2, (s, err)
+    assert np.max(np.abs(lse - ref_l)) <= 1e-3 + 1e-4 * np.max(np.abs(ref_l))
+
+
+E4M3_CASES = [
+    # (a_len, s_anchor, s_len, hq, hkv)
+    ([64], [0] * 3, [32, 32, 32], 4, 1),
+    ([1], [0, 0], [1, 2], 4, 1),
+    ([130, 5], [-1, 0, -1, 1, 1], [9, 40, 1, 96, 32], 4, 2),
+    ([200, 77], [0, 1, 0, 1, 0], [7, 64, 65, 3, 128], 32, 8),
+    ([768] * 3, [0, 1, 2], [1, 4, 33], 32, 8),
+    ([300], [0, 0], [50, 20], 16, 2),
+]
+
+
+def _e4m3_anchor_case(case):
+    """Anchor K/V as E4M3 codes of the drawn bf16 values (the oracle's
+    encoder), and the same case with the anchors replaced by the decoded
+    codes (exact in bf16) for the oracle's reference."""
+    codes = {k: OC.e4m3_encode(OC.bf16_value(case[k])) for k in ("ak", "av")}
+    ref_case = dict(case)
+    for k in ("ak", "av"):
+        ref_case[k] = OC.bf16_bits(OC.e4m3_decode(codes[k]))
+    return codes, ref_case
+
+
+@pytest.mark.parametrize("ci", range(len(E4M3_CASES)))
+def test_e4m3_anchor_cases(B, ci):
+    """Anchor K/V given as E4M3 codes (the multi-join configuration's resident
+    KV format), decoded after each LDS read: ragged anchors and suffixes,
+    filter rows, GQA groups 4, 2 and 8."""
+    import torch
+    from query_aware_prefill_amd.device import to_device
+    a_len, s_anchor, s_len, hq, hkv = E4M3_CASES[ci]
+    say("e4m3 anchor case", ci, a_len, s_len, hq, hkv)
+    case = W.cascade_case(60 + ci, a_len, s_anchor, s_len, hq=hq, hkv=hkv, d=128, dtype="bf16", cfg_id=13)
+    codes, ref_case = _e4m3_anchor_case(case)
+    dev = {k: to_device(case[k]) for k in ("q", "k", "v")}
+    ak, av = to_device(codes["ak"]), to_device(codes["av"])
+    T = int(case["s_off"][-1])
+    out = torch.empty((T, hq, 128), dtype=torch.int16, device="cuda")
+    lse = torch.empty((T, hq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.quail_cascade_workspace_bytes(case["a_off"], case["s_off"]), dtype=torch.uint8,
+                     device="cuda")
+    B.quail_cascade_attn(B.DTYPE_FP8_E4M3, hq, hkv, 128, case["sm_scale"], ak, av, case["a_off"],
+                         case["s_anchor"], dev["q"], dev["k"], dev["v"], case["s_off"], out, lse, ws)
+    torch.cuda.synchronize()
+    o, lse = bf16_f64(u16(out)), lse.cpu().numpy().astype(np.float64)
+    ref_o, ref_l = OA.cascade_case_reference(ref_case)
     for s in range(len(s_len)):
         sl = slice(case["s_off"][s], case["s_off"][s + 1])
         err = rel_inf(o[sl], ref_o[sl])

@@ -340,10 +340,12 @@ def c1_case(seed: int = 1, n_anchors: int = 256, per_anchor: int = 64,
                         dtype="bf16", cfg_id=1)
 
 
-def cascade_device(seed, a_len, s_anchor, s_len, device="cuda", hq=32, hkv=8, d=128):
+def cascade_device(seed, a_len, s_anchor, s_len, device="cuda", hq=32, hkv=8, d=128,
+                   anchor_kv="bf16"):
     """A bf16 cascade-attention case drawn directly in device memory with
     torch's seeded generator (N(0,1) float32 draws converted to bf16); the
-    arrays and keys are those of ``cascade_case``."""
+    arrays and keys are those of ``cascade_case``. anchor_kv="e4m3" stores
+    the anchor K/V as OCP E4M3 codes of the N(0,1) draws (uint8)."""
     import torch
     a_len = np.asarray(a_len, np.int32)
     s_anchor = np.asarray(s_anchor, np.int32)
@@ -355,19 +357,23 @@ def cascade_device(seed, a_len, s_anchor, s_len, device="cuda", hq=32, hkv=8, d=
     g = torch.Generator(device=device)
     g.manual_seed(1_000_003 * seed + 17)
 
-    def draw(shape):
-        out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    def draw(shape, dt=None):
+        dt = dt or torch.bfloat16
+        out = torch.empty(shape, dtype=dt, device=device)
         # draw in chunks to bound the float32 temporary
         flat = out.view(-1)
         step = 1 << 28
         for i in range(0, flat.numel(), step):
             n = min(step, flat.numel() - i)
-            flat[i:i + n] = torch.randn(n, generator=g, device=device,
-                                        dtype=torch.float32).to(torch.bfloat16)
+            flat[i:i + n] = torch.randn(n, generator=g, device=device, dtype=torch.float32).to(dt)
         return out
 
     TA, TS = int(a_off[-1]), int(s_off[-1])
-    ak = draw((TA, hkv, d)); av = draw((TA, hkv, d))
+    if anchor_kv == "e4m3":
+        ak = draw((TA, hkv, d), torch.float8_e4m3fn).view(torch.uint8)
+        av = draw((TA, hkv, d), torch.float8_e4m3fn).view(torch.uint8)
+    else:
+        ak = draw((TA, hkv, d)); av = draw((TA, hkv, d))
     q = draw((TS, hq, d)); k = draw((TS, hkv, d)); v = draw((TS, hkv, d))
     return dict(a_len=a_len, a_off=a_off, s_anchor=s_anchor, s_len=s_len,
                 s_off=s_off, ak=ak, av=av, q=q, k=k, v=v, hq=hq, hkv=hkv, d=d,
