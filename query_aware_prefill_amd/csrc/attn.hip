@@ -175,11 +175,10 @@ attn_bf16_kernel(AttnParams p) {
   // Q fragments: B operand, lane holds query row l32, dims ks*16 + hi*8 .. +7
   bf16x8_t qf[8];
   {
-    const uint16_t* qp = p.q + tok * p.q_stride + head * kHeadDim + hi * 16;
+    const uint16_t* qp = p.q + tok * p.q_stride + head * kHeadDim + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const int d = 32 * (ks >> 1) + 8 * (ks & 1);
-      uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qp + d) : make_uint4(0, 0, 0, 0);
+      uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
       qf[ks] = bitcast<bf16x8_t>(u);
     }
   }

@@ -73,11 +73,13 @@ def _setup(shape, seed, a_len, pairs, B, pool_bytes=None, mbt=512):
     return wts, case, dm, ctx, to_device(case["a_tok"]), to_device(case["s_tok"])
 
 
-@pytest.mark.parametrize("kv_fp8", [False, True])
-def test_tiny_model_anchor_join_head(B, kv_fp8):
+@pytest.mark.parametrize("kv_fp8,k_scale,v_scale", [(False, 1.0, 1.0), (True, 1.0, 1.0), (True, 0.5, 2.0)])
+def test_tiny_model_anchor_join_head(B, kv_fp8, k_scale, v_scale):
+    """bf16 slabs; E4M3 slabs with unit scales (read directly by the attention
+    kernel); E4M3 slabs with non-unit scales (the register-staged kernel)."""
     import torch
     shape = W.tiny_shape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128,
-                         intermediate=384, vocab=512, kv_fp8=kv_fp8)
+                         intermediate=384, vocab=512, kv_fp8=kv_fp8, k_scale=k_scale, v_scale=v_scale)
     a_len = [1, 70, 130]
     pairs = [(1, 5), (0, 3), (1, 33), (-1, 7), (2, 17), (1, 64), (0, 1), (-1, 2)]
     wts, case, dm, ctx, a_tok, s_tok = _setup(shape, 3, a_len, pairs, B)
