@@ -793,7 +793,9 @@ attn_direct_kernel(AttnParams p) {
   w.store(p, tok, row_ok, head);
 }
 
-int attn_tile_tokens(int group, bool) { return kQRows * (group >= 4 ? group : 4) / group; }
+// both the direct and the register-staged kernel: max(G, 4) waves of G heads
+// x (waves / G) groups of 32 query tokens
+int attn_tile_tokens(int group) { return kQRows * (group >= 4 ? group : 4) / group; }
 
 template <bool FC, bool FS>
 static hipError_t launch_direct(const AttnParams& p, int group, dim3 gr, hipStream_t s) {

@@ -128,8 +128,6 @@ class Blob {
   std::vector<uint8_t> bytes_;
 };
 
-// query tokens per attention tile for GQA group size G
-int group_tokens(int G, bool any_fp8) { return attn_tile_tokens(G, any_fp8); }
 
 bool valid_group(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
 
@@ -564,7 +562,7 @@ quail_status anchor_core(quail_ctx* c, int32_t n, const int32_t* tokens, const i
   if (quail_status st = ensure_rope(c, s)) return st;
   const quail_model_config& cf = c->cfg;
   const int G = cf.n_q_heads / cf.n_kv_heads;
-  const int TQ = group_tokens(G, cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3);
+  const int TQ = attn_tile_tokens(G);
   const size_t esz = kv_elem_bytes(cf);
   // batches of whole anchors up to T tokens
   int32_t a0 = 0;
@@ -793,7 +791,7 @@ quail_status join_core(quail_ctx* c, int32_t n, const quail_anchor* ha, const in
     return kx < ky;
   });
   const int G = cf.n_q_heads / cf.n_kv_heads;
-  const int TQ = group_tokens(G, cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3);
+  const int TQ = attn_tile_tokens(G);
   const size_t esz = kv_elem_bytes(cf);
   int32_t p0 = 0;
   while (p0 < n) {
@@ -1106,7 +1104,7 @@ quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t 
     HIP_TRY(launch_attn_f32(p, st));
     return QUAIL_OK;
   }
-  const int TQ = group_tokens(G, false);
+  const int TQ = attn_tile_tokens(G);
   std::vector<KVSrc> srcs;
   KVSrc self{};
   self.k = k; self.v = v; self.tok_stride = (int64_t)hkv * d; self.head_stride = d; self.len = T; self.fp8 = 0;

@@ -118,7 +118,7 @@ struct Head8Params {
 // HBM->LDS kernel; other scales take the register-staged kernel.
 hipError_t launch_attn_bf16(const AttnParams& p, int group, bool fp8_cross, bool fp8_self, hipStream_t s);
 // query tokens per attention tile (one workgroup) for GQA group size `group`
-int attn_tile_tokens(int group, bool any_fp8);
+int attn_tile_tokens(int group);
 hipError_t launch_attn_f32(const AttnF32Params& p, hipStream_t s);
 hipError_t launch_gemm(const GemmParams& p, GemmEpi epi, hipStream_t s);
 hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s);
