@@ -110,3 +110,24 @@ def test_gemm_qwen3_shapes_sampled_rows(B, N, K):
     err = rel_inf(bf16_f64(u16(y)[rows]), ref)
     say("  rel err", err)
     assert err < 8e-3
+
+
+@pytest.mark.parametrize("N,K,M", [(19456, 2560, 3000), (2560, 9728, 8200)])
+def test_gemm_many_tiles_per_workgroup_ragged(B, N, K, M):
+    """More output tiles than workgroups (each workgroup runs several tiles in
+    a row) with a ragged last token tile; sampled rows and the last 16 rows
+    are checked against the oracle."""
+    import torch
+    say("gemm many tiles", M, N, K)
+    r = np.random.default_rng(M + N + K)
+    x = W.draw_bf16(r, (M, K))
+    w = W.draw_fp8_codes(r, (N, K))
+    s = W.bf16_bits_from_f32((0.0002 * (1 + r.random(N))).astype(np.float32))
+    y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    B.quail_gemm_w8a16(_dev(x), _dev(w), _dev(s), y)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([r.choice(M - 16, 48, replace=False), np.arange(M - 16, M)]))
+    ref = codecs.bf16_round(codecs.bf16_value(x[rows]) @ OM.weight_eff(w, s).T)
+    err = rel_inf(bf16_f64(u16(y)[rows]), ref)
+    say("  rel err", err)
+    assert err < 8e-3
