@@ -507,6 +507,14 @@ struct WaveAttn {
     m_run = -1e30f;
     l_run = 0.0f;
     scale_log2 = p.scale_log2;
+    // Make the Q and segment loads complete here, visibly to the compiler:
+    // otherwise its wait-count pass, which does not see the inline-asm tile
+    // copies, keeps these loads pending into the tile loop and waits for
+    // vmcnt(0) before the first MFMA of every step -- which also waits for
+    // the tile copies just issued and undoes the prefetch.
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf[ks]));
+    asm volatile("" ::"v"(lo_self));
   }
 
   // S^T = K . Q^T of the tile at Kt (two 32-key halves); lane l32 reads key
@@ -693,24 +701,36 @@ __device__ __forceinline__ void publish() {
   wait_vmcnt<0>();
   __syncthreads();
 }
+// Same, leaving this wave's N most recent copies in flight (copies complete
+// in issue order for the wait count).
+template <int N>
+__device__ __forceinline__ void publish_keep() {
+  wait_vmcnt<N>();
+  __syncthreads();
+}
 
 // Software pipeline over the key tiles: while the softmax of tile j (exp,
 // bf16 packing, row sums) runs on the VALU, the S MFMAs of tile j+1 are in
 // flight, and the PV MFMAs of tile j overlap the masking and row max of tile
-// j+1. K and V have two LDS slots each; at step j the copies of K(j+2) and
-// V(j+1) are issued into the slots that step j-1 finished reading, so one
-// barrier per tile suffices. The step is instantiated per tile format (FC:
+// j+1. K has two LDS slots and V three; at step j the copies of K(j+2) and
+// V(j+2) are issued into the slots that step j-1 finished reading, so one
+// barrier per tile suffices, and both K and V copies have two steps to land
+// (with two workgroups per CU, 2 x 80 KB fill the 160-KB LDS). The step is instantiated per tile format (FC:
 // cross tiles are E4M3 codes, FS: self tiles are) and per masking need, so
 // that no MFMA accumulator crosses a runtime branch: full cross tiles, the
 // remaining (ragged) cross tiles, the cross -> self transition, self tiles.
 // One workgroup: the G query heads of one kv head x (waves / G) groups of 32
-// query tokens, all sharing every K/V tile copied into LDS.
-template <int G, bool FC, bool FS>
-__global__ void __launch_bounds__(64 * (G >= 4 ? G : 4), 2)
+// query tokens, all sharing every K/V tile copied into LDS. PACK (launches
+// whose anchors have few query tokens, where K/V streaming is the work): one
+// wave whose 32 rows are the G heads x 32/G tokens, so that every K/V tile
+// feeds 32 useful rows instead of 32 per head.
+template <int G, bool FC, bool FS, bool PACK>
+__global__ void __launch_bounds__(PACK ? 64 : 64 * (G >= 4 ? G : 4), 2)
 attn_direct_kernel(AttnParams p) {
-  constexpr int NW = G >= 4 ? G : 4;
+  constexpr int NW = PACK ? 1 : (G >= 4 ? G : 4);
   constexpr uint32_t kSlotBytes = kTileElems * 2;
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][kTileElems];   // [K,V][slot]
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k[2][kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v[3][kTileElems];
 
   const int64_t total = (int64_t)p.n_tiles * p.hkv;
   const int64_t wid = xcd_remap(blockIdx.x, total);
@@ -721,8 +741,8 @@ attn_direct_kernel(AttnParams p) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int head = g * G + (wave % G);
-  const int qrow = (wave / G) * kQRows + (lane & 31);
+  const int head = PACK ? g * G + (lane & 31) / (kQRows / G) : g * G + (wave % G);
+  const int qrow = PACK ? (lane & 31) % (kQRows / G) : (wave / G) * kQRows + (lane & 31);
   const bool row_ok = qrow < tile.nq;
   const int64_t tok = (int64_t)tile.q0 + qrow;
 
@@ -731,11 +751,14 @@ attn_direct_kernel(AttnParams p) {
     store_empty(p, tok, row_ok, head, lane >> 5);
     return;
   }
-  const uint32_t lds_k0 = lds_addr_of(&lds[0][0][0]);
-  const uint32_t lds_v0 = lds_addr_of(&lds[1][0][0]);
+  const uint32_t lds_k0 = lds_addr_of(&lds_k[0][0]);
+  const uint32_t lds_v0 = lds_addr_of(&lds_v[0][0]);
   TileCopy<NW, false>(ts.src(0), g, ts.kbase(0), lds_k0).issue_all(wave, lane);
   TileCopy<NW, true>(ts.src(0), g, ts.kbase(0), lds_v0).issue_all(wave, lane);
-  if (ts.n_tiles > 1) TileCopy<NW, false>(ts.src(1), g, ts.kbase(1), lds_k0 + kSlotBytes).issue_all(wave, lane);
+  if (ts.n_tiles > 1) {
+    TileCopy<NW, false>(ts.src(1), g, ts.kbase(1), lds_k0 + kSlotBytes).issue_all(wave, lane);
+    TileCopy<NW, true>(ts.src(1), g, ts.kbase(1), lds_v0 + kSlotBytes).issue_all(wave, lane);
+  }
 
   WaveAttn w;
   w.init(p, tile, tok, row_ok, qrow, head, lane);
@@ -743,29 +766,35 @@ attn_direct_kernel(AttnParams p) {
   // prologue: scores of tile 0
   f32x16_t s_cur[2];
   publish();
-  if (ts.n_ct > 0) w.scores<FC>(lds[0][0], s_cur);
-  else w.scores<FS>(lds[0][0], s_cur);
+  if (ts.n_ct > 0) w.scores<FC>(lds_k[0], s_cur);
+  else w.scores<FS>(lds_k[0], s_cur);
   if (ts.n_full == 0) w.mask(s_cur, ts.kbase(0), 0 < ts.n_ct, ts.cs.len);
   w.rescale(w.row_max(s_cur));
 
-  // step j: issue K(j+2), V(j+1); S(j+1) with P(j); PV(j) with mask/max of
-  // j+1. PV_FP8 / S_FP8: formats of tiles j and j+1.
+  // step j: issue K(j+2), V(j+2); S(j+1) with P(j); PV(j) with mask/max of
+  // j+1. PV_FP8 / S_FP8: formats of tiles j and j+1. vs: V slot of tile j
+  // (j mod 3, kept as a rotating counter).
+  int vs = 0;
   auto step = [&](int j, auto pv_tag, auto s_tag, auto mask_tag) {
     constexpr bool PV_FP8 = decltype(pv_tag)::value;
     constexpr bool S_FP8 = decltype(s_tag)::value;
     constexpr bool MASK_NEXT = decltype(mask_tag)::value;
-    // waits for this wave's copies of K(j+1) and V(j); the barrier then makes
-    // every wave's copies visible and guarantees that step j-1 (which read
-    // K(j) and V(j-1)) is finished everywhere
-    publish();
-    if (j + 2 < ts.n_tiles)
+    // waits for this wave's copies of K(j+1) and V(j) -- the copies of
+    // V(j+1), issued last (by step j-1 or the prologue), may stay in flight;
+    // the barrier then makes every wave's copies visible and guarantees that
+    // step j-1 (which read K(j) and V(j-1)) is finished everywhere
+    publish_keep<(S_FP8 ? 8 : 16) / NW>();
+    const int vs_new = vs == 0 ? 2 : vs - 1;        // (j + 2) mod 3
+    if (j + 2 < ts.n_tiles) {
       TileCopy<NW, false>(ts.src(j + 2), g, ts.kbase(j + 2), lds_k0 + (j & 1) * kSlotBytes).issue_all(wave, lane);
-    TileCopy<NW, true>(ts.src(j + 1), g, ts.kbase(j + 1), lds_v0 + ((j + 1) & 1) * kSlotBytes).issue_all(wave, lane);
+      TileCopy<NW, true>(ts.src(j + 2), g, ts.kbase(j + 2), lds_v0 + vs_new * kSlotBytes).issue_all(wave, lane);
+    }
     bf16x8_t pb[2][2];
     w.probs(s_cur, pb);
     f32x16_t s_nxt[2];
-    w.scores<S_FP8>(lds[0][(j + 1) & 1], s_nxt);
-    w.pv<PV_FP8>(lds[1][j & 1], pb);
+    w.scores<S_FP8>(lds_k[(j + 1) & 1], s_nxt);
+    w.pv<PV_FP8>(lds_v[vs], pb);
+    vs = vs == 2 ? 0 : vs + 1;
     if constexpr (MASK_NEXT) w.mask(s_nxt, ts.kbase(j + 1), j + 1 < ts.n_ct, ts.cs.len);
     w.rescale(w.row_max(s_nxt));
 #pragma unroll
@@ -787,43 +816,60 @@ attn_direct_kernel(AttnParams p) {
     publish();
     bf16x8_t pb[2][2];
     w.probs(s_cur, pb);
-    if (j < ts.n_ct) w.pv<FC>(lds[1][j & 1], pb);
-    else w.pv<FS>(lds[1][j & 1], pb);
+    if (j < ts.n_ct) w.pv<FC>(lds_v[vs], pb);
+    else w.pv<FS>(lds_v[vs], pb);
   }
   w.store(p, tok, row_ok, head);
 }
 
-// both the direct and the register-staged kernel: max(G, 4) waves of G heads
-// x (waves / G) groups of 32 query tokens
-int attn_tile_tokens(int group) { return kQRows * (group >= 4 ? group : 4) / group; }
+// query tokens per tile: unpacked (both the direct and the register-staged
+// kernel), max(G, 4) waves of G heads x (waves / G) groups of 32 tokens;
+// packed, one wave of G heads x 32/G tokens
+int attn_tile_tokens(int group, bool packed) {
+  return packed ? kQRows / group : kQRows * (group >= 4 ? group : 4) / group;
+}
 
-template <bool FC, bool FS>
+bool attn_direct_ok(bool fp8_cross, bool fp8_self, float k_scale, float v_scale) {
+  // E4M3 sources with unit scales are read by the direct kernel (decoded after
+  // each LDS read); other scales take the register-staged kernel, which
+  // applies them while staging
+  return !(fp8_cross || fp8_self) || (k_scale == 1.0f && v_scale == 1.0f);
+}
+
+template <bool FC, bool FS, bool PACK>
 static hipError_t launch_direct(const AttnParams& p, int group, dim3 gr, hipStream_t s) {
+  const dim3 blk(PACK ? 64 : 256);
   switch (group) {
-    case 1: attn_direct_kernel<1, FC, FS><<<gr, dim3(256), 0, s>>>(p); break;
-    case 2: attn_direct_kernel<2, FC, FS><<<gr, dim3(256), 0, s>>>(p); break;
-    case 4: attn_direct_kernel<4, FC, FS><<<gr, dim3(256), 0, s>>>(p); break;
-    case 8: attn_direct_kernel<8, FC, FS><<<gr, dim3(512), 0, s>>>(p); break;
+    case 1: attn_direct_kernel<1, FC, FS, PACK><<<gr, blk, 0, s>>>(p); break;
+    case 2: attn_direct_kernel<2, FC, FS, PACK><<<gr, blk, 0, s>>>(p); break;
+    case 4: attn_direct_kernel<4, FC, FS, PACK><<<gr, blk, 0, s>>>(p); break;
+    case 8: attn_direct_kernel<8, FC, FS, PACK><<<gr, dim3(PACK ? 64 : 512), 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bf16(const AttnParams& p, int group, bool fp8_cross, bool fp8_self, hipStream_t s) {
+template <bool PACK>
+static hipError_t launch_direct_fmt(const AttnParams& p, int group, bool fp8_cross, bool fp8_self,
+                                    dim3 gr, hipStream_t s) {
+  if (fp8_cross && fp8_self) return launch_direct<true, true, PACK>(p, group, gr, s);
+  if (fp8_cross) return launch_direct<true, false, PACK>(p, group, gr, s);
+  if (fp8_self) return launch_direct<false, true, PACK>(p, group, gr, s);
+  return launch_direct<false, false, PACK>(p, group, gr, s);
+}
+
+hipError_t launch_attn_bf16(const AttnParams& p, int group, bool fp8_cross, bool fp8_self, bool packed,
+                            hipStream_t s) {
   if (p.n_tiles == 0) return hipSuccess;
   const int64_t total = (int64_t)p.n_tiles * p.hkv;
   const int64_t grid = (total + 7) / 8 * 8;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 gr((unsigned)grid);
-  const bool any_fp8 = fp8_cross || fp8_self;
-  // E4M3 sources with unit scales are read by the direct kernel (decoded after
-  // each LDS read); other scales take the register-staged kernel, which
-  // applies them while staging
-  if (!any_fp8 || (p.k_scale == 1.0f && p.v_scale == 1.0f)) {
-    if (fp8_cross && fp8_self) return launch_direct<true, true>(p, group, gr, s);
-    if (fp8_cross) return launch_direct<true, false>(p, group, gr, s);
-    if (fp8_self) return launch_direct<false, true>(p, group, gr, s);
-    return launch_direct<false, false>(p, group, gr, s);
+  const bool direct = attn_direct_ok(fp8_cross, fp8_self, p.k_scale, p.v_scale);
+  if (packed && !direct) return hipErrorInvalidValue;      // packed tiles need the direct kernel
+  if (direct) {
+    return packed ? launch_direct_fmt<true>(p, group, fp8_cross, fp8_self, gr, s)
+                  : launch_direct_fmt<false>(p, group, fp8_cross, fp8_self, gr, s);
   }
   switch (group) {
     case 1: attn_bf16_kernel<1><<<gr, dim3(256), 0, s>>>(p); break;

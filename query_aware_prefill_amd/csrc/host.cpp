@@ -369,6 +369,7 @@ quail_status ensure_rope(quail_ctx* c, hipStream_t s) {
 // One batch of token rows through the decoder stack.
 struct Batch {
   bool anchor_mode = false;
+  bool packed = false;                      // attention tiles are packed (one wave each)
   int32_t n_tok = 0;
   std::vector<int32_t> tok_src, pos, seg_lo, kv_lapad;
   std::vector<int64_t> kv_row;
@@ -464,7 +465,7 @@ quail_status run_batch(quail_ctx* c, const Batch& b, const int32_t* tokens, uint
     // anchor batches attend over their own slab (self source); join batches
     // read the anchor slab as the cross source and bf16 suffix K/V as self
     const bool slab_fp8 = cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3;
-    HIP_TRY(launch_attn_bf16(ap, G, !b.anchor_mode && slab_fp8, b.anchor_mode && slab_fp8, s));
+    HIP_TRY(launch_attn_bf16(ap, G, !b.anchor_mode && slab_fp8, b.anchor_mode && slab_fp8, b.packed, s));
 
     GemmParams go{};
     go.A = obuf; go.lda = (int64_t)Hq * kHeadDim; go.B = lw.w_o; go.scale = lw.s_o;
@@ -562,19 +563,26 @@ quail_status anchor_core(quail_ctx* c, int32_t n, const int32_t* tokens, const i
   if (quail_status st = ensure_rope(c, s)) return st;
   const quail_model_config& cf = c->cfg;
   const int G = cf.n_q_heads / cf.n_kv_heads;
-  const int TQ = attn_tile_tokens(G);
   const size_t esz = kv_elem_bytes(cf);
+  const bool slab_fp8 = cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3;
   // batches of whole anchors up to T tokens
   int32_t a0 = 0;
   while (a0 < n) {
     Batch b;
     b.anchor_mode = true;
     int32_t a1 = a0;
-    int32_t tok = 0;
+    int32_t tok = 0, max_len = 0;
     while (a1 < n && (n_uses[a1] == 0 || tok + lens[a1] <= c->T)) {
-      if (n_uses[a1] > 0) tok += lens[a1];
+      if (n_uses[a1] > 0) {
+        tok += lens[a1];
+        max_len = std::max(max_len, lens[a1]);
+      }
       ++a1;
     }
+    // packed tiles when every anchor is that short (see attn_tile_tokens)
+    b.packed = max_len <= attn_tile_tokens(G, true) &&
+               attn_direct_ok(false, slab_fp8, cf.k_scale, cf.v_scale);
+    const int TQ = attn_tile_tokens(G, b.packed);
     for (int32_t a = a0; a < a1; ++a) {
       if (n_uses[a] == 0) continue;
       const quail_ctx::Slot& sl = c->slots[slot_of[a]];
@@ -791,8 +799,8 @@ quail_status join_core(quail_ctx* c, int32_t n, const quail_anchor* ha, const in
     return kx < ky;
   });
   const int G = cf.n_q_heads / cf.n_kv_heads;
-  const int TQ = attn_tile_tokens(G);
   const size_t esz = kv_elem_bytes(cf);
+  const bool slab_fp8 = cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3;
   int32_t p0 = 0;
   while (p0 < n) {
     Batch b;
@@ -802,6 +810,18 @@ quail_status join_core(quail_ctx* c, int32_t n, const quail_anchor* ha, const in
       tok += lens[order[p1]];
       ++p1;
     }
+    // packed attention tiles when every run of pairs sharing an anchor has
+    // that few query tokens (the anchor K/V stream is then the work)
+    int32_t max_group = 0;
+    for (int32_t i = p0; i < p1;) {
+      int32_t j = i, gtok = 0;
+      while (j < p1 && slot[order[j]] == slot[order[i]]) gtok += lens[order[j++]];
+      max_group = std::max(max_group, gtok);
+      i = j;
+    }
+    b.packed = max_group <= attn_tile_tokens(G, true) &&
+               attn_direct_ok(slab_fp8, false, cf.k_scale, cf.v_scale);
+    const int TQ = attn_tile_tokens(G, b.packed);
     // source 0: this batch's suffix K/V (token-major, reused every layer)
     KVSrc self{};
     self.k = ws_ptr<uint16_t>(c, c->L.k);
@@ -1104,7 +1124,6 @@ quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t 
     HIP_TRY(launch_attn_f32(p, st));
     return QUAIL_OK;
   }
-  const int TQ = attn_tile_tokens(G);
   std::vector<KVSrc> srcs;
   KVSrc self{};
   self.k = k; self.v = v; self.tok_stride = (int64_t)hkv * d; self.head_stride = d; self.len = T; self.fp8 = 0;
@@ -1120,6 +1139,16 @@ quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t 
     x.fp8 = a_fp8 ? 1 : 0;
     srcs.push_back(x);
   }
+  // packed tiles when every run of suffixes sharing an anchor is that short
+  int32_t max_group = 0;
+  for (int32_t s0 = 0; s0 < n_suffix;) {
+    int32_t s1 = s0 + 1;
+    while (s1 < n_suffix && s_anchor[s1] == s_anchor[s0]) ++s1;
+    max_group = std::max(max_group, s_off[s1] - s_off[s0]);
+    s0 = s1;
+  }
+  const bool packed = max_group <= attn_tile_tokens(G, true);
+  const int TQ = attn_tile_tokens(G, packed);
   std::vector<AttnTile> tiles;
   int32_t s0 = 0;
   while (s0 < n_suffix) {
@@ -1150,7 +1179,7 @@ quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t 
   p.lse = lse; p.hq = hq; p.hkv = hkv;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
   p.k_scale = 1.0f; p.v_scale = 1.0f;
-  HIP_TRY(launch_attn_bf16(p, G, a_fp8, false, st));
+  HIP_TRY(launch_attn_bf16(p, G, a_fp8, false, packed, st));
   return QUAIL_OK;
 }
 

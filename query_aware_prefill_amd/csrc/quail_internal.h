@@ -116,9 +116,14 @@ struct Head8Params {
 // fp8_cross / fp8_self: the cross (anchor) / self key sources of this launch
 // hold E4M3 codes. With unit k/v scales every combination runs the direct
 // HBM->LDS kernel; other scales take the register-staged kernel.
-hipError_t launch_attn_bf16(const AttnParams& p, int group, bool fp8_cross, bool fp8_self, hipStream_t s);
+// packed: tiles of attn_tile_tokens(group, true) tokens, one wave each
+// (G heads x 32/G tokens in its 32 rows); requires the direct kernel.
+hipError_t launch_attn_bf16(const AttnParams& p, int group, bool fp8_cross, bool fp8_self, bool packed,
+                            hipStream_t s);
+// whether a launch with these formats and scales runs the direct kernel
+bool attn_direct_ok(bool fp8_cross, bool fp8_self, float k_scale, float v_scale);
 // query tokens per attention tile (one workgroup) for GQA group size `group`
-int attn_tile_tokens(int group);
+int attn_tile_tokens(int group, bool packed);
 hipError_t launch_attn_f32(const AttnF32Params& p, hipStream_t s);
 hipError_t launch_gemm(const GemmParams& p, GemmEpi epi, hipStream_t s);
 hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s);

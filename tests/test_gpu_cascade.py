@@ -175,6 +175,52 @@ def test_e4m3_anchor_cases(B, ci):
     assert np.max(np.abs(lse - ref_l)) <= 1e-3 + 1e-4 * np.max(np.abs(ref_l))
 
 
+PACKED_CASES = [
+    # (a_len, s_anchor, s_len, hq, hkv): every run of suffixes sharing an
+    # anchor has at most 32/G query tokens, so each tile is one wave holding
+    # G heads x 32/G tokens; one run exactly at that size, several suffixes
+    # in one tile, filter rows, ragged anchors
+    ([65, 1, 130], [0, 1, 2, 2, -1], [1, 3, 5, 3, 2], 32, 8),     # G = 4: 8 tokens per tile
+    ([768, 200], [0, 1, 1], [2, 1, 3], 32, 4),                     # G = 8: 4 tokens
+    ([100, 64], [0, 0, 1], [7, 9, 16], 8, 4),                      # G = 2: 16 tokens
+    ([33], [0, 0, -1], [20, 12, 32], 4, 4),                        # G = 1: 32 tokens
+]
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "e4m3"])
+@pytest.mark.parametrize("ci", range(len(PACKED_CASES)))
+def test_packed_tiles(B, ci, fmt):
+    """Launches whose anchors each have few query tokens run packed tiles (one
+    wave per tile, rows = heads x tokens); bf16 and E4M3 anchor K/V."""
+    import torch
+    from query_aware_prefill_amd.device import to_device
+    a_len, s_anchor, s_len, hq, hkv = PACKED_CASES[ci]
+    say("packed case", ci, fmt, a_len, s_len, hq, hkv)
+    case = W.cascade_case(80 + ci, a_len, s_anchor, s_len, hq=hq, hkv=hkv, d=128, dtype="bf16", cfg_id=14)
+    if fmt == "bf16":
+        o, lse = _run(B, case)
+        ref_o, ref_l = OA.cascade_case_reference(case)
+    else:
+        codes, ref_case = _e4m3_anchor_case(case)
+        dev = {k: to_device(case[k]) for k in ("q", "k", "v")}
+        T = int(case["s_off"][-1])
+        out = torch.empty((T, hq, 128), dtype=torch.int16, device="cuda")
+        lse_t = torch.empty((T, hq), dtype=torch.float32, device="cuda")
+        ws = torch.empty(B.quail_cascade_workspace_bytes(case["a_off"], case["s_off"]), dtype=torch.uint8,
+                         device="cuda")
+        B.quail_cascade_attn(B.DTYPE_FP8_E4M3, hq, hkv, 128, case["sm_scale"], to_device(codes["ak"]),
+                             to_device(codes["av"]), case["a_off"], case["s_anchor"], dev["q"], dev["k"],
+                             dev["v"], case["s_off"], out, lse_t, ws)
+        torch.cuda.synchronize()
+        o, lse = bf16_f64(u16(out)), lse_t.cpu().numpy().astype(np.float64)
+        ref_o, ref_l = OA.cascade_case_reference(ref_case)
+    for s in range(len(s_len)):
+        sl = slice(case["s_off"][s], case["s_off"][s + 1])
+        err = rel_inf(o[sl], ref_o[sl])
+        assert err <= 2e-2, (s, err)
+    assert np.max(np.abs(lse - ref_l)) <= 1e-3 + 1e-4 * np.max(np.abs(ref_l))
+
+
 def test_c1_reduced_full_length_ranges(B):
     """4 anchors of U{512..2048} x 8 suffixes of U{32..128}, 32q/8kv x 128."""
     say("C1 reduced")
