@@ -406,7 +406,7 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 // length are clamped to its last row (their scores are masked); full tiles
 // skip the clamp. Per-lane offsets are 24-bit products (token strides are
 // bounded on the host).
-template <int NW, bool IS_V>
+template <int NW, bool IS_V, int ROWS = kKeyTile>
 struct TileCopy {
   const uint8_t* b8;
   uint32_t tb, last, dst;
@@ -417,13 +417,13 @@ struct TileCopy {
     tb = (uint32_t)src.tok_stride << sh;
     const int64_t base = ((int64_t)g * src.head_stride + (int64_t)kbase * src.tok_stride) << sh;
     b8 = reinterpret_cast<const uint8_t*>(IS_V ? src.v : src.k) + base;
-    full = kbase + kKeyTile <= src.len;
+    full = kbase + ROWS <= src.len;
     last = (uint32_t)max(src.len - 1 - kbase, 0);
     dst = dst_;
   }
   __device__ __forceinline__ void issue_all(int wave, int lane) const {
     if (!fp8) {
-      constexpr int PER = 16 / NW;
+      constexpr int PER = ROWS / 4 / NW;
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         const int slice = wave * PER + i;
@@ -433,7 +433,7 @@ struct TileCopy {
         copy16_to_lds_off(b8, __umul24(r, tb) + off, dst + slice * 1024);
       }
     } else {
-      constexpr int PER = 8 / NW;
+      constexpr int PER = ROWS / 8 / NW;
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         const int slice = wave * PER + i;
@@ -519,16 +519,18 @@ struct WaveAttn {
 
   // S^T = K . Q^T of the tile at Kt (two 32-key halves); lane l32 reads key
   // row pi(l32) of each half
-  template <bool FP8>
+  // HALF: only the first 32 keys exist in the slot; the second half's
+  // scores are -inf (no key).
+  template <bool FP8, bool HALF = false>
   __device__ __forceinline__ void scores(const uint16_t* Kt, f32x16_t (&s)[2]) const {
     const int krow = key_pi(lane & 31);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) s[kb][r] = (HALF && kb == 1) ? -INFINITY : 0.0f;
     if constexpr (!FP8) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < (HALF ? 1 : 2); ++kb) {
         const int row = kb * 32 + krow;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
@@ -541,7 +543,7 @@ struct WaveAttn {
     } else {
       const uint8_t* K8 = reinterpret_cast<const uint8_t*>(Kt);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < (HALF ? 1 : 2); ++kb) {
         const int row = kb * 32 + krow;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -619,7 +621,8 @@ struct WaveAttn {
   // O^T += V^T . P^T with the tile at Vt; A lane: dim row cb*32 + l32, keys
   // kb*32 + 16sp + 8hi + 0..7. The 16-lane block (lane / 16) covers dims
   // cb*32 + 16*(block % 2) .. +15 and keys +8 for blocks 2, 3.
-  template <bool FP8>
+  // HALF: only the first 32 keys exist in the slot (their P is all there is)
+  template <bool FP8, bool HALF = false>
   __device__ __forceinline__ void pv(const uint16_t* Vt, const bf16x8_t (&pb)[2][2]) {
     const int s16 = lane & 15;
     const int dhalf = (lane >> 4) & 1;
@@ -628,7 +631,7 @@ struct WaveAttn {
       // s16 / 4 of the group and dims 4*(s16 % 4) .. +3 of the 16-dim half
       const int key0 = hi * 8 + (s16 >> 2);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < (HALF ? 1 : 2); ++kb)
 #pragma unroll
         for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
@@ -647,7 +650,7 @@ struct WaveAttn {
       const uint8_t* V8 = reinterpret_cast<const uint8_t*>(Vt);
       const int key0 = hi * 8 + (s16 >> 1);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < (HALF ? 1 : 2); ++kb)
 #pragma unroll
         for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
@@ -728,9 +731,17 @@ template <int G, bool FC, bool FS, bool PACK>
 __global__ void __launch_bounds__(PACK ? 64 : 64 * (G >= 4 ? G : 4), 2)
 attn_direct_kernel(AttnParams p) {
   constexpr int NW = PACK ? 1 : (G >= 4 ? G : 4);
-  constexpr uint32_t kSlotBytes = kTileElems * 2;
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_k[2][kTileElems];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_v[3][kTileElems];
+  // Packed launches with E4M3 anchors use 8-KB slots (an E4M3 tile is 8 KB),
+  // 40 KB per workgroup, four workgroups per CU. Their bf16 self tiles hold
+  // only the first 32 keys (HALF_SELF): a packed tile's tokens, and so its
+  // self keys, never exceed 32 (the host packs only runs of at most 32/G
+  // tokens per anchor), and one self tile covers them.
+  constexpr bool SMALL = PACK && FC;
+  constexpr bool HALF_SELF = SMALL && !FS;
+  constexpr uint32_t kSlotBytes = SMALL ? 8192 : kTileElems * 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[5 * kSlotBytes];   // K: 2 slots, V: 3
+  auto kslot = [&](int i) __attribute__((always_inline)) { return reinterpret_cast<const uint16_t*>(lds_raw + i * kSlotBytes); };
+  auto vslot = [&](int i) __attribute__((always_inline)) { return reinterpret_cast<const uint16_t*>(lds_raw + (2 + i) * kSlotBytes); };
 
   const int64_t total = (int64_t)p.n_tiles * p.hkv;
   const int64_t wid = xcd_remap(blockIdx.x, total);
@@ -751,14 +762,20 @@ attn_direct_kernel(AttnParams p) {
     store_empty(p, tok, row_ok, head, lane >> 5);
     return;
   }
-  const uint32_t lds_k0 = lds_addr_of(&lds_k[0][0]);
-  const uint32_t lds_v0 = lds_addr_of(&lds_v[0][0]);
-  TileCopy<NW, false>(ts.src(0), g, ts.kbase(0), lds_k0).issue_all(wave, lane);
-  TileCopy<NW, true>(ts.src(0), g, ts.kbase(0), lds_v0).issue_all(wave, lane);
-  if (ts.n_tiles > 1) {
-    TileCopy<NW, false>(ts.src(1), g, ts.kbase(1), lds_k0 + kSlotBytes).issue_all(wave, lane);
-    TileCopy<NW, true>(ts.src(1), g, ts.kbase(1), lds_v0 + kSlotBytes).issue_all(wave, lane);
-  }
+  const uint32_t lds_k0 = lds_addr_of(lds_raw);
+  const uint32_t lds_v0 = lds_k0 + 2 * kSlotBytes;
+  // K and V copies of tile j into K slot ks and V slot vs
+  auto issue = [&](int j, int ks, int vs) __attribute__((always_inline)) {
+    if (HALF_SELF && j >= ts.n_ct) {
+      TileCopy<NW, false, kKeyTile / 2>(ts.src(j), g, ts.kbase(j), lds_k0 + ks * kSlotBytes).issue_all(wave, lane);
+      TileCopy<NW, true, kKeyTile / 2>(ts.src(j), g, ts.kbase(j), lds_v0 + vs * kSlotBytes).issue_all(wave, lane);
+    } else {
+      TileCopy<NW, false>(ts.src(j), g, ts.kbase(j), lds_k0 + ks * kSlotBytes).issue_all(wave, lane);
+      TileCopy<NW, true>(ts.src(j), g, ts.kbase(j), lds_v0 + vs * kSlotBytes).issue_all(wave, lane);
+    }
+  };
+  issue(0, 0, 0);
+  if (ts.n_tiles > 1) issue(1, 1, 1);
 
   WaveAttn w;
   w.init(p, tile, tok, row_ok, qrow, head, lane);
@@ -766,58 +783,58 @@ attn_direct_kernel(AttnParams p) {
   // prologue: scores of tile 0
   f32x16_t s_cur[2];
   publish();
-  if (ts.n_ct > 0) w.scores<FC>(lds_k[0], s_cur);
-  else w.scores<FS>(lds_k[0], s_cur);
+  if (ts.n_ct > 0) w.scores<FC>(kslot(0), s_cur);
+  else w.scores<FS, HALF_SELF>(kslot(0), s_cur);
   if (ts.n_full == 0) w.mask(s_cur, ts.kbase(0), 0 < ts.n_ct, ts.cs.len);
   w.rescale(w.row_max(s_cur));
 
   // step j: issue K(j+2), V(j+2); S(j+1) with P(j); PV(j) with mask/max of
-  // j+1. PV_FP8 / S_FP8: formats of tiles j and j+1. vs: V slot of tile j
-  // (j mod 3, kept as a rotating counter).
+  // j+1. PV_SELF / S_SELF: tiles j and j+1 are self tiles (format FS, else
+  // FC). vs: V slot of tile j (j mod 3, kept as a rotating counter).
   int vs = 0;
-  auto step = [&](int j, auto pv_tag, auto s_tag, auto mask_tag) {
-    constexpr bool PV_FP8 = decltype(pv_tag)::value;
-    constexpr bool S_FP8 = decltype(s_tag)::value;
+  auto step = [&](int j, auto pv_tag, auto s_tag, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool PV_SELF = decltype(pv_tag)::value;
+    constexpr bool S_SELF = decltype(s_tag)::value;
     constexpr bool MASK_NEXT = decltype(mask_tag)::value;
+    constexpr bool PV_FP8 = PV_SELF ? FS : FC, S_FP8 = S_SELF ? FS : FC;
+    constexpr bool PV_HALF = PV_SELF && HALF_SELF, S_HALF = S_SELF && HALF_SELF;
+    // copies per wave of one V tile of tile j+1's format and size
+    constexpr int NV_NEXT = (S_FP8 ? 8 : 16) / (S_HALF ? 2 : 1) / NW;
     // waits for this wave's copies of K(j+1) and V(j) -- the copies of
     // V(j+1), issued last (by step j-1 or the prologue), may stay in flight;
     // the barrier then makes every wave's copies visible and guarantees that
     // step j-1 (which read K(j) and V(j-1)) is finished everywhere
-    publish_keep<(S_FP8 ? 8 : 16) / NW>();
-    const int vs_new = vs == 0 ? 2 : vs - 1;        // (j + 2) mod 3
-    if (j + 2 < ts.n_tiles) {
-      TileCopy<NW, false>(ts.src(j + 2), g, ts.kbase(j + 2), lds_k0 + (j & 1) * kSlotBytes).issue_all(wave, lane);
-      TileCopy<NW, true>(ts.src(j + 2), g, ts.kbase(j + 2), lds_v0 + vs_new * kSlotBytes).issue_all(wave, lane);
-    }
+    publish_keep<NV_NEXT>();
+    if (j + 2 < ts.n_tiles) issue(j + 2, j & 1, vs == 0 ? 2 : vs - 1);   // V slot (j + 2) mod 3
     bf16x8_t pb[2][2];
     w.probs(s_cur, pb);
     f32x16_t s_nxt[2];
-    w.scores<S_FP8>(lds_k[(j + 1) & 1], s_nxt);
-    w.pv<PV_FP8>(lds_v[vs], pb);
+    w.scores<S_FP8, S_HALF>(kslot((j + 1) & 1), s_nxt);
+    w.pv<PV_FP8, PV_HALF>(vslot(vs), pb);
     vs = vs == 2 ? 0 : vs + 1;
     if constexpr (MASK_NEXT) w.mask(s_nxt, ts.kbase(j + 1), j + 1 < ts.n_ct, ts.cs.len);
     w.rescale(w.row_max(s_nxt));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
   };
-  using C8 = MaskTag<FC>;
-  using S8 = MaskTag<FS>;
+  using Cross = MaskTag<false>;
+  using Self = MaskTag<true>;
   int j = 0;
-  for (; j + 1 < ts.n_full; ++j) step(j, C8{}, C8{}, MaskTag<false>{});
-  for (; j + 1 < ts.n_ct; ++j) step(j, C8{}, C8{}, MaskTag<true>{});
+  for (; j + 1 < ts.n_full; ++j) step(j, Cross{}, Cross{}, MaskTag<false>{});
+  for (; j + 1 < ts.n_ct; ++j) step(j, Cross{}, Cross{}, MaskTag<true>{});
   if (j + 1 < ts.n_tiles && j < ts.n_ct) {
-    step(j, C8{}, S8{}, MaskTag<true>{});
+    step(j, Cross{}, Self{}, MaskTag<true>{});
     ++j;
   }
-  for (; j + 1 < ts.n_tiles; ++j) step(j, S8{}, S8{}, MaskTag<true>{});
+  for (; j + 1 < ts.n_tiles; ++j) step(j, Self{}, Self{}, MaskTag<true>{});
   // epilogue: the last tile's PV (its V copy was issued by the last step, or
   // by the prologue)
   {
     publish();
     bf16x8_t pb[2][2];
     w.probs(s_cur, pb);
-    if (j < ts.n_ct) w.pv<FC>(lds_v[vs], pb);
-    else w.pv<FS>(lds_v[vs], pb);
+    if (j < ts.n_ct) w.pv<FC>(vslot(vs), pb);
+    else w.pv<FS, HALF_SELF>(vslot(vs), pb);
   }
   w.store(p, tok, row_ok, head);
 }
