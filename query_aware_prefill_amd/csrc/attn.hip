@@ -452,24 +452,27 @@ struct MaskTag { static constexpr bool value = B; };
 // The key tiles one workgroup visits: first the cross tiles of its anchor
 // source (the last one ragged), then the self tiles from self_k0 up to its
 // last query. Tiles j >= n_full need masking.
+// TKC / TKS: keys per cross / self tile (64, or 32 for the half tiles of
+// packed launches).
+template <int TKC = kKeyTile, int TKS = kKeyTile>
 struct TileSeq {
   KVSrc cs{}, ss{};
   int n_ct = 0, n_st = 0, n_full = 0, n_tiles = 0, self_k0 = 0;
   __device__ __forceinline__ TileSeq(const AttnParams& p, const AttnTile& tile) {
     if (tile.cross >= 0) {
       cs = p.srcs[tile.cross];
-      n_ct = (cs.len + kKeyTile - 1) / kKeyTile;
-      n_full = cs.len / kKeyTile;
+      n_ct = (cs.len + TKC - 1) / TKC;
+      n_full = cs.len / TKC;
     }
     if (tile.self >= 0) {
       ss = p.srcs[tile.self];
-      n_st = max(0, (tile.self_qbase + tile.nq - tile.self_k0 + kKeyTile - 1) / kKeyTile);
+      n_st = max(0, (tile.self_qbase + tile.nq - tile.self_k0 + TKS - 1) / TKS);
     }
     n_tiles = n_ct + n_st;
     self_k0 = tile.self_k0;
   }
   __device__ __forceinline__ const KVSrc& src(int j) const { return j < n_ct ? cs : ss; }
-  __device__ __forceinline__ int kbase(int j) const { return j < n_ct ? j * kKeyTile : self_k0 + (j - n_ct) * kKeyTile; }
+  __device__ __forceinline__ int kbase(int j) const { return j < n_ct ? j * TKC : self_k0 + (j - n_ct) * TKS; }
 };
 
 // One wave's share of the bf16 MFMA attention: 32 query rows of one head
@@ -731,14 +734,12 @@ template <int G, bool FC, bool FS, bool PACK>
 __global__ void __launch_bounds__(PACK ? 64 : 64 * (G >= 4 ? G : 4), 2)
 attn_direct_kernel(AttnParams p) {
   constexpr int NW = PACK ? 1 : (G >= 4 ? G : 4);
-  // Packed launches with E4M3 anchors use 8-KB slots (an E4M3 tile is 8 KB),
-  // 40 KB per workgroup, four workgroups per CU. Their bf16 self tiles hold
-  // only the first 32 keys (HALF_SELF): a packed tile's tokens, and so its
-  // self keys, never exceed 32 (the host packs only runs of at most 32/G
-  // tokens per anchor), and one self tile covers them.
-  constexpr bool SMALL = PACK && FC;
-  constexpr bool HALF_SELF = SMALL && !FS;
-  constexpr uint32_t kSlotBytes = SMALL ? 8192 : kTileElems * 2;
+  // Packed launches use 8-KB slots, 40 KB per workgroup, four workgroups per
+  // CU: an E4M3 tile of 64 keys is 8 KB, and bf16 tiles are half tiles of 32
+  // keys (HALF_*), whose second 32-key half of the scores is -inf.
+  constexpr bool HALF_CROSS = PACK && !FC;
+  constexpr bool HALF_SELF = PACK && !FS;
+  constexpr uint32_t kSlotBytes = PACK ? 8192 : kTileElems * 2;
   __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[5 * kSlotBytes];   // K: 2 slots, V: 3
   auto kslot = [&](int i) __attribute__((always_inline)) { return reinterpret_cast<const uint16_t*>(lds_raw + i * kSlotBytes); };
   auto vslot = [&](int i) __attribute__((always_inline)) { return reinterpret_cast<const uint16_t*>(lds_raw + (2 + i) * kSlotBytes); };
@@ -757,7 +758,7 @@ attn_direct_kernel(AttnParams p) {
   const bool row_ok = qrow < tile.nq;
   const int64_t tok = (int64_t)tile.q0 + qrow;
 
-  const TileSeq ts(p, tile);
+  const TileSeq<HALF_CROSS ? kKeyTile / 2 : kKeyTile, HALF_SELF ? kKeyTile / 2 : kKeyTile> ts(p, tile);
   if (ts.n_tiles == 0) {
     store_empty(p, tok, row_ok, head, lane >> 5);
     return;
@@ -766,7 +767,7 @@ attn_direct_kernel(AttnParams p) {
   const uint32_t lds_v0 = lds_k0 + 2 * kSlotBytes;
   // K and V copies of tile j into K slot ks and V slot vs
   auto issue = [&](int j, int ks, int vs) __attribute__((always_inline)) {
-    if (HALF_SELF && j >= ts.n_ct) {
+    if (j < ts.n_ct ? HALF_CROSS : HALF_SELF) {
       TileCopy<NW, false, kKeyTile / 2>(ts.src(j), g, ts.kbase(j), lds_k0 + ks * kSlotBytes).issue_all(wave, lane);
       TileCopy<NW, true, kKeyTile / 2>(ts.src(j), g, ts.kbase(j), lds_v0 + vs * kSlotBytes).issue_all(wave, lane);
     } else {
@@ -783,7 +784,7 @@ attn_direct_kernel(AttnParams p) {
   // prologue: scores of tile 0
   f32x16_t s_cur[2];
   publish();
-  if (ts.n_ct > 0) w.scores<FC>(kslot(0), s_cur);
+  if (ts.n_ct > 0) w.scores<FC, HALF_CROSS>(kslot(0), s_cur);
   else w.scores<FS, HALF_SELF>(kslot(0), s_cur);
   if (ts.n_full == 0) w.mask(s_cur, ts.kbase(0), 0 < ts.n_ct, ts.cs.len);
   w.rescale(w.row_max(s_cur));
@@ -797,7 +798,7 @@ attn_direct_kernel(AttnParams p) {
     constexpr bool S_SELF = decltype(s_tag)::value;
     constexpr bool MASK_NEXT = decltype(mask_tag)::value;
     constexpr bool PV_FP8 = PV_SELF ? FS : FC, S_FP8 = S_SELF ? FS : FC;
-    constexpr bool PV_HALF = PV_SELF && HALF_SELF, S_HALF = S_SELF && HALF_SELF;
+    constexpr bool PV_HALF = PV_SELF ? HALF_SELF : HALF_CROSS, S_HALF = S_SELF ? HALF_SELF : HALF_CROSS;
     // copies per wave of one V tile of tile j+1's format and size
     constexpr int NV_NEXT = (S_FP8 ? 8 : 16) / (S_HALF ? 2 : 1) / NW;
     // waits for this wave's copies of K(j+1) and V(j) -- the copies of
@@ -833,7 +834,7 @@ attn_direct_kernel(AttnParams p) {
     publish();
     bf16x8_t pb[2][2];
     w.probs(s_cur, pb);
-    if (j < ts.n_ct) w.pv<FC>(vslot(vs), pb);
+    if (j < ts.n_ct) w.pv<FC, HALF_CROSS>(vslot(vs), pb);
     else w.pv<FS, HALF_SELF>(vslot(vs), pb);
   }
   w.store(p, tok, row_ok, head);
