@@ -406,7 +406,7 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 // length are clamped to its last row (their scores are masked); full tiles
 // skip the clamp. Per-lane offsets are 24-bit products (token strides are
 // bounded on the host).
-template <int NW, bool IS_V, int ROWS = kKeyTile>
+template <int NW, bool IS_V, int ROWS = kKeyTile, bool NT = false>
 struct TileCopy {
   const uint8_t* b8;
   uint32_t tb, last, dst;
@@ -430,7 +430,8 @@ struct TileCopy {
         const uint32_t row = slice * 4 + (lane >> 4);
         const uint32_t off = (IS_V ? swz_v(row, lane & 15) : swz_k(row, lane & 15)) * 16;
         const uint32_t r = full ? row : min(row, last);
-        copy16_to_lds_off(b8, __umul24(r, tb) + off, dst + slice * 1024);
+        if (NT) copy16_to_lds_off_nt(b8, __umul24(r, tb) + off, dst + slice * 1024);
+        else copy16_to_lds_off(b8, __umul24(r, tb) + off, dst + slice * 1024);
       }
     } else {
       constexpr int PER = ROWS / 8 / NW;
@@ -440,7 +441,8 @@ struct TileCopy {
         const uint32_t row = slice * 8 + (lane >> 3);
         const uint32_t off = (IS_V ? swz8_v(row, lane & 7) : swz8_k(row, lane & 7)) * 16;
         const uint32_t r = full ? row : min(row, last);
-        copy16_to_lds_off(b8, __umul24(r, tb) + off, dst + slice * 1024);
+        if (NT) copy16_to_lds_off_nt(b8, __umul24(r, tb) + off, dst + slice * 1024);
+        else copy16_to_lds_off(b8, __umul24(r, tb) + off, dst + slice * 1024);
       }
     }
   }
@@ -766,13 +768,14 @@ attn_direct_kernel(AttnParams p) {
   const uint32_t lds_k0 = lds_addr_of(lds_raw);
   const uint32_t lds_v0 = lds_k0 + 2 * kSlotBytes;
   // K and V copies of tile j into K slot ks and V slot vs
+  // (packed launches stream each anchor's K/V once per kv head: non-temporal)
   auto issue = [&](int j, int ks, int vs) __attribute__((always_inline)) {
     if (j < ts.n_ct ? HALF_CROSS : HALF_SELF) {
-      TileCopy<NW, false, kKeyTile / 2>(ts.src(j), g, ts.kbase(j), lds_k0 + ks * kSlotBytes).issue_all(wave, lane);
-      TileCopy<NW, true, kKeyTile / 2>(ts.src(j), g, ts.kbase(j), lds_v0 + vs * kSlotBytes).issue_all(wave, lane);
+      TileCopy<NW, false, kKeyTile / 2, PACK>(ts.src(j), g, ts.kbase(j), lds_k0 + ks * kSlotBytes).issue_all(wave, lane);
+      TileCopy<NW, true, kKeyTile / 2, PACK>(ts.src(j), g, ts.kbase(j), lds_v0 + vs * kSlotBytes).issue_all(wave, lane);
     } else {
-      TileCopy<NW, false>(ts.src(j), g, ts.kbase(j), lds_k0 + ks * kSlotBytes).issue_all(wave, lane);
-      TileCopy<NW, true>(ts.src(j), g, ts.kbase(j), lds_v0 + vs * kSlotBytes).issue_all(wave, lane);
+      TileCopy<NW, false, kKeyTile, PACK>(ts.src(j), g, ts.kbase(j), lds_k0 + ks * kSlotBytes).issue_all(wave, lane);
+      TileCopy<NW, true, kKeyTile, PACK>(ts.src(j), g, ts.kbase(j), lds_v0 + vs * kSlotBytes).issue_all(wave, lane);
     }
   };
   issue(0, 0, 0);

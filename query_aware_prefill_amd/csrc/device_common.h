@@ -131,6 +131,19 @@ __device__ __forceinline__ void copy16_to_lds_off(const void* sbase, uint32_t vo
                : "memory", "m0");
 }
 
+// The same copy with the non-temporal hint (data read once: streamed past
+// the caches rather than kept in them).
+__device__ __forceinline__ void copy16_to_lds_off_nt(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  const uint64_t a = reinterpret_cast<uint64_t>(sbase);
+  const uint32_t a_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const uint32_t a_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t sa = ((uint64_t)a_hi << 32) | (uint64_t)a_lo;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(voff), "s"(reinterpret_cast<const void*>(sa)), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
 // a wave-uniform value as such (v_readfirstlane; free for values in SGPRs)
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
