@@ -549,7 +549,7 @@ def main():
         "roofline": {
             "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
-            "kernel": "quail::attn_direct_kernel<4, false, false>", "flops_per_launch": flops,
+            "kernel": "quail::attn_direct_kernel<4, false, false, false>", "flops_per_launch": flops,
             "launch_ms": kernel_ms,
             "algorithmic_bytes_per_launch": algorithmic_bytes(a_len, s_len),
         },
