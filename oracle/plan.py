@@ -108,3 +108,93 @@ def replay_residency(anchor_slab, anchor_len, pair_anchor, order, step_bounds):
             del resident[a]
             evictions += 1
     return dict(prefills=prefills, evictions=evictions, regret_tokens=regret, peak=peak)
+
+
+def multijoin_reference(anchor_slab, anchor_len, joins, pool_bytes, max_batch_tokens):
+    """Several joins over one anchor table, run one after another (a later
+    join may depend on an earlier one's results, so their pairs are not
+    merged). [pt] query-aware KV cache bullet: with the whole plan known, KV
+    is kept for its next use and evicted when nothing will use it again.
+
+    Readings taken (the pages give no algorithm):
+      * each join is ordered and cut into steps exactly as one join alone
+        (plan_reference, full pool budget);
+      * the steps of all joins form one sequence; an anchor's last use is its
+        last step in that whole sequence (plan-wide), so an anchor used by
+        several joins stays resident across the joins in between;
+      * before a step, its anchors that are not resident are prefilled (a
+        second prefill of an anchor counts its tokens as regret); when they
+        do not fit beside the anchors kept for later steps, kept anchors are
+        evicted farthest next use first (never used again first; ties: the
+        larger slab, then the lower index) until they fit -- each step's own
+        anchors always fit, the step cutting guarantees it;
+      * after a step, the anchors whose last use it was are evicted.
+
+    joins: list of (pair_anchor, pair_len). Returns dict with the per-join
+    plans, and per global step: the join, its pair range, the anchors
+    prefilled before it (in order of first use within the step), the anchors
+    evicted to make room before it (in eviction order) and the anchors
+    evicted after it (ascending); plus prefills, evictions, regret_tokens and
+    peak (largest resident bytes, measured after each step's prefills)."""
+    plans = [plan_reference(anchor_slab, pa, pl, pool_bytes, max_batch_tokens) for pa, pl in joins]
+    steps = []   # (join, lo, hi, anchors in first-use order)
+    for j, ((pa, _), p) in enumerate(zip(joins, plans)):
+        pa = np.asarray(pa, np.int64)
+        b = p["step_bounds"]
+        for s in range(len(b) - 1):
+            seen = []
+            for i in p["order"][b[s]:b[s + 1]]:
+                a = int(pa[i])
+                if a >= 0 and a not in seen:
+                    seen.append(a)
+            steps.append((j, int(b[s]), int(b[s + 1]), seen))
+    INF = len(steps)
+    uses_at = {}
+    for t, (_, _, _, an) in enumerate(steps):
+        for a in an:
+            uses_at.setdefault(a, []).append(t)
+
+    def next_use(a, t):
+        for u in uses_at[a]:
+            if u > t:
+                return u
+        return INF
+
+    resident = {}
+    ever = set()
+    prefills = evictions = regret = peak = 0
+    out_steps = []
+    for t, (j, lo, hi, an) in enumerate(steps):
+        need = [a for a in an if a not in resident]
+        need_b = sum(int(anchor_slab[a]) for a in need)
+        room_evict = []
+        while sum(resident.values()) + need_b > pool_bytes:
+            cand = [a for a in resident if a not in an]
+            a = max(cand, key=lambda x: (next_use(x, t), int(anchor_slab[x]), -x))
+            del resident[a]
+            evictions += 1
+            room_evict.append(a)
+        for a in need:
+            if a in ever:
+                regret += int(anchor_len[a])
+            ever.add(a)
+            resident[a] = int(anchor_slab[a])
+            prefills += 1
+        peak = max(peak, sum(resident.values()))
+        after = sorted(a for a in an if next_use(a, t) == INF)
+        for a in after:
+            del resident[a]
+            evictions += 1
+        out_steps.append(dict(join=j, lo=lo, hi=hi, prefill=need, evict_before=room_evict, evict_after=after))
+    return dict(plans=plans, steps=out_steps, prefills=prefills, evictions=evictions,
+                regret_tokens=regret, peak=peak)
+
+
+def multijoin_naive_regret(anchor_len, joins):
+    """Regret of planning each join alone (every anchor evicted at its last use
+    inside its join): an anchor used by k joins is prefilled k times."""
+    k = {}
+    for pa, _ in joins:
+        for a in set(int(x) for x in pa if x >= 0):
+            k[a] = k.get(a, 0) + 1
+    return sum(int(anchor_len[a]) * (c - 1) for a, c in k.items())
