@@ -142,6 +142,38 @@ quail_status quail_plan_build(const quail_model_config* cfg, size_t pool_bytes,
                               int32_t* pair_order, int32_t* step_bounds, int32_t* n_steps,
                               size_t* peak_bytes);
 
+/* Plan for several joins over one anchor table, run one after another (a
+ * later join may depend on an earlier one's results): [pt] "Como funciona",
+ * query-aware KV cache bullet -- with the whole plan known, an anchor's KV is
+ * kept for its next use, in whichever join, and evicted when nothing will
+ * use it again. Each join is ordered and cut into steps as by
+ * quail_plan_build; the steps of all joins form one sequence; an anchor is
+ * prefilled before the first step that needs it while not resident, and
+ * evicted after its last step in the whole sequence; when a step's new
+ * anchors do not fit beside the kept ones, kept anchors are evicted farthest
+ * next use first (never used again first; ties: larger slab, lower index).
+ * join_offsets: host [n_joins+1], join j owns pairs [join_offsets[j],
+ * join_offsets[j+1]) of pair_anchor / pair_len (host; anchor index or -1,
+ * suffix tokens).
+ * Outputs, host, caller-allocated for P = join_offsets[n_joins] pairs:
+ *   pair_order [P]: per join, its pairs' indices within the join in plan
+ *     order, joins back to back;
+ *   step_info [3*P]: per step (join, lo, hi), positions lo..hi-1 of that
+ *     join's plan order; n_steps: the number of steps (<= P);
+ *   event_off [3*P+1], event_anchor [2*P]: per step t, three anchor lists:
+ *     prefilled before the step event_anchor[event_off[3t] .. event_off[3t+1]),
+ *     evicted to make room before it [event_off[3t+1] .. event_off[3t+2]),
+ *     evicted after it [event_off[3t+2] .. event_off[3t+3]);
+ *   totals [4]: prefills, evictions, regret tokens, peak resident bytes.
+ * E_INVAL / E_NOMEM as quail_plan_build. Touches no GPU. */
+quail_status quail_multiplan_build(const quail_model_config* cfg, size_t pool_bytes,
+                                   int32_t max_batch_tokens, int32_t n_anchors,
+                                   const int32_t* anchor_len, int32_t n_joins,
+                                   const int32_t* join_offsets, const int32_t* pair_anchor,
+                                   const int32_t* pair_len, int32_t* pair_order, int32_t* step_info,
+                                   int32_t* n_steps, int32_t* event_off, int32_t* event_anchor,
+                                   int64_t* totals);
+
 /* ---- context -------------------------------------------------------------- */
 /* Borrows the weights (they must outlive the context), the KV pool (dev,
  * pool_bytes, 256-B aligned) and the workspace (dev, at least
@@ -227,6 +259,23 @@ quail_status quail_join_run(quail_ctx* ctx, int32_t n_anchors, const int32_t* a_
                             const int32_t* pair_anchor, const int32_t* s_tokens,
                             const int32_t* s_offsets, uint8_t true_mask, float* logits,
                             uint8_t* token, uint8_t* decision, quail_stream stream);
+
+/* Runs several joins over one anchor table with the plan of
+ * quail_multiplan_build (pool budget: the largest free block of the pool
+ * now): per step, prefills its listed anchors, runs its pairs and applies
+ * the head. Each prefill declares the pairs the anchor serves until its next
+ * prefill, so an anchor the plan evicts early is freed right after its last
+ * use before the gap (same prefills and regret, lower peak). Pair indices
+ * and outputs are global over the joins (join_offsets as above): a_tokens
+ * dev + a_offsets host [n_anchors+1]; pair_anchor host [P]; s_tokens dev +
+ * s_offsets host [P+1]; logits f32 [P, 8] (nullable), token u8 (nullable),
+ * decision u8 [P], all dev. */
+quail_status quail_multijoin_run(quail_ctx* ctx, int32_t n_anchors, const int32_t* a_tokens,
+                                 const int32_t* a_offsets, int32_t n_joins,
+                                 const int32_t* join_offsets, const int32_t* pair_anchor,
+                                 const int32_t* s_tokens, const int32_t* s_offsets,
+                                 uint8_t true_mask, float* logits, uint8_t* token,
+                                 uint8_t* decision, quail_stream stream);
 
 /* Residency counters: bytes resident now and at peak, anchors prefilled,
  * anchors evicted, regret tokens (anchor tokens prefilled again after an

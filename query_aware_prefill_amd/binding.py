@@ -61,6 +61,8 @@ _SIGS = {
     "quail_workspace_bytes": ([C.POINTER(ModelConfig), C.c_int32, _szp], C.c_int32),
     "quail_plan_build": ([C.POINTER(ModelConfig), C.c_size_t, C.c_int32, C.c_int32, _i32p, C.c_int32,
                           _i32p, _i32p, _i32p, _i32p, _i32p, _szp], C.c_int32),
+    "quail_multiplan_build": ([C.POINTER(ModelConfig), C.c_size_t, C.c_int32, C.c_int32, _i32p, C.c_int32,
+                               _i32p, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p, _i64p], C.c_int32),
     "quail_ctx_create": ([C.POINTER(ModelConfig), C.POINTER(Weights), _vp, C.c_size_t, _vp, C.c_size_t,
                           C.c_int32, C.POINTER(_vp)], C.c_int32),
     "quail_ctx_destroy": ([_vp], C.c_int32),
@@ -73,6 +75,8 @@ _SIGS = {
     "quail_head8_f32": ([C.c_int32, C.c_int32, _vp, _vp, C.c_uint8, _vp, _vp, _vp, _vp], C.c_int32),
     "quail_join_run": ([_vp, C.c_int32, _vp, _i32p, C.c_int32, _i32p, _vp, _i32p, C.c_uint8, _vp, _vp,
                         _vp, _vp], C.c_int32),
+    "quail_multijoin_run": ([_vp, C.c_int32, _vp, _i32p, C.c_int32, _i32p, _i32p, _vp, _i32p, C.c_uint8,
+                             _vp, _vp, _vp, _vp], C.c_int32),
     "quail_pool_stats": ([_vp, _szp, _szp, _i64p, _i64p, _i64p], C.c_int32),
     "quail_cascade_workspace_bytes": ([C.c_int32, _i32p, C.c_int32, _i32p, _szp], C.c_int32),
     "quail_cascade_attn": ([C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_float, C.c_int32, _vp, _vp,
@@ -168,6 +172,33 @@ def quail_plan_build(cfg: ModelConfig, pool_bytes: int, max_batch_tokens: int, a
     return order, bounds[: nsteps.value + 1].copy(), peak.value
 
 
+def quail_multiplan_build(cfg: ModelConfig, pool_bytes: int, max_batch_tokens: int, anchor_len,
+                          join_offsets, pair_anchor, pair_len) -> dict:
+    """Plan of several joins over one anchor table (see include/quail.h).
+    Returns pair_order, steps [(join, lo, hi, prefill, evict_before,
+    evict_after)] and the totals."""
+    al, alp = _i32(anchor_len)
+    jo, jop = _i32(join_offsets)
+    pa, pap = _i32(pair_anchor)
+    pl, plp = _i32(pair_len)
+    P = int(jo[-1]) if len(jo) else 0
+    order, op = _i32(np.zeros(max(P, 1), np.int32))
+    info, ip = _i32(np.zeros(3 * max(P, 1), np.int32))
+    eoff, eop = _i32(np.zeros(3 * P + 1, np.int32))
+    ean, eap = _i32(np.zeros(2 * max(P, 1), np.int32))
+    tot = np.zeros(4, np.int64)
+    nsteps = C.c_int32()
+    _check(load().quail_multiplan_build(C.byref(cfg), pool_bytes, max_batch_tokens, len(al), alp, len(jo) - 1,
+                                        jop, pap, plp, op, ip, C.byref(nsteps), eop, eap,
+                                        tot.ctypes.data_as(_i64p)))
+    steps = []
+    for t in range(nsteps.value):
+        lists = [ean[eoff[3 * t + q]:eoff[3 * t + q + 1]].tolist() for q in range(3)]
+        steps.append((int(info[3 * t]), int(info[3 * t + 1]), int(info[3 * t + 2]), *lists))
+    return dict(pair_order=order[:P].copy(), steps=steps, prefills=int(tot[0]), evictions=int(tot[1]),
+                regret_tokens=int(tot[2]), peak=int(tot[3]))
+
+
 class Context:
     """Owns a quail_ctx; device buffers (weights, pool, workspace) are torch
     tensors held by the caller and borrowed here."""
@@ -244,6 +275,17 @@ def quail_join_run(ctx: Context, a_tokens, a_offsets, pair_anchor, s_tokens, s_o
     _check(load().quail_join_run(ctx.handle, len(ao) - 1, dptr(a_tokens), aop, len(pa), pap,
                                  dptr(s_tokens), sop, true_mask, dptr(logits), dptr(token),
                                  dptr(decision), stream_handle(stream)))
+
+
+def quail_multijoin_run(ctx: Context, a_tokens, a_offsets, join_offsets, pair_anchor, s_tokens, s_offsets,
+                        true_mask, logits, token, decision, stream=None):
+    ao, aop = _i32(a_offsets)
+    jo, jop = _i32(join_offsets)
+    pa, pap = _i32(pair_anchor)
+    so, sop = _i32(s_offsets)
+    _check(load().quail_multijoin_run(ctx.handle, len(ao) - 1, dptr(a_tokens), aop, len(jo) - 1, jop, pap,
+                                      dptr(s_tokens), sop, true_mask, dptr(logits), dptr(token),
+                                      dptr(decision), stream_handle(stream)))
 
 
 def quail_pool_stats(ctx: Context) -> dict:

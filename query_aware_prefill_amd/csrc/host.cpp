@@ -265,6 +265,110 @@ quail_status build_plan(const std::vector<size_t>& slab, int32_t n_pairs, const 
   return QUAIL_OK;
 }
 
+// ---------------------------------------------------------------------------
+// plan-wide residency over several joins that share one anchor table
+// ([pt] query-aware KV cache bullet: with the whole plan known, KV is kept
+// for its next use and evicted when nothing will need it). Each join keeps
+// its own single-join plan (it may depend on an earlier join's results, so
+// pairs of different joins are not merged); the steps of all joins form one
+// sequence, an anchor's last use is its last step in that sequence, and when
+// a step's new anchors do not fit beside the kept ones, kept anchors are
+// evicted farthest next use first (never again first; ties: larger slab,
+// then lower index).
+// ---------------------------------------------------------------------------
+struct MultiStep {
+  int32_t join = 0, lo = 0, hi = 0;           // positions in that join's plan order
+  std::vector<int32_t> prefill, evict_before, evict_after;
+};
+struct MultiPlan {
+  std::vector<Plan> plans;
+  std::vector<MultiStep> steps;
+  int64_t prefills = 0, evictions = 0, regret = 0;
+  size_t peak = 0;
+};
+
+quail_status build_multiplan(const std::vector<size_t>& slab, const std::vector<int32_t>& alen,
+                             int32_t n_joins, const int32_t* join_off, const int32_t* pair_anchor,
+                             const int32_t* pair_len, size_t pool_bytes, int32_t max_batch_tokens,
+                             MultiPlan& out) {
+  const int32_t na = (int32_t)slab.size();
+  out = MultiPlan{};
+  out.plans.resize(n_joins);
+  std::vector<std::vector<int32_t>> step_anchors;   // per global step, first-use order
+  for (int32_t j = 0; j < n_joins; ++j) {
+    const int32_t p0 = join_off[j], np = join_off[j + 1] - join_off[j];
+    if (quail_status st = build_plan(slab, np, pair_anchor + p0, pair_len + p0, pool_bytes,
+                                     max_batch_tokens, out.plans[j]))
+      return st;
+    const Plan& pl = out.plans[j];
+    for (size_t t = 0; t + 1 < pl.bounds.size(); ++t) {
+      MultiStep ms;
+      ms.join = j;
+      ms.lo = pl.bounds[t];
+      ms.hi = pl.bounds[t + 1];
+      std::vector<int32_t> an;
+      for (int32_t k = ms.lo; k < ms.hi; ++k) {
+        const int32_t a = pair_anchor[p0 + pl.order[k]];
+        if (a >= 0 && std::find(an.begin(), an.end(), a) == an.end()) an.push_back(a);
+      }
+      out.steps.push_back(std::move(ms));
+      step_anchors.push_back(std::move(an));
+    }
+  }
+  const int32_t T = (int32_t)out.steps.size();
+  std::vector<std::vector<int32_t>> uses_at(na);
+  for (int32_t t = 0; t < T; ++t)
+    for (int32_t a : step_anchors[t]) uses_at[a].push_back(t);
+  auto next_use = [&](int32_t a, int32_t t) -> int32_t {
+    auto it = std::upper_bound(uses_at[a].begin(), uses_at[a].end(), t);
+    return it == uses_at[a].end() ? T : *it;
+  };
+  std::vector<char> resident(na, 0), ever(na, 0);
+  size_t bytes = 0;
+  for (int32_t t = 0; t < T; ++t) {
+    MultiStep& ms = out.steps[t];
+    const std::vector<int32_t>& an = step_anchors[t];
+    size_t need_b = 0;
+    for (int32_t a : an)
+      if (!resident[a]) need_b += slab[a];
+    while (bytes + need_b > pool_bytes) {
+      int32_t best = -1;
+      for (int32_t a = 0; a < na; ++a) {
+        if (!resident[a] || std::find(an.begin(), an.end(), a) != an.end()) continue;
+        if (best < 0) { best = a; continue; }
+        const int32_t nu = next_use(a, t), nb = next_use(best, t);
+        if (nu > nb || (nu == nb && slab[a] > slab[best])) best = a;   // lower index wins the rest
+      }
+      if (best < 0) return fail(QUAIL_E_NOMEM, "step %d: its anchors do not fit the pool", t);
+      resident[best] = 0;
+      bytes -= slab[best];
+      out.evictions++;
+      ms.evict_before.push_back(best);
+    }
+    for (int32_t a : an) {
+      if (resident[a]) continue;
+      if (ever[a]) out.regret += alen[a];
+      ever[a] = 1;
+      resident[a] = 1;
+      bytes += slab[a];
+      out.prefills++;
+      ms.prefill.push_back(a);
+    }
+    out.peak = std::max(out.peak, bytes);
+    std::vector<int32_t> after;
+    for (int32_t a : an)
+      if (next_use(a, t) == T) after.push_back(a);
+    std::sort(after.begin(), after.end());
+    for (int32_t a : after) {
+      resident[a] = 0;
+      bytes -= slab[a];
+      out.evictions++;
+    }
+    ms.evict_after = std::move(after);
+  }
+  return QUAIL_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -674,6 +778,56 @@ quail_status quail_plan_build(const quail_model_config* cfg, size_t pool_bytes, 
   return QUAIL_OK;
 }
 
+quail_status quail_multiplan_build(const quail_model_config* cfg, size_t pool_bytes, int32_t max_batch_tokens,
+                                   int32_t n_anchors, const int32_t* anchor_len, int32_t n_joins,
+                                   const int32_t* join_offsets, const int32_t* pair_anchor,
+                                   const int32_t* pair_len, int32_t* pair_order, int32_t* step_info,
+                                   int32_t* n_steps, int32_t* event_off, int32_t* event_anchor,
+                                   int64_t* totals) {
+  if (quail_status st = check_cfg(cfg)) return st;
+  if (n_anchors < 0 || n_joins < 0) return fail(QUAIL_E_INVAL, "negative count");
+  if (max_batch_tokens <= 0) return fail(QUAIL_E_INVAL, "max_batch_tokens must be positive");
+  if (!join_offsets || (n_anchors > 0 && !anchor_len))
+    return fail(QUAIL_E_INVAL, "join_offsets and anchor_len are required");
+  if (join_offsets[0] != 0) return fail(QUAIL_E_INVAL, "join_offsets[0] must be 0");
+  for (int32_t j = 0; j < n_joins; ++j)
+    if (join_offsets[j + 1] < join_offsets[j]) return fail(QUAIL_E_INVAL, "join_offsets must not decrease");
+  const int32_t n_pairs = join_offsets[n_joins];
+  if (n_pairs > 0 && (!pair_anchor || !pair_len)) return fail(QUAIL_E_INVAL, "pair arrays are required");
+  if (!pair_order || !step_info || !n_steps || !event_off || !event_anchor || !totals)
+    return fail(QUAIL_E_INVAL, "output arrays are required");
+  std::vector<size_t> slab(n_anchors);
+  std::vector<int32_t> alen(anchor_len, anchor_len + n_anchors);
+  for (int32_t a = 0; a < n_anchors; ++a) {
+    if (anchor_len[a] <= 0) return fail(QUAIL_E_INVAL, "anchor %d: length must be positive", a);
+    slab[a] = slab_bytes(*cfg, anchor_len[a]);
+  }
+  MultiPlan mp;
+  if (quail_status st = build_multiplan(slab, alen, n_joins, join_offsets, pair_anchor, pair_len, pool_bytes,
+                                        max_batch_tokens, mp))
+    return st;
+  for (int32_t j = 0; j < n_joins; ++j)
+    std::copy(mp.plans[j].order.begin(), mp.plans[j].order.end(), pair_order + join_offsets[j]);
+  int32_t e = 0;
+  event_off[0] = 0;
+  for (size_t t = 0; t < mp.steps.size(); ++t) {
+    const MultiStep& ms = mp.steps[t];
+    step_info[3 * t] = ms.join;
+    step_info[3 * t + 1] = ms.lo;
+    step_info[3 * t + 2] = ms.hi;
+    for (const std::vector<int32_t>* lst : {&ms.prefill, &ms.evict_before, &ms.evict_after}) {
+      for (int32_t a : *lst) event_anchor[e++] = a;
+      event_off[3 * t + 1 + (lst == &ms.prefill ? 0 : (lst == &ms.evict_before ? 1 : 2))] = e;
+    }
+  }
+  *n_steps = (int32_t)mp.steps.size();
+  totals[0] = mp.prefills;
+  totals[1] = mp.evictions;
+  totals[2] = mp.regret;
+  totals[3] = (int64_t)mp.peak;
+  return QUAIL_OK;
+}
+
 quail_status quail_ctx_create(const quail_model_config* cfg, const quail_weights* w, void* kv_pool,
                               size_t pool_bytes, void* workspace, size_t ws_bytes,
                               int32_t max_batch_tokens, quail_ctx** out) {
@@ -940,6 +1094,32 @@ quail_status quail_head8_f32(int32_t n, int32_t hidden, const float* x, const fl
   return QUAIL_OK;
 }
 
+// One step of a join: its pairs through the decoder stack (join_core), then the
+// head on each pair's last row, written to the caller's pair slots outmap[k]
+// (the map goes to the metadata region; stream order protects earlier
+// readers).
+static quail_status run_step_with_head(quail_ctx* c, int32_t np, const quail_anchor* ha,
+                                       const int32_t* s_tokens, const int32_t* starts, const int32_t* lens,
+                                       const int32_t* outmap, uint8_t true_mask, float* logits, uint8_t* token,
+                                       uint8_t* decision, hipStream_t s) {
+  uint16_t* hl = ws_ptr<uint16_t>(c, c->L.hlast);
+  std::vector<int32_t> dst(np);
+  std::iota(dst.begin(), dst.end(), 0);
+  if (quail_status r = join_core(c, np, ha, s_tokens, starts, lens, hl, dst.data(), nullptr, s)) return r;
+  Blob& bl = c->blob;
+  bl.clear();
+  bl.add(std::vector<int32_t>(outmap, outmap + np));
+  uint8_t* md = c->ws + c->L.meta;
+  HIP_TRY(stager().copy(md, bl.data(), bl.size(), s));
+  Head8Params p{};
+  p.h = hl; p.ldh = c->cfg.hidden; p.gamma = c->w.final_norm; p.w8 = c->w.head8;
+  p.out_map = reinterpret_cast<const int32_t*>(md);
+  p.logits = logits; p.token = token; p.decision = decision;
+  p.rows = np; p.H = c->cfg.hidden; p.eps = c->cfg.rms_eps; p.true_mask = true_mask;
+  HIP_TRY(launch_head8(p, s));
+  return QUAIL_OK;
+}
+
 quail_status quail_join_run(quail_ctx* c, int32_t n_anchors, const int32_t* a_tokens,
                             const int32_t* a_offsets, int32_t n_pairs, const int32_t* pair_anchor,
                             const int32_t* s_tokens, const int32_t* s_offsets, uint8_t true_mask,
@@ -983,7 +1163,6 @@ quail_status quail_join_run(quail_ctx* c, int32_t n_anchors, const int32_t* a_to
   // regret counts re-prefills within one plan only
   const int64_t id_base = (++c->run_serial) << 32;
   hipStream_t s = as_stream(stream);
-  uint16_t* hl = ws_ptr<uint16_t>(c, c->L.hlast);
   for (size_t st = 0; st + 1 < plan.bounds.size(); ++st) {
     const int32_t b0 = plan.bounds[st], b1 = plan.bounds[st + 1];
     // Prefill the anchors this step needs; batch later steps' anchors with
@@ -1026,31 +1205,108 @@ quail_status quail_join_run(quail_ctx* c, int32_t n_anchors, const int32_t* a_to
     }
     const int32_t np = b1 - b0;
     std::vector<quail_anchor> ha(np);
-    std::vector<int32_t> starts(np), lens(np), dst(np), outmap(np);
+    std::vector<int32_t> starts(np), lens(np), outmap(np);
     for (int32_t k = 0; k < np; ++k) {
       const int32_t pi = plan.order[b0 + k];
       ha[k] = pair_anchor[pi] >= 0 ? handle[pair_anchor[pi]] : QUAIL_NO_ANCHOR;
       starts[k] = s_offsets[pi];
       lens[k] = plen[pi];
-      dst[k] = k;
       outmap[k] = pi;
     }
-    if (quail_status r = join_core(c, np, ha.data(), s_tokens, starts.data(), lens.data(), hl, dst.data(),
-                                   nullptr, s))
+    if (quail_status r = run_step_with_head(c, np, ha.data(), s_tokens, starts.data(), lens.data(),
+                                            outmap.data(), true_mask, logits, token, decision, s))
       return r;
-    // head on this step's last rows, written to the caller's pair slots (the
-    // map goes to the metadata region; stream order protects earlier readers)
-    Blob& bl = c->blob;
-    bl.clear();
-    bl.add(outmap);
-    uint8_t* md = c->ws + c->L.meta;
-    HIP_TRY(stager().copy(md, bl.data(), bl.size(), s));
-    Head8Params p{};
-    p.h = hl; p.ldh = c->cfg.hidden; p.gamma = c->w.final_norm; p.w8 = c->w.head8;
-    p.out_map = reinterpret_cast<const int32_t*>(md);
-    p.logits = logits; p.token = token; p.decision = decision;
-    p.rows = np; p.H = c->cfg.hidden; p.eps = c->cfg.rms_eps; p.true_mask = true_mask;
-    HIP_TRY(launch_head8(p, s));
+  }
+  return QUAIL_OK;
+}
+
+quail_status quail_multijoin_run(quail_ctx* c, int32_t n_anchors, const int32_t* a_tokens,
+                                 const int32_t* a_offsets, int32_t n_joins, const int32_t* join_offsets,
+                                 const int32_t* pair_anchor, const int32_t* s_tokens, const int32_t* s_offsets,
+                                 uint8_t true_mask, float* logits, uint8_t* token, uint8_t* decision,
+                                 quail_stream stream) {
+  if (!c) return fail(QUAIL_E_INVAL, "ctx is NULL");
+  if (n_joins < 0 || !join_offsets) return fail(QUAIL_E_INVAL, "join_offsets is required");
+  if (join_offsets[0] != 0) return fail(QUAIL_E_INVAL, "join_offsets[0] must be 0");
+  for (int32_t j = 0; j < n_joins; ++j)
+    if (join_offsets[j + 1] < join_offsets[j]) return fail(QUAIL_E_INVAL, "join_offsets must not decrease");
+  const int32_t n_pairs = join_offsets[n_joins];
+  if (n_pairs == 0) return QUAIL_OK;
+  if (!decision) return fail(QUAIL_E_INVAL, "decision is required");
+  const int32_t amax = std::min(c->cfg.max_anchor_len, c->T);
+  if (quail_status st = check_offsets(n_anchors, a_offsets, 1, amax, "anchor")) return st;
+  if (quail_status st = check_offsets(n_pairs, s_offsets, 1, std::min(c->cfg.max_suffix_len, c->T), "pair"))
+    return st;
+  if (!pair_anchor) return fail(QUAIL_E_INVAL, "pair_anchor is NULL");
+  std::vector<size_t> slab(n_anchors);
+  std::vector<int32_t> alen(n_anchors), plen(n_pairs);
+  for (int32_t a = 0; a < n_anchors; ++a) {
+    alen[a] = a_offsets[a + 1] - a_offsets[a];
+    slab[a] = slab_bytes(c->cfg, alen[a]);
+  }
+  for (int32_t i = 0; i < n_pairs; ++i) plen[i] = s_offsets[i + 1] - s_offsets[i];
+  // the plan is built against the largest free block of the pool now
+  size_t free_bytes = 0;
+  for (auto& f : c->free_list) free_bytes = std::max(free_bytes, f.second);
+  MultiPlan mp;
+  if (quail_status st = build_multiplan(slab, alen, n_joins, join_offsets, pair_anchor, plen.data(), free_bytes,
+                                        c->T, mp))
+    return st;
+  // Each prefill declares the pairs the anchor serves until its next prefill
+  // (or the end), so the residency manager frees it right after the last of
+  // them: an anchor the plan evicts early is freed at its last use before
+  // the gap, which changes no prefill or regret and only lowers the peak.
+  const int32_t T = (int32_t)mp.steps.size();
+  std::vector<std::vector<int32_t>> pairs_in(T);   // per step: global pair indices in plan order
+  for (int32_t t = 0; t < T; ++t) {
+    const MultiStep& ms = mp.steps[t];
+    const int32_t p0 = join_offsets[ms.join];
+    for (int32_t k = ms.lo; k < ms.hi; ++k) pairs_in[t].push_back(p0 + mp.plans[ms.join].order[k]);
+  }
+  std::vector<std::vector<int32_t>> prefill_at(n_anchors);
+  for (int32_t t = 0; t < T; ++t)
+    for (int32_t a : mp.steps[t].prefill) prefill_at[a].push_back(t);
+  auto uses_until = [&](int32_t a, int32_t t0) -> int32_t {
+    auto it = std::upper_bound(prefill_at[a].begin(), prefill_at[a].end(), t0);
+    const int32_t t1 = it == prefill_at[a].end() ? T : *it;
+    int32_t u = 0;
+    for (int32_t t = t0; t < t1; ++t)
+      for (int32_t pi : pairs_in[t]) u += pair_anchor[pi] == a;
+    return u;
+  };
+  std::vector<quail_anchor> handle(n_anchors, QUAIL_NO_ANCHOR);
+  const int64_t id_base = (++c->run_serial) << 32;
+  hipStream_t s = as_stream(stream);
+  for (int32_t t = 0; t < T; ++t) {
+    const MultiStep& ms = mp.steps[t];
+    if (!ms.prefill.empty()) {
+      const int32_t nb = (int32_t)ms.prefill.size();
+      std::vector<int32_t> st_(nb), ln(nb), nu(nb);
+      std::vector<int64_t> ids(nb);
+      for (int32_t f = 0; f < nb; ++f) {
+        const int32_t a = ms.prefill[f];
+        st_[f] = a_offsets[a];
+        ln[f] = alen[a];
+        nu[f] = uses_until(a, t);
+        ids[f] = id_base | a;
+      }
+      std::vector<quail_anchor> hnd(nb);
+      if (quail_status r = anchor_core(c, nb, a_tokens, st_.data(), ln.data(), nu.data(), ids.data(), hnd.data(), s))
+        return r;
+      for (int32_t f = 0; f < nb; ++f) handle[ms.prefill[f]] = hnd[f];
+    }
+    const int32_t np = (int32_t)pairs_in[t].size();
+    std::vector<quail_anchor> ha(np);
+    std::vector<int32_t> starts(np), lens(np);
+    for (int32_t k = 0; k < np; ++k) {
+      const int32_t pi = pairs_in[t][k];
+      ha[k] = pair_anchor[pi] >= 0 ? handle[pair_anchor[pi]] : QUAIL_NO_ANCHOR;
+      starts[k] = s_offsets[pi];
+      lens[k] = plen[pi];
+    }
+    if (quail_status r = run_step_with_head(c, np, ha.data(), s_tokens, starts.data(), lens.data(),
+                                            pairs_in[t].data(), true_mask, logits, token, decision, s))
+      return r;
   }
   return QUAIL_OK;
 }

@@ -74,6 +74,53 @@ def test_plan_build_matches_oracle(seed):
     assert peak == ref["peak"]
 
 
+@pytest.mark.parametrize("seed", range(40))
+def test_multiplan_build_matches_oracle(seed):
+    """Several joins over one anchor table: the library's plan (orders, steps,
+    prefill / eviction events, totals) equals the oracle's, bit for bit."""
+    r = np.random.default_rng(300 + seed)
+    cfg = _cfg(layers=2, n_kv_heads=2, n_q_heads=4, hidden=256, intermediate=384)
+    na = int(r.integers(1, 8))
+    a_len = r.integers(1, 300, na).astype(np.int32)
+    if seed % 3 == 0:
+        a_len[:] = 128                       # equal slabs: eviction order decided by next use alone
+    slab = np.array([OP.slab_bytes(x, 2, 2, 128, 2) for x in a_len])
+    joins = []
+    for _ in range(int(r.integers(1, 5))):
+        n = int(r.integers(0, 25))
+        joins.append((r.integers(-1, na, n).astype(np.int32), r.integers(1, 64, n).astype(np.int32)))
+    pool = int(slab.max() * r.integers(1, 4))
+    mbt = int(r.integers(64, 300))
+    ref = OP.multijoin_reference(slab, a_len, joins, pool, mbt)
+    jo = np.cumsum([0] + [len(pa) for pa, _ in joins]).astype(np.int32)
+    pa_all = np.concatenate([pa for pa, _ in joins]) if jo[-1] else np.zeros(0, np.int32)
+    pl_all = np.concatenate([pl for _, pl in joins]) if jo[-1] else np.zeros(0, np.int32)
+    got = B.quail_multiplan_build(cfg, pool, mbt, a_len, jo, pa_all, pl_all)
+    for j, p in enumerate(ref["plans"]):
+        assert np.array_equal(got["pair_order"][jo[j]:jo[j + 1]], p["order"])
+    assert len(got["steps"]) == len(ref["steps"])
+    for g, e in zip(got["steps"], ref["steps"]):
+        assert g == (e["join"], e["lo"], e["hi"], e["prefill"], e["evict_before"], e["evict_after"])
+    assert (got["prefills"], got["evictions"], got["regret_tokens"], got["peak"]) == \
+        (ref["prefills"], ref["evictions"], ref["regret_tokens"], ref["peak"])
+
+
+def test_multiplan_build_errors():
+    cfg = _cfg(layers=1)
+    slab = B.quail_anchor_bytes(cfg, 100)
+    with pytest.raises(B.QuailError) as e:      # an anchor larger than the pool
+        B.quail_multiplan_build(cfg, slab - 1, 64, [100], [0, 1], [0], [5])
+    assert e.value.status == B.E_NOMEM
+    with pytest.raises(B.QuailError) as e:      # anchor index out of range in the second join
+        B.quail_multiplan_build(cfg, slab, 64, [100], [0, 1, 2], [0, 1], [5, 5])
+    assert e.value.status == B.E_INVAL
+    with pytest.raises(B.QuailError) as e:      # decreasing join offsets
+        B.quail_multiplan_build(cfg, slab, 64, [100], [0, 2, 1], [0, 0], [5, 5])
+    assert e.value.status == B.E_INVAL
+    got = B.quail_multiplan_build(cfg, slab, 64, [100], [0, 0, 0], [], [])   # two empty joins
+    assert got["steps"] == [] and got["prefills"] == 0
+
+
 def test_plan_build_errors():
     cfg = _cfg(layers=1)
     slab = B.quail_anchor_bytes(cfg, 100)
@@ -182,6 +229,37 @@ def test_join_rejects_bad_suffix_lengths():
         off, offp = _i32(offs)
         st = fc.lib.quail_join_prefill(fc.h, 2, hap, 0x7F0000000000, offp, 0x7F0000000000, None, None)
         assert st == B.E_INVAL, offs
+    fc.close()
+
+
+def test_multijoin_run_rejects_bad_arguments_before_any_gpu_work():
+    fc = _FakeCtx(pool_bytes=1 << 26)
+    fake = 0x7F0000000000
+    ao, aop = _i32([0, 10])
+    so, sop = _i32([0, 4, 8])
+    cases = [
+        ([0, 2, 1], [0, 0]),          # decreasing join offsets
+        ([1, 2], [0, 0]),             # first offset not 0
+        ([0, 1, 2], [0, 1]),          # anchor index out of range in the second join
+        ([0, 1, 2], [0, -2]),         # anchor index below -1
+    ]
+    for jo_, pa_ in cases:
+        jo, jop = _i32(jo_)
+        pa, pap = _i32(pa_)
+        st = fc.lib.quail_multijoin_run(fc.h, 1, fake, aop, len(jo_) - 1, jop, pap, fake, sop, 0x0F,
+                                        None, None, fake, None)
+        assert st == B.E_INVAL, (jo_, pa_)
+    jo, jop = _i32([0, 2])
+    pa, pap = _i32([0, 0])
+    bad_so, bad_sop = _i32([0, 4, 4 + 129])        # a suffix longer than max_suffix_len
+    st = fc.lib.quail_multijoin_run(fc.h, 1, fake, aop, 1, jop, pap, fake, bad_sop, 0x0F, None, None, fake,
+                                    None)
+    assert st == B.E_INVAL
+    # nothing was prefilled
+    r, p = C.c_size_t(), C.c_size_t()
+    pf, ev, rg = C.c_int64(), C.c_int64(), C.c_int64()
+    fc.lib.quail_pool_stats(fc.h, C.byref(r), C.byref(p), C.byref(pf), C.byref(ev), C.byref(rg))
+    assert r.value == 0 and pf.value == 0
     fc.close()
 
 

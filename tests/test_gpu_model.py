@@ -226,3 +226,83 @@ def test_qwen3_shaped_layer(B):
         err = rel_inf(ha[case["s_off"][i]:case["s_off"][i + 1]], h[len(at):])
         say("  pair", i, "rel", err)
         assert err <= 2e-2
+
+
+def test_multijoin_run_keeps_anchors_across_joins(B):
+    """Three joins over one anchor table run one after another: with a pool
+    for every anchor, each anchor is prefilled once for all joins (regret 0,
+    where planning the joins one by one prefills an anchor once per join);
+    with a pool for two anchors, the prefills and regret are the plan's. Every
+    pair's logits equal those of running its join alone (same kernels on the
+    same rows), and the decisions agree with the oracle on a sample."""
+    import torch
+    shape = W.tiny_shape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                         intermediate=384, vocab=512)
+    r = np.random.default_rng(21)
+    a_len = [64] * 5                        # equal slabs: the pool never fragments
+    joins = [[(0, 9), (2, 14), (0, 3), (3, 30)],
+             [(2, 5), (4, 17), (1, 8), (-1, 6)],
+             [(0, 11), (3, 2), (2, 25), (4, 4), (1, 19)]]
+    pairs = [p for j in joins for p in j]
+    jo = np.cumsum([0] + [len(j) for j in joins]).astype(np.int32)
+    n = len(pairs)
+    slab = None
+    results = {}
+    for label, n_slabs in (("ample", 5), ("tight", 2)):
+        wts, case, dm, ctx, a_tok, s_tok = _setup(shape, 9, a_len, pairs, B, mbt=96)
+        slab = B.quail_anchor_bytes(dm.cfg, 64)
+        if n_slabs != 5:
+            ctx = dm.context(n_slabs * slab, 96)
+        logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+        dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+        say("multijoin_run", label, n, "pairs in", len(joins), "joins")
+        B.quail_multijoin_run(ctx, a_tok, case["a_off"], jo, case["pair_anchor"], s_tok, case["s_off"], 0x0F,
+                              logits, None, dec)
+        torch.cuda.synchronize()
+        st = B.quail_pool_stats(ctx)
+        plan = B.quail_multiplan_build(dm.cfg, n_slabs * slab if n_slabs != 5 else
+                                       sum(B.quail_anchor_bytes(dm.cfg, x) for x in a_len) + 4096, 96,
+                                       a_len, jo, case["pair_anchor"], np.diff(case["s_off"]))
+        assert (st["prefills"], st["evictions"], st["regret_tokens"]) == \
+            (plan["prefills"], plan["evictions"], plan["regret_tokens"]), (label, st, plan)
+        assert st["resident"] == 0 and st["peak"] <= plan["peak"]
+        results[label] = (logits.cpu().numpy(), dec.cpu().numpy(), st)
+    used = {a for a, _ in pairs if a >= 0}
+    assert results["ample"][2]["prefills"] == len(used) and results["ample"][2]["regret_tokens"] == 0
+    assert results["tight"][2]["regret_tokens"] > 0
+    # a tighter pool cuts smaller steps, so batches (and with them the
+    # attention tile shapes) differ: same results within the bf16 contract
+    la, lt = results["ample"][0], results["tight"][0]
+    assert rel_inf(lt, la) <= 2e-2
+    tau = 2e-2 * np.max(np.abs(la))
+    gap = np.sort(la, axis=1)[:, -1] - np.sort(la, axis=1)[:, -2]
+    sure = gap > tau
+    assert np.array_equal(results["ample"][1][sure], results["tight"][1][sure])
+    # each join alone on a fresh context
+    wts, case, dm, ctx, a_tok, s_tok = _setup(shape, 9, a_len, pairs, B, mbt=96)
+    alone = np.zeros((n, 8), np.float32)
+    naive_prefills = 0
+    for j in range(len(joins)):
+        idx = np.arange(jo[j], jo[j + 1])
+        s_off = np.concatenate([[0], np.cumsum(np.diff(case["s_off"])[idx])]).astype(np.int32)
+        toks = np.concatenate([case["s_tok"][case["s_off"][i]:case["s_off"][i + 1]] for i in idx]).astype(np.int32)
+        lg = torch.empty((len(idx), 8), dtype=torch.float32, device="cuda")
+        dj = torch.empty(len(idx), dtype=torch.uint8, device="cuda")
+        from query_aware_prefill_amd.device import to_device
+        B.quail_join_run(ctx, a_tok, case["a_off"], case["pair_anchor"][idx], to_device(toks), s_off, 0x0F,
+                         lg, None, dj)
+        torch.cuda.synchronize()
+        alone[idx] = lg.cpu().numpy()
+        naive_prefills += len({a for a in case["pair_anchor"][idx] if a >= 0})
+    # same pool, so the same steps: the same batches through the same kernels
+    assert np.array_equal(alone, results["ample"][0])
+    assert B.quail_pool_stats(ctx)["prefills"] == naive_prefills > len(used)
+    # oracle on a sample of pairs
+    for i in (0, 5, 7, 12):
+        a = pairs[i][0]
+        at = case["a_tok"][case["a_off"][a]:case["a_off"][a + 1]] if a >= 0 else []
+        stoks = case["s_tok"][case["s_off"][i]:case["s_off"][i + 1]]
+        ref = OM.forward_pair(at, stoks, wts, shape, true_mask=0x0F)
+        assert rel_inf(results["ample"][0][i], ref["logits"]) <= 2e-2
+        if abs(ref["margin"]) > 2e-2 * np.max(np.abs(ref["logits"])):
+            assert results["ample"][1][i] == ref["decision"]
