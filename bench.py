@@ -47,6 +47,14 @@ Secondary measurements (not the headline line; each prints its own JSON):
                      Logical and computed tokens/min; the oracle leg runs the
                      per-pair definition on a few sampled pairs and compares
                      logits and decisions.
+  --workload multiplan36
+                     three joins over the join36 anchor table (64 anchors x
+                     1024 tokens), 8,192 pairs of 64-token suffixes each, on
+                     the 36-layer stack: plan-wide residency across the joins
+                     (quail_multijoin_run: each anchor prefilled once) against
+                     the joins run one by one (quail_join_run each: each anchor
+                     prefilled once per join); times, prefills and whether the
+                     logits are identical.
   --workload layer   one decoder layer of the Qwen3-4B shape, random-init fp8
                      weights: 16 anchors x 1024 tokens, 512 suffixes x 64
                      tokens per anchor, run end to end by quail_join_run
@@ -446,6 +454,70 @@ def bench_layer(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_multiplan(args):
+    """Three joins over one anchor table (64 anchors x 1024 tokens of the join
+    workload; join k takes suffixes k*128 .. k*128+127 of every anchor, 64
+    tokens each), 36-layer stack: plan-wide residency (quail_multijoin_run)
+    against running the joins one by one (quail_join_run each)."""
+    import torch
+    import workloads as W
+    from query_aware_prefill_amd import binding as B
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    B.load()
+    shape = W.QWEN3_4B
+    case = W.c3b_case()
+    a_len, a_off, a_tok = case["a_len"], case["a_off"], case["a_tok"]
+    pa_all, s_off_all, s_tok_all = case["pair_anchor"], case["s_off"], case["s_tok"]
+    rank = np.zeros(len(pa_all), np.int64)
+    seen = {}
+    for i, a in enumerate(pa_all):
+        rank[i] = seen.get(int(a), 0)
+        seen[int(a)] = rank[i] + 1
+    per = 128
+    sel = [np.nonzero((rank >= k * per) & (rank < (k + 1) * per))[0] for k in range(3)]
+    idx = np.concatenate(sel)
+    jo = np.array([0, len(sel[0]), len(sel[0]) + len(sel[1]), len(idx)], np.int32)
+    pair_anchor = pa_all[idx].astype(np.int32)
+    s_len = np.diff(s_off_all)[idx].astype(np.int64)
+    s_off = np.concatenate([[0], np.cumsum(s_len)]).astype(np.int32)
+    s_tok = np.concatenate([s_tok_all[s_off_all[i]:s_off_all[i + 1]] for i in idx]).astype(np.int32)
+    n = len(idx)
+    log(f"multiplan36: 3 joins x {n // 3} pairs over {len(a_len)} anchors; weights on device")
+    wd = W.model_weights_device(shape, 0)
+    dm = DeviceModel(shape, wd, max_anchor_len=int(np.max(a_len)), max_suffix_len=int(np.max(s_len)))
+    T = 65536
+    pool = sum(B.quail_anchor_bytes(dm.cfg, int(x)) for x in a_len) + (1 << 20)
+    a_tok_d, s_tok_d = to_device(a_tok.astype(np.int32)), to_device(s_tok)
+    res = {"metric": "multi-join plan: plan-wide residency vs joins one by one (36-layer stack)",
+           "workload": "3 joins over 64 anchors x 1024 tokens, 8,192 pairs of 64-token suffixes each",
+           "pairs": int(n)}
+    out = {}
+    for mode in ("plan_wide", "one_by_one"):
+        ctx = dm.context(pool, T)
+        logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+        dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        if mode == "plan_wide":
+            B.quail_multijoin_run(ctx, a_tok_d, a_off, jo, pair_anchor, s_tok_d, s_off, 0x0F, logits, None, dec)
+        else:
+            for j in range(3):
+                lo, hi = int(jo[j]), int(jo[j + 1])
+                so = (s_off[lo:hi + 1] - s_off[lo]).astype(np.int32)
+                B.quail_join_run(ctx, a_tok_d, a_off, pair_anchor[lo:hi], s_tok_d[int(s_off[lo]):int(s_off[hi])],
+                                 so, 0x0F, logits[lo:hi], None, dec[lo:hi])
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1000.0
+        st = B.quail_pool_stats(ctx)
+        out[mode] = logits.cpu().numpy()
+        res[mode] = {"ms": ms, "pool": st}
+        log(f"multiplan36 {mode}: {ms / 1000:.2f} s, prefills {st['prefills']}, regret {st['regret_tokens']} tokens")
+        del ctx
+    res["logits_identical"] = bool(np.array_equal(out["plan_wide"], out["one_by_one"]))
+    res["speedup"] = res["one_by_one"]["ms"] / res["plan_wide"]["ms"]
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -454,7 +526,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--workload", choices=["cascade", "gemm", "layer", "copy", "stream", "join36",
-                                           "filter36", "multijoin36"], default="cascade")
+                                           "filter36", "multijoin36", "multiplan36"], default="cascade")
     ap.add_argument("--rows", type=int, default=625, help="multijoin36: rows of the 5,000 used")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -471,6 +543,8 @@ def main():
         return bench_copy(args)
     if args.workload == "stream":
         return bench_stream(args)
+    if args.workload == "multiplan36":
+        return bench_multiplan(args)
     if args.workload in ("join36", "filter36", "multijoin36"):
         return bench_e2e(args)
 
