@@ -102,7 +102,10 @@ __device__ __forceinline__ float wave_max(float v) {
 // Issued through inline asm so that the compiler does not treat every later
 // LDS read as a possible alias of the copy and wait for all copies in flight;
 // callers wait explicitly (s_waitcnt vmcnt) before the barrier that publishes
-// the data.
+// the data. M0 is a register the compiler reserves and does not preserve
+// across asm statements; the kernels that use these copies have no other M0
+// user (no LDS-DMA builtin, no indexed register moves), so nothing of the
+// compiler's lives in M0 across them.
 __device__ __forceinline__ void copy16_to_lds(const void* gptr, const void* lds_base) {
   // the low 32 bits of a generic pointer into LDS are its LDS offset (no null
   // check needed: lds_base always points into a __shared__ array)
