@@ -42,131 +42,224 @@ __device__ __forceinline__ float silu_f(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
 }
 
-// Epilogue of one 32-row block of a wave: lane owns row m and, in column block
-// nb, columns nb*32 + rg*8 + hi*4 + e (e = 0..3) of the wave's 128 columns,
-// which start at n_base (SWIGLU: output column o_base, gate rows o_base + j,
-// up rows inter + o_base + j for j < 64).
-template <int EPI>
-__device__ __forceinline__ void epilogue(const GemmParams& p, const f32x16_t (&acc)[4], int m,
-                                         int n_base, int o_base, int hi) {
-  if (EPI == EPI_STORE || EPI == EPI_RESID) {
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int n = n_base + nb * 32 + rg * 8 + hi * 4;
-        const uint2 sc = *reinterpret_cast<const uint2*>(p.scale + n);
-        float v0 = acc[nb][rg * 4 + 0] * bf16_bits_to_f32(sc.x & 0xFFFF);
-        float v1 = acc[nb][rg * 4 + 1] * bf16_bits_to_f32(sc.x >> 16);
-        float v2 = acc[nb][rg * 4 + 2] * bf16_bits_to_f32(sc.y & 0xFFFF);
-        float v3 = acc[nb][rg * 4 + 3] * bf16_bits_to_f32(sc.y >> 16);
-        uint2* yp = reinterpret_cast<uint2*>(p.Y + (int64_t)m * p.ldy + n);
-        if (EPI == EPI_RESID) {
-          const uint2 h = *yp;
-          v0 += bf16_bits_to_f32(h.x & 0xFFFF);
-          v1 += bf16_bits_to_f32(h.x >> 16);
-          v2 += bf16_bits_to_f32(h.y & 0xFFFF);
-          v3 += bf16_bits_to_f32(h.y >> 16);
-        }
-        *yp = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-      }
-    }
-  } else if (EPI == EPI_SWIGLU) {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int j = nb * 32 + rg * 8 + hi * 4;
-        const uint2 sg = *reinterpret_cast<const uint2*>(p.scale + o_base + j);
-        const uint2 su = *reinterpret_cast<const uint2*>(p.scale + p.inter + o_base + j);
-        float g[4], u[4];
-        g[0] = acc[nb][rg * 4 + 0] * bf16_bits_to_f32(sg.x & 0xFFFF);
-        g[1] = acc[nb][rg * 4 + 1] * bf16_bits_to_f32(sg.x >> 16);
-        g[2] = acc[nb][rg * 4 + 2] * bf16_bits_to_f32(sg.y & 0xFFFF);
-        g[3] = acc[nb][rg * 4 + 3] * bf16_bits_to_f32(sg.y >> 16);
-        u[0] = acc[nb + 2][rg * 4 + 0] * bf16_bits_to_f32(su.x & 0xFFFF);
-        u[1] = acc[nb + 2][rg * 4 + 1] * bf16_bits_to_f32(su.x >> 16);
-        u[2] = acc[nb + 2][rg * 4 + 2] * bf16_bits_to_f32(su.y & 0xFFFF);
-        u[3] = acc[nb + 2][rg * 4 + 3] * bf16_bits_to_f32(su.y >> 16);
-        uint2 w;
-        w.x = pack_bf16x2(silu_f(g[0]) * u[0], silu_f(g[1]) * u[1]);
-        w.y = pack_bf16x2(silu_f(g[2]) * u[2], silu_f(g[3]) * u[3]);
-        *reinterpret_cast<uint2*>(p.Y + (int64_t)m * p.ldy + o_base + j) = w;
-      }
-    }
-  } else {  // EPI_QKV: the wave's 128 columns are one head
+// ----------------------------------------------------------------------------
+// Staged epilogue of one wave tile (MB blocks of 32 tokens x 128 columns).
+// In the MFMA output layout a lane owns one token and, in column block nb,
+// columns nb*32 + rg*8 + hi*4 + e (e = 0..3) of the wave's 128 columns, which
+// start at n_base (SWIGLU: output column o_base, gate rows o_base + j, up rows
+// inter + o_base + j for j < 64). Stored directly, one instruction would write
+// 8-byte pieces of 32 different rows; instead each 32-token block is written
+// to an 8-KB LDS region of the wave (rows XOR-swizzled by 16-byte chunk) and
+// read back so that 8 or 16 lanes cover one row: every global store and
+// residual load then moves whole 16-byte pieces of contiguous rows. The
+// caller hands each wave its own region after a workgroup barrier that ends
+// the use of the pipeline stages; LDS operations of one wave complete in
+// order, so no further barrier is needed.
+//   lds: wave-uniform LDS byte address of the region; m_row0: first token of
+//   the wave tile.
+// ----------------------------------------------------------------------------
+typedef uint32_t lds_u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t lds_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void lds_write_b64(uint32_t addr, uint2 v) {
+  *reinterpret_cast<__attribute__((address_space(3))) lds_u32x2*>(addr) = __builtin_bit_cast(lds_u32x2, v);
+}
+__device__ __forceinline__ void lds_write_b128(uint32_t addr, uint4 v) {
+  *reinterpret_cast<__attribute__((address_space(3))) lds_u32x4*>(addr) = __builtin_bit_cast(lds_u32x4, v);
+}
+__device__ __forceinline__ void lds_write_b32(uint32_t addr, uint32_t v) {
+  *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(addr) = v;
+}
+__device__ __forceinline__ uint4 lds_read_b128(uint32_t addr) {
+  return __builtin_bit_cast(uint4, *reinterpret_cast<const __attribute__((address_space(3))) lds_u32x4*>(addr));
+}
+
+// bf16 (or E4M3 when FP8) rows of 128 columns: STORE and QKV
+template <int EPI, bool FP8, int MB>
+__device__ __forceinline__ void epilogue_rows(const GemmParams& p, const f32x16_t (&acc)[MB][4],
+                                              uint32_t lds, int m_row0, int n_base, int lane) {
+  const int l32 = lane & 31, hi = lane >> 5;
+  int kind = 0, g = 0;
+  float inv = 1.0f;
+  if (EPI == EPI_QKV) {
     const int head = n_base / kHeadDim;
-    const int kind = head < p.hq ? 0 : (head < p.hq + p.hkv ? 1 : 2);   // q, k, v
-    float y[4][16];
+    kind = head < p.hq ? 0 : (head < p.hq + p.hkv ? 1 : 2);
+    g = head - p.hq - (kind == 2 ? p.hkv : 0);
+    inv = kind == 1 ? p.k_inv_scale : p.v_inv_scale;
+  }
+  // bf16 rows: 256 B = 16 chunks, swizzle row & 15; E4M3 rows: 128 B = 8
+  // chunks, swizzle row & 7
+  constexpr int ROW = FP8 ? 128 : 256;
+  constexpr int SWM = FP8 ? 7 : 15;
+  constexpr int LPR = FP8 ? 8 : 16;          // lanes per row on the way out
+  constexpr int PASSES = 32 * LPR / 64;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = m_row0 + mb * 32 + l32;
+    const float2* rp = nullptr;
+    if (EPI == EPI_QKV && kind != 2) rp = p.rope + (int64_t)p.pos[min(m, p.M - 1)] * 64;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const int n = n_base + nb * 32 + rg * 8 + hi * 4;
-        const uint2 sc = *reinterpret_cast<const uint2*>(p.scale + n);
-        y[nb][rg * 4 + 0] = acc[nb][rg * 4 + 0] * bf16_bits_to_f32(sc.x & 0xFFFF);
-        y[nb][rg * 4 + 1] = acc[nb][rg * 4 + 1] * bf16_bits_to_f32(sc.x >> 16);
-        y[nb][rg * 4 + 2] = acc[nb][rg * 4 + 2] * bf16_bits_to_f32(sc.y & 0xFFFF);
-        y[nb][rg * 4 + 3] = acc[nb][rg * 4 + 3] * bf16_bits_to_f32(sc.y >> 16);
+        const int i0 = nb * 32 + rg * 8 + hi * 4;
+        const uint2 s1 = *reinterpret_cast<const uint2*>(p.scale + n_base + i0);
+        const uint2 s2 = *reinterpret_cast<const uint2*>(p.scale + n_base + 64 + i0);
+        float x1[4], x2[4];
+        x1[0] = acc[mb][nb][rg * 4 + 0] * bf16_bits_to_f32(s1.x & 0xFFFF);
+        x1[1] = acc[mb][nb][rg * 4 + 1] * bf16_bits_to_f32(s1.x >> 16);
+        x1[2] = acc[mb][nb][rg * 4 + 2] * bf16_bits_to_f32(s1.y & 0xFFFF);
+        x1[3] = acc[mb][nb][rg * 4 + 3] * bf16_bits_to_f32(s1.y >> 16);
+        x2[0] = acc[mb][nb + 2][rg * 4 + 0] * bf16_bits_to_f32(s2.x & 0xFFFF);
+        x2[1] = acc[mb][nb + 2][rg * 4 + 1] * bf16_bits_to_f32(s2.x >> 16);
+        x2[2] = acc[mb][nb + 2][rg * 4 + 2] * bf16_bits_to_f32(s2.y & 0xFFFF);
+        x2[3] = acc[mb][nb + 2][rg * 4 + 3] * bf16_bits_to_f32(s2.y >> 16);
+        if (EPI == EPI_QKV && kind != 2) {
+          // RoPE (rotate-half): pairs (i, i + 64) sit in blocks nb, nb + 2
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float2 cs = rp[i0 + e];
+            const float a = x1[e], b = x2[e];
+            x1[e] = a * cs.x - b * cs.y;
+            x2[e] = b * cs.x + a * cs.y;
+          }
+        }
+        if (!FP8) {
+          // column i0 is chunk i0/8 = nb*4 + rg, 8-byte half hi
+          const int c1 = nb * 4 + rg, c2 = c1 + 8;
+          lds_write_b64(lds + l32 * ROW + ((c1 ^ (l32 & SWM)) << 4) + hi * 8,
+                        make_uint2(pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3])));
+          lds_write_b64(lds + l32 * ROW + ((c2 ^ (l32 & SWM)) << 4) + hi * 8,
+                        make_uint2(pack_bf16x2(x2[0], x2[1]), pack_bf16x2(x2[2], x2[3])));
+        } else {
+          // E4M3 code of (value / scale), after the bf16 rounding the value
+          // has in the bf16 pipeline; column i0 is chunk i0/16
+          uint32_t w1 = 0, w2 = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            w1 |= f32_to_e4m3(bf16_bits_to_f32(f32_to_bf16_bits(x1[e])) * inv) << (8 * e);
+            w2 |= f32_to_e4m3(bf16_bits_to_f32(f32_to_bf16_bits(x2[e])) * inv) << (8 * e);
+          }
+          const int c1 = i0 >> 4, c2 = c1 + 4;
+          lds_write_b32(lds + l32 * ROW + ((c1 ^ (l32 & SWM)) << 4) + (i0 & 15), w1);
+          lds_write_b32(lds + l32 * ROW + ((c2 ^ (l32 & SWM)) << 4) + (i0 & 15), w2);
+        }
       }
-    if (kind != 2) {
-      const float2* rp = p.rope + (int64_t)p.pos[m] * 64;
+#pragma unroll
+    for (int it = 0; it < PASSES; ++it) {
+      const int r = it * (64 / LPR) + lane / LPR;
+      const int c = lane % LPR;
+      const uint4 v = lds_read_b128(lds + r * ROW + ((c ^ (r & SWM)) << 4));
+      const int mr = m_row0 + mb * 32 + r;
+      if (mr >= p.M) continue;
+      uint4* dst;
+      if (EPI == EPI_STORE) {
+        dst = reinterpret_cast<uint4*>(p.Y + (int64_t)mr * p.ldy + n_base + c * 8);
+      } else if (kind == 0) {
+        dst = reinterpret_cast<uint4*>(p.q_out + (int64_t)mr * p.hq * kHeadDim + n_base + c * 8);
+      } else if (p.kv_mode == 0) {
+        dst = reinterpret_cast<uint4*>((kind == 1 ? p.k_out : p.v_out) + ((int64_t)mr * p.hkv + g) * kHeadDim + c * 8);
+      } else {
+        const int64_t off = p.kv_row[mr] +
+            ((int64_t)(p.layer * 2 + (kind == 2)) * p.hkv + g) * (int64_t)p.kv_lapad[mr] * kHeadDim;
+        dst = FP8 ? reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(p.pool) + off + c * 16)
+                  : reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.pool) + off + c * 8);
+      }
+      *dst = v;
+    }
+  }
+}
+
+template <int EPI, int MB>
+__device__ __forceinline__ void epilogue_staged(const GemmParams& p, const f32x16_t (&acc)[MB][4],
+                                                uint32_t lds, int m_row0, int n_base, int o_base,
+                                                int lane) {
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int sw16 = l32 & 15;                 // row swizzle of the writing lane (row = l32)
+  if (EPI == EPI_STORE) {
+    epilogue_rows<EPI_STORE, false, MB>(p, acc, lds, m_row0, n_base, lane);
+  } else if (EPI == EPI_QKV) {
+    const int head = n_base / kHeadDim;
+    const bool to_fp8 = head >= p.hq && p.kv_mode == 1 && p.kv_fp8;
+    if (to_fp8) epilogue_rows<EPI_QKV, true, MB>(p, acc, lds, m_row0, n_base, lane);
+    else epilogue_rows<EPI_QKV, false, MB>(p, acc, lds, m_row0, n_base, lane);
+  } else if (EPI == EPI_RESID) {
+    // fp32 staging (the residual add and the single bf16 rounding happen
+    // after the read-back): per 32 tokens and 64 columns, 256-B rows
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int nbl = 0; nbl < 2; ++nbl)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const int nb = half * 2 + nbl;
+            const int n = n_base + nb * 32 + rg * 8 + hi * 4;
+            const uint2 sc = *reinterpret_cast<const uint2*>(p.scale + n);
+            uint4 v;
+            v.x = __float_as_uint(acc[mb][nb][rg * 4 + 0] * bf16_bits_to_f32(sc.x & 0xFFFF));
+            v.y = __float_as_uint(acc[mb][nb][rg * 4 + 1] * bf16_bits_to_f32(sc.x >> 16));
+            v.z = __float_as_uint(acc[mb][nb][rg * 4 + 2] * bf16_bits_to_f32(sc.y & 0xFFFF));
+            v.w = __float_as_uint(acc[mb][nb][rg * 4 + 3] * bf16_bits_to_f32(sc.y >> 16));
+            const int c = nbl * 8 + rg * 2 + hi;             // 16-B chunk of 4 fp32
+            lds_write_b128(lds + l32 * 256 + ((c ^ sw16) << 4), v);
+          }
+        // 8 lanes per row (8 columns each): 8 rows per pass
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int r = it * 8 + (lane >> 3);
+          const int c8 = lane & 7;                           // 8 columns = chunks 2c8, 2c8+1
+          const uint4 a = lds_read_b128(lds + r * 256 + (((2 * c8) ^ (r & 15)) << 4));
+          const uint4 b = lds_read_b128(lds + r * 256 + (((2 * c8 + 1) ^ (r & 15)) << 4));
+          const int mr = m_row0 + mb * 32 + r;
+          if (mr >= p.M) continue;
+          uint4* yp = reinterpret_cast<uint4*>(p.Y + (int64_t)mr * p.ldy + n_base + half * 64 + c8 * 8);
+          const uint4 h = *yp;
+          uint4 o;
+          o.x = pack_bf16x2(__uint_as_float(a.x) + bf16_bits_to_f32(h.x & 0xFFFF),
+                            __uint_as_float(a.y) + bf16_bits_to_f32(h.x >> 16));
+          o.y = pack_bf16x2(__uint_as_float(a.z) + bf16_bits_to_f32(h.y & 0xFFFF),
+                            __uint_as_float(a.w) + bf16_bits_to_f32(h.y >> 16));
+          o.z = pack_bf16x2(__uint_as_float(b.x) + bf16_bits_to_f32(h.z & 0xFFFF),
+                            __uint_as_float(b.y) + bf16_bits_to_f32(h.z >> 16));
+          o.w = pack_bf16x2(__uint_as_float(b.z) + bf16_bits_to_f32(h.w & 0xFFFF),
+                            __uint_as_float(b.w) + bf16_bits_to_f32(h.w >> 16));
+          *yp = o;
+        }
+      }
+    }
+  } else {  // EPI_SWIGLU: 64 output columns, bf16 rows of 128 B (8 chunks)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg)
+        for (int rg = 0; rg < 4; ++rg) {
+          const int j = nb * 32 + rg * 8 + hi * 4;
+          const uint2 sg = *reinterpret_cast<const uint2*>(p.scale + o_base + j);
+          const uint2 su = *reinterpret_cast<const uint2*>(p.scale + p.inter + o_base + j);
+          float gt[4], u[4];
+          gt[0] = acc[mb][nb][rg * 4 + 0] * bf16_bits_to_f32(sg.x & 0xFFFF);
+          gt[1] = acc[mb][nb][rg * 4 + 1] * bf16_bits_to_f32(sg.x >> 16);
+          gt[2] = acc[mb][nb][rg * 4 + 2] * bf16_bits_to_f32(sg.y & 0xFFFF);
+          gt[3] = acc[mb][nb][rg * 4 + 3] * bf16_bits_to_f32(sg.y >> 16);
+          u[0] = acc[mb][nb + 2][rg * 4 + 0] * bf16_bits_to_f32(su.x & 0xFFFF);
+          u[1] = acc[mb][nb + 2][rg * 4 + 1] * bf16_bits_to_f32(su.x >> 16);
+          u[2] = acc[mb][nb + 2][rg * 4 + 2] * bf16_bits_to_f32(su.y & 0xFFFF);
+          u[3] = acc[mb][nb + 2][rg * 4 + 3] * bf16_bits_to_f32(su.y >> 16);
+          const int c = nb * 4 + rg;
+          lds_write_b64(lds + l32 * 128 + ((c ^ (l32 & 7)) << 4) + hi * 8,
+                        make_uint2(pack_bf16x2(silu_f(gt[0]) * u[0], silu_f(gt[1]) * u[1]),
+                                   pack_bf16x2(silu_f(gt[2]) * u[2], silu_f(gt[3]) * u[3])));
+        }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = nb * 32 + rg * 8 + hi * 4 + e;
-            const float2 cs = rp[i];
-            const float x1 = y[nb][rg * 4 + e];
-            const float x2 = y[nb + 2][rg * 4 + e];
-            y[nb][rg * 4 + e] = x1 * cs.x - x2 * cs.y;
-            y[nb + 2][rg * 4 + e] = x2 * cs.x + x1 * cs.y;
-          }
-    }
-    if (kind == 0 || p.kv_mode == 0 || !p.kv_fp8) {
-      uint16_t* dst;
-      if (kind == 0) {
-        dst = p.q_out + (int64_t)m * p.hq * kHeadDim + head * kHeadDim;
-      } else if (p.kv_mode == 0) {
-        const int g = head - p.hq - (kind == 2 ? p.hkv : 0);
-        dst = (kind == 1 ? p.k_out : p.v_out) + ((int64_t)m * p.hkv + g) * kHeadDim;
-      } else {
-        const int g = head - p.hq - (kind == 2 ? p.hkv : 0);
-        const int64_t off = p.kv_row[m] +
-            ((int64_t)(p.layer * 2 + (kind == 2)) * p.hkv + g) * (int64_t)p.kv_lapad[m] * kHeadDim;
-        dst = reinterpret_cast<uint16_t*>(p.pool) + off;
+      for (int it = 0; it < 4; ++it) {
+        const int r = it * 8 + (lane >> 3);
+        const int c = lane & 7;
+        const uint4 v = lds_read_b128(lds + r * 128 + ((c ^ (r & 7)) << 4));
+        const int mr = m_row0 + mb * 32 + r;
+        if (mr < p.M) *reinterpret_cast<uint4*>(p.Y + (int64_t)mr * p.ldy + o_base + c * 8) = v;
       }
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          uint2 w;
-          w.x = pack_bf16x2(y[nb][rg * 4 + 0], y[nb][rg * 4 + 1]);
-          w.y = pack_bf16x2(y[nb][rg * 4 + 2], y[nb][rg * 4 + 3]);
-          *reinterpret_cast<uint2*>(dst + nb * 32 + rg * 8 + hi * 4) = w;
-        }
-    } else {
-      // anchor K/V into an fp8 slab: E4M3 code of (value / scale), after the
-      // bf16 rounding the value has in the bf16 pipeline
-      const int g = head - p.hq - (kind == 2 ? p.hkv : 0);
-      const float inv = kind == 1 ? p.k_inv_scale : p.v_inv_scale;
-      const int64_t off = p.kv_row[m] +
-          ((int64_t)(p.layer * 2 + (kind == 2)) * p.hkv + g) * (int64_t)p.kv_lapad[m] * kHeadDim;
-      uint8_t* dst = reinterpret_cast<uint8_t*>(p.pool) + off;
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          uint32_t w = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float b = bf16_bits_to_f32(f32_to_bf16_bits(y[nb][rg * 4 + e]));
-            w |= f32_to_e4m3(b * inv) << (8 * e);
-          }
-          *reinterpret_cast<uint32_t*>(dst + nb * 32 + rg * 8 + hi * 4) = w;
-        }
     }
   }
 }
@@ -322,12 +415,8 @@ gemm_direct_kernel(GemmParams p) {
 
   const int n_base = tn * BN + wn * 128;
   const int o_base = tn * (BN / 2) + wn * 64;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int m = m0 + wm * MW + mb * 32 + l32;
-    if (m >= p.M) continue;
-    epilogue<EPI>(p, acc[mb], m, n_base, o_base, hi);
-  }
+  __syncthreads();   // every wave is done with the stages: they become staging space
+  epilogue_staged<EPI, MB>(p, acc, lds_addr_of(&smem[0][0]) + wave * 8192, m0 + wm * MW, n_base, o_base, lane);
 }
 
 hipError_t launch_gemm(const GemmParams& p, GemmEpi epi, hipStream_t s) {
