@@ -103,6 +103,23 @@ def cascade_attention(q, k_anchor, v_anchor, k_suffix, v_suffix, scale):
     return lse_merge([cross, self_])
 
 
+def cascade_attention_levels(q, levels, k_suffix, v_suffix, scale):
+    """Suffix queries against several fully visible key sets, then causally
+    against themselves, merged by LSE rescaling.
+
+    ``levels`` = [(K, V), ...] in position order, e.g. the anchor and then a
+    prefix shared by several suffixes (a multi-level cascade: every key of an
+    earlier level precedes every suffix token, so no mask applies to it).
+    q [Ls, Hq, d]; each K, V [n_i, Hkv, d]; suffix keys [Ls, Hkv, d].
+    Returns (O, LSE).
+    """
+    ls = q.shape[0]
+    parts = [attention_partial(q, k, v, np.ones((ls, k.shape[0]), bool), scale) for k, v in levels]
+    parts.append(attention_partial(q, k_suffix, v_suffix,
+                                   causal_visible(np.arange(ls), np.arange(ls)), scale))
+    return lse_merge(parts)
+
+
 def monolithic_pair_attention(q_suffix, k_anchor, v_anchor, k_suffix, v_suffix,
                               scale, q_anchor=None):
     """The definition: causal attention over the concatenation [anchor ‖ suffix],

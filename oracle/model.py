@@ -183,13 +183,17 @@ def decide(logits, true_mask):
 
 
 def forward_pair(anchor_tokens, suffix_tokens, weights, shape, true_mask=0x0F,
-                 mode="contract", dtype=np.float64, layers=None, n_layers=None):
+                 mode="contract", dtype=np.float64, layers=None, n_layers=None, shared_len=0):
     """The per-pair definition: causal forward over [anchor ‖ suffix], then the
-    head at the last position. An empty anchor is a filter row."""
+    head at the last position. An empty anchor is a filter row.
+
+    ``shared_len``: the suffix's first tokens are a prefix shared with other
+    suffixes of the anchor, whose K/V is stored once like the anchor's; with an
+    fp8 KV store those positions are stored (and read) in E4M3 too."""
     a = np.asarray(anchor_tokens, np.int64)
     s = np.asarray(suffix_tokens, np.int64)
     tokens = np.concatenate([a, s])
-    fp8_upto = len(a) if shape.kv_fp8 else 0
+    fp8_upto = len(a) + int(shared_len) if shape.kv_fp8 else 0
     h = forward_tokens(tokens, weights, shape, mode, fp8_upto, dtype, layers,
                        n_layers=n_layers)
     logits, tok, dec, margin = head8(h[-1:], weights.get("final_norm"), weights["head8"],

@@ -150,3 +150,27 @@ def test_planted_gqa_mistake_is_caught():
                                           v[:, h % 2:h % 2 + 1], vis, 0.3)[0][:, 0]
                       for h in range(4)], axis=1)
     assert np.max(np.abs(wrong - ref)) > 1e-3
+
+
+@pytest.mark.parametrize("la,lp,ls,G", [(1, 1, 1, 1), (7, 64, 2, 2), (64, 7, 33, 4), (65, 1, 2, 2),
+                                        (1, 33, 33, 1)])
+def test_two_level_cascade_equals_monolithic(la, lp, ls, G):
+    """anchor -> shared prefix -> suffix: two fully visible levels and the
+    causal suffix, merged by LSE, equal causal attention over the concatenation
+    (and the two-level cascade with anchor and prefix as one level)."""
+    r = np.random.default_rng(la * 1000 + lp * 10 + ls)
+    hkv, d = 2, 16
+    hq = hkv * G
+    ka, va = _rand(r, la, hkv, d), _rand(r, la, hkv, d)
+    kp, vp = _rand(r, lp, hkv, d), _rand(r, lp, hkv, d)
+    q, ks, vs = _rand(r, ls, hq, d), _rand(r, ls, hkv, d), _rand(r, ls, hkv, d)
+    o, lse = A.cascade_attention_levels(q, [(ka, va), (kp, vp)], ks, vs, 0.3)
+    n = la + lp + ls
+    k = np.concatenate([ka, kp, ks]); v = np.concatenate([va, vp, vs])
+    om, lm = A.attention_causal(q, k, v, 0.3, q_pos=np.arange(la + lp, n), k_pos=np.arange(n))
+    assert np.max(np.abs(o - om)) < 1e-12 and np.max(np.abs(lse - lm)) < 1e-12
+    o1, l1 = A.cascade_attention(q, np.concatenate([ka, kp]), np.concatenate([va, vp]), ks, vs, 0.3)
+    assert np.max(np.abs(o - o1)) < 1e-12 and np.max(np.abs(lse - l1)) < 1e-12
+    # the SDPA pin on the same visibility
+    vis = np.arange(n)[None, :] <= np.arange(la + lp, n)[:, None]
+    assert np.max(np.abs(o - _sdpa_reference(q, k, v, vis, 0.3))) < 1e-12

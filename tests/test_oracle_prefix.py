@@ -1,0 +1,77 @@
+"""Pins for oracle/prefix.py (shared-prefix grouping) by brute force over all
+pairs of sequences, plus one hand-worked case."""
+import numpy as np
+import pytest
+
+from oracle import prefix as P
+
+
+def _cases():
+    for seed in range(40):
+        r = np.random.default_rng(seed)
+        vocab = int(r.integers(2, 5))
+        seqs = []
+        for _ in range(int(r.integers(0, 25))):
+            if seqs and r.random() < 0.5:      # plant a family member: copy a prefix of an earlier one
+                src = seqs[int(r.integers(len(seqs)))]
+                k = int(r.integers(0, len(src) + 1))
+                tail = r.integers(0, vocab, int(r.integers(0, 6))).tolist()
+                s = src[:k] + tail
+                if not s:
+                    s = [0]
+            else:
+                s = r.integers(0, vocab, int(r.integers(1, 9))).tolist()
+            seqs.append(s)
+        keys = None if seed % 4 == 0 else r.integers(-1, 3, len(seqs)).tolist()
+        yield seqs, keys, int(r.choice([1, 2, 3, 5]))
+
+
+def test_hand_worked_case():
+    seqs = [[1, 2, 3, 4], [1, 2, 3, 5], [1, 2, 9], [7, 7], [1, 2, 3, 4, 6]]
+    # one key: 0, 1, 2, 4 share [1, 2] (LCP 2); [7, 7] stands alone
+    g, f, ln = P.prefix_groups_reference(seqs, None, 2)
+    assert g.tolist() == [0, 0, 0, -1, 0] and f.tolist() == [0] and ln.tolist() == [2]
+    # sequence 2 under another key: 0, 1, 4 share [1, 2, 3]; its shortest member
+    # has 4 tokens, so the node keeps 3 and every member keeps >= 1
+    g, f, ln = P.prefix_groups_reference(seqs, [0, 0, 1, 0, 0], 2)
+    assert g.tolist() == [0, 0, -1, -1, 0] and f.tolist() == [0] and ln.tolist() == [3]
+    # identical sequences: the node stops one token short of their end
+    g, f, ln = P.prefix_groups_reference([[5, 6, 7], [5, 6, 7]], None, 1)
+    assert g.tolist() == [0, 0] and ln.tolist() == [2]
+    # min_len equal to a member's length: that member cannot keep a token
+    g, _, _ = P.prefix_groups_reference([[5, 6], [5, 6, 7], [5, 6, 8]], None, 2)
+    assert g.tolist() == [-1, 0, 0]
+
+
+@pytest.mark.parametrize("case", list(_cases()))
+def test_grouping_by_brute_force(case):
+    seqs, keys, m = case
+    g, first, ln = P.prefix_groups_reference(seqs, keys, m)
+    n = len(seqs)
+    key = [0 if keys is None else keys[i] for i in range(n)]
+    cand = [key[i] >= 0 and len(seqs[i]) > m for i in range(n)]
+    # exactly: same group <=> both candidates, same key, same first m tokens
+    for i in range(n):
+        if not cand[i]:
+            assert g[i] == -1
+        for j in range(i + 1, n):
+            same = cand[i] and cand[j] and key[i] == key[j] and seqs[i][:m] == seqs[j][:m]
+            assert (g[i] >= 0 and g[i] == g[j]) == same, (i, j)
+    # a candidate with no partner stays alone
+    for i in range(n):
+        if cand[i] and g[i] < 0:
+            assert not any(cand[j] and j != i and key[j] == key[i] and seqs[j][:m] == seqs[i][:m]
+                           for j in range(n))
+    # numbering and node contents
+    assert list(first) == sorted(first)
+    for k in range(len(first)):
+        mem = [i for i in range(n) if g[i] == k]
+        assert len(mem) >= 2 and first[k] == min(mem)
+        L = int(ln[k])
+        assert L >= m
+        head = seqs[first[k]][:L]
+        assert all(seqs[i][:L] == head and len(seqs[i]) > L for i in mem)
+        # maximal: one more token would either leave a member empty or not be shared
+        longer_ok = all(len(seqs[i]) > L + 1 for i in mem) and \
+            len({seqs[i][L] for i in mem}) == 1
+        assert not longer_ok

@@ -498,3 +498,31 @@ def c4_case(seed: int = 5, n_anchors: int = 1024, la: int = 768,
     return dict(a_len=a_len, a_off=a_off, a_tok=a_tok, pair_anchor=pair_anchor,
                 pair_row=pair_row, row_len=row_len, row_off=row_off,
                 row_tok=row_tok, true_mask=0x0F)
+
+
+def shared_prefix_case(seed: int, vocab: int, a_len, families, cfg_id: int = 6,
+                       true_mask: int = 0x0F) -> dict:
+    """Suffixes that come in families sharing a leading token run, as in agent
+    traces whose documents repeat a common prefix.
+
+    families: list of (anchor index, shared length, [tail lengths]); each tail
+    length gives one pair whose suffix is the family's shared tokens followed
+    by its own tokens. Returns a join_case-shaped dict (pairs in family order)
+    plus ``family`` [n_pairs] and ``shared_len`` [n_families]. Only seeded
+    draws and layout: which pairs the library groups is for it to find.
+    """
+    pair_anchor, s_len, fam = [], [], []
+    for f, (a, shared, tails) in enumerate(families):
+        for t in tails:
+            pair_anchor.append(a)
+            s_len.append(shared + t)
+            fam.append(f)
+    case = join_case(seed, vocab, a_len, pair_anchor, s_len, cfg_id=cfg_id, true_mask=true_mask)
+    s_tok, s_off = case["s_tok"], case["s_off"]
+    for f, (a, shared, tails) in enumerate(families):
+        head = _rng(cfg_id, seed, 7, f).integers(0, vocab, size=shared, dtype=np.int32)
+        for i in np.flatnonzero(np.asarray(fam) == f):
+            s_tok[s_off[i]:s_off[i] + shared] = head
+    case["family"] = np.asarray(fam, np.int32)
+    case["shared_len"] = np.asarray([f[1] for f in families], np.int32)
+    return case
