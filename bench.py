@@ -518,6 +518,80 @@ def bench_multiplan(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_shared(args):
+    """Suffixes sharing prefixes (agent-trace shaped), 36-layer stack: 16
+    anchors x 1024 tokens, each probed by 16 families of 8 suffixes whose
+    first 384 tokens are the family's, then U{16..64} tokens of their own.
+    The join with shared-prefix nodes (quail_join_run_shared, min_shared 32)
+    against the plain join (quail_join_run) on the same inputs; the second of
+    two runs of each is timed."""
+    import torch
+    import workloads as W
+    from query_aware_prefill_amd import binding as B
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    B.load()
+    shape = W.QWEN3_4B
+    r = np.random.default_rng([7, 0])
+    n_anchors, n_fam, per_fam, shared, min_shared = 16, 16, 8, 384, 32
+    fams = [(a, shared, r.integers(16, 65, per_fam).tolist()) for a in range(n_anchors) for _ in range(n_fam)]
+    case = W.shared_prefix_case(7, shape.vocab, [1024] * n_anchors, fams, cfg_id=7)
+    pa, s_off, s_tok = case["pair_anchor"], case["s_off"], case["s_tok"]
+    a_len, a_off = case["a_len"], case["a_off"]
+    s_len = np.diff(s_off)
+    n = len(pa)
+    log(f"shared36: {n} pairs over {n_anchors} anchors, families of {per_fam} sharing {shared} tokens; "
+        "weights on device")
+    wd = W.model_weights_device(shape, 0)
+    dm = DeviceModel(shape, wd, max_anchor_len=1024, max_suffix_len=int(np.max(s_len)))
+    T = 65536
+    pool = sum(B.quail_anchor_bytes(dm.cfg, int(x)) for x in a_len) + (4 << 30)
+    # tokens the shared run computes: the library's plan steps and grouping
+    order, bounds, _ = B.quail_plan_build(dm.cfg, pool, T, a_len, pa, s_len)
+    node_tok = 0
+    for b0, b1 in zip(bounds[:-1], bounds[1:]):
+        idx = order[b0:b1]
+        offs = np.concatenate([[0], np.cumsum(s_len[idx])]).astype(np.int32)
+        toks = np.concatenate([s_tok[s_off[i]:s_off[i + 1]] for i in idx])
+        g, _, nl = B.quail_prefix_groups(toks, offs, pa[idx], min_shared)
+        node_tok += int(np.sum(nl)) - int(np.sum(nl[g[g >= 0]]))
+    a_tok_d, s_tok_d = to_device(case["a_tok"].astype(np.int32)), to_device(s_tok.astype(np.int32))
+    logical = float(np.sum(a_len[pa] + s_len))
+    prefilled = float(np.sum(a_len))
+    computed = {"plain": prefilled + float(np.sum(s_len)), "shared": prefilled + float(np.sum(s_len)) + node_tok}
+    res = {"metric": "AI.IF join with shared suffix prefixes: two-level cascade vs plain join (36-layer stack)",
+           "workload": f"{n_anchors} anchors x 1024 tokens; {n_fam} families x {per_fam} suffixes per anchor, "
+                       f"{shared} shared tokens + U{{16..64}} own tokens each",
+           "pairs": int(n), "logical_tokens": logical}
+    out = {}
+    for mode in ("shared", "plain"):
+        ctx = dm.context(pool, T)
+        logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+        dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+        for _ in range(2):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            if mode == "shared":
+                B.quail_join_run_shared(ctx, a_tok_d, a_off, pa, s_tok_d, s_off, s_tok, min_shared, 0x0F,
+                                        logits, None, dec)
+            else:
+                B.quail_join_run(ctx, a_tok_d, a_off, pa, s_tok_d, s_off, 0x0F, logits, None, dec)
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1000.0
+        st = B.quail_pool_stats(ctx)
+        out[mode] = (logits.cpu().numpy(), dec.cpu().numpy())
+        res[mode] = {"ms": ms, "logical_tokens_per_min": logical / ms * 60e3,
+                     "computed_tokens": computed[mode], "computed_tokens_per_min": computed[mode] / ms * 60e3,
+                     "pool_over_two_runs": st}
+        log(f"shared36 {mode}: {ms / 1000:.2f} s, {computed[mode] / 1e6:.3f} M computed tokens, "
+            f"{logical / ms * 60e3 / 1e6:.1f} M logical tokens/min")
+        del ctx
+    res["speedup"] = res["plain"]["ms"] / res["shared"]["ms"]
+    ls, lp = out["shared"][0].astype(np.float64), out["plain"][0].astype(np.float64)
+    res["logits_rel_inf_shared_vs_plain"] = float(np.max(np.abs(ls - lp)) / np.max(np.abs(lp)))
+    res["decisions_equal_frac"] = float(np.mean(out["shared"][1] == out["plain"][1]))
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -526,7 +600,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--workload", choices=["cascade", "gemm", "layer", "copy", "stream", "join36",
-                                           "filter36", "multijoin36", "multiplan36"], default="cascade")
+                                           "filter36", "multijoin36", "multiplan36", "shared36"],
+                    default="cascade")
     ap.add_argument("--rows", type=int, default=625, help="multijoin36: rows of the 5,000 used")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -545,6 +620,8 @@ def main():
         return bench_stream(args)
     if args.workload == "multiplan36":
         return bench_multiplan(args)
+    if args.workload == "shared36":
+        return bench_shared(args)
     if args.workload in ("join36", "filter36", "multijoin36"):
         return bench_e2e(args)
 
@@ -623,7 +700,7 @@ def main():
         "roofline": {
             "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
-            "kernel": "quail::attn_direct_kernel<4, false, false, false>", "flops_per_launch": flops,
+            "kernel": "quail::attn_direct_kernel<4, false, false, false, false>", "flops_per_launch": flops,
             "launch_ms": kernel_ms,
             "algorithmic_bytes_per_launch": algorithmic_bytes(a_len, s_len),
         },

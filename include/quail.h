@@ -205,8 +205,52 @@ quail_status quail_anchor_prefill(quail_ctx* ctx, int32_t n, const int32_t* toke
                                   quail_stream stream);
 
 /* Gives up an anchor before its declared uses are spent (its slab is freed;
- * later use returns E_STALE). */
+ * later use returns E_STALE). E_INVAL while prefix nodes of the anchor (see
+ * quail_prefix_prefill) are alive. Releasing a prefix node spends the anchor
+ * use it holds. */
 quail_status quail_anchor_release(quail_ctx* ctx, quail_anchor handle);
+
+/* ---- shared suffix prefixes: two-level cascade ------------------------------ */
+/* [pt] "Futuro e método" lists a radix index for prefix sharing as future
+ * work, and [fa] (body) names the one workload where vLLM wins: agent traces,
+ * whose documents share prefixes the engine cannot exploit. These calls add
+ * one shared level between an anchor and its suffixes: anchor -> shared
+ * suffix prefix (a "prefix node") -> the rest of each suffix.
+ *
+ * Groups sequences by shared prefix (host only, no GPU): sequence i =
+ * tokens[offsets[i] .. offsets[i+1]) (host int32; offsets host [n+1],
+ * non-decreasing, lengths >= 1) with key keys[i] (host [n], e.g. the anchor
+ * index; negative = never grouped; NULL = one key for all). Sequences with the
+ * same key and the same first min_len tokens (min_len >= 1), at least two of
+ * them and each longer than min_len, form one node: the subtrees of the
+ * per-key radix tree at depth min_len. The node's prefix is the members'
+ * longest common prefix, shortened if needed so every member keeps at least
+ * one token: node_len[k] >= min_len, and its tokens are the first node_len[k]
+ * tokens of member node_first[k] (its smallest member). Nodes are numbered in
+ * increasing node_first. Outputs (host, caller-allocated [n]): group_of[i] =
+ * node of sequence i or -1; node_first, node_len; *n_nodes = node count. */
+quail_status quail_prefix_groups(int32_t n, const int32_t* tokens, const int32_t* offsets,
+                                 const int32_t* keys, int32_t min_len, int32_t* group_of,
+                                 int32_t* node_first, int32_t* node_len, int32_t* n_nodes);
+
+/* Prefills prefix nodes: node a = tokens[offsets[a] .. offsets[a+1]) (dev
+ * int32; host offsets [n+1], lengths in [1, max_batch_tokens]) continues
+ * anchor parent[a] (host handle of a live anchor that is not itself a node)
+ * at positions La.. : it attends to every key of the anchor and causally to
+ * itself, and every layer's K/V goes to a slab of its own, as for an anchor.
+ * n_uses: host [n], the pairs that will name the node (0 = not prefilled,
+ * handle QUAIL_NO_ANCHOR). Each node holds one of its anchor's declared uses
+ * and spends it when the node is evicted, so the anchor outlives its nodes.
+ * A pair naming a node handle in quail_join_prefill runs its tokens at
+ * positions La + Lp.. against the anchor's keys, the node's keys (both
+ * unmasked) and its own keys (causal): the same result as the full suffix
+ * [node tokens ‖ pair tokens] after the anchor. out: host [n] handles.
+ * E_STALE: a parent handle is stale or has no use to spare; E_INVAL: a parent
+ * is a node, or La + Lp + 1 exceeds max_anchor_len + max_suffix_len; E_NOMEM
+ * as quail_anchor_prefill. */
+quail_status quail_prefix_prefill(quail_ctx* ctx, int32_t n, const quail_anchor* parent,
+                                  const int32_t* tokens, const int32_t* offsets,
+                                  const int32_t* n_uses, quail_anchor* out, quail_stream stream);
 
 /* Device addresses of an anchor's K and V for one layer ([kv_head][La_pad]
  * [head_dim], bf16 or fp8 per kv_dtype) and its lengths. For tests/tools. */
@@ -226,7 +270,11 @@ quail_status quail_anchor_kv(const quail_ctx* ctx, quail_anchor handle, int32_t 
  * position's final hidden state to h_all (dev bf16 [offsets[n], hidden]).
  * Pairs may come in any order; each pair spends one use of its anchor and an
  * anchor whose uses reach 0 is evicted (its slab is reused in stream order).
- * E_STALE if a handle is stale or used more often than declared. */
+ * A handle may also name a prefix node (quail_prefix_prefill): the pair's
+ * tokens then sit at positions La + Lp + j and attend to the anchor's keys,
+ * the node's keys and their own. E_STALE if a handle is stale or used more
+ * often than declared (an anchor's uses held by live nodes are not
+ * available to pairs). */
 quail_status quail_join_prefill(quail_ctx* ctx, int32_t n, const quail_anchor* pair_anchor,
                                 const int32_t* tokens, const int32_t* offsets,
                                 uint16_t* h_last, uint16_t* h_all, quail_stream stream);
@@ -259,6 +307,21 @@ quail_status quail_join_run(quail_ctx* ctx, int32_t n_anchors, const int32_t* a_
                             const int32_t* pair_anchor, const int32_t* s_tokens,
                             const int32_t* s_offsets, uint8_t true_mask, float* logits,
                             uint8_t* token, uint8_t* decision, quail_stream stream);
+
+/* quail_join_run with shared suffix prefixes: within each step of the plan,
+ * the pairs of one anchor are grouped by quail_prefix_groups(min_shared) over
+ * s_tokens_host (a host copy of s_tokens, same layout); each group's prefix
+ * node is prefilled once (quail_prefix_prefill, in chunks that fit half the
+ * largest free pool block) and its members run only their remaining tokens.
+ * The anchor's uses are its ungrouped pairs plus one per node. Outputs equal
+ * quail_join_run's up to floating-point rounding (the cascade split is
+ * exact). min_shared >= 1; other arguments as quail_join_run. */
+quail_status quail_join_run_shared(quail_ctx* ctx, int32_t n_anchors, const int32_t* a_tokens,
+                                   const int32_t* a_offsets, int32_t n_pairs,
+                                   const int32_t* pair_anchor, const int32_t* s_tokens,
+                                   const int32_t* s_offsets, const int32_t* s_tokens_host,
+                                   int32_t min_shared, uint8_t true_mask, float* logits,
+                                   uint8_t* token, uint8_t* decision, quail_stream stream);
 
 /* Runs several joins over one anchor table with the plan of
  * quail_multiplan_build (pool budget: the largest free block of the pool

@@ -68,6 +68,9 @@ _SIGS = {
     "quail_ctx_destroy": ([_vp], C.c_int32),
     "quail_anchor_prefill": ([_vp, C.c_int32, _vp, _i32p, _i32p, _i64p, _i64p, _vp], C.c_int32),
     "quail_anchor_release": ([_vp, C.c_int64], C.c_int32),
+    "quail_prefix_groups": ([C.c_int32, _i32p, _i32p, _i32p, C.c_int32, _i32p, _i32p, _i32p, _i32p],
+                            C.c_int32),
+    "quail_prefix_prefill": ([_vp, C.c_int32, _i64p, _vp, _i32p, _i32p, _i64p, _vp], C.c_int32),
     "quail_anchor_kv": ([_vp, C.c_int64, C.c_int32, C.POINTER(_vp), C.POINTER(_vp), _i32p, _i32p],
                         C.c_int32),
     "quail_join_prefill": ([_vp, C.c_int32, _i64p, _vp, _i32p, _vp, _vp, _vp], C.c_int32),
@@ -75,6 +78,8 @@ _SIGS = {
     "quail_head8_f32": ([C.c_int32, C.c_int32, _vp, _vp, C.c_uint8, _vp, _vp, _vp, _vp], C.c_int32),
     "quail_join_run": ([_vp, C.c_int32, _vp, _i32p, C.c_int32, _i32p, _vp, _i32p, C.c_uint8, _vp, _vp,
                         _vp, _vp], C.c_int32),
+    "quail_join_run_shared": ([_vp, C.c_int32, _vp, _i32p, C.c_int32, _i32p, _vp, _i32p, _i32p, C.c_int32,
+                               C.c_uint8, _vp, _vp, _vp, _vp], C.c_int32),
     "quail_multijoin_run": ([_vp, C.c_int32, _vp, _i32p, C.c_int32, _i32p, _i32p, _vp, _i32p, C.c_uint8,
                              _vp, _vp, _vp, _vp], C.c_int32),
     "quail_pool_stats": ([_vp, _szp, _szp, _i64p, _i64p, _i64p], C.c_int32),
@@ -242,6 +247,31 @@ def quail_anchor_release(ctx: Context, handle: int):
     _check(load().quail_anchor_release(ctx.handle, int(handle)))
 
 
+def quail_prefix_groups(tokens, offsets, keys, min_len: int):
+    """Host radix grouping; returns (group_of, node_first, node_len) numpy int32."""
+    tok, tokp = _i32(np.asarray(tokens).reshape(-1) if len(tokens) else np.zeros(1, np.int32))
+    off, offp = _i32(offsets)
+    n = len(off) - 1
+    ks, ksp = (None, None) if keys is None else _i32(keys)
+    g, gp = _i32(np.zeros(max(n, 1), np.int32))
+    f, fp = _i32(np.zeros(max(n, 1), np.int32))
+    ln, lnp = _i32(np.zeros(max(n, 1), np.int32))
+    nn = C.c_int32()
+    _check(load().quail_prefix_groups(n, tokp, offp, ksp, int(min_len), gp, fp, lnp, C.byref(nn)))
+    return g[:n].copy(), f[:nn.value].copy(), ln[:nn.value].copy()
+
+
+def quail_prefix_prefill(ctx: Context, parent, tokens, offsets, n_uses, stream=None):
+    pa, pap = _i64(parent)
+    off, offp = _i32(offsets)
+    nu, nup = _i32(n_uses)
+    n = len(off) - 1
+    out, outp = _i64(np.zeros(n, np.int64))
+    _check(load().quail_prefix_prefill(ctx.handle, n, pap, dptr(tokens), offp, nup, outp,
+                                       stream_handle(stream)))
+    return out
+
+
 def quail_anchor_kv(ctx: Context, handle: int, layer: int):
     k, v = C.c_void_p(), C.c_void_p()
     la, lp = C.c_int32(), C.c_int32()
@@ -275,6 +305,17 @@ def quail_join_run(ctx: Context, a_tokens, a_offsets, pair_anchor, s_tokens, s_o
     _check(load().quail_join_run(ctx.handle, len(ao) - 1, dptr(a_tokens), aop, len(pa), pap,
                                  dptr(s_tokens), sop, true_mask, dptr(logits), dptr(token),
                                  dptr(decision), stream_handle(stream)))
+
+
+def quail_join_run_shared(ctx: Context, a_tokens, a_offsets, pair_anchor, s_tokens, s_offsets, s_tokens_host,
+                          min_shared, true_mask, logits, token, decision, stream=None):
+    ao, aop = _i32(a_offsets)
+    pa, pap = _i32(pair_anchor)
+    so, sop = _i32(s_offsets)
+    sh, shp = _i32(s_tokens_host)
+    _check(load().quail_join_run_shared(ctx.handle, len(ao) - 1, dptr(a_tokens), aop, len(pa), pap,
+                                        dptr(s_tokens), sop, shp, int(min_shared), true_mask, dptr(logits),
+                                        dptr(token), dptr(decision), stream_handle(stream)))
 
 
 def quail_multijoin_run(ctx: Context, a_tokens, a_offsets, join_offsets, pair_anchor, s_tokens, s_offsets,

@@ -185,9 +185,11 @@ attn_bf16_kernel(AttnParams p) {
   const int seg_lo = row_ok ? p.seg_lo[tok] : 0x7FFFFFFF;
   const int self_q = tile.self_qbase + qrow;       // self-key index of this query
 
-  KVSrc cs{}, ss{};
-  int n_ct = 0, n_st = 0;
-  if (tile.cross >= 0) { cs = p.srcs[tile.cross]; n_ct = (cs.len + kKeyTile - 1) / kKeyTile; }
+  KVSrc cs{}, cs2{}, ss{};
+  int n_c1 = 0, n_ct = 0, n_st = 0;
+  if (tile.cross >= 0) { cs = p.srcs[tile.cross]; n_c1 = (cs.len + kKeyTile - 1) / kKeyTile; }
+  n_ct = n_c1;
+  if (tile.cross2 >= 0) { cs2 = p.srcs[tile.cross2]; n_ct += (cs2.len + kKeyTile - 1) / kKeyTile; }
   if (tile.self >= 0) {
     ss = p.srcs[tile.self];
     const int self_end = tile.self_qbase + tile.nq;
@@ -198,12 +200,13 @@ attn_bf16_kernel(AttnParams p) {
 
   auto view = [&](int it) {
     TileView t;
-    const KVSrc& s = it < n_ct ? cs : ss;
+    const KVSrc& s = it < n_c1 ? cs : (it < n_ct ? cs2 : ss);
     const int esz = s.fp8 ? 1 : 2;
     t.k = reinterpret_cast<const uint8_t*>(s.k) + (int64_t)g * s.head_stride * esz;
     t.v = reinterpret_cast<const uint8_t*>(s.v) + (int64_t)g * s.head_stride * esz;
     t.tok_bytes = s.tok_stride * esz;
-    t.kbase = it < n_ct ? it * kKeyTile : tile.self_k0 + (it - n_ct) * kKeyTile;
+    t.kbase = it < n_c1 ? it * kKeyTile
+                        : (it < n_ct ? (it - n_c1) * kKeyTile : tile.self_k0 + (it - n_ct) * kKeyTile);
     t.len = s.len;
     t.fp8 = s.fp8;
     return t;
@@ -222,8 +225,10 @@ attn_bf16_kernel(AttnParams p) {
 
   for (int it = 0; it < n_tiles; ++it) {
     const bool is_cross = it < n_ct;
-    const int fp8 = is_cross ? cs.fp8 : ss.fp8;
-    const int kbase = is_cross ? it * kKeyTile : tile.self_k0 + (it - n_ct) * kKeyTile;
+    const int fp8 = is_cross ? cs.fp8 : ss.fp8;   // both cross levels are slabs of one format
+    const int kbase = it < n_c1 ? it * kKeyTile
+                                : (is_cross ? (it - n_c1) * kKeyTile : tile.self_k0 + (it - n_ct) * kKeyTile);
+    const int clen = it < n_c1 ? cs.len : cs2.len;
     __syncthreads();
     store_tile<NT>(regs, fp8, p.k_scale, p.v_scale, Ks, Vt, tid);
     __syncthreads();
@@ -245,10 +250,10 @@ attn_bf16_kernel(AttnParams p) {
     // Mask (key of (kb, r) = kbase + kb*32 + (r/4)*8 + hi*4 + r%4), then the
     // row max of this tile over both lanes of the row (scores are raw here;
     // the softmax scale is folded into the exponent below).
-    const bool need_mask = is_cross ? (kbase + kKeyTile > cs.len) : true;
+    const bool need_mask = is_cross ? (kbase + kKeyTile > clen) : true;
     if (need_mask) {
       const int lo = is_cross ? 0 : seg_lo;
-      const int hi_k = is_cross ? cs.len - 1 : self_q;
+      const int hi_k = is_cross ? clen - 1 : self_q;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -452,19 +457,29 @@ template <bool B>
 struct MaskTag { static constexpr bool value = B; };
 
 // The key tiles one workgroup visits: first the cross tiles of its anchor
-// source (the last one ragged), then the self tiles from self_k0 up to its
-// last query. Tiles j >= n_full need masking.
+// source (the last one ragged), then those of the second cross source (a
+// shared suffix prefix; its last tile ragged), then the self tiles from
+// self_k0 up to its last query. Tiles j >= n_full need masking. kbase is the
+// tile's first key within its own source.
 // TKC / TKS: keys per cross / self tile (64, or 32 for the half tiles of
-// packed launches).
-template <int TKC = kKeyTile, int TKS = kKeyTile>
+// packed launches). L2: launches with a second cross level; without it the
+// tile -> source selects stay two-way (they sit in the copy and mask paths of
+// every step).
+template <int TKC = kKeyTile, int TKS = kKeyTile, bool L2 = false>
 struct TileSeq {
-  KVSrc cs{}, ss{};
-  int n_ct = 0, n_st = 0, n_full = 0, n_tiles = 0, self_k0 = 0;
+  KVSrc cs{}, cs2{}, ss{};
+  int n_c1 = 0, n_ct = 0, n_st = 0, n_full = 0, n_tiles = 0, self_k0 = 0;
   __device__ __forceinline__ TileSeq(const AttnParams& p, const AttnTile& tile) {
     if (tile.cross >= 0) {
       cs = p.srcs[tile.cross];
-      n_ct = (cs.len + TKC - 1) / TKC;
+      n_c1 = (cs.len + TKC - 1) / TKC;
       n_full = cs.len / TKC;
+    }
+    n_ct = n_c1;
+    if (L2 && tile.cross2 >= 0) {
+      cs2 = p.srcs[tile.cross2];
+      n_ct += (cs2.len + TKC - 1) / TKC;
+      if (n_full == n_c1) n_full += cs2.len / TKC;   // the first level ends on a tile boundary
     }
     if (tile.self >= 0) {
       ss = p.srcs[tile.self];
@@ -473,8 +488,19 @@ struct TileSeq {
     n_tiles = n_ct + n_st;
     self_k0 = tile.self_k0;
   }
-  __device__ __forceinline__ const KVSrc& src(int j) const { return j < n_ct ? cs : ss; }
-  __device__ __forceinline__ int kbase(int j) const { return j < n_ct ? j * TKC : self_k0 + (j - n_ct) * TKS; }
+  __device__ __forceinline__ const KVSrc& src(int j) const {
+    if constexpr (!L2) return j < n_ct ? cs : ss;
+    else return j < n_c1 ? cs : (j < n_ct ? cs2 : ss);
+  }
+  __device__ __forceinline__ int kbase(int j) const {
+    if constexpr (!L2) return j < n_ct ? j * TKC : self_k0 + (j - n_ct) * TKS;
+    else return j < n_c1 ? j * TKC : (j < n_ct ? (j - n_c1) * TKC : self_k0 + (j - n_ct) * TKS);
+  }
+  // valid keys of a cross tile's source
+  __device__ __forceinline__ int clen(int j) const {
+    if constexpr (!L2) return cs.len;
+    else return j < n_c1 ? cs.len : cs2.len;
+  }
 };
 
 // One wave's share of the bf16 MFMA attention: 32 query rows of one head
@@ -732,7 +758,7 @@ __device__ __forceinline__ void publish_keep() {
 // whose anchors have few query tokens, where K/V streaming is the work): one
 // wave whose 32 rows are the G heads x 32/G tokens, so that every K/V tile
 // feeds 32 useful rows instead of 32 per head.
-template <int G, bool FC, bool FS, bool PACK>
+template <int G, bool FC, bool FS, bool PACK, bool L2>
 __global__ void __launch_bounds__(PACK ? 64 : 64 * (G >= 4 ? G : 4), 2)
 attn_direct_kernel(AttnParams p) {
   constexpr int NW = PACK ? 1 : (G >= 4 ? G : 4);
@@ -760,7 +786,7 @@ attn_direct_kernel(AttnParams p) {
   const bool row_ok = qrow < tile.nq;
   const int64_t tok = (int64_t)tile.q0 + qrow;
 
-  const TileSeq<HALF_CROSS ? kKeyTile / 2 : kKeyTile, HALF_SELF ? kKeyTile / 2 : kKeyTile> ts(p, tile);
+  const TileSeq<HALF_CROSS ? kKeyTile / 2 : kKeyTile, HALF_SELF ? kKeyTile / 2 : kKeyTile, L2> ts(p, tile);
   if (ts.n_tiles == 0) {
     store_empty(p, tok, row_ok, head, lane >> 5);
     return;
@@ -789,7 +815,7 @@ attn_direct_kernel(AttnParams p) {
   publish();
   if (ts.n_ct > 0) w.scores<FC, HALF_CROSS>(kslot(0), s_cur);
   else w.scores<FS, HALF_SELF>(kslot(0), s_cur);
-  if (ts.n_full == 0) w.mask(s_cur, ts.kbase(0), 0 < ts.n_ct, ts.cs.len);
+  if (ts.n_full == 0) w.mask(s_cur, ts.kbase(0), 0 < ts.n_ct, ts.clen(0));
   w.rescale(w.row_max(s_cur));
 
   // step j: issue K(j+2), V(j+2); S(j+1) with P(j); PV(j) with mask/max of
@@ -816,7 +842,7 @@ attn_direct_kernel(AttnParams p) {
     w.scores<S_FP8, S_HALF>(kslot((j + 1) & 1), s_nxt);
     w.pv<PV_FP8, PV_HALF>(vslot(vs), pb);
     vs = vs == 2 ? 0 : vs + 1;
-    if constexpr (MASK_NEXT) w.mask(s_nxt, ts.kbase(j + 1), j + 1 < ts.n_ct, ts.cs.len);
+    if constexpr (MASK_NEXT) w.mask(s_nxt, ts.kbase(j + 1), j + 1 < ts.n_ct, ts.clen(j + 1));
     w.rescale(w.row_max(s_nxt));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
@@ -857,26 +883,26 @@ bool attn_direct_ok(bool fp8_cross, bool fp8_self, float k_scale, float v_scale)
   return !(fp8_cross || fp8_self) || (k_scale == 1.0f && v_scale == 1.0f);
 }
 
-template <bool FC, bool FS, bool PACK>
+template <bool FC, bool FS, bool PACK, bool L2>
 static hipError_t launch_direct(const AttnParams& p, int group, dim3 gr, hipStream_t s) {
   const dim3 blk(PACK ? 64 : 256);
   switch (group) {
-    case 1: attn_direct_kernel<1, FC, FS, PACK><<<gr, blk, 0, s>>>(p); break;
-    case 2: attn_direct_kernel<2, FC, FS, PACK><<<gr, blk, 0, s>>>(p); break;
-    case 4: attn_direct_kernel<4, FC, FS, PACK><<<gr, blk, 0, s>>>(p); break;
-    case 8: attn_direct_kernel<8, FC, FS, PACK><<<gr, dim3(PACK ? 64 : 512), 0, s>>>(p); break;
+    case 1: attn_direct_kernel<1, FC, FS, PACK, L2><<<gr, blk, 0, s>>>(p); break;
+    case 2: attn_direct_kernel<2, FC, FS, PACK, L2><<<gr, blk, 0, s>>>(p); break;
+    case 4: attn_direct_kernel<4, FC, FS, PACK, L2><<<gr, blk, 0, s>>>(p); break;
+    case 8: attn_direct_kernel<8, FC, FS, PACK, L2><<<gr, dim3(PACK ? 64 : 512), 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <bool PACK>
+template <bool PACK, bool L2>
 static hipError_t launch_direct_fmt(const AttnParams& p, int group, bool fp8_cross, bool fp8_self,
                                     dim3 gr, hipStream_t s) {
-  if (fp8_cross && fp8_self) return launch_direct<true, true, PACK>(p, group, gr, s);
-  if (fp8_cross) return launch_direct<true, false, PACK>(p, group, gr, s);
-  if (fp8_self) return launch_direct<false, true, PACK>(p, group, gr, s);
-  return launch_direct<false, false, PACK>(p, group, gr, s);
+  if (fp8_cross && fp8_self) return launch_direct<true, true, PACK, L2>(p, group, gr, s);
+  if (fp8_cross) return launch_direct<true, false, PACK, L2>(p, group, gr, s);
+  if (fp8_self) return launch_direct<false, true, PACK, L2>(p, group, gr, s);
+  return launch_direct<false, false, PACK, L2>(p, group, gr, s);
 }
 
 hipError_t launch_attn_bf16(const AttnParams& p, int group, bool fp8_cross, bool fp8_self, bool packed,
@@ -889,8 +915,11 @@ hipError_t launch_attn_bf16(const AttnParams& p, int group, bool fp8_cross, bool
   const bool direct = attn_direct_ok(fp8_cross, fp8_self, p.k_scale, p.v_scale);
   if (packed && !direct) return hipErrorInvalidValue;      // packed tiles need the direct kernel
   if (direct) {
-    return packed ? launch_direct_fmt<true>(p, group, fp8_cross, fp8_self, gr, s)
-                  : launch_direct_fmt<false>(p, group, fp8_cross, fp8_self, gr, s);
+    if (p.two_level)
+      return packed ? launch_direct_fmt<true, true>(p, group, fp8_cross, fp8_self, gr, s)
+                    : launch_direct_fmt<false, true>(p, group, fp8_cross, fp8_self, gr, s);
+    return packed ? launch_direct_fmt<true, false>(p, group, fp8_cross, fp8_self, gr, s)
+                  : launch_direct_fmt<false, false>(p, group, fp8_cross, fp8_self, gr, s);
   }
   switch (group) {
     case 1: attn_bf16_kernel<1><<<gr, dim3(256), 0, s>>>(p); break;

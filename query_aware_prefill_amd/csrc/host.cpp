@@ -369,6 +369,74 @@ quail_status build_multiplan(const std::vector<size_t>& slab, const std::vector<
   return QUAIL_OK;
 }
 
+// ---------------------------------------------------------------------------
+// radix index over suffix token sequences (shared-prefix grouping)
+// ---------------------------------------------------------------------------
+// Sequence i = tokens[starts[i] .. starts[i] + lens[i]) with key keys[i]
+// (the anchor it continues; negative = not grouped). The sequences are sorted
+// by (key, tokens); in that order the longest common prefix of a run is the
+// minimum of its adjacent LCPs, and the sequences sharing their first
+// min_len tokens form one contiguous run -- the subtrees of the per-key radix
+// tree at depth min_len. A run of two or more becomes a node whose prefix is
+// the run's common prefix, cut so every member keeps at least one token.
+// Nodes are numbered by their smallest member. Returns the node count.
+int32_t prefix_groups(int32_t n, const int32_t* tokens, const int32_t* starts, const int32_t* lens,
+                      const int32_t* keys, int32_t min_len, int32_t* group_of, int32_t* node_first,
+                      int32_t* node_len) {
+  auto key = [&](int32_t i) { return keys ? keys[i] : 0; };
+  std::vector<int32_t> cand;
+  for (int32_t i = 0; i < n; ++i) {
+    group_of[i] = -1;
+    if (key(i) >= 0 && lens[i] > min_len) cand.push_back(i);
+  }
+  auto lcp = [&](int32_t x, int32_t y) {
+    const int32_t m = std::min(lens[x], lens[y]);
+    const int32_t* a = tokens + starts[x];
+    const int32_t* b = tokens + starts[y];
+    int32_t k = 0;
+    while (k < m && a[k] == b[k]) ++k;
+    return k;
+  };
+  std::sort(cand.begin(), cand.end(), [&](int32_t x, int32_t y) {
+    if (key(x) != key(y)) return key(x) < key(y);
+    const int32_t k = lcp(x, y);
+    if (k < lens[x] && k < lens[y]) return tokens[starts[x] + k] < tokens[starts[y] + k];
+    if (lens[x] != lens[y]) return lens[x] < lens[y];
+    return x < y;
+  });
+  std::vector<std::pair<int32_t, int32_t>> nodes;   // (smallest member, prefix length)
+  std::vector<std::vector<int32_t>> members;
+  for (size_t i = 0; i < cand.size();) {
+    size_t j = i + 1;
+    int32_t run_lcp = INT32_MAX;
+    while (j < cand.size() && key(cand[j]) == key(cand[i])) {
+      const int32_t l = lcp(cand[j - 1], cand[j]);
+      if (l < min_len) break;
+      run_lcp = std::min(run_lcp, l);
+      ++j;
+    }
+    if (j - i >= 2) {
+      int32_t shortest = INT32_MAX, first = INT32_MAX;
+      for (size_t k = i; k < j; ++k) {
+        shortest = std::min(shortest, lens[cand[k]]);
+        first = std::min(first, cand[k]);
+      }
+      nodes.push_back({first, std::min(run_lcp, shortest - 1)});
+      members.emplace_back(cand.begin() + i, cand.begin() + j);
+    }
+    i = j;
+  }
+  std::vector<int32_t> idx(nodes.size());
+  std::iota(idx.begin(), idx.end(), 0);
+  std::sort(idx.begin(), idx.end(), [&](int32_t x, int32_t y) { return nodes[x].first < nodes[y].first; });
+  for (size_t r = 0; r < idx.size(); ++r) {
+    node_first[r] = nodes[idx[r]].first;
+    node_len[r] = nodes[idx[r]].second;
+    for (int32_t m : members[idx[r]]) group_of[m] = (int32_t)r;
+  }
+  return (int32_t)nodes.size();
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -393,6 +461,11 @@ struct quail_ctx {
     size_t off = 0, bytes = 0;
     int32_t len = 0, lapad = 0;
     int64_t uses = 0;
+    // two-level cascade: a shared-prefix node continues anchor slot `parent`
+    // at positions pos0.. (pos0 = the anchor's length) and holds one of the
+    // anchor's uses until it is evicted; `held` counts such holds on an anchor
+    int32_t parent = -1, pos0 = 0;
+    int64_t held = 0;
   };
   std::vector<Slot> slots;
   std::vector<int32_t> free_slots;
@@ -446,6 +519,14 @@ struct quail_ctx {
     s.gen++;
     free_slots.push_back(slot);
     evictions++;
+    const int32_t par = s.parent;
+    s.parent = -1;
+    s.held = 0;
+    if (par >= 0) {   // a prefix node spends the anchor use it held
+      Slot& ps = slots[par];
+      ps.held--;
+      if (--ps.uses == 0) evict(par);
+    }
   }
 };
 
@@ -473,6 +554,8 @@ quail_status ensure_rope(quail_ctx* c, hipStream_t s) {
 // One batch of token rows through the decoder stack.
 struct Batch {
   bool anchor_mode = false;
+  bool has_parent = false;                  // anchor_mode: prefix nodes (cross = their anchor's slab)
+  bool two_level = false;                   // some tile reads a prefix node as cross2
   bool packed = false;                      // attention tiles are packed (one wave each)
   int32_t n_tok = 0;
   std::vector<int32_t> tok_src, pos, seg_lo, kv_lapad;
@@ -566,10 +649,12 @@ quail_status run_batch(quail_ctx* c, const Batch& b, const int32_t* tokens, uint
     ap.hq = Hq; ap.hkv = Hkv;
     ap.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)kHeadDim));
     ap.k_scale = cf.k_scale; ap.v_scale = cf.v_scale;
+    ap.two_level = b.two_level;
     // anchor batches attend over their own slab (self source); join batches
     // read the anchor slab as the cross source and bf16 suffix K/V as self
     const bool slab_fp8 = cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3;
-    HIP_TRY(launch_attn_bf16(ap, G, !b.anchor_mode && slab_fp8, b.anchor_mode && slab_fp8, b.packed, s));
+    HIP_TRY(launch_attn_bf16(ap, G, (!b.anchor_mode || b.has_parent) && slab_fp8, b.anchor_mode && slab_fp8,
+                             b.packed, s));
 
     GemmParams go{};
     go.A = obuf; go.lda = (int64_t)Hq * kHeadDim; go.B = lw.w_o; go.scale = lw.s_o;
@@ -604,6 +689,32 @@ quail_status run_batch(quail_ctx* c, const Batch& b, const int32_t* tokens, uint
   return QUAIL_OK;
 }
 
+// Append the KV source of a slab (K and V of layer 0; run_batch adds the
+// layer stride).
+void push_slab_src(quail_ctx* c, Batch& b, const quail_ctx::Slot& sl) {
+  const quail_model_config& cf = c->cfg;
+  const size_t esz = kv_elem_bytes(cf);
+  KVSrc ks{};
+  ks.k = c->pool + sl.off;
+  ks.v = c->pool + sl.off + (size_t)cf.n_kv_heads * sl.lapad * kHeadDim * esz;
+  ks.tok_stride = kHeadDim;
+  ks.head_stride = (int64_t)sl.lapad * kHeadDim;
+  ks.len = sl.len;
+  ks.fp8 = cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3;
+  b.srcs.push_back(ks);
+  b.src_layer_stride.push_back((int64_t)2 * cf.n_kv_heads * sl.lapad * kHeadDim);
+}
+
+// The batch's source index of slab `slot`, added on first use.
+int32_t slab_src(quail_ctx* c, Batch& b, int32_t slot, std::unordered_map<int32_t, int32_t>& src_of) {
+  auto it = src_of.find(slot);
+  if (it != src_of.end()) return it->second;
+  const int32_t idx = (int32_t)b.srcs.size();
+  push_slab_src(c, b, c->slots[slot]);
+  src_of[slot] = idx;
+  return idx;
+}
+
 quail_status check_offsets(int32_t n, const int32_t* off, int32_t lo, int32_t hi, const char* what) {
   if (n < 0) return fail(QUAIL_E_INVAL, "%s: negative count", what);
   if (n > 0 && !off) return fail(QUAIL_E_INVAL, "%s: offsets are NULL", what);
@@ -619,9 +730,13 @@ quail_status check_offsets(int32_t n, const int32_t* off, int32_t lo, int32_t hi
 hipStream_t as_stream(quail_stream s) { return reinterpret_cast<hipStream_t>(s); }
 
 // Anchor prefill core: anchor a = tokens[starts[a] .. starts[a] + lens[a]).
+// With `parents`, entry a is a shared-prefix node continuing anchor slot
+// parents[a]: its tokens sit at positions La.. and attend to the whole anchor
+// (cross) and causally to themselves (its own slab); the caller has checked
+// that each parent has a use to spare per node.
 quail_status anchor_core(quail_ctx* c, int32_t n, const int32_t* tokens, const int32_t* starts,
                          const int32_t* lens, const int32_t* n_uses, const int64_t* anchor_ids,
-                         quail_anchor* out, hipStream_t s) {
+                         quail_anchor* out, hipStream_t s, const int32_t* parents = nullptr) {
   if (!n_uses || !out) return fail(QUAIL_E_INVAL, "n_uses and out are required");
   if (!tokens) return fail(QUAIL_E_INVAL, "tokens is NULL");
   for (int32_t a = 0; a < n; ++a)
@@ -653,6 +768,10 @@ quail_status anchor_core(quail_ctx* c, int32_t n, const int32_t* tokens, const i
     sl.len = lens[a];
     sl.lapad = pad_len(sl.len);
     sl.uses = n_uses[a];
+    sl.held = 0;
+    sl.parent = parents ? parents[a] : -1;
+    sl.pos0 = parents ? c->slots[parents[a]].len : 0;
+    if (parents) c->slots[parents[a]].held++;
     slot_of[a] = slot;
     out[a] = ((int64_t)sl.gen << 32) | (uint32_t)slot;
     c->resident += sl.bytes;
@@ -684,35 +803,31 @@ quail_status anchor_core(quail_ctx* c, int32_t n, const int32_t* tokens, const i
       ++a1;
     }
     // packed tiles when every anchor is that short (see attn_tile_tokens)
+    b.has_parent = parents != nullptr;
     b.packed = max_len <= attn_tile_tokens(G, true) &&
-               attn_direct_ok(false, slab_fp8, cf.k_scale, cf.v_scale);
+               attn_direct_ok(b.has_parent && slab_fp8, slab_fp8, cf.k_scale, cf.v_scale);
     const int TQ = attn_tile_tokens(G, b.packed);
+    std::unordered_map<int32_t, int32_t> parent_src;
     for (int32_t a = a0; a < a1; ++a) {
       if (n_uses[a] == 0) continue;
       const quail_ctx::Slot& sl = c->slots[slot_of[a]];
       const int32_t r0 = b.n_tok;
+      const int32_t cross = sl.parent >= 0 ? slab_src(c, b, sl.parent, parent_src) : -1;
       const int32_t src = (int32_t)b.srcs.size();
-      KVSrc ks{};
-      ks.k = c->pool + sl.off;
-      ks.v = c->pool + sl.off + (size_t)cf.n_kv_heads * sl.lapad * kHeadDim * esz;
-      ks.tok_stride = kHeadDim;
-      ks.head_stride = (int64_t)sl.lapad * kHeadDim;
-      ks.len = sl.len;
-      ks.fp8 = cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3;
-      b.srcs.push_back(ks);
-      b.src_layer_stride.push_back((int64_t)2 * cf.n_kv_heads * sl.lapad * kHeadDim);
+      push_slab_src(c, b, sl);
       for (int32_t t = 0; t < sl.len; ++t) {
         b.tok_src.push_back(starts[a] + t);
-        b.pos.push_back(t);
+        b.pos.push_back(sl.pos0 + t);
         b.seg_lo.push_back(0);
         b.kv_row.push_back((int64_t)(sl.off / esz) + (int64_t)t * kHeadDim);
         b.kv_lapad.push_back(sl.lapad);
       }
       for (int32_t t0 = 0; t0 < sl.len; t0 += TQ) {
         AttnTile tl{};
+        tl.cross2 = -1;
         tl.q0 = r0 + t0;
         tl.nq = std::min(TQ, sl.len - t0);
-        tl.cross = -1;
+        tl.cross = cross;
         tl.self = src;
         tl.self_qbase = t0;
         tl.self_k0 = 0;
@@ -750,6 +865,22 @@ quail_status quail_workspace_bytes(const quail_model_config* cfg, int32_t max_ba
   if (quail_status st = check_cfg(cfg)) return st;
   if (!out || max_batch_tokens < 1) return fail(QUAIL_E_INVAL, "max_batch_tokens >= 1 and out required");
   *out = ws_layout(*cfg, max_batch_tokens).total;
+  return QUAIL_OK;
+}
+
+quail_status quail_prefix_groups(int32_t n, const int32_t* tokens, const int32_t* offsets, const int32_t* keys,
+                                 int32_t min_len, int32_t* group_of, int32_t* node_first, int32_t* node_len,
+                                 int32_t* n_nodes) {
+  if (!n_nodes) return fail(QUAIL_E_INVAL, "n_nodes is NULL");
+  *n_nodes = 0;
+  if (n == 0) return QUAIL_OK;
+  if (min_len < 1) return fail(QUAIL_E_INVAL, "min_len must be at least 1");
+  if (!tokens || !group_of || !node_first || !node_len)
+    return fail(QUAIL_E_INVAL, "tokens, group_of, node_first and node_len are required");
+  if (quail_status st = check_offsets(n, offsets, 1, INT32_MAX, "sequence")) return st;
+  std::vector<int32_t> starts(offsets, offsets + n), lens(n);
+  for (int32_t i = 0; i < n; ++i) lens[i] = offsets[i + 1] - offsets[i];
+  *n_nodes = prefix_groups(n, tokens, starts.data(), lens.data(), keys, min_len, group_of, node_first, node_len);
   return QUAIL_OK;
 }
 
@@ -884,6 +1015,9 @@ quail_status quail_anchor_release(quail_ctx* c, quail_anchor h) {
   if (!c) return fail(QUAIL_E_INVAL, "ctx is NULL");
   quail_ctx::Slot* s = c->lookup(h);
   if (!s) return fail(QUAIL_E_STALE, "anchor handle %lld is stale", (long long)h);
+  if (s->held > 0)
+    return fail(QUAIL_E_INVAL, "anchor handle %lld still has %lld live prefix nodes", (long long)h,
+                (long long)s->held);
   c->evict((int32_t)(h & 0xFFFFFFFF));
   return QUAIL_OK;
 }
@@ -918,6 +1052,33 @@ quail_status quail_anchor_prefill(quail_ctx* c, int32_t n, const int32_t* tokens
                      as_stream(stream));
 }
 
+quail_status quail_prefix_prefill(quail_ctx* c, int32_t n, const quail_anchor* parent, const int32_t* tokens,
+                                  const int32_t* offsets, const int32_t* n_uses, quail_anchor* out,
+                                  quail_stream stream) {
+  if (!c) return fail(QUAIL_E_INVAL, "ctx is NULL");
+  if (n == 0) return QUAIL_OK;
+  if (!parent || !n_uses || !out) return fail(QUAIL_E_INVAL, "parent, n_uses and out are required");
+  if (quail_status st = check_offsets(n, offsets, 1, c->T, "prefix node")) return st;
+  std::vector<int32_t> starts(n), lens(n), par(n);
+  std::unordered_map<int32_t, int64_t> need;
+  for (int32_t a = 0; a < n; ++a) {
+    starts[a] = offsets[a];
+    lens[a] = offsets[a + 1] - offsets[a];
+    quail_ctx::Slot* ps = c->lookup(parent[a]);
+    if (!ps) return fail(QUAIL_E_STALE, "node %d: anchor handle %lld is stale", a, (long long)parent[a]);
+    if (ps->parent >= 0)
+      return fail(QUAIL_E_INVAL, "node %d: its anchor is itself a prefix node (one shared-prefix level)", a);
+    if (n_uses[a] < 0) return fail(QUAIL_E_INVAL, "node %d: negative use count", a);
+    par[a] = (int32_t)(parent[a] & 0xFFFFFFFF);
+    if (n_uses[a] > 0 && ++need[par[a]] > ps->uses - ps->held)
+      return fail(QUAIL_E_STALE, "node %d: its anchor has no declared use to spare", a);
+    if ((int64_t)ps->len + lens[a] + 1 > max_pos(c->cfg))
+      return fail(QUAIL_E_INVAL, "node %d: anchor + prefix leaves no position for a suffix token", a);
+  }
+  return anchor_core(c, n, tokens, starts.data(), lens.data(), n_uses, nullptr, out, as_stream(stream),
+                     par.data());
+}
+
 }  // extern "C"
 
 namespace {
@@ -939,10 +1100,10 @@ quail_status join_core(quail_ctx* c, int32_t n, const quail_anchor* ha, const in
     quail_ctx::Slot* sl = c->lookup(ha[i]);
     if (!sl) return fail(QUAIL_E_STALE, "pair %d: anchor handle %lld is stale", i, (long long)ha[i]);
     slot[i] = (int32_t)(ha[i] & 0xFFFFFFFF);
-    if (++need[slot[i]] > sl->uses)
+    if (++need[slot[i]] > sl->uses - sl->held)
       return fail(QUAIL_E_STALE, "pair %d: anchor used more often than its declared %lld uses", i,
-                  (long long)sl->uses);
-    if (sl->len + lens[i] > max_pos(cf))
+                  (long long)(sl->uses - sl->held));
+    if (sl->pos0 + sl->len + lens[i] > max_pos(cf))
       return fail(QUAIL_E_INVAL, "pair %d: anchor + suffix exceeds the position range", i);
   }
   if (quail_status st = ensure_rope(c, s)) return st;
@@ -992,25 +1153,17 @@ quail_status join_core(quail_ctx* c, int32_t n, const quail_anchor* ha, const in
       // a run of pairs with the same anchor
       int32_t j = i;
       while (j < p1 && slot[order[j]] == slot[order[i]]) ++j;
-      int32_t cross = -1, la = 0;
+      // cross: the anchor's slab; for a shared-prefix node, the node's
+      // anchor and then the node's own slab (cross2)
+      int32_t cross = -1, cross2 = -1, la = 0;
       if (slot[order[i]] >= 0) {
         const quail_ctx::Slot& sl = c->slots[slot[order[i]]];
-        la = sl.len;
-        auto it = src_of_slot.find(slot[order[i]]);
-        if (it == src_of_slot.end()) {
-          KVSrc ks{};
-          ks.k = c->pool + sl.off;
-          ks.v = c->pool + sl.off + (size_t)cf.n_kv_heads * sl.lapad * kHeadDim * esz;
-          ks.tok_stride = kHeadDim;
-          ks.head_stride = (int64_t)sl.lapad * kHeadDim;
-          ks.len = sl.len;
-          ks.fp8 = cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3;
-          cross = (int32_t)b.srcs.size();
-          b.srcs.push_back(ks);
-          b.src_layer_stride.push_back((int64_t)2 * cf.n_kv_heads * sl.lapad * kHeadDim);
-          src_of_slot[slot[order[i]]] = cross;
+        la = sl.pos0 + sl.len;
+        if (sl.parent >= 0) {
+          cross = slab_src(c, b, sl.parent, src_of_slot);
+          cross2 = slab_src(c, b, slot[order[i]], src_of_slot);
         } else {
-          cross = it->second;
+          cross = slab_src(c, b, slot[order[i]], src_of_slot);
         }
       }
       const int32_t g0 = b.n_tok;
@@ -1030,6 +1183,8 @@ quail_status join_core(quail_ctx* c, int32_t n, const quail_anchor* ha, const in
       }
       for (int32_t t0 = g0; t0 < b.n_tok; t0 += TQ) {
         AttnTile tl{};
+        tl.cross2 = cross2;
+        b.two_level |= cross2 >= 0;
         tl.q0 = t0;
         tl.nq = std::min(TQ, b.n_tok - t0);
         tl.cross = cross;
@@ -1120,13 +1275,20 @@ static quail_status run_step_with_head(quail_ctx* c, int32_t np, const quail_anc
   return QUAIL_OK;
 }
 
-quail_status quail_join_run(quail_ctx* c, int32_t n_anchors, const int32_t* a_tokens,
-                            const int32_t* a_offsets, int32_t n_pairs, const int32_t* pair_anchor,
-                            const int32_t* s_tokens, const int32_t* s_offsets, uint8_t true_mask,
-                            float* logits, uint8_t* token, uint8_t* decision, quail_stream stream) {
+// quail_join_run, and with s_tokens_host / min_shared > 0 the same plan with
+// the suffixes of each step that share a prefix of at least min_shared tokens
+// (under one anchor) grouped into prefix nodes: each node is prefilled once
+// after its anchor, and its members run only their remaining tokens against
+// anchor + node + themselves (two-level cascade).
+static quail_status join_run_core(quail_ctx* c, int32_t n_anchors, const int32_t* a_tokens,
+                                  const int32_t* a_offsets, int32_t n_pairs, const int32_t* pair_anchor,
+                                  const int32_t* s_tokens, const int32_t* s_offsets,
+                                  const int32_t* s_tokens_host, int32_t min_shared, uint8_t true_mask,
+                                  float* logits, uint8_t* token, uint8_t* decision, quail_stream stream) {
   if (!c) return fail(QUAIL_E_INVAL, "ctx is NULL");
   if (n_pairs == 0) return QUAIL_OK;
   if (!decision) return fail(QUAIL_E_INVAL, "decision is required");
+  if (min_shared > 0 && !s_tokens_host) return fail(QUAIL_E_INVAL, "s_tokens_host is required for sharing");
   const int32_t amax = std::min(c->cfg.max_anchor_len, c->T);
   if (quail_status st = check_offsets(n_anchors, a_offsets, 1, amax, "anchor")) return st;
   if (quail_status st = check_offsets(n_pairs, s_offsets, 1, std::min(c->cfg.max_suffix_len, c->T), "pair"))
@@ -1145,9 +1307,43 @@ quail_status quail_join_run(quail_ctx* c, int32_t n_anchors, const int32_t* a_to
   Plan plan;
   if (quail_status st = build_plan(slab, n_pairs, pair_anchor, plen.data(), free_bytes, c->T, plan))
     return st;
+  // shared-prefix nodes per step (plan positions of their members)
+  struct Node { int32_t anchor, first, len; std::vector<int32_t> members; };
+  const int32_t n_steps = (int32_t)plan.bounds.size() - 1;
+  std::vector<std::vector<Node>> step_nodes(n_steps);
+  std::vector<char> grouped(n_pairs, 0);
+  if (min_shared > 0) {
+    for (int32_t st = 0; st < n_steps; ++st) {
+      const int32_t b0 = plan.bounds[st], np = plan.bounds[st + 1] - b0;
+      std::vector<int32_t> starts(np), lens(np), keys(np), gof(np), nf(np), nl(np);
+      for (int32_t k = 0; k < np; ++k) {
+        const int32_t pi = plan.order[b0 + k];
+        starts[k] = s_offsets[pi];
+        lens[k] = plen[pi];
+        keys[k] = pair_anchor[pi];
+      }
+      const int32_t nn = prefix_groups(np, s_tokens_host, starts.data(), lens.data(), keys.data(), min_shared,
+                                       gof.data(), nf.data(), nl.data());
+      step_nodes[st].resize(nn);
+      for (int32_t q = 0; q < nn; ++q) {
+        const int32_t pi = plan.order[b0 + nf[q]];
+        step_nodes[st][q].anchor = pair_anchor[pi];
+        step_nodes[st][q].first = s_offsets[pi];
+        step_nodes[st][q].len = nl[q];
+      }
+      for (int32_t k = 0; k < np; ++k)
+        if (gof[k] >= 0) {
+          step_nodes[st][gof[k]].members.push_back(plan.order[b0 + k]);
+          grouped[plan.order[b0 + k]] = 1;
+        }
+    }
+  }
+  // an anchor's uses: its ungrouped pairs plus one per node under it
   std::vector<int32_t> uses(n_anchors, 0);
   for (int32_t i = 0; i < n_pairs; ++i)
-    if (pair_anchor[i] >= 0) uses[pair_anchor[i]]++;
+    if (pair_anchor[i] >= 0 && !grouped[i]) uses[pair_anchor[i]]++;
+  for (auto& sn : step_nodes)
+    for (auto& nd : sn) uses[nd.anchor]++;
   // anchors in order of first use along the plan
   std::vector<int32_t> first_use;
   {
@@ -1203,21 +1399,81 @@ quail_status quail_join_run(quail_ctx* c, int32_t n_anchors, const int32_t* a_to
         return r;
       for (size_t f = 0; f < batch.size(); ++f) handle[batch[f]] = hnd[f];
     }
-    const int32_t np = b1 - b0;
-    std::vector<quail_anchor> ha(np);
-    std::vector<int32_t> starts(np), lens(np), outmap(np);
-    for (int32_t k = 0; k < np; ++k) {
-      const int32_t pi = plan.order[b0 + k];
-      ha[k] = pair_anchor[pi] >= 0 ? handle[pair_anchor[pi]] : QUAIL_NO_ANCHOR;
-      starts[k] = s_offsets[pi];
-      lens[k] = plen[pi];
-      outmap[k] = pi;
+    std::vector<quail_anchor> ha;
+    std::vector<int32_t> starts, lens, outmap;
+    for (int32_t k = b0; k < b1; ++k) {
+      const int32_t pi = plan.order[k];
+      if (grouped[pi]) continue;
+      ha.push_back(pair_anchor[pi] >= 0 ? handle[pair_anchor[pi]] : QUAIL_NO_ANCHOR);
+      starts.push_back(s_offsets[pi]);
+      lens.push_back(plen[pi]);
+      outmap.push_back(pi);
     }
-    if (quail_status r = run_step_with_head(c, np, ha.data(), s_tokens, starts.data(), lens.data(),
-                                            outmap.data(), true_mask, logits, token, decision, s))
-      return r;
+    if (!ha.empty())
+      if (quail_status r = run_step_with_head(c, (int32_t)ha.size(), ha.data(), s_tokens, starts.data(),
+                                              lens.data(), outmap.data(), true_mask, logits, token, decision, s))
+        return r;
+    // shared-prefix nodes of this step, in chunks that fit half the free pool:
+    // prefill the chunk's nodes, then their members' remaining tokens
+    const std::vector<Node>& nodes = step_nodes[st];
+    for (size_t q0 = 0; q0 < nodes.size();) {
+      size_t fb = 0;
+      for (auto& f : c->free_list) fb = std::max(fb, f.second);
+      size_t q1 = q0, bytes = 0;
+      int32_t ntok = 0;
+      while (q1 < nodes.size()) {
+        const size_t nb = slab_bytes(c->cfg, nodes[q1].len);
+        if (q1 > q0 && (bytes + nb > fb / 2 || ntok + nodes[q1].len > c->T)) break;
+        bytes += nb;
+        ntok += nodes[q1].len;
+        ++q1;
+      }
+      const int32_t nn = (int32_t)(q1 - q0);
+      std::vector<int32_t> nst(nn), nln(nn), nnu(nn), npar(nn);
+      std::vector<quail_anchor> nh(nn);
+      for (int32_t q = 0; q < nn; ++q) {
+        const Node& nd = nodes[q0 + q];
+        nst[q] = nd.first;
+        nln[q] = nd.len;
+        nnu[q] = (int32_t)nd.members.size();
+        npar[q] = (int32_t)(handle[nd.anchor] & 0xFFFFFFFF);
+      }
+      if (quail_status r = anchor_core(c, nn, s_tokens, nst.data(), nln.data(), nnu.data(), nullptr, nh.data(), s,
+                                       npar.data()))
+        return r;
+      ha.clear(); starts.clear(); lens.clear(); outmap.clear();
+      for (int32_t q = 0; q < nn; ++q)
+        for (int32_t pi : nodes[q0 + q].members) {
+          ha.push_back(nh[q]);
+          starts.push_back(s_offsets[pi] + nodes[q0 + q].len);
+          lens.push_back(plen[pi] - nodes[q0 + q].len);
+          outmap.push_back(pi);
+        }
+      if (quail_status r = run_step_with_head(c, (int32_t)ha.size(), ha.data(), s_tokens, starts.data(),
+                                              lens.data(), outmap.data(), true_mask, logits, token, decision, s))
+        return r;
+      q0 = q1;
+    }
   }
   return QUAIL_OK;
+}
+
+quail_status quail_join_run(quail_ctx* c, int32_t n_anchors, const int32_t* a_tokens,
+                            const int32_t* a_offsets, int32_t n_pairs, const int32_t* pair_anchor,
+                            const int32_t* s_tokens, const int32_t* s_offsets, uint8_t true_mask,
+                            float* logits, uint8_t* token, uint8_t* decision, quail_stream stream) {
+  return join_run_core(c, n_anchors, a_tokens, a_offsets, n_pairs, pair_anchor, s_tokens, s_offsets, nullptr, 0,
+                       true_mask, logits, token, decision, stream);
+}
+
+quail_status quail_join_run_shared(quail_ctx* c, int32_t n_anchors, const int32_t* a_tokens,
+                                   const int32_t* a_offsets, int32_t n_pairs, const int32_t* pair_anchor,
+                                   const int32_t* s_tokens, const int32_t* s_offsets,
+                                   const int32_t* s_tokens_host, int32_t min_shared, uint8_t true_mask,
+                                   float* logits, uint8_t* token, uint8_t* decision, quail_stream stream) {
+  if (min_shared < 1) return fail(QUAIL_E_INVAL, "min_shared must be at least 1");
+  return join_run_core(c, n_anchors, a_tokens, a_offsets, n_pairs, pair_anchor, s_tokens, s_offsets,
+                       s_tokens_host, min_shared, true_mask, logits, token, decision, stream);
 }
 
 quail_status quail_multijoin_run(quail_ctx* c, int32_t n_anchors, const int32_t* a_tokens,
@@ -1413,6 +1669,7 @@ quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t 
     const int32_t t_end = s_off[s1];
     for (int32_t t0 = s_off[s0]; t0 < t_end; t0 += TQ) {
       AttnTile tl{};
+      tl.cross2 = -1;
       tl.q0 = t0; tl.nq = std::min(TQ, t_end - t0);
       tl.cross = s_anchor[s0] >= 0 ? 1 + s_anchor[s0] : -1;
       tl.self = 0; tl.self_qbase = t0; tl.self_k0 = seg[t0];

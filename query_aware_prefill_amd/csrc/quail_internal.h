@@ -24,15 +24,18 @@ struct KVSrc {
 
 // One attention work item: query tokens [q0, q0+nq) against
 //   - every key of source `cross` (no mask), then
+//   - every key of source `cross2` (no mask; the shared-prefix level of a
+//     two-level cascade: anchor -> shared suffix prefix -> suffix), then
 //   - keys [self_k0, self_qbase + row] of source `self` (causal), where row is
 //     the query's offset from q0, and keys below seg_lo[q0 + row] are hidden.
-// Either source may be -1 (absent).
+// Any source may be -1 (absent); cross2 only together with cross.
 struct AttnTile {
   int32_t q0, nq;
   int32_t cross;
   int32_t self;
   int32_t self_qbase;
   int32_t self_k0;
+  int32_t cross2;
 };
 
 struct AttnParams {
@@ -48,6 +51,7 @@ struct AttnParams {
   int32_t hq, hkv;
   float scale_log2;         // softmax scale * log2(e)
   float k_scale, v_scale;   // fp8 dequantisation scales
+  int32_t two_level;        // some tile has a cross2 source (selects that kernel variant)
 };
 
 // fp32 reference-precision cascade (small head dims, explicit two partials + merge)

@@ -281,3 +281,62 @@ def test_cascade_attn_argument_checks():
     # workspace too small
     assert lib.quail_cascade_attn(B.DTYPE_BF16, 4, 2, 128, 0.1, 1, fake, fake, aop, 1, sap, fake, fake,
                                   fake, sop, fake, None, fake, 16, None) == B.E_NOMEM
+
+
+def _prefix_cases():
+    from tests.test_oracle_prefix import _cases
+    return list(_cases())
+
+
+@pytest.mark.parametrize("case", _prefix_cases())
+def test_prefix_groups_match_oracle(case):
+    """The library's radix grouping (sorted order + adjacent LCPs) equals the
+    oracle's (hash of the first min_len tokens + token-by-token LCP)."""
+    from oracle import prefix as OPX
+    seqs, keys, m = case
+    off = np.zeros(len(seqs) + 1, np.int32)
+    off[1:] = np.cumsum([len(s) for s in seqs])
+    toks = np.array([t for s in seqs for t in s], np.int32)
+    g, f, ln = B.quail_prefix_groups(toks, off, keys, m)
+    rg, rf, rl = OPX.prefix_groups_reference(seqs, keys, m)
+    assert np.array_equal(g, rg) and np.array_equal(f, rf) and np.array_equal(ln, rl)
+
+
+def test_prefix_groups_argument_checks():
+    lib = B.load()
+    toks, tp = _i32([1, 2, 3, 4])
+    g, gp = _i32([0, 0])
+    nn = C.c_int32(7)
+    off, offp = _i32([0, 2, 4])
+    assert lib.quail_prefix_groups(2, tp, offp, None, 0, gp, gp, gp, C.byref(nn)) == B.E_INVAL
+    assert lib.quail_prefix_groups(2, tp, offp, None, 1, None, gp, gp, C.byref(nn)) == B.E_INVAL
+    for offs in ([0, 3, 2], [0, 0, 4], [-1, 2, 4]):
+        off, offp = _i32(offs)
+        assert lib.quail_prefix_groups(2, tp, offp, None, 1, gp, gp, gp, C.byref(nn)) == B.E_INVAL, offs
+    assert lib.quail_prefix_groups(0, None, None, None, 1, None, None, None, C.byref(nn)) == B.OK
+    assert nn.value == 0
+
+
+def test_prefix_prefill_and_shared_run_reject_bad_arguments():
+    fc = _FakeCtx(pool_bytes=1 << 26)
+    nu, nup = _i32([1])
+    out, outp = _i64([0])
+    off, offp = _i32([0, 4])
+    for h in (5, (3 << 32) | 0, B.NO_ANCHOR):       # no live anchor behind these handles
+        pa, pap = _i64([h])
+        st = fc.lib.quail_prefix_prefill(fc.h, 1, pap, 0x7F0000000000, offp, nup, outp, None)
+        assert st == B.E_STALE, h
+    pa, pap = _i64([0])
+    assert fc.lib.quail_prefix_prefill(fc.h, 1, None, 0x7F0000000000, offp, nup, outp, None) == B.E_INVAL
+    off0, off0p = _i32([0, 0])
+    assert fc.lib.quail_prefix_prefill(fc.h, 1, pap, 0x7F0000000000, off0p, nup, outp, None) == B.E_INVAL
+    ao, aop = _i32([0, 8])
+    pa1, pa1p = _i32([0])
+    so, sop = _i32([0, 4])
+    sh, shp = _i32([1, 2, 3, 4])
+    dec = 0x7F0000000000
+    st = fc.lib.quail_join_run_shared(fc.h, 1, dec, aop, 1, pa1p, dec, sop, shp, 0, 0x0F, None, None, dec, None)
+    assert st == B.E_INVAL
+    st = fc.lib.quail_join_run_shared(fc.h, 1, dec, aop, 1, pa1p, dec, sop, None, 2, 0x0F, None, None, dec, None)
+    assert st == B.E_INVAL
+    fc.close()

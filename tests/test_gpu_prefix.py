@@ -1,0 +1,200 @@
+"""GPU parity of the two-level cascade (anchor -> shared suffix prefix ->
+suffix) against the oracle's per-pair monolithic forward: prefix-node
+prefill (slab contents), joins through node handles (packed and unpacked
+attention tiles, bf16 and E4M3 stores, unit and non-unit scales), residency
+of nodes and their anchors, handle errors, and the whole-join entry point
+with sharing against the one without."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import model as OM, prefix as OPX
+from tests.gpu_util import bf16_f64, decisions_agree, rel_inf, say, u16
+from tests.test_gpu_model import _fp8_codes_valid, _slab
+
+pytestmark = pytest.mark.gpu
+
+FAMILIES = [(1, 40, [5, 1, 33]), (2, 64, [17, 2]), (0, 3, [1, 4, 2]), (1, 2, [6]), (-1, 5, [3, 4]),
+            (2, 9, [3, 2])]
+
+
+@pytest.fixture(scope="module")
+def B():
+    import torch
+    assert torch.cuda.is_available()
+    from query_aware_prefill_amd import binding
+    binding.load()
+    return binding
+
+
+def _pack(tok, ranges):
+    off = np.zeros(len(ranges) + 1, np.int32)
+    off[1:] = np.cumsum([b - a for a, b in ranges])
+    return np.concatenate([tok[a:b] for a, b in ranges]).astype(np.int32), off
+
+
+@pytest.mark.parametrize("kv_fp8,k_scale,v_scale", [(False, 1.0, 1.0), (True, 1.0, 1.0), (True, 0.5, 2.0)])
+def test_two_level_cascade_model(B, kv_fp8, k_scale, v_scale):
+    import torch
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    shape = W.tiny_shape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                         intermediate=384, vocab=512, kv_fp8=kv_fp8, k_scale=k_scale, v_scale=v_scale)
+    wts = W.model_weights(shape, 7)
+    a_len = [1, 70, 130]
+    case = W.shared_prefix_case(7, shape.vocab, a_len, FAMILIES)
+    s_tok, s_off, pa = case["s_tok"], case["s_off"], case["pair_anchor"]
+    n = len(pa)
+    g, nfirst, nlen = B.quail_prefix_groups(s_tok, s_off, pa, 2)
+    seqs = [s_tok[s_off[i]:s_off[i + 1]] for i in range(n)]
+    rg, rf, rl = OPX.prefix_groups_reference(seqs, pa, 2)
+    assert np.array_equal(g, rg) and np.array_equal(nfirst, rf) and np.array_equal(nlen, rl)
+    nn = len(nfirst)
+    assert nn == 4      # families 0, 1, 2, 5; the lone pair and the filter rows stay ungrouped
+    node_anchor = pa[nfirst]
+    uses = np.zeros(3, np.int32)
+    for i in range(n):
+        if pa[i] >= 0 and g[i] < 0:
+            uses[pa[i]] += 1
+    for a in node_anchor:
+        uses[a] += 1
+    dm = DeviceModel(shape, wts, max_anchor_len=1024, max_suffix_len=256)
+    pool_bytes = sum(B.quail_anchor_bytes(dm.cfg, x) for x in a_len) + \
+        sum(B.quail_anchor_bytes(dm.cfg, int(x)) for x in nlen) + 4096
+    ctx = dm.context(pool_bytes, 512)
+    say("two-level: anchor prefill", "fp8" if kv_fp8 else "bf16", k_scale, v_scale)
+    handles = B.quail_anchor_prefill(ctx, to_device(case["a_tok"]), case["a_off"], uses)
+    # nodes: the short ones (packed tiles) and the rest, in two calls
+    node_tok, node_off = _pack(s_tok, [(s_off[f], s_off[f] + L) for f, L in zip(nfirst, nlen)])
+    members = np.array([np.sum(g == k) for k in range(nn)], np.int32)
+    nh = np.zeros(nn, np.int64)
+    for sel in (nlen <= 16, nlen > 16):
+        idx = np.flatnonzero(sel)
+        if len(idx) == 0:
+            continue
+        tk, of = _pack(node_tok, [(node_off[k], node_off[k + 1]) for k in idx])
+        say("two-level: prefix prefill", idx.tolist())
+        nh[idx] = B.quail_prefix_prefill(ctx, handles[node_anchor[idx]], to_device(tk), of, members[idx])
+    torch.cuda.synchronize()
+    # node slabs hold the K/V of positions La.. of the monolithic run
+    for k in range(nn):
+        a = int(node_anchor[k])
+        at = case["a_tok"][case["a_off"][a]:case["a_off"][a + 1]]
+        toks = np.concatenate([at, node_tok[node_off[k]:node_off[k + 1]]])
+        _, kv = OM.forward_tokens(toks, wts, shape, return_kv=True, fp8_kv_upto=len(toks) if kv_fp8 else 0)
+        for l in range(shape.n_layers):
+            kk, vv = _slab(ctx, nh[k], l, B, shape)
+            la = len(at)
+            if not kv_fp8:
+                assert rel_inf(kk, kv[l][0][la:]) <= 2e-2, (k, l, "K")
+                assert rel_inf(vv, kv[l][1][la:]) <= 2e-2, (k, l, "V")
+            else:
+                for got, stored, pre in ((kk, kv[l][0][la:], kv[l][2][la:]), (vv, kv[l][1][la:], kv[l][3][la:])):
+                    _fp8_codes_valid(got, stored, pre)
+    # an anchor with live nodes cannot be released; a node cannot be a parent
+    with pytest.raises(B.QuailError) as e:
+        B.quail_anchor_release(ctx, handles[1])
+    assert e.value.status == B.E_INVAL
+    with pytest.raises(B.QuailError) as e:
+        B.quail_prefix_prefill(ctx, [nh[0]], to_device(node_tok[:4]), [0, 4], [1])
+    assert e.value.status == B.E_INVAL
+    # joins: the members of the short nodes (few tokens per node: packed
+    # tiles), then everything else (node members and ungrouped pairs)
+    order_a = [i for i in range(n) if g[i] >= 0 and nlen[g[i]] <= 16 and
+               sum(s_off[j + 1] - s_off[j] - nlen[g[j]] for j in range(n) if g[j] == g[i]) <= 16]
+    order_b = [i for i in range(n) if i not in order_a]
+    h_last = torch.empty((n, shape.hidden), dtype=torch.int16, device="cuda")
+    for part in (order_a, order_b):
+        if not part:
+            continue
+        rng = [(s_off[i] + (nlen[g[i]] if g[i] >= 0 else 0), s_off[i + 1]) for i in part]
+        tk, of = _pack(s_tok, rng)
+        hp = [nh[g[i]] if g[i] >= 0 else (handles[pa[i]] if pa[i] >= 0 else B.NO_ANCHOR) for i in part]
+        hl = torch.empty((len(part), shape.hidden), dtype=torch.int16, device="cuda")
+        say("two-level: join", len(part), "pairs")
+        B.quail_join_prefill(ctx, hp, to_device(tk), of, hl)
+        h_last[torch.tensor(part, device="cuda")] = hl
+    assert len(order_a) >= 2
+    logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+    tok = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+    B.quail_head8(ctx, h_last, 0x0F, logits, tok, dec)
+    torch.cuda.synchronize()
+    hl = bf16_f64(u16(h_last))
+    ref_logits, ref_dec, ref_margin = [], [], []
+    for i in range(n):
+        a = int(pa[i])
+        at = case["a_tok"][case["a_off"][a]:case["a_off"][a + 1]] if a >= 0 else []
+        ref = OM.forward_pair(at, seqs[i], wts, shape, true_mask=0x0F,
+                              shared_len=int(nlen[g[i]]) if g[i] >= 0 else 0)
+        assert rel_inf(hl[i], ref["h_last"]) <= 2e-2, (i, rel_inf(hl[i], ref["h_last"]))
+        ref_logits.append(ref["logits"]); ref_dec.append(ref["decision"]); ref_margin.append(ref["margin"])
+    ref_logits = np.array(ref_logits)
+    assert rel_inf(logits.cpu().numpy(), ref_logits) <= 2e-2
+    ok, _ = decisions_agree(dec.cpu().numpy(), ref_dec, ref_margin, 2e-2 * np.max(np.abs(ref_logits)))
+    assert ok
+    st = B.quail_pool_stats(ctx)
+    assert st["prefills"] == 3 + nn and st["evictions"] == 3 + nn and st["resident"] == 0
+    with pytest.raises(B.QuailError) as e:
+        B.quail_join_prefill(ctx, [nh[0]], to_device(node_tok[:2]), [0, 2], h_last[:1])
+    assert e.value.status == B.E_STALE
+
+
+def test_join_run_shared_matches_join_run(B):
+    """Whole join with and without sharing on the same inputs: the same
+    logits up to rounding, the oracle's decisions, node prefills counted, no
+    regret, nothing left resident."""
+    import torch
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    shape = W.tiny_shape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                         intermediate=384, vocab=512)
+    wts = W.model_weights(shape, 9)
+    r = np.random.default_rng(9)
+    a_len = r.integers(20, 120, 4).tolist()
+    fam = []
+    for f in range(10):
+        fam.append((int(r.integers(0, 4)), int(r.integers(1, 50)),
+                    r.integers(1, 20, int(r.integers(1, 5))).tolist()))
+    fam.append((-1, 6, [5, 7]))
+    case = W.shared_prefix_case(9, shape.vocab, a_len, fam)
+    n = len(case["pair_anchor"])
+    dm = DeviceModel(shape, wts, max_anchor_len=1024, max_suffix_len=256)
+    ctx = dm.context(64 << 20, 128)           # small batches: several plan steps
+    a_tok, s_tok = to_device(case["a_tok"]), to_device(case["s_tok"])
+    outs = []
+    for shared in (False, True):
+        logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+        dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+        say("join_run", "shared" if shared else "plain", n, "pairs")
+        if shared:
+            B.quail_join_run_shared(ctx, a_tok, case["a_off"], case["pair_anchor"], s_tok, case["s_off"],
+                                    case["s_tok"], 4, 0x0F, logits, None, dec)
+        else:
+            B.quail_join_run(ctx, a_tok, case["a_off"], case["pair_anchor"], s_tok, case["s_off"], 0x0F,
+                             logits, None, dec)
+        torch.cuda.synchronize()
+        outs.append((logits.cpu().numpy(), dec.cpu().numpy(), B.quail_pool_stats(ctx)))
+    (l0, d0, s0), (l1, d1, s1) = outs
+    assert rel_inf(l1, l0) <= 2e-2
+    used = len({a for a in case["pair_anchor"] if a >= 0})
+    assert s0["prefills"] == used and s0["regret_tokens"] == 0
+    # nodes: the oracle's grouping of each plan step's pairs (plan from the
+    # library's builder, pool fully free as at the shared run's start)
+    order, bounds, _ = B.quail_plan_build(dm.cfg, 64 << 20, 128, a_len, case["pair_anchor"], case["s_len"])
+    expect = 0
+    for b0, b1 in zip(bounds[:-1], bounds[1:]):
+        idx = order[b0:b1]
+        seqs = [case["s_tok"][case["s_off"][i]:case["s_off"][i + 1]] for i in idx]
+        expect += len(OPX.prefix_groups_reference(seqs, case["pair_anchor"][idx], 4)[1])
+    nodes = s1["prefills"] - s0["prefills"] - used
+    assert nodes == expect and nodes >= 3, (nodes, expect)
+    assert s1["evictions"] == s1["prefills"] and s1["resident"] == 0 and s1["regret_tokens"] == 0
+    ref_logits, ref_dec, ref_margin = [], [], []
+    for i in range(n):
+        a = int(case["pair_anchor"][i])
+        at = case["a_tok"][case["a_off"][a]:case["a_off"][a + 1]] if a >= 0 else []
+        ref = OM.forward_pair(at, case["s_tok"][case["s_off"][i]:case["s_off"][i + 1]], wts, shape)
+        ref_logits.append(ref["logits"]); ref_dec.append(ref["decision"]); ref_margin.append(ref["margin"])
+    ref_logits = np.array(ref_logits)
+    assert rel_inf(l1, ref_logits) <= 2e-2
+    ok, _ = decisions_agree(d1, ref_dec, ref_margin, 2e-2 * np.max(np.abs(ref_logits)))
+    assert ok
