@@ -31,4 +31,4 @@ the tests can pin the rewrite against the definition.
 
 Parity status of each function is stated in its module header.
 """
-from . import codecs, attention, model, plan, prefix  # noqa: F401
+from . import codecs, attention, model, plan, prefix, joinorder  # noqa: F401
