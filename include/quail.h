@@ -184,6 +184,54 @@ quail_status quail_ctx_create(const quail_model_config* cfg, const quail_weights
                               quail_ctx** out);
 quail_status quail_ctx_destroy(quail_ctx* ctx);
 
+/* ---- KV-aware join-order search, speed-of-light cost model (host only) ---- */
+/* [pt] "Como funciona": the join-order search keeps several candidate plans,
+ * drops those that are Pareto-dominated (more tokens, more attention pairs
+ * and more cache) and picks among the rest with a "speed-of-light" cost model,
+ * a roofline that overstates the hardware's peak on purpose; [fa] (body): the
+ * planner chooses the join order with the KV cache in mind.
+ *
+ * A query is a tree of AI.IF joins over n_tables tables (1..12). Table t has
+ * `rows` rows whose prompt field has `field_tokens` tokens. Join k relates
+ * tables `left` and `right` (n_tables - 1 joins, no cycle); `anchor_glue` /
+ * `suffix_glue` are the template tokens that go with the anchor / suffix
+ * part of the prompt; `selectivity` in (0, 1] is the expected fraction of
+ * pairs that pass; `symmetric` != 0 lets the search put either table first
+ * (else the left table is the anchor). A plan is a left-deep order in which
+ * each table joins the earlier ones through one join, plus the anchor side of
+ * each symmetric join. Under independence a subset S of tables yields
+ * N(S) = prod rows * prod selectivity; table u contributes D_u = min(rows_u,
+ * N(S)) distinct rows. Adding table t through join k (other end u in S) runs
+ * P = D_u * rows_t pairs with A distinct anchors of La tokens and suffixes of
+ * Ls tokens, and adds computed tokens A*La + P*Ls, attention pairs
+ * P*(La*Ls + Ls*(Ls+1)/2) + A*La*(La+1)/2 and cache bytes A*La*(KV bytes per
+ * token over all layers of cfg). A plan's time is the roofline of its totals,
+ * max(FLOP / peak_flops, 2 * cache bytes / peak_bytes_per_s), with FLOP =
+ * tokens * GEMM FLOP per token + attention pairs * 4 * Hq * d * layers.
+ * The search keeps, for every connected subset of tables, the Pareto set of
+ * its partial plans (pruning is exact: extensions add the same amounts to
+ * every plan of a subset) and returns the least-time plan of the final set.
+ * Outputs (host): order [n_tables]; anchor_right [n_tables - 1] (1 = the
+ * right table is join k's anchor); metrics [4] = computed tokens, attention
+ * pairs, cache bytes, seconds; frontier [cap][4] (nullable when cap = 0)
+ * sorted by the metrics; *n_frontier = the final Pareto set's size. E_INVAL
+ * on a bad config, sizes, selectivities, peaks, or joins that are not a tree. */
+typedef struct {
+  int32_t rows;
+  float field_tokens;
+} quail_table;
+typedef struct {
+  int32_t left, right;
+  float anchor_glue, suffix_glue, selectivity;
+  int32_t symmetric;
+} quail_ai_join;
+quail_status quail_join_search(const quail_model_config* cfg, int32_t n_tables,
+                               const quail_table* tables, int32_t n_joins,
+                               const quail_ai_join* joins, double peak_flops,
+                               double peak_bytes_per_s, int32_t* order, int32_t* anchor_right,
+                               double* metrics, double* frontier, int32_t cap,
+                               int32_t* n_frontier);
+
 /* ---- anchor prefill + KV writer (a2, a3, a9) -------------------------------- */
 /* Runs the decoder stack over each anchor's tokens (positions 0..La-1) and
  * stores every layer's post-RoPE K and its V in a pool slab carved for the

@@ -54,6 +54,17 @@ _i64p = C.POINTER(C.c_int64)
 _szp = C.POINTER(C.c_size_t)
 _vp = C.c_void_p
 
+class Table(C.Structure):
+    _fields_ = [("rows", C.c_int32), ("field_tokens", C.c_float)]
+
+
+class AIJoin(C.Structure):
+    _fields_ = [("left", C.c_int32), ("right", C.c_int32), ("anchor_glue", C.c_float),
+                ("suffix_glue", C.c_float), ("selectivity", C.c_float), ("symmetric", C.c_int32)]
+
+
+_f64p = C.POINTER(C.c_double)
+
 _SIGS = {
     "quail_version": ([], C.c_char_p),
     "quail_last_error": ([], C.c_char_p),
@@ -68,6 +79,8 @@ _SIGS = {
     "quail_ctx_destroy": ([_vp], C.c_int32),
     "quail_anchor_prefill": ([_vp, C.c_int32, _vp, _i32p, _i32p, _i64p, _i64p, _vp], C.c_int32),
     "quail_anchor_release": ([_vp, C.c_int64], C.c_int32),
+    "quail_join_search": ([C.POINTER(ModelConfig), C.c_int32, C.POINTER(Table), C.c_int32, C.POINTER(AIJoin),
+                           C.c_double, C.c_double, _i32p, _i32p, _f64p, _f64p, C.c_int32, _i32p], C.c_int32),
     "quail_prefix_groups": ([C.c_int32, _i32p, _i32p, _i32p, C.c_int32, _i32p, _i32p, _i32p, _i32p],
                             C.c_int32),
     "quail_prefix_prefill": ([_vp, C.c_int32, _i64p, _vp, _i32p, _i32p, _i64p, _vp], C.c_int32),
@@ -245,6 +258,26 @@ def quail_anchor_prefill(ctx: Context, tokens, offsets, n_uses, anchor_ids=None,
 
 def quail_anchor_release(ctx: Context, handle: int):
     _check(load().quail_anchor_release(ctx.handle, int(handle)))
+
+
+def quail_join_search(cfg: ModelConfig, tables, joins, peak_flops: float, peak_bytes_per_s: float,
+                      cap: int = 256):
+    """tables: [(rows, field_tokens)]; joins: [(left, right, anchor_glue,
+    suffix_glue, selectivity, symmetric)]. Returns dict(order, anchor_right,
+    metrics, frontier)."""
+    nt, nj = len(tables), len(joins)
+    ta = (Table * max(nt, 1))(*[Table(int(r), float(t)) for r, t in tables])
+    ja = (AIJoin * max(nj, 1))(*[AIJoin(int(a), int(b), float(ga), float(gs), float(s), int(y))
+                                 for a, b, ga, gs, s, y in joins])
+    order, op = _i32(np.zeros(max(nt, 1), np.int32))
+    ar, arp = _i32(np.zeros(max(nj, 1), np.int32))
+    met = np.zeros(4, np.float64)
+    fr = np.zeros((max(cap, 1), 4), np.float64)
+    nf = C.c_int32()
+    _check(load().quail_join_search(C.byref(cfg), nt, ta, nj, ja, peak_flops, peak_bytes_per_s, op, arp,
+                                    met.ctypes.data_as(_f64p), fr.ctypes.data_as(_f64p), cap, C.byref(nf)))
+    return dict(order=order[:nt].copy(), anchor_right=ar[:nj].copy(), metrics=met,
+                frontier=fr[:min(cap, nf.value)].copy(), n_frontier=nf.value)
 
 
 def quail_prefix_groups(tokens, offsets, keys, min_len: int):

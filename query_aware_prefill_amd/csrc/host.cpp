@@ -884,6 +884,132 @@ quail_status quail_prefix_groups(int32_t n, const int32_t* tokens, const int32_t
   return QUAIL_OK;
 }
 
+// ---- KV-aware join-order search with a speed-of-light cost model ----------
+namespace {
+// One candidate (partial) plan: metrics (computed tokens, attention pairs,
+// cache bytes), the table order so far, and bit k = join k's right table is
+// its anchor.
+struct JoinPlan {
+  double m[3];
+  std::vector<int8_t> order;
+  uint32_t right = 0;
+};
+
+// Adds p to a Pareto set unless a member is <= p in every metric; drops the
+// members p now dominates.
+void pareto_insert(std::vector<JoinPlan>& set, JoinPlan&& p) {
+  for (const JoinPlan& q : set)
+    if (q.m[0] <= p.m[0] && q.m[1] <= p.m[1] && q.m[2] <= p.m[2]) return;
+  set.erase(std::remove_if(set.begin(), set.end(),
+                           [&](const JoinPlan& q) {
+                             return p.m[0] <= q.m[0] && p.m[1] <= q.m[1] && p.m[2] <= q.m[2];
+                           }),
+            set.end());
+  set.push_back(std::move(p));
+}
+}  // namespace
+
+quail_status quail_join_search(const quail_model_config* cfg, int32_t n_tables, const quail_table* tables,
+                               int32_t n_joins, const quail_ai_join* joins, double peak_flops,
+                               double peak_bytes_per_s, int32_t* order, int32_t* anchor_right, double* metrics,
+                               double* frontier, int32_t cap, int32_t* n_frontier) {
+  if (quail_status st = check_cfg(cfg)) return st;
+  if (n_tables < 1 || n_tables > 12) return fail(QUAIL_E_INVAL, "n_tables must be in [1, 12]");
+  if (n_joins != n_tables - 1) return fail(QUAIL_E_INVAL, "a tree of n tables has n - 1 joins");
+  if (!tables || (n_joins > 0 && !joins) || !order || (n_joins > 0 && !anchor_right) || !metrics || !n_frontier)
+    return fail(QUAIL_E_INVAL, "tables, joins, order, anchor_right, metrics and n_frontier are required");
+  if (!(peak_flops > 0) || !(peak_bytes_per_s > 0)) return fail(QUAIL_E_INVAL, "peaks must be positive");
+  if (cap < 0 || (cap > 0 && !frontier)) return fail(QUAIL_E_INVAL, "frontier is NULL");
+  for (int32_t t = 0; t < n_tables; ++t)
+    if (tables[t].rows < 1 || !(tables[t].field_tokens >= 0))
+      return fail(QUAIL_E_INVAL, "table %d: rows must be >= 1 and tokens >= 0", t);
+  std::vector<int32_t> root(n_tables);
+  std::iota(root.begin(), root.end(), 0);
+  auto find = [&](int32_t x) { while (root[x] != x) x = root[x] = root[root[x]]; return x; };
+  for (int32_t k = 0; k < n_joins; ++k) {
+    const quail_ai_join& j = joins[k];
+    if (j.left < 0 || j.left >= n_tables || j.right < 0 || j.right >= n_tables || j.left == j.right)
+      return fail(QUAIL_E_INVAL, "join %d: tables out of range or equal", k);
+    if (!(j.selectivity > 0 && j.selectivity <= 1) || !(j.anchor_glue >= 0) || !(j.suffix_glue >= 0))
+      return fail(QUAIL_E_INVAL, "join %d: selectivity must be in (0, 1] and glue >= 0", k);
+    const int32_t a = find(j.left), b = find(j.right);
+    if (a == b) return fail(QUAIL_E_INVAL, "join %d closes a cycle: the joins must form a tree", k);
+    root[a] = b;
+  }
+  const quail_model_config& c = *cfg;
+  const double L = c.n_layers, H = c.hidden, Hq = c.n_q_heads, Hkv = c.n_kv_heads, d = c.head_dim;
+  const double gemm = 2.0 * L * (H * (Hq + 2 * Hkv) * d + Hq * d * H + 3.0 * H * c.intermediate);
+  const double attn = 4.0 * Hq * d * L;
+  const double kv = 2.0 * L * Hkv * d * (double)kv_elem_bytes(c);
+  auto seconds = [&](const double* m) {
+    return std::max((m[0] * gemm + m[1] * attn) / peak_flops, 2.0 * m[2] / peak_bytes_per_s);
+  };
+  const uint32_t full = (1u << n_tables) - 1;
+  // result cardinality of each subset (independence): rows times the
+  // selectivities of the joins inside it
+  std::vector<double> card(full + 1, 1.0);
+  for (uint32_t S = 1; S <= full; ++S) {
+    for (int32_t t = 0; t < n_tables; ++t)
+      if (S >> t & 1) card[S] *= tables[t].rows;
+    for (int32_t k = 0; k < n_joins; ++k)
+      if ((S >> joins[k].left & 1) && (S >> joins[k].right & 1)) card[S] *= joins[k].selectivity;
+  }
+  std::vector<std::vector<JoinPlan>> dp(full + 1);
+  for (int32_t t = 0; t < n_tables; ++t) {
+    JoinPlan p{};
+    p.order.push_back((int8_t)t);
+    dp[1u << t].push_back(std::move(p));
+  }
+  for (uint32_t S = 1; S < full; ++S) {
+    if (dp[S].empty()) continue;
+    for (int32_t t = 0; t < n_tables; ++t) {
+      if (S >> t & 1) continue;
+      int32_t k = -1, cnt = 0;
+      for (int32_t q = 0; q < n_joins; ++q)
+        if ((joins[q].left == t && (S >> joins[q].right & 1)) || (joins[q].right == t && (S >> joins[q].left & 1))) {
+          k = q;
+          ++cnt;
+        }
+      if (cnt != 1) continue;
+      const quail_ai_join& j = joins[k];
+      const int32_t u = j.left == t ? j.right : j.left;
+      const double Du = std::min((double)tables[u].rows, card[S]);
+      const double P = Du * tables[t].rows;
+      for (int side = 0; side < (j.symmetric ? 2 : 1); ++side) {
+        const int32_t x = side ? j.right : j.left, y = side ? j.left : j.right;
+        const double A = x == u ? Du : (double)tables[t].rows;
+        const double La = tables[x].field_tokens + j.anchor_glue, Ls = tables[y].field_tokens + j.suffix_glue;
+        for (const JoinPlan& p : dp[S]) {
+          JoinPlan q = p;
+          q.m[0] += A * La + P * Ls;
+          q.m[1] += P * (La * Ls + Ls * (Ls + 1) / 2.0) + A * La * (La + 1) / 2.0;
+          q.m[2] += A * La * kv;
+          q.order.push_back((int8_t)t);
+          if (side) q.right |= 1u << k;
+          pareto_insert(dp[S | (1u << t)], std::move(q));
+        }
+      }
+    }
+  }
+  std::vector<JoinPlan>& fr = dp[full];
+  std::sort(fr.begin(), fr.end(), [](const JoinPlan& a, const JoinPlan& b) {
+    return std::lexicographical_compare(a.m, a.m + 3, b.m, b.m + 3);
+  });
+  size_t best = 0;
+  for (size_t i = 1; i < fr.size(); ++i)
+    if (seconds(fr[i].m) < seconds(fr[best].m)) best = i;
+  for (int32_t t = 0; t < n_tables; ++t) order[t] = fr[best].order[t];
+  for (int32_t k = 0; k < n_joins; ++k) anchor_right[k] = (int32_t)(fr[best].right >> k & 1);
+  for (int i = 0; i < 3; ++i) metrics[i] = fr[best].m[i];
+  metrics[3] = seconds(fr[best].m);
+  for (int32_t i = 0; i < std::min<int32_t>(cap, (int32_t)fr.size()); ++i) {
+    for (int q = 0; q < 3; ++q) frontier[4 * i + q] = fr[i].m[q];
+    frontier[4 * i + 3] = seconds(fr[i].m);
+  }
+  *n_frontier = (int32_t)fr.size();
+  return QUAIL_OK;
+}
+
 quail_status quail_plan_build(const quail_model_config* cfg, size_t pool_bytes, int32_t max_batch_tokens,
                               int32_t n_anchors, const int32_t* anchor_len, int32_t n_pairs,
                               const int32_t* pair_anchor, const int32_t* pair_len, int32_t* pair_order,

@@ -340,3 +340,45 @@ def test_prefix_prefill_and_shared_run_reject_bad_arguments():
     st = fc.lib.quail_join_run_shared(fc.h, 1, dec, aop, 1, pa1p, dec, sop, None, 2, 0x0F, None, None, dec, None)
     assert st == B.E_INVAL
     fc.close()
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_join_search_matches_brute_force(seed):
+    """The library's subset DP with Pareto pruning returns the frontier and the
+    least-time plan that enumerating every plan finds."""
+    from oracle import joinorder as OJ
+    from tests.test_oracle_joinorder import QWEN, random_query
+    tables, joins = random_query(seed)
+    res = B.quail_join_search(_cfg(max_anchor_len=512), tables, joins, 2.5166e15, 8e12)
+    ref = OJ.search_reference(tables, joins, QWEN, 2.5166e15, 8e12)
+    assert res["n_frontier"] == len(ref["frontier"])
+    got = np.array(sorted(map(tuple, res["frontier"])))
+    want = np.array(sorted(ref["frontier"]))
+    assert np.allclose(got, want, rtol=1e-9, atol=0)
+    assert abs(res["metrics"][3] - ref["best_seconds"]) <= 1e-9 * ref["best_seconds"]
+    replay = OJ.plan_metrics(list(res["order"]), list(res["anchor_right"]), tables, joins, QWEN)
+    assert replay is not None and np.allclose(replay, res["metrics"][:3], rtol=1e-9, atol=0)
+
+
+def test_join_search_argument_checks():
+    cfg = _cfg()
+    good = [(10, 5.0), (20, 5.0), (30, 5.0)]
+    with pytest.raises(B.QuailError):             # a cycle, and one join too many
+        B.quail_join_search(cfg, good, [(0, 1, 0, 0, 0.5, 0), (1, 2, 0, 0, 0.5, 0), (2, 0, 0, 0, 0.5, 0)], 1e15, 8e12)
+    for joins in ([(0, 1, 0, 0, 0.5, 0)],                               # too few joins
+                  [(0, 1, 0, 0, 0.0, 0), (1, 2, 0, 0, 0.5, 0)],          # selectivity 0
+                  [(0, 1, 0, 0, 1.5, 0), (1, 2, 0, 0, 0.5, 0)],          # selectivity > 1
+                  [(0, 0, 0, 0, 0.5, 0), (1, 2, 0, 0, 0.5, 0)],          # self join
+                  [(0, 3, 0, 0, 0.5, 0), (1, 2, 0, 0, 0.5, 0)],          # table out of range
+                  [(0, 1, 0, 0, 0.5, 0), (0, 1, 0, 0, 0.5, 0)]):         # not spanning
+        with pytest.raises(B.QuailError) as e:
+            B.quail_join_search(cfg, good, joins, 1e15, 8e12)
+        assert e.value.status == B.E_INVAL, joins
+    with pytest.raises(B.QuailError):
+        B.quail_join_search(cfg, good, [(0, 1, 0, 0, 0.5, 0), (1, 2, 0, 0, 0.5, 0)], 0.0, 8e12)
+    with pytest.raises(B.QuailError):
+        B.quail_join_search(cfg, [(0, 5.0)], [], 1e15, 8e12)
+    with pytest.raises(B.QuailError):
+        B.quail_join_search(cfg, [(1, 1.0)] * 13, [(i, i + 1, 0, 0, 0.5, 0) for i in range(12)], 1e15, 8e12)
+    one = B.quail_join_search(cfg, [(7, 3.0)], [], 1e15, 8e12)
+    assert list(one["order"]) == [0] and one["n_frontier"] == 1 and one["metrics"][0] == 0
