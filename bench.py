@@ -388,6 +388,13 @@ def bench_e2e(args):
            "computed_tokens_per_min": (suffix_tok + anchor_tok) / (ms * 1e-3) * 60.0,
            "algorithmic_tflops": (gemm + attn) / (ms * 1e-3) / 1e12, "pool": st,
            "weights": "random init on device (W ~ N(0, 0.02), per-row bf16 scales, E4M3 codes)"}
+    if kind == "join36":
+        # the planner's speed-of-light time for this join: anchor table (64 rows
+        # x 1024 tokens) against the suffix table (2048 rows x 64 tokens)
+        sol = B.quail_join_search(dm.cfg, [(64, 1024), (2048, 64)], [(0, 1, 0, 0, 1.0, 1)],
+                                  PEAK_BF16_TFLOPS * 1e12, HBM_PEAK_GBS * 1e9)
+        res["speed_of_light_s"] = float(sol["metrics"][3])
+        res["measured_over_speed_of_light"] = ms * 1e-3 / float(sol["metrics"][3])
     log(f"{kind}: {ms / 1000:.2f} s, {res['logical_tokens_per_min'] / 1e9:.3f} G logical tok/min, "
         f"{res['algorithmic_tflops']:.1f} TFLOP/s")
     if not args.no_cpu_baseline:
@@ -592,6 +599,38 @@ def bench_shared(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_search(args):
+    """Planner latency (host only): quail_join_search on random tree queries of
+    4 to 12 tables (Qwen3-4B cost constants, datasheet peaks)."""
+    from query_aware_prefill_amd import binding as B
+    import workloads as W
+    B.load()
+    shape = W.QWEN3_4B
+    cfg = B.ModelConfig(n_layers=shape.n_layers, hidden=shape.hidden, n_q_heads=shape.n_q_heads,
+                        n_kv_heads=shape.n_kv_heads, head_dim=shape.head_dim, intermediate=shape.intermediate,
+                        vocab=shape.vocab, rope_theta=1e6, rms_eps=1e-6, kv_dtype=B.DTYPE_BF16, k_scale=1.0,
+                        v_scale=1.0, max_anchor_len=2048, max_suffix_len=2048)
+    out = {"metric": "join-order search latency (host)", "unit": "ms", "queries": {}}
+    for n in (4, 8, 10, 12):
+        r = np.random.default_rng([11, n])
+        times, fronts = [], []
+        for q in range(5):
+            tables = [(int(r.integers(10, 100000)), float(r.integers(16, 2048))) for _ in range(n)]
+            joins = []
+            for t in range(1, n):
+                u = int(r.integers(0, t))
+                joins.append((u, t, float(r.integers(0, 64)), float(r.integers(0, 64)),
+                              float(r.integers(1, 65)) / 1024.0, int(r.random() < 0.5)))
+            t0 = time.perf_counter()
+            res = B.quail_join_search(cfg, tables, joins, PEAK_BF16_TFLOPS * 1e12, HBM_PEAK_GBS * 1e9, cap=0)
+            times.append((time.perf_counter() - t0) * 1e3)
+            fronts.append(res["n_frontier"])
+        out["queries"][str(n)] = {"tables": n, "median_ms": float(np.median(times)), "max_ms": float(np.max(times)),
+                                  "frontier_sizes": fronts}
+        log(f"search: {n} tables, median {np.median(times):.2f} ms, frontier sizes {fronts}")
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -600,7 +639,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--workload", choices=["cascade", "gemm", "layer", "copy", "stream", "join36",
-                                           "filter36", "multijoin36", "multiplan36", "shared36"],
+                                           "filter36", "multijoin36", "multiplan36", "shared36", "search"],
                     default="cascade")
     ap.add_argument("--rows", type=int, default=625, help="multijoin36: rows of the 5,000 used")
     args = ap.parse_args()
@@ -622,6 +661,8 @@ def main():
         return bench_multiplan(args)
     if args.workload == "shared36":
         return bench_shared(args)
+    if args.workload == "search":
+        return bench_search(args)
     if args.workload in ("join36", "filter36", "multijoin36"):
         return bench_e2e(args)
 
