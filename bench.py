@@ -553,7 +553,12 @@ def bench_shared(args):
     T = 65536
     pool = sum(B.quail_anchor_bytes(dm.cfg, int(x)) for x in a_len) + (4 << 30)
     # tokens the shared run computes: the library's plan steps and grouping
-    order, bounds, _ = B.quail_plan_build(dm.cfg, pool, T, a_len, pa, s_len)
+    g_all, _, nl_all = B.quail_prefix_groups(s_tok, s_off, pa, min_shared)
+    step_len = s_len.astype(np.int64).copy()
+    for k in range(len(nl_all)):          # the shared run sizes its steps by computed tokens
+        m = np.flatnonzero(g_all == k)
+        step_len[m] = s_len[m] - nl_all[k] + (nl_all[k] + len(m) - 1) // len(m)
+    order, bounds, _ = B.quail_plan_build(dm.cfg, pool, T, a_len, pa, step_len.astype(np.int32))
     node_tok = 0
     for b0, b1 in zip(bounds[:-1], bounds[1:]):
         idx = order[b0:b1]
@@ -593,6 +598,15 @@ def bench_shared(args):
             f"{logical / ms * 60e3 / 1e6:.1f} M logical tokens/min")
         del ctx
     res["speedup"] = res["plain"]["ms"] / res["shared"]["ms"]
+    if not args.no_cpu_baseline:
+        # oracle leg on the shared run's outputs: the per-pair definition over
+        # [anchor | whole suffix] (the shared prefix included)
+        order = np.random.default_rng(1).permutation(n)[:8]
+        pairs = [(int(i), case["a_tok"][a_off[pa[i]]:a_off[pa[i] + 1]], s_tok[s_off[i]:s_off[i + 1]])
+                 for i in order]
+        log("shared36: oracle leg")
+        res["cpu_baseline"] = cpu_baseline_e2e(wd, shape, pairs, out["shared"][0].astype(np.float64), 0x0F,
+                                               args.cpu_budget)
     ls, lp = out["shared"][0].astype(np.float64), out["plain"][0].astype(np.float64)
     res["logits_rel_inf_shared_vs_plain"] = float(np.max(np.abs(ls - lp)) / np.max(np.abs(lp)))
     res["decisions_equal_frac"] = float(np.mean(out["shared"][1] == out["plain"][1]))

@@ -1430,8 +1430,24 @@ static quail_status join_run_core(quail_ctx* c, int32_t n_anchors, const int32_t
   // the plan is built against the largest free block of the pool now
   size_t free_bytes = 0;
   for (auto& f : c->free_list) free_bytes = std::max(free_bytes, f.second);
+  // With sharing, steps are sized by the tokens each pair will compute: its
+  // own tokens after the prefix it shares, plus its share of that prefix
+  // (grouping all pairs of each anchor); steps are regrouped below.
+  std::vector<int32_t> step_len(plen);
+  if (min_shared > 0) {
+    std::vector<int32_t> gof(n_pairs), nf(n_pairs), nl(n_pairs), starts(n_pairs);
+    for (int32_t i = 0; i < n_pairs; ++i) starts[i] = s_offsets[i];
+    const int32_t nn = prefix_groups(n_pairs, s_tokens_host, starts.data(), plen.data(), pair_anchor, min_shared,
+                                     gof.data(), nf.data(), nl.data());
+    std::vector<int32_t> members(nn, 0);
+    for (int32_t i = 0; i < n_pairs; ++i)
+      if (gof[i] >= 0) members[gof[i]]++;
+    for (int32_t i = 0; i < n_pairs; ++i)
+      if (gof[i] >= 0)
+        step_len[i] = plen[i] - nl[gof[i]] + (nl[gof[i]] + members[gof[i]] - 1) / members[gof[i]];
+  }
   Plan plan;
-  if (quail_status st = build_plan(slab, n_pairs, pair_anchor, plen.data(), free_bytes, c->T, plan))
+  if (quail_status st = build_plan(slab, n_pairs, pair_anchor, step_len.data(), free_bytes, c->T, plan))
     return st;
   // shared-prefix nodes per step (plan positions of their members)
   struct Node { int32_t anchor, first, len; std::vector<int32_t> members; };

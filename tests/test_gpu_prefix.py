@@ -33,6 +33,18 @@ def _pack(tok, ranges):
     return np.concatenate([tok[a:b] for a, b in ranges]).astype(np.int32), off
 
 
+def shared_step_lengths(B, case, min_shared):
+    """Tokens each pair computes with sharing, as the shared run sizes its
+    plan steps: own tokens after the shared prefix + its share of the prefix."""
+    g, _, nl = B.quail_prefix_groups(case["s_tok"], case["s_off"], case["pair_anchor"], min_shared)
+    s_len = np.diff(case["s_off"]).astype(np.int64)
+    out = s_len.copy()
+    for k in range(len(nl)):
+        m = np.flatnonzero(g == k)
+        out[m] = s_len[m] - nl[k] + (nl[k] + len(m) - 1) // len(m)
+    return out.astype(np.int32)
+
+
 @pytest.mark.parametrize("kv_fp8,k_scale,v_scale", [(False, 1.0, 1.0), (True, 1.0, 1.0), (True, 0.5, 2.0)])
 def test_two_level_cascade_model(B, kv_fp8, k_scale, v_scale):
     import torch
@@ -179,7 +191,8 @@ def test_join_run_shared_matches_join_run(B):
     assert s0["prefills"] == used and s0["regret_tokens"] == 0
     # nodes: the oracle's grouping of each plan step's pairs (plan from the
     # library's builder, pool fully free as at the shared run's start)
-    order, bounds, _ = B.quail_plan_build(dm.cfg, 64 << 20, 128, a_len, case["pair_anchor"], case["s_len"])
+    order, bounds, _ = B.quail_plan_build(dm.cfg, 64 << 20, 128, a_len, case["pair_anchor"],
+                                          shared_step_lengths(B, case, 4))
     expect = 0
     for b0, b1 in zip(bounds[:-1], bounds[1:]):
         idx = order[b0:b1]
@@ -197,4 +210,49 @@ def test_join_run_shared_matches_join_run(B):
     ref_logits = np.array(ref_logits)
     assert rel_inf(l1, ref_logits) <= 2e-2
     ok, _ = decisions_agree(d1, ref_dec, ref_margin, 2e-2 * np.max(np.abs(ref_logits)))
+    assert ok
+
+
+def test_join_run_shared_under_a_tight_pool(B):
+    """A pool that holds the anchors and one prefix node at a time: nodes are
+    prefilled one per chunk and evicted after their members; the results
+    equal the plain run's and the oracle's."""
+    import torch
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    shape = W.tiny_shape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                         intermediate=384, vocab=512)
+    wts = W.model_weights(shape, 12)
+    a_len = [60, 90]
+    fam = [(0, 40, [3, 4, 5]), (0, 30, [2, 6]), (1, 50, [4, 4, 4, 4]), (1, 20, [7, 9])]
+    case = W.shared_prefix_case(12, shape.vocab, a_len, fam)
+    n = len(case["pair_anchor"])
+    dm = DeviceModel(shape, wts, max_anchor_len=1024, max_suffix_len=256)
+    slab64 = B.quail_anchor_bytes(dm.cfg, 64)
+    tight = B.quail_anchor_bytes(dm.cfg, 60) + B.quail_anchor_bytes(dm.cfg, 90) + 2 * slab64 + 4096
+    a_tok, s_tok = to_device(case["a_tok"]), to_device(case["s_tok"])
+    res = []
+    for shared, pool in ((True, tight), (False, 64 << 20)):
+        ctx = dm.context(pool, 512)
+        logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+        dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+        say("join_run tight pool", "shared" if shared else "plain")
+        if shared:
+            B.quail_join_run_shared(ctx, a_tok, case["a_off"], case["pair_anchor"], s_tok, case["s_off"],
+                                    case["s_tok"], 8, 0x0F, logits, None, dec)
+        else:
+            B.quail_join_run(ctx, a_tok, case["a_off"], case["pair_anchor"], s_tok, case["s_off"], 0x0F,
+                             logits, None, dec)
+        torch.cuda.synchronize()
+        res.append((logits.cpu().numpy(), dec.cpu().numpy(), B.quail_pool_stats(ctx)))
+    (l1, d1, st1), (l0, d0, _) = res
+    assert st1["prefills"] == 2 + 4 and st1["evictions"] == 6 and st1["resident"] == 0
+    assert st1["peak"] <= tight
+    assert rel_inf(l1, l0) <= 2e-2
+    ref = [OM.forward_pair(case["a_tok"][case["a_off"][a]:case["a_off"][a + 1]],
+                           case["s_tok"][case["s_off"][i]:case["s_off"][i + 1]], wts, shape)
+           for i, a in enumerate(case["pair_anchor"])]
+    ref_logits = np.array([r["logits"] for r in ref])
+    assert rel_inf(l1, ref_logits) <= 2e-2
+    ok, _ = decisions_agree(d1, [r["decision"] for r in ref], [r["margin"] for r in ref],
+                            2e-2 * np.max(np.abs(ref_logits)))
     assert ok
