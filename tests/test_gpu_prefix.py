@@ -256,3 +256,55 @@ def test_join_run_shared_under_a_tight_pool(B):
     ok, _ = decisions_agree(d1, [r["decision"] for r in ref], [r["margin"] for r in ref],
                             2e-2 * np.max(np.abs(ref_logits)))
     assert ok
+
+
+def test_qwen3_shaped_layer_through_prefix_nodes(B):
+    """One decoder layer with the Qwen3-4B shapes (hidden 2560, 32q/8kv x 128,
+    SwiGLU 9728, fp8 weights): 2 anchors x 1000 tokens, a 300-token prefix
+    node under each, and members of 64 and 33 tokens after it; all positions
+    of one member per anchor and the first node's slab against the oracle's
+    monolithic layer over [anchor | node | member]."""
+    import torch
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    shape = W.ModelShape(n_layers=1, hidden=2560, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                         intermediate=9728, vocab=4096)
+    wts = W.model_weights(shape, 13)
+    a_len = [1000, 1000]
+    case = W.shared_prefix_case(13, shape.vocab, a_len, [(0, 300, [64, 33]), (1, 300, [33, 64])])
+    s_tok, s_off = case["s_tok"], case["s_off"]
+    g, nfirst, nlen = B.quail_prefix_groups(s_tok, s_off, case["pair_anchor"], 16)
+    assert list(nlen) == [300, 300] and list(g) == [0, 0, 1, 1]
+    dm = DeviceModel(shape, wts, max_anchor_len=1024, max_suffix_len=512)
+    pool = 2 * B.quail_anchor_bytes(dm.cfg, 1000) + 2 * B.quail_anchor_bytes(dm.cfg, 300) + 4096
+    ctx = dm.context(pool, 2048)
+    say("qwen3 layer through prefix nodes: anchors")
+    handles = B.quail_anchor_prefill(ctx, to_device(case["a_tok"]), case["a_off"], [1, 1])
+    node_tok, node_off = _pack(s_tok, [(s_off[f], s_off[f] + L) for f, L in zip(nfirst, nlen)])
+    say("qwen3 layer through prefix nodes: nodes")
+    nh = B.quail_prefix_prefill(ctx, handles, to_device(node_tok), node_off, [2, 2])
+    tails, toff = _pack(s_tok, [(s_off[i] + 300, s_off[i + 1]) for i in range(4)])
+    T = int(toff[-1])
+    h_last = torch.empty((4, shape.hidden), dtype=torch.int16, device="cuda")
+    h_all = torch.empty((T, shape.hidden), dtype=torch.int16, device="cuda")
+    k0, v0, la, lap = B.quail_anchor_kv(ctx, int(nh[0]), 0)
+    node0 = _slab(ctx, nh[0], 0, B, shape)
+    say("qwen3 layer through prefix nodes: join")
+    B.quail_join_prefill(ctx, [nh[g[i]] for i in range(4)], to_device(tails), toff, h_last, h_all)
+    torch.cuda.synchronize()
+    ha = bf16_f64(u16(h_all))
+    for i in (0, 3):                       # one member per anchor (the oracle layer is slow)
+        a = int(case["pair_anchor"][i])
+        at = case["a_tok"][case["a_off"][a]:case["a_off"][a + 1]]
+        st = s_tok[s_off[i]:s_off[i + 1]]
+        if i == 0:
+            h, kv = OM.forward_tokens(np.concatenate([at, st]), wts, shape, return_kv=True)
+            assert la == 300
+            assert rel_inf(node0[0], kv[0][0][1000:1300]) <= 2e-2
+            assert rel_inf(node0[1], kv[0][1][1000:1300]) <= 2e-2
+        else:
+            h = OM.forward_tokens(np.concatenate([at, st]), wts, shape)
+        err = rel_inf(ha[toff[i]:toff[i + 1]], h[1300:])
+        say("  member", i, "rel", err)
+        assert err <= 2e-2
+    st = B.quail_pool_stats(ctx)
+    assert st["prefills"] == 4 and st["evictions"] == 4 and st["resident"] == 0
