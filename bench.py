@@ -575,7 +575,7 @@ def bench_shared(args):
                        f"{shared} shared tokens + U{{16..64}} own tokens each",
            "pairs": int(n), "logical_tokens": logical}
     out = {}
-    for mode in ("shared", "plain"):
+    for mode in (("shared",) if args.shared_only else ("shared", "plain")):
         ctx = dm.context(pool, T)
         logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
         dec = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -597,6 +597,9 @@ def bench_shared(args):
         log(f"shared36 {mode}: {ms / 1000:.2f} s, {computed[mode] / 1e6:.3f} M computed tokens, "
             f"{logical / ms * 60e3 / 1e6:.1f} M logical tokens/min")
         del ctx
+    if args.shared_only:
+        print(json.dumps(res), flush=True)
+        return
     res["speedup"] = res["plain"]["ms"] / res["shared"]["ms"]
     if not args.no_cpu_baseline:
         # oracle leg on the shared run's outputs: the per-pair definition over
@@ -656,6 +659,7 @@ def main():
                                            "filter36", "multijoin36", "multiplan36", "shared36", "search"],
                     default="cascade")
     ap.add_argument("--rows", type=int, default=625, help="multijoin36: rows of the 5,000 used")
+    ap.add_argument("--shared-only", action="store_true", help="shared36: run only the join with prefix nodes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
