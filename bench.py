@@ -553,7 +553,8 @@ def bench_shared(args):
     T = 65536
     pool = sum(B.quail_anchor_bytes(dm.cfg, int(x)) for x in a_len) + (4 << 30)
     # tokens the shared run computes: the library's plan steps and grouping
-    g_all, _, nl_all = B.quail_prefix_groups(s_tok, s_off, pa, min_shared)
+    g_all, _, nl_all = B.quail_prefix_groups(s_tok, s_off, np.where(pa >= 0, pa, n_anchors).astype(np.int32),
+                                             min_shared)
     step_len = s_len.astype(np.int64).copy()
     for k in range(len(nl_all)):          # the shared run sizes its steps by computed tokens
         m = np.flatnonzero(g_all == k)
@@ -564,7 +565,8 @@ def bench_shared(args):
         idx = order[b0:b1]
         offs = np.concatenate([[0], np.cumsum(s_len[idx])]).astype(np.int32)
         toks = np.concatenate([s_tok[s_off[i]:s_off[i + 1]] for i in idx])
-        g, _, nl = B.quail_prefix_groups(toks, offs, pa[idx], min_shared)
+        g, _, nl = B.quail_prefix_groups(toks, offs, np.where(pa[idx] >= 0, pa[idx], n_anchors).astype(np.int32),
+                                         min_shared)
         node_tok += int(np.sum(nl)) - int(np.sum(nl[g[g >= 0]]))
     a_tok_d, s_tok_d = to_device(case["a_tok"].astype(np.int32)), to_device(s_tok.astype(np.int32))
     logical = float(np.sum(a_len[pa] + s_len))

@@ -361,9 +361,14 @@ quail_status quail_join_run(quail_ctx* ctx, int32_t n_anchors, const int32_t* a_
  * s_tokens_host (a host copy of s_tokens, same layout); each group's prefix
  * node is prefilled once (quail_prefix_prefill, in chunks that fit half the
  * largest free pool block) and its members run only their remaining tokens.
- * The anchor's uses are its ungrouped pairs plus one per node. Outputs equal
- * quail_join_run's up to floating-point rounding (the cascade split is
- * exact). min_shared >= 1; other arguments as quail_join_run. */
+ * Filter rows (pair_anchor -1) are grouped among themselves; their shared
+ * prefix is prefilled as a plain anchor and the rows run after it. The
+ * anchor's uses are its ungrouped pairs plus one per node. Plan steps are
+ * sized by the tokens each pair computes (its own tokens after its group's
+ * prefix plus its share of the prefix). Outputs equal quail_join_run's up to
+ * floating-point rounding (the cascade split is exact), except that with an
+ * fp8 KV store the shared positions are stored in E4M3 like anchor KV.
+ * min_shared >= 1; other arguments as quail_join_run. */
 quail_status quail_join_run_shared(quail_ctx* ctx, int32_t n_anchors, const int32_t* a_tokens,
                                    const int32_t* a_offsets, int32_t n_pairs,
                                    const int32_t* pair_anchor, const int32_t* s_tokens,

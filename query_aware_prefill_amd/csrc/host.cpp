@@ -730,10 +730,11 @@ quail_status check_offsets(int32_t n, const int32_t* off, int32_t lo, int32_t hi
 hipStream_t as_stream(quail_stream s) { return reinterpret_cast<hipStream_t>(s); }
 
 // Anchor prefill core: anchor a = tokens[starts[a] .. starts[a] + lens[a]).
-// With `parents`, entry a is a shared-prefix node continuing anchor slot
-// parents[a]: its tokens sit at positions La.. and attend to the whole anchor
-// (cross) and causally to themselves (its own slab); the caller has checked
-// that each parent has a use to spare per node.
+// With `parents`, entry a with parents[a] >= 0 is a shared-prefix node
+// continuing anchor slot parents[a]: its tokens sit at positions La.. and
+// attend to the whole anchor (cross) and causally to themselves (its own
+// slab); the caller has checked that each parent has a use to spare per node.
+// parents[a] = -1 is a plain anchor (the shared prefix of filter rows).
 quail_status anchor_core(quail_ctx* c, int32_t n, const int32_t* tokens, const int32_t* starts,
                          const int32_t* lens, const int32_t* n_uses, const int64_t* anchor_ids,
                          quail_anchor* out, hipStream_t s, const int32_t* parents = nullptr) {
@@ -770,8 +771,8 @@ quail_status anchor_core(quail_ctx* c, int32_t n, const int32_t* tokens, const i
     sl.uses = n_uses[a];
     sl.held = 0;
     sl.parent = parents ? parents[a] : -1;
-    sl.pos0 = parents ? c->slots[parents[a]].len : 0;
-    if (parents) c->slots[parents[a]].held++;
+    sl.pos0 = sl.parent >= 0 ? c->slots[sl.parent].len : 0;
+    if (sl.parent >= 0) c->slots[sl.parent].held++;
     slot_of[a] = slot;
     out[a] = ((int64_t)sl.gen << 32) | (uint32_t)slot;
     c->resident += sl.bytes;
@@ -803,7 +804,8 @@ quail_status anchor_core(quail_ctx* c, int32_t n, const int32_t* tokens, const i
       ++a1;
     }
     // packed tiles when every anchor is that short (see attn_tile_tokens)
-    b.has_parent = parents != nullptr;
+    b.has_parent = false;
+    for (int32_t a = a0; a < a1 && parents; ++a) b.has_parent |= n_uses[a] > 0 && parents[a] >= 0;
     b.packed = max_len <= attn_tile_tokens(G, true) &&
                attn_direct_ok(b.has_parent && slab_fp8, slab_fp8, cf.k_scale, cf.v_scale);
     const int TQ = attn_tile_tokens(G, b.packed);
@@ -1435,9 +1437,12 @@ static quail_status join_run_core(quail_ctx* c, int32_t n_anchors, const int32_t
   // (grouping all pairs of each anchor); steps are regrouped below.
   std::vector<int32_t> step_len(plen);
   if (min_shared > 0) {
-    std::vector<int32_t> gof(n_pairs), nf(n_pairs), nl(n_pairs), starts(n_pairs);
-    for (int32_t i = 0; i < n_pairs; ++i) starts[i] = s_offsets[i];
-    const int32_t nn = prefix_groups(n_pairs, s_tokens_host, starts.data(), plen.data(), pair_anchor, min_shared,
+    std::vector<int32_t> gof(n_pairs), nf(n_pairs), nl(n_pairs), starts(n_pairs), keys(n_pairs);
+    for (int32_t i = 0; i < n_pairs; ++i) {
+      starts[i] = s_offsets[i];
+      keys[i] = pair_anchor[i] >= 0 ? pair_anchor[i] : n_anchors;   // filter rows group among themselves
+    }
+    const int32_t nn = prefix_groups(n_pairs, s_tokens_host, starts.data(), plen.data(), keys.data(), min_shared,
                                      gof.data(), nf.data(), nl.data());
     std::vector<int32_t> members(nn, 0);
     for (int32_t i = 0; i < n_pairs; ++i)
@@ -1462,7 +1467,7 @@ static quail_status join_run_core(quail_ctx* c, int32_t n_anchors, const int32_t
         const int32_t pi = plan.order[b0 + k];
         starts[k] = s_offsets[pi];
         lens[k] = plen[pi];
-        keys[k] = pair_anchor[pi];
+        keys[k] = pair_anchor[pi] >= 0 ? pair_anchor[pi] : n_anchors;
       }
       const int32_t nn = prefix_groups(np, s_tokens_host, starts.data(), lens.data(), keys.data(), min_shared,
                                        gof.data(), nf.data(), nl.data());
@@ -1480,12 +1485,14 @@ static quail_status join_run_core(quail_ctx* c, int32_t n_anchors, const int32_t
         }
     }
   }
-  // an anchor's uses: its ungrouped pairs plus one per node under it
+  // an anchor's uses: its ungrouped pairs plus one per node under it (a
+  // node of filter rows, anchor -1, is a plain anchor of its own)
   std::vector<int32_t> uses(n_anchors, 0);
   for (int32_t i = 0; i < n_pairs; ++i)
     if (pair_anchor[i] >= 0 && !grouped[i]) uses[pair_anchor[i]]++;
   for (auto& sn : step_nodes)
-    for (auto& nd : sn) uses[nd.anchor]++;
+    for (auto& nd : sn)
+      if (nd.anchor >= 0) uses[nd.anchor]++;
   // anchors in order of first use along the plan
   std::vector<int32_t> first_use;
   {
@@ -1578,7 +1585,7 @@ static quail_status join_run_core(quail_ctx* c, int32_t n_anchors, const int32_t
         nst[q] = nd.first;
         nln[q] = nd.len;
         nnu[q] = (int32_t)nd.members.size();
-        npar[q] = (int32_t)(handle[nd.anchor] & 0xFFFFFFFF);
+        npar[q] = nd.anchor >= 0 ? (int32_t)(handle[nd.anchor] & 0xFFFFFFFF) : -1;
       }
       if (quail_status r = anchor_core(c, nn, s_tokens, nst.data(), nln.data(), nnu.data(), nullptr, nh.data(), s,
                                        npar.data()))

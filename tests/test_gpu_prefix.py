@@ -33,10 +33,17 @@ def _pack(tok, ranges):
     return np.concatenate([tok[a:b] for a, b in ranges]).astype(np.int32), off
 
 
+def shared_keys(case):
+    """Grouping keys of the shared run: the anchor, or one key of their own
+    for filter rows (their shared prefix becomes a plain anchor)."""
+    pa = np.asarray(case["pair_anchor"])
+    return np.where(pa >= 0, pa, len(case["a_len"])).astype(np.int32)
+
+
 def shared_step_lengths(B, case, min_shared):
     """Tokens each pair computes with sharing, as the shared run sizes its
     plan steps: own tokens after the shared prefix + its share of the prefix."""
-    g, _, nl = B.quail_prefix_groups(case["s_tok"], case["s_off"], case["pair_anchor"], min_shared)
+    g, _, nl = B.quail_prefix_groups(case["s_tok"], case["s_off"], shared_keys(case), min_shared)
     s_len = np.diff(case["s_off"]).astype(np.int64)
     out = s_len.copy()
     for k in range(len(nl)):
@@ -197,9 +204,9 @@ def test_join_run_shared_matches_join_run(B):
     for b0, b1 in zip(bounds[:-1], bounds[1:]):
         idx = order[b0:b1]
         seqs = [case["s_tok"][case["s_off"][i]:case["s_off"][i + 1]] for i in idx]
-        expect += len(OPX.prefix_groups_reference(seqs, case["pair_anchor"][idx], 4)[1])
+        expect += len(OPX.prefix_groups_reference(seqs, shared_keys(case)[idx], 4)[1])
     nodes = s1["prefills"] - s0["prefills"] - used
-    assert nodes == expect and nodes >= 3, (nodes, expect)
+    assert nodes == expect and nodes >= 4, (nodes, expect)
     assert s1["evictions"] == s1["prefills"] and s1["resident"] == 0 and s1["regret_tokens"] == 0
     ref_logits, ref_dec, ref_margin = [], [], []
     for i in range(n):
@@ -308,3 +315,39 @@ def test_qwen3_shaped_layer_through_prefix_nodes(B):
         assert err <= 2e-2
     st = B.quail_pool_stats(ctx)
     assert st["prefills"] == 4 and st["evictions"] == 4 and st["resident"] == 0
+
+
+@pytest.mark.parametrize("kv_fp8", [False, True])
+def test_filter_rows_sharing_a_prefix(B, kv_fp8):
+    """Filter rows (no anchor) whose leading tokens repeat: each group's prefix
+    is prefilled once as a plain anchor and the rows run their own tokens after
+    it. Logits and decisions against the oracle's per-row forward (the shared
+    positions stored like anchor KV: E4M3 with an fp8 store)."""
+    import torch
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    shape = W.tiny_shape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                         intermediate=384, vocab=512, kv_fp8=kv_fp8)
+    wts = W.model_weights(shape, 14)
+    fam = [(-1, 70, [3, 9, 1]), (-1, 12, [20, 2]), (-1, 5, [6]), (-1, 40, [1, 1, 30, 4])]
+    case = W.shared_prefix_case(14, shape.vocab, [], fam)
+    n = len(case["pair_anchor"])
+    g, _, nl = B.quail_prefix_groups(case["s_tok"], case["s_off"], shared_keys(case), 8)
+    assert len(nl) == 3
+    dm = DeviceModel(shape, wts, max_anchor_len=1024, max_suffix_len=256)
+    ctx = dm.context(16 << 20, 256)
+    logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+    dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+    say("filter rows sharing prefixes", "fp8" if kv_fp8 else "bf16")
+    B.quail_join_run_shared(ctx, to_device(np.zeros(1, np.int32)), case["a_off"], case["pair_anchor"],
+                            to_device(case["s_tok"]), case["s_off"], case["s_tok"], 8, 0x0F, logits, None, dec)
+    torch.cuda.synchronize()
+    st = B.quail_pool_stats(ctx)
+    assert st["prefills"] == 3 and st["evictions"] == 3 and st["resident"] == 0
+    lg = logits.cpu().numpy()
+    ref = [OM.forward_pair([], case["s_tok"][case["s_off"][i]:case["s_off"][i + 1]], wts, shape,
+                           shared_len=int(nl[g[i]]) if g[i] >= 0 else 0) for i in range(n)]
+    ref_logits = np.array([r["logits"] for r in ref])
+    assert rel_inf(lg, ref_logits) <= 2e-2, rel_inf(lg, ref_logits)
+    ok, _ = decisions_agree(dec.cpu().numpy(), [r["decision"] for r in ref], [r["margin"] for r in ref],
+                            2e-2 * np.max(np.abs(ref_logits)))
+    assert ok
