@@ -526,12 +526,14 @@ def bench_multiplan(args):
 
 
 def bench_shared(args):
-    """Suffixes sharing prefixes (agent-trace shaped), 36-layer stack: 16
-    anchors x 1024 tokens, each probed by 16 families of 8 suffixes whose
-    first 384 tokens are the family's, then U{16..64} tokens of their own.
-    The join with shared-prefix nodes (quail_join_run_shared, min_shared 32)
-    against the plain join (quail_join_run) on the same inputs; the second of
-    two runs of each is timed."""
+    """Suffixes sharing prefixes, 36-layer stack. shared36: 16 anchors x 1024
+    tokens, each probed by 16 families of 8 suffixes whose first 384 tokens
+    are the family's, then U{16..64} tokens of their own. traces36 (agent-
+    trace shaped filter, no anchor): 128 families of 16 documents that repeat
+    a 768-token prefix, then U{32..128} tokens of their own. The run with
+    shared-prefix nodes (quail_join_run_shared, min_shared 32) against the
+    plain run (quail_join_run) on the same inputs; the second of two runs of
+    each is timed."""
     import torch
     import workloads as W
     from query_aware_prefill_amd import binding as B
@@ -539,19 +541,25 @@ def bench_shared(args):
     B.load()
     shape = W.QWEN3_4B
     r = np.random.default_rng([7, 0])
-    n_anchors, n_fam, per_fam, shared, min_shared = 16, 16, 8, 384, 32
-    fams = [(a, shared, r.integers(16, 65, per_fam).tolist()) for a in range(n_anchors) for _ in range(n_fam)]
+    traces = args.workload == "traces36"
+    min_shared = 32
+    if traces:
+        n_anchors, n_fam, per_fam, shared = 0, 128, 16, 768
+        fams = [(-1, shared, r.integers(32, 129, per_fam).tolist()) for _ in range(n_fam)]
+    else:
+        n_anchors, n_fam, per_fam, shared = 16, 16, 8, 384
+        fams = [(a, shared, r.integers(16, 65, per_fam).tolist()) for a in range(n_anchors) for _ in range(n_fam)]
     case = W.shared_prefix_case(7, shape.vocab, [1024] * n_anchors, fams, cfg_id=7)
     pa, s_off, s_tok = case["pair_anchor"], case["s_off"], case["s_tok"]
     a_len, a_off = case["a_len"], case["a_off"]
     s_len = np.diff(s_off)
     n = len(pa)
-    log(f"shared36: {n} pairs over {n_anchors} anchors, families of {per_fam} sharing {shared} tokens; "
+    log(f"{args.workload}: {n} rows over {n_anchors} anchors, families of {per_fam} sharing {shared} tokens; "
         "weights on device")
     wd = W.model_weights_device(shape, 0)
     dm = DeviceModel(shape, wd, max_anchor_len=1024, max_suffix_len=int(np.max(s_len)))
     T = 65536
-    pool = sum(B.quail_anchor_bytes(dm.cfg, int(x)) for x in a_len) + (4 << 30)
+    pool = sum(B.quail_anchor_bytes(dm.cfg, int(x)) for x in a_len) + (8 << 30)
     # tokens the shared run computes: the library's plan steps and grouping
     g_all, _, nl_all = B.quail_prefix_groups(s_tok, s_off, np.where(pa >= 0, pa, n_anchors).astype(np.int32),
                                              min_shared)
@@ -568,14 +576,22 @@ def bench_shared(args):
         g, _, nl = B.quail_prefix_groups(toks, offs, np.where(pa[idx] >= 0, pa[idx], n_anchors).astype(np.int32),
                                          min_shared)
         node_tok += int(np.sum(nl)) - int(np.sum(nl[g[g >= 0]]))
-    a_tok_d, s_tok_d = to_device(case["a_tok"].astype(np.int32)), to_device(s_tok.astype(np.int32))
-    logical = float(np.sum(a_len[pa] + s_len))
+    a_tok_d = to_device(case["a_tok"].astype(np.int32) if n_anchors else np.zeros(1, np.int32))
+    s_tok_d = to_device(s_tok.astype(np.int32))
+    logical = float(np.sum(np.where(pa >= 0, a_len[np.maximum(pa, 0)] if n_anchors else 0, 0) + s_len))
     prefilled = float(np.sum(a_len))
     computed = {"plain": prefilled + float(np.sum(s_len)), "shared": prefilled + float(np.sum(s_len)) + node_tok}
-    res = {"metric": "AI.IF join with shared suffix prefixes: two-level cascade vs plain join (36-layer stack)",
-           "workload": f"{n_anchors} anchors x 1024 tokens; {n_fam} families x {per_fam} suffixes per anchor, "
-                       f"{shared} shared tokens + U{{16..64}} own tokens each",
-           "pairs": int(n), "logical_tokens": logical}
+    if traces:
+        res = {"metric": "AI.IF filter over documents sharing prefixes: prefix prefilled once vs per row "
+                         "(36-layer stack)",
+               "workload": f"{n_fam} families x {per_fam} documents, {shared} shared tokens + U{{32..128}} own "
+                           "tokens each, no anchor",
+               "pairs": int(n), "logical_tokens": logical}
+    else:
+        res = {"metric": "AI.IF join with shared suffix prefixes: two-level cascade vs plain join (36-layer stack)",
+               "workload": f"{n_anchors} anchors x 1024 tokens; {n_fam} families x {per_fam} suffixes per anchor, "
+                           f"{shared} shared tokens + U{{16..64}} own tokens each",
+               "pairs": int(n), "logical_tokens": logical}
     out = {}
     for mode in (("shared",) if args.shared_only else ("shared", "plain")):
         ctx = dm.context(pool, T)
@@ -596,7 +612,7 @@ def bench_shared(args):
         res[mode] = {"ms": ms, "logical_tokens_per_min": logical / ms * 60e3,
                      "computed_tokens": computed[mode], "computed_tokens_per_min": computed[mode] / ms * 60e3,
                      "pool_over_two_runs": st}
-        log(f"shared36 {mode}: {ms / 1000:.2f} s, {computed[mode] / 1e6:.3f} M computed tokens, "
+        log(f"{args.workload} {mode}: {ms / 1000:.2f} s, {computed[mode] / 1e6:.3f} M computed tokens, "
             f"{logical / ms * 60e3 / 1e6:.1f} M logical tokens/min")
         del ctx
     if args.shared_only:
@@ -607,9 +623,9 @@ def bench_shared(args):
         # oracle leg on the shared run's outputs: the per-pair definition over
         # [anchor | whole suffix] (the shared prefix included)
         order = np.random.default_rng(1).permutation(n)[:8]
-        pairs = [(int(i), case["a_tok"][a_off[pa[i]]:a_off[pa[i] + 1]], s_tok[s_off[i]:s_off[i + 1]])
-                 for i in order]
-        log("shared36: oracle leg")
+        pairs = [(int(i), case["a_tok"][a_off[pa[i]]:a_off[pa[i] + 1]] if pa[i] >= 0 else np.zeros(0, np.int32),
+                  s_tok[s_off[i]:s_off[i + 1]]) for i in order]
+        log(f"{args.workload}: oracle leg")
         res["cpu_baseline"] = cpu_baseline_e2e(wd, shape, pairs, out["shared"][0].astype(np.float64), 0x0F,
                                                args.cpu_budget)
     ls, lp = out["shared"][0].astype(np.float64), out["plain"][0].astype(np.float64)
@@ -658,7 +674,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--workload", choices=["cascade", "gemm", "layer", "copy", "stream", "join36",
-                                           "filter36", "multijoin36", "multiplan36", "shared36", "search"],
+                                           "filter36", "multijoin36", "multiplan36", "shared36", "traces36",
+                                           "search"],
                     default="cascade")
     ap.add_argument("--rows", type=int, default=625, help="multijoin36: rows of the 5,000 used")
     ap.add_argument("--shared-only", action="store_true", help="shared36: run only the join with prefix nodes")
@@ -679,7 +696,7 @@ def main():
         return bench_stream(args)
     if args.workload == "multiplan36":
         return bench_multiplan(args)
-    if args.workload == "shared36":
+    if args.workload in ("shared36", "traces36"):
         return bench_shared(args)
     if args.workload == "search":
         return bench_search(args)

@@ -1,6 +1,9 @@
 // Host runtime of the AI.IF join-prefill library: argument validation and the
-// error model, the plan builder, the anchor-KV residency manager, per-batch
-// metadata, and the layer loop that enqueues the gfx950 kernels.
+// error model, the plan builders (one join; several joins over one anchor
+// table), the radix grouping of suffixes that share a prefix, the anchor-KV
+// residency manager (anchors and the prefix nodes that continue them), the
+// KV-aware join-order search, per-batch metadata, and the layer loop that
+// enqueues the gfx950 kernels.
 //
 // [pt] "Como funciona": the engine knows the whole plan, so it can predict KV
 // accesses and evict with no regret; each anchor's KV is computed once and the
