@@ -631,6 +631,13 @@ def bench_shared(args):
     ls, lp = out["shared"][0].astype(np.float64), out["plain"][0].astype(np.float64)
     res["logits_rel_inf_shared_vs_plain"] = float(np.max(np.abs(ls - lp)) / np.max(np.abs(lp)))
     res["decisions_equal_frac"] = float(np.mean(out["shared"][1] == out["plain"][1]))
+    # where the plain run's TRUE-vs-FALSE margin exceeds the tolerance
+    # (2e-2 of the largest |logit| of the pair), the decision is fixed
+    tmask = np.array([(0x0F >> j) & 1 for j in range(8)], bool)
+    margin = np.max(np.where(tmask, lp, -np.inf), axis=1) - np.max(np.where(~tmask, lp, -np.inf), axis=1)
+    sure = np.abs(margin) > 2e-2 * np.max(np.abs(lp), axis=1)
+    res["decisions_beyond_tau"] = int(np.sum(sure))
+    res["decisions_beyond_tau_equal"] = int(np.sum(out["shared"][1][sure] == out["plain"][1][sure]))
     print(json.dumps(res), flush=True)
 
 
