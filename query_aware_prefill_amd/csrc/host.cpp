@@ -183,11 +183,17 @@ struct WsLayout {
   size_t meta_cap;
 };
 
-size_t meta_capacity(int32_t T) {
+// KV-source table entries reserved per batch: the table holds every source
+// once per layer, and batches are cut so that it fits (max_batch_srcs).
+size_t src_entries(int32_t T, int32_t n_layers) {
+  return std::max<size_t>((size_t)T + 2, (size_t)4 * std::max(n_layers, 1));
+}
+
+size_t meta_capacity(int32_t T, int32_t n_layers) {
   // tok_src, pos, seg_lo, kv_lapad, last_idx, out_idx (int32), kv_row (int64),
-  // tiles (<= T + 64), srcs (<= T + 2), plus alignment slack
+  // tiles (<= T + 64), per-layer source tables, plus alignment slack
   return align_up((size_t)T * 4) * 6 + align_up((size_t)T * 8) +
-         align_up((size_t)(T + 64) * sizeof(AttnTile)) + align_up((size_t)(T + 2) * sizeof(KVSrc)) +
+         align_up((size_t)(T + 64) * sizeof(AttnTile)) + align_up(src_entries(T, n_layers) * sizeof(KVSrc)) +
          16 * kAlign;
 }
 
@@ -205,7 +211,7 @@ WsLayout ws_layout(const quail_model_config& c, int32_t T) {
   w.o = take(Tt * c.n_q_heads * c.head_dim * 2);
   w.m = take(Tt * c.intermediate * 2);
   w.hlast = take(Tt * c.hidden * 2);
-  w.meta_cap = meta_capacity(T);
+  w.meta_cap = meta_capacity(T, c.n_layers);
   w.meta = take(w.meta_cap);
   w.total = off;
   return w;
@@ -718,6 +724,28 @@ int32_t slab_src(quail_ctx* c, Batch& b, int32_t slot, std::unordered_map<int32_
   return idx;
 }
 
+// Sources one batch may read (suffix K/V and slabs) so that its per-layer
+// source tables fit the metadata region: at least 4 (suffix K/V, a node and
+// its anchor, and one more).
+int32_t max_batch_srcs(const quail_ctx* c) {
+  return (int32_t)(src_entries(c->T, c->cfg.n_layers) / std::max(c->cfg.n_layers, 1));
+}
+
+// Slab sources that reading slot `sl` adds to a batch whose slabs are `in`
+// (the slot itself, and a node's anchor), recording them.
+int32_t add_slab_srcs(const quail_ctx* c, int32_t sl, std::unordered_set<int32_t>& in, bool commit) {
+  int32_t add = 0;
+  if (sl < 0) return 0;
+  const int32_t par = c->slots[sl].parent;
+  if (!in.count(sl)) ++add;
+  if (par >= 0 && !in.count(par)) ++add;
+  if (commit) {
+    in.insert(sl);
+    if (par >= 0) in.insert(par);
+  }
+  return add;
+}
+
 quail_status check_offsets(int32_t n, const int32_t* off, int32_t lo, int32_t hi, const char* what) {
   if (n < 0) return fail(QUAIL_E_INVAL, "%s: negative count", what);
   if (n > 0 && !off) return fail(QUAIL_E_INVAL, "%s: offsets are NULL", what);
@@ -798,9 +826,13 @@ quail_status anchor_core(quail_ctx* c, int32_t n, const int32_t* tokens, const i
     Batch b;
     b.anchor_mode = true;
     int32_t a1 = a0;
-    int32_t tok = 0, max_len = 0;
+    int32_t tok = 0, max_len = 0, nsrc = 0;
+    std::unordered_set<int32_t> in;
     while (a1 < n && (n_uses[a1] == 0 || tok + lens[a1] <= c->T)) {
       if (n_uses[a1] > 0) {
+        const int32_t add = add_slab_srcs(c, slot_of[a1], in, false);
+        if (tok > 0 && nsrc + add > max_batch_srcs(c)) break;
+        nsrc += add_slab_srcs(c, slot_of[a1], in, true);
         tok += lens[a1];
         max_len = std::max(max_len, lens[a1]);
       }
@@ -1251,8 +1283,12 @@ quail_status join_core(quail_ctx* c, int32_t n, const quail_anchor* ha, const in
   while (p0 < n) {
     Batch b;
     b.anchor_mode = false;
-    int32_t p1 = p0, tok = 0;
+    int32_t p1 = p0, tok = 0, nsrc = 1;   // source 0: the batch's suffix K/V
+    std::unordered_set<int32_t> in;
     while (p1 < n && tok + lens[order[p1]] <= c->T) {
+      const int32_t add = add_slab_srcs(c, slot[order[p1]], in, false);
+      if (p1 > p0 && nsrc + add > max_batch_srcs(c)) break;
+      nsrc += add_slab_srcs(c, slot[order[p1]], in, true);
       tok += lens[order[p1]];
       ++p1;
     }

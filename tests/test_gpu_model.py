@@ -306,3 +306,32 @@ def test_multijoin_run_keeps_anchors_across_joins(B):
         assert rel_inf(results["ample"][0][i], ref["logits"]) <= 2e-2
         if abs(ref["margin"]) > 2e-2 * np.max(np.abs(ref["logits"])):
             assert results["ample"][1][i] == ref["decision"]
+
+
+def test_many_anchors_per_batch_split_by_source_table(B):
+    """60 anchors with one 1-token suffix each, 6 layers, a 64-token batch:
+    one batch would read 61 KV sources, whose per-layer tables exceed the
+    batch metadata region; batches are cut so they fit (anchor prefill and
+    join alike), and every pair matches the oracle."""
+    import torch
+    shape = W.tiny_shape(n_layers=6, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                         intermediate=384, vocab=512)
+    a_len = [3] * 60
+    pairs = [(a, 1) for a in range(60)]
+    wts, case, dm, ctx, a_tok, s_tok = _setup(shape, 15, a_len, pairs, B, mbt=64)
+    n = len(pairs)
+    logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+    dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+    say("many anchors per batch: join_run")
+    B.quail_join_run(ctx, a_tok, case["a_off"], case["pair_anchor"], s_tok, case["s_off"], 0x0F, logits, None, dec)
+    torch.cuda.synchronize()
+    ref = [OM.forward_pair(case["a_tok"][case["a_off"][a]:case["a_off"][a + 1]],
+                           case["s_tok"][case["s_off"][i]:case["s_off"][i + 1]], wts, shape)
+           for i, (a, _) in enumerate(pairs)]
+    ref_logits = np.array([r["logits"] for r in ref])
+    assert rel_inf(logits.cpu().numpy(), ref_logits) <= 2e-2
+    ok, _ = decisions_agree(dec.cpu().numpy(), [r["decision"] for r in ref], [r["margin"] for r in ref],
+                            2e-2 * np.max(np.abs(ref_logits)))
+    assert ok
+    st = B.quail_pool_stats(ctx)
+    assert st["prefills"] == 60 and st["evictions"] == 60 and st["resident"] == 0
