@@ -567,7 +567,8 @@ def bench_shared(args):
     for k in range(len(nl_all)):          # the shared run sizes its steps by computed tokens
         m = np.flatnonzero(g_all == k)
         step_len[m] = s_len[m] - nl_all[k] + (nl_all[k] + len(m) - 1) // len(m)
-    order, bounds, _ = B.quail_plan_build(dm.cfg, pool, T, a_len, pa, step_len.astype(np.int32))
+    reserve = B.quail_anchor_bytes(dm.cfg, int(np.max(s_len)))   # room kept for a prefix node
+    order, bounds, _ = B.quail_plan_build(dm.cfg, pool - reserve, T, a_len, pa, step_len.astype(np.int32))
     node_tok = 0
     for b0, b1 in zip(bounds[:-1], bounds[1:]):
         idx = order[b0:b1]

@@ -368,7 +368,10 @@ quail_status quail_join_run(quail_ctx* ctx, int32_t n_anchors, const int32_t* a_
  * prefix plus its share of the prefix). Outputs equal quail_join_run's up to
  * floating-point rounding (the cascade split is exact), except that with an
  * fp8 KV store the shared positions are stored in E4M3 like anchor KV.
- * min_shared >= 1; other arguments as quail_join_run. */
+ * The plan is built against the largest free pool block less the slab of
+ * the longest possible prefix node (the longest pair), so nodes fit beside
+ * their step's anchors; E_NOMEM, before anything is enqueued, when that
+ * leaves nothing. min_shared >= 1; other arguments as quail_join_run. */
 quail_status quail_join_run_shared(quail_ctx* ctx, int32_t n_anchors, const int32_t* a_tokens,
                                    const int32_t* a_offsets, int32_t n_pairs,
                                    const int32_t* pair_anchor, const int32_t* s_tokens,

@@ -1468,9 +1468,18 @@ static quail_status join_run_core(quail_ctx* c, int32_t n_anchors, const int32_t
     slab[a] = slab_bytes(c->cfg, alen[a]);
   }
   for (int32_t i = 0; i < n_pairs; ++i) plen[i] = s_offsets[i + 1] - s_offsets[i];
-  // the plan is built against the largest free block of the pool now
+  // the plan is built against the largest free block of the pool now; with
+  // sharing, less the slab of the longest possible prefix node, so that a
+  // step's nodes fit beside its anchors
   size_t free_bytes = 0;
   for (auto& f : c->free_list) free_bytes = std::max(free_bytes, f.second);
+  if (min_shared > 0) {
+    const size_t reserve = slab_bytes(c->cfg, *std::max_element(plen.begin(), plen.end()));
+    if (free_bytes <= reserve)
+      return fail(QUAIL_E_NOMEM, "KV pool (largest free block %zu B) leaves no room for a prefix node (%zu B)",
+                  free_bytes, reserve);
+    free_bytes -= reserve;
+  }
   // With sharing, steps are sized by the tokens each pair will compute: its
   // own tokens after the prefix it shares, plus its share of that prefix
   // (grouping all pairs of each anchor); steps are regrouped below.

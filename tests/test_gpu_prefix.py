@@ -198,7 +198,9 @@ def test_join_run_shared_matches_join_run(B):
     assert s0["prefills"] == used and s0["regret_tokens"] == 0
     # nodes: the oracle's grouping of each plan step's pairs (plan from the
     # library's builder, pool fully free as at the shared run's start)
-    order, bounds, _ = B.quail_plan_build(dm.cfg, 64 << 20, 128, a_len, case["pair_anchor"],
+    # the shared run plans against the pool less the slab of its longest possible prefix node
+    reserve = B.quail_anchor_bytes(dm.cfg, int(np.max(case["s_len"])))
+    order, bounds, _ = B.quail_plan_build(dm.cfg, (64 << 20) - reserve, 128, a_len, case["pair_anchor"],
                                           shared_step_lengths(B, case, 4))
     expect = 0
     for b0, b1 in zip(bounds[:-1], bounds[1:]):
@@ -351,3 +353,23 @@ def test_filter_rows_sharing_a_prefix(B, kv_fp8):
     ok, _ = decisions_agree(dec.cpu().numpy(), [r["decision"] for r in ref], [r["margin"] for r in ref],
                             2e-2 * np.max(np.abs(ref_logits)))
     assert ok
+
+
+def test_join_run_shared_rejects_a_pool_without_room_for_a_node(B):
+    """A pool that holds the anchors but not one more slab: E_NOMEM before
+    anything is enqueued, and nothing stays resident."""
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    shape = W.tiny_shape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                         intermediate=384, vocab=512)
+    wts = W.model_weights(shape, 16)
+    case = W.shared_prefix_case(16, shape.vocab, [60], [(0, 40, [3, 4])])
+    dm = DeviceModel(shape, wts, max_anchor_len=1024, max_suffix_len=256)
+    ctx = dm.context(B.quail_anchor_bytes(dm.cfg, 60) + 4096, 512)
+    import torch
+    dec = torch.empty(2, dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.QuailError) as e:
+        B.quail_join_run_shared(ctx, to_device(case["a_tok"]), case["a_off"], case["pair_anchor"],
+                                to_device(case["s_tok"]), case["s_off"], case["s_tok"], 8, 0x0F, None, None, dec)
+    assert e.value.status == B.E_NOMEM
+    st = B.quail_pool_stats(ctx)
+    assert st["prefills"] == 0 and st["resident"] == 0
