@@ -335,3 +335,42 @@ def test_many_anchors_per_batch_split_by_source_table(B):
     assert ok
     st = B.quail_pool_stats(ctx)
     assert st["prefills"] == 60 and st["evictions"] == 60 and st["resident"] == 0
+
+
+def test_c2_full_size_layer_sampled(B):
+    """The one-layer workload at full size in the launch configuration the
+    bench times (16 anchors x 1024 tokens, 512 suffixes x 64 tokens each,
+    8,192 pairs, 65,536-token batches, Qwen3-4B layer shapes): logits of
+    sampled pairs (first and last pair of the first and last anchor, two
+    more) against the oracle's per-pair forward, decisions where the margin
+    exceeds the tolerance."""
+    import torch
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    shape = W.ModelShape(n_layers=1, hidden=2560, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                         intermediate=9728, vocab=W.QWEN3_4B.vocab)
+    say("C2 full size: weights and workload")
+    wts = W.model_weights(shape, 0)
+    case = W.c2_case(seed=2)
+    n = len(case["pair_anchor"])
+    dm = DeviceModel(shape, wts, max_anchor_len=1024, max_suffix_len=64)
+    ctx = dm.context(16 * B.quail_anchor_bytes(dm.cfg, 1024) + (1 << 20), 65536)
+    logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+    dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+    say("C2 full size: join_run over", n, "pairs")
+    B.quail_join_run(ctx, to_device(case["a_tok"]), case["a_off"], case["pair_anchor"], to_device(case["s_tok"]),
+                     case["s_off"], 0x0F, logits, None, dec)
+    torch.cuda.synchronize()
+    lg, dg = logits.cpu().numpy(), dec.cpu().numpy()
+    st = B.quail_pool_stats(ctx)
+    assert st["prefills"] == 16 and st["evictions"] == 16 and st["regret_tokens"] == 0
+    sample = [0, 511, 8192 - 512, 8191] + np.random.default_rng(2).integers(0, n, 2).tolist()
+    say("C2 full size: oracle on pairs", sample)
+    for i in sample:
+        a = int(case["pair_anchor"][i])
+        ref = OM.forward_pair(case["a_tok"][case["a_off"][a]:case["a_off"][a + 1]],
+                              case["s_tok"][case["s_off"][i]:case["s_off"][i + 1]], wts, shape)
+        err = rel_inf(lg[i], ref["logits"])
+        say("  pair", i, "rel", err)
+        assert err <= 2e-2, (i, err)
+        if abs(ref["margin"]) > 2e-2 * np.max(np.abs(ref["logits"])):
+            assert dg[i] == ref["decision"], i
