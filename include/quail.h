@@ -283,9 +283,13 @@ quail_status quail_prefix_groups(int32_t n, const int32_t* tokens, const int32_t
 
 /* Prefills prefix nodes: node a = tokens[offsets[a] .. offsets[a+1]) (dev
  * int32; host offsets [n+1], lengths in [1, max_batch_tokens]) continues
- * anchor parent[a] (host handle of a live anchor that is not itself a node)
+ * parent[a] (host handle of a live anchor or node). Under an anchor it sits
  * at positions La.. : it attends to every key of the anchor and causally to
  * itself, and every layer's K/V goes to a slab of its own, as for an anchor.
+ * Under a node P (a nested level) it continues P's anchor after P's tokens:
+ * its slab starts with a copy of P's rows, its own tokens follow, and it
+ * spends one of P's declared uses once its prefill is enqueued (P may then
+ * be evicted; the copy precedes any reuse in stream order).
  * n_uses: host [n], the pairs that will name the node (0 = not prefilled,
  * handle QUAIL_NO_ANCHOR). Each node holds one of its anchor's declared uses
  * and spends it when the node is evicted, so the anchor outlives its nodes.
@@ -293,9 +297,9 @@ quail_status quail_prefix_groups(int32_t n, const int32_t* tokens, const int32_t
  * positions La + Lp.. against the anchor's keys, the node's keys (both
  * unmasked) and its own keys (causal): the same result as the full suffix
  * [node tokens ‖ pair tokens] after the anchor. out: host [n] handles.
- * E_STALE: a parent handle is stale or has no use to spare; E_INVAL: a parent
- * is a node, or La + Lp + 1 exceeds max_anchor_len + max_suffix_len; E_NOMEM
- * as quail_anchor_prefill. */
+ * E_STALE: a parent handle is stale, or the anchor (or parent node) has no
+ * declared use to spare; E_INVAL: La + (all node rows) + 1 exceeds
+ * max_anchor_len + max_suffix_len; E_NOMEM as quail_anchor_prefill. */
 quail_status quail_prefix_prefill(quail_ctx* ctx, int32_t n, const quail_anchor* parent,
                                   const int32_t* tokens, const int32_t* offsets,
                                   const int32_t* n_uses, quail_anchor* out, quail_stream stream);

@@ -475,6 +475,9 @@ struct quail_ctx {
     // anchor's uses until it is evicted; `held` counts such holds on an anchor
     int32_t parent = -1, pos0 = 0;
     int64_t held = 0;
+    // nested node: its first `copied` slab rows are its parent node's rows
+    // (copied at prefill), then its own tokens
+    int32_t copied = 0;
   };
   std::vector<Slot> slots;
   std::vector<int32_t> free_slots;
@@ -766,9 +769,13 @@ hipStream_t as_stream(quail_stream s) { return reinterpret_cast<hipStream_t>(s);
 // attend to the whole anchor (cross) and causally to themselves (its own
 // slab); the caller has checked that each parent has a use to spare per node.
 // parents[a] = -1 is a plain anchor (the shared prefix of filter rows).
+// With copy_from[a] >= 0 (a node slot), entry a is a nested node: its slab
+// starts with that node's rows (copied here), and its own lens[a] tokens
+// follow at positions La + (copied rows)..
 quail_status anchor_core(quail_ctx* c, int32_t n, const int32_t* tokens, const int32_t* starts,
                          const int32_t* lens, const int32_t* n_uses, const int64_t* anchor_ids,
-                         quail_anchor* out, hipStream_t s, const int32_t* parents = nullptr) {
+                         quail_anchor* out, hipStream_t s, const int32_t* parents = nullptr,
+                         const int32_t* copy_from = nullptr) {
   if (!n_uses || !out) return fail(QUAIL_E_INVAL, "n_uses and out are required");
   if (!tokens) return fail(QUAIL_E_INVAL, "tokens is NULL");
   for (int32_t a = 0; a < n; ++a)
@@ -776,9 +783,10 @@ quail_status anchor_core(quail_ctx* c, int32_t n, const int32_t* tokens, const i
   // carve all slabs first (all or nothing)
   std::vector<std::pair<size_t, size_t>> got;
   std::vector<int32_t> slot_of(n, -1);
+  auto copied_rows = [&](int32_t a) { return copy_from && copy_from[a] >= 0 ? c->slots[copy_from[a]].len : 0; };
   for (int32_t a = 0; a < n; ++a) {
     if (n_uses[a] == 0) continue;
-    const size_t bytes = slab_bytes(c->cfg, lens[a]);
+    const size_t bytes = slab_bytes(c->cfg, copied_rows(a) + lens[a]);
     size_t off;
     if (!c->alloc(bytes, off)) {
       for (auto& g : got) c->release(g.first, g.second);
@@ -797,7 +805,8 @@ quail_status anchor_core(quail_ctx* c, int32_t n, const int32_t* tokens, const i
     sl.off = got[gi].first;
     sl.bytes = got[gi].second;
     ++gi;
-    sl.len = lens[a];
+    sl.copied = copied_rows(a);
+    sl.len = sl.copied + lens[a];
     sl.lapad = pad_len(sl.len);
     sl.uses = n_uses[a];
     sl.held = 0;
@@ -820,6 +829,16 @@ quail_status anchor_core(quail_ctx* c, int32_t n, const int32_t* tokens, const i
   const int G = cf.n_q_heads / cf.n_kv_heads;
   const size_t esz = kv_elem_bytes(cf);
   const bool slab_fp8 = cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3;
+  // nested nodes: the parent node's rows, every layer, K and V, every kv head
+  for (int32_t a = 0; a < n && copy_from; ++a) {
+    if (n_uses[a] == 0 || copy_from[a] < 0) continue;
+    const quail_ctx::Slot& from = c->slots[copy_from[a]];
+    const quail_ctx::Slot& to = c->slots[slot_of[a]];
+    const int32_t row_bytes = (int32_t)(kHeadDim * esz);
+    HIP_TRY(launch_copy_slab_rows(c->pool + from.off, (int64_t)from.lapad * row_bytes, c->pool + to.off,
+                                  (int64_t)to.lapad * row_bytes, to.copied, row_bytes,
+                                  cf.n_layers * 2 * cf.n_kv_heads, s));
+  }
   // batches of whole anchors up to T tokens
   int32_t a0 = 0;
   while (a0 < n) {
@@ -852,25 +871,27 @@ quail_status anchor_core(quail_ctx* c, int32_t n, const int32_t* tokens, const i
       const int32_t cross = sl.parent >= 0 ? slab_src(c, b, sl.parent, parent_src) : -1;
       const int32_t src = (int32_t)b.srcs.size();
       push_slab_src(c, b, sl);
-      for (int32_t t = 0; t < sl.len; ++t) {
+      // own tokens: slab rows copied.., positions pos0 + copied..
+      const int32_t own = sl.len - sl.copied;
+      for (int32_t t = 0; t < own; ++t) {
         b.tok_src.push_back(starts[a] + t);
-        b.pos.push_back(sl.pos0 + t);
+        b.pos.push_back(sl.pos0 + sl.copied + t);
         b.seg_lo.push_back(0);
-        b.kv_row.push_back((int64_t)(sl.off / esz) + (int64_t)t * kHeadDim);
+        b.kv_row.push_back((int64_t)(sl.off / esz) + (int64_t)(sl.copied + t) * kHeadDim);
         b.kv_lapad.push_back(sl.lapad);
       }
-      for (int32_t t0 = 0; t0 < sl.len; t0 += TQ) {
+      for (int32_t t0 = 0; t0 < own; t0 += TQ) {
         AttnTile tl{};
         tl.cross2 = -1;
         tl.q0 = r0 + t0;
-        tl.nq = std::min(TQ, sl.len - t0);
+        tl.nq = std::min(TQ, own - t0);
         tl.cross = cross;
         tl.self = src;
-        tl.self_qbase = t0;
+        tl.self_qbase = sl.copied + t0;
         tl.self_k0 = 0;
         b.tiles.push_back(tl);
       }
-      b.n_tok += sl.len;
+      b.n_tok += own;
     }
     if (quail_status st = run_batch(c, b, tokens, nullptr, nullptr, s)) return st;
     a0 = a1;
@@ -1222,24 +1243,40 @@ quail_status quail_prefix_prefill(quail_ctx* c, int32_t n, const quail_anchor* p
   if (n == 0) return QUAIL_OK;
   if (!parent || !n_uses || !out) return fail(QUAIL_E_INVAL, "parent, n_uses and out are required");
   if (quail_status st = check_offsets(n, offsets, 1, c->T, "prefix node")) return st;
-  std::vector<int32_t> starts(n), lens(n), par(n);
+  // a parent that is itself a node: the new node continues it (nested
+  // level) -- it copies that node's rows, continues the same anchor, and
+  // spends one of the parent node's uses once its prefill is enqueued
+  std::vector<int32_t> starts(n), lens(n), par(n), from(n, -1);
   std::unordered_map<int32_t, int64_t> need;
   for (int32_t a = 0; a < n; ++a) {
     starts[a] = offsets[a];
     lens[a] = offsets[a + 1] - offsets[a];
     quail_ctx::Slot* ps = c->lookup(parent[a]);
-    if (!ps) return fail(QUAIL_E_STALE, "node %d: anchor handle %lld is stale", a, (long long)parent[a]);
-    if (ps->parent >= 0)
-      return fail(QUAIL_E_INVAL, "node %d: its anchor is itself a prefix node (one shared-prefix level)", a);
+    if (!ps) return fail(QUAIL_E_STALE, "node %d: parent handle %lld is stale", a, (long long)parent[a]);
     if (n_uses[a] < 0) return fail(QUAIL_E_INVAL, "node %d: negative use count", a);
-    par[a] = (int32_t)(parent[a] & 0xFFFFFFFF);
-    if (n_uses[a] > 0 && ++need[par[a]] > ps->uses - ps->held)
-      return fail(QUAIL_E_STALE, "node %d: its anchor has no declared use to spare", a);
-    if ((int64_t)ps->len + lens[a] + 1 > max_pos(c->cfg))
+    const int32_t ps_slot = (int32_t)(parent[a] & 0xFFFFFFFF);
+    if (ps->parent >= 0) from[a] = ps_slot;
+    par[a] = ps->parent >= 0 ? ps->parent : ps_slot;
+    const quail_ctx::Slot& anc = c->slots[par[a]];
+    if (n_uses[a] > 0) {
+      if (++need[par[a]] > anc.uses - anc.held)
+        return fail(QUAIL_E_STALE, "node %d: its anchor has no declared use to spare", a);
+      if (from[a] >= 0 && ++need[from[a]] > ps->uses - ps->held)
+        return fail(QUAIL_E_STALE, "node %d: its parent node has no declared use to spare", a);
+    }
+    const int64_t rows = (from[a] >= 0 ? ps->len : 0) + (int64_t)lens[a];
+    if ((int64_t)anc.len + rows + 1 > max_pos(c->cfg))
       return fail(QUAIL_E_INVAL, "node %d: anchor + prefix leaves no position for a suffix token", a);
   }
-  return anchor_core(c, n, tokens, starts.data(), lens.data(), n_uses, nullptr, out, as_stream(stream),
-                     par.data());
+  if (quail_status st = anchor_core(c, n, tokens, starts.data(), lens.data(), n_uses, nullptr, out,
+                                    as_stream(stream), par.data(), from.data()))
+    return st;
+  for (int32_t a = 0; a < n; ++a) {
+    if (n_uses[a] == 0 || from[a] < 0) continue;
+    quail_ctx::Slot& ps = c->slots[from[a]];
+    if (--ps.uses == 0) c->evict(from[a]);
+  }
+  return QUAIL_OK;
 }
 
 }  // extern "C"

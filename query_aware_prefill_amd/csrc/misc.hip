@@ -51,6 +51,31 @@ hipError_t launch_copy_rows(const uint16_t* src, int64_t lds, const int32_t* src
   return hipGetLastError();
 }
 
+// The first `rows` rows of every (layer, K|V, kv head) block of one slab into
+// the same rows of another slab whose blocks are longer: each block is
+// [padded length][head_dim], so those rows are one contiguous run of
+// rows x row_chunks 16-byte chunks at the start of the block.
+__global__ void __launch_bounds__(256) copy_slab_rows_kernel(const uint8_t* src, int64_t src_block,
+                                                             uint8_t* dst, int64_t dst_block,
+                                                             int64_t per_block, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int64_t b = i / per_block, c = i - b * per_block;
+  reinterpret_cast<uint4*>(dst + b * dst_block)[c] = reinterpret_cast<const uint4*>(src + b * src_block)[c];
+}
+
+hipError_t launch_copy_slab_rows(const uint8_t* src, int64_t src_block, uint8_t* dst, int64_t dst_block,
+                                 int32_t rows, int32_t row_bytes, int32_t n_blocks, hipStream_t s) {
+  if (rows <= 0 || n_blocks <= 0) return hipSuccess;
+  if (row_bytes % 16 != 0 || (int64_t)rows * row_bytes > src_block || (int64_t)rows * row_bytes > dst_block)
+    return hipErrorInvalidValue;
+  const int64_t per_block = (int64_t)rows * (row_bytes / 16);
+  const int64_t total = per_block * n_blocks;
+  copy_slab_rows_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(src, src_block, dst, dst_block,
+                                                                                     per_block, total);
+  return hipGetLastError();
+}
+
 // y = bf16(x / sqrt(mean(x^2) + eps) * gamma)
 __global__ void __launch_bounds__(256) rmsnorm_kernel(NormParams p) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);

@@ -137,6 +137,10 @@ hipError_t launch_embed(const int32_t* tokens, const int32_t* tok_map, const uin
 hipError_t launch_copy_rows(const uint16_t* src, int64_t lds, const int32_t* src_idx,
                             uint16_t* dst, int64_t ldd, const int32_t* dst_idx, int32_t rows,
                             int32_t H, hipStream_t s);
+// rows 0..rows-1 of each of n_blocks slab blocks (src_block / dst_block bytes
+// apart) into the same rows of another slab's blocks
+hipError_t launch_copy_slab_rows(const uint8_t* src, int64_t src_block, uint8_t* dst, int64_t dst_block,
+                                 int32_t rows, int32_t row_bytes, int32_t n_blocks, hipStream_t s);
 hipError_t launch_head8(const Head8Params& p, hipStream_t s);
 hipError_t launch_head8_f32(int32_t n, int32_t H, const float* x, const float* w8,
                             uint32_t true_mask, float* logits, uint8_t* token,

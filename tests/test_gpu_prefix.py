@@ -109,13 +109,14 @@ def test_two_level_cascade_model(B, kv_fp8, k_scale, v_scale):
             else:
                 for got, stored, pre in ((kk, kv[l][0][la:], kv[l][2][la:]), (vv, kv[l][1][la:], kv[l][3][la:])):
                     _fp8_codes_valid(got, stored, pre)
-    # an anchor with live nodes cannot be released; a node cannot be a parent
+    # an anchor with live nodes cannot be released; an anchor whose declared
+    # uses are all held cannot take another node
     with pytest.raises(B.QuailError) as e:
         B.quail_anchor_release(ctx, handles[1])
     assert e.value.status == B.E_INVAL
     with pytest.raises(B.QuailError) as e:
-        B.quail_prefix_prefill(ctx, [nh[0]], to_device(node_tok[:4]), [0, 4], [1])
-    assert e.value.status == B.E_INVAL
+        B.quail_prefix_prefill(ctx, [handles[0]], to_device(node_tok[:4]), [0, 4], [1])
+    assert e.value.status == B.E_STALE
     # joins: the members of the short nodes (few tokens per node: packed
     # tiles), then everything else (node members and ungrouped pairs)
     order_a = [i for i in range(n) if g[i] >= 0 and nlen[g[i]] <= 16 and
@@ -373,3 +374,59 @@ def test_join_run_shared_rejects_a_pool_without_room_for_a_node(B):
     assert e.value.status == B.E_NOMEM
     st = B.quail_pool_stats(ctx)
     assert st["prefills"] == 0 and st["resident"] == 0
+
+
+@pytest.mark.parametrize("kv_fp8", [False, True])
+def test_nested_prefix_nodes(B, kv_fp8):
+    """anchor (70 tokens) -> node P (30 shared tokens) -> node N (20 more):
+    N's slab starts with P's rows (copied) and continues at positions 100..;
+    one join mixes a direct anchor pair, a member of P and two members of N.
+    Logits against the oracle's per-pair forward, N's own rows against the
+    oracle's K/V, residency through the chain."""
+    import torch
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    shape = W.tiny_shape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                         intermediate=384, vocab=512, kv_fp8=kv_fp8)
+    wts = W.model_weights(shape, 17)
+    r = np.random.default_rng(17)
+    a_tok = r.integers(0, 512, 70).astype(np.int32)
+    lvl1, lvl2 = r.integers(0, 512, 30).astype(np.int32), r.integers(0, 512, 20).astype(np.int32)
+    own = [r.integers(0, 512, k).astype(np.int32) for k in (9, 5, 7, 1)]
+    suffixes = [own[0], np.concatenate([lvl1, own[1]]), np.concatenate([lvl1, lvl2, own[2]]),
+                np.concatenate([lvl1, lvl2, own[3]])]
+    shared = [0, 30, 50, 50]
+    dm = DeviceModel(shape, wts, max_anchor_len=1024, max_suffix_len=256)
+    ctx = dm.context(8 << 20, 256)
+    say("nested nodes: anchor, P, N", "fp8" if kv_fp8 else "bf16")
+    ha = B.quail_anchor_prefill(ctx, to_device(a_tok), [0, 70], [3])       # direct pair, P, N
+    hp = B.quail_prefix_prefill(ctx, ha, to_device(lvl1), [0, 30], [2])     # member of P, N
+    hn = B.quail_prefix_prefill(ctx, hp, to_device(lvl2), [0, 20], [2])     # two members
+    torch.cuda.synchronize()
+    kp, vp = _slab(ctx, hp[0], 1, B, shape)
+    kn, vn = _slab(ctx, hn[0], 1, B, shape)
+    assert kn.shape[0] == 50 and np.array_equal(kn[:30], kp) and np.array_equal(vn[:30], vp)
+    _, kv = OM.forward_tokens(np.concatenate([a_tok, lvl1, lvl2]), wts, shape, return_kv=True,
+                              fp8_kv_upto=120 if kv_fp8 else 0)
+    if not kv_fp8:
+        assert rel_inf(kn[30:], kv[1][0][100:120]) <= 2e-2 and rel_inf(vn[30:], kv[1][1][100:120]) <= 2e-2
+    else:
+        _fp8_codes_valid(kn[30:], kv[1][0][100:120], kv[1][2][100:120])
+        _fp8_codes_valid(vn[30:], kv[1][1][100:120], kv[1][3][100:120])
+    tails, toff = _pack(np.concatenate(own), [(0, 9), (9, 14), (14, 21), (21, 22)])
+    h_last = torch.empty((4, shape.hidden), dtype=torch.int16, device="cuda")
+    say("nested nodes: join")
+    B.quail_join_prefill(ctx, [ha[0], hp[0], hn[0], hn[0]], to_device(tails), toff, h_last)
+    logits = torch.empty((4, 8), dtype=torch.float32, device="cuda")
+    tok = torch.empty(4, dtype=torch.uint8, device="cuda")
+    dec = torch.empty(4, dtype=torch.uint8, device="cuda")
+    B.quail_head8(ctx, h_last, 0x0F, logits, tok, dec)
+    torch.cuda.synchronize()
+    ref = [OM.forward_pair(a_tok, suffixes[i], wts, shape, shared_len=shared[i]) for i in range(4)]
+    ref_logits = np.array([x["logits"] for x in ref])
+    lg = logits.cpu().numpy()
+    assert rel_inf(lg, ref_logits) <= 2e-2, rel_inf(lg, ref_logits)
+    ok, _ = decisions_agree(dec.cpu().numpy(), [x["decision"] for x in ref], [x["margin"] for x in ref],
+                            2e-2 * np.max(np.abs(ref_logits)))
+    assert ok
+    st = B.quail_pool_stats(ctx)
+    assert st["prefills"] == 3 and st["evictions"] == 3 and st["resident"] == 0
