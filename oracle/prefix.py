@@ -59,3 +59,50 @@ def prefix_groups_reference(seqs, keys, min_len):
         group_of[members] = g
     return (group_of, np.array([x[0] for x in nodes], np.int32),
             np.array([x[1] for x in nodes], np.int32))
+
+
+def prefix_tree_reference(seqs, keys, min_len):
+    """Nested shared prefixes (reading): the groups of ``prefix_groups_reference``
+    are the top level; inside a node that covers tokens [.., l) its members are
+    split by their token at position l, and a part of two or more whose own
+    common prefix (cut to leave each member a token) reaches l + min_len
+    becomes a child node covering [l, l'), recursively; everyone else stays a
+    direct member of the node.
+
+    Returns (group_of [n] = deepest node of each sequence or -1, nodes = list
+    of (parent node or -1, smallest member, start, end)) with nodes numbered
+    parents first: top-level nodes by smallest member, each followed by its
+    subtree, children by smallest member."""
+    n = len(seqs)
+    group_of = np.full(n, -1, np.int32)
+    nodes = []
+
+    def lcp_cut(members):
+        ref = [int(x) for x in seqs[members[0]]]
+        common = len(ref)
+        for m in members[1:]:
+            s = [int(x) for x in seqs[m]]
+            k = 0
+            while k < min(common, len(s)) and s[k] == ref[k]:
+                k += 1
+            common = k
+        return min(common, min(len(seqs[m]) for m in members) - 1)
+
+    def build(members, parent, start):
+        end = lcp_cut(members)
+        me = len(nodes)
+        nodes.append((parent, min(members), start, end))
+        for m in members:
+            group_of[m] = me
+        parts = {}
+        for m in members:
+            parts.setdefault(int(seqs[m][end]), []).append(m)
+        for part in sorted(parts.values(), key=min):
+            if len(part) >= 2 and lcp_cut(part) >= end + min_len:
+                build(part, me, end)
+
+    _, firsts, _ = prefix_groups_reference(seqs, keys, min_len)
+    g1, _, _ = prefix_groups_reference(seqs, keys, min_len)
+    for k in range(len(firsts)):
+        build(sorted(np.flatnonzero(g1 == k).tolist()), -1, 0)
+    return group_of, nodes

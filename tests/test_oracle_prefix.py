@@ -75,3 +75,62 @@ def test_grouping_by_brute_force(case):
         longer_ok = all(len(seqs[i]) > L + 1 for i in mem) and \
             len({seqs[i][L] for i in mem}) == 1
         assert not longer_ok
+
+
+def test_tree_hand_worked_case():
+    seqs = [[1, 2, 3, 4, 5, 6, 7], [1, 2, 3, 4, 5, 6, 8], [1, 2, 3, 9, 9, 9, 9], [1, 2, 3, 9, 9, 9, 1],
+            [1, 2, 3, 7], [5, 5]]
+    g, nodes = P.prefix_tree_reference(seqs, None, 2)
+    # [1 2 3] for the first five; [4 5 6] and [9 9 9] below it; [1 2 3 7] stays at the top node
+    assert nodes == [(-1, 0, 0, 3), (0, 0, 3, 6), (0, 2, 3, 6)]
+    assert g.tolist() == [1, 1, 2, 2, 0, -1]
+    # with min_len 4 the top-level cut already separates the two families
+    g, nodes = P.prefix_tree_reference(seqs, None, 4)
+    assert nodes == [(-1, 0, 0, 6), (-1, 2, 0, 6)] and g.tolist() == [0, 0, 1, 1, -1, -1]
+    # a part whose extra shared run is shorter than min_len stays with its parent
+    abc = [[1, 2, 3, 4, 5, 7], [1, 2, 3, 4, 5, 8], [1, 2, 3, 9, 0]]
+    g, nodes = P.prefix_tree_reference(abc, None, 3)
+    assert nodes == [(-1, 0, 0, 3)] and g.tolist() == [0, 0, 0]
+    g, nodes = P.prefix_tree_reference(abc, None, 2)
+    assert nodes == [(-1, 0, 0, 3), (0, 0, 3, 5)] and g.tolist() == [1, 1, 0]
+
+
+@pytest.mark.parametrize("case", list(_cases()))
+@pytest.mark.parametrize("m", [1, 2])
+def test_tree_by_brute_force(case, m):
+    seqs, keys, _ = case
+    g, nodes = P.prefix_tree_reference(seqs, keys, m)
+    n = len(seqs)
+    g1, f1, l1 = P.prefix_groups_reference(seqs, keys, m)
+    roots = [k for k, x in enumerate(nodes) if x[0] < 0]
+    assert [nodes[k][1] for k in roots] == list(f1) and [nodes[k][3] for k in roots] == list(l1)
+
+    def subtree(k):
+        out = {i for i in range(n) if g[i] == k}
+        for c, x in enumerate(nodes):
+            if x[0] == k:
+                out |= subtree(c)
+        return out
+
+    for k, (par, first, start, end) in enumerate(nodes):
+        assert par < k                                              # parents first
+        mem = sorted(subtree(k))
+        assert len(mem) >= 2 and first == mem[0]
+        assert start == (nodes[par][3] if par >= 0 else 0)
+        assert end >= start + m
+        head = seqs[first][:end]
+        assert all(seqs[i][:end] == head and len(seqs[i]) > end for i in mem)
+        longer = all(len(seqs[i]) > end + 1 for i in mem) and len({seqs[i][end] for i in mem}) == 1
+        assert not longer                                           # end is the cut common prefix
+        # each next-token part is a child exactly when it qualifies
+        parts = {}
+        for i in mem:
+            parts.setdefault(seqs[i][end], []).append(i)
+        kids = {nodes[c][1]: c for c, x in enumerate(nodes) if x[0] == k}
+        for part in parts.values():
+            cut = min(min(len(seqs[i]) for i in part) - 1,
+                      next((t for t in range(len(seqs[part[0]]))
+                            if any(t >= len(seqs[i]) or seqs[i][t] != seqs[part[0]][t] for i in part)),
+                           len(seqs[part[0]])))
+            qualifies = len(part) >= 2 and cut >= end + m
+            assert qualifies == (min(part) in kids and sorted(subtree(kids[min(part)])) == sorted(part))
