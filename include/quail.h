@@ -281,6 +281,25 @@ quail_status quail_prefix_groups(int32_t n, const int32_t* tokens, const int32_t
                                  const int32_t* keys, int32_t min_len, int32_t* group_of,
                                  int32_t* node_first, int32_t* node_len, int32_t* n_nodes);
 
+/* Nested form of quail_prefix_groups (host only): its nodes are the top
+ * level; inside a node that covers tokens [.., end) the members are split by
+ * their token at position `end`, and a part of two or more whose common
+ * prefix (cut to leave each member a token) reaches end + min_len becomes a
+ * child node covering [end, its cut), recursively; every other member stays
+ * with the node. Outputs (host, caller-allocated [n]; there are at most n - 1
+ * nodes): group_of[i] = the deepest node of sequence i or -1; per node k:
+ * node_parent[k] (-1 at the top), node_first[k] (smallest member in its
+ * subtree: the node's tokens are tokens [node_start[k], node_end[k]) of that
+ * member), node_start[k] (the parent's end, 0 at the top), node_end[k]. Nodes
+ * are numbered parents first (each top-level node followed by its subtree,
+ * children by smallest member). A child is prefilled with
+ * quail_prefix_prefill under its parent's handle. E_INVAL as
+ * quail_prefix_groups. */
+quail_status quail_prefix_tree(int32_t n, const int32_t* tokens, const int32_t* offsets,
+                               const int32_t* keys, int32_t min_len, int32_t* group_of,
+                               int32_t* node_parent, int32_t* node_first, int32_t* node_start,
+                               int32_t* node_end, int32_t* n_nodes);
+
 /* Prefills prefix nodes: node a = tokens[offsets[a] .. offsets[a+1]) (dev
  * int32; host offsets [n+1], lengths in [1, max_batch_tokens]) continues
  * parent[a] (host handle of a live anchor or node). Under an anchor it sits

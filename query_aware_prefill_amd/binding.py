@@ -83,6 +83,8 @@ _SIGS = {
                            C.c_double, C.c_double, _i32p, _i32p, _f64p, _f64p, C.c_int32, _i32p], C.c_int32),
     "quail_prefix_groups": ([C.c_int32, _i32p, _i32p, _i32p, C.c_int32, _i32p, _i32p, _i32p, _i32p],
                             C.c_int32),
+    "quail_prefix_tree": ([C.c_int32, _i32p, _i32p, _i32p, C.c_int32, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p],
+                          C.c_int32),
     "quail_prefix_prefill": ([_vp, C.c_int32, _i64p, _vp, _i32p, _i32p, _i64p, _vp], C.c_int32),
     "quail_anchor_kv": ([_vp, C.c_int64, C.c_int32, C.POINTER(_vp), C.POINTER(_vp), _i32p, _i32p],
                         C.c_int32),
@@ -292,6 +294,21 @@ def quail_prefix_groups(tokens, offsets, keys, min_len: int):
     nn = C.c_int32()
     _check(load().quail_prefix_groups(n, tokp, offp, ksp, int(min_len), gp, fp, lnp, C.byref(nn)))
     return g[:n].copy(), f[:nn.value].copy(), ln[:nn.value].copy()
+
+
+def quail_prefix_tree(tokens, offsets, keys, min_len: int):
+    """Nested radix grouping; returns (group_of, nodes) with nodes a list of
+    (parent, first, start, end) tuples."""
+    tok, tokp = _i32(np.asarray(tokens).reshape(-1) if len(tokens) else np.zeros(1, np.int32))
+    off, offp = _i32(offsets)
+    n = len(off) - 1
+    ks, ksp = (None, None) if keys is None else _i32(keys)
+    arrs = [_i32(np.zeros(max(n, 1), np.int32)) for _ in range(5)]
+    nn = C.c_int32()
+    _check(load().quail_prefix_tree(n, tokp, offp, ksp, int(min_len), *[a[1] for a in arrs], C.byref(nn)))
+    g, par, first, start, end = [a[0] for a in arrs]
+    nodes = [(int(par[k]), int(first[k]), int(start[k]), int(end[k])) for k in range(nn.value)]
+    return g[:n].copy(), nodes
 
 
 def quail_prefix_prefill(ctx: Context, parent, tokens, offsets, n_uses, stream=None):

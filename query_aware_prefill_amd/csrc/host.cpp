@@ -20,6 +20,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <functional>
+#include <map>
 #include <mutex>
 #include <numeric>
 #include <string>
@@ -444,6 +446,55 @@ int32_t prefix_groups(int32_t n, const int32_t* tokens, const int32_t* starts, c
     for (int32_t m : members[idx[r]]) group_of[m] = (int32_t)r;
   }
   return (int32_t)nodes.size();
+}
+
+// Nested shared prefixes: prefix_groups' nodes are the top level; inside a
+// node that covers tokens up to `end`, its members are split by their token
+// at `end`, and a part of two or more whose common prefix (cut so that each
+// member keeps a token) reaches end + min_len becomes a child node covering
+// [end, its cut), recursively; all other members stay with the node. Nodes
+// are numbered parents first: each top-level node (by smallest member)
+// followed by its subtree, children by smallest member. group_of[i] = the
+// deepest node of sequence i, or -1.
+struct TreeNode {
+  int32_t parent, first, start, end;
+};
+void prefix_tree(int32_t n, const int32_t* tokens, const int32_t* starts, const int32_t* lens,
+                 const int32_t* keys, int32_t min_len, int32_t* group_of, std::vector<TreeNode>& out) {
+  std::vector<int32_t> nf(std::max(n, 1)), nl(std::max(n, 1));
+  const int32_t nn = prefix_groups(n, tokens, starts, lens, keys, min_len, group_of, nf.data(), nl.data());
+  std::vector<std::vector<int32_t>> top(nn);
+  for (int32_t i = 0; i < n; ++i)
+    if (group_of[i] >= 0) top[group_of[i]].push_back(i);
+  auto tok = [&](int32_t i, int32_t k) { return tokens[starts[i] + k]; };
+  auto cut_lcp = [&](const std::vector<int32_t>& m) {
+    int32_t common = lens[m[0]], shortest = INT32_MAX;
+    for (int32_t i : m) {
+      const int32_t lim = std::min(common, lens[i]);
+      int32_t k = 0;
+      while (k < lim && tok(i, k) == tok(m[0], k)) ++k;
+      common = k;
+      shortest = std::min(shortest, lens[i]);
+    }
+    return std::min(common, shortest - 1);
+  };
+  std::function<void(const std::vector<int32_t>&, int32_t, int32_t)> build =
+      [&](const std::vector<int32_t>& m, int32_t parent, int32_t start) {
+        const int32_t end = cut_lcp(m);
+        const int32_t me = (int32_t)out.size();
+        out.push_back({parent, *std::min_element(m.begin(), m.end()), start, end});
+        for (int32_t i : m) group_of[i] = me;
+        std::map<int32_t, std::vector<int32_t>> parts;
+        for (int32_t i : m) parts[tok(i, end)].push_back(i);
+        std::vector<std::vector<int32_t>> ps;
+        for (auto& kv : parts) ps.push_back(std::move(kv.second));
+        std::sort(ps.begin(), ps.end(), [](const std::vector<int32_t>& a, const std::vector<int32_t>& b) {
+          return *std::min_element(a.begin(), a.end()) < *std::min_element(b.begin(), b.end());
+        });
+        for (const auto& part : ps)
+          if (part.size() >= 2 && cut_lcp(part) >= end + min_len) build(part, me, end);
+      };
+  for (int32_t k = 0; k < nn; ++k) build(top[k], -1, 0);
 }
 
 }  // namespace
@@ -1065,6 +1116,30 @@ quail_status quail_join_search(const quail_model_config* cfg, int32_t n_tables, 
     frontier[4 * i + 3] = seconds(fr[i].m);
   }
   *n_frontier = (int32_t)fr.size();
+  return QUAIL_OK;
+}
+
+quail_status quail_prefix_tree(int32_t n, const int32_t* tokens, const int32_t* offsets, const int32_t* keys,
+                               int32_t min_len, int32_t* group_of, int32_t* node_parent, int32_t* node_first,
+                               int32_t* node_start, int32_t* node_end, int32_t* n_nodes) {
+  if (!n_nodes) return fail(QUAIL_E_INVAL, "n_nodes is NULL");
+  *n_nodes = 0;
+  if (n == 0) return QUAIL_OK;
+  if (min_len < 1) return fail(QUAIL_E_INVAL, "min_len must be at least 1");
+  if (!tokens || !group_of || !node_parent || !node_first || !node_start || !node_end)
+    return fail(QUAIL_E_INVAL, "tokens, group_of and the node arrays are required");
+  if (quail_status st = check_offsets(n, offsets, 1, INT32_MAX, "sequence")) return st;
+  std::vector<int32_t> starts(offsets, offsets + n), lens(n);
+  for (int32_t i = 0; i < n; ++i) lens[i] = offsets[i + 1] - offsets[i];
+  std::vector<TreeNode> nodes;
+  prefix_tree(n, tokens, starts.data(), lens.data(), keys, min_len, group_of, nodes);
+  for (size_t k = 0; k < nodes.size(); ++k) {
+    node_parent[k] = nodes[k].parent;
+    node_first[k] = nodes[k].first;
+    node_start[k] = nodes[k].start;
+    node_end[k] = nodes[k].end;
+  }
+  *n_nodes = (int32_t)nodes.size();
   return QUAIL_OK;
 }
 

@@ -382,3 +382,18 @@ def test_join_search_argument_checks():
         B.quail_join_search(cfg, [(1, 1.0)] * 13, [(i, i + 1, 0, 0, 0.5, 0) for i in range(12)], 1e15, 8e12)
     one = B.quail_join_search(cfg, [(7, 3.0)], [], 1e15, 8e12)
     assert list(one["order"]) == [0] and one["n_frontier"] == 1 and one["metrics"][0] == 0
+
+
+@pytest.mark.parametrize("m", [1, 2, 3])
+@pytest.mark.parametrize("case", _prefix_cases())
+def test_prefix_tree_matches_oracle(case, m):
+    """Nested radix grouping: library (recursive split of sorted members) equals
+    the oracle's, nodes, numbering and deepest node of every sequence."""
+    from oracle import prefix as OPX
+    seqs, keys, _ = case
+    off = np.zeros(len(seqs) + 1, np.int32)
+    off[1:] = np.cumsum([len(s) for s in seqs])
+    toks = np.array([t for s in seqs for t in s], np.int32)
+    g, nodes = B.quail_prefix_tree(toks, off, keys, m)
+    rg, rnodes = OPX.prefix_tree_reference(seqs, keys, m)
+    assert np.array_equal(g, rg) and nodes == rnodes

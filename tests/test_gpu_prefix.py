@@ -430,3 +430,58 @@ def test_nested_prefix_nodes(B, kv_fp8):
     assert ok
     st = B.quail_pool_stats(ctx)
     assert st["prefills"] == 3 and st["evictions"] == 3 and st["resident"] == 0
+
+
+@pytest.mark.parametrize("kv_fp8", [False, True])
+def test_prefix_tree_composed_with_nested_nodes(B, kv_fp8):
+    """Suffixes of one anchor that share a 24-token prompt, then one of two
+    documents (20 and 16 tokens) in families of three, or nothing more: the
+    nested grouping finds the prompt node and the two document nodes under it;
+    they are prefilled parents first, every suffix runs its own tokens after
+    its deepest node, and the logits match the oracle's per-pair forward."""
+    import torch
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    shape = W.tiny_shape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                         intermediate=384, vocab=512, kv_fp8=kv_fp8)
+    wts = W.model_weights(shape, 18)
+    r = np.random.default_rng(18)
+    a_tok = r.integers(0, 512, 70).astype(np.int32)
+    prompt = r.integers(0, 512, 24).astype(np.int32)
+    docs = [r.integers(0, 512, 20).astype(np.int32), r.integers(0, 512, 16).astype(np.int32)]
+    seqs = [np.concatenate([prompt, docs[i // 3], r.integers(0, 512, 3 + i).astype(np.int32)]) for i in range(6)]
+    seqs.append(np.concatenate([prompt, r.integers(0, 512, 5).astype(np.int32)]))
+    off = np.zeros(len(seqs) + 1, np.int32)
+    off[1:] = np.cumsum([len(x) for x in seqs])
+    s_tok = np.concatenate(seqs).astype(np.int32)
+    keys = np.zeros(len(seqs), np.int32)
+    g, nodes = B.quail_prefix_tree(s_tok, off, keys, 8)
+    assert [(p, st, en) for p, _, st, en in nodes] == [(-1, 0, 24), (0, 24, 44), (0, 24, 40)]
+    n = len(seqs)
+    uses = [int(np.sum(g == k)) + sum(1 for q in nodes if q[0] == k) for k in range(len(nodes))]
+    dm = DeviceModel(shape, wts, max_anchor_len=1024, max_suffix_len=256)
+    ctx = dm.context(8 << 20, 256)
+    say("prefix tree: anchor and nodes, parents first", "fp8" if kv_fp8 else "bf16")
+    ha = B.quail_anchor_prefill(ctx, to_device(a_tok), [0, 70], [len(nodes)])   # each node holds one use
+    handles = []
+    for k, (par, first, start, end) in enumerate(nodes):
+        tk = s_tok[off[first] + start:off[first] + end]
+        parent = ha[0] if par < 0 else handles[par]
+        handles.append(B.quail_prefix_prefill(ctx, [parent], to_device(tk), [0, end - start], [uses[k]])[0])
+    tails, toff = _pack(s_tok, [(off[i] + nodes[g[i]][3], off[i + 1]) for i in range(n)])
+    h_last = torch.empty((n, shape.hidden), dtype=torch.int16, device="cuda")
+    say("prefix tree: join")
+    B.quail_join_prefill(ctx, [handles[g[i]] for i in range(n)], to_device(tails), toff, h_last)
+    logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+    tok = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+    B.quail_head8(ctx, h_last, 0x0F, logits, tok, dec)
+    torch.cuda.synchronize()
+    ref = [OM.forward_pair(a_tok, seqs[i], wts, shape, shared_len=nodes[g[i]][3]) for i in range(n)]
+    ref_logits = np.array([x["logits"] for x in ref])
+    lg = logits.cpu().numpy()
+    assert rel_inf(lg, ref_logits) <= 2e-2, rel_inf(lg, ref_logits)
+    ok, _ = decisions_agree(dec.cpu().numpy(), [x["decision"] for x in ref], [x["margin"] for x in ref],
+                            2e-2 * np.max(np.abs(ref_logits)))
+    assert ok
+    st = B.quail_pool_stats(ctx)
+    assert st["prefills"] == 1 + len(nodes) and st["evictions"] == 1 + len(nodes) and st["resident"] == 0
