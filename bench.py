@@ -642,6 +642,102 @@ def bench_shared(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_nested(args):
+    """Documents under two shared levels, 36-layer stack, no anchor: 2,048
+    documents share a 512-token prompt, then each family of 16 shares a
+    384-token document, then U{32..128} tokens of their own. Three runs on
+    the same inputs: the plain filter (quail_join_run), one shared level
+    (quail_join_run_shared, min_shared 32: the prompt), and the nested radix
+    index (quail_prefix_tree) with its nodes prefilled parents first
+    (quail_anchor_prefill for the prompt, quail_prefix_prefill for the
+    family documents) and every document's own tokens joined after its node
+    (quail_join_prefill, quail_head8). The second of two runs is timed."""
+    import torch
+    import workloads as W
+    from query_aware_prefill_amd import binding as B
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    B.load()
+    shape = W.QWEN3_4B
+    r = np.random.default_rng([8, 0])
+    n_fam, per_fam, min_shared = 128, 16, 32
+    prompt = r.integers(0, shape.vocab, 512).astype(np.int32)
+    fam_doc = [r.integers(0, shape.vocab, 384).astype(np.int32) for _ in range(n_fam)]
+    seqs = [np.concatenate([prompt, fam_doc[i // per_fam], r.integers(0, shape.vocab, int(r.integers(32, 129)))
+                            .astype(np.int32)]) for i in range(n_fam * per_fam)]
+    n = len(seqs)
+    s_off = np.zeros(n + 1, np.int32)
+    s_off[1:] = np.cumsum([len(x) for x in seqs])
+    s_tok = np.concatenate(seqs).astype(np.int32)
+    s_len = np.diff(s_off)
+    pa = -np.ones(n, np.int32)
+    log(f"nested36: {n} documents, 512-token prompt, {n_fam} families x {per_fam} sharing 384 tokens; weights")
+    wd = W.model_weights_device(shape, 0)
+    dm = DeviceModel(shape, wd, max_anchor_len=1024, max_suffix_len=int(np.max(s_len)))
+    T = 65536
+    pool = 8 << 30
+    s_tok_d, dummy = to_device(s_tok), to_device(np.zeros(1, np.int32))
+    g, nodes = B.quail_prefix_tree(s_tok, s_off, np.zeros(n, np.int32), min_shared)
+    assert nodes[0][0] < 0 and nodes[0][3] == 512 and len(nodes) == 1 + n_fam, nodes[:3]
+    logical = float(np.sum(s_len))
+    res = {"metric": "AI.IF filter over documents under two shared levels: nested prefix nodes vs one level vs "
+                     "plain (36-layer stack)",
+           "workload": f"{n} documents: 512 shared prompt tokens, {n_fam} families x {per_fam} sharing 384 "
+                       "document tokens, U{32..128} own tokens each, no anchor",
+           "rows": n, "logical_tokens": logical}
+    out = {}
+    for mode in ("nested", "shared", "plain"):
+        ctx = dm.context(pool, T)
+        logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+        dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+        for _ in range(2):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            if mode == "plain":
+                B.quail_join_run(ctx, dummy, [0], pa, s_tok_d, s_off, 0x0F, logits, None, dec)
+            elif mode == "shared":
+                B.quail_join_run_shared(ctx, dummy, [0], pa, s_tok_d, s_off, s_tok, min_shared, 0x0F, logits,
+                                        None, dec)
+            else:
+                uses = [int(np.sum(g == k)) + sum(1 for q in nodes if q[0] == k) for k in range(len(nodes))]
+                p0, f0, st0, en0 = nodes[0]
+                root = B.quail_anchor_prefill(ctx, s_tok_d[int(s_off[f0]):int(s_off[f0]) + en0], [0, en0],
+                                              [uses[0]])
+                kids = list(range(1, len(nodes)))
+                ktok = np.concatenate([s_tok[s_off[nodes[k][1]] + nodes[k][2]:s_off[nodes[k][1]] + nodes[k][3]]
+                                       for k in kids])
+                koff = np.concatenate([[0], np.cumsum([nodes[k][3] - nodes[k][2] for k in kids])]).astype(np.int32)
+                kh = B.quail_prefix_prefill(ctx, [root[0]] * len(kids), to_device(ktok), koff,
+                                            [uses[k] for k in kids])
+                handle = [root[0]] + list(kh)
+                tails = np.concatenate([s_tok[s_off[i] + nodes[g[i]][3]:s_off[i + 1]] for i in range(n)])
+                toff = np.concatenate([[0], np.cumsum([s_len[i] - nodes[g[i]][3] for i in range(n)])]).astype(np.int32)
+                h_last = torch.empty((n, shape.hidden), dtype=torch.int16, device="cuda")
+                B.quail_join_prefill(ctx, [handle[g[i]] for i in range(n)], to_device(tails), toff, h_last)
+                B.quail_head8(ctx, h_last, 0x0F, logits, None, dec)
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1000.0
+        st = B.quail_pool_stats(ctx)
+        out[mode] = (logits.cpu().numpy().astype(np.float64), dec.cpu().numpy())
+        res[mode] = {"ms": ms, "logical_tokens_per_min": logical / ms * 60e3, "pool_over_two_runs": st}
+        log(f"nested36 {mode}: {ms / 1000:.2f} s, {logical / ms * 60e3 / 1e6:.1f} M logical tokens/min")
+        del ctx
+    computed = {"plain": logical, "shared": 512.0 + float(np.sum(s_len - 512)),
+                "nested": 512.0 + n_fam * 384.0 + float(np.sum(s_len - 896))}
+    for mode in out:
+        res[mode]["computed_tokens"] = computed[mode]
+        res[mode]["computed_tokens_per_min"] = computed[mode] / res[mode]["ms"] * 60e3
+    lp = out["plain"][0]
+    tmask = np.array([(0x0F >> j) & 1 for j in range(8)], bool)
+    margin = np.max(np.where(tmask, lp, -np.inf), axis=1) - np.max(np.where(~tmask, lp, -np.inf), axis=1)
+    sure = np.abs(margin) > 2e-2 * np.max(np.abs(lp), axis=1)
+    for mode in ("nested", "shared"):
+        res[mode]["speedup_over_plain"] = res["plain"]["ms"] / res[mode]["ms"]
+        res[mode]["logits_rel_inf_vs_plain"] = float(np.max(np.abs(out[mode][0] - lp)) / np.max(np.abs(lp)))
+        res[mode]["decisions_beyond_tau_equal"] = [int(np.sum(out[mode][1][sure] == out["plain"][1][sure])),
+                                                   int(np.sum(sure))]
+    print(json.dumps(res), flush=True)
+
+
 def bench_search(args):
     """Planner latency (host only): quail_join_search on random tree queries of
     4 to 12 tables (Qwen3-4B cost constants, datasheet peaks)."""
@@ -683,7 +779,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--workload", choices=["cascade", "gemm", "layer", "copy", "stream", "join36",
                                            "filter36", "multijoin36", "multiplan36", "shared36", "traces36",
-                                           "search"],
+                                           "nested36", "search"],
                     default="cascade")
     ap.add_argument("--rows", type=int, default=625, help="multijoin36: rows of the 5,000 used")
     ap.add_argument("--shared-only", action="store_true", help="shared36: run only the join with prefix nodes")
@@ -708,6 +804,8 @@ def main():
         return bench_shared(args)
     if args.workload == "search":
         return bench_search(args)
+    if args.workload == "nested36":
+        return bench_nested(args)
     if args.workload in ("join36", "filter36", "multijoin36"):
         return bench_e2e(args)
 
