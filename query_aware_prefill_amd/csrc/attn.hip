@@ -550,10 +550,13 @@ struct WaveAttn {
 
   // S^T = K . Q^T of the tile at Kt (two 32-key halves); lane l32 reads key
   // row pi(l32) of each half
-  // HALF: only the first 32 keys exist in the slot; the second half's
-  // scores are -inf (no key).
-  template <bool FP8, bool HALF = false>
+  // NK: keys in the tile's slot (64, 32 or 16). Below 64 only the first
+  // 32-key half is computed and the second half's scores are -inf (no key);
+  // with 16, rows 16..31 of that half read past the slot (inside this
+  // workgroup's LDS) and are masked by the caller (mask with the same NK).
+  template <bool FP8, int NK = kKeyTile>
   __device__ __forceinline__ void scores(const uint16_t* Kt, f32x16_t (&s)[2]) const {
+    constexpr bool HALF = NK < kKeyTile;
     const int krow = key_pi(lane & 31);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -587,11 +590,13 @@ struct WaveAttn {
   }
 
   // mask a tile starting at key kbase: visible keys are [0, cross_len) for a
-  // cross tile, [lo_self, hi_self] for a self tile; register i of half kb
-  // holds key kbase + kb*32 + 16*(i/8) + 8*hi + i%8 (unsigned range test)
+  // cross tile, [lo_self, hi_self] for a self tile -- never past the tile's
+  // NK keys when a self tile has NK = 16; register i of half kb holds key
+  // kbase + kb*32 + 16*(i/8) + 8*hi + i%8 (unsigned range test)
+  template <int NKS = kKeyTile>
   __device__ __forceinline__ void mask(f32x16_t (&s)[2], int kbase, bool cross, int cross_len) const {
     const int lo = cross ? 0 : lo_self;
-    const int hk = cross ? cross_len - 1 : hi_self;
+    const int hk = cross ? cross_len - 1 : (NKS < 32 ? min(hi_self, kbase + NKS - 1) : hi_self);
     const uint32_t range = (uint32_t)(hk - lo);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -632,9 +637,12 @@ struct WaveAttn {
   // P = 2^(s*scale - m_run) in bf16 as the B operand: k-step (kb, sp) takes
   // regs 8*sp .. 8*sp+7 of half kb, i.e. keys kb*32 + 16sp + 8hi + 0..7; the
   // row sum adds the fp32 values
+  // NK < 64: the second half's scores are -inf and its P is never read (pv
+  // with the same NK skips it), so it is not computed
+  template <int NK = kKeyTile>
   __device__ __forceinline__ void probs(const f32x16_t (&s)[2], bf16x8_t (&pb)[2][2]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < (NK < kKeyTile ? 1 : 2); ++kb)
 #pragma unroll
       for (int sp = 0; sp < 2; ++sp) {
         uint32_t w[4];
@@ -652,9 +660,11 @@ struct WaveAttn {
   // O^T += V^T . P^T with the tile at Vt; A lane: dim row cb*32 + l32, keys
   // kb*32 + 16sp + 8hi + 0..7. The 16-lane block (lane / 16) covers dims
   // cb*32 + 16*(block % 2) .. +15 and keys +8 for blocks 2, 3.
-  // HALF: only the first 32 keys exist in the slot (their P is all there is)
-  template <bool FP8, bool HALF = false>
+  // NK: keys in the slot (64, 32 or 16); only their P is used
+  template <bool FP8, int NK = kKeyTile>
   __device__ __forceinline__ void pv(const uint16_t* Vt, const bf16x8_t (&pb)[2][2]) {
+    constexpr bool HALF = NK < kKeyTile;
+    constexpr int NSP = NK < 32 ? 1 : 2;       // 16-key k-steps per 32-key half
     const int s16 = lane & 15;
     const int dhalf = (lane >> 4) & 1;
     if constexpr (!FP8) {
@@ -664,7 +674,7 @@ struct WaveAttn {
 #pragma unroll
       for (int kb = 0; kb < (HALF ? 1 : 2); ++kb)
 #pragma unroll
-        for (int sp = 0; sp < 2; ++sp)
+        for (int sp = 0; sp < NSP; ++sp)
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
             const int key = kb * 32 + sp * 16 + key0;
@@ -683,7 +693,7 @@ struct WaveAttn {
 #pragma unroll
       for (int kb = 0; kb < (HALF ? 1 : 2); ++kb)
 #pragma unroll
-        for (int sp = 0; sp < 2; ++sp)
+        for (int sp = 0; sp < NSP; ++sp)
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
             const int key = kb * 32 + sp * 16 + key0;
@@ -764,10 +774,15 @@ attn_direct_kernel(AttnParams p) {
   constexpr int NW = PACK ? 1 : (G >= 4 ? G : 4);
   // Packed launches use 8-KB slots, 40 KB per workgroup, four workgroups per
   // CU: an E4M3 tile of 64 keys is 8 KB, and bf16 tiles are half tiles of 32
-  // keys (HALF_*), whose second 32-key half of the scores is -inf.
-  constexpr bool HALF_CROSS = PACK && !FC;
-  constexpr bool HALF_SELF = PACK && !FS;
-  constexpr uint32_t kSlotBytes = PACK ? 8192 : kTileElems * 2;
+  // keys, whose second 32-key half of the scores is -inf. With E4M3 cross
+  // and bf16 self tiles and G >= 2 (SMALL: a packed tile's queries, hence
+  // its self keys, number at most 32/G <= 16), slots are 4 KB -- E4M3 half
+  // tiles of 32 keys, bf16 quarter tiles of 16 keys -- 20 KB per workgroup,
+  // eight workgroups (two waves per SIMD) per CU.
+  constexpr bool SMALL = PACK && FC && !FS && G >= 2;
+  constexpr int NKC = PACK && (SMALL || !FC) ? kKeyTile / 2 : kKeyTile;          // keys per cross tile
+  constexpr int NKS = PACK && !FS ? (SMALL ? kKeyTile / 4 : kKeyTile / 2) : kKeyTile;   // per self tile
+  constexpr uint32_t kSlotBytes = PACK ? (SMALL ? 4096 : 8192) : kTileElems * 2;
   __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[5 * kSlotBytes];   // K: 2 slots, V: 3
   auto kslot = [&](int i) __attribute__((always_inline)) { return reinterpret_cast<const uint16_t*>(lds_raw + i * kSlotBytes); };
   auto vslot = [&](int i) __attribute__((always_inline)) { return reinterpret_cast<const uint16_t*>(lds_raw + (2 + i) * kSlotBytes); };
@@ -786,7 +801,7 @@ attn_direct_kernel(AttnParams p) {
   const bool row_ok = qrow < tile.nq;
   const int64_t tok = (int64_t)tile.q0 + qrow;
 
-  const TileSeq<HALF_CROSS ? kKeyTile / 2 : kKeyTile, HALF_SELF ? kKeyTile / 2 : kKeyTile, L2> ts(p, tile);
+  const TileSeq<NKC, NKS, L2> ts(p, tile);
   if (ts.n_tiles == 0) {
     store_empty(p, tok, row_ok, head, lane >> 5);
     return;
@@ -796,12 +811,12 @@ attn_direct_kernel(AttnParams p) {
   // K and V copies of tile j into K slot ks and V slot vs
   // (packed launches stream each anchor's K/V once per kv head: non-temporal)
   auto issue = [&](int j, int ks, int vs) __attribute__((always_inline)) {
-    if (j < ts.n_ct ? HALF_CROSS : HALF_SELF) {
-      TileCopy<NW, false, kKeyTile / 2, PACK>(ts.src(j), g, ts.kbase(j), lds_k0 + ks * kSlotBytes).issue_all(wave, lane);
-      TileCopy<NW, true, kKeyTile / 2, PACK>(ts.src(j), g, ts.kbase(j), lds_v0 + vs * kSlotBytes).issue_all(wave, lane);
+    if (NKC == NKS || j < ts.n_ct) {
+      TileCopy<NW, false, NKC, PACK>(ts.src(j), g, ts.kbase(j), lds_k0 + ks * kSlotBytes).issue_all(wave, lane);
+      TileCopy<NW, true, NKC, PACK>(ts.src(j), g, ts.kbase(j), lds_v0 + vs * kSlotBytes).issue_all(wave, lane);
     } else {
-      TileCopy<NW, false, kKeyTile, PACK>(ts.src(j), g, ts.kbase(j), lds_k0 + ks * kSlotBytes).issue_all(wave, lane);
-      TileCopy<NW, true, kKeyTile, PACK>(ts.src(j), g, ts.kbase(j), lds_v0 + vs * kSlotBytes).issue_all(wave, lane);
+      TileCopy<NW, false, NKS, PACK>(ts.src(j), g, ts.kbase(j), lds_k0 + ks * kSlotBytes).issue_all(wave, lane);
+      TileCopy<NW, true, NKS, PACK>(ts.src(j), g, ts.kbase(j), lds_v0 + vs * kSlotBytes).issue_all(wave, lane);
     }
   };
   issue(0, 0, 0);
@@ -813,9 +828,9 @@ attn_direct_kernel(AttnParams p) {
   // prologue: scores of tile 0
   f32x16_t s_cur[2];
   publish();
-  if (ts.n_ct > 0) w.scores<FC, HALF_CROSS>(kslot(0), s_cur);
-  else w.scores<FS, HALF_SELF>(kslot(0), s_cur);
-  if (ts.n_full == 0) w.mask(s_cur, ts.kbase(0), 0 < ts.n_ct, ts.clen(0));
+  if (ts.n_ct > 0) w.scores<FC, NKC>(kslot(0), s_cur);
+  else w.scores<FS, NKS>(kslot(0), s_cur);
+  if (ts.n_full == 0) w.mask<NKS>(s_cur, ts.kbase(0), 0 < ts.n_ct, ts.clen(0));
   w.rescale(w.row_max(s_cur));
 
   // step j: issue K(j+2), V(j+2); S(j+1) with P(j); PV(j) with mask/max of
@@ -827,9 +842,9 @@ attn_direct_kernel(AttnParams p) {
     constexpr bool S_SELF = decltype(s_tag)::value;
     constexpr bool MASK_NEXT = decltype(mask_tag)::value;
     constexpr bool PV_FP8 = PV_SELF ? FS : FC, S_FP8 = S_SELF ? FS : FC;
-    constexpr bool PV_HALF = PV_SELF ? HALF_SELF : HALF_CROSS, S_HALF = S_SELF ? HALF_SELF : HALF_CROSS;
-    // copies per wave of one V tile of tile j+1's format and size
-    constexpr int NV_NEXT = (S_FP8 ? 8 : 16) / (S_HALF ? 2 : 1) / NW;
+    constexpr int PV_NK = PV_SELF ? NKS : NKC, S_NK = S_SELF ? NKS : NKC;
+    // copies (1 KB each) per wave of one V tile of tile j+1's format and size
+    constexpr int NV_NEXT = S_NK * (S_FP8 ? 128 : 256) / 1024 / NW;
     // waits for this wave's copies of K(j+1) and V(j) -- the copies of
     // V(j+1), issued last (by step j-1 or the prologue), may stay in flight;
     // the barrier then makes every wave's copies visible and guarantees that
@@ -837,12 +852,12 @@ attn_direct_kernel(AttnParams p) {
     publish_keep<NV_NEXT>();
     if (j + 2 < ts.n_tiles) issue(j + 2, j & 1, vs == 0 ? 2 : vs - 1);   // V slot (j + 2) mod 3
     bf16x8_t pb[2][2];
-    w.probs(s_cur, pb);
+    w.probs<PV_NK>(s_cur, pb);
     f32x16_t s_nxt[2];
-    w.scores<S_FP8, S_HALF>(kslot((j + 1) & 1), s_nxt);
-    w.pv<PV_FP8, PV_HALF>(vslot(vs), pb);
+    w.scores<S_FP8, S_NK>(kslot((j + 1) & 1), s_nxt);
+    w.pv<PV_FP8, PV_NK>(vslot(vs), pb);
     vs = vs == 2 ? 0 : vs + 1;
-    if constexpr (MASK_NEXT) w.mask(s_nxt, ts.kbase(j + 1), j + 1 < ts.n_ct, ts.clen(j + 1));
+    if constexpr (MASK_NEXT) w.mask<NKS>(s_nxt, ts.kbase(j + 1), j + 1 < ts.n_ct, ts.clen(j + 1));
     w.rescale(w.row_max(s_nxt));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
@@ -862,9 +877,9 @@ attn_direct_kernel(AttnParams p) {
   {
     publish();
     bf16x8_t pb[2][2];
-    w.probs(s_cur, pb);
-    if (j < ts.n_ct) w.pv<FC, HALF_CROSS>(vslot(vs), pb);
-    else w.pv<FS, HALF_SELF>(vslot(vs), pb);
+    w.probs<(NKC > NKS ? NKC : NKS)>(s_cur, pb);   // a -inf half only adds zeros
+    if (j < ts.n_ct) w.pv<FC, NKC>(vslot(vs), pb);
+    else w.pv<FS, NKS>(vslot(vs), pb);
   }
   w.store(p, tok, row_ok, head);
 }
