@@ -738,6 +738,79 @@ def bench_nested(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_multijoin_full(args):
+    """The multi-join configuration at full size, 36-layer stack: 1024 anchors
+    x 768 tokens with E4M3 KV (about 58 GB resident), 5,000 rows of
+    U{48..256} tokens each probing 51 anchors (255,000 pairs). Every anchor is
+    prefilled once (quail_anchor_prefill, use count = its pairs) into a pool
+    that holds all of them; the rows then run in 8 chunks of 625 (one progress
+    line each), each chunk's pairs through quail_join_prefill (grouped by
+    anchor inside) and quail_head8; an anchor is evicted after its last pair."""
+    import torch
+    import workloads as W
+    from query_aware_prefill_amd import binding as B
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    B.load()
+    shape = W.ModelShape(**{**W.QWEN3_4B.__dict__, "kv_fp8": True})
+    log("multijoin36 full: generating the workload")
+    case = W.c4_case()
+    a_len, a_off, a_tok = case["a_len"], case["a_off"], case["a_tok"]
+    pa, prow = case["pair_anchor"], case["pair_row"]
+    plen = case["row_len"][prow].astype(np.int64)
+    n = len(pa)
+    s_off = np.zeros(n + 1, np.int64)
+    s_off[1:] = np.cumsum(plen)
+    s_tok = np.concatenate([case["row_tok"][case["row_off"][r]:case["row_off"][r + 1]] for r in prow]).astype(np.int32)
+    log(f"multijoin36 full: {n} pairs, {int(s_off[-1])} suffix tokens; weights on device")
+    wd = W.model_weights_device(shape, 0)
+    dm = DeviceModel(shape, wd, max_anchor_len=768, max_suffix_len=int(np.max(plen)))
+    T = 65536
+    pool = len(a_len) * B.quail_anchor_bytes(dm.cfg, 768) + (1 << 20)
+    ctx = dm.context(pool, T)
+    a_tok_d, s_tok_d = to_device(a_tok), to_device(s_tok)
+    uses = np.bincount(pa, minlength=len(a_len)).astype(np.int32)
+    logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+    dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+    rows_per_chunk = 625
+    chunk_pairs = int(np.max(np.bincount(prow // rows_per_chunk)))
+    h_last = torch.empty((chunk_pairs, shape.hidden), dtype=torch.int16, device="cuda")
+    log(f"multijoin36 full: pool {pool / 2**30:.1f} GiB; prefilling {len(a_len)} anchors")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    handles = B.quail_anchor_prefill(ctx, a_tok_d, a_off, uses, anchor_ids=np.arange(len(a_len)))
+    torch.cuda.synchronize()
+    t_pre = time.perf_counter() - t0
+    log(f"multijoin36 full: anchors prefilled in {t_pre:.2f} s, resident {B.quail_pool_stats(ctx)['resident'] / 1e9:.1f} GB")
+    for r0 in range(0, len(case["row_len"]), rows_per_chunk):
+        p0 = int(np.searchsorted(prow, r0))
+        p1 = int(np.searchsorted(prow, r0 + rows_per_chunk))
+        off = (s_off[p0:p1 + 1] - s_off[p0]).astype(np.int32)
+        B.quail_join_prefill(ctx, handles[pa[p0:p1]], s_tok_d[int(s_off[p0]):int(s_off[p1])], off, h_last[:p1 - p0])
+        B.quail_head8(ctx, h_last[:p1 - p0], 0x0F, logits[p0:p1], None, dec[p0:p1])
+        torch.cuda.synchronize()
+        log(f"multijoin36 full: rows {r0}..{r0 + rows_per_chunk - 1} done at {time.perf_counter() - t0:.1f} s")
+    ms = (time.perf_counter() - t0) * 1000.0
+    st = B.quail_pool_stats(ctx)
+    suffix_tok = float(np.sum(plen))
+    anchor_tok = float(np.sum(a_len))
+    logical = float(np.sum(a_len[pa]) + suffix_tok)
+    L = shape.n_layers
+    gemm = 201_850_880.0 * suffix_tok * L + anchor_tok * (201_850_880.0 * (L - 1) + 31_457_280.0)
+    attn = 16384.0 * L * float(np.sum(plen * a_len[pa]) + np.sum(plen * (plen + 1) / 2))
+    attn += 16384.0 * (L - 1) * float(np.sum(a_len.astype(np.float64) * (a_len + 1) / 2))
+    res = {"metric": "end-to-end prefill tokens/min (36-layer stack)",
+           "workload": "multi-join at full size: 1024 anchors x 768 tokens (E4M3 KV resident), 5,000 rows of "
+                       "U{48..256} tokens x 51 anchors each (255,000 pairs)",
+           "unit": "tokens/min", "ms": ms, "anchor_prefill_ms": t_pre * 1e3, "pairs": int(n),
+           "logical_tokens": logical, "computed_tokens": suffix_tok + anchor_tok,
+           "logical_tokens_per_min": logical / ms * 60e3,
+           "computed_tokens_per_min": (suffix_tok + anchor_tok) / ms * 60e3,
+           "algorithmic_tflops": (gemm + attn) / (ms * 1e-3) / 1e12, "pool": st}
+    log(f"multijoin36 full: {ms / 1000:.1f} s, {res['logical_tokens_per_min'] / 1e6:.1f} M logical tokens/min, "
+        f"{res['algorithmic_tflops']:.0f} TFLOP/s")
+    print(json.dumps(res), flush=True)
+
+
 def bench_search(args):
     """Planner latency (host only): quail_join_search on random tree queries of
     4 to 12 tables (Qwen3-4B cost constants, datasheet peaks)."""
@@ -778,8 +851,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--workload", choices=["cascade", "gemm", "layer", "copy", "stream", "join36",
-                                           "filter36", "multijoin36", "multiplan36", "shared36", "traces36",
-                                           "nested36", "search"],
+                                           "filter36", "multijoin36", "multijoin36full", "multiplan36", "shared36",
+                                           "traces36", "nested36", "search"],
                     default="cascade")
     ap.add_argument("--rows", type=int, default=625, help="multijoin36: rows of the 5,000 used")
     ap.add_argument("--shared-only", action="store_true", help="shared36: run only the join with prefix nodes")
@@ -806,6 +879,8 @@ def main():
         return bench_search(args)
     if args.workload == "nested36":
         return bench_nested(args)
+    if args.workload == "multijoin36full":
+        return bench_multijoin_full(args)
     if args.workload in ("join36", "filter36", "multijoin36"):
         return bench_e2e(args)
 
