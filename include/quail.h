@@ -391,16 +391,21 @@ quail_status quail_join_run(quail_ctx* ctx, int32_t n_anchors, const int32_t* a_
  * prefix plus its share of the prefix). Outputs equal quail_join_run's up to
  * floating-point rounding (the cascade split is exact), except that with an
  * fp8 KV store the shared positions are stored in E4M3 like anchor KV.
- * The plan is built against the largest free pool block less the slab of
- * the longest possible prefix node (the longest pair), so nodes fit beside
- * their step's anchors; E_NOMEM, before anything is enqueued, when that
- * leaves nothing. min_shared >= 1; other arguments as quail_join_run. */
+ * nested != 0 groups each step with quail_prefix_tree instead: nodes under
+ * nodes are prefilled parents first (a child copies its parent's rows, as
+ * quail_prefix_prefill under a node does), whole subtrees at a time.
+ * The plan is built against the largest free pool block less a reserve that
+ * covers one step's largest node subtree (at least the slab of the longest
+ * pair), re-planning while the subtrees grow, so nodes fit beside their
+ * step's anchors; E_NOMEM, before anything is enqueued, when that leaves
+ * nothing. min_shared >= 1; other arguments as quail_join_run. */
 quail_status quail_join_run_shared(quail_ctx* ctx, int32_t n_anchors, const int32_t* a_tokens,
                                    const int32_t* a_offsets, int32_t n_pairs,
                                    const int32_t* pair_anchor, const int32_t* s_tokens,
                                    const int32_t* s_offsets, const int32_t* s_tokens_host,
-                                   int32_t min_shared, uint8_t true_mask, float* logits,
-                                   uint8_t* token, uint8_t* decision, quail_stream stream);
+                                   int32_t min_shared, int32_t nested, uint8_t true_mask,
+                                   float* logits, uint8_t* token, uint8_t* decision,
+                                   quail_stream stream);
 
 /* Runs several joins over one anchor table with the plan of
  * quail_multiplan_build (pool budget: the largest free block of the pool

@@ -94,7 +94,7 @@ _SIGS = {
     "quail_join_run": ([_vp, C.c_int32, _vp, _i32p, C.c_int32, _i32p, _vp, _i32p, C.c_uint8, _vp, _vp,
                         _vp, _vp], C.c_int32),
     "quail_join_run_shared": ([_vp, C.c_int32, _vp, _i32p, C.c_int32, _i32p, _vp, _i32p, _i32p, C.c_int32,
-                               C.c_uint8, _vp, _vp, _vp, _vp], C.c_int32),
+                               C.c_int32, C.c_uint8, _vp, _vp, _vp, _vp], C.c_int32),
     "quail_multijoin_run": ([_vp, C.c_int32, _vp, _i32p, C.c_int32, _i32p, _i32p, _vp, _i32p, C.c_uint8,
                              _vp, _vp, _vp, _vp], C.c_int32),
     "quail_pool_stats": ([_vp, _szp, _szp, _i64p, _i64p, _i64p], C.c_int32),
@@ -358,14 +358,14 @@ def quail_join_run(ctx: Context, a_tokens, a_offsets, pair_anchor, s_tokens, s_o
 
 
 def quail_join_run_shared(ctx: Context, a_tokens, a_offsets, pair_anchor, s_tokens, s_offsets, s_tokens_host,
-                          min_shared, true_mask, logits, token, decision, stream=None):
+                          min_shared, true_mask, logits, token, decision, stream=None, nested=False):
     ao, aop = _i32(a_offsets)
     pa, pap = _i32(pair_anchor)
     so, sop = _i32(s_offsets)
     sh, shp = _i32(s_tokens_host)
     _check(load().quail_join_run_shared(ctx.handle, len(ao) - 1, dptr(a_tokens), aop, len(pa), pap,
-                                        dptr(s_tokens), sop, shp, int(min_shared), true_mask, dptr(logits),
-                                        dptr(token), dptr(decision), stream_handle(stream)))
+                                        dptr(s_tokens), sop, shp, int(min_shared), int(bool(nested)), true_mask,
+                                        dptr(logits), dptr(token), dptr(decision), stream_handle(stream)))
 
 
 def quail_multijoin_run(ctx: Context, a_tokens, a_offsets, join_offsets, pair_anchor, s_tokens, s_offsets,

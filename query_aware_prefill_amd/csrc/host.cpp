@@ -1562,7 +1562,7 @@ static quail_status run_step_with_head(quail_ctx* c, int32_t np, const quail_anc
 static quail_status join_run_core(quail_ctx* c, int32_t n_anchors, const int32_t* a_tokens,
                                   const int32_t* a_offsets, int32_t n_pairs, const int32_t* pair_anchor,
                                   const int32_t* s_tokens, const int32_t* s_offsets,
-                                  const int32_t* s_tokens_host, int32_t min_shared, uint8_t true_mask,
+                                  const int32_t* s_tokens_host, int32_t min_shared, bool nested, uint8_t true_mask,
                                   float* logits, uint8_t* token, uint8_t* decision, quail_stream stream) {
   if (!c) return fail(QUAIL_E_INVAL, "ctx is NULL");
   if (n_pairs == 0) return QUAIL_OK;
@@ -1585,13 +1585,6 @@ static quail_status join_run_core(quail_ctx* c, int32_t n_anchors, const int32_t
   // step's nodes fit beside its anchors
   size_t free_bytes = 0;
   for (auto& f : c->free_list) free_bytes = std::max(free_bytes, f.second);
-  if (min_shared > 0) {
-    const size_t reserve = slab_bytes(c->cfg, *std::max_element(plen.begin(), plen.end()));
-    if (free_bytes <= reserve)
-      return fail(QUAIL_E_NOMEM, "KV pool (largest free block %zu B) leaves no room for a prefix node (%zu B)",
-                  free_bytes, reserve);
-    free_bytes -= reserve;
-  }
   // With sharing, steps are sized by the tokens each pair will compute: its
   // own tokens after the prefix it shares, plus its share of that prefix
   // (grouping all pairs of each anchor); steps are regrouped below.
@@ -1611,39 +1604,98 @@ static quail_status join_run_core(quail_ctx* c, int32_t n_anchors, const int32_t
       if (gof[i] >= 0)
         step_len[i] = plen[i] - nl[gof[i]] + (nl[gof[i]] + members[gof[i]] - 1) / members[gof[i]];
   }
+  // Shared-prefix nodes of each plan step, parents first: one level
+  // (prefix_groups) or the nested tree (prefix_tree). A node continues its
+  // anchor; in a tree of filter rows the root is a plain anchor that its
+  // descendants continue. A node below another node of an anchor (or below a
+  // filter tree's second level) copies its parent's rows. Uses: a node's own
+  // members, plus one per node that continues it (held until that node is
+  // evicted) or copies it (spent when that node is prefilled).
+  struct Node {
+    int32_t anchor, parent, root, depth, first, start, end, rows, uses;
+    std::vector<int32_t> members;   // pairs whose deepest node this is
+  };
   Plan plan;
-  if (quail_status st = build_plan(slab, n_pairs, pair_anchor, step_len.data(), free_bytes, c->T, plan))
-    return st;
-  // shared-prefix nodes per step (plan positions of their members)
-  struct Node { int32_t anchor, first, len; std::vector<int32_t> members; };
-  const int32_t n_steps = (int32_t)plan.bounds.size() - 1;
-  std::vector<std::vector<Node>> step_nodes(n_steps);
+  std::vector<std::vector<Node>> step_nodes;
   std::vector<char> grouped(n_pairs, 0);
-  if (min_shared > 0) {
+  auto group_steps = [&]() -> size_t {   // returns the largest root subtree's slab bytes
+    const int32_t n_steps = (int32_t)plan.bounds.size() - 1;
+    step_nodes.assign(n_steps, {});
+    std::fill(grouped.begin(), grouped.end(), 0);
+    size_t need = 0;
     for (int32_t st = 0; st < n_steps; ++st) {
       const int32_t b0 = plan.bounds[st], np = plan.bounds[st + 1] - b0;
-      std::vector<int32_t> starts(np), lens(np), keys(np), gof(np), nf(np), nl(np);
+      std::vector<int32_t> starts(np), lens(np), keys(np), gof(np);
       for (int32_t k = 0; k < np; ++k) {
         const int32_t pi = plan.order[b0 + k];
         starts[k] = s_offsets[pi];
         lens[k] = plen[pi];
         keys[k] = pair_anchor[pi] >= 0 ? pair_anchor[pi] : n_anchors;
       }
-      const int32_t nn = prefix_groups(np, s_tokens_host, starts.data(), lens.data(), keys.data(), min_shared,
-                                       gof.data(), nf.data(), nl.data());
-      step_nodes[st].resize(nn);
-      for (int32_t q = 0; q < nn; ++q) {
-        const int32_t pi = plan.order[b0 + nf[q]];
-        step_nodes[st][q].anchor = pair_anchor[pi];
-        step_nodes[st][q].first = s_offsets[pi];
-        step_nodes[st][q].len = nl[q];
+      std::vector<TreeNode> tn;
+      if (nested) {
+        prefix_tree(np, s_tokens_host, starts.data(), lens.data(), keys.data(), min_shared, gof.data(), tn);
+      } else {
+        std::vector<int32_t> nf(np), nl(np);
+        const int32_t nn = prefix_groups(np, s_tokens_host, starts.data(), lens.data(), keys.data(), min_shared,
+                                         gof.data(), nf.data(), nl.data());
+        for (int32_t q = 0; q < nn; ++q) tn.push_back({-1, nf[q], 0, nl[q]});
+      }
+      std::vector<Node>& nodes = step_nodes[st];
+      nodes.resize(tn.size());
+      for (size_t q = 0; q < tn.size(); ++q) {
+        Node& nd = nodes[q];
+        nd.anchor = pair_anchor[plan.order[b0 + tn[q].first]];
+        nd.parent = tn[q].parent;
+        nd.root = nd.parent < 0 ? (int32_t)q : nodes[nd.parent].root;
+        nd.depth = nd.parent < 0 ? 0 : nodes[nd.parent].depth + 1;
+        nd.first = s_offsets[plan.order[b0 + tn[q].first]];
+        nd.start = tn[q].start;
+        nd.end = tn[q].end;
+        nd.rows = (nd.anchor < 0 && nd.parent >= 0) ? nd.end - nodes[nd.root].end : nd.end;
+        nd.uses = 0;
       }
       for (int32_t k = 0; k < np; ++k)
         if (gof[k] >= 0) {
-          step_nodes[st][gof[k]].members.push_back(plan.order[b0 + k]);
+          nodes[gof[k]].members.push_back(plan.order[b0 + k]);
           grouped[plan.order[b0 + k]] = 1;
         }
+      std::vector<size_t> sub(nodes.size(), 0);
+      for (size_t q = 0; q < nodes.size(); ++q) {
+        Node& nd = nodes[q];
+        nd.uses += (int32_t)nd.members.size();
+        if (nd.parent >= 0) {
+          if (nd.anchor < 0) nodes[nd.root].uses++;                      // continues the filter root
+          if (nd.anchor >= 0 || nd.parent != nd.root) nodes[nd.parent].uses++;   // copies its parent
+        }
+        sub[nd.root] += slab_bytes(c->cfg, nd.rows);
+      }
+      for (size_t q = 0; q < nodes.size(); ++q)
+        if (nodes[q].parent < 0) need = std::max(need, sub[q]);
     }
+    return need;
+  };
+  // The plan is built against the largest free pool block less a reserve for
+  // one step's largest node subtree, so that it fits beside the step's
+  // anchors; the reserve starts at the slab of the longest possible node and
+  // grows (re-planning) until it covers the subtrees the plan's steps form.
+  size_t reserve = min_shared > 0 ? slab_bytes(c->cfg, *std::max_element(plen.begin(), plen.end())) : 0;
+  for (int32_t it = 0;; ++it) {
+    if (min_shared > 0 && free_bytes <= reserve)
+      return fail(QUAIL_E_NOMEM, "KV pool (largest free block %zu B) leaves no room for prefix nodes (%zu B)",
+                  free_bytes, reserve);
+    plan = Plan{};
+    if (quail_status st = build_plan(slab, n_pairs, pair_anchor, step_len.data(), free_bytes - reserve, c->T, plan))
+      return st;
+    if (min_shared <= 0) {
+      step_nodes.assign(plan.bounds.size() - 1, {});
+      break;
+    }
+    const size_t need = group_steps();
+    if (need <= reserve) break;
+    if (it == 3)
+      return fail(QUAIL_E_NOMEM, "KV pool cannot hold a step's prefix nodes (%zu B) beside its anchors", need);
+    reserve = need;
   }
   // an anchor's uses: its ungrouped pairs plus one per node under it (a
   // node of filter rows, anchor -1, is a plain anchor of its own)
@@ -1722,46 +1774,77 @@ static quail_status join_run_core(quail_ctx* c, int32_t n_anchors, const int32_t
       if (quail_status r = run_step_with_head(c, (int32_t)ha.size(), ha.data(), s_tokens, starts.data(),
                                               lens.data(), outmap.data(), true_mask, logits, token, decision, s))
         return r;
-    // shared-prefix nodes of this step, in chunks that fit half the free pool:
-    // prefill the chunk's nodes, then their members' remaining tokens
-    const std::vector<Node>& nodes = step_nodes[st];
-    for (size_t q0 = 0; q0 < nodes.size();) {
+    // shared-prefix nodes of this step, whole root subtrees per chunk (chunks
+    // fit half the free pool, at least one subtree): prefill the chunk's
+    // nodes depth by depth, then run their members' remaining tokens
+    std::vector<Node>& nodes = step_nodes[st];
+    const size_t nn = nodes.size();
+    std::vector<quail_anchor> nh(nn, QUAIL_NO_ANCHOR);
+    std::vector<size_t> sub(nn, 0);
+    std::vector<int32_t> roots;
+    int32_t maxd = 0;
+    for (size_t q = 0; q < nn; ++q) {
+      sub[nodes[q].root] += slab_bytes(c->cfg, nodes[q].rows);
+      if (nodes[q].parent < 0) roots.push_back((int32_t)q);
+      maxd = std::max(maxd, nodes[q].depth);
+    }
+    auto slot_of = [](quail_anchor h) { return (int32_t)(h & 0xFFFFFFFF); };
+    for (size_t r0 = 0; r0 < roots.size();) {
       size_t fb = 0;
       for (auto& f : c->free_list) fb = std::max(fb, f.second);
-      size_t q1 = q0, bytes = 0;
-      int32_t ntok = 0;
-      while (q1 < nodes.size()) {
-        const size_t nb = slab_bytes(c->cfg, nodes[q1].len);
-        if (q1 > q0 && (bytes + nb > fb / 2 || ntok + nodes[q1].len > c->T)) break;
-        bytes += nb;
-        ntok += nodes[q1].len;
-        ++q1;
+      size_t r1 = r0, bytes = 0;
+      while (r1 < roots.size()) {
+        if (r1 > r0 && bytes + sub[roots[r1]] > fb / 2) break;
+        bytes += sub[roots[r1]];
+        ++r1;
       }
-      const int32_t nn = (int32_t)(q1 - q0);
-      std::vector<int32_t> nst(nn), nln(nn), nnu(nn), npar(nn);
-      std::vector<quail_anchor> nh(nn);
-      for (int32_t q = 0; q < nn; ++q) {
-        const Node& nd = nodes[q0 + q];
-        nst[q] = nd.first;
-        nln[q] = nd.len;
-        nnu[q] = (int32_t)nd.members.size();
-        npar[q] = nd.anchor >= 0 ? (int32_t)(handle[nd.anchor] & 0xFFFFFFFF) : -1;
+      std::vector<char> in_chunk(nn, 0);
+      for (size_t r = r0; r < r1; ++r) in_chunk[roots[r]] = 1;
+      for (size_t q = 0; q < nn; ++q) in_chunk[q] = in_chunk[nodes[q].root];
+      for (int32_t d = 0; d <= maxd; ++d) {
+        std::vector<int32_t> idx, nst, nln, nnu, npar, nfrom;
+        for (size_t q = 0; q < nn; ++q) {
+          if (!in_chunk[q] || nodes[q].depth != d) continue;
+          const Node& nd = nodes[q];
+          int32_t par = -1, from = -1;
+          if (nd.anchor >= 0) {
+            par = slot_of(handle[nd.anchor]);
+            if (nd.parent >= 0) from = slot_of(nh[nd.parent]);
+          } else if (nd.parent >= 0) {
+            par = slot_of(nh[nd.root]);
+            if (nd.parent != nd.root) from = slot_of(nh[nd.parent]);
+          }
+          idx.push_back((int32_t)q);
+          nst.push_back(nd.first + nd.start);
+          nln.push_back(nd.end - nd.start);
+          nnu.push_back(nd.uses);
+          npar.push_back(par);
+          nfrom.push_back(from);
+        }
+        if (idx.empty()) continue;
+        std::vector<quail_anchor> out(idx.size());
+        if (quail_status r = anchor_core(c, (int32_t)idx.size(), s_tokens, nst.data(), nln.data(), nnu.data(),
+                                         nullptr, out.data(), s, npar.data(), nfrom.data()))
+          return r;
+        for (size_t k = 0; k < idx.size(); ++k) nh[idx[k]] = out[k];
+        for (size_t k = 0; k < idx.size(); ++k)      // a copied parent's use is spent
+          if (nfrom[k] >= 0 && --c->slots[nfrom[k]].uses == 0) c->evict(nfrom[k]);
       }
-      if (quail_status r = anchor_core(c, nn, s_tokens, nst.data(), nln.data(), nnu.data(), nullptr, nh.data(), s,
-                                       npar.data()))
-        return r;
       ha.clear(); starts.clear(); lens.clear(); outmap.clear();
-      for (int32_t q = 0; q < nn; ++q)
-        for (int32_t pi : nodes[q0 + q].members) {
+      for (size_t q = 0; q < nn; ++q) {
+        if (!in_chunk[q]) continue;
+        for (int32_t pi : nodes[q].members) {
           ha.push_back(nh[q]);
-          starts.push_back(s_offsets[pi] + nodes[q0 + q].len);
-          lens.push_back(plen[pi] - nodes[q0 + q].len);
+          starts.push_back(s_offsets[pi] + nodes[q].end);
+          lens.push_back(plen[pi] - nodes[q].end);
           outmap.push_back(pi);
         }
-      if (quail_status r = run_step_with_head(c, (int32_t)ha.size(), ha.data(), s_tokens, starts.data(),
-                                              lens.data(), outmap.data(), true_mask, logits, token, decision, s))
-        return r;
-      q0 = q1;
+      }
+      if (!ha.empty())
+        if (quail_status r = run_step_with_head(c, (int32_t)ha.size(), ha.data(), s_tokens, starts.data(),
+                                                lens.data(), outmap.data(), true_mask, logits, token, decision, s))
+          return r;
+      r0 = r1;
     }
   }
   return QUAIL_OK;
@@ -1772,17 +1855,18 @@ quail_status quail_join_run(quail_ctx* c, int32_t n_anchors, const int32_t* a_to
                             const int32_t* s_tokens, const int32_t* s_offsets, uint8_t true_mask,
                             float* logits, uint8_t* token, uint8_t* decision, quail_stream stream) {
   return join_run_core(c, n_anchors, a_tokens, a_offsets, n_pairs, pair_anchor, s_tokens, s_offsets, nullptr, 0,
-                       true_mask, logits, token, decision, stream);
+                       false, true_mask, logits, token, decision, stream);
 }
 
 quail_status quail_join_run_shared(quail_ctx* c, int32_t n_anchors, const int32_t* a_tokens,
                                    const int32_t* a_offsets, int32_t n_pairs, const int32_t* pair_anchor,
                                    const int32_t* s_tokens, const int32_t* s_offsets,
-                                   const int32_t* s_tokens_host, int32_t min_shared, uint8_t true_mask,
-                                   float* logits, uint8_t* token, uint8_t* decision, quail_stream stream) {
+                                   const int32_t* s_tokens_host, int32_t min_shared, int32_t nested,
+                                   uint8_t true_mask, float* logits, uint8_t* token, uint8_t* decision,
+                                   quail_stream stream) {
   if (min_shared < 1) return fail(QUAIL_E_INVAL, "min_shared must be at least 1");
   return join_run_core(c, n_anchors, a_tokens, a_offsets, n_pairs, pair_anchor, s_tokens, s_offsets,
-                       s_tokens_host, min_shared, true_mask, logits, token, decision, stream);
+                       s_tokens_host, min_shared, nested != 0, true_mask, logits, token, decision, stream);
 }
 
 quail_status quail_multijoin_run(quail_ctx* c, int32_t n_anchors, const int32_t* a_tokens,

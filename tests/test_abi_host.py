@@ -335,9 +335,9 @@ def test_prefix_prefill_and_shared_run_reject_bad_arguments():
     so, sop = _i32([0, 4])
     sh, shp = _i32([1, 2, 3, 4])
     dec = 0x7F0000000000
-    st = fc.lib.quail_join_run_shared(fc.h, 1, dec, aop, 1, pa1p, dec, sop, shp, 0, 0x0F, None, None, dec, None)
+    st = fc.lib.quail_join_run_shared(fc.h, 1, dec, aop, 1, pa1p, dec, sop, shp, 0, 0, 0x0F, None, None, dec, None)
     assert st == B.E_INVAL
-    st = fc.lib.quail_join_run_shared(fc.h, 1, dec, aop, 1, pa1p, dec, sop, None, 2, 0x0F, None, None, dec, None)
+    st = fc.lib.quail_join_run_shared(fc.h, 1, dec, aop, 1, pa1p, dec, sop, None, 2, 1, 0x0F, None, None, dec, None)
     assert st == B.E_INVAL
     fc.close()
 

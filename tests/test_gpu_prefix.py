@@ -485,3 +485,63 @@ def test_prefix_tree_composed_with_nested_nodes(B, kv_fp8):
     assert ok
     st = B.quail_pool_stats(ctx)
     assert st["prefills"] == 1 + len(nodes) and st["evictions"] == 1 + len(nodes) and st["resident"] == 0
+
+
+def test_join_run_shared_nested(B):
+    """The one-call join with nested grouping: under two anchors and among
+    filter rows, suffixes share a prompt and then, in families, a document.
+    Logits equal the plain run's and the oracle's; the nested run prefills
+    more nodes than one level does (a prompt node and document nodes under
+    it), evicts everything and has no regret."""
+    import torch
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    shape = W.tiny_shape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                         intermediate=384, vocab=512)
+    wts = W.model_weights(shape, 19)
+    r = np.random.default_rng(19)
+    a_len = [40, 90]
+    a_tok = r.integers(0, 512, sum(a_len)).astype(np.int32)
+    a_off = np.array([0, 40, 130], np.int32)
+    pairs, seqs = [], []
+    for a in (0, 1, -1):
+        prompt = r.integers(0, 512, 20).astype(np.int32)
+        for f in range(2):
+            doc = r.integers(0, 512, 12 + 4 * f).astype(np.int32)
+            for m in range(3):
+                seqs.append(np.concatenate([prompt, doc, r.integers(0, 512, 2 + m).astype(np.int32)]))
+                pairs.append(a)
+        seqs.append(np.concatenate([prompt, r.integers(0, 512, 6).astype(np.int32)]))
+        pairs.append(a)
+    n = len(seqs)
+    pa = np.array(pairs, np.int32)
+    s_off = np.zeros(n + 1, np.int32)
+    s_off[1:] = np.cumsum([len(x) for x in seqs])
+    s_tok = np.concatenate(seqs).astype(np.int32)
+    dm = DeviceModel(shape, wts, max_anchor_len=1024, max_suffix_len=256)
+    outs = {}
+    for mode in ("plain", "one", "nested"):
+        ctx = dm.context(16 << 20, 1024)           # one plan step: every tree whole
+        logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+        dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+        say("join_run", mode)
+        if mode == "plain":
+            B.quail_join_run(ctx, to_device(a_tok), a_off, pa, to_device(s_tok), s_off, 0x0F, logits, None, dec)
+        else:
+            B.quail_join_run_shared(ctx, to_device(a_tok), a_off, pa, to_device(s_tok), s_off, s_tok, 8, 0x0F,
+                                    logits, None, dec, nested=(mode == "nested"))
+        torch.cuda.synchronize()
+        outs[mode] = (logits.cpu().numpy(), dec.cpu().numpy(), B.quail_pool_stats(ctx))
+    l0 = outs["plain"][0]
+    for mode in ("one", "nested"):
+        lg, _, st = outs[mode]
+        assert rel_inf(lg, l0) <= 2e-2, (mode, rel_inf(lg, l0))
+        assert st["evictions"] == st["prefills"] and st["resident"] == 0 and st["regret_tokens"] == 0
+    assert outs["one"][2]["prefills"] == 2 + 3          # anchors + one prompt node per tree
+    assert outs["nested"][2]["prefills"] == 2 + 3 * 3   # anchors + prompt and two document nodes per tree
+    ref = [OM.forward_pair(a_tok[a_off[a]:a_off[a + 1]] if a >= 0 else [], seqs[i], wts, shape)
+           for i, a in enumerate(pairs)]
+    ref_logits = np.array([x["logits"] for x in ref])
+    assert rel_inf(outs["nested"][0], ref_logits) <= 2e-2
+    ok, _ = decisions_agree(outs["nested"][1], [x["decision"] for x in ref], [x["margin"] for x in ref],
+                            2e-2 * np.max(np.abs(ref_logits)))
+    assert ok
