@@ -645,13 +645,15 @@ def bench_shared(args):
 def bench_nested(args):
     """Documents under two shared levels, 36-layer stack, no anchor: 2,048
     documents share a 512-token prompt, then each family of 16 shares a
-    384-token document, then U{32..128} tokens of their own. Three runs on
+    384-token document, then U{32..128} tokens of their own. Four runs on
     the same inputs: the plain filter (quail_join_run), one shared level
     (quail_join_run_shared, min_shared 32: the prompt), and the nested radix
     index (quail_prefix_tree) with its nodes prefilled parents first
     (quail_anchor_prefill for the prompt, quail_prefix_prefill for the
     family documents) and every document's own tokens joined after its node
-    (quail_join_prefill, quail_head8). The second of two runs is timed."""
+    (quail_join_prefill, quail_head8), and the same nested grouping inside
+    one call (quail_join_run_shared, nested). The second of two runs is
+    timed."""
     import torch
     import workloads as W
     from query_aware_prefill_amd import binding as B
@@ -685,14 +687,17 @@ def bench_nested(args):
                        "document tokens, U{32..128} own tokens each, no anchor",
            "rows": n, "logical_tokens": logical}
     out = {}
-    for mode in ("nested", "shared", "plain"):
+    for mode in ("nested", "nested_call", "shared", "plain"):
         ctx = dm.context(pool, T)
         logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
         dec = torch.empty(n, dtype=torch.uint8, device="cuda")
         for _ in range(2):
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            if mode == "plain":
+            if mode == "nested_call":
+                B.quail_join_run_shared(ctx, dummy, [0], pa, s_tok_d, s_off, s_tok, min_shared, 0x0F, logits,
+                                        None, dec, nested=True)
+            elif mode == "plain":
                 B.quail_join_run(ctx, dummy, [0], pa, s_tok_d, s_off, 0x0F, logits, None, dec)
             elif mode == "shared":
                 B.quail_join_run_shared(ctx, dummy, [0], pa, s_tok_d, s_off, s_tok, min_shared, 0x0F, logits,
@@ -724,13 +729,14 @@ def bench_nested(args):
     computed = {"plain": logical, "shared": 512.0 + float(np.sum(s_len - 512)),
                 "nested": 512.0 + n_fam * 384.0 + float(np.sum(s_len - 896))}
     for mode in out:
-        res[mode]["computed_tokens"] = computed[mode]
-        res[mode]["computed_tokens_per_min"] = computed[mode] / res[mode]["ms"] * 60e3
+        if mode in computed:       # the one-call nested run regroups per plan step
+            res[mode]["computed_tokens"] = computed[mode]
+            res[mode]["computed_tokens_per_min"] = computed[mode] / res[mode]["ms"] * 60e3
     lp = out["plain"][0]
     tmask = np.array([(0x0F >> j) & 1 for j in range(8)], bool)
     margin = np.max(np.where(tmask, lp, -np.inf), axis=1) - np.max(np.where(~tmask, lp, -np.inf), axis=1)
     sure = np.abs(margin) > 2e-2 * np.max(np.abs(lp), axis=1)
-    for mode in ("nested", "shared"):
+    for mode in ("nested", "nested_call", "shared"):
         res[mode]["speedup_over_plain"] = res["plain"]["ms"] / res[mode]["ms"]
         res[mode]["logits_rel_inf_vs_plain"] = float(np.max(np.abs(out[mode][0] - lp)) / np.max(np.abs(lp)))
         res[mode]["decisions_beyond_tau_equal"] = [int(np.sum(out[mode][1][sure] == out["plain"][1][sure])),

@@ -1595,14 +1595,30 @@ static quail_status join_run_core(quail_ctx* c, int32_t n_anchors, const int32_t
       starts[i] = s_offsets[i];
       keys[i] = pair_anchor[i] >= 0 ? pair_anchor[i] : n_anchors;   // filter rows group among themselves
     }
-    const int32_t nn = prefix_groups(n_pairs, s_tokens_host, starts.data(), plen.data(), keys.data(), min_shared,
-                                     gof.data(), nf.data(), nl.data());
-    std::vector<int32_t> members(nn, 0);
-    for (int32_t i = 0; i < n_pairs; ++i)
-      if (gof[i] >= 0) members[gof[i]]++;
-    for (int32_t i = 0; i < n_pairs; ++i)
-      if (gof[i] >= 0)
-        step_len[i] = plen[i] - nl[gof[i]] + (nl[gof[i]] + members[gof[i]] - 1) / members[gof[i]];
+    if (!nested) {
+      const int32_t nn = prefix_groups(n_pairs, s_tokens_host, starts.data(), plen.data(), keys.data(), min_shared,
+                                       gof.data(), nf.data(), nl.data());
+      std::vector<int32_t> members(nn, 0);
+      for (int32_t i = 0; i < n_pairs; ++i)
+        if (gof[i] >= 0) members[gof[i]]++;
+      for (int32_t i = 0; i < n_pairs; ++i)
+        if (gof[i] >= 0)
+          step_len[i] = plen[i] - nl[gof[i]] + (nl[gof[i]] + members[gof[i]] - 1) / members[gof[i]];
+    } else {
+      // own tokens after the deepest node, plus a share of every node above
+      std::vector<TreeNode> tn;
+      prefix_tree(n_pairs, s_tokens_host, starts.data(), plen.data(), keys.data(), min_shared, gof.data(), tn);
+      std::vector<int32_t> members(tn.size(), 0);
+      for (int32_t i = 0; i < n_pairs; ++i)
+        for (int32_t v = gof[i]; v >= 0; v = tn[v].parent) members[v]++;
+      for (int32_t i = 0; i < n_pairs; ++i) {
+        if (gof[i] < 0) continue;
+        int32_t len = plen[i] - tn[gof[i]].end;
+        for (int32_t v = gof[i]; v >= 0; v = tn[v].parent)
+          len += (tn[v].end - tn[v].start + members[v] - 1) / members[v];
+        step_len[i] = len;
+      }
+    }
   }
   // Shared-prefix nodes of each plan step, parents first: one level
   // (prefix_groups) or the nested tree (prefix_tree). A node continues its
