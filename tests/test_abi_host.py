@@ -397,3 +397,46 @@ def test_prefix_tree_matches_oracle(case, m):
     g, nodes = B.quail_prefix_tree(toks, off, keys, m)
     rg, rnodes = OPX.prefix_tree_reference(seqs, keys, m)
     assert np.array_equal(g, rg) and nodes == rnodes
+
+
+def test_prefix_tree_argument_checks():
+    lib = B.load()
+    toks, tp = _i32([1, 2, 3, 4])
+    a, ap = _i32([0, 0])
+    nn = C.c_int32(7)
+    off, offp = _i32([0, 2, 4])
+    assert lib.quail_prefix_tree(2, tp, offp, None, 0, ap, ap, ap, ap, ap, C.byref(nn)) == B.E_INVAL
+    assert lib.quail_prefix_tree(2, tp, offp, None, 1, ap, None, ap, ap, ap, C.byref(nn)) == B.E_INVAL
+    assert lib.quail_prefix_tree(2, tp, offp, None, 1, ap, ap, ap, ap, ap, None) == B.E_INVAL
+    for offs in ([0, 3, 2], [0, 0, 4]):
+        off, offp = _i32(offs)
+        assert lib.quail_prefix_tree(2, tp, offp, None, 1, ap, ap, ap, ap, ap, C.byref(nn)) == B.E_INVAL, offs
+    assert lib.quail_prefix_tree(0, None, None, None, 1, None, None, None, None, None, C.byref(nn)) == B.OK
+    assert nn.value == 0
+
+
+def test_join_search_frontier_buffer():
+    """The frontier output is optional with cap 0, truncated to cap, and
+    rejected as NULL with cap > 0; n_frontier always gives the full size."""
+    cfg = _cfg()
+    tables = [(64, 1024.0), (2048, 64.0), (300, 200.0)]
+    joins = [(0, 1, 4.0, 2.0, 0.25, 1), (1, 2, 3.0, 1.0, 0.5, 1)]
+    full = B.quail_join_search(cfg, tables, joins, 2.5e15, 8e12)
+    assert full["n_frontier"] >= 1
+    one = B.quail_join_search(cfg, tables, joins, 2.5e15, 8e12, cap=1)
+    assert one["n_frontier"] == full["n_frontier"] and len(one["frontier"]) == 1
+    assert np.array_equal(one["frontier"][0], full["frontier"][0])
+    lib = B.load()
+    ta = (B.Table * 3)(*[B.Table(r, t) for r, t in tables])
+    ja = (B.AIJoin * 2)(*[B.AIJoin(*j) for j in joins])
+    order, op = _i32([0, 0, 0])
+    ar, arp = _i32([0, 0])
+    met = np.zeros(4)
+    nf = C.c_int32()
+    f64p = C.POINTER(C.c_double)
+    st = lib.quail_join_search(C.byref(cfg), 3, ta, 2, ja, 2.5e15, 8e12, op, arp, met.ctypes.data_as(f64p),
+                               None, 4, C.byref(nf))
+    assert st == B.E_INVAL
+    st = lib.quail_join_search(C.byref(cfg), 3, ta, 2, ja, 2.5e15, 8e12, op, arp, met.ctypes.data_as(f64p),
+                               None, 0, C.byref(nf))
+    assert st == B.OK and nf.value == full["n_frontier"]
