@@ -68,8 +68,9 @@ class Stager {
  public:
   ~Stager() {
     for (auto& s : slots_) {
-      if (s.ev) { hipEventSynchronize(s.ev); hipEventDestroy(s.ev); }
-      if (s.buf) hipHostFree(s.buf);
+      // teardown: nothing to report an error to
+      if (s.ev) { (void)hipEventSynchronize(s.ev); (void)hipEventDestroy(s.ev); }
+      if (s.buf) (void)hipHostFree(s.buf);
     }
   }
   // Copies `bytes` from host memory `src` to device `dst` on `stream`; `src`
@@ -89,7 +90,7 @@ class Stager {
       if (e != hipSuccess) return e;
     }
     if (s.cap < bytes) {
-      if (s.buf) hipHostFree(s.buf);
+      if (s.buf) (void)hipHostFree(s.buf);   // its last copy completed (event above)
       s.buf = nullptr;
       s.cap = 0;
       e = hipHostMalloc(&s.buf, align_up(bytes, 1 << 20), hipHostMallocDefault);
@@ -1389,7 +1390,6 @@ quail_status join_core(quail_ctx* c, int32_t n, const quail_anchor* ha, const in
     return kx < ky;
   });
   const int G = cf.n_q_heads / cf.n_kv_heads;
-  const size_t esz = kv_elem_bytes(cf);
   const bool slab_fp8 = cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3;
   int32_t p0 = 0;
   while (p0 < n) {
