@@ -41,9 +41,11 @@ position 0 is the identity, preserves pair norms and is relative
 (<R_p q, R_p' k> = <R_(p-p') q, k>); one decoder layer in "exact" mode against
 the transformers library's Llama decoder layer (rotate-half RoPE, RMSNorm,
 SwiGLU, GQA) in float64; the 8-column head equals the same columns of a full
-head; argmax tie-break; anchor K/V independent of the suffix. The 36-layer
-composition has no external value to compare against: parity unpinned beyond
-its parts and the invariants above.
+head; argmax tie-break; anchor K/V independent of the suffix; the whole
+stack (embedding, three decoder layers over [anchor | suffix], final norm, the
+head at the last position) in "exact" mode against the transformers library's
+Llama causal LM in float64 whose first 8 vocabulary rows are the 8-column
+head. The 36-layer stack is the same loop at a larger count.
 """
 from __future__ import annotations
 

@@ -1,7 +1,8 @@
 """Pins for oracle/model.py: library RMSNorm/SiLU, RoPE properties, one decoder
 layer against the transformers library's Llama decoder layer (float64), the
-8-column head against the same columns of a full head, argmax tie-break, and
-anchor-KV independence from the suffix."""
+8-column head against the same columns of a full head, argmax tie-break,
+anchor-KV independence from the suffix, and the whole stack against the
+transformers library's Llama causal LM (float64)."""
 import math
 
 import numpy as np
@@ -190,3 +191,53 @@ def test_forward_pair_filter_row_and_decision_consistency():
     o1 = M.forward_pair(a, s, wts, shape)
     h = M.forward_tokens(np.concatenate([a, s]), wts, shape)
     assert np.array_equal(o1["h_last"], h[-1])
+
+
+def test_stack_exact_matches_transformers_llama_model():
+    """The composition: embedding lookup, several decoder layers over
+    [anchor | suffix] at positions 0..N-1, the final RMSNorm and the head at
+    the last position, against the transformers library's Llama causal LM in
+    float64 whose first 8 vocabulary rows are the 8-column head (the other
+    rows zero) -- so a mistake in the stacking (a layer skipped or repeated,
+    the positions, the final norm, the row the head reads) fails here."""
+    from transformers import LlamaConfig, LlamaForCausalLM
+    shape = W.tiny_shape(n_layers=3, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                         intermediate=384, vocab=64)
+    wts = W.model_weights(shape, 5)
+    cfg = LlamaConfig(hidden_size=shape.hidden, intermediate_size=shape.intermediate,
+                      num_attention_heads=shape.n_q_heads, num_key_value_heads=shape.n_kv_heads,
+                      head_dim=shape.head_dim, rms_norm_eps=shape.rms_eps, rope_theta=shape.rope_theta,
+                      max_position_embeddings=8192, attention_bias=False, mlp_bias=False,
+                      vocab_size=shape.vocab, num_hidden_layers=shape.n_layers, tie_word_embeddings=False)
+    cfg._attn_implementation = "sdpa"
+    lm = LlamaForCausalLM(cfg).double().eval()
+    qd, kd = shape.q_dim, shape.kv_dim
+    with torch.no_grad():
+        lm.model.embed_tokens.weight.copy_(torch.from_numpy(codecs.bf16_value(wts["embed"])))
+        for l, layer in enumerate(lm.model.layers):
+            lw = M.LayerWeights(wts["layers"][l], shape)
+            layer.self_attn.q_proj.weight.copy_(torch.from_numpy(lw.w_qkv[:qd]))
+            layer.self_attn.k_proj.weight.copy_(torch.from_numpy(lw.w_qkv[qd:qd + kd]))
+            layer.self_attn.v_proj.weight.copy_(torch.from_numpy(lw.w_qkv[qd + kd:]))
+            layer.self_attn.o_proj.weight.copy_(torch.from_numpy(lw.w_o))
+            layer.mlp.gate_proj.weight.copy_(torch.from_numpy(lw.w_gate))
+            layer.mlp.up_proj.weight.copy_(torch.from_numpy(lw.w_up))
+            layer.mlp.down_proj.weight.copy_(torch.from_numpy(lw.w_down))
+            layer.input_layernorm.weight.copy_(torch.from_numpy(lw.attn_norm))
+            layer.post_attention_layernorm.weight.copy_(torch.from_numpy(lw.mlp_norm))
+        lm.model.norm.weight.copy_(torch.from_numpy(codecs.bf16_value(wts["final_norm"])))
+        head = np.zeros((shape.vocab, shape.hidden))
+        head[:8] = codecs.bf16_value(wts["head8"]).T
+        lm.lm_head.weight.copy_(torch.from_numpy(head))
+    r = np.random.default_rng(11)
+    for a_len, s_len in [(23, 9), (0, 17), (40, 1)]:
+        a = r.integers(0, shape.vocab, a_len)
+        s = r.integers(0, shape.vocab, s_len)
+        ours = M.forward_pair(a, s, wts, shape, true_mask=0x0F, mode="exact")
+        with torch.no_grad():
+            ids = torch.from_numpy(np.concatenate([a, s]).astype(np.int64))[None]
+            ref = lm(input_ids=ids).logits[0, -1, :8].numpy()
+        rel = np.max(np.abs(ours["logits"] - ref)) / np.max(np.abs(ref))
+        assert rel < 1e-5, (a_len, s_len, rel)
+        tok, dec, _ = M.decide(ref[None], 0x0F)
+        assert ours["token"] == int(tok[0]) and ours["decision"] == int(dec[0])
