@@ -240,7 +240,9 @@ def test_c1_full_size_sampled(B):
     """The full configuration (256 anchors x 64 suffixes, 1.31M suffix tokens,
     32q/8kv x 128) in one launch, as the benchmark runs it; 12 sampled
     suffixes (first and last of the batch included) are checked against the
-    oracle."""
+    oracle, and every output by properties: a second launch gives the same
+    bits, every LSE is finite, and each output lies in the range of the V
+    values its row sees."""
     import torch
     say("C1 full size: generating on device")
     case = W.c1_device(seed=1)
@@ -273,3 +275,45 @@ def test_c1_full_size_sampled(B):
         lerr = float(np.max(np.abs(host(lse[t0:t1]) - rl)))
         say("  suffix", s, "rel", err, "lse", lerr)
         assert err <= 2e-2 and lerr <= 1e-2
+    # properties over every output of the full launch: a second launch gives
+    # the same bits (no order-dependent reduction), every LSE is finite (each
+    # suffix token sees at least itself), and each output lies in the range of
+    # the values its row can see -- the anchor's and its suffix's V rows of the
+    # row's KV head -- up to the bf16 rounding of P and of the output
+    say("C1 full size: second launch and properties of every output")
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    B.quail_cascade_attn(B.DTYPE_BF16, 32, 8, 128, case["sm_scale"], case["ak"], case["av"],
+                         case["a_off"], case["s_anchor"], case["q"], case["k"], case["v"],
+                         case["s_off"], out2, lse2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse, lse2)
+    assert bool(torch.isfinite(lse).all())
+    dev = out.device
+    s_len = torch.from_numpy(np.diff(case["s_off"]).astype(np.int64)).to(dev)
+    a_len = torch.from_numpy(np.diff(case["a_off"]).astype(np.int64)).to(dev)
+    seg = torch.repeat_interleave(torch.arange(n_suf, device=dev), s_len)
+    aseg = torch.repeat_interleave(torch.arange(len(a_len), device=dev), a_len)
+
+    def seg_range(v, idx, n):
+        ix = idx[:, None, None].expand(-1, v.shape[1], v.shape[2])
+        lo = torch.full((n, v.shape[1], v.shape[2]), math.inf, device=dev)
+        hi = torch.full((n, v.shape[1], v.shape[2]), -math.inf, device=dev)
+        return lo.scatter_reduce(0, ix, v, "amin"), hi.scatter_reduce(0, ix, v, "amax")
+
+    s_lo, s_hi = seg_range(case["v"].float(), seg, n_suf)
+    a_lo, a_hi = seg_range(case["av"].float(), aseg, len(a_len))
+    sa = torch.from_numpy(case["s_anchor"].astype(np.int64)).to(dev)
+    lo = torch.minimum(s_lo, a_lo[sa]).repeat_interleave(4, dim=1)     # [suffix, q head, dim]
+    hi = torch.maximum(s_hi, a_hi[sa]).repeat_interleave(4, dim=1)
+    worst = 0.0
+    for t0 in range(0, T, 1 << 17):
+        t1 = min(T, t0 + (1 << 17))
+        o = out[t0:t1].float()
+        sg = seg[t0:t1]
+        l, h = lo[sg], hi[sg]
+        tol = 1e-2 * torch.maximum(l.abs(), h.abs())
+        assert bool(((o >= l - tol) & (o <= h + tol)).all()), t0
+        worst = max(worst, float(torch.clamp(torch.maximum(l - o, o - h), min=0).max()))
+    say("  largest step outside the visible value range", worst)
