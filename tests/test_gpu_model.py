@@ -343,7 +343,9 @@ def test_c2_full_size_layer_sampled(B):
     8,192 pairs, 65,536-token batches, Qwen3-4B layer shapes): logits of
     sampled pairs (first and last pair of the first and last anchor, two
     more) against the oracle's per-pair forward, decisions where the margin
-    exceeds the tolerance."""
+    exceeds the tolerance; every pair by properties (finite logits, decision
+    = the mask bit of its logits' first argmax, identical bits on a second
+    run)."""
     import torch
     from query_aware_prefill_amd.device import DeviceModel, to_device
     shape = W.ModelShape(n_layers=1, hidden=2560, n_q_heads=32, n_kv_heads=8, head_dim=128,
@@ -374,3 +376,17 @@ def test_c2_full_size_layer_sampled(B):
         assert err <= 2e-2, (i, err)
         if abs(ref["margin"]) > 2e-2 * np.max(np.abs(ref["logits"])):
             assert dg[i] == ref["decision"], i
+    # every pair: finite logits, each decision is its own logits' first
+    # argmax mapped through the TRUE mask, and a second run (anchors
+    # prefilled again after their eviction) gives the same bits
+    say("C2 full size: properties of every pair and a second run")
+    assert np.isfinite(lg).all()
+    tok = np.argmax(lg, axis=1)
+    assert np.array_equal(dg, ((0x0F >> tok) & 1).astype(np.uint8))
+    logits2 = torch.empty_like(logits)
+    dec2 = torch.empty_like(dec)
+    B.quail_join_run(ctx, to_device(case["a_tok"]), case["a_off"], case["pair_anchor"], to_device(case["s_tok"]),
+                     case["s_off"], 0x0F, logits2, None, dec2)
+    torch.cuda.synchronize()
+    assert np.array_equal(logits2.cpu().numpy().view(np.uint32), lg.view(np.uint32))
+    assert np.array_equal(dec2.cpu().numpy(), dg)
