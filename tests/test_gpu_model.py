@@ -390,3 +390,45 @@ def test_c2_full_size_layer_sampled(B):
     torch.cuda.synchronize()
     assert np.array_equal(logits2.cpu().numpy().view(np.uint32), lg.view(np.uint32))
     assert np.array_equal(dec2.cpu().numpy(), dg)
+
+
+def test_filter_full_size_one_layer_sampled(B):
+    """The filter workload at full size (10,000 rows, lognormal lengths
+    200..2000, 7.2 M tokens, no anchor) through one Qwen3-4B-shaped layer in
+    the launch configuration the benchmark uses (one quail_join_run call,
+    65,536-token batches): the shortest, the longest and two more rows
+    against the oracle's per-row forward, and every row by properties
+    (finite logits, decision = the mask bit of its logits' first argmax)."""
+    import torch
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    shape = W.ModelShape(n_layers=1, hidden=2560, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                         intermediate=9728, vocab=W.QWEN3_4B.vocab)
+    say("filter full size: weights and workload")
+    wts = W.model_weights(shape, 0)
+    case = W.c3a_case()
+    s_off, s_tok = case["s_off"], case["s_tok"]
+    s_len = np.diff(s_off)
+    n = len(s_len)
+    assert n == 10000 and 200 <= s_len.min() and s_len.max() <= 2000
+    pa = -np.ones(n, np.int32)
+    dm = DeviceModel(shape, wts, max_anchor_len=1, max_suffix_len=int(s_len.max()))
+    ctx = dm.context(1 << 20, 65536)
+    logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+    dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+    say("filter full size: join_run over", n, "rows,", int(s_off[-1]), "tokens")
+    B.quail_join_run(ctx, to_device(np.zeros(1, np.int32)), [0], pa, to_device(s_tok), s_off, 0x0F,
+                     logits, None, dec)
+    torch.cuda.synchronize()
+    lg, dg = logits.cpu().numpy(), dec.cpu().numpy()
+    assert np.isfinite(lg).all()
+    assert np.array_equal(dg, ((0x0F >> np.argmax(lg, axis=1)) & 1).astype(np.uint8))
+    sample = [int(np.argmin(s_len)), int(np.argmax(s_len))] + np.random.default_rng(3).integers(0, n, 2).tolist()
+    say("filter full size: oracle on rows", sample, "of lengths", [int(s_len[i]) for i in sample])
+    layers = [OM.LayerWeights(wts["layers"][0], shape)]
+    for i in sample:
+        ref = OM.forward_pair(np.zeros(0, np.int32), s_tok[s_off[i]:s_off[i + 1]], wts, shape, layers=layers)
+        err = rel_inf(lg[i], ref["logits"])
+        say("  row", i, "rel", err)
+        assert err <= 2e-2, (i, err)
+        if abs(ref["margin"]) > 2e-2 * np.max(np.abs(ref["logits"])):
+            assert dg[i] == ref["decision"], i
