@@ -432,3 +432,58 @@ def test_filter_full_size_one_layer_sampled(B):
         assert err <= 2e-2, (i, err)
         if abs(ref["margin"]) > 2e-2 * np.max(np.abs(ref["logits"])):
             assert dg[i] == ref["decision"], i
+
+
+def test_multijoin_full_size_one_layer_sampled(B):
+    """The multi-join workload at full size (1024 anchors x 768 tokens with
+    E4M3 K/V slabs; 5,000 rows of U{48..256} tokens, each against 51 random
+    anchors: 255,000 pairs, 38.9 M suffix tokens) through one Qwen3-4B-shaped
+    layer in one quail_join_run call: every anchor prefilled once and evicted
+    after its last pair, sampled pairs (first, last, two more) against the
+    oracle's per-pair forward with the anchor's K/V stored in E4M3, and every
+    pair by properties (finite logits, decision = the mask bit of its logits'
+    first argmax)."""
+    import torch
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    shape = W.ModelShape(n_layers=1, hidden=2560, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                         intermediate=9728, vocab=W.QWEN3_4B.vocab, kv_fp8=True)
+    say("multi-join full size: weights and workload")
+    wts = W.model_weights(shape, 0)
+    case = W.c4_case()
+    pa, prow = case["pair_anchor"], case["pair_row"]
+    plen = case["row_len"][prow]
+    n = len(pa)
+    assert n == 255000
+    s_off = np.zeros(n + 1, np.int64)
+    s_off[1:] = np.cumsum(plen)
+    assert s_off[-1] < 2 ** 31
+    s_off = s_off.astype(np.int32)
+    ro = case["row_off"]
+    s_tok = np.concatenate([case["row_tok"][ro[r]:ro[r + 1]] for r in prow])
+    dm = DeviceModel(shape, wts, max_anchor_len=768, max_suffix_len=int(plen.max()))
+    pool = 1024 * B.quail_anchor_bytes(dm.cfg, 768) + (1 << 20)
+    ctx = dm.context(pool, 65536)
+    logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+    dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+    say("multi-join full size: join_run over", n, "pairs,", int(s_off[-1]), "suffix tokens")
+    B.quail_join_run(ctx, to_device(case["a_tok"]), case["a_off"], pa, to_device(s_tok), s_off, 0x0F,
+                     logits, None, dec)
+    torch.cuda.synchronize()
+    lg, dg = logits.cpu().numpy(), dec.cpu().numpy()
+    st = B.quail_pool_stats(ctx)
+    assert st["prefills"] == 1024 and st["evictions"] == 1024 and st["resident"] == 0
+    assert st["regret_tokens"] == 0
+    assert np.isfinite(lg).all()
+    assert np.array_equal(dg, ((0x0F >> np.argmax(lg, axis=1)) & 1).astype(np.uint8))
+    sample = [0, n - 1] + np.random.default_rng(4).integers(0, n, 2).tolist()
+    say("multi-join full size: oracle on pairs", sample)
+    layers = [OM.LayerWeights(wts["layers"][0], shape)]
+    for i in sample:
+        a = int(pa[i])
+        ref = OM.forward_pair(case["a_tok"][case["a_off"][a]:case["a_off"][a + 1]], s_tok[s_off[i]:s_off[i + 1]],
+                              wts, shape, layers=layers)
+        err = rel_inf(lg[i], ref["logits"])
+        say("  pair", i, "rel", err)
+        assert err <= 2e-2, (i, err)
+        if abs(ref["margin"]) > 2e-2 * np.max(np.abs(ref["logits"])):
+            assert dg[i] == ref["decision"], i
