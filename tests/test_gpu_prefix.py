@@ -545,3 +545,88 @@ def test_join_run_shared_nested(B):
     ok, _ = decisions_agree(outs["nested"][1], [x["decision"] for x in ref], [x["margin"] for x in ref],
                             2e-2 * np.max(np.abs(ref_logits)))
     assert ok
+
+
+def _full_size_case(kind, vocab):
+    """Token layouts of the 36-layer benchmark workloads at their full sizes:
+    the plain join (64 anchors x 1024, 2048 suffixes of 64 per anchor), the
+    join with shared suffix prefixes (16 anchors x 1024, 16 families x 8 per
+    anchor sharing 384 tokens), documents sharing a prefix per family (128 x
+    16 sharing 768, no anchor) and documents under two shared levels (a
+    512-token prompt, families of 16 sharing 384 more, no anchor)."""
+    if kind == "join":
+        c = W.c3b_case()
+        return c["a_tok"], c["a_off"], c["pair_anchor"], c["s_tok"], c["s_off"]
+    r = np.random.default_rng([7, 0])
+    if kind == "nested":
+        r = np.random.default_rng([8, 0])
+        prompt = r.integers(0, vocab, 512).astype(np.int32)
+        docs = [r.integers(0, vocab, 384).astype(np.int32) for _ in range(128)]
+        seqs = [np.concatenate([prompt, docs[i // 16], r.integers(0, vocab, int(r.integers(32, 129)))
+                                .astype(np.int32)]) for i in range(128 * 16)]
+        s_off = np.zeros(len(seqs) + 1, np.int32)
+        s_off[1:] = np.cumsum([len(x) for x in seqs])
+        return (np.zeros(1, np.int32), np.zeros(1, np.int32), -np.ones(len(seqs), np.int32),
+                np.concatenate(seqs).astype(np.int32), s_off)
+    if kind == "traces":
+        n_anchors = 0
+        fams = [(-1, 768, r.integers(32, 129, 16).tolist()) for _ in range(128)]
+    else:
+        n_anchors = 16
+        fams = [(a, 384, r.integers(16, 65, 8).tolist()) for a in range(16) for _ in range(16)]
+    c = W.shared_prefix_case(7, vocab, [1024] * n_anchors, fams, cfg_id=7)
+    a_tok = c["a_tok"] if len(c["a_tok"]) else np.zeros(1, np.int32)
+    return a_tok, c["a_off"], c["pair_anchor"], c["s_tok"], c["s_off"]
+
+
+@pytest.mark.parametrize("kind", ["join", "shared", "traces", "nested"])
+def test_full_size_workloads_one_layer_sampled(B, kind):
+    """The 36-layer benchmark workloads at full size through one
+    Qwen3-4B-shaped layer, in the calls the benchmark makes (quail_join_run
+    for the plain join; quail_join_run_shared with min_shared 32, one level or
+    nested, for the others): four sampled pairs (first, last, two more)
+    against the oracle's per-pair forward over [anchor | whole suffix], every
+    pair by properties (finite logits, decision = the mask bit of its logits'
+    first argmax), and every slab evicted after its last use with no regret."""
+    import torch
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    shape = W.ModelShape(n_layers=1, hidden=2560, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                         intermediate=9728, vocab=W.QWEN3_4B.vocab)
+    say("full size", kind, ": weights and workload")
+    wts = W.model_weights(shape, 0)
+    a_tok, a_off, pa, s_tok, s_off = _full_size_case(kind, shape.vocab)
+    n = len(pa)
+    s_len = np.diff(s_off)
+    a_len = np.diff(a_off)
+    dm = DeviceModel(shape, wts, max_anchor_len=1024, max_suffix_len=int(s_len.max()))
+    pool = sum(B.quail_anchor_bytes(dm.cfg, int(x)) for x in a_len) + (2 << 30)
+    ctx = dm.context(pool, 65536)
+    logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+    dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a_d, s_d = to_device(a_tok), to_device(s_tok)
+    say("full size", kind, ":", n, "pairs,", int(s_off[-1]), "suffix tokens")
+    if kind == "join":
+        B.quail_join_run(ctx, a_d, a_off, pa, s_d, s_off, 0x0F, logits, None, dec)
+    else:
+        B.quail_join_run_shared(ctx, a_d, a_off, pa, s_d, s_off, s_tok, 32, 0x0F, logits, None, dec,
+                                nested=(kind == "nested"))
+    torch.cuda.synchronize()
+    lg, dg = logits.cpu().numpy(), dec.cpu().numpy()
+    st = B.quail_pool_stats(ctx)
+    say("  pool", st)
+    assert st["resident"] == 0 and st["evictions"] == st["prefills"] and st["regret_tokens"] == 0
+    if kind != "join":
+        assert st["prefills"] > len(a_len)              # prefix nodes were prefilled
+    assert np.isfinite(lg).all()
+    assert np.array_equal(dg, ((0x0F >> np.argmax(lg, axis=1)) & 1).astype(np.uint8))
+    sample = [0, n - 1] + np.random.default_rng(6).integers(0, n, 2).tolist()
+    layers = [OM.LayerWeights(wts["layers"][0], shape)]
+    for i in sample:
+        a = int(pa[i])
+        at = a_tok[a_off[a]:a_off[a + 1]] if a >= 0 else np.zeros(0, np.int32)
+        ref = OM.forward_pair(at, s_tok[s_off[i]:s_off[i + 1]], wts, shape, layers=layers)
+        err = rel_inf(lg[i], ref["logits"])
+        say("  pair", i, "rel", err)
+        assert err <= 2e-2, (kind, i, err)
+        if abs(ref["margin"]) > 2e-2 * np.max(np.abs(ref["logits"])):
+            assert dg[i] == ref["decision"], (kind, i)
