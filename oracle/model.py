@@ -60,8 +60,10 @@ def _bf(x, mode):
 
 
 def weight_eff(codes, scale_bits, dtype=np.float64):
-    """W_eff[o, i] = decode(codes[o, i]) * scale[o]."""
-    w = codecs.e4m3_decode(codes) * codecs.bf16_value(scale_bits)[:, None]
+    """W_eff[o, i] = decode(codes[o, i]) * scale[o]. The decode is looked up
+    in the 256-entry table of e4m3_decode over every code (same values)."""
+    table = codecs.e4m3_decode(np.arange(256, dtype=np.uint8))
+    w = table[np.asarray(codes, np.uint8)] * codecs.bf16_value(scale_bits)[:, None]
     return w.astype(dtype)
 
 
@@ -202,3 +204,68 @@ def forward_pair(anchor_tokens, suffix_tokens, weights, shape, true_mask=0x0F,
                                      true_mask, shape, mode)
     return dict(h=h, h_last=h[-1], logits=logits[0], token=int(tok[0]),
                 decision=int(dec[0]), margin=float(margin[0]))
+
+
+def forward_many(seqs, weights, shape, true_mask=0x0F, mode="contract", dtype=np.float64,
+                 fp8_kv_upto=None, n_layers=None, taps=()):
+    """The per-pair definition applied to many sequences at once.
+
+    seqs: list of token sequences (each [anchor ‖ suffix], or a filter row);
+    each is its own causal sequence at positions 0..N-1, exactly as in
+    forward_pair. The per-token maps (norms, projections, RoPE, SwiGLU,
+    residual adds) are applied to the rows of all sequences stacked into one
+    matrix, which changes nothing for any row; attention runs per sequence.
+    fp8_kv_upto: per sequence, the leading positions whose K/V are held as
+    fp8 (None = none). Each layer's weights are dequantised once.
+
+    Returns a dict with logits [S, 8], token, decision, margin [S] after
+    n_layers layers and, for every depth d in ``taps``, the same four arrays
+    for the head applied after layer d (key d).
+    """
+    L = shape.n_layers if n_layers is None else n_layers
+    lens = [len(x) for x in seqs]
+    starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    tokens = np.concatenate([np.asarray(x, np.int64) for x in seqs])
+    pos = np.concatenate([np.arange(n) for n in lens])
+    last = starts[1:] - 1
+    upto = [0] * len(seqs) if fp8_kv_upto is None else list(fp8_kv_upto)
+    Hq, Hkv, d = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    h = embed(tokens, weights, dtype)
+    out = {}
+
+    def head(hl):
+        lg, tk, dc, mg = head8(hl, weights.get("final_norm"), weights["head8"], true_mask, shape, mode)
+        return dict(logits=lg, token=tk, decision=dc, margin=mg)
+
+    for l in range(L):
+        W = LayerWeights(weights["layers"][l], shape, dtype)
+        N = h.shape[0]
+        u = _bf(rmsnorm(h, W.attn_norm, shape.rms_eps), mode)
+        qkv = u @ W.w_qkv.T
+        q = qkv[:, :Hq * d].reshape(N, Hq, d)
+        k = qkv[:, Hq * d:(Hq + Hkv) * d].reshape(N, Hkv, d)
+        v = qkv[:, (Hq + Hkv) * d:].reshape(N, Hkv, d)
+        q = _bf(rope(q, pos, shape.rope_theta), mode)
+        k = _bf(rope(k, pos, shape.rope_theta), mode)
+        v = _bf(v, mode)
+        o = np.empty((N, Hq, d), q.dtype)
+        for i in range(len(seqs)):
+            a, b = starts[i], starts[i + 1]
+            ks, vs = k[a:b], v[a:b]
+            if upto[i] > 0:
+                ks = ks.copy()
+                vs = vs.copy()
+                ks[:upto[i]] = codecs.e4m3_roundtrip(ks[:upto[i]], shape.k_scale)
+                vs[:upto[i]] = codecs.e4m3_roundtrip(vs[:upto[i]], shape.v_scale)
+            o[a:b], _ = attention_causal(q[a:b], ks, vs, 1.0 / np.sqrt(d))
+        o = _bf(o.reshape(N, Hq * d), mode)
+        h = _bf(h + o @ W.w_o.T, mode)
+        u = _bf(rmsnorm(h, W.mlp_norm, shape.rms_eps), mode)
+        m = _bf(silu(u @ W.w_gate.T) * (u @ W.w_up.T), mode)
+        h = _bf(h + m @ W.w_down.T, mode)
+        del W
+        if (l + 1) in taps:
+            out[l + 1] = head(h[last])
+    out.update(head(h[last]))
+    out["h_last"] = h[last]
+    return out

@@ -241,3 +241,50 @@ def test_stack_exact_matches_transformers_llama_model():
         assert rel < 1e-5, (a_len, s_len, rel)
         tok, dec, _ = M.decide(ref[None], 0x0F)
         assert ours["token"] == int(tok[0]) and ours["decision"] == int(dec[0])
+
+
+def test_forward_many_equals_forward_pair():
+    """The batched form is the per-pair definition applied to each sequence:
+    the same logits, tokens and decisions as forward_pair for every sequence
+    (joins, a filter row, fp8 anchor K/V on some sequences), and each tapped
+    depth d equals forward_pair truncated to d layers. A position that ran on
+    across sequences, a row mixed into another sequence's attention, or an
+    fp8 store applied to the wrong rows fails here."""
+    shape = W.tiny_shape(n_layers=3, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                         intermediate=384, vocab=64, kv_fp8=True)
+    wts = W.model_weights(shape, 21)
+    r = np.random.default_rng(22)
+    pairs = [(r.integers(0, 64, 19), r.integers(0, 64, 5)), ([], r.integers(0, 64, 11)),
+             (r.integers(0, 64, 7), r.integers(0, 64, 1)), (r.integers(0, 64, 30), r.integers(0, 64, 12))]
+    seqs = [np.concatenate([np.asarray(a, np.int64), s]) for a, s in pairs]
+    upto = [len(a) for a, _ in pairs]
+    for mode in ("exact", "contract"):
+        got = M.forward_many(seqs, wts, shape, mode=mode, fp8_kv_upto=upto, taps=(1, 2))
+        for depth in (1, 2, 3):
+            g = got if depth == 3 else got[depth]
+            for i, (a, s) in enumerate(pairs):
+                ref = M.forward_pair(a, s, wts, shape, mode=mode, n_layers=depth)
+                rel = np.max(np.abs(g["logits"][i] - ref["logits"])) / np.max(np.abs(ref["logits"]))
+                # exact: equal up to BLAS summation order; contract: also up to
+                # the rare one-ulp bf16 flip that order causes
+                assert rel <= (1e-12 if mode == "exact" else 2e-2), (mode, depth, i, rel)
+                if mode == "exact":
+                    assert g["token"][i] == ref["token"] and g["decision"][i] == ref["decision"]
+    # without fp8 rows it is the bf16-KV definition again
+    plain = W.tiny_shape(n_layers=3, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                         intermediate=384, vocab=64)
+    got = M.forward_many(seqs, wts, plain, mode="exact")
+    for i, (a, s) in enumerate(pairs):
+        ref = M.forward_pair(a, s, wts, plain, mode="exact")
+        assert np.max(np.abs(got["logits"][i] - ref["logits"])) <= 1e-12 * np.max(np.abs(ref["logits"]))
+
+
+def test_depth_scaled_residual_projections():
+    """The random-init reading: QKV and gate/up weights have std 0.02, the
+    residual-writing O and down projections 0.02 / sqrt(2 * n_layers)."""
+    shape = W.tiny_shape(n_layers=8, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                         intermediate=384, vocab=64)
+    lw = M.LayerWeights(W.layer_weights(shape, 3, 0), shape)
+    for w, std in ((lw.w_qkv, 0.02), (lw.w_gate, 0.02), (lw.w_up, 0.02),
+                   (lw.w_o, 0.02 / 4.0), (lw.w_down, 0.02 / 4.0)):
+        assert abs(np.std(w) / std - 1.0) < 0.15, (np.std(w), std)

@@ -12,10 +12,12 @@ Byte formats
     keeping the top 16 bits of a float32 draw (truncation). That choice only
     shapes the input distribution; it is not the round-to-nearest-even rule
     the method applies to its own intermediates.
-  * fp8 weights are ``uint8`` OCP E4M3 codes drawn bit-field by bit-field
-    (sign, exponent field, mantissa field), with an exponent-field histogram
-    close to that of a half-normal sample spanning the E4M3 range. No float
-    is ever encoded to fp8 here.
+  * fp8 weights are ``uint8`` OCP E4M3 codes. The host generator draws them
+    bit-field by bit-field (sign, exponent field, mantissa field), with an
+    exponent-field histogram close to that of a half-normal sample spanning
+    the E4M3 range, so no float is encoded there. The device generator for
+    full-size models (``model_weights_device``) draws float weights and
+    encodes them with torch's float8_e4m3fn cast: input synthesis only.
   * token ids are ``int32``.
 
 Seeding: every tensor block has its own ``np.random.default_rng`` keyed by
@@ -40,7 +42,7 @@ __all__ = [
     "ModelShape", "QWEN3_4B", "tiny_shape", "bf16_bits_from_f32", "draw_bf16",
     "draw_fp8_codes", "model_weights", "cascade_case", "c0_case", "c1_case",
     "join_case", "filter_case", "c2_case", "c3a_case", "c3b_case", "c4_case",
-    "bf16_to_f32",
+    "bf16_to_f32", "depth_case", "residual_std", "W_STD",
 ]
 
 
@@ -168,8 +170,24 @@ _T_ATTN_NORM, _T_MLP_NORM = 10, 11
 _T_QKV, _T_O, _T_GU, _T_D = 20, 21, 22, 23
 
 
+# Standard deviation of the decoded projection weights. The two projections
+# that write into the residual stream (attention output and MLP down) are
+# scaled by 1 / sqrt(2 * n_layers), the depth-scaled initialisation of GPT-2
+# style decoders: each layer then adds a small update to the residual stream,
+# so a deep random-init stack stays well conditioned and last-bit rounding
+# differences do not grow into percent-level differences at the last layer.
+W_STD = 0.02
+
+
+def residual_std(shape: ModelShape) -> float:
+    """Std of the residual-writing projections (O and down)."""
+    return W_STD / math.sqrt(2.0 * shape.n_layers)
+
+
 def layer_weights(shape: ModelShape, seed: int, layer: int) -> dict:
-    """One decoder layer: fp8 codes [out, in] + bf16 per-output-row scales."""
+    """One decoder layer: fp8 codes [out, in] + bf16 per-output-row scales.
+    Decoded weights have std W_STD (QKV, gate/up) or residual_std(shape)
+    (O, down)."""
     H, I = shape.hidden, shape.intermediate
     out = {}
     r = _rng(7, seed, layer, _T_ATTN_NORM)
@@ -183,7 +201,8 @@ def layer_weights(shape: ModelShape, seed: int, layer: int) -> dict:
             ("down", _T_D, (H, I))):
         r = _rng(7, seed, layer, tid)
         out["w_" + name] = draw_fp8_codes(r, (n_out, n_in))
-        out["s_" + name] = _row_scales(r, n_out)
+        std = residual_std(shape) if name in ("o", "down") else W_STD
+        out["s_" + name] = _row_scales(r, n_out, std)
     return out
 
 
@@ -208,8 +227,11 @@ def model_weights_device(shape: ModelShape, seed: int = 0, device="cuda") -> dic
     generator (for full-size models, whose host generation takes minutes).
     Same keys and formats as ``model_weights`` (bf16 as int16 bits, fp8 as
     uint8 OCP E4M3 codes); values differ. Projection weights follow the recipe
-    W ~ N(0, 0.02), per-row scale = bf16(max|W_row| / 448), codes = the E4M3
-    rounding of W / scale (clamped to +-448 first)."""
+    W ~ N(0, std) with std = W_STD, or residual_std(shape) for the O and down
+    projections; per-row scale = bf16(max|W_row| / 448); codes = E4M3 of
+    W / scale (clamped to +-448 first), encoded by torch's float8_e4m3fn cast.
+    This is input synthesis only (the library's and the oracle's codecs are
+    not involved)."""
     import torch
     g = torch.Generator(device=device)
     g.manual_seed(7_000_003 * seed + 11)
@@ -219,13 +241,13 @@ def model_weights_device(shape: ModelShape, seed: int = 0, device="cuda") -> dic
         x = torch.randn(shape_, generator=g, device=device, dtype=torch.float32) * std + mean
         return x.to(torch.bfloat16).view(torch.int16)
 
-    def fp8_rows(n_out, n_in):
+    def fp8_rows(n_out, n_in, std):
         codes = torch.empty((n_out, n_in), dtype=torch.uint8, device=device)
         scales = torch.empty(n_out, dtype=torch.int16, device=device)
         step = max(1, (1 << 26) // n_in)
         for r0 in range(0, n_out, step):
             r1 = min(n_out, r0 + step)
-            w = torch.randn((r1 - r0, n_in), generator=g, device=device, dtype=torch.float32) * 0.02
+            w = torch.randn((r1 - r0, n_in), generator=g, device=device, dtype=torch.float32) * std
             sc = (w.abs().amax(dim=1) / 448.0).to(torch.bfloat16)
             q = (w / sc.float()[:, None]).clamp_(-448.0, 448.0)
             codes[r0:r1] = q.to(torch.float8_e4m3fn).view(torch.uint8)
@@ -238,7 +260,8 @@ def model_weights_device(shape: ModelShape, seed: int = 0, device="cuda") -> dic
         lw = {"attn_norm": bf16((H,), 0.1, 1.0), "mlp_norm": bf16((H,), 0.1, 1.0)}
         for name, (n_out, n_in) in (("qkv", (shape.qkv_dim, H)), ("o", (H, shape.q_dim)),
                                      ("gate_up", (2 * I, H)), ("down", (H, I))):
-            lw["w_" + name], lw["s_" + name] = fp8_rows(n_out, n_in)
+            std = residual_std(shape) if name in ("o", "down") else W_STD
+            lw["w_" + name], lw["s_" + name] = fp8_rows(n_out, n_in, std)
         w["layers"].append(lw)
     return w
 
@@ -498,6 +521,22 @@ def c4_case(seed: int = 5, n_anchors: int = 1024, la: int = 768,
     return dict(a_len=a_len, a_off=a_off, a_tok=a_tok, pair_anchor=pair_anchor,
                 pair_row=pair_row, row_len=row_len, row_off=row_off,
                 row_tok=row_tok, true_mask=0x0F)
+
+
+def depth_case(seed: int, a_len, per_anchor: int, n_filter: int, ls_range=(2, 12),
+               filter_range=(4, 24), vocab: int = QWEN3_4B.vocab, cfg_id: int = 8) -> dict:
+    """A small join for full-depth parity: every anchor joined to
+    ``per_anchor`` suffixes of U{ls_range} tokens, plus ``n_filter`` filter
+    rows of U{filter_range} tokens, the pairs listed in a seeded random order
+    (sorting them is the plan's job)."""
+    r = _rng(cfg_id, seed, 0, 0)
+    n_anchors = len(a_len)
+    pa = np.concatenate([np.repeat(np.arange(n_anchors), per_anchor),
+                         -np.ones(n_filter, np.int64)]).astype(np.int32)
+    sl = np.concatenate([r.integers(ls_range[0], ls_range[1] + 1, size=n_anchors * per_anchor),
+                         r.integers(filter_range[0], filter_range[1] + 1, size=n_filter)])
+    perm = r.permutation(len(pa))
+    return join_case(seed, vocab, a_len, pa[perm], sl[perm].astype(np.int32), cfg_id=cfg_id)
 
 
 def shared_prefix_case(seed: int, vocab: int, a_len, families, cfg_id: int = 6,
