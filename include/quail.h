@@ -59,6 +59,10 @@ typedef int32_t quail_status;
 #define QUAIL_E_HIP          (-4)   /* HIP runtime / launch failure */
 #define QUAIL_E_UNSUPPORTED  (-5)   /* shape the kernels do not cover */
 
+/* Guard region size: every anchor slab ends with one, and the last one of
+ * the KV pool is one more (see quail_anchor_bytes and quail_ctx_check). */
+#define QUAIL_GUARD_BYTES     256
+
 #define QUAIL_DTYPE_F32       0
 #define QUAIL_DTYPE_BF16      1
 #define QUAIL_DTYPE_FP8_E4M3  2
@@ -71,8 +75,9 @@ typedef void* quail_stream;                      /* hipStream_t */
 typedef int64_t quail_anchor;
 #define QUAIL_NO_ANCHOR ((quail_anchor)-1)
 
-/* Model shape. Supported by the kernels: head_dim == 128; hidden,
- * intermediate multiples of 64; n_q_heads a multiple of n_kv_heads with
+/* Model shape. Supported by the kernels: head_dim == 128; hidden a
+ * multiple of 128 and intermediate a multiple of 64 (else
+ * QUAIL_E_UNSUPPORTED); n_q_heads a multiple of n_kv_heads with
  * group size 1, 2, 4 or 8. kv_dtype is QUAIL_DTYPE_BF16 or
  * QUAIL_DTYPE_FP8_E4M3 (anchor KV stored as E4M3 codes of k/k_scale and
  * v/v_scale, saturating, round-to-nearest-even). RoPE is rotate-half with
@@ -113,7 +118,8 @@ const char*  quail_last_error(void);
 /* ---- sizing --------------------------------------------------------------- */
 /* Pool bytes one anchor of `anchor_len` tokens occupies: layers x {K,V} x
  * kv heads x ceil(anchor_len/64)*64 tokens x head_dim x (2 B bf16 | 1 B fp8),
- * rounded up to 256 B. Slab layout [layer][K|V][kv_head][token][head_dim]. */
+ * rounded up to 256 B, plus a QUAIL_GUARD_BYTES guard region at its end.
+ * Slab layout [layer][K|V][kv_head][token][head_dim], then the guard. */
 quail_status quail_anchor_bytes(const quail_model_config* cfg, int32_t anchor_len, size_t* out);
 
 /* Workspace bytes a context needs for batches of up to `max_batch_tokens`
@@ -176,13 +182,43 @@ quail_status quail_multiplan_build(const quail_model_config* cfg, size_t pool_by
 
 /* ---- context -------------------------------------------------------------- */
 /* Borrows the weights (they must outlive the context), the KV pool (dev,
- * pool_bytes, 256-B aligned) and the workspace (dev, at least
- * quail_workspace_bytes(cfg, max_batch_tokens)). Touches no GPU. */
+ * pool_bytes, 256-B aligned; when it holds at least 2 * QUAIL_GUARD_BYTES,
+ * its last QUAIL_GUARD_BYTES are a guard region and slabs are carved from
+ * the rest) and the workspace (dev, at least quail_workspace_bytes(cfg,
+ * max_batch_tokens)). Touches no GPU. */
 quail_status quail_ctx_create(const quail_model_config* cfg, const quail_weights* w,
                               void* kv_pool, size_t pool_bytes,
                               void* workspace, size_t ws_bytes, int32_t max_batch_tokens,
                               quail_ctx** out);
 quail_status quail_ctx_destroy(quail_ctx* ctx);
+
+/* Debug counters of a context (its guard bytes and token-range check). A
+ * slab's guard region is written when the slab is carved and checked when it
+ * is evicted (before its memory is written again); this call also checks the
+ * guards of every live slab and the pool's tail guard now. guard_errors = the
+ * number of guard regions found overwritten since the context was created;
+ * bad_tokens = the number of token ids outside [0, vocab) the embedding has
+ * met (each such row embeds token 0 instead of reading out of range).
+ * Enqueues the checks on `stream` and waits for it. Either pointer may be
+ * NULL. Token ids outside [0, vocab) are a caller error: results of a call
+ * that met one are undefined, but the GPU never reads outside the table. */
+quail_status quail_ctx_check(quail_ctx* ctx, quail_stream stream, int64_t* guard_errors,
+                             int64_t* bad_tokens);
+
+/* Per-launch timing of a context's kernels, for measurement: with profiling
+ * on, every launch of the model path is bracketed by two HIP events on its
+ * stream. Kinds: 0 QKV projection (+ RoPE, KV writer), 1 O projection
+ * (+ residual), 2 gate/up projection (+ SwiGLU), 3 down projection
+ * (+ residual), 4 cascade attention, 5 RMSNorm, 6 other (embedding, head,
+ * row copies). quail_ctx_profile(enable) switches it and discards what was
+ * recorded. quail_ctx_profile_read waits for the recorded launches and
+ * returns per kind (host arrays of 7, each nullable): the launch count, the
+ * summed launch durations in ms and the summed algorithmic FLOP (GEMMs
+ * 2*M*N*K with N the weight rows; attention 4 * n_q_heads * head_dim per
+ * visible (query, key) pair), then discards the records. */
+#define QUAIL_PROF_KINDS 7
+quail_status quail_ctx_profile(quail_ctx* ctx, int32_t enable);
+quail_status quail_ctx_profile_read(quail_ctx* ctx, int64_t* launches, double* ms, double* flop);
 
 /* ---- KV-aware join-order search, speed-of-light cost model (host only) ---- */
 /* [pt] "Como funciona": the join-order search keeps several candidate plans,
@@ -425,8 +461,11 @@ quail_status quail_multijoin_run(quail_ctx* ctx, int32_t n_anchors, const int32_
                                  uint8_t* decision, quail_stream stream);
 
 /* Residency counters: bytes resident now and at peak, anchors prefilled,
- * anchors evicted, regret tokens (anchor tokens prefilled again after an
- * eviction). Any pointer may be NULL. */
+ * anchors evicted, regret tokens -- anchor tokens prefilled again after an
+ * eviction, the "KV regret" [it] measures for the vLLM baseline on its
+ * BIO-4 query (paragraph on the optimistic roofline and KV regret); with the
+ * whole plan known it is 0 ([pt] "Como funciona", query-aware KV cache
+ * bullet). Any pointer may be NULL. */
 quail_status quail_pool_stats(const quail_ctx* ctx, size_t* resident, size_t* peak,
                               int64_t* prefills, int64_t* evictions, int64_t* regret_tokens);
 

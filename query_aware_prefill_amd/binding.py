@@ -16,6 +16,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libquail.s
 _lib = None
 
 OK, E_INVAL, E_NOMEM, E_STALE, E_HIP, E_UNSUPPORTED = 0, -1, -2, -3, -4, -5
+GUARD_BYTES = 256          # QUAIL_GUARD_BYTES
+PROF_KINDS = ("qkv", "o", "gate_up", "down", "attn", "norm", "other")
 DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
 NO_ANCHOR = -1
 
@@ -98,6 +100,9 @@ _SIGS = {
     "quail_multijoin_run": ([_vp, C.c_int32, _vp, _i32p, C.c_int32, _i32p, _i32p, _vp, _i32p, C.c_uint8,
                              _vp, _vp, _vp, _vp], C.c_int32),
     "quail_pool_stats": ([_vp, _szp, _szp, _i64p, _i64p, _i64p], C.c_int32),
+    "quail_ctx_check": ([_vp, _vp, _i64p, _i64p], C.c_int32),
+    "quail_ctx_profile": ([_vp, C.c_int32], C.c_int32),
+    "quail_ctx_profile_read": ([_vp, _i64p, _f64p, _f64p], C.c_int32),
     "quail_cascade_workspace_bytes": ([C.c_int32, _i32p, C.c_int32, _i32p, _szp], C.c_int32),
     "quail_cascade_attn": ([C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_float, C.c_int32, _vp, _vp,
                             _i32p, C.c_int32, _i32p, _vp, _vp, _vp, _i32p, _vp, _vp, _vp, C.c_size_t,
@@ -386,6 +391,27 @@ def quail_pool_stats(ctx: Context) -> dict:
                                    C.byref(rg)))
     return dict(resident=r.value, peak=p.value, prefills=pf.value, evictions=ev.value,
                 regret_tokens=rg.value)
+
+
+def quail_ctx_check(ctx: Context, stream=None) -> dict:
+    """Guard-region and token-range counters (waits for the stream)."""
+    g, t = C.c_int64(), C.c_int64()
+    _check(load().quail_ctx_check(ctx.handle, stream_handle(stream), C.byref(g), C.byref(t)))
+    return dict(guard_errors=g.value, bad_tokens=t.value)
+
+
+def quail_ctx_profile(ctx: Context, enable: bool) -> None:
+    _check(load().quail_ctx_profile(ctx.handle, 1 if enable else 0))
+
+
+def quail_ctx_profile_read(ctx: Context) -> dict:
+    """Per kind (PROF_KINDS): launches, summed launch ms and algorithmic FLOP."""
+    n = len(PROF_KINDS)
+    la = (C.c_int64 * n)()
+    ms = (C.c_double * n)()
+    fl = (C.c_double * n)()
+    _check(load().quail_ctx_profile_read(ctx.handle, la, ms, fl))
+    return {k: dict(launches=la[i], ms=ms[i], flop=fl[i]) for i, k in enumerate(PROF_KINDS)}
 
 
 def quail_cascade_workspace_bytes(a_off, s_off) -> int:

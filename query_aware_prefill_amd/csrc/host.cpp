@@ -154,8 +154,11 @@ quail_status check_cfg(const quail_model_config* c) {
     return fail(QUAIL_E_INVAL, "rms_eps >= 0 and rope_theta > 0 required");
   if (c->head_dim != kHeadDim)
     return fail(QUAIL_E_UNSUPPORTED, "head_dim %d (the kernels take 128)", c->head_dim);
-  if (c->hidden % 64 || c->intermediate % 64)
-    return fail(QUAIL_E_UNSUPPORTED, "hidden and intermediate must be multiples of 64");
+  // hidden is the column count of the O and down projections, whose residual
+  // epilogue tiles are 128 columns wide; intermediate is cut into 64-column
+  // SwiGLU tiles and 64-deep k-steps of the down projection
+  if (c->hidden % 128 || c->intermediate % 64)
+    return fail(QUAIL_E_UNSUPPORTED, "hidden must be a multiple of 128 and intermediate of 64");
   if (c->n_q_heads % c->n_kv_heads || !valid_group(c->n_q_heads / c->n_kv_heads))
     return fail(QUAIL_E_UNSUPPORTED, "GQA group size must be 1, 2, 4 or 8");
   if (c->n_kv_heads > kMaxKVHeads)
@@ -173,16 +176,23 @@ size_t kv_elem_bytes(const quail_model_config& c) {
 
 int32_t pad_len(int32_t la) { return (la + kKeyTile - 1) / kKeyTile * kKeyTile; }
 
+// Every slab ends with a guard region (a fixed pattern written when the slab
+// is carved and checked when it is evicted); the pool's last guard-sized
+// block is one more.
+constexpr size_t kGuard = QUAIL_GUARD_BYTES;
+// guard regions checked or written per launch (device offset table capacity)
+constexpr int32_t kGuardCap = 4096;
+
 size_t slab_bytes(const quail_model_config& c, int32_t la) {
   return align_up((size_t)c.n_layers * 2 * c.n_kv_heads * (size_t)pad_len(la) * c.head_dim *
-                  kv_elem_bytes(c));
+                  kv_elem_bytes(c)) + kGuard;
 }
 
 int32_t max_pos(const quail_model_config& c) { return c.max_anchor_len + c.max_suffix_len; }
 
 // Workspace carve for a context.
 struct WsLayout {
-  size_t rope, h, u, q, k, v, o, m, hlast, meta, total;
+  size_t rope, h, u, q, k, v, o, m, hlast, meta, status, guard, total;
   size_t meta_cap;
 };
 
@@ -216,6 +226,8 @@ WsLayout ws_layout(const quail_model_config& c, int32_t T) {
   w.hlast = take(Tt * c.hidden * 2);
   w.meta_cap = meta_capacity(T, c.n_layers);
   w.meta = take(w.meta_cap);
+  w.status = take(kAlign);                        // debug counters (uint32): guard errors, bad tokens
+  w.guard = take((size_t)kGuardCap * sizeof(int64_t));
   w.total = off;
   return w;
 }
@@ -513,7 +525,17 @@ struct quail_ctx {
   size_t ws_bytes = 0;
   int32_t T = 0;                      // max batch tokens
   WsLayout L{};
-  bool rope_ready = false;
+  bool ready = false;                 // RoPE table, debug counters and the pool's tail guard are set
+  bool dry = false;                   // placement dry run: bookkeeping only, nothing enqueued
+  size_t tail_guard = SIZE_MAX;       // pool offset of the tail guard (none if the pool is too small)
+  std::vector<int64_t> pending_checks;   // guard regions of evicted slabs, checked before reuse
+
+  // per-launch timing (quail_ctx_profile): an event before and after each launch
+  struct ProfRec { int32_t kind; hipEvent_t e0, e1; double flop; };
+  bool prof_on = false;
+  std::vector<ProfRec> prof;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_next = 0;
 
   // residency
   struct Slot {
@@ -577,6 +599,7 @@ struct quail_ctx {
   }
   void evict(int32_t slot) {
     Slot& s = slots[slot];
+    pending_checks.push_back((int64_t)(s.off + s.bytes - kGuard));
     release(s.off, s.bytes);
     resident -= s.bytes;
     s.live = false;
@@ -599,8 +622,10 @@ namespace {
 template <typename T>
 T* ws_ptr(quail_ctx* c, size_t off) { return reinterpret_cast<T*>(c->ws + off); }
 
-quail_status ensure_rope(quail_ctx* c, hipStream_t s) {
-  if (c->rope_ready) return QUAIL_OK;
+// First enqueueing call of a context: the RoPE table, zeroed debug counters
+// and the pool's tail guard.
+quail_status ensure_ready(quail_ctx* c, hipStream_t s) {
+  if (c->ready || c->dry) return QUAIL_OK;
   const int P = max_pos(c->cfg);
   const int half = c->cfg.head_dim / 2;
   std::vector<float2> tab((size_t)P * half);
@@ -611,9 +636,68 @@ quail_status ensure_rope(quail_ctx* c, hipStream_t s) {
       tab[(size_t)p * half + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
     }
   HIP_TRY(stager().copy(c->ws + c->L.rope, tab.data(), tab.size() * sizeof(float2), s));
-  c->rope_ready = true;
+  HIP_TRY(launch_zero_words(ws_ptr<uint32_t>(c, c->L.status), 2, s));
+  if (c->tail_guard != SIZE_MAX) {
+    const int64_t off = (int64_t)c->tail_guard;
+    HIP_TRY(stager().copy(c->ws + c->L.guard, &off, sizeof off, s));
+    HIP_TRY(launch_guard(c->pool, ws_ptr<const int64_t>(c, c->L.guard), 1, 1, nullptr, s));
+  }
+  c->ready = true;
   return QUAIL_OK;
 }
+
+// Writes (mode 1) or checks (mode 0) the guard regions at pool offsets offs.
+quail_status guard_op(quail_ctx* c, const std::vector<int64_t>& offs, int32_t mode, hipStream_t s) {
+  if (c->dry || offs.empty()) return QUAIL_OK;
+  if (quail_status st = ensure_ready(c, s)) return st;
+  for (size_t i = 0; i < offs.size(); i += kGuardCap) {
+    const int32_t n = (int32_t)std::min<size_t>(kGuardCap, offs.size() - i);
+    HIP_TRY(stager().copy(c->ws + c->L.guard, offs.data() + i, n * sizeof(int64_t), s));
+    HIP_TRY(launch_guard(c->pool, ws_ptr<const int64_t>(c, c->L.guard), n, mode,
+                         ws_ptr<uint32_t>(c, c->L.status), s));
+  }
+  return QUAIL_OK;
+}
+
+// Checks the guards of slabs evicted since the last flush. Called before any
+// work that may reuse their memory is enqueued.
+quail_status flush_guard_checks(quail_ctx* c, hipStream_t s) {
+  if (c->dry || c->pending_checks.empty()) return QUAIL_OK;
+  if (quail_status st = guard_op(c, c->pending_checks, 0, s)) return st;
+  c->pending_checks.clear();
+  return QUAIL_OK;
+}
+
+// Per-launch timing marks (no-ops unless profiling is on).
+enum ProfKind : int32_t { PK_QKV = 0, PK_O = 1, PK_GATE_UP = 2, PK_DOWN = 3, PK_ATTN = 4, PK_NORM = 5,
+                          PK_OTHER = 6, PK_COUNT = 7 };
+
+hipError_t prof_mark(quail_ctx* c, hipStream_t s, hipEvent_t* ev) {
+  *ev = nullptr;
+  if (!c->prof_on) return hipSuccess;
+  if (c->ev_next == c->ev_pool.size()) {
+    hipEvent_t e;
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) return r;
+    c->ev_pool.push_back(e);
+  }
+  *ev = c->ev_pool[c->ev_next++];
+  return hipEventRecord(*ev, s);
+}
+
+void prof_add(quail_ctx* c, int32_t kind, hipEvent_t e0, hipEvent_t e1, double flop) {
+  if (c->prof_on && e0 && e1) c->prof.push_back({kind, e0, e1, flop});
+}
+
+// Launch `expr` between two timing marks of kind `kind` (algorithmic FLOP `flop`).
+#define TIMED(kind, flop, expr)                                   \
+  do {                                                            \
+    hipEvent_t e0_, e1_;                                          \
+    HIP_TRY(prof_mark(c, s, &e0_));                               \
+    HIP_TRY(expr);                                                \
+    HIP_TRY(prof_mark(c, s, &e1_));                               \
+    prof_add(c, kind, e0_, e1_, (double)(flop));                  \
+  } while (0)
 
 // One batch of token rows through the decoder stack.
 struct Batch {
@@ -661,6 +745,21 @@ quail_status run_batch(quail_ctx* c, const Batch& b, const int32_t* tokens, uint
   const size_t o_src = bl.add(srcs_all);
   if (bl.size() > c->L.meta_cap)
     return fail(QUAIL_E_NOMEM, "batch metadata (%zu B) exceeds its workspace region", bl.size());
+  if (c->dry) return QUAIL_OK;
+  // algorithmic attention FLOP of the batch (per layer): 4 * Hq * d per
+  // (query row, visible key) -- every key of the cross sources, the causal
+  // self keys from the segment start to the row
+  double attn_flop = 0.0;
+  if (c->prof_on) {
+    double keys = 0.0;
+    for (const AttnTile& tl : b.tiles)
+      for (int32_t r = 0; r < tl.nq; ++r) {
+        if (tl.cross >= 0) keys += b.srcs[tl.cross].len;
+        if (tl.cross2 >= 0) keys += b.srcs[tl.cross2].len;
+        if (tl.self >= 0) keys += tl.self_qbase + r - std::max(tl.self_k0, b.seg_lo[tl.q0 + r]) + 1;
+      }
+    attn_flop = 4.0 * Hq * kHeadDim * keys;
+  }
   uint8_t* md = c->ws + c->L.meta;
   HIP_TRY(stager().copy(md, bl.data(), bl.size(), s));
 
@@ -682,13 +781,14 @@ quail_status run_batch(quail_ctx* c, const Batch& b, const int32_t* tokens, uint
   uint16_t* mbuf = ws_ptr<uint16_t>(c, c->L.m);
   const float2* rope = ws_ptr<const float2>(c, c->L.rope);
 
-  HIP_TRY(launch_embed(tokens, d_tok, c->w.embed, hbuf, n, H, s));
+  uint32_t* status = ws_ptr<uint32_t>(c, c->L.status);
+  TIMED(PK_OTHER, 0, launch_embed(tokens, d_tok, c->w.embed, hbuf, n, H, cf.vocab, status + 1, s));
   for (int l = 0; l < cf.n_layers; ++l) {
     const quail_layer_weights& lw = c->layers[l];
     NormParams np{};
     np.x = hbuf; np.ldx = H; np.gamma = lw.attn_norm; np.y = ubuf; np.ldy = H;
     np.rows = n; np.H = H; np.eps = cf.rms_eps;
-    HIP_TRY(launch_rmsnorm(np, s));
+    TIMED(PK_NORM, 0, launch_rmsnorm(np, s));
 
     GemmParams gp{};
     gp.A = ubuf; gp.lda = H; gp.B = lw.w_qkv; gp.scale = lw.s_qkv;
@@ -702,7 +802,7 @@ quail_status run_batch(quail_ctx* c, const Batch& b, const int32_t* tokens, uint
     } else {
       gp.kv_mode = 0; gp.k_out = kbuf; gp.v_out = vbuf;
     }
-    HIP_TRY(launch_gemm(gp, EPI_QKV, s));
+    TIMED(PK_QKV, 2.0 * n * gp.N * gp.K, launch_gemm(gp, EPI_QKV, s));
     if (b.anchor_mode && l == cf.n_layers - 1) break;   // last layer: K/V is all an anchor needs
 
     AttnParams ap{};
@@ -717,26 +817,27 @@ quail_status run_batch(quail_ctx* c, const Batch& b, const int32_t* tokens, uint
     // anchor batches attend over their own slab (self source); join batches
     // read the anchor slab as the cross source and bf16 suffix K/V as self
     const bool slab_fp8 = cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3;
-    HIP_TRY(launch_attn_bf16(ap, G, (!b.anchor_mode || b.has_parent) && slab_fp8, b.anchor_mode && slab_fp8,
-                             b.packed, s));
+    TIMED(PK_ATTN, attn_flop,
+          launch_attn_bf16(ap, G, (!b.anchor_mode || b.has_parent) && slab_fp8, b.anchor_mode && slab_fp8,
+                           b.packed, s));
 
     GemmParams go{};
     go.A = obuf; go.lda = (int64_t)Hq * kHeadDim; go.B = lw.w_o; go.scale = lw.s_o;
     go.M = n; go.N = H; go.K = Hq * kHeadDim; go.Y = hbuf; go.ldy = H;
-    HIP_TRY(launch_gemm(go, EPI_RESID, s));
+    TIMED(PK_O, 2.0 * n * go.N * go.K, launch_gemm(go, EPI_RESID, s));
 
     np.gamma = lw.mlp_norm;
-    HIP_TRY(launch_rmsnorm(np, s));
+    TIMED(PK_NORM, 0, launch_rmsnorm(np, s));
 
     GemmParams gg{};
     gg.A = ubuf; gg.lda = H; gg.B = lw.w_gate_up; gg.scale = lw.s_gate_up;
     gg.M = n; gg.N = I; gg.K = H; gg.Y = mbuf; gg.ldy = I; gg.inter = I;
-    HIP_TRY(launch_gemm(gg, EPI_SWIGLU, s));
+    TIMED(PK_GATE_UP, 2.0 * n * 2.0 * gg.N * gg.K, launch_gemm(gg, EPI_SWIGLU, s));
 
     GemmParams gd{};
     gd.A = mbuf; gd.lda = I; gd.B = lw.w_down; gd.scale = lw.s_down;
     gd.M = n; gd.N = H; gd.K = I; gd.Y = hbuf; gd.ldy = H;
-    HIP_TRY(launch_gemm(gd, EPI_RESID, s));
+    TIMED(PK_DOWN, 2.0 * n * gd.N * gd.K, launch_gemm(gd, EPI_RESID, s));
   }
   if (!b.anchor_mode) {
     if (h_last && !b.last_row.empty()) {
@@ -875,8 +976,21 @@ quail_status anchor_core(quail_ctx* c, int32_t n, const int32_t* tokens, const i
     }
   }
   c->peak = std::max(c->peak, c->resident);
+  if (c->dry) return QUAIL_OK;
 
-  if (quail_status st = ensure_rope(c, s)) return st;
+  if (quail_status st = ensure_ready(c, s)) return st;
+  // slabs evicted earlier are checked before their memory is written again;
+  // then every new slab's guard is set
+  if (quail_status st = flush_guard_checks(c, s)) return st;
+  {
+    std::vector<int64_t> guards;
+    for (int32_t a = 0; a < n; ++a)
+      if (slot_of[a] >= 0) {
+        const quail_ctx::Slot& sl = c->slots[slot_of[a]];
+        guards.push_back((int64_t)(sl.off + sl.bytes - kGuard));
+      }
+    if (quail_status st = guard_op(c, guards, 1, s)) return st;
+  }
   const quail_model_config& cf = c->cfg;
   const int G = cf.n_q_heads / cf.n_kv_heads;
   const size_t esz = kv_elem_bytes(cf);
@@ -1250,13 +1364,69 @@ quail_status quail_ctx_create(const quail_model_config* cfg, const quail_weights
   c->ws_bytes = ws_bytes;
   c->T = max_batch_tokens;
   c->L = L;
-  if (c->pool_bytes) c->free_list.push_back({0, c->pool_bytes});
+  // the pool's last guard-sized block is a guard region of its own
+  if (c->pool_bytes >= 2 * kGuard) {
+    c->tail_guard = c->pool_bytes - kGuard;
+    c->free_list.push_back({0, c->pool_bytes - kGuard});
+  } else if (c->pool_bytes) {
+    c->free_list.push_back({0, c->pool_bytes});
+  }
   *out = c;
   return QUAIL_OK;
 }
 
 quail_status quail_ctx_destroy(quail_ctx* ctx) {
+  if (ctx)
+    for (hipEvent_t e : ctx->ev_pool) (void)hipEventDestroy(e);   // teardown: nothing to report to
   delete ctx;
+  return QUAIL_OK;
+}
+
+quail_status quail_ctx_check(quail_ctx* c, quail_stream stream, int64_t* guard_errors, int64_t* bad_tokens) {
+  if (!c) return fail(QUAIL_E_INVAL, "ctx is NULL");
+  if (guard_errors) *guard_errors = 0;
+  if (bad_tokens) *bad_tokens = 0;
+  if (!c->ready) return QUAIL_OK;                  // nothing has run on this context yet
+  hipStream_t s = as_stream(stream);
+  if (quail_status st = flush_guard_checks(c, s)) return st;
+  std::vector<int64_t> live;
+  for (const quail_ctx::Slot& sl : c->slots)
+    if (sl.live) live.push_back((int64_t)(sl.off + sl.bytes - kGuard));
+  if (c->tail_guard != SIZE_MAX) live.push_back((int64_t)c->tail_guard);
+  if (quail_status st = guard_op(c, live, 0, s)) return st;
+  uint32_t cnt[2] = {0, 0};
+  HIP_TRY(hipMemcpyAsync(cnt, c->ws + c->L.status, sizeof cnt, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  if (guard_errors) *guard_errors = cnt[0];
+  if (bad_tokens) *bad_tokens = cnt[1];
+  return QUAIL_OK;
+}
+
+quail_status quail_ctx_profile(quail_ctx* c, int32_t enable) {
+  if (!c) return fail(QUAIL_E_INVAL, "ctx is NULL");
+  c->prof_on = enable != 0;
+  c->prof.clear();
+  c->ev_next = 0;
+  return QUAIL_OK;
+}
+
+quail_status quail_ctx_profile_read(quail_ctx* c, int64_t* launches, double* ms, double* flop) {
+  if (!c) return fail(QUAIL_E_INVAL, "ctx is NULL");
+  for (int k = 0; k < PK_COUNT; ++k) {
+    if (launches) launches[k] = 0;
+    if (ms) ms[k] = 0.0;
+    if (flop) flop[k] = 0.0;
+  }
+  if (!c->prof.empty()) HIP_TRY(hipEventSynchronize(c->prof.back().e1));
+  for (const quail_ctx::ProfRec& r : c->prof) {
+    float t = 0.0f;
+    HIP_TRY(hipEventElapsedTime(&t, r.e0, r.e1));
+    if (launches) launches[r.kind] += 1;
+    if (ms) ms[r.kind] += t;
+    if (flop) flop[r.kind] += r.flop;
+  }
+  c->prof.clear();
+  c->ev_next = 0;
   return QUAIL_OK;
 }
 
@@ -1382,7 +1552,8 @@ quail_status join_core(quail_ctx* c, int32_t n, const quail_anchor* ha, const in
     if (sl->pos0 + sl->len + lens[i] > max_pos(cf))
       return fail(QUAIL_E_INVAL, "pair %d: anchor + suffix exceeds the position range", i);
   }
-  if (quail_status st = ensure_rope(c, s)) return st;
+  if (quail_status st = ensure_ready(c, s)) return st;
+  if (quail_status st = flush_guard_checks(c, s)) return st;
   std::vector<int32_t> order(n);
   std::iota(order.begin(), order.end(), 0);
   std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
@@ -1391,7 +1562,7 @@ quail_status join_core(quail_ctx* c, int32_t n, const quail_anchor* ha, const in
   });
   const int G = cf.n_q_heads / cf.n_kv_heads;
   const bool slab_fp8 = cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3;
-  int32_t p0 = 0;
+  int32_t p0 = c->dry ? n : 0;      // a dry run only spends uses
   while (p0 < n) {
     Batch b;
     b.anchor_mode = false;
@@ -1483,7 +1654,7 @@ quail_status join_core(quail_ctx* c, int32_t n, const quail_anchor* ha, const in
     sl.uses -= kv.second;
     if (sl.uses == 0) c->evict(kv.first);
   }
-  return QUAIL_OK;
+  return flush_guard_checks(c, s);
 }
 
 }  // namespace
@@ -1540,6 +1711,7 @@ static quail_status run_step_with_head(quail_ctx* c, int32_t np, const quail_anc
   std::vector<int32_t> dst(np);
   std::iota(dst.begin(), dst.end(), 0);
   if (quail_status r = join_core(c, np, ha, s_tokens, starts, lens, hl, dst.data(), nullptr, s)) return r;
+  if (c->dry) return QUAIL_OK;
   Blob& bl = c->blob;
   bl.clear();
   bl.add(std::vector<int32_t>(outmap, outmap + np));
@@ -1550,8 +1722,51 @@ static quail_status run_step_with_head(quail_ctx* c, int32_t np, const quail_anc
   p.out_map = reinterpret_cast<const int32_t*>(md);
   p.logits = logits; p.token = token; p.decision = decision;
   p.rows = np; p.H = c->cfg.hidden; p.eps = c->cfg.rms_eps; p.true_mask = true_mask;
-  HIP_TRY(launch_head8(p, s));
+  TIMED(PK_OTHER, 0, launch_head8(p, s));
   return QUAIL_OK;
+}
+
+// Residency state of a context, saved around a placement dry run.
+struct ResidencySnapshot {
+  std::vector<quail_ctx::Slot> slots;
+  std::vector<int32_t> free_slots;
+  std::vector<std::pair<size_t, size_t>> free_list;
+  size_t resident, peak;
+  int64_t prefills, evictions, regret, run_serial;
+  std::unordered_set<int64_t> seen_ids;
+  std::vector<int64_t> pending_checks;
+  explicit ResidencySnapshot(const quail_ctx* c)
+      : slots(c->slots), free_slots(c->free_slots), free_list(c->free_list), resident(c->resident),
+        peak(c->peak), prefills(c->prefills), evictions(c->evictions), regret(c->regret),
+        run_serial(c->run_serial), seen_ids(c->seen_ids), pending_checks(c->pending_checks) {}
+  void restore(quail_ctx* c) const {
+    c->slots = slots; c->free_slots = free_slots; c->free_list = free_list; c->resident = resident;
+    c->peak = peak; c->prefills = prefills; c->evictions = evictions; c->regret = regret;
+    c->run_serial = run_serial; c->seen_ids = seen_ids; c->pending_checks = pending_checks;
+  }
+};
+
+// Runs `schedule(budget)` as a dry run first: slabs are carved first-fit from
+// a free list that can fragment, so a plan that fits the pool by its byte
+// total may still find no block for a slab. The dry run replays the whole
+// schedule's allocations and evictions with nothing enqueued; on E_NOMEM the
+// plan is rebuilt against a smaller budget (a step then holds fewer anchors,
+// so fewer slabs are live at once). The real run follows only once a dry run
+// fits, so a call either enqueues its whole schedule or nothing.
+static quail_status run_placed(quail_ctx* c, size_t budget,
+                               const std::function<quail_status(size_t, bool)>& schedule) {
+  for (int attempt = 0;; ++attempt) {
+    ResidencySnapshot snap(c);
+    c->dry = true;
+    const std::string err0 = g_err;
+    quail_status st = schedule(budget, true);
+    c->dry = false;
+    snap.restore(c);
+    if (st == QUAIL_OK) return schedule(budget, false);
+    if (st != QUAIL_E_NOMEM || attempt == 8 || budget < 2) return st;
+    g_err = err0;
+    budget = budget / 4 * 3;
+  }
 }
 
 // quail_join_run, and with s_tokens_host / min_shared > 0 the same plan with
@@ -1695,13 +1910,15 @@ static quail_status join_run_core(quail_ctx* c, int32_t n_anchors, const int32_t
   // one step's largest node subtree, so that it fits beside the step's
   // anchors; the reserve starts at the slab of the longest possible node and
   // grows (re-planning) until it covers the subtrees the plan's steps form.
+  auto schedule = [&](size_t budget, bool dry) -> quail_status {
+  (void)dry;
   size_t reserve = min_shared > 0 ? slab_bytes(c->cfg, *std::max_element(plen.begin(), plen.end())) : 0;
   for (int32_t it = 0;; ++it) {
-    if (min_shared > 0 && free_bytes <= reserve)
+    if (min_shared > 0 && budget <= reserve)
       return fail(QUAIL_E_NOMEM, "KV pool (largest free block %zu B) leaves no room for prefix nodes (%zu B)",
-                  free_bytes, reserve);
+                  budget, reserve);
     plan = Plan{};
-    if (quail_status st = build_plan(slab, n_pairs, pair_anchor, step_len.data(), free_bytes - reserve, c->T, plan))
+    if (quail_status st = build_plan(slab, n_pairs, pair_anchor, step_len.data(), budget - reserve, c->T, plan))
       return st;
     if (min_shared <= 0) {
       step_nodes.assign(plan.bounds.size() - 1, {});
@@ -1864,6 +2081,8 @@ static quail_status join_run_core(quail_ctx* c, int32_t n_anchors, const int32_t
     }
   }
   return QUAIL_OK;
+  };
+  return run_placed(c, free_bytes, schedule);
 }
 
 quail_status quail_join_run(quail_ctx* c, int32_t n_anchors, const int32_t* a_tokens,
@@ -1913,8 +2132,10 @@ quail_status quail_multijoin_run(quail_ctx* c, int32_t n_anchors, const int32_t*
   // the plan is built against the largest free block of the pool now
   size_t free_bytes = 0;
   for (auto& f : c->free_list) free_bytes = std::max(free_bytes, f.second);
+  auto schedule = [&](size_t budget, bool dry) -> quail_status {
+  (void)dry;
   MultiPlan mp;
-  if (quail_status st = build_multiplan(slab, alen, n_joins, join_offsets, pair_anchor, plen.data(), free_bytes,
+  if (quail_status st = build_multiplan(slab, alen, n_joins, join_offsets, pair_anchor, plen.data(), budget,
                                         c->T, mp))
     return st;
   // Each prefill declares the pairs the anchor serves until its next prefill
@@ -1974,6 +2195,8 @@ quail_status quail_multijoin_run(quail_ctx* c, int32_t n_anchors, const int32_t*
       return r;
   }
   return QUAIL_OK;
+  };
+  return run_placed(c, free_bytes, schedule);
 }
 
 // ---- cascade attention on given Q/K/V ---------------------------------------

@@ -7,24 +7,71 @@
 
 namespace quail {
 
-// h[r] = embed[tokens[tok_map ? tok_map[r] : r]]
+// h[r] = embed[tokens[tok_map ? tok_map[r] : r]]. A token id outside
+// [0, vocab) is counted in *bad (when given) and embeds row 0 instead, so a
+// bad id never becomes an out-of-range read.
 __global__ void __launch_bounds__(256) embed_kernel(const int32_t* tokens, const int32_t* tok_map,
                                                     const uint16_t* embed, uint16_t* h,
-                                                    int32_t rows, int32_t H) {
+                                                    int32_t rows, int32_t H, int32_t vocab,
+                                                    uint32_t* bad) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= rows) return;
   const int src = tok_map ? tok_map[r] : r;
-  const int64_t tok = tokens[src];
+  int64_t tok = tokens[src];
+  if (tok < 0 || tok >= vocab) {
+    if (lane == 0 && bad) atomicAdd(bad, 1u);
+    tok = 0;
+  }
   const uint4* s = reinterpret_cast<const uint4*>(embed + tok * H);
   uint4* d = reinterpret_cast<uint4*>(h + (int64_t)r * H);
   for (int c = lane; c < H / 8; c += 64) d[c] = s[c];
 }
 
 hipError_t launch_embed(const int32_t* tokens, const int32_t* tok_map, const uint16_t* embed,
-                        uint16_t* h, int32_t rows, int32_t H, hipStream_t s) {
+                        uint16_t* h, int32_t rows, int32_t H, int32_t vocab, uint32_t* bad,
+                        hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  embed_kernel<<<dim3((rows + 3) / 4), dim3(256), 0, s>>>(tokens, tok_map, embed, h, rows, H);
+  embed_kernel<<<dim3((rows + 3) / 4), dim3(256), 0, s>>>(tokens, tok_map, embed, h, rows, H, vocab, bad);
+  return hipGetLastError();
+}
+
+// Guard regions of the KV pool: 256 bytes after every slab (and at the
+// pool's end) hold a fixed pattern. mode 1 writes the pattern into regions
+// base + offs[i]; mode 0 checks it and counts every region that differs in
+// *bad. One wave per region, 4 bytes per lane.
+constexpr uint32_t kGuardWord = 0xA5C3965Au;
+
+__global__ void __launch_bounds__(256) guard_kernel(uint8_t* base, const int64_t* offs, int32_t n,
+                                                    int32_t mode, uint32_t* bad) {
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= n) return;
+  uint32_t* g = reinterpret_cast<uint32_t*>(base + offs[i]) + lane;
+  if (mode == 1) {
+    *g = kGuardWord ^ (uint32_t)lane;
+  } else {
+    const bool ok = *g == (kGuardWord ^ (uint32_t)lane);
+    if (__ballot(!ok) != 0 && lane == 0) atomicAdd(bad, 1u);
+  }
+}
+
+hipError_t launch_guard(uint8_t* base, const int64_t* offs, int32_t n, int32_t mode, uint32_t* bad,
+                        hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  guard_kernel<<<dim3((n + 3) / 4), dim3(256), 0, s>>>(base, offs, n, mode, bad);
+  return hipGetLastError();
+}
+
+// n 32-bit words = 0 (a kernel rather than a memset node, so that it also
+// behaves under graph capture)
+__global__ void __launch_bounds__(64) zero_words_kernel(uint32_t* p, int32_t n) {
+  for (int i = threadIdx.x; i < n; i += 64) p[i] = 0u;
+}
+
+hipError_t launch_zero_words(uint32_t* p, int32_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  zero_words_kernel<<<dim3(1), dim3(64), 0, s>>>(p, n);
   return hipGetLastError();
 }
 

@@ -131,8 +131,15 @@ int attn_tile_tokens(int group, bool packed);
 hipError_t launch_attn_f32(const AttnF32Params& p, hipStream_t s);
 hipError_t launch_gemm(const GemmParams& p, GemmEpi epi, hipStream_t s);
 hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s);
+// token ids outside [0, vocab) embed row 0 and are counted in *bad (nullable)
 hipError_t launch_embed(const int32_t* tokens, const int32_t* tok_map, const uint16_t* embed,
-                        uint16_t* h, int32_t rows, int32_t H, hipStream_t s);
+                        uint16_t* h, int32_t rows, int32_t H, int32_t vocab, uint32_t* bad,
+                        hipStream_t s);
+// 256-byte guard regions at base + offs[i] (offs on the device): mode 1
+// writes the guard pattern, mode 0 counts regions that differ from it in *bad
+hipError_t launch_guard(uint8_t* base, const int64_t* offs, int32_t n, int32_t mode, uint32_t* bad,
+                        hipStream_t s);
+hipError_t launch_zero_words(uint32_t* p, int32_t n, hipStream_t s);
 // dst[dst_idx ? dst_idx[r] : r] = src[src_idx ? src_idx[r] : r], bf16 rows of H
 hipError_t launch_copy_rows(const uint16_t* src, int64_t lds, const int32_t* src_idx,
                             uint16_t* dst, int64_t ldd, const int32_t* dst_idx, int32_t rows,

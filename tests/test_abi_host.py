@@ -39,13 +39,22 @@ def _cfg(layers=36, fp8=False, **kw):
     return B.ModelConfig(**d)
 
 
+# every slab the library carves ends with a guard region (quail.h)
+G = B.GUARD_BYTES
+
+
+def _slab(la, layers, kv_heads, d, esz):
+    """Pool bytes of a slab: the oracle's KV layout plus the library's guard."""
+    return OP.slab_bytes(la, layers, kv_heads, d, esz) + G
+
+
 @pytest.mark.parametrize("fp8", [False, True])
 def test_anchor_bytes_matches_oracle_slab(fp8):
     cfg = _cfg(fp8=fp8)
     for la in (1, 63, 64, 65, 768, 1024, 2048):
-        assert B.quail_anchor_bytes(cfg, la) == OP.slab_bytes(la, 36, 8, 128, 1 if fp8 else 2)
-    # 1024 anchors of 768 tokens: 57.98 GB in fp8 (twice that in bf16)
-    assert B.quail_anchor_bytes(cfg, 768) * 1024 == 36 * 2 * 8 * 768 * 128 * 1024 * (1 if fp8 else 2)
+        assert B.quail_anchor_bytes(cfg, la) == _slab(la, 36, 8, 128, 1 if fp8 else 2)
+    # 1024 anchors of 768 tokens: 57.98 GB in fp8 (twice that in bf16), plus the guards
+    assert B.quail_anchor_bytes(cfg, 768) * 1024 == (36 * 2 * 8 * 768 * 128 * (1 if fp8 else 2) + G) * 1024
 
 
 def test_workspace_bytes_grows_with_batch():
@@ -61,7 +70,7 @@ def test_plan_build_matches_oracle(seed):
     cfg = _cfg(layers=2, n_kv_heads=2, n_q_heads=4, hidden=256, intermediate=384)
     na = int(r.integers(1, 9))
     a_len = r.integers(1, 300, na).astype(np.int32)
-    slab = np.array([OP.slab_bytes(x, 2, 2, 128, 2) for x in a_len])
+    slab = np.array([_slab(x, 2, 2, 128, 2) for x in a_len])
     n = int(r.integers(0, 60))
     pa = r.integers(-1, na, n).astype(np.int32)
     pl = r.integers(1, 64, n).astype(np.int32)
@@ -84,7 +93,7 @@ def test_multiplan_build_matches_oracle(seed):
     a_len = r.integers(1, 300, na).astype(np.int32)
     if seed % 3 == 0:
         a_len[:] = 128                       # equal slabs: eviction order decided by next use alone
-    slab = np.array([OP.slab_bytes(x, 2, 2, 128, 2) for x in a_len])
+    slab = np.array([_slab(x, 2, 2, 128, 2) for x in a_len])
     joins = []
     for _ in range(int(r.integers(1, 5))):
         n = int(r.integers(0, 25))
@@ -186,7 +195,7 @@ def _i64(a):
 
 
 def test_anchor_prefill_pool_too_small_is_nomem_and_keeps_nothing():
-    cfg_slab = OP.slab_bytes(100, 2, 2, 128, 2)
+    cfg_slab = _slab(100, 2, 2, 128, 2)
     fc = _FakeCtx(pool_bytes=cfg_slab + cfg_slab // 2)
     off, offp = _i32([0, 100, 200])
     nu, nup = _i32([3, 4])

@@ -252,7 +252,7 @@ def test_multijoin_run_keeps_anchors_across_joins(B):
         wts, case, dm, ctx, a_tok, s_tok = _setup(shape, 9, a_len, pairs, B, mbt=96)
         slab = B.quail_anchor_bytes(dm.cfg, 64)
         if n_slabs != 5:
-            ctx = dm.context(n_slabs * slab, 96)
+            ctx = dm.context(n_slabs * slab + B.GUARD_BYTES, 96)   # + the pool's tail guard
         logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
         dec = torch.empty(n, dtype=torch.uint8, device="cuda")
         say("multijoin_run", label, n, "pairs in", len(joins), "joins")
@@ -487,3 +487,92 @@ def test_multijoin_full_size_one_layer_sampled(B):
         assert err <= 2e-2, (i, err)
         if abs(ref["margin"]) > 2e-2 * np.max(np.abs(ref["logits"])):
             assert dg[i] == ref["decision"], i
+
+
+def test_fragmented_pool_is_replanned_before_enqueueing(B):
+    """A plan that fits the pool by its byte total but not by placement: slabs
+    of 1, 2 and 3 units (64-token steps), a pool of 5 units, pairs [A, C | C,
+    D] in two 400-token steps. First-fit puts A at [0, 1) and C at [1, 3);
+    once A is evicted, D (3 units) finds only [0, 1) and [3, 5). The join
+    replays its placements on the host first and, finding that, re-plans with
+    a smaller budget (C's second pair, then D's pair, in steps of their own)
+    before anything is enqueued; results match the oracle, no regret."""
+    import torch
+    shape = W.tiny_shape(n_layers=1, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                         intermediate=384, vocab=512)
+    a_len = [64, 128, 192]
+    pairs = [(0, 200), (1, 200), (1, 200), (2, 200)]
+    wts, case, dm, ctx, a_tok, s_tok = _setup(shape, 23, a_len, pairs, B)
+    pool = B.quail_anchor_bytes(dm.cfg, 128) + B.quail_anchor_bytes(dm.cfg, 192) + B.GUARD_BYTES
+    ctx = dm.context(pool, 400)
+    # the plan alone (byte totals) puts C and D in one step
+    order, bounds, peak = B.quail_plan_build(dm.cfg, pool - B.GUARD_BYTES, 400, a_len, case["pair_anchor"],
+                                             case["s_len"])
+    assert len(bounds) - 1 == 2 and peak == pool - B.GUARD_BYTES
+    n = len(pairs)
+    logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+    dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+    say("fragmented pool: join_run", n, "pairs")
+    B.quail_join_run(ctx, a_tok, case["a_off"], case["pair_anchor"], s_tok, case["s_off"], 0x0F,
+                     logits, None, dec)
+    torch.cuda.synchronize()
+    ref = [OM.forward_pair(case["a_tok"][case["a_off"][a]:case["a_off"][a + 1]],
+                           case["s_tok"][case["s_off"][i]:case["s_off"][i + 1]], wts, shape)
+           for i, (a, _) in enumerate(pairs)]
+    ref_logits = np.array([r["logits"] for r in ref])
+    assert rel_inf(logits.cpu().numpy(), ref_logits) <= 2e-2
+    ok, _ = decisions_agree(dec.cpu().numpy(), [r["decision"] for r in ref], [r["margin"] for r in ref],
+                            2e-2 * np.max(np.abs(ref_logits)))
+    assert ok
+    st = B.quail_pool_stats(ctx)
+    assert st["prefills"] == 3 and st["evictions"] == 3 and st["regret_tokens"] == 0 and st["resident"] == 0
+
+
+def test_out_of_range_token_ids_are_counted_not_read(B):
+    """Token ids outside [0, vocab) are a caller error: the embedding counts
+    each one in the context's debug counter and reads row 0 instead (never
+    outside the table); every in-range pair is unaffected."""
+    import torch
+    from query_aware_prefill_amd.device import to_device
+    shape = W.tiny_shape(n_layers=1, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                         intermediate=384, vocab=512)
+    pairs = [(0, 5), (-1, 6), (0, 7)]
+    wts, case, dm, ctx, a_tok, s_tok = _setup(shape, 24, [40], pairs, B)
+    bad = case["s_tok"].copy()
+    o = case["s_off"]
+    bad[o[1] + 2] = shape.vocab + 5          # filter row: one id past the table
+    bad[o[1] + 4] = -3                       # and a negative one
+    n = len(pairs)
+    logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+    dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+    say("out-of-range token ids")
+    B.quail_join_run(ctx, a_tok, case["a_off"], case["pair_anchor"], to_device(bad), o, 0x0F, logits, None, dec)
+    torch.cuda.synchronize()
+    chk = B.quail_ctx_check(ctx)
+    assert chk == {"guard_errors": 0, "bad_tokens": 2}, chk
+    ctx.expect_counts = chk
+    lg = logits.cpu().numpy()
+    assert np.all(np.isfinite(lg))
+    for i in (0, 2):
+        ref = OM.forward_pair(case["a_tok"], case["s_tok"][o[i]:o[i + 1]], wts, shape)
+        assert rel_inf(lg[i], ref["logits"]) <= 2e-2
+
+
+def test_overwritten_guard_is_detected(B):
+    """The guard region after a live slab, overwritten from the host, is
+    reported by quail_ctx_check; an intact pool reports nothing."""
+    import torch
+    shape = W.tiny_shape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                         intermediate=384, vocab=512)
+    wts, case, dm, ctx, a_tok, s_tok = _setup(shape, 25, [30, 100], [(0, 3), (1, 4)], B)
+    h = B.quail_anchor_prefill(ctx, a_tok, case["a_off"], [1, 1])
+    torch.cuda.synchronize()
+    assert B.quail_ctx_check(ctx) == {"guard_errors": 0, "bad_tokens": 0}
+    # the guard follows the last layer's V block of the slab
+    kp, vp, la, lap = B.quail_anchor_kv(ctx, h[1], shape.n_layers - 1)
+    guard = vp + shape.n_kv_heads * lap * shape.head_dim * 2 - ctx._pool.data_ptr()
+    ctx._pool[guard + 8] ^= 0xFF
+    torch.cuda.synchronize()
+    chk = B.quail_ctx_check(ctx)
+    assert chk == {"guard_errors": 1, "bad_tokens": 0}, chk
+    ctx.expect_counts = {"guard_errors": 2, "bad_tokens": 0}   # checked again at teardown
