@@ -30,10 +30,13 @@ Readings where the pages are silent (all standard for this model family):
 
 Precision modes:
   * "contract": round to bf16 exactly where a bf16 tensor exists in the
-    pipeline: the normed input u, post-RoPE q/k/v, the attention output o, the
-    residual stream after each add, the MLP product m and the normed head
-    input z. Everything between those points is float64 (or float32 for
-    large cases when the caller asks).
+    pipeline: the activations every projection reads (the normed input u,
+    the attention output o, the MLP product m), the post-RoPE q/k/v, the last
+    position's hidden state handed to the head (h_last) and the normed head
+    input z. The residual stream itself -- the running sum the O and down
+    projections add into -- is not an activation any projection reads and
+    is kept unrounded (the GPU keeps it in fp32). Everything between those
+    points is float64 (or float32 for large cases when the caller asks).
   * "exact": no bf16 rounding at all (inputs are still bf16/fp8 values).
 
 Pins (tests/test_oracle_model.py): RMSNorm and SiLU against torch; RoPE at
@@ -129,10 +132,10 @@ def decoder_layer(h, pos, W: LayerWeights, shape, mode="contract", fp8_kv_upto=0
         v[:n] = codecs.e4m3_roundtrip(v[:n], shape.v_scale)
     o, _ = attention_causal(q, k, v, 1.0 / np.sqrt(d), q_pos=pos, k_pos=pos)
     o = _bf(o.reshape(N, Hq * d), mode)
-    h = _bf(h + o @ W.w_o.T, mode)
+    h = h + o @ W.w_o.T
     u = _bf(rmsnorm(h, W.mlp_norm, shape.rms_eps), mode)
     m = _bf(silu(u @ W.w_gate.T) * (u @ W.w_up.T), mode)
-    h = _bf(h + m @ W.w_down.T, mode)
+    h = h + m @ W.w_down.T
     if return_kv:
         return h, (k, v, k_pre, v_pre)
     return h
@@ -200,9 +203,10 @@ def forward_pair(anchor_tokens, suffix_tokens, weights, shape, true_mask=0x0F,
     fp8_upto = len(a) + int(shared_len) if shape.kv_fp8 else 0
     h = forward_tokens(tokens, weights, shape, mode, fp8_upto, dtype, layers,
                        n_layers=n_layers)
-    logits, tok, dec, margin = head8(h[-1:], weights.get("final_norm"), weights["head8"],
+    h_last = _bf(h[-1:], mode)          # the hidden state handed to the head
+    logits, tok, dec, margin = head8(h_last, weights.get("final_norm"), weights["head8"],
                                      true_mask, shape, mode)
-    return dict(h=h, h_last=h[-1], logits=logits[0], token=int(tok[0]),
+    return dict(h=h, h_last=h_last[0], logits=logits[0], token=int(tok[0]),
                 decision=int(dec[0]), margin=float(margin[0]))
 
 
@@ -234,7 +238,8 @@ def forward_many(seqs, weights, shape, true_mask=0x0F, mode="contract", dtype=np
     out = {}
 
     def head(hl):
-        lg, tk, dc, mg = head8(hl, weights.get("final_norm"), weights["head8"], true_mask, shape, mode)
+        lg, tk, dc, mg = head8(_bf(hl, mode), weights.get("final_norm"), weights["head8"], true_mask,
+                               shape, mode)
         return dict(logits=lg, token=tk, decision=dc, margin=mg)
 
     for l in range(L):
@@ -259,13 +264,13 @@ def forward_many(seqs, weights, shape, true_mask=0x0F, mode="contract", dtype=np
                 vs[:upto[i]] = codecs.e4m3_roundtrip(vs[:upto[i]], shape.v_scale)
             o[a:b], _ = attention_causal(q[a:b], ks, vs, 1.0 / np.sqrt(d))
         o = _bf(o.reshape(N, Hq * d), mode)
-        h = _bf(h + o @ W.w_o.T, mode)
+        h = h + o @ W.w_o.T
         u = _bf(rmsnorm(h, W.mlp_norm, shape.rms_eps), mode)
         m = _bf(silu(u @ W.w_gate.T) * (u @ W.w_up.T), mode)
-        h = _bf(h + m @ W.w_down.T, mode)
+        h = h + m @ W.w_down.T
         del W
         if (l + 1) in taps:
             out[l + 1] = head(h[last])
     out.update(head(h[last]))
-    out["h_last"] = h[last]
+    out["h_last"] = _bf(h[last], mode)
     return out

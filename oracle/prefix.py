@@ -101,8 +101,7 @@ def prefix_tree_reference(seqs, keys, min_len):
             if len(part) >= 2 and lcp_cut(part) >= end + min_len:
                 build(part, me, end)
 
-    _, firsts, _ = prefix_groups_reference(seqs, keys, min_len)
-    g1, _, _ = prefix_groups_reference(seqs, keys, min_len)
+    g1, firsts, _ = prefix_groups_reference(seqs, keys, min_len)
     for k in range(len(firsts)):
         build(sorted(np.flatnonzero(g1 == k).tolist()), -1, 0)
     return group_of, nodes

@@ -22,7 +22,7 @@
 //
 // Epilogues (fused so no extra pass touches HBM):
 //   STORE : y = bf16(acc * scale)
-//   RESID : h = bf16(h + acc * scale)                   (O and down projections)
+//   RESID : h = h + acc * scale, h the fp32 residual     (O and down projections)
 //   SWIGLU: m = bf16(silu(acc_gate * s_g) * acc_up * s_u)  (gate/up projection;
 //           a column tile holds 64 gate rows and the 64 matching up rows)
 //   QKV   : RoPE (rotate-half, table of cos/sin per position) on q and k heads,
@@ -183,8 +183,8 @@ __device__ __forceinline__ void epilogue_staged(const GemmParams& p, const f32x1
     if (to_fp8) epilogue_rows<EPI_QKV, true, MB>(p, acc, lds, m_row0, n_base, lane);
     else epilogue_rows<EPI_QKV, false, MB>(p, acc, lds, m_row0, n_base, lane);
   } else if (EPI == EPI_RESID) {
-    // fp32 staging (the residual add and the single bf16 rounding happen
-    // after the read-back): per 32 tokens and 64 columns, 256-B rows
+    // fp32 staging (the residual add happens after the read-back): per 32
+    // tokens and 64 columns, 256-B rows
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -213,18 +213,12 @@ __device__ __forceinline__ void epilogue_staged(const GemmParams& p, const f32x1
           const uint4 b = lds_read_b128(lds + r * 256 + (((2 * c8 + 1) ^ (r & 15)) << 4));
           const int mr = m_row0 + mb * 32 + r;
           if (mr >= p.M) continue;
-          uint4* yp = reinterpret_cast<uint4*>(p.Y + (int64_t)mr * p.ldy + n_base + half * 64 + c8 * 8);
-          const uint4 h = *yp;
-          uint4 o;
-          o.x = pack_bf16x2(__uint_as_float(a.x) + bf16_bits_to_f32(h.x & 0xFFFF),
-                            __uint_as_float(a.y) + bf16_bits_to_f32(h.x >> 16));
-          o.y = pack_bf16x2(__uint_as_float(a.z) + bf16_bits_to_f32(h.y & 0xFFFF),
-                            __uint_as_float(a.w) + bf16_bits_to_f32(h.y >> 16));
-          o.z = pack_bf16x2(__uint_as_float(b.x) + bf16_bits_to_f32(h.z & 0xFFFF),
-                            __uint_as_float(b.y) + bf16_bits_to_f32(h.z >> 16));
-          o.w = pack_bf16x2(__uint_as_float(b.z) + bf16_bits_to_f32(h.w & 0xFFFF),
-                            __uint_as_float(b.w) + bf16_bits_to_f32(h.w >> 16));
-          *yp = o;
+          float4* yp = reinterpret_cast<float4*>(p.Yf + (int64_t)mr * p.ldy + n_base + half * 64 + c8 * 8);
+          const float4 h0 = yp[0], h1 = yp[1];
+          yp[0] = make_float4(__uint_as_float(a.x) + h0.x, __uint_as_float(a.y) + h0.y,
+                              __uint_as_float(a.z) + h0.z, __uint_as_float(a.w) + h0.w);
+          yp[1] = make_float4(__uint_as_float(b.x) + h1.x, __uint_as_float(b.y) + h1.y,
+                              __uint_as_float(b.z) + h1.z, __uint_as_float(b.w) + h1.w);
         }
       }
     }

@@ -216,7 +216,7 @@ WsLayout ws_layout(const quail_model_config& c, int32_t T) {
   auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
   const size_t Tt = (size_t)T;
   w.rope = take((size_t)max_pos(c) * (c.head_dim / 2) * sizeof(float2));
-  w.h = take(Tt * c.hidden * 2);
+  w.h = take(Tt * c.hidden * 4);                  // fp32 residual stream
   w.u = take(Tt * c.hidden * 2);
   w.q = take(Tt * c.n_q_heads * c.head_dim * 2);
   w.k = take(Tt * c.n_kv_heads * c.head_dim * 2);
@@ -772,7 +772,7 @@ quail_status run_batch(quail_ctx* c, const Batch& b, const int32_t* tokens, uint
   const AttnTile* d_til = reinterpret_cast<const AttnTile*>(dp(o_til));
   const KVSrc* d_src = reinterpret_cast<const KVSrc*>(dp(o_src));
 
-  uint16_t* hbuf = ws_ptr<uint16_t>(c, c->L.h);
+  float* hbuf = ws_ptr<float>(c, c->L.h);
   uint16_t* ubuf = ws_ptr<uint16_t>(c, c->L.u);
   uint16_t* qbuf = ws_ptr<uint16_t>(c, c->L.q);
   uint16_t* kbuf = ws_ptr<uint16_t>(c, c->L.k);
@@ -823,7 +823,7 @@ quail_status run_batch(quail_ctx* c, const Batch& b, const int32_t* tokens, uint
 
     GemmParams go{};
     go.A = obuf; go.lda = (int64_t)Hq * kHeadDim; go.B = lw.w_o; go.scale = lw.s_o;
-    go.M = n; go.N = H; go.K = Hq * kHeadDim; go.Y = hbuf; go.ldy = H;
+    go.M = n; go.N = H; go.K = Hq * kHeadDim; go.Yf = hbuf; go.ldy = H;
     TIMED(PK_O, 2.0 * n * go.N * go.K, launch_gemm(go, EPI_RESID, s));
 
     np.gamma = lw.mlp_norm;
@@ -836,7 +836,7 @@ quail_status run_batch(quail_ctx* c, const Batch& b, const int32_t* tokens, uint
 
     GemmParams gd{};
     gd.A = mbuf; gd.lda = I; gd.B = lw.w_down; gd.scale = lw.s_down;
-    gd.M = n; gd.N = H; gd.K = I; gd.Y = hbuf; gd.ldy = H;
+    gd.M = n; gd.N = H; gd.K = I; gd.Yf = hbuf; gd.ldy = H;
     TIMED(PK_DOWN, 2.0 * n * gd.N * gd.K, launch_gemm(gd, EPI_RESID, s));
   }
   if (!b.anchor_mode) {
@@ -2214,11 +2214,32 @@ quail_status quail_cascade_workspace_bytes(int32_t n_anchors, const int32_t* a_o
   return QUAIL_OK;
 }
 
-quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t d, float sm_scale,
-                                int32_t n_anchors, const void* ak, const void* av, const int32_t* a_off,
-                                int32_t n_suffix, const int32_t* s_anchor, const void* q, const void* k,
-                                const void* v, const int32_t* s_off, void* out, float* lse,
-                                void* workspace, size_t ws_bytes, quail_stream stream) {
+}  // extern "C"
+
+namespace {
+
+// Where the cascade call's per-call metadata (token segments, tiles, KV
+// sources) goes: a caller workspace, filled through the pinned staging ring,
+// or the library's static scratch array, filled by one plain copy from host
+// memory (nothing allocated).
+struct MetaDest {
+  uint8_t* dev;
+  size_t bytes;
+  bool staged;
+};
+
+quail_status meta_copy(const MetaDest& m, const Blob& bl, hipStream_t st) {
+  if (bl.size() > m.bytes)
+    return fail(QUAIL_E_NOMEM, "cascade metadata of %zu B exceeds the %zu B available", bl.size(), m.bytes);
+  if (m.staged) HIP_TRY(stager().copy(m.dev, bl.data(), bl.size(), st));
+  else HIP_TRY(hipMemcpyAsync(m.dev, bl.data(), bl.size(), hipMemcpyHostToDevice, st));
+  return QUAIL_OK;
+}
+
+quail_status cascade_check(int32_t dtype, int32_t hq, int32_t hkv, int32_t d, float sm_scale, int32_t n_anchors,
+                           const void* ak, const void* av, const int32_t* a_off, int32_t n_suffix,
+                           const int32_t* s_anchor, const void* q, const void* k, const void* v,
+                           const int32_t* s_off, void* out) {
   if (dtype != QUAIL_DTYPE_F32 && dtype != QUAIL_DTYPE_BF16 && dtype != QUAIL_DTYPE_FP8_E4M3)
     return fail(QUAIL_E_UNSUPPORTED, "dtype must be F32, BF16 or FP8_E4M3");
   if (hq <= 0 || hkv <= 0 || hq % hkv) return fail(QUAIL_E_INVAL, "hq must be a positive multiple of hkv");
@@ -2239,12 +2260,16 @@ quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t 
     if (s_anchor[s] < -1 || s_anchor[s] >= n_anchors)
       return fail(QUAIL_E_INVAL, "suffix %d: anchor %d out of range", s, s_anchor[s]);
   if (n_anchors > 0 && (!ak || !av)) return fail(QUAIL_E_INVAL, "anchor K/V are NULL");
-  size_t need = 0;
-  quail_cascade_workspace_bytes(n_anchors, a_off, n_suffix, s_off, &need);
-  if (!workspace || ws_bytes < need) return fail(QUAIL_E_NOMEM, "workspace %zu B < %zu B", ws_bytes, need);
+  return QUAIL_OK;
+}
 
+// The cascade call after validation (n_suffix > 0).
+quail_status cascade_core(int32_t dtype, int32_t hq, int32_t hkv, int32_t d, float sm_scale, int32_t n_anchors,
+                          const void* ak, const void* av, const int32_t* a_off, int32_t n_suffix,
+                          const int32_t* s_anchor, const void* q, const void* k, const void* v,
+                          const int32_t* s_off, void* out, float* lse, const MetaDest& meta, hipStream_t st) {
+  const int G = hq / hkv;
   const int32_t T = s_off[n_suffix];
-  hipStream_t st = as_stream(stream);
   std::vector<int32_t> seg(T), tok_anchor(T);
   for (int32_t s = 0; s < n_suffix; ++s)
     for (int32_t t = s_off[s]; t < s_off[s + 1]; ++t) { seg[t] = s_off[s]; tok_anchor[t] = s_anchor[s]; }
@@ -2255,8 +2280,8 @@ quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t 
     std::vector<int32_t> ao(a_off, a_off + (n_anchors > 0 ? n_anchors + 1 : 0));
     if (ao.empty()) ao.push_back(0);
     const size_t o_ao = bl.add(ao);
-    uint8_t* md = static_cast<uint8_t*>(workspace);
-    HIP_TRY(stager().copy(md, bl.data(), bl.size(), st));
+    uint8_t* md = meta.dev;
+    if (quail_status r = meta_copy(meta, bl, st)) return r;
     AttnF32Params p{};
     p.ak = static_cast<const float*>(ak); p.av = static_cast<const float*>(av);
     p.a_off = reinterpret_cast<const int32_t*>(md + o_ao);
@@ -2311,9 +2336,8 @@ quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t 
   }
   const size_t o_til = bl.add(tiles);
   const size_t o_src = bl.add(srcs);
-  if (bl.size() > ws_bytes) return fail(QUAIL_E_NOMEM, "workspace too small for tiles");
-  uint8_t* md = static_cast<uint8_t*>(workspace);
-  HIP_TRY(stager().copy(md, bl.data(), bl.size(), st));
+  uint8_t* md = meta.dev;
+  if (quail_status r = meta_copy(meta, bl, st)) return r;
   AttnParams p{};
   p.tiles = reinterpret_cast<const AttnTile*>(md + o_til);
   p.n_tiles = (int32_t)tiles.size();
@@ -2326,6 +2350,27 @@ quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t 
   p.k_scale = 1.0f; p.v_scale = 1.0f;
   HIP_TRY(launch_attn_bf16(p, G, a_fp8, false, packed, st));
   return QUAIL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t d, float sm_scale,
+                                int32_t n_anchors, const void* ak, const void* av, const int32_t* a_off,
+                                int32_t n_suffix, const int32_t* s_anchor, const void* q, const void* k,
+                                const void* v, const int32_t* s_off, void* out, float* lse,
+                                void* workspace, size_t ws_bytes, quail_stream stream) {
+  if (quail_status r = cascade_check(dtype, hq, hkv, d, sm_scale, n_anchors, ak, av, a_off, n_suffix, s_anchor,
+                                     q, k, v, s_off, out))
+    return r;
+  if (n_suffix == 0) return QUAIL_OK;
+  size_t need = 0;
+  quail_cascade_workspace_bytes(n_anchors, a_off, n_suffix, s_off, &need);
+  if (!workspace || ws_bytes < need) return fail(QUAIL_E_NOMEM, "workspace %zu B < %zu B", ws_bytes, need);
+  const MetaDest meta{static_cast<uint8_t*>(workspace), ws_bytes, true};
+  return cascade_core(dtype, hq, hkv, d, sm_scale, n_anchors, ak, av, a_off, n_suffix, s_anchor, q, k, v, s_off,
+                      out, lse, meta, as_stream(stream));
 }
 
 quail_status quail_gemm_w8a16(int32_t M, int32_t N, int32_t K, const uint16_t* x, const uint8_t* w,

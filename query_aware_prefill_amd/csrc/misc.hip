@@ -7,11 +7,12 @@
 
 namespace quail {
 
-// h[r] = embed[tokens[tok_map ? tok_map[r] : r]]. A token id outside
-// [0, vocab) is counted in *bad (when given) and embeds row 0 instead, so a
-// bad id never becomes an out-of-range read.
+// h[r] = embed[tokens[tok_map ? tok_map[r] : r]], widened to the fp32
+// residual stream. A token id outside [0, vocab) is counted in *bad (when
+// given) and embeds row 0 instead, so a bad id never becomes an out-of-range
+// read.
 __global__ void __launch_bounds__(256) embed_kernel(const int32_t* tokens, const int32_t* tok_map,
-                                                    const uint16_t* embed, uint16_t* h,
+                                                    const uint16_t* embed, float* h,
                                                     int32_t rows, int32_t H, int32_t vocab,
                                                     uint32_t* bad) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -24,12 +25,18 @@ __global__ void __launch_bounds__(256) embed_kernel(const int32_t* tokens, const
     tok = 0;
   }
   const uint4* s = reinterpret_cast<const uint4*>(embed + tok * H);
-  uint4* d = reinterpret_cast<uint4*>(h + (int64_t)r * H);
-  for (int c = lane; c < H / 8; c += 64) d[c] = s[c];
+  float4* d = reinterpret_cast<float4*>(h + (int64_t)r * H);
+  for (int c = lane; c < H / 8; c += 64) {
+    const uint4 v = s[c];
+    d[2 * c] = make_float4(bf16_bits_to_f32(v.x & 0xFFFF), bf16_bits_to_f32(v.x >> 16),
+                           bf16_bits_to_f32(v.y & 0xFFFF), bf16_bits_to_f32(v.y >> 16));
+    d[2 * c + 1] = make_float4(bf16_bits_to_f32(v.z & 0xFFFF), bf16_bits_to_f32(v.z >> 16),
+                               bf16_bits_to_f32(v.w & 0xFFFF), bf16_bits_to_f32(v.w >> 16));
+  }
 }
 
 hipError_t launch_embed(const int32_t* tokens, const int32_t* tok_map, const uint16_t* embed,
-                        uint16_t* h, int32_t rows, int32_t H, int32_t vocab, uint32_t* bad,
+                        float* h, int32_t rows, int32_t H, int32_t vocab, uint32_t* bad,
                         hipStream_t s) {
   if (rows == 0) return hipSuccess;
   embed_kernel<<<dim3((rows + 3) / 4), dim3(256), 0, s>>>(tokens, tok_map, embed, h, rows, H, vocab, bad);
@@ -75,7 +82,8 @@ hipError_t launch_zero_words(uint32_t* p, int32_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
-__global__ void __launch_bounds__(256) copy_rows_kernel(const uint16_t* src, int64_t lds,
+// fp32 residual rows -> bf16 rows (round to nearest even)
+__global__ void __launch_bounds__(256) copy_rows_kernel(const float* src, int64_t lds,
                                                         const int32_t* src_idx, uint16_t* dst,
                                                         int64_t ldd, const int32_t* dst_idx,
                                                         int32_t rows, int32_t H) {
@@ -84,12 +92,16 @@ __global__ void __launch_bounds__(256) copy_rows_kernel(const uint16_t* src, int
   if (r >= rows) return;
   const int64_t sr = src_idx ? src_idx[r] : r;
   const int64_t dr = dst_idx ? dst_idx[r] : r;
-  const uint4* s = reinterpret_cast<const uint4*>(src + sr * lds);
+  const float4* s = reinterpret_cast<const float4*>(src + sr * lds);
   uint4* d = reinterpret_cast<uint4*>(dst + dr * ldd);
-  for (int c = lane; c < H / 8; c += 64) d[c] = s[c];
+  for (int c = lane; c < H / 8; c += 64) {
+    const float4 a = s[2 * c], b = s[2 * c + 1];
+    d[c] = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
+                      pack_bf16x2(b.z, b.w));
+  }
 }
 
-hipError_t launch_copy_rows(const uint16_t* src, int64_t lds, const int32_t* src_idx,
+hipError_t launch_copy_rows(const float* src, int64_t lds, const int32_t* src_idx,
                             uint16_t* dst, int64_t ldd, const int32_t* dst_idx, int32_t rows,
                             int32_t H, hipStream_t s) {
   if (rows == 0) return hipSuccess;
@@ -123,40 +135,34 @@ hipError_t launch_copy_slab_rows(const uint8_t* src, int64_t src_block, uint8_t*
   return hipGetLastError();
 }
 
-// y = bf16(x / sqrt(mean(x^2) + eps) * gamma)
+// y = bf16(x / sqrt(mean(x^2) + eps) * gamma), x an fp32 residual row; 8
+// columns per lane and step (two 16-B loads, one 16-B store)
 __global__ void __launch_bounds__(256) rmsnorm_kernel(NormParams p) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= p.rows) return;
   const int src = p.row_map ? p.row_map[r] : r;
-  const uint4* x = reinterpret_cast<const uint4*>(p.x + (int64_t)src * p.ldx);
+  const float4* x = reinterpret_cast<const float4*>(p.x + (int64_t)src * p.ldx);
   const int nc = p.H / 8;
   float ss = 0.0f;
   for (int c = lane; c < nc; c += 64) {
-    const uint4 u = x[c];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = bf16_bits_to_f32(w[i] & 0xFFFF), b = bf16_bits_to_f32(w[i] >> 16);
-      ss += a * a + b * b;
-    }
+    const float4 a = x[2 * c], b = x[2 * c + 1];
+    ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + b.x * b.x + b.y * b.y + b.z * b.z + b.w * b.w;
   }
   ss = wave_sum(ss);
   const float inv = 1.0f / sqrtf(ss / (float)p.H + p.eps);
   uint4* y = reinterpret_cast<uint4*>(p.y + (int64_t)r * p.ldy);
   const uint4* gm = reinterpret_cast<const uint4*>(p.gamma);
   for (int c = lane; c < nc; c += 64) {
-    const uint4 u = x[c];
+    const float4 a = x[2 * c], b = x[2 * c + 1];
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     const uint4 gg = gm ? gm[c] : make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
     const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
     uint32_t o[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = bf16_bits_to_f32(w[i] & 0xFFFF) * inv * bf16_bits_to_f32(gw[i] & 0xFFFF);
-      const float b = bf16_bits_to_f32(w[i] >> 16) * inv * bf16_bits_to_f32(gw[i] >> 16);
-      o[i] = pack_bf16x2(a, b);
-    }
+    for (int i = 0; i < 4; ++i)
+      o[i] = pack_bf16x2(v[2 * i] * inv * bf16_bits_to_f32(gw[i] & 0xFFFF),
+                         v[2 * i + 1] * inv * bf16_bits_to_f32(gw[i] >> 16));
     y[c] = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }

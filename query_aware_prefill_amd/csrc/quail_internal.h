@@ -68,7 +68,7 @@ struct AttnF32Params {
 
 enum GemmEpi : int32_t {
   EPI_STORE = 0,    // y = bf16(acc * scale)
-  EPI_RESID = 1,    // y = bf16(y + acc * scale)           (residual add in place)
+  EPI_RESID = 1,    // y = y + acc * scale, y fp32         (residual add in place)
   EPI_SWIGLU = 2,   // y[n] = bf16(silu(g) * u), g from row n, u from row n + inter
   EPI_QKV = 3,      // RoPE on q/k heads, q -> q_out, k/v -> suffix buffers or slabs
 };
@@ -78,7 +78,8 @@ struct GemmParams {
   const uint8_t* B;                      // fp8 [N_rows][K]
   const uint16_t* scale;                 // bf16 [N_rows]
   int32_t M, N, K;                       // N = output columns
-  uint16_t* Y; int64_t ldy;              // STORE / RESID / SWIGLU output
+  uint16_t* Y; int64_t ldy;              // STORE / SWIGLU output (bf16)
+  float* Yf;                             // RESID: fp32 residual rows (stride ldy)
   int32_t inter;                         // SWIGLU: up rows start at `inter`
   // QKV epilogue
   int32_t hq, hkv;
@@ -96,7 +97,7 @@ struct GemmParams {
 };
 
 struct NormParams {
-  const uint16_t* x; int64_t ldx;
+  const float* x; int64_t ldx;           // fp32 residual rows
   const uint16_t* gamma;                 // bf16 [H] (null: gain 1)
   uint16_t* y; int64_t ldy;
   const int32_t* row_map;                // optional: y row r reads x row row_map[r]
@@ -131,17 +132,19 @@ int attn_tile_tokens(int group, bool packed);
 hipError_t launch_attn_f32(const AttnF32Params& p, hipStream_t s);
 hipError_t launch_gemm(const GemmParams& p, GemmEpi epi, hipStream_t s);
 hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s);
-// token ids outside [0, vocab) embed row 0 and are counted in *bad (nullable)
+// h (fp32) = embedding rows; token ids outside [0, vocab) embed row 0 and are
+// counted in *bad (nullable)
 hipError_t launch_embed(const int32_t* tokens, const int32_t* tok_map, const uint16_t* embed,
-                        uint16_t* h, int32_t rows, int32_t H, int32_t vocab, uint32_t* bad,
+                        float* h, int32_t rows, int32_t H, int32_t vocab, uint32_t* bad,
                         hipStream_t s);
 // 256-byte guard regions at base + offs[i] (offs on the device): mode 1
 // writes the guard pattern, mode 0 counts regions that differ from it in *bad
 hipError_t launch_guard(uint8_t* base, const int64_t* offs, int32_t n, int32_t mode, uint32_t* bad,
                         hipStream_t s);
 hipError_t launch_zero_words(uint32_t* p, int32_t n, hipStream_t s);
-// dst[dst_idx ? dst_idx[r] : r] = src[src_idx ? src_idx[r] : r], bf16 rows of H
-hipError_t launch_copy_rows(const uint16_t* src, int64_t lds, const int32_t* src_idx,
+// dst[dst_idx ? dst_idx[r] : r] = bf16(src[src_idx ? src_idx[r] : r]): fp32
+// residual rows of H to bf16 rows
+hipError_t launch_copy_rows(const float* src, int64_t lds, const int32_t* src_idx,
                             uint16_t* dst, int64_t ldd, const int32_t* dst_idx, int32_t rows,
                             int32_t H, hipStream_t s);
 // rows 0..rows-1 of each of n_blocks slab blocks (src_block / dst_block bytes

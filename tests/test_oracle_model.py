@@ -109,8 +109,10 @@ def test_contract_mode_rounds_and_stays_close_to_exact():
     shape, wts = _tiny_layer_case(seed=1)
     toks = np.random.default_rng(2).integers(0, shape.vocab, 20)
     he = M.forward_tokens(toks, wts, shape, mode="exact")
-    hc = M.forward_tokens(toks, wts, shape, mode="contract")
-    assert np.array_equal(codecs.bf16_round(hc), hc)   # residual stream is bf16
+    hc, kv = M.forward_tokens(toks, wts, shape, mode="contract", return_kv=True)
+    k, v = kv[0][0], kv[0][1]
+    assert np.array_equal(codecs.bf16_round(k), k) and np.array_equal(codecs.bf16_round(v), v)  # bf16 K/V
+    assert not np.array_equal(codecs.bf16_round(hc), hc)   # the residual stream is not rounded
     assert np.max(np.abs(he - hc)) / np.max(np.abs(he)) < 2e-2
     assert not np.array_equal(he, hc)
 
@@ -190,7 +192,7 @@ def test_forward_pair_filter_row_and_decision_consistency():
     a, s = r.integers(0, 64, 11), r.integers(0, 64, 4)
     o1 = M.forward_pair(a, s, wts, shape)
     h = M.forward_tokens(np.concatenate([a, s]), wts, shape)
-    assert np.array_equal(o1["h_last"], h[-1])
+    assert np.array_equal(o1["h_last"], codecs.bf16_round(h[-1]))   # handed to the head as bf16
 
 
 def test_stack_exact_matches_transformers_llama_model():
