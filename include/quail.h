@@ -496,6 +496,26 @@ quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t 
                                 void* out, float* lse, void* workspace, size_t ws_bytes,
                                 quail_stream stream);
 
+/* quail_cascade_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and kernels, without the workspace
+ * argument. The per-call metadata (token segments, attention tiles, KV
+ * sources) goes to a static scratch array of the library, one per device, of
+ * QUAIL_NOALLOC_SCRATCH_BYTES (16 MiB), filled by one hipMemcpyAsync from host
+ * memory; nothing is allocated. A call whose metadata
+ * (quail_cascade_workspace_bytes) exceeds that returns QUAIL_E_NOMEM before
+ * anything is enqueued. Every call on one device shares that device's array:
+ * calls in one stream order are safe (each call's copy follows the previous
+ * call's kernel), calls that overlap on one device (other streams, other
+ * threads) race on it. Other arguments, results and errors as
+ * quail_cascade_attn. */
+#define QUAIL_NOALLOC_SCRATCH_BYTES (16u << 20)
+quail_status quail_cascade_attn_noalloc(int32_t dtype, int32_t hq, int32_t hkv, int32_t d, float sm_scale,
+                                        int32_t n_anchors, const void* ak, const void* av,
+                                        const int32_t* a_off, int32_t n_suffix, const int32_t* s_anchor,
+                                        const void* q, const void* k, const void* v, const int32_t* s_off,
+                                        void* out, float* lse, quail_stream stream);
+
 /* ---- W8A16 GEMM (the projections of a4, a6, a7) ----------------------------- */
 /* y[m][n] = bf16( scale[n] * sum_k x[m][k] * decode(w[n][k]) ), fp32
  * accumulation. x dev bf16 [M, K] (row stride K); w dev fp8 [N, K]; scale dev

@@ -107,6 +107,9 @@ _SIGS = {
     "quail_cascade_attn": ([C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_float, C.c_int32, _vp, _vp,
                             _i32p, C.c_int32, _i32p, _vp, _vp, _vp, _i32p, _vp, _vp, _vp, C.c_size_t,
                             _vp], C.c_int32),
+    "quail_cascade_attn_noalloc": ([C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_float, C.c_int32, _vp,
+                                    _vp, _i32p, C.c_int32, _i32p, _vp, _vp, _vp, _i32p, _vp, _vp, _vp],
+                                   C.c_int32),
     "quail_gemm_w8a16": ([C.c_int32, C.c_int32, C.c_int32, _vp, _vp, _vp, _vp, _vp], C.c_int32),
     "quail_fp8_e4m3_encode": ([C.c_int64, _vp, C.c_float, _vp, _vp], C.c_int32),
     "quail_fp8_e4m3_decode": ([C.c_int64, _vp, C.c_float, _vp, _vp], C.c_int32),
@@ -433,6 +436,17 @@ def quail_cascade_attn(dtype, hq, hkv, d, sm_scale, ak, av, a_off, s_anchor, q, 
                                      dptr(out), dptr(lse), dptr(workspace),
                                      workspace.numel() * workspace.element_size() if workspace is not None else 0,
                                      stream_handle(stream)))
+
+
+def quail_cascade_attn_noalloc(dtype, hq, hkv, d, sm_scale, ak, av, a_off, s_anchor, q, k, v, s_off, out,
+                               lse=None, stream=None):
+    """quail_cascade_attn without a workspace (the library's static scratch)."""
+    ao, aop = _i32(a_off)
+    sa, sap = _i32(s_anchor)
+    so, sop = _i32(s_off)
+    _check(load().quail_cascade_attn_noalloc(dtype, hq, hkv, d, sm_scale, max(len(ao) - 1, 0), dptr(ak),
+                                             dptr(av), aop, len(sa), sap, dptr(q), dptr(k), dptr(v), sop,
+                                             dptr(out), dptr(lse), stream_handle(stream)))
 
 
 def quail_gemm_w8a16(x, w, scale, y, stream=None):

@@ -2216,6 +2216,15 @@ quail_status quail_cascade_workspace_bytes(int32_t n_anchors, const int32_t* a_o
 
 }  // extern "C"
 
+// Scratch memory of the allocation-free cascade call
+// (quail_cascade_attn_noalloc): its per-call metadata, at most 16 MiB. One
+// array per device: each GPU the library runs on holds its own copy until the
+// process ends. Host code never passes the array's name to a kernel or a
+// copy -- on the host the name is only a stand-in -- but the device address
+// hipGetSymbolAddress returns, taken once per device (scratch_ptr below).
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 namespace {
 
 // Where the cascade call's per-call metadata (token segments, tiles, KV
@@ -2352,6 +2361,25 @@ quail_status cascade_core(int32_t dtype, int32_t hq, int32_t hkv, int32_t d, flo
   return QUAIL_OK;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+quail_status scratch_ptr(uint8_t** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(QUAIL_E_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr) return fail(QUAIL_E_HIP, "hipGetSymbolAddress returned NULL for the scratch array");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<uint8_t*>(g_scratch_ptr[dev]);
+  return QUAIL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2369,6 +2397,27 @@ quail_status quail_cascade_attn(int32_t dtype, int32_t hq, int32_t hkv, int32_t 
   quail_cascade_workspace_bytes(n_anchors, a_off, n_suffix, s_off, &need);
   if (!workspace || ws_bytes < need) return fail(QUAIL_E_NOMEM, "workspace %zu B < %zu B", ws_bytes, need);
   const MetaDest meta{static_cast<uint8_t*>(workspace), ws_bytes, true};
+  return cascade_core(dtype, hq, hkv, d, sm_scale, n_anchors, ak, av, a_off, n_suffix, s_anchor, q, k, v, s_off,
+                      out, lse, meta, as_stream(stream));
+}
+
+quail_status quail_cascade_attn_noalloc(int32_t dtype, int32_t hq, int32_t hkv, int32_t d, float sm_scale,
+                                        int32_t n_anchors, const void* ak, const void* av, const int32_t* a_off,
+                                        int32_t n_suffix, const int32_t* s_anchor, const void* q, const void* k,
+                                        const void* v, const int32_t* s_off, void* out, float* lse,
+                                        quail_stream stream) {
+  if (quail_status r = cascade_check(dtype, hq, hkv, d, sm_scale, n_anchors, ak, av, a_off, n_suffix, s_anchor,
+                                     q, k, v, s_off, out))
+    return r;
+  if (n_suffix == 0) return QUAIL_OK;
+  size_t need = 0;
+  quail_cascade_workspace_bytes(n_anchors, a_off, n_suffix, s_off, &need);
+  if (need > kScratchBytes)
+    return fail(QUAIL_E_NOMEM, "call needs %zu B of metadata; the allocation-free entry point holds at most %zu B",
+                need, kScratchBytes);
+  uint8_t* ptr = nullptr;
+  if (quail_status r = scratch_ptr(&ptr)) return r;
+  const MetaDest meta{ptr, kScratchBytes, false};
   return cascade_core(dtype, hq, hkv, d, sm_scale, n_anchors, ak, av, a_off, n_suffix, s_anchor, q, k, v, s_off,
                       out, lse, meta, as_stream(stream));
 }

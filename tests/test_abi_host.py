@@ -449,3 +449,17 @@ def test_join_search_frontier_buffer():
     st = lib.quail_join_search(C.byref(cfg), 3, ta, 2, ja, 2.5e15, 8e12, op, arp, met.ctypes.data_as(f64p),
                                None, 0, C.byref(nf))
     assert st == B.OK and nf.value == full["n_frontier"]
+
+
+def test_noalloc_cascade_rejects_metadata_beyond_its_scratch():
+    """The allocation-free cascade entry point refuses, before any GPU work, a
+    call whose metadata exceeds its 16 MiB scratch array (here 5 M query
+    tokens: 20 MB of per-token segments alone)."""
+    lib = B.load()
+    fake = 0x7F0000000000
+    so, sop = _i32([0, 5_000_000])
+    sa, sap = _i32([-1])
+    st = lib.quail_cascade_attn_noalloc(B.DTYPE_BF16, 32, 8, 128, 0.088, 0, None, None, None, 1, sap, fake,
+                                        fake, fake, sop, fake, None, None)
+    assert st == B.E_NOMEM
+    assert b"16777216" in lib.quail_last_error()
