@@ -1,28 +1,41 @@
-"""Benchmark: AI.IF join prefill, cascade-attention layer at the Qwen3-4B shape.
+"""Benchmark: AI.IF join prefill on the 36-layer Qwen3-4B-shaped stack.
 
-Workload (one step = one pass of the whole batch through the cascade
-attention layer): 256 anchors of U{512..2048} tokens, each joined to 64
-suffixes of U{32..128} tokens; 32 query / 8 KV heads of 128; bf16 Q/K/V ~
-N(0, 1) resident in HBM; softmax scale 1/sqrt(128). Each suffix attends to
-all of its anchor's keys (cross partial) and causally to its own keys (self
-partial); the partials merge by LSE rescaling.
+Headline workload: the 36-layer join -- 64 anchors of 1024 tokens, each
+joined to 2048 suffixes of 64 tokens (131,072 pairs; random-init fp8
+weights, bf16 activations and anchor KV). One step is a fixed 1/32 share of
+that join: two consecutive anchors with all of their 4,096 pairs, run end to
+end by quail_join_run (plan, anchor prefill + KV writer, join prefill through
+all 36 layers with cascade attention, the 8-column head and the booleans).
+Step k takes anchors 2k and 2k+1 (mod 64); every step is the same amount of
+work, so 32 steps are the whole join.
 
 Reported:
-  value      logical prefill tokens per minute: sum over (anchor, suffix)
-             pairs of La + Ls -- the tokens a naive per-pair engine would
-             prefill for this layer; the suffix tokens actually computed are
-             reported beside it.
-  roofline   cascade kernel: algorithmic FLOPs per launch (4*Hq*d*La per
-             suffix token for the cross part, 4*Hq*d*(j+1) at suffix
-             position j for the self part) / its average launch duration,
-             timed with HIP events on the launch stream, against the bf16
-             dense MFMA peak (2.5 PFLOP/s).
-  cpu_baseline  the CPU oracle (monolithic causal attention per pair, fp64)
-             on a time-bounded sample of the same pairs, scaled to tokens/min.
+  value      logical prefill tokens per minute: sum over the step's pairs of
+             La + Ls (1088 tokens per pair) -- the tokens a per-pair engine
+             would prefill; the tokens actually computed (suffixes plus each
+             anchor once) are reported beside it.
+  roofline   the dominant kernel, the gate/up projection with the SwiGLU
+             epilogue (W8A16 GEMM): algorithmic FLOP per launch (2 * M *
+             19456 * 2560 for M batch tokens) / its average launch duration,
+             both from HIP events recorded around every launch on the
+             launch stream during the timed steps (quail_ctx_profile),
+             against the bf16 dense MFMA peak (2.5 PFLOP/s). The other
+             kernels' rates are listed beside it, and the headline
+             cascade-attention configuration (256 anchors x 64 suffixes,
+             one layer, bf16 Q/K/V) is timed as a field of its own.
+  cpu_baseline  the CPU oracle's per-pair forward (36 layers over
+             [anchor | suffix], float32 with the bf16 rounding points) on
+             sampled pairs of the same join, scaled to logical tokens/min.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
 Secondary measurements (not the headline line; each prints its own JSON):
+  --workload cascade the cascade-attention layer alone at the Qwen3-4B shape:
+                     256 anchors of U{512..2048} tokens, each joined to 64
+                     suffixes of U{32..128} tokens; bf16 Q/K/V ~ N(0, 1)
+                     resident in HBM; TFLOP/s of the attention kernel
+                     (4*Hq*d*La per suffix token for the cross part,
+                     4*Hq*d*(j+1) at suffix position j for the self part).
   --workload gemm    the four W8A16 projection shapes of the Qwen3-4B layer
                      (QKV 6144x2560, O 2560x4096, gate/up 19456x2560, down
                      2560x9728) at M = 65536 tokens, TFLOP/s against the bf16
@@ -849,6 +862,255 @@ def bench_search(args):
     print(json.dumps(out), flush=True)
 
 
+def host_cpu():
+    """CPU model, logical CPUs and the BLAS thread count the oracle runs with."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"),
+                      default=None)
+    except Exception:
+        threads = None
+    if not threads:
+        import torch
+        threads = torch.get_num_threads()
+    return {"cpu_model": model, "host_cpus": os.cpu_count(), "blas_threads": int(threads)}
+
+
+JOIN_ANCHORS, JOIN_SUFFIXES, JOIN_LA, JOIN_LS = 64, 2048, 1024, 64
+ANCHORS_PER_STEP = 2
+
+
+def bench_join(args):
+    """Headline: the 36-layer join, one step = two anchors with all their pairs."""
+    import torch
+    import workloads as W
+    from query_aware_prefill_amd import binding as B
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    B.load()
+    shape = W.QWEN3_4B
+    log("join: generating the workload (64 anchors x 1024 tokens, 2048 suffixes x 64 tokens each)")
+    case = W.c3b_case(n_anchors=JOIN_ANCHORS, per_anchor=JOIN_SUFFIXES, la=JOIN_LA, ls=JOIN_LS)
+    a_off, s_off, pair_anchor = case["a_off"], case["s_off"], case["pair_anchor"]
+    assert np.all(np.diff(pair_anchor) >= 0)        # pairs grouped by anchor
+    log("join: random-init weights on the device")
+    wd = W.model_weights_device(shape, 0)
+    dm = DeviceModel(shape, wd, max_anchor_len=JOIN_LA, max_suffix_len=JOIN_LS)
+    T = 65536
+    pool = ANCHORS_PER_STEP * B.quail_anchor_bytes(dm.cfg, JOIN_LA) + (1 << 20)
+    ctx = dm.context(pool, T)
+    a_tok_d = to_device(case["a_tok"])
+    s_tok_d = to_device(case["s_tok"])
+    per_step_pairs = ANCHORS_PER_STEP * JOIN_SUFFIXES
+    logits = torch.empty((per_step_pairs, 8), dtype=torch.float32, device="cuda")
+    dec = torch.empty(per_step_pairs, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    n_groups = JOIN_ANCHORS // ANCHORS_PER_STEP
+
+    def step_inputs(k):
+        g = k % n_groups
+        a0, a1 = g * ANCHORS_PER_STEP, (g + 1) * ANCHORS_PER_STEP
+        p0, p1 = a0 * JOIN_SUFFIXES, a1 * JOIN_SUFFIXES
+        return (a_tok_d[int(a_off[a0]):int(a_off[a1])], (a_off[a0:a1 + 1] - a_off[a0]).astype(np.int32),
+                (pair_anchor[p0:p1] - a0).astype(np.int32), s_tok_d[int(s_off[p0]):int(s_off[p1])],
+                (s_off[p0:p1 + 1] - s_off[p0]).astype(np.int32), a0, p0)
+
+    inputs = [step_inputs(k) for k in range(args.warmup + args.steps)]
+
+    def step(k):
+        at, ao, pa, st, so, _, _ = inputs[k]
+        B.quail_join_run(ctx, at, ao, pa, st, so, 0x0F, logits, None, dec, stream=stream)
+
+    log(f"join: warmup {args.warmup}")
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    B.quail_ctx_profile(ctx, True)
+    log(f"join: timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for k in range(args.warmup, args.warmup + args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    prof = B.quail_ctx_profile_read(ctx)
+    B.quail_ctx_profile(ctx, False)
+    chk = B.quail_ctx_check(ctx)
+    st = B.quail_pool_stats(ctx)
+    ms_step = el * 1000.0 / args.steps
+    logical = per_step_pairs * (JOIN_LA + JOIN_LS)
+    computed = per_step_pairs * JOIN_LS + ANCHORS_PER_STEP * JOIN_LA
+    value = logical / (ms_step * 1e-3) * 60.0
+    kern = {}
+    for kname, v in prof.items():
+        if v["launches"]:
+            kern[kname] = {"launches": v["launches"], "ms": v["ms"], "avg_launch_ms": v["ms"] / v["launches"],
+                           "share_of_step_time": v["ms"] / (el * 1000.0)}
+            if v["flop"] > 0:
+                kern[kname]["tflops"] = v["flop"] / (v["ms"] * 1e-3) / 1e12
+                kern[kname]["frac"] = kern[kname]["tflops"] / PEAK_BF16_TFLOPS
+    gu = prof["gate_up"]
+    gu_ms = gu["ms"] / gu["launches"]
+    gu_flop = gu["flop"] / gu["launches"]
+    gu_tf = gu_flop / (gu_ms * 1e-3) / 1e12
+    gemm_ms = sum(prof[k]["ms"] for k in ("qkv", "o", "gate_up", "down"))
+    gemm_flop = sum(prof[k]["flop"] for k in ("qkv", "o", "gate_up", "down"))
+    tokens_per_launch = gu_flop / (2.0 * 2 * shape.intermediate * shape.hidden)
+    log(f"join: step {ms_step:.1f} ms, {value / 1e6:.1f} M logical tok/min; gate/up {gu_ms:.3f} ms per launch, "
+        f"{gu_tf:.1f} TFLOP/s; all GEMMs {gemm_flop / (gemm_ms * 1e-3) / 1e12:.1f} TFLOP/s "
+        f"({gemm_ms / (el * 1000.0):.1%} of the time)")
+    res = {
+        "metric": METRIC, "value": value, "unit": "tokens/min", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": "36-layer AI.IF join, Qwen3-4B shape with random-init fp8 weights: 64 anchors x 1024 "
+                        "tokens, each joined to 2048 suffixes of 64 tokens (131,072 pairs, bf16 anchor KV); "
+                        "one step = 2 anchors with their 4,096 pairs (1/32 of the join) through "
+                        "quail_join_run: plan, anchor prefill + KV writer, 36-layer join prefill, 8-column head",
+            "anchors_per_step": ANCHORS_PER_STEP, "pairs_per_step": per_step_pairs,
+            "logical_tokens_per_step": logical, "computed_tokens_per_step": computed,
+            "computed_tokens_per_min": computed / (ms_step * 1e-3) * 60.0,
+            "whole_join_s_at_this_rate": ms_step * 1e-3 * n_groups,
+            "max_batch_tokens": T, "parallelism": "single GPU",
+            "kernels": kern,
+            "gemm_all_tflops": gemm_flop / (gemm_ms * 1e-3) / 1e12,
+            "pool": st, "debug_counters": chk,
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": gu_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": gu_tf / PEAK_BF16_TFLOPS, "traffic": None,
+            "kernel": "quail::gemm_direct_kernel<(quail::GemmEpi)2, 256, 256, 4, 2> (gate/up + SwiGLU)",
+            "flops_per_launch": gu_flop, "launch_ms": gu_ms, "launches": gu["launches"],
+            "tokens_per_launch": tokens_per_launch,
+            "algorithmic_bytes_per_launch": 2 * shape.intermediate * shape.hidden
+                + tokens_per_launch * (shape.hidden * 2 + shape.intermediate * 2),
+        },
+        "cpu_baseline": None,
+    }
+    # the cascade-attention headline configuration, timed on its own
+    c1 = bench_cascade(args, steps=5, warmup=2, cpu=False)
+    res["config"]["cascade_attention_layer"] = {
+        "workload": c1["config"]["workload"], "tflops": c1["roofline"]["achieved"],
+        "frac": c1["roofline"]["frac"], "launch_ms": c1["roofline"]["launch_ms"],
+        "kernel": c1["roofline"]["kernel"]}
+    if not args.no_cpu_baseline:
+        lg = logits.cpu().numpy().astype(np.float64)
+        at, ao, pa, st_, so, a0, p0 = inputs[args.warmup + args.steps - 1]
+        order = np.random.default_rng(0).permutation(per_step_pairs)[:8]
+        pairs = []
+        for i in order:
+            a = a0 + int(pa[i])
+            pi = p0 + int(i)
+            pairs.append((int(i), case["a_tok"][a_off[a]:a_off[a + 1]], case["s_tok"][s_off[pi]:s_off[pi + 1]]))
+        log("join: oracle leg")
+        cpu = cpu_baseline_e2e(wd, shape, pairs, lg, 0x0F, args.cpu_budget)
+        cpu.update(host_cpu())
+        cpu["cores"] = cpu["blas_threads"]
+        res["cpu_baseline"] = cpu
+    print(json.dumps(res), flush=True)
+
+
+def bench_cascade(args, steps=None, warmup=None, cpu=True):
+    """The cascade-attention layer alone (256 anchors of U{512..2048} tokens x
+    64 suffixes of U{32..128} tokens, bf16 Q/K/V in HBM): its JSON line."""
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
+    import torch
+    import workloads as W
+    from query_aware_prefill_amd import binding as B
+
+    B.load()
+    log("generating the workload in HBM")
+    case = W.c1_device(seed=1)
+    a_len, s_anchor, s_len = case["a_len"], case["s_anchor"], case["s_len"]
+    T = int(case["s_off"][-1])
+    out = torch.empty((T, 32, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(B.quail_cascade_workspace_bytes(case["a_off"], case["s_off"]), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.quail_cascade_attn(B.DTYPE_BF16, 32, 8, 128, case["sm_scale"], case["ak"], case["av"],
+                             case["a_off"], s_anchor, case["q"], case["k"], case["v"], case["s_off"],
+                             out, None, ws, stream=stream)
+
+    log(f"cascade: warmup {warmup}")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    log(f"cascade: timing {steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms_step = el * 1000.0 / steps
+    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    logical = float(np.sum(a_len[s_anchor] + s_len))
+    computed = float(np.sum(s_len))
+    cross, self_ = algorithmic_flops(a_len, s_anchor, s_len)
+    flops = cross + self_
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    value = logical / (ms_step * 1e-3) * 60.0
+    log(f"step {ms_step:.3f} ms, launch {kernel_ms:.3f} ms, {achieved:.1f} TFLOP/s")
+
+    cpu = None
+    if cpu and not args.no_cpu_baseline:
+        log("oracle CPU baseline")
+        cpu = cpu_baseline(case, args.cpu_budget)
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/min",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "cascade-attention layer, Qwen3-4B shape: 256 anchors of U{512..2048} tokens x 64 "
+                        "suffixes of U{32..128} tokens each, 32q/8kv heads x 128, bf16, N(0,1) Q/K/V",
+            "anchors": 256, "suffixes": int(len(s_len)), "anchor_tokens": int(np.sum(a_len)),
+            "suffix_tokens": int(computed), "logical_tokens_per_step": int(logical),
+            "computed_tokens_per_min": computed / (ms_step * 1e-3) * 60.0,
+            "cascade_tflops": achieved,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
+            "kernel": "quail::attn_direct_kernel<4, false, false, false, false>", "flops_per_launch": flops,
+            "launch_ms": kernel_ms,
+            "algorithmic_bytes_per_launch": algorithmic_bytes(a_len, s_len),
+        },
+        "cpu_baseline": cpu,
+    }
+    del case, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -856,10 +1118,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--workload", choices=["cascade", "gemm", "layer", "copy", "stream", "join36",
+    ap.add_argument("--workload", choices=["join", "cascade", "gemm", "layer", "copy", "stream", "join36",
                                            "filter36", "multijoin36", "multijoin36full", "multiplan36", "shared36",
                                            "traces36", "nested36", "search"],
-                    default="cascade")
+                    default="join")
     ap.add_argument("--rows", type=int, default=625, help="multijoin36: rows of the 5,000 used")
     ap.add_argument("--shared-only", action="store_true", help="shared36: run only the join with prefix nodes")
     args = ap.parse_args()
@@ -890,88 +1152,11 @@ def main():
     if args.workload in ("join36", "filter36", "multijoin36"):
         return bench_e2e(args)
 
-    import torch
-    import workloads as W
-    from query_aware_prefill_amd import binding as B
-
-    B.load()
-    log("generating the workload in HBM")
-    case = W.c1_device(seed=1)
-    a_len, s_anchor, s_len = case["a_len"], case["s_anchor"], case["s_len"]
-    T = int(case["s_off"][-1])
-    out = torch.empty((T, 32, 128), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(B.quail_cascade_workspace_bytes(case["a_off"], case["s_off"]), dtype=torch.uint8,
-                     device="cuda")
-    stream = torch.cuda.current_stream()
-
-    def step():
-        B.quail_cascade_attn(B.DTYPE_BF16, 32, 8, 128, case["sm_scale"], case["ak"], case["av"],
-                             case["a_off"], s_anchor, case["q"], case["k"], case["v"], case["s_off"],
-                             out, None, ws, stream=stream)
-
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    ms_step = el * 1000.0 / args.steps
-    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-
-    logical = float(np.sum(a_len[s_anchor] + s_len))
-    computed = float(np.sum(s_len))
-    cross, self_ = algorithmic_flops(a_len, s_anchor, s_len)
-    flops = cross + self_
-    achieved = flops / (kernel_ms * 1e-3) / 1e12
-    value = logical / (ms_step * 1e-3) * 60.0
-    log(f"step {ms_step:.3f} ms, launch {kernel_ms:.3f} ms, {achieved:.1f} TFLOP/s")
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("oracle CPU baseline")
-        cpu = cpu_baseline(case, args.cpu_budget)
-
-    res = {
-        "metric": METRIC,
-        "value": value,
-        "unit": "tokens/min",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {
-            "workload": "cascade-attention layer, Qwen3-4B shape: 256 anchors of U{512..2048} tokens x 64 "
-                        "suffixes of U{32..128} tokens each, 32q/8kv heads x 128, bf16, N(0,1) Q/K/V",
-            "anchors": 256, "suffixes": int(len(s_len)), "anchor_tokens": int(np.sum(a_len)),
-            "suffix_tokens": int(computed), "logical_tokens_per_step": int(logical),
-            "computed_tokens_per_min": computed / (ms_step * 1e-3) * 60.0,
-            "cascade_tflops": achieved,
-            "parallelism": "single GPU",
-        },
-        "roofline": {
-            "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
-            "kernel": "quail::attn_direct_kernel<4, false, false, false, false>", "flops_per_launch": flops,
-            "launch_ms": kernel_ms,
-            "algorithmic_bytes_per_launch": algorithmic_bytes(a_len, s_len),
-        },
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(res), flush=True)
+    if args.workload == "cascade":
+        res = bench_cascade(args)
+        print(json.dumps(res), flush=True)
+        return
+    return bench_join(args)
 
 
 if __name__ == "__main__":
