@@ -99,20 +99,23 @@ def log(*a):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cascade_attn_c1_hbm_traffic.txt")
 KERNEL_SOURCES = ["query_aware_prefill_amd/csrc/attn.hip", "query_aware_prefill_amd/csrc/device_common.h",
                   "query_aware_prefill_amd/csrc/quail_internal.h"]
+GEMM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_join36_hbm_traffic.txt")
+GEMM_SOURCES = ["query_aware_prefill_amd/csrc/gemm.hip", "query_aware_prefill_amd/csrc/device_common.h",
+                "query_aware_prefill_amd/csrc/quail_internal.h"]
 
 
-def measured_traffic():
-    """HBM bytes per launch from the committed counter summary, or None when
+def measured_traffic(path=TRAFFIC_FILE, sources=KERNEL_SOURCES):
+    """HBM bytes per launch from a committed counter summary, or None when
     the kernel sources have changed since the counters were taken."""
     import hashlib
     try:
         kv = {}
-        for line in open(TRAFFIC_FILE):
+        for line in open(path):
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
         h = hashlib.sha256()
-        for f in KERNEL_SOURCES:
+        for f in sources:
             h.update(open(os.path.join(ROOT, f), "rb").read())
         if h.hexdigest() != kv.get("kernel_sources_sha256"):
             return None
@@ -986,8 +989,9 @@ def bench_join(args):
         },
         "roofline": {
             "bound": "mfma", "achieved": gu_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": gu_tf / PEAK_BF16_TFLOPS, "traffic": None,
-            "kernel": "quail::gemm_direct_kernel<(quail::GemmEpi)2, 256, 256, 4, 2> (gate/up + SwiGLU)",
+            "frac": gu_tf / PEAK_BF16_TFLOPS, "traffic": measured_traffic(GEMM_TRAFFIC_FILE, GEMM_SOURCES),
+            "kernel": "quail::gemm_direct_kernel<2, 256, 256, 4, 2>",
+            "what": "gate/up projection (W8A16 GEMM, 19456 x 2560) with the SwiGLU epilogue",
             "flops_per_launch": gu_flop, "launch_ms": gu_ms, "launches": gu["launches"],
             "tokens_per_launch": tokens_per_launch,
             "algorithmic_bytes_per_launch": 2 * shape.intermediate * shape.hidden
@@ -996,11 +1000,12 @@ def bench_join(args):
         "cpu_baseline": None,
     }
     # the cascade-attention headline configuration, timed on its own
-    c1 = bench_cascade(args, steps=5, warmup=2, cpu=False)
-    res["config"]["cascade_attention_layer"] = {
-        "workload": c1["config"]["workload"], "tflops": c1["roofline"]["achieved"],
-        "frac": c1["roofline"]["frac"], "launch_ms": c1["roofline"]["launch_ms"],
-        "kernel": c1["roofline"]["kernel"]}
+    if not args.no_cascade:
+        c1 = bench_cascade(args, steps=5, warmup=2, cpu=False)
+        res["config"]["cascade_attention_layer"] = {
+            "workload": c1["config"]["workload"], "tflops": c1["roofline"]["achieved"],
+            "frac": c1["roofline"]["frac"], "launch_ms": c1["roofline"]["launch_ms"],
+            "kernel": c1["roofline"]["kernel"], "traffic": c1["roofline"]["traffic"]}
     if not args.no_cpu_baseline:
         lg = logits.cpu().numpy().astype(np.float64)
         at, ao, pa, st_, so, a0, p0 = inputs[args.warmup + args.steps - 1]
@@ -1117,6 +1122,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cascade", action="store_true",
+                    help="join: skip the separately timed cascade-attention layer (profiling runs)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--workload", choices=["join", "cascade", "gemm", "layer", "copy", "stream", "join36",
                                            "filter36", "multijoin36", "multijoin36full", "multiplan36", "shared36",

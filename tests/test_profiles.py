@@ -55,7 +55,7 @@ def test_every_summary_names_existing_kernels_and_its_command():
 
 def test_roofline_kernel_is_in_the_library():
     src = open(os.path.join(ROOT, "bench.py")).read()
-    names = re.findall(r'"(quail::attn_direct_kernel<[^"]*>)"', src)
+    names = re.findall(r'"(quail::(?:attn|gemm)_direct_kernel<[^"]*>)"', src)
     assert names
     have = _kernel_names()
     for n in names:
