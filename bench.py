@@ -44,8 +44,8 @@ Secondary measurements (not the headline line; each prints its own JSON):
                      4 GiB): the calibration kernel for the HBM byte counters.
   --workload stream  anchor-KV streaming sweep: 1024 anchors of 768 tokens
                      (K/V of one layer: bf16, 3.2 GB, or E4M3 codes, 1.6 GB),
-                     each read by one suffix of S tokens, S in {1, 4, 16, 64,
-                     256}; anchor KV bytes per launch / launch time against
+                     each read by one suffix of S tokens, S in {1, 4, 16, 32,
+                     64, 256, 4096}; anchor KV bytes per launch / launch time against
                      8 TB/s, and TFLOP/s (4*S FLOP per bf16 KV byte, 8*S per
                      E4M3 byte).
   --workload join36 | filter36 | multijoin36
@@ -249,7 +249,7 @@ def bench_stream(args):
     out = {"metric": "anchor-KV streaming (cascade attention)", "unit": "GB/s",
            "peak_GBs": HBM_PEAK_GBS, "anchors": 1024, "anchor_len": 768, "points": []}
     for kv, dtype, esz in (("bf16", B.DTYPE_BF16, 2), ("e4m3", B.DTYPE_FP8_E4M3, 1)):
-        for S in (1, 4, 16, 64, 256):
+        for S in (1, 4, 16, 32, 64, 256, 4096):
             a_len, s_anchor, s_len = W.stream_lengths(S)
             case = W.cascade_device(7, a_len, s_anchor, s_len, anchor_kv=kv)
             T = int(case["s_off"][-1])
@@ -1103,7 +1103,7 @@ def bench_cascade(args, steps=None, warmup=None, cpu=True):
         "roofline": {
             "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
-            "kernel": "quail::attn_direct_kernel<4, false, false, false, false>", "flops_per_launch": flops,
+            "kernel": "quail::attn_direct_kernel<4, false, false, 0, false>", "flops_per_launch": flops,
             "launch_ms": kernel_ms,
             "algorithmic_bytes_per_launch": algorithmic_bytes(a_len, s_len),
         },

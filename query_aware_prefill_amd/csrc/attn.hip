@@ -427,6 +427,9 @@ struct TileCopy {
     dst = dst_;
   }
   __device__ __forceinline__ void issue_all(int wave, int lane) const {
+    // every wave copies at least one 1-KB slice (E4M3 tiles have 32 or 64
+    // keys; the 16-key quarter tiles are bf16 only)
+    static_assert(ROWS / 4 / NW >= 1 && (ROWS < 32 || ROWS / 8 / NW >= 1), "copy split");
     if (!fp8) {
       constexpr int PER = ROWS / 4 / NW;
 #pragma unroll
@@ -593,10 +596,14 @@ struct WaveAttn {
   // cross tile, [lo_self, hi_self] for a self tile -- never past the tile's
   // NK keys when a self tile has NK = 16; register i of half kb holds key
   // kbase + kb*32 + 16*(i/8) + 8*hi + i%8 (unsigned range test)
+  // A row's range is empty (hk < lo) when a 16-key self tile lies wholly
+  // before the row's segment (packed tiles of several waves span more than
+  // one such tile); the unsigned test alone would wrap there.
   template <int NKS = kKeyTile>
   __device__ __forceinline__ void mask(f32x16_t (&s)[2], int kbase, bool cross, int cross_len) const {
     const int lo = cross ? 0 : lo_self;
     const int hk = cross ? cross_len - 1 : (NKS < 32 ? min(hi_self, kbase + NKS - 1) : hi_self);
+    const bool any = hk >= lo;
     const uint32_t range = (uint32_t)(hk - lo);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -604,7 +611,7 @@ struct WaveAttn {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const uint32_t c = (uint32_t)(16 * (r >> 3) + (r & 7));
-        s[kb][r] = (x + c <= range) ? s[kb][r] : -INFINITY;
+        s[kb][r] = (any && x + c <= range) ? s[kb][r] : -INFINITY;
       }
     }
   }
@@ -764,14 +771,15 @@ __device__ __forceinline__ void publish_keep() {
 // that no MFMA accumulator crosses a runtime branch: full cross tiles, the
 // remaining (ragged) cross tiles, the cross -> self transition, self tiles.
 // One workgroup: the G query heads of one kv head x (waves / G) groups of 32
-// query tokens, all sharing every K/V tile copied into LDS. PACK (launches
-// whose anchors have few query tokens, where K/V streaming is the work): one
-// wave whose 32 rows are the G heads x 32/G tokens, so that every K/V tile
-// feeds 32 useful rows instead of 32 per head.
-template <int G, bool FC, bool FS, bool PACK, bool L2>
-__global__ void __launch_bounds__(PACK ? 64 : 64 * (G >= 4 ? G : 4), 2)
+// query tokens, all sharing every K/V tile copied into LDS. PACK > 0
+// (launches whose anchors have few query tokens, where K/V streaming is the
+// work): PACK waves, each of whose 32 rows are the G heads x 32/G tokens of
+// its share of the tile (wave w holds tokens w*32/G .. (w+1)*32/G - 1), so
+// that every K/V tile feeds rows that exist instead of 32 per head.
+template <int G, bool FC, bool FS, int PACK, bool L2>
+__global__ void __launch_bounds__(PACK ? 64 * PACK : 64 * (G >= 4 ? G : 4), 2)
 attn_direct_kernel(AttnParams p) {
-  constexpr int NW = PACK ? 1 : (G >= 4 ? G : 4);
+  constexpr int NW = PACK ? PACK : (G >= 4 ? G : 4);
   // Packed launches use 8-KB slots, 40 KB per workgroup, four workgroups per
   // CU: an E4M3 tile of 64 keys is 8 KB, and bf16 tiles are half tiles of 32
   // keys, whose second 32-key half of the scores is -inf. With E4M3 cross
@@ -797,7 +805,7 @@ attn_direct_kernel(AttnParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int head = PACK ? g * G + (lane & 31) / (kQRows / G) : g * G + (wave % G);
-  const int qrow = PACK ? (lane & 31) % (kQRows / G) : (wave / G) * kQRows + (lane & 31);
+  const int qrow = PACK ? wave * (kQRows / G) + (lane & 31) % (kQRows / G) : (wave / G) * kQRows + (lane & 31);
   const bool row_ok = qrow < tile.nq;
   const int64_t tok = (int64_t)tile.q0 + qrow;
 
@@ -812,11 +820,11 @@ attn_direct_kernel(AttnParams p) {
   // (packed launches stream each anchor's K/V once per kv head: non-temporal)
   auto issue = [&](int j, int ks, int vs) __attribute__((always_inline)) {
     if (NKC == NKS || j < ts.n_ct) {
-      TileCopy<NW, false, NKC, PACK>(ts.src(j), g, ts.kbase(j), lds_k0 + ks * kSlotBytes).issue_all(wave, lane);
-      TileCopy<NW, true, NKC, PACK>(ts.src(j), g, ts.kbase(j), lds_v0 + vs * kSlotBytes).issue_all(wave, lane);
+      TileCopy<NW, false, NKC, (PACK > 0)>(ts.src(j), g, ts.kbase(j), lds_k0 + ks * kSlotBytes).issue_all(wave, lane);
+      TileCopy<NW, true, NKC, (PACK > 0)>(ts.src(j), g, ts.kbase(j), lds_v0 + vs * kSlotBytes).issue_all(wave, lane);
     } else {
-      TileCopy<NW, false, NKS, PACK>(ts.src(j), g, ts.kbase(j), lds_k0 + ks * kSlotBytes).issue_all(wave, lane);
-      TileCopy<NW, true, NKS, PACK>(ts.src(j), g, ts.kbase(j), lds_v0 + vs * kSlotBytes).issue_all(wave, lane);
+      TileCopy<NW, false, NKS, (PACK > 0)>(ts.src(j), g, ts.kbase(j), lds_k0 + ks * kSlotBytes).issue_all(wave, lane);
+      TileCopy<NW, true, NKS, (PACK > 0)>(ts.src(j), g, ts.kbase(j), lds_v0 + vs * kSlotBytes).issue_all(wave, lane);
     }
   };
   issue(0, 0, 0);
@@ -884,11 +892,21 @@ attn_direct_kernel(AttnParams p) {
   w.store(p, tok, row_ok, head);
 }
 
-// query tokens per tile: unpacked (both the direct and the register-staged
-// kernel), max(G, 4) waves of G heads x (waves / G) groups of 32 tokens;
-// packed, one wave of G heads x 32/G tokens
-int attn_tile_tokens(int group, bool packed) {
-  return packed ? kQRows / group : kQRows * (group >= 4 ? group : 4) / group;
+// query tokens per tile: unpacked (pack 0; both the direct and the
+// register-staged kernel), max(G, 4) waves of G heads x (waves / G) groups of
+// 32 tokens; packed, `pack` waves of G heads x 32/G tokens
+int attn_tile_tokens(int group, int pack) {
+  return pack ? pack * (kQRows / group) : kQRows * (group >= 4 ? group : 4) / group;
+}
+
+// the packed width for launches whose runs of queries sharing an anchor have
+// at most max_run tokens: the fewest waves (1, 2 or 4) whose rows hold them,
+// or 0 (unpacked tiles) when more than four waves' worth, or when the
+// unpacked tile has no more tokens than that packed one
+int attn_pack_waves(int group, int max_run) {
+  for (int w = 1; w <= 4; w *= 2)
+    if (max_run <= w * (kQRows / group)) return w * (kQRows / group) < attn_tile_tokens(group, 0) ? w : 0;
+  return 0;
 }
 
 bool attn_direct_ok(bool fp8_cross, bool fp8_self, float k_scale, float v_scale) {
@@ -898,20 +916,20 @@ bool attn_direct_ok(bool fp8_cross, bool fp8_self, float k_scale, float v_scale)
   return !(fp8_cross || fp8_self) || (k_scale == 1.0f && v_scale == 1.0f);
 }
 
-template <bool FC, bool FS, bool PACK, bool L2>
+template <bool FC, bool FS, int PACK, bool L2>
 static hipError_t launch_direct(const AttnParams& p, int group, dim3 gr, hipStream_t s) {
-  const dim3 blk(PACK ? 64 : 256);
+  const dim3 blk(PACK ? 64 * PACK : 256);
   switch (group) {
     case 1: attn_direct_kernel<1, FC, FS, PACK, L2><<<gr, blk, 0, s>>>(p); break;
     case 2: attn_direct_kernel<2, FC, FS, PACK, L2><<<gr, blk, 0, s>>>(p); break;
     case 4: attn_direct_kernel<4, FC, FS, PACK, L2><<<gr, blk, 0, s>>>(p); break;
-    case 8: attn_direct_kernel<8, FC, FS, PACK, L2><<<gr, dim3(PACK ? 64 : 512), 0, s>>>(p); break;
+    case 8: attn_direct_kernel<8, FC, FS, PACK, L2><<<gr, dim3(PACK ? 64 * PACK : 512), 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <bool PACK, bool L2>
+template <int PACK, bool L2>
 static hipError_t launch_direct_fmt(const AttnParams& p, int group, bool fp8_cross, bool fp8_self,
                                     dim3 gr, hipStream_t s) {
   if (fp8_cross && fp8_self) return launch_direct<true, true, PACK, L2>(p, group, gr, s);
@@ -920,7 +938,19 @@ static hipError_t launch_direct_fmt(const AttnParams& p, int group, bool fp8_cro
   return launch_direct<false, false, PACK, L2>(p, group, gr, s);
 }
 
-hipError_t launch_attn_bf16(const AttnParams& p, int group, bool fp8_cross, bool fp8_self, bool packed,
+template <bool L2>
+static hipError_t launch_direct_pack(const AttnParams& p, int group, bool fp8_cross, bool fp8_self, int pack,
+                                     dim3 gr, hipStream_t s) {
+  switch (pack) {
+    case 0: return launch_direct_fmt<0, L2>(p, group, fp8_cross, fp8_self, gr, s);
+    case 1: return launch_direct_fmt<1, L2>(p, group, fp8_cross, fp8_self, gr, s);
+    case 2: return launch_direct_fmt<2, L2>(p, group, fp8_cross, fp8_self, gr, s);
+    case 4: return launch_direct_fmt<4, L2>(p, group, fp8_cross, fp8_self, gr, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attn_bf16(const AttnParams& p, int group, bool fp8_cross, bool fp8_self, int pack,
                             hipStream_t s) {
   if (p.n_tiles == 0) return hipSuccess;
   const int64_t total = (int64_t)p.n_tiles * p.hkv;
@@ -928,13 +958,10 @@ hipError_t launch_attn_bf16(const AttnParams& p, int group, bool fp8_cross, bool
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 gr((unsigned)grid);
   const bool direct = attn_direct_ok(fp8_cross, fp8_self, p.k_scale, p.v_scale);
-  if (packed && !direct) return hipErrorInvalidValue;      // packed tiles need the direct kernel
+  if (pack && !direct) return hipErrorInvalidValue;      // packed tiles need the direct kernel
   if (direct) {
-    if (p.two_level)
-      return packed ? launch_direct_fmt<true, true>(p, group, fp8_cross, fp8_self, gr, s)
-                    : launch_direct_fmt<false, true>(p, group, fp8_cross, fp8_self, gr, s);
-    return packed ? launch_direct_fmt<true, false>(p, group, fp8_cross, fp8_self, gr, s)
-                  : launch_direct_fmt<false, false>(p, group, fp8_cross, fp8_self, gr, s);
+    if (p.two_level) return launch_direct_pack<true>(p, group, fp8_cross, fp8_self, pack, gr, s);
+    return launch_direct_pack<false>(p, group, fp8_cross, fp8_self, pack, gr, s);
   }
   switch (group) {
     case 1: attn_bf16_kernel<1><<<gr, dim3(256), 0, s>>>(p); break;

@@ -704,7 +704,7 @@ struct Batch {
   bool anchor_mode = false;
   bool has_parent = false;                  // anchor_mode: prefix nodes (cross = their anchor's slab)
   bool two_level = false;                   // some tile reads a prefix node as cross2
-  bool packed = false;                      // attention tiles are packed (one wave each)
+  int pack = 0;                             // packed attention tiles: waves per tile (0 = unpacked)
   int32_t n_tok = 0;
   std::vector<int32_t> tok_src, pos, seg_lo, kv_lapad;
   std::vector<int64_t> kv_row;
@@ -819,7 +819,7 @@ quail_status run_batch(quail_ctx* c, const Batch& b, const int32_t* tokens, uint
     const bool slab_fp8 = cf.kv_dtype == QUAIL_DTYPE_FP8_E4M3;
     TIMED(PK_ATTN, attn_flop,
           launch_attn_bf16(ap, G, (!b.anchor_mode || b.has_parent) && slab_fp8, b.anchor_mode && slab_fp8,
-                           b.packed, s));
+                           b.pack, s));
 
     GemmParams go{};
     go.A = obuf; go.lda = (int64_t)Hq * kHeadDim; go.B = lw.w_o; go.scale = lw.s_o;
@@ -1026,9 +1026,9 @@ quail_status anchor_core(quail_ctx* c, int32_t n, const int32_t* tokens, const i
     // packed tiles when every anchor is that short (see attn_tile_tokens)
     b.has_parent = false;
     for (int32_t a = a0; a < a1 && parents; ++a) b.has_parent |= n_uses[a] > 0 && parents[a] >= 0;
-    b.packed = max_len <= attn_tile_tokens(G, true) &&
-               attn_direct_ok(b.has_parent && slab_fp8, slab_fp8, cf.k_scale, cf.v_scale);
-    const int TQ = attn_tile_tokens(G, b.packed);
+    b.pack = attn_direct_ok(b.has_parent && slab_fp8, slab_fp8, cf.k_scale, cf.v_scale)
+                 ? attn_pack_waves(G, max_len) : 0;
+    const int TQ = attn_tile_tokens(G, b.pack);
     std::unordered_map<int32_t, int32_t> parent_src;
     for (int32_t a = a0; a < a1; ++a) {
       if (n_uses[a] == 0) continue;
@@ -1584,9 +1584,8 @@ quail_status join_core(quail_ctx* c, int32_t n, const quail_anchor* ha, const in
       max_group = std::max(max_group, gtok);
       i = j;
     }
-    b.packed = max_group <= attn_tile_tokens(G, true) &&
-               attn_direct_ok(slab_fp8, false, cf.k_scale, cf.v_scale);
-    const int TQ = attn_tile_tokens(G, b.packed);
+    b.pack = attn_direct_ok(slab_fp8, false, cf.k_scale, cf.v_scale) ? attn_pack_waves(G, max_group) : 0;
+    const int TQ = attn_tile_tokens(G, b.pack);
     // source 0: this batch's suffix K/V (token-major, reused every layer)
     KVSrc self{};
     self.k = ws_ptr<uint16_t>(c, c->L.k);
@@ -2325,8 +2324,8 @@ quail_status cascade_core(int32_t dtype, int32_t hq, int32_t hkv, int32_t d, flo
     max_group = std::max(max_group, s_off[s1] - s_off[s0]);
     s0 = s1;
   }
-  const bool packed = max_group <= attn_tile_tokens(G, true);
-  const int TQ = attn_tile_tokens(G, packed);
+  const int pack = attn_pack_waves(G, max_group);
+  const int TQ = attn_tile_tokens(G, pack);
   std::vector<AttnTile> tiles;
   int32_t s0 = 0;
   while (s0 < n_suffix) {
@@ -2357,7 +2356,7 @@ quail_status cascade_core(int32_t dtype, int32_t hq, int32_t hkv, int32_t d, flo
   p.lse = lse; p.hq = hq; p.hkv = hkv;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
   p.k_scale = 1.0f; p.v_scale = 1.0f;
-  HIP_TRY(launch_attn_bf16(p, G, a_fp8, false, packed, st));
+  HIP_TRY(launch_attn_bf16(p, G, a_fp8, false, pack, st));
   return QUAIL_OK;
 }
 

@@ -121,14 +121,18 @@ struct Head8Params {
 // fp8_cross / fp8_self: the cross (anchor) / self key sources of this launch
 // hold E4M3 codes. With unit k/v scales every combination runs the direct
 // HBM->LDS kernel; other scales take the register-staged kernel.
-// packed: tiles of attn_tile_tokens(group, true) tokens, one wave each
-// (G heads x 32/G tokens in its 32 rows); requires the direct kernel.
-hipError_t launch_attn_bf16(const AttnParams& p, int group, bool fp8_cross, bool fp8_self, bool packed,
+// pack > 0: packed tiles of attn_tile_tokens(group, pack) tokens, `pack`
+// waves each of G heads x 32/G tokens in its 32 rows (attn_pack_waves picks
+// it); requires the direct kernel. pack 0: unpacked tiles.
+hipError_t launch_attn_bf16(const AttnParams& p, int group, bool fp8_cross, bool fp8_self, int pack,
                             hipStream_t s);
 // whether a launch with these formats and scales runs the direct kernel
 bool attn_direct_ok(bool fp8_cross, bool fp8_self, float k_scale, float v_scale);
 // query tokens per attention tile (one workgroup) for GQA group size `group`
-int attn_tile_tokens(int group, bool packed);
+int attn_tile_tokens(int group, int pack);
+// packed width (1, 2 or 4 waves; 0 = unpacked) for runs of at most max_run
+// query tokens per anchor
+int attn_pack_waves(int group, int max_run);
 hipError_t launch_attn_f32(const AttnF32Params& p, hipStream_t s);
 hipError_t launch_gemm(const GemmParams& p, GemmEpi epi, hipStream_t s);
 hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s);

@@ -184,6 +184,13 @@ PACKED_CASES = [
     ([768, 200], [0, 1, 1], [2, 1, 3], 32, 4),                     # G = 8: 4 tokens
     ([100, 64], [0, 0, 1], [7, 9, 16], 8, 4),                      # G = 2: 16 tokens
     ([33], [0, 0, -1], [20, 12, 32], 4, 4),                        # G = 1: 32 tokens
+    # several waves per tile (each G heads x 32/G tokens, sharing the K/V tiles)
+    ([300, 77], [0, 0, 1, -1], [9, 7, 16, 3], 32, 8),              # G = 4, 2 waves: 16 tokens
+    ([130, 64, 1], [0, 1, 2], [12, 11, 5], 32, 8),                 # G = 4, 2 waves, ragged tiles
+    ([500, 70], [0, 0, 1], [6, 10, 3], 32, 4),                     # G = 8, 4 waves: 16 tokens
+    ([257], [0, -1], [7, 2], 32, 4),                               # G = 8, 2 waves: 8 tokens
+    ([90, 40], [0, 1, 1], [29, 20, 12], 8, 4),                     # G = 2, 2 waves: 32 tokens
+    ([65, 200], [0, 1, -1], [50, 33, 64], 4, 4),                   # G = 1, 2 waves: 64 tokens
 ]
 
 
@@ -319,7 +326,7 @@ def test_c1_full_size_sampled(B):
     say("  largest step outside the visible value range", worst)
 
 
-@pytest.mark.parametrize("S", [1, 4, 64])
+@pytest.mark.parametrize("S", [1, 4, 16, 32, 64])
 @pytest.mark.parametrize("kv", ["bf16", "e4m3"])
 def test_stream_full_size_sampled(B, kv, S):
     """The anchor-KV streaming workload at full size, as the benchmark's

@@ -576,3 +576,37 @@ def test_overwritten_guard_is_detected(B):
     chk = B.quail_ctx_check(ctx)
     assert chk == {"guard_errors": 1, "bad_tokens": 0}, chk
     ctx.expect_counts = {"guard_errors": 2, "bad_tokens": 0}   # checked again at teardown
+
+
+@pytest.mark.parametrize("kv_fp8", [False, True])
+def test_join_with_packed_multiwave_tiles(B, kv_fp8):
+    """Pairs so short that every anchor's run of query tokens in a batch fits
+    two waves of packed rows (G = 2: 16 tokens per wave; runs of 17-32 tokens),
+    so the join's attention runs packed tiles of two waves, with several
+    16-key self tiles per tile when the slabs are E4M3: logits and decisions
+    against the oracle."""
+    import torch
+    shape = W.tiny_shape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                         intermediate=384, vocab=512, kv_fp8=kv_fp8)
+    a_len = [40, 97, 3]
+    pairs = [(0, 20), (0, 12), (1, 9), (1, 8), (1, 11), (2, 30), (-1, 7)]
+    wts, case, dm, ctx, a_tok, s_tok = _setup(shape, 26, a_len, pairs, B)
+    n = len(pairs)
+    logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+    dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+    say("packed multi-wave join", "fp8" if kv_fp8 else "bf16")
+    B.quail_join_run(ctx, a_tok, case["a_off"], case["pair_anchor"], s_tok, case["s_off"], 0x0F,
+                     logits, None, dec)
+    torch.cuda.synchronize()
+    ref = []
+    for i, (a, _) in enumerate(pairs):
+        at = case["a_tok"][case["a_off"][a]:case["a_off"][a + 1]] if a >= 0 else []
+        ref.append(OM.forward_pair(at, case["s_tok"][case["s_off"][i]:case["s_off"][i + 1]], wts, shape))
+    ref_logits = np.array([r["logits"] for r in ref])
+    lg = logits.cpu().numpy()
+    for i in range(n):
+        assert rel_inf(lg[i], ref_logits[i]) <= 2e-2 * np.max(np.abs(ref_logits)) / np.max(np.abs(ref_logits[i])), i
+    assert rel_inf(lg, ref_logits) <= 2e-2
+    ok, _ = decisions_agree(dec.cpu().numpy(), [r["decision"] for r in ref], [r["margin"] for r in ref],
+                            2e-2 * np.max(np.abs(ref_logits)))
+    assert ok
