@@ -34,6 +34,16 @@
 
 namespace quail {
 
+// A wave-uniform value as an opaque register operand: a choice among
+// members of one object, made on such values, cannot be folded into a load
+// through a chosen member address (which would keep the object in scratch
+// memory instead of registers).
+template <typename T>
+__device__ __forceinline__ T in_sreg(T x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
 constexpr int KSTR = kHeadDim + 8;   // K tile row stride in LDS (u16): 272 B
 constexpr int VSTR = kKeyTile + 4;   // V^T tile row stride in LDS (u16): 136 B
 
@@ -200,15 +210,20 @@ attn_bf16_kernel(AttnParams p) {
 
   auto view = [&](int it) {
     TileView t;
-    const KVSrc& s = it < n_c1 ? cs : (it < n_ct ? cs2 : ss);
-    const int esz = s.fp8 ? 1 : 2;
-    t.k = reinterpret_cast<const uint8_t*>(s.k) + (int64_t)g * s.head_stride * esz;
-    t.v = reinterpret_cast<const uint8_t*>(s.v) + (int64_t)g * s.head_stride * esz;
-    t.tok_bytes = s.tok_stride * esz;
-    t.kbase = it < n_c1 ? it * kKeyTile
-                        : (it < n_ct ? (it - n_c1) * kKeyTile : tile.self_k0 + (it - n_ct) * kKeyTile);
-    t.len = s.len;
-    t.fp8 = s.fp8;
+    // the source's fields, chosen among register values (in_sreg)
+    const bool a = it < n_c1, b = it < n_ct;
+    const int fp8 = a ? in_sreg(cs.fp8) : (b ? in_sreg(cs2.fp8) : in_sreg(ss.fp8));
+    const int64_t hs = a ? in_sreg(cs.head_stride) : (b ? in_sreg(cs2.head_stride) : in_sreg(ss.head_stride));
+    const int64_t ts = a ? in_sreg(cs.tok_stride) : (b ? in_sreg(cs2.tok_stride) : in_sreg(ss.tok_stride));
+    const void* kp = a ? in_sreg(cs.k) : (b ? in_sreg(cs2.k) : in_sreg(ss.k));
+    const void* vp = a ? in_sreg(cs.v) : (b ? in_sreg(cs2.v) : in_sreg(ss.v));
+    const int esz = fp8 ? 1 : 2;
+    t.k = reinterpret_cast<const uint8_t*>(kp) + (int64_t)g * hs * esz;
+    t.v = reinterpret_cast<const uint8_t*>(vp) + (int64_t)g * hs * esz;
+    t.tok_bytes = ts * esz;
+    t.kbase = a ? it * kKeyTile : (b ? (it - n_c1) * kKeyTile : tile.self_k0 + (it - n_ct) * kKeyTile);
+    t.len = a ? in_sreg(cs.len) : (b ? in_sreg(cs2.len) : in_sreg(ss.len));
+    t.fp8 = fp8;
     return t;
   };
 
@@ -225,10 +240,10 @@ attn_bf16_kernel(AttnParams p) {
 
   for (int it = 0; it < n_tiles; ++it) {
     const bool is_cross = it < n_ct;
-    const int fp8 = is_cross ? cs.fp8 : ss.fp8;   // both cross levels are slabs of one format
+    const int fp8 = is_cross ? in_sreg(cs.fp8) : in_sreg(ss.fp8);   // both cross levels: slabs of one format
     const int kbase = it < n_c1 ? it * kKeyTile
                                 : (is_cross ? (it - n_c1) * kKeyTile : tile.self_k0 + (it - n_ct) * kKeyTile);
-    const int clen = it < n_c1 ? cs.len : cs2.len;
+    const int clen = it < n_c1 ? in_sreg(cs.len) : in_sreg(cs2.len);
     __syncthreads();
     store_tile<NT>(regs, fp8, p.k_scale, p.v_scale, Ks, Vt, tid);
     __syncthreads();
@@ -491,9 +506,21 @@ struct TileSeq {
     n_tiles = n_ct + n_st;
     self_k0 = tile.self_k0;
   }
-  __device__ __forceinline__ const KVSrc& src(int j) const {
-    if constexpr (!L2) return j < n_ct ? cs : ss;
-    else return j < n_c1 ? cs : (j < n_ct ? cs2 : ss);
+  // by value, field by field, choosing among register values (in_sreg)
+  __device__ __forceinline__ KVSrc src(int j) const {
+    if constexpr (!L2) {
+      return j < n_ct ? cs : ss;
+    } else {
+      const bool a = j < n_c1, b = j < n_ct;
+      KVSrc r;
+      r.k = a ? in_sreg(cs.k) : (b ? in_sreg(cs2.k) : in_sreg(ss.k));
+      r.v = a ? in_sreg(cs.v) : (b ? in_sreg(cs2.v) : in_sreg(ss.v));
+      r.tok_stride = a ? in_sreg(cs.tok_stride) : (b ? in_sreg(cs2.tok_stride) : in_sreg(ss.tok_stride));
+      r.head_stride = a ? in_sreg(cs.head_stride) : (b ? in_sreg(cs2.head_stride) : in_sreg(ss.head_stride));
+      r.len = a ? in_sreg(cs.len) : (b ? in_sreg(cs2.len) : in_sreg(ss.len));
+      r.fp8 = a ? in_sreg(cs.fp8) : (b ? in_sreg(cs2.fp8) : in_sreg(ss.fp8));
+      return r;
+    }
   }
   __device__ __forceinline__ int kbase(int j) const {
     if constexpr (!L2) return j < n_ct ? j * TKC : self_k0 + (j - n_ct) * TKS;
@@ -502,7 +529,7 @@ struct TileSeq {
   // valid keys of a cross tile's source
   __device__ __forceinline__ int clen(int j) const {
     if constexpr (!L2) return cs.len;
-    else return j < n_c1 ? cs.len : cs2.len;
+    else return j < n_c1 ? in_sreg(cs.len) : in_sreg(cs2.len);
   }
 };
 
