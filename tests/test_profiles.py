@@ -45,7 +45,7 @@ def _named(text):
 def test_every_summary_names_existing_kernels_and_its_command():
     assert SUMMARIES
     have = _kernel_names()
-    assert "quail::attn_direct_kernel<4, false, false, false, false>" in have
+    assert "quail::attn_direct_kernel<4, false, false, 0, false>" in have
     for path in SUMMARIES:
         text = open(path).read()
         missing = sorted(n for n in _named(text) if n not in have)
