@@ -1,11 +1,16 @@
 """GPU parity at full depth: the 36-layer Qwen3-4B-shaped stack (random
-init, fp8 weights) through quail_join_run, against the oracle's per-pair
-forward (float64, bf16 contract) stored in tests/golden/depth36_qwen3.json by
+init, fp8 weights) against the oracle's per-pair forward (float64, bf16
+contract) stored in tests/golden/depth36_qwen3.json by
 tests/golden/make_depth36.py.
 
-Two joins: three anchors of 17, 40 and 71 tokens with 22 suffixes of 2-12
-tokens each plus 6 filter rows, with bf16 anchor KV; two anchors of 33 and 90
-tokens with 14 suffixes each plus 2 filter rows, with E4M3 anchor KV. The
+Through quail_join_run, two joins: three anchors of 17, 40 and 71 tokens
+with 22 suffixes of 2-12 tokens each plus 6 filter rows, with bf16 anchor KV;
+two anchors of 33 and 90 tokens with 14 suffixes each plus 2 filter rows, with
+E4M3 anchor KV. Through quail_multijoin_run, three joins of 8 pairs over four
+anchors (E4M3 KV) in a pool for two anchors, so anchors are evicted and
+prefilled again between joins (counters against the plan). Through
+quail_join_run_shared, suffix families sharing 6-14 prefix tokens under two
+anchors and among filter rows (bf16 KV; prefix nodes prefilled once). The
 same weights run at depths 1, 4, 12 and 36 (the first d layers of the
 36-layer model), so the error's growth with depth is printed as well as
 checked. Bar at every depth: logits within 2e-2 (infinity-norm relative over
@@ -50,40 +55,67 @@ def setup():
     return B, dm, cases, doc, G
 
 
-def _run(B, dm, case, depth, fp8):
-    """quail_join_run on the first `depth` layers; returns logits, decisions."""
+def _run(B, dm, case, depth, fp8, run):
+    """The case through the first `depth` layers by entry point `run`
+    (quail_join_run, quail_multijoin_run with a pool for the two largest
+    anchors, or quail_join_run_shared); returns logits and decisions."""
     import torch
     from query_aware_prefill_amd.device import model_config, to_device
     shape = dataclasses.replace(W.QWEN3_4B, n_layers=depth, kv_fp8=fp8)
     cfg = model_config(shape, 128, 64)
-    pool_bytes = sum(B.quail_anchor_bytes(cfg, int(x)) for x in case["a_len"]) + 4096
+    slabs = sorted(B.quail_anchor_bytes(cfg, int(x)) for x in case["a_len"])
+    if run == "quail_multijoin_run":
+        pool_bytes = slabs[-1] + slabs[-2] + B.GUARD_BYTES      # forces evictions between joins
+    elif run == "quail_join_run_shared":
+        pool_bytes = sum(slabs) + 6 * B.quail_anchor_bytes(cfg, int(np.max(case["s_len"]))) + 4096
+    else:
+        pool_bytes = sum(slabs) + 4096
     pool = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda")
     ws = torch.empty(B.quail_workspace_bytes(cfg, 512), dtype=torch.uint8, device="cuda")
     ctx = B.Context(cfg, dm.weights, pool, ws, 512)
     n = len(case["pair_anchor"])
     logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
     dec = torch.empty(n, dtype=torch.uint8, device="cuda")
-    B.quail_join_run(ctx, to_device(case["a_tok"]), case["a_off"], case["pair_anchor"],
-                     to_device(case["s_tok"]), case["s_off"], 0x0F, logits, None, dec)
+    a_tok, s_tok = to_device(case["a_tok"]), to_device(case["s_tok"])
+    used = len({int(a) for a in case["pair_anchor"] if a >= 0})
+    if run == "quail_multijoin_run":
+        B.quail_multijoin_run(ctx, a_tok, case["a_off"], case["join_offsets"], case["pair_anchor"], s_tok,
+                              case["s_off"], 0x0F, logits, None, dec)
+    elif run == "quail_join_run_shared":
+        B.quail_join_run_shared(ctx, a_tok, case["a_off"], case["pair_anchor"], s_tok, case["s_off"],
+                                case["s_tok"], 4, 0x0F, logits, None, dec)
+    else:
+        B.quail_join_run(ctx, a_tok, case["a_off"], case["pair_anchor"], s_tok, case["s_off"], 0x0F, logits,
+                         None, dec)
     torch.cuda.synchronize()
     st = B.quail_pool_stats(ctx)
-    used = len({int(a) for a in case["pair_anchor"] if a >= 0})
-    assert st["prefills"] == used and st["evictions"] == used and st["regret_tokens"] == 0
+    if run == "quail_multijoin_run":
+        plan = B.quail_multiplan_build(cfg, pool_bytes - B.GUARD_BYTES, 512, case["a_len"], case["join_offsets"],
+                                       case["pair_anchor"], case["s_len"])
+        assert (st["prefills"], st["evictions"], st["regret_tokens"]) == \
+            (plan["prefills"], plan["evictions"], plan["regret_tokens"]), (st, plan)
+        assert plan["prefills"] > used          # the tight pool re-prefills some anchor
+    elif run == "quail_join_run_shared":
+        assert st["prefills"] > used and st["prefills"] == st["evictions"] and st["regret_tokens"] == 0
+    else:
+        assert st["prefills"] == used and st["evictions"] == used and st["regret_tokens"] == 0
+    assert st["resident"] == 0
     assert B.quail_ctx_check(ctx) == {"guard_errors": 0, "bad_tokens": 0}
     return logits.cpu().numpy().astype(np.float64), dec.cpu().numpy()
 
 
-@pytest.mark.parametrize("name", ["bf16", "e4m3"])
+@pytest.mark.parametrize("name", ["bf16", "e4m3", "multijoin_e4m3", "shared_bf16"])
 def test_full_depth_join_against_oracle(setup, name):
     B, dm, cases, doc, G = setup
     case = cases[name]
     fp8 = doc["cases"][name]["fp8_kv"]
+    run = doc["cases"][name]["run"]
     rows = []
     for depth in doc["taps"]:
         ref = doc["results"][name][str(depth)]
         ref_logits = np.array(ref["logits"])
         say(f"depth36 {name}: {depth} layers, {len(ref_logits)} pairs")
-        lg, dec = _run(B, dm, case, depth, fp8)
+        lg, dec = _run(B, dm, case, depth, fp8, run)
         err = float(np.max(np.abs(lg - ref_logits)) / np.max(np.abs(ref_logits)))
         tau = 2e-2 * float(np.max(np.abs(ref_logits)))
         sure = np.abs(np.array(ref["margin"])) > tau

@@ -42,7 +42,7 @@ __all__ = [
     "ModelShape", "QWEN3_4B", "tiny_shape", "bf16_bits_from_f32", "draw_bf16",
     "draw_fp8_codes", "model_weights", "cascade_case", "c0_case", "c1_case",
     "join_case", "filter_case", "c2_case", "c3a_case", "c3b_case", "c4_case",
-    "bf16_to_f32", "depth_case", "residual_std", "W_STD",
+    "bf16_to_f32", "depth_case", "depth_multijoin_case", "residual_std", "W_STD",
 ]
 
 
@@ -537,6 +537,21 @@ def depth_case(seed: int, a_len, per_anchor: int, n_filter: int, ls_range=(2, 12
                          r.integers(filter_range[0], filter_range[1] + 1, size=n_filter)])
     perm = r.permutation(len(pa))
     return join_case(seed, vocab, a_len, pa[perm], sl[perm].astype(np.int32), cfg_id=cfg_id)
+
+
+def depth_multijoin_case(seed: int, a_len, n_joins: int, per_join: int, ls_range=(2, 12),
+                         vocab: int = QWEN3_4B.vocab, cfg_id: int = 9) -> dict:
+    """Several joins over one anchor table for full-depth parity: join k has
+    ``per_join`` pairs, each naming a seeded random anchor (with repetition,
+    across and within joins) and suffix tokens of U{ls_range}. A join_case
+    dict plus ``join_offsets`` [n_joins + 1]."""
+    r = _rng(cfg_id, seed, 0, 0)
+    n = n_joins * per_join
+    pa = r.integers(0, len(a_len), size=n).astype(np.int32)
+    sl = r.integers(ls_range[0], ls_range[1] + 1, size=n).astype(np.int32)
+    case = join_case(seed, vocab, a_len, pa, sl, cfg_id=cfg_id)
+    case["join_offsets"] = (np.arange(n_joins + 1) * per_join).astype(np.int32)
+    return case
 
 
 def shared_prefix_case(seed: int, vocab: int, a_len, families, cfg_id: int = 6,
