@@ -23,6 +23,8 @@
 // Epilogues (fused so no extra pass touches HBM):
 //   STORE : y = bf16(acc * scale)
 //   RESID : h = h + acc * scale, h the fp32 residual     (O and down projections)
+//           (optionally gathered: A rows and residual rows through row maps,
+//           for the rows whose output is still needed)
 //   SWIGLU: m = bf16(silu(acc_gate * s_g) * acc_up * s_u)  (gate/up projection;
 //           a column tile holds 64 gate rows and the 64 matching up rows)
 //   QKV   : RoPE (rotate-half, table of cos/sin per position) on q and k heads,
@@ -213,7 +215,8 @@ __device__ __forceinline__ void epilogue_staged(const GemmParams& p, const f32x1
           const uint4 b = lds_read_b128(lds + r * 256 + (((2 * c8 + 1) ^ (r & 15)) << 4));
           const int mr = m_row0 + mb * 32 + r;
           if (mr >= p.M) continue;
-          float4* yp = reinterpret_cast<float4*>(p.Yf + (int64_t)mr * p.ldy + n_base + half * 64 + c8 * 8);
+          const int yr = p.y_map ? p.y_map[mr] : mr;
+          float4* yp = reinterpret_cast<float4*>(p.Yf + (int64_t)yr * p.ldy + n_base + half * 64 + c8 * 8);
           const float4 h0 = yp[0], h1 = yp[1];
           yp[0] = make_float4(__uint_as_float(a.x) + h0.x, __uint_as_float(a.y) + h0.y,
                               __uint_as_float(a.z) + h0.z, __uint_as_float(a.w) + h0.w);
@@ -346,7 +349,8 @@ gemm_direct_kernel(GemmParams p) {
   for (int i = 0; i < A_PW; ++i) {
     const int row = (wave * A_PW + i) * 8 + (lane >> 3);
     const int m = min(m0 + row, p.M - 1);
-    a_src[i] = reinterpret_cast<const uint8_t*>(p.A + (int64_t)m * p.lda) + swz_a(row, lane & 7) * 16;
+    const int ma = p.a_map ? p.a_map[m] : m;
+    a_src[i] = reinterpret_cast<const uint8_t*>(p.A + (int64_t)ma * p.lda) + swz_a(row, lane & 7) * 16;
   }
 #pragma unroll
   for (int i = 0; i < B_PW; ++i) {

@@ -782,6 +782,15 @@ quail_status run_batch(quail_ctx* c, const Batch& b, const int32_t* tokens, uint
   const float2* rope = ws_ptr<const float2>(c, c->L.rope);
 
   uint32_t* status = ws_ptr<uint32_t>(c, c->L.status);
+  // A join batch whose only output is each pair's last row (h_last, no
+  // h_all) needs, at the last layer, every row's K/V and attention (the last
+  // rows attend to them) but the O projection, the MLP and their residual
+  // adds only for the last rows: those run on the gathered last rows. Each
+  // row's arithmetic is the same wherever it sits in a GEMM tile, so the
+  // result is bit-identical to running every row.
+  const bool prune_tail = !b.anchor_mode && h_all == nullptr && h_last != nullptr && !b.last_row.empty();
+  const int32_t* d_last = reinterpret_cast<const int32_t*>(dp(o_ldst));
+  const int32_t n_last = (int32_t)b.last_row.size();
   TIMED(PK_OTHER, 0, launch_embed(tokens, d_tok, c->w.embed, hbuf, n, H, cf.vocab, status + 1, s));
   for (int l = 0; l < cf.n_layers; ++l) {
     const quail_layer_weights& lw = c->layers[l];
@@ -821,23 +830,31 @@ quail_status run_batch(quail_ctx* c, const Batch& b, const int32_t* tokens, uint
           launch_attn_bf16(ap, G, (!b.anchor_mode || b.has_parent) && slab_fp8, b.anchor_mode && slab_fp8,
                            b.pack, s));
 
+    // rows that go on (the last rows only, gathered, at the last layer of a
+    // pruned batch)
+    const bool tail = prune_tail && l == cf.n_layers - 1;
+    const int32_t m = tail ? n_last : n;
+    const int32_t* rmap = tail ? d_last : nullptr;
+
     GemmParams go{};
     go.A = obuf; go.lda = (int64_t)Hq * kHeadDim; go.B = lw.w_o; go.scale = lw.s_o;
-    go.M = n; go.N = H; go.K = Hq * kHeadDim; go.Yf = hbuf; go.ldy = H;
-    TIMED(PK_O, 2.0 * n * go.N * go.K, launch_gemm(go, EPI_RESID, s));
+    go.M = m; go.N = H; go.K = Hq * kHeadDim; go.Yf = hbuf; go.ldy = H;
+    go.a_map = rmap; go.y_map = rmap;
+    TIMED(PK_O, 2.0 * m * go.N * go.K, launch_gemm(go, EPI_RESID, s));
 
-    np.gamma = lw.mlp_norm;
+    np.gamma = lw.mlp_norm; np.rows = m; np.row_map = rmap;
     TIMED(PK_NORM, 0, launch_rmsnorm(np, s));
 
     GemmParams gg{};
     gg.A = ubuf; gg.lda = H; gg.B = lw.w_gate_up; gg.scale = lw.s_gate_up;
-    gg.M = n; gg.N = I; gg.K = H; gg.Y = mbuf; gg.ldy = I; gg.inter = I;
-    TIMED(PK_GATE_UP, 2.0 * n * 2.0 * gg.N * gg.K, launch_gemm(gg, EPI_SWIGLU, s));
+    gg.M = m; gg.N = I; gg.K = H; gg.Y = mbuf; gg.ldy = I; gg.inter = I;
+    TIMED(PK_GATE_UP, 2.0 * m * 2.0 * gg.N * gg.K, launch_gemm(gg, EPI_SWIGLU, s));
 
     GemmParams gd{};
     gd.A = mbuf; gd.lda = I; gd.B = lw.w_down; gd.scale = lw.s_down;
-    gd.M = n; gd.N = H; gd.K = I; gd.Yf = hbuf; gd.ldy = H;
-    TIMED(PK_DOWN, 2.0 * n * gd.N * gd.K, launch_gemm(gd, EPI_RESID, s));
+    gd.M = m; gd.N = H; gd.K = I; gd.Yf = hbuf; gd.ldy = H;
+    gd.y_map = rmap;
+    TIMED(PK_DOWN, 2.0 * m * gd.N * gd.K, launch_gemm(gd, EPI_RESID, s));
   }
   if (!b.anchor_mode) {
     if (h_last && !b.last_row.empty()) {

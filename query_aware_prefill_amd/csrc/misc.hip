@@ -135,8 +135,26 @@ hipError_t launch_copy_slab_rows(const uint8_t* src, int64_t src_block, uint8_t*
   return hipGetLastError();
 }
 
-// y = bf16(x / sqrt(mean(x^2) + eps) * gamma), x an fp32 residual row; 8
-// columns per lane and step (two 16-B loads, one 16-B store)
+// y = bf16(x / sqrt(mean(x^2) + eps) * gamma), x an fp32 residual row, one
+// wave per row; 8 columns per lane and chunk (two 16-B loads, one 16-B
+// store). Up to kNormChunks chunks per lane stay in registers: rows of up to
+// 64 * 8 * 8 = 4096 columns are read once, with all their loads in flight
+// together; longer rows are read a second time for the output pass.
+constexpr int kNormChunks = 8;
+
+// bf16(x * inv * gamma) of one 8-column chunk
+__device__ __forceinline__ uint4 norm_chunk(const float4& a, const float4& b, float inv, const uint4* gm, int c) {
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  const uint4 gg = gm ? gm[c] : make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+  const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = pack_bf16x2(v[2 * i] * inv * bf16_bits_to_f32(gw[i] & 0xFFFF),
+                       v[2 * i + 1] * inv * bf16_bits_to_f32(gw[i] >> 16));
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 __global__ void __launch_bounds__(256) rmsnorm_kernel(NormParams p) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -144,6 +162,35 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(NormParams p) {
   const int src = p.row_map ? p.row_map[r] : r;
   const float4* x = reinterpret_cast<const float4*>(p.x + (int64_t)src * p.ldx);
   const int nc = p.H / 8;
+  uint4* y = reinterpret_cast<uint4*>(p.y + (int64_t)r * p.ldy);
+  const uint4* gm = reinterpret_cast<const uint4*>(p.gamma);
+  // per lane, chunks lane, lane + 64, ... in order (the same summation order
+  // in both branches)
+  if (nc <= 64 * kNormChunks) {
+    float4 a[kNormChunks], b[kNormChunks];
+#pragma unroll
+    for (int i = 0; i < kNormChunks; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nc) {
+        a[i] = x[2 * c];
+        b[i] = x[2 * c + 1];
+      }
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kNormChunks; ++i)
+      if (lane + 64 * i < nc)
+        ss += a[i].x * a[i].x + a[i].y * a[i].y + a[i].z * a[i].z + a[i].w * a[i].w + b[i].x * b[i].x +
+              b[i].y * b[i].y + b[i].z * b[i].z + b[i].w * b[i].w;
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)p.H + p.eps);
+#pragma unroll
+    for (int i = 0; i < kNormChunks; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nc) y[c] = norm_chunk(a[i], b[i], inv, gm, c);
+    }
+    return;
+  }
   float ss = 0.0f;
   for (int c = lane; c < nc; c += 64) {
     const float4 a = x[2 * c], b = x[2 * c + 1];
@@ -151,20 +198,7 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(NormParams p) {
   }
   ss = wave_sum(ss);
   const float inv = 1.0f / sqrtf(ss / (float)p.H + p.eps);
-  uint4* y = reinterpret_cast<uint4*>(p.y + (int64_t)r * p.ldy);
-  const uint4* gm = reinterpret_cast<const uint4*>(p.gamma);
-  for (int c = lane; c < nc; c += 64) {
-    const float4 a = x[2 * c], b = x[2 * c + 1];
-    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    const uint4 gg = gm ? gm[c] : make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
-    const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = pack_bf16x2(v[2 * i] * inv * bf16_bits_to_f32(gw[i] & 0xFFFF),
-                         v[2 * i + 1] * inv * bf16_bits_to_f32(gw[i] >> 16));
-    y[c] = make_uint4(o[0], o[1], o[2], o[3]);
-  }
+  for (int c = lane; c < nc; c += 64) y[c] = norm_chunk(x[2 * c], x[2 * c + 1], inv, gm, c);
 }
 
 hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s) {

@@ -75,6 +75,8 @@ enum GemmEpi : int32_t {
 
 struct GemmParams {
   const uint16_t* A; int64_t lda;        // bf16 [M][K]
+  const int32_t* a_map;                  // optional: A row m is row a_map[m] of A
+  const int32_t* y_map;                  // optional (RESID): output row m adds into Yf row y_map[m]
   const uint8_t* B;                      // fp8 [N_rows][K]
   const uint16_t* scale;                 // bf16 [N_rows]
   int32_t M, N, K;                       // N = output columns

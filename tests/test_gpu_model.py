@@ -201,6 +201,49 @@ def test_join_run_end_to_end(B):
     assert st["prefills"] == 2 * used and st["regret_tokens"] == 0 and st["resident"] == 0
 
 
+@pytest.mark.parametrize("kv_fp8", [False, True])
+def test_last_layer_runs_only_the_last_rows(B, kv_fp8):
+    """A join prefill that returns only each pair's last row runs the last
+    layer's O projection and MLP on the last rows alone (gathered through row
+    maps in the GEMMs and the norm). Its last rows must be bit-identical to
+    those of the same prefill returning every row (which runs every row), and
+    match the oracle. More than 256 pairs, so the gathered rows span several
+    GEMM row tiles; lengths from 1 (the last row is the only row) to 64."""
+    import torch
+    shape = W.tiny_shape(n_layers=3, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                         intermediate=384, vocab=512, kv_fp8=kv_fp8)
+    r = np.random.default_rng(31)
+    a_len = [40, 97, 150]
+    pairs = [(int(r.integers(-1, 3)), int(r.integers(1, 13))) for _ in range(300)]
+    pairs += [(0, 64), (1, 1), (2, 64), (-1, 1), (-1, 64)]
+    wts, case, dm, ctx, a_tok, s_tok = _setup(shape, 11, a_len, pairs, B, mbt=2048)
+    uses = 2 * np.bincount([p[0] for p in pairs if p[0] >= 0], minlength=3)
+    say("last-layer rows: anchor prefill", "fp8" if kv_fp8 else "bf16")
+    handles = B.quail_anchor_prefill(ctx, a_tok, case["a_off"], uses, anchor_ids=np.arange(3))
+    n = len(pairs)
+    T = int(case["s_off"][-1])
+    ph = [handles[a] if a >= 0 else B.NO_ANCHOR for a, _ in pairs]
+    h_full = torch.empty((n, shape.hidden), dtype=torch.int16, device="cuda")
+    h_all = torch.empty((T, shape.hidden), dtype=torch.int16, device="cuda")
+    say("last-layer rows: every row", n, "pairs,", T, "rows")
+    B.quail_join_prefill(ctx, ph, s_tok, case["s_off"], h_full, h_all)
+    h_tail = torch.empty((n, shape.hidden), dtype=torch.int16, device="cuda")
+    say("last-layer rows: last rows only")
+    B.quail_join_prefill(ctx, ph, s_tok, case["s_off"], h_tail, None)
+    torch.cuda.synchronize()
+    full, tail = u16(h_full), u16(h_tail)
+    assert np.array_equal(full, tail), int(np.sum(full != tail))
+    assert np.array_equal(u16(h_all)[case["s_off"][1:] - 1], full)
+    st = B.quail_pool_stats(ctx)
+    assert st["evictions"] == 3 and st["regret_tokens"] == 0 and st["resident"] == 0
+    for i in list(range(0, n, 37)) + [n - 5, n - 4, n - 1]:
+        a = pairs[i][0]
+        at = case["a_tok"][case["a_off"][a]:case["a_off"][a + 1]] if a >= 0 else []
+        st_ = case["s_tok"][case["s_off"][i]:case["s_off"][i + 1]]
+        ref = OM.forward_pair(at, st_, wts, shape)
+        assert rel_inf(bf16_f64(tail[i]), ref["h_last"]) <= 2e-2, i
+
+
 def test_qwen3_shaped_layer(B):
     """One decoder layer with the Qwen3-4B shapes (hidden 2560, 32q/8kv x 128,
     SwiGLU 9728, RoPE theta 1e6, fp8 weights): 2 anchors x 1024 tokens, two
