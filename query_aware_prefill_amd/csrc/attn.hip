@@ -471,6 +471,38 @@ struct TileCopy {
   }
 };
 
+// The same copies for the full tiles of one source whose element format is
+// known at compile time: a lane's source offsets depend only on its slice,
+// the token stride and the swizzle, so they are formed once per workgroup
+// and each tile adds only its (wave-uniform) base.
+template <int NW, bool IS_V, int ROWS, bool NT, bool FP8>
+struct FullTileCopy {
+  static constexpr int PER = FP8 ? ROWS / 8 / NW : ROWS / 4 / NW;
+  uint32_t voff[PER];
+  __device__ __forceinline__ FullTileCopy(const KVSrc& src, int wave, int lane) {
+    static_assert(PER >= 1, "copy split");
+    const uint32_t tb = (uint32_t)src.tok_stride << (FP8 ? 0 : 1);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int slice = wave * PER + i;
+      const uint32_t row = FP8 ? slice * 8 + (lane >> 3) : slice * 4 + (lane >> 4);
+      const uint32_t off = FP8 ? (IS_V ? swz8_v(row, lane & 7) : swz8_k(row, lane & 7)) * 16
+                               : (IS_V ? swz_v(row, lane & 15) : swz_k(row, lane & 15)) * 16;
+      voff[i] = __umul24(row, tb) + off;
+    }
+  }
+  // the tile of kv head g starting at key kbase into the slot at dst
+  __device__ __forceinline__ void issue(const KVSrc& src, int g, int kbase, uint32_t dst, int wave) const {
+    const int64_t base = ((int64_t)g * src.head_stride + (int64_t)kbase * src.tok_stride) << (FP8 ? 0 : 1);
+    const uint8_t* b8 = reinterpret_cast<const uint8_t*>(IS_V ? src.v : src.k) + base;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (NT) copy16_to_lds_off_nt(b8, voff[i], dst + (wave * PER + i) * 1024);
+      else copy16_to_lds_off(b8, voff[i], dst + (wave * PER + i) * 1024);
+    }
+  }
+};
+
 template <bool B>
 struct MaskTag { static constexpr bool value = B; };
 
@@ -645,9 +677,10 @@ struct WaveAttn {
 
   // row max of a tile over both lanes of the row, log2 units
   __device__ __forceinline__ float row_max(const f32x16_t (&s)[2]) const {
+    // max(m, a, b) per register pair: one v_max3_f32 each
     float m0 = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) m0 = fmaxf(m0, fmaxf(s[0][r], s[1][r]));
+    for (int r = 1; r < 16; ++r) m0 = fmaxf(fmaxf(m0, s[0][r]), s[1][r]);
     return xor32_max(m0) * scale_log2;
   }
 
@@ -845,8 +878,18 @@ attn_direct_kernel(AttnParams p) {
   const uint32_t lds_v0 = lds_k0 + 2 * kSlotBytes;
   // K and V copies of tile j into K slot ks and V slot vs
   // (packed launches stream each anchor's K/V once per kv head: non-temporal)
+  // full tiles of the first cross source (the anchor) take the copies with
+  // offsets formed here; the rest (ragged, second-level and self tiles) the
+  // general ones
+  const FullTileCopy<NW, false, NKC, (PACK > 0), FC> kfull(ts.cs, wave, lane);
+  const FullTileCopy<NW, true, NKC, (PACK > 0), FC> vfull(ts.cs, wave, lane);
+  // (one-level launches: the two-level variants have no registers to spare)
+  const int n_fast = L2 ? 0 : min(ts.n_full, ts.n_c1);
   auto issue = [&](int j, int ks, int vs) __attribute__((always_inline)) {
-    if (NKC == NKS || j < ts.n_ct) {
+    if (j < n_fast) {
+      kfull.issue(ts.cs, g, j * NKC, lds_k0 + ks * kSlotBytes, wave);
+      vfull.issue(ts.cs, g, j * NKC, lds_v0 + vs * kSlotBytes, wave);
+    } else if (NKC == NKS || j < ts.n_ct) {
       TileCopy<NW, false, NKC, (PACK > 0)>(ts.src(j), g, ts.kbase(j), lds_k0 + ks * kSlotBytes).issue_all(wave, lane);
       TileCopy<NW, true, NKC, (PACK > 0)>(ts.src(j), g, ts.kbase(j), lds_v0 + vs * kSlotBytes).issue_all(wave, lane);
     } else {
