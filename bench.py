@@ -70,8 +70,9 @@ Secondary measurements (not the headline line; each prints its own JSON):
                      logits are identical.
   --workload layer   one decoder layer of the Qwen3-4B shape, random-init fp8
                      weights: 16 anchors x 1024 tokens, 512 suffixes x 64
-                     tokens per anchor, run end to end by quail_join_run
-                     (plan, anchor prefill + KV writer, join prefill, head).
+                     tokens per anchor: anchor prefill + KV writer, join
+                     prefill of every suffix row (all hidden rows returned),
+                     head.
 """
 from __future__ import annotations
 
@@ -88,6 +89,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0
+# projection FLOP per token per layer (Qwen3-4B shapes): QKV 2*2560*6144, O
+# 2*4096*2560, gate/up 2*2560*19456, down 2*9728*2560; and the QKV share
+GEMM_FLOP_LAYER = 201_850_880.0
+GEMM_FLOP_QKV = 31_457_280.0
+
+
+def executed_gemm_flops(n_layers, suffix_tok, n_last, anchor_tok):
+    """Projection FLOP a join prefill returning each pair's last row executes:
+    suffix tokens run every layer but the last, and the last layer's QKV
+    projection (their K/V feed the last rows' attention); the pairs' last rows
+    also the last layer's O projection and MLP; anchors every layer but the
+    last, and the last layer's QKV projection (their K/V is all the pairs
+    read)."""
+    per_tok = GEMM_FLOP_LAYER * (n_layers - 1) + GEMM_FLOP_QKV
+    return per_tok * (suffix_tok + anchor_tok) + (GEMM_FLOP_LAYER - GEMM_FLOP_QKV) * n_last
 HBM_PEAK_GBS = 8000.0
 METRIC = "prefill tokens/min per GPU on join workload; cascade-attn TFLOP/s vs MFMA peak"
 
@@ -391,11 +407,7 @@ def bench_e2e(args):
     anchor_tok = int(np.sum(a_len[used])) if len(used) else 0
     logical = int(np.sum(la) + suffix_tok)
     st = B.quail_pool_stats(ctx)
-    # executed GEMM work: every suffix token runs all 36 layers (201.85 MFLOP
-    # per token per layer); anchors run 35 full layers and the last layer's
-    # QKV projection only (their last-layer output is not needed)
-    gemm = 201_850_880.0 * suffix_tok * shape.n_layers + anchor_tok * (
-        201_850_880.0 * (shape.n_layers - 1) + 31_457_280.0)
+    gemm = executed_gemm_flops(shape.n_layers, suffix_tok, n, anchor_tok)
     attn = 16384.0 * shape.n_layers * float(np.sum(s_len * la) + np.sum(s_len * (s_len + 1) / 2))
     attn += 16384.0 * (shape.n_layers - 1) * float(sum(int(a_len[a]) * (int(a_len[a]) + 1) / 2 for a in used))
     res = {"metric": "end-to-end prefill tokens/min (36-layer stack)", "workload": desc, "unit": "tokens/min",
@@ -445,10 +457,18 @@ def bench_layer(args):
     a_tok, s_tok = to_device(case["a_tok"]), to_device(case["s_tok"])
     logits = torch.empty((n_pairs, 8), dtype=torch.float32, device="cuda")
     dec = torch.empty(n_pairs, dtype=torch.uint8, device="cuda")
+    n_anchors = len(case["a_off"]) - 1
+    uses = np.bincount(case["pair_anchor"], minlength=n_anchors)
+    h_last = torch.empty((n_pairs, shape.hidden), dtype=torch.int16, device="cuda")
+    h_all = torch.empty((int(case["s_off"][-1]), shape.hidden), dtype=torch.int16, device="cuda")
 
+    # the whole layer for every suffix row (h_all requested: a join prefill
+    # that returns only the last rows would run the O projection and MLP of
+    # its last layer, here the only one, on the last rows alone)
     def step():
-        B.quail_join_run(ctx, a_tok, case["a_off"], case["pair_anchor"], s_tok, case["s_off"], 0x0F,
-                         logits, None, dec)
+        handles = B.quail_anchor_prefill(ctx, a_tok, case["a_off"], uses, anchor_ids=np.arange(n_anchors))
+        B.quail_join_prefill(ctx, handles[case["pair_anchor"]], s_tok, case["s_off"], h_last, h_all)
+        B.quail_head8(ctx, h_last, 0x0F, logits, None, dec)
 
     for _ in range(args.warmup):
         step()
@@ -464,7 +484,7 @@ def bench_layer(args):
     # executed algorithmic work: suffix tokens run the whole layer (201.85
     # MFLOP/token of projections); with one layer, the anchors' last layer only
     # needs its K/V, i.e. the QKV projection (31.46 MFLOP/token).
-    gemm_flops = 201_850_880.0 * suffix_tok + 31_457_280.0 * anchor_tok
+    gemm_flops = GEMM_FLOP_LAYER * suffix_tok + GEMM_FLOP_QKV * anchor_tok
     attn_flops = 16384.0 * (np.sum(case["s_len"] * case["a_len"][case["pair_anchor"]]) +
                             np.sum(case["s_len"] * (case["s_len"] + 1) / 2))
     st = B.quail_pool_stats(ctx)
@@ -817,7 +837,7 @@ def bench_multijoin_full(args):
     anchor_tok = float(np.sum(a_len))
     logical = float(np.sum(a_len[pa]) + suffix_tok)
     L = shape.n_layers
-    gemm = 201_850_880.0 * suffix_tok * L + anchor_tok * (201_850_880.0 * (L - 1) + 31_457_280.0)
+    gemm = executed_gemm_flops(L, suffix_tok, n, anchor_tok)
     attn = 16384.0 * L * float(np.sum(plen * a_len[pa]) + np.sum(plen * (plen + 1) / 2))
     attn += 16384.0 * (L - 1) * float(np.sum(a_len.astype(np.float64) * (a_len + 1) / 2))
     res = {"metric": "end-to-end prefill tokens/min (36-layer stack)",
