@@ -375,7 +375,9 @@ quail_status quail_anchor_kv(const quail_ctx* ctx, quail_anchor handle, int32_t 
  * RMSNorm, SwiGLU MLP + residual. Writes the last position's hidden state to
  * h_last (dev bf16 [n, hidden], caller order) and, if h_all is not NULL, every
  * position's final hidden state to h_all (dev bf16 [offsets[n], hidden]).
- * Pairs may come in any order; each pair spends one use of its anchor and an
+ * Without h_all only the last positions' states are needed, so the last
+ * layer runs its O projection and MLP on those rows alone (their values are
+ * the same bit for bit). Pairs may come in any order; each pair spends one use of its anchor and an
  * anchor whose uses reach 0 is evicted (its slab is reused in stream order).
  * A handle may also name a prefix node (quail_prefix_prefill): the pair's
  * tokens then sit at positions La + Lp + j and attend to the anchor's keys,
