@@ -47,7 +47,8 @@ Secondary measurements (not the headline line; each prints its own JSON):
                      each read by one suffix of S tokens, S in {1, 4, 16, 32,
                      64, 256, 4096}; anchor KV bytes per launch / launch time against
                      8 TB/s, and TFLOP/s (4*S FLOP per bf16 KV byte, 8*S per
-                     E4M3 byte).
+                     E4M3 byte); then the whole 36-layer E4M3 pool (57.98 GB,
+                     one launch per layer) for S in {1, 4, 16, 32}.
   --workload join36 | filter36 | multijoin36
                      end to end on the 36-layer Qwen3-4B-shaped stack with
                      random-init fp8 weights (quail_join_run: plan, anchor
@@ -301,6 +302,56 @@ def bench_stream(args):
                 f"{pt['tflops']:.1f} TFLOP/s")
             del case, o, ws
             torch.cuda.empty_cache()
+    # The whole E4M3 pool of the multi-join configuration: 36 layers of the
+    # same 1024 anchors x 768 tokens (57.98 GB); one pass is 36 launches, each
+    # reading its layer's anchor K/V once for S query tokens per anchor.
+    n_layers = 36
+    a_len, _, _ = W.stream_lengths(1)
+    ta = int(np.sum(a_len))
+    pool = torch.empty((n_layers, 2, ta, 8, 128), dtype=torch.float8_e4m3fn, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(29)
+    flat = pool.view(-1)
+    for i in range(0, flat.numel(), 1 << 28):
+        n = min(1 << 28, flat.numel() - i)
+        flat[i:i + n] = torch.randn(n, generator=gen, device="cuda", dtype=torch.float32).to(torch.float8_e4m3fn)
+    pool = pool.view(torch.uint8)
+    pool_bytes = float(pool.numel())
+    out["pool"] = {"layers": n_layers, "anchor_kv_bytes": pool_bytes, "points": []}
+    for S in (1, 4, 16, 32):
+        _, s_anchor, s_len = W.stream_lengths(S)
+        case = W.cascade_device(7, a_len, s_anchor, s_len, anchor_kv="e4m3")
+        del case["ak"], case["av"]
+        T = int(case["s_off"][-1])
+        o = torch.empty((T, 32, 128), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(B.quail_cascade_workspace_bytes(case["a_off"], case["s_off"]), dtype=torch.uint8,
+                         device="cuda")
+        stream = torch.cuda.current_stream()
+
+        def one_pass():
+            for layer in range(n_layers):
+                B.quail_cascade_attn(B.DTYPE_FP8_E4M3, 32, 8, 128, case["sm_scale"], pool[layer, 0],
+                                     pool[layer, 1], case["a_off"], s_anchor, case["q"], case["k"], case["v"],
+                                     case["s_off"], o, None, ws, stream=stream)
+
+        one_pass()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(max(args.steps // 2, 1))]
+        for a, b in ev:
+            a.record(stream)
+            one_pass()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        pt = {"kv": "e4m3", "S": S, "ms_per_pass": ms, "GB/s": pool_bytes / (ms * 1e-3) / 1e9,
+              "frac_hbm": pool_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        out["pool"]["points"].append(pt)
+        log(f"stream pool e4m3 S={S}: {ms:.2f} ms per pass of {pool_bytes / 1e9:.2f} GB, {pt['GB/s']:.0f} GB/s "
+            f"({pt['frac_hbm']:.2f} of HBM)")
+        del case, o, ws
+    del pool
+    torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 
 
