@@ -40,6 +40,11 @@ Secondary measurements (not the headline line; each prints its own JSON):
                      (QKV 6144x2560, O 2560x4096, gate/up 19456x2560, down
                      2560x9728) at M = 65536 tokens, TFLOP/s against the bf16
                      MFMA peak.
+  --workload gemm8   the W8A8 path at the same four shapes and M = 65536:
+                     per-token E4M3 activation quantisation (GB/s against
+                     8 TB/s: 2 B read + 1 B written per element) and the
+                     fp8 x fp8 GEMM (TFLOP/s against the fp8 MFMA peak),
+                     beside the W8A16 kernel on the same shapes.
   --workload copy    a plain 4 GiB device-to-device copy (read 4 GiB, write
                      4 GiB): the calibration kernel for the HBM byte counters.
   --workload stream  anchor-KV streaming sweep: 1024 anchors of 768 tokens
@@ -90,6 +95,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
 # projection FLOP per token per layer (Qwen3-4B shapes): QKV 2*2560*6144, O
 # 2*4096*2560, gate/up 2*2560*19456, down 2*9728*2560; and the QKV share
 GEMM_FLOP_LAYER = 201_850_880.0
@@ -236,6 +242,58 @@ def bench_gemm(args):
                                "torch_bf16_matmul_tflops": 2.0 * M * N * K / (ref_ms * 1e-3) / 1e12}
         log(f"gemm {name} {M}x{N}x{K}: {ms:.3f} ms, {tf:.1f} TFLOP/s "
             f"(torch bf16 matmul {out['shapes'][name]['torch_bf16_matmul_tflops']:.1f})")
+    print(json.dumps(out), flush=True)
+
+
+def _timed(fn, steps, warmup):
+    """Mean ms of fn() over `steps` launches (events around each)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def bench_gemm8(args):
+    import torch
+    import workloads as W
+    from query_aware_prefill_amd import binding as B
+    from query_aware_prefill_amd.device import to_device
+    B.load()
+    M = 65536
+    r = np.random.default_rng(0)
+    out = {"metric": "W8A8 GEMM TFLOP/s", "unit": "TFLOP/s", "M": M, "peak_fp8_tflops": PEAK_FP8_TFLOPS,
+           "shapes": {}}
+    x_full = torch.randn((M, 9728), device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    for name, (N, K) in {"qkv": (6144, 2560), "o": (2560, 4096), "gate_up": (19456, 2560),
+                         "down": (2560, 9728)}.items():
+        x = x_full[:, :K].contiguous()
+        xc = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+        xs = torch.empty(M, dtype=torch.float32, device="cuda")
+        w = to_device(W.draw_fp8_codes(r, (N, K)))
+        sc = to_device(W.bf16_bits_from_f32((0.0002 * (1 + r.random(N))).astype(np.float32)))
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        q_ms = _timed(lambda: B.quail_act_quant_e4m3(x, xc, xs), args.steps, args.warmup)
+        g_ms = _timed(lambda: B.quail_gemm_w8a8(xc, xs, w, sc, y), args.steps, args.warmup)
+        w16_ms = _timed(lambda: B.quail_gemm_w8a16(x, w, sc, y), args.steps, args.warmup)
+        flop = 2.0 * M * N * K
+        q_gbs = 3.0 * M * K / (q_ms * 1e-3) / 1e9
+        tf = flop / (g_ms * 1e-3) / 1e12
+        out["shapes"][name] = {
+            "N": N, "K": K,
+            "act_quant": {"ms": q_ms, "GB/s": q_gbs, "frac_hbm": q_gbs / HBM_PEAK_GBS},
+            "gemm_w8a8": {"ms": g_ms, "tflops": tf, "frac": tf / PEAK_FP8_TFLOPS},
+            "w8a8_total_ms": q_ms + g_ms,
+            "gemm_w8a16": {"ms": w16_ms, "tflops": flop / (w16_ms * 1e-3) / 1e12}}
+        log(f"w8a8 {name} {M}x{N}x{K}: quant {q_ms:.3f} ms ({q_gbs:.0f} GB/s), gemm {g_ms:.3f} ms "
+            f"({tf:.1f} TFLOP/s, {tf / PEAK_FP8_TFLOPS:.3f} of fp8 peak); W8A16 {w16_ms:.3f} ms")
+        del x, xc, xs, w, sc, y
     print(json.dumps(out), flush=True)
 
 
@@ -1196,7 +1254,7 @@ def main():
     ap.add_argument("--no-cascade", action="store_true",
                     help="join: skip the separately timed cascade-attention layer (profiling runs)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--workload", choices=["join", "cascade", "gemm", "layer", "copy", "stream", "join36",
+    ap.add_argument("--workload", choices=["join", "cascade", "gemm", "gemm8", "layer", "copy", "stream", "join36",
                                            "filter36", "multijoin36", "multijoin36full", "multiplan36", "shared36",
                                            "traces36", "nested36", "search"],
                     default="join")
@@ -1211,6 +1269,8 @@ def main():
 
     if args.workload == "gemm":
         return bench_gemm(args)
+    if args.workload == "gemm8":
+        return bench_gemm8(args)
     if args.workload == "layer":
         return bench_layer(args)
     if args.workload == "copy":

@@ -527,6 +527,32 @@ quail_status quail_gemm_w8a16(int32_t M, int32_t N, int32_t K, const uint16_t* x
                               const uint8_t* w, const uint16_t* scale, uint16_t* y,
                               quail_stream stream);
 
+/* ---- W8A8: E4M3 activations on the fp8 MFMA --------------------------------- */
+/* The FP8 GEMM of the engine ([pt] "Como funciona", FP8 GEMM kernels) with
+ * both operands in E4M3: one scale per token for the activations, one bf16
+ * scale per output row for the weights. Not the contract of
+ * quail_join_prefill (whose projections are W8A16): a standalone pair of
+ * calls for callers that accept per-token fp8 activations.
+ *
+ * Per-token quantisation: amax = max_k |x[m][k]|;
+ *   codes[m][k] = E4M3(x[m][k] * (448 / amax))  (saturating, round to nearest,
+ *                                                ties to the even code)
+ *   scale[m]    = amax / 448
+ * where 448 / amax, the product and amax / 448 are each one fp32 operation
+ * rounded to nearest even. A row of zeros gets codes 0 and scale 0. x dev
+ * bf16 [M, K] (row stride K, finite values, 16-byte aligned); codes dev u8
+ * [M, K]; scale dev f32 [M]. K a multiple of 8. Caller owns every buffer. */
+quail_status quail_act_quant_e4m3(int32_t M, int32_t K, const uint16_t* x, uint8_t* codes,
+                                  float* scale, quail_stream stream);
+/* y[m][n] = bf16( w_scale[n] * x_scale[m] * sum_k decode(xc[m][k]) * decode(wc[n][k]) ),
+ * fp32 accumulation of the exact fp8 products. xc dev u8 [M, K]; x_scale dev
+ * f32 [M]; wc dev u8 [N, K]; w_scale dev bf16 [N]; y dev bf16 [M, N]. N a
+ * multiple of 256, K a multiple of 128, buffers 16-byte aligned (w_scale
+ * 8-byte); otherwise QUAIL_E_UNSUPPORTED. */
+quail_status quail_gemm_w8a8(int32_t M, int32_t N, int32_t K, const uint8_t* xc, const float* x_scale,
+                             const uint8_t* wc, const uint16_t* w_scale, uint16_t* y,
+                             quail_stream stream);
+
 /* ---- E4M3 codec of the fp8 KV store -------------------------------------- */
 /* codes[i] = E4M3(x[i] / scale): saturate to +-448, round to nearest, ties to
  * the even code (the KV writer's quantiser for anchor K/V held as fp8; the

@@ -111,6 +111,8 @@ _SIGS = {
                                     _vp, _i32p, C.c_int32, _i32p, _vp, _vp, _vp, _i32p, _vp, _vp, _vp],
                                    C.c_int32),
     "quail_gemm_w8a16": ([C.c_int32, C.c_int32, C.c_int32, _vp, _vp, _vp, _vp, _vp], C.c_int32),
+    "quail_act_quant_e4m3": ([C.c_int32, C.c_int32, _vp, _vp, _vp, _vp], C.c_int32),
+    "quail_gemm_w8a8": ([C.c_int32, C.c_int32, C.c_int32, _vp, _vp, _vp, _vp, _vp, _vp], C.c_int32),
     "quail_fp8_e4m3_encode": ([C.c_int64, _vp, C.c_float, _vp, _vp], C.c_int32),
     "quail_fp8_e4m3_decode": ([C.c_int64, _vp, C.c_float, _vp, _vp], C.c_int32),
 }
@@ -454,6 +456,18 @@ def quail_gemm_w8a16(x, w, scale, y, stream=None):
     N = w.shape[0]
     _check(load().quail_gemm_w8a16(M, N, K, dptr(x), dptr(w), dptr(scale), dptr(y),
                                    stream_handle(stream)))
+
+
+def quail_act_quant_e4m3(x, codes, scale, stream=None):
+    M, K = x.shape
+    _check(load().quail_act_quant_e4m3(M, K, dptr(x), dptr(codes), dptr(scale), stream_handle(stream)))
+
+
+def quail_gemm_w8a8(xc, x_scale, wc, w_scale, y, stream=None):
+    M, K = xc.shape
+    N = wc.shape[0]
+    _check(load().quail_gemm_w8a8(M, N, K, dptr(xc), dptr(x_scale), dptr(wc), dptr(w_scale), dptr(y),
+                                  stream_handle(stream)))
 
 
 def quail_fp8_e4m3_encode(x, scale, codes, stream=None):

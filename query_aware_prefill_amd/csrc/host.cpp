@@ -31,6 +31,7 @@
 
 #include "../../include/quail.h"
 #include "quail_internal.h"
+#include "w8a8.h"
 
 using namespace quail;
 
@@ -2447,6 +2448,35 @@ quail_status quail_gemm_w8a16(int32_t M, int32_t N, int32_t K, const uint16_t* x
   GemmParams p{};
   p.A = x; p.lda = K; p.B = w; p.scale = scale; p.M = M; p.N = N; p.K = K; p.Y = y; p.ldy = N;
   HIP_TRY(launch_gemm(p, EPI_STORE, as_stream(stream)));
+  return QUAIL_OK;
+}
+
+static bool aligned_to(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
+
+quail_status quail_act_quant_e4m3(int32_t M, int32_t K, const uint16_t* x, uint8_t* codes, float* scale,
+                                  quail_stream stream) {
+  if (M < 0 || K <= 0) return fail(QUAIL_E_INVAL, "M >= 0 and K > 0 required");
+  if (K % 8) return fail(QUAIL_E_UNSUPPORTED, "K must be a multiple of 8");
+  if (M == 0) return QUAIL_OK;
+  if (!x || !codes || !scale) return fail(QUAIL_E_INVAL, "NULL argument");
+  if (!aligned_to(x, 16) || !aligned_to(codes, 8) || !aligned_to(scale, 4))
+    return fail(QUAIL_E_UNSUPPORTED, "x must be 16-byte aligned, codes 8-byte, scale 4-byte");
+  HIP_TRY(launch_act_quant_e4m3(M, K, x, codes, scale, as_stream(stream)));
+  return QUAIL_OK;
+}
+
+quail_status quail_gemm_w8a8(int32_t M, int32_t N, int32_t K, const uint8_t* xc, const float* x_scale,
+                             const uint8_t* wc, const uint16_t* w_scale, uint16_t* y, quail_stream stream) {
+  if (M < 0 || N <= 0 || K <= 0) return fail(QUAIL_E_INVAL, "M >= 0, N > 0, K > 0 required");
+  if (K % 128 || N % 256) return fail(QUAIL_E_UNSUPPORTED, "K must be a multiple of 128 and N of 256");
+  if (M == 0) return QUAIL_OK;
+  if (!xc || !x_scale || !wc || !w_scale || !y) return fail(QUAIL_E_INVAL, "NULL argument");
+  if (!aligned_to(xc, 16) || !aligned_to(wc, 16) || !aligned_to(y, 16) || !aligned_to(w_scale, 8) ||
+      !aligned_to(x_scale, 4))
+    return fail(QUAIL_E_UNSUPPORTED, "xc, wc and y must be 16-byte aligned, w_scale 8-byte");
+  W8A8Params p{};
+  p.A = xc; p.a_scale = x_scale; p.B = wc; p.b_scale = w_scale; p.Y = y; p.M = M; p.N = N; p.K = K;
+  HIP_TRY(launch_gemm_w8a8(p, as_stream(stream)));
   return QUAIL_OK;
 }
 

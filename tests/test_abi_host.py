@@ -463,3 +463,20 @@ def test_noalloc_cascade_rejects_metadata_beyond_its_scratch():
                                         fake, fake, sop, fake, None, None)
     assert st == B.E_NOMEM
     assert b"16777216" in lib.quail_last_error()
+
+
+def test_w8a8_argument_checks():
+    """Shape, alignment and NULL checks of the W8A8 calls return before any
+    GPU work (no device is touched)."""
+    lib = B.load()
+    fake = 0x7F0000000000
+    assert lib.quail_act_quant_e4m3(4, 12, fake, fake, fake, None) == B.E_UNSUPPORTED      # K % 8
+    assert lib.quail_act_quant_e4m3(-1, 8, fake, fake, fake, None) == B.E_INVAL
+    assert lib.quail_act_quant_e4m3(4, 8, None, fake, fake, None) == B.E_INVAL
+    assert lib.quail_act_quant_e4m3(4, 8, fake + 8, fake, fake, None) == B.E_UNSUPPORTED   # x alignment
+    assert lib.quail_act_quant_e4m3(0, 8, None, None, None, None) == B.OK
+    assert lib.quail_gemm_w8a8(4, 256, 192, fake, fake, fake, fake, fake, None) == B.E_UNSUPPORTED  # K % 128
+    assert lib.quail_gemm_w8a8(4, 128, 128, fake, fake, fake, fake, fake, None) == B.E_UNSUPPORTED  # N % 256
+    assert lib.quail_gemm_w8a8(4, 256, 128, fake, fake, None, fake, fake, None) == B.E_INVAL
+    assert lib.quail_gemm_w8a8(4, 256, 128, fake, fake, fake, fake + 4, fake, None) == B.E_UNSUPPORTED
+    assert lib.quail_gemm_w8a8(0, 256, 128, None, None, None, None, None, None) == B.OK
