@@ -27,6 +27,10 @@ Readings where the pages are silent (all standard for this model family):
   * fp8 anchor KV (multi-join configuration): the anchor's post-RoPE K and its
     V are stored as E4M3 codes of k / k_scale and v / v_scale, and every
     reader (the anchor itself and all suffixes) sees the decoded values.
+  * W8A8 (shape.act_fp8, off by default): the four projections read their
+    activations (u before QKV and before gate/up, o, m) as per-token E4M3
+    codes times the token's scale (oracle/w8a8.py), quantised from the values
+    the W8A16 pipeline hands them; nothing else changes.
 
 Precision modes:
   * "contract": round to bf16 exactly where a bf16 tensor exists in the
@@ -48,14 +52,30 @@ head; argmax tie-break; anchor K/V independent of the suffix; the whole
 stack (embedding, three decoder layers over [anchor | suffix], final norm, the
 head at the last position) in "exact" mode against the transformers library's
 Llama causal LM in float64 whose first 8 vocabulary rows are the 8-column
-head. The 36-layer stack is the same loop at a larger count.
+head. The 36-layer stack is the same loop at a larger count. W8A8: the
+batched and per-pair forms agree with act_fp8 on; dropping any one of the
+four quantisation points changes the result; the whole effect stays within
+the few-percent size that E4M3's 3 mantissa bits allow.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from . import codecs
+from . import codecs, w8a8
 from .attention import attention_causal
+
+# projection inputs that the W8A8 reading quantises (all four; the pins drop
+# one at a time to show each is applied)
+ACT_POINTS = frozenset({"qkv", "o", "gate_up", "down"})
+
+
+def _aq(x, shape, point):
+    """What a projection reads: with per-token E4M3 activations
+    (shape.act_fp8) the dequantised per-token codes of x, else x itself."""
+    if not getattr(shape, "act_fp8", False) or point not in ACT_POINTS:
+        return x
+    codes, scale = w8a8.act_quant_e4m3(np.asarray(x, np.float32))
+    return w8a8.act_dequant(codes, scale).astype(x.dtype)
 
 
 def _bf(x, mode):
@@ -116,7 +136,7 @@ def decoder_layer(h, pos, W: LayerWeights, shape, mode="contract", fp8_kv_upto=0
     N = h.shape[0]
     Hq, Hkv, d = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
     u = _bf(rmsnorm(h, W.attn_norm, shape.rms_eps), mode)
-    qkv = u @ W.w_qkv.T
+    qkv = _aq(u, shape, "qkv") @ W.w_qkv.T
     q = qkv[:, :Hq * d].reshape(N, Hq, d)
     k = qkv[:, Hq * d:(Hq + Hkv) * d].reshape(N, Hkv, d)
     v = qkv[:, (Hq + Hkv) * d:].reshape(N, Hkv, d)
@@ -132,10 +152,10 @@ def decoder_layer(h, pos, W: LayerWeights, shape, mode="contract", fp8_kv_upto=0
         v[:n] = codecs.e4m3_roundtrip(v[:n], shape.v_scale)
     o, _ = attention_causal(q, k, v, 1.0 / np.sqrt(d), q_pos=pos, k_pos=pos)
     o = _bf(o.reshape(N, Hq * d), mode)
-    h = h + o @ W.w_o.T
-    u = _bf(rmsnorm(h, W.mlp_norm, shape.rms_eps), mode)
+    h = h + _aq(o, shape, "o") @ W.w_o.T
+    u = _aq(_bf(rmsnorm(h, W.mlp_norm, shape.rms_eps), mode), shape, "gate_up")
     m = _bf(silu(u @ W.w_gate.T) * (u @ W.w_up.T), mode)
-    h = h + m @ W.w_down.T
+    h = h + _aq(m, shape, "down") @ W.w_down.T
     if return_kv:
         return h, (k, v, k_pre, v_pre)
     return h
@@ -246,7 +266,7 @@ def forward_many(seqs, weights, shape, true_mask=0x0F, mode="contract", dtype=np
         W = LayerWeights(weights["layers"][l], shape, dtype)
         N = h.shape[0]
         u = _bf(rmsnorm(h, W.attn_norm, shape.rms_eps), mode)
-        qkv = u @ W.w_qkv.T
+        qkv = _aq(u, shape, "qkv") @ W.w_qkv.T
         q = qkv[:, :Hq * d].reshape(N, Hq, d)
         k = qkv[:, Hq * d:(Hq + Hkv) * d].reshape(N, Hkv, d)
         v = qkv[:, (Hq + Hkv) * d:].reshape(N, Hkv, d)
@@ -264,10 +284,10 @@ def forward_many(seqs, weights, shape, true_mask=0x0F, mode="contract", dtype=np
                 vs[:upto[i]] = codecs.e4m3_roundtrip(vs[:upto[i]], shape.v_scale)
             o[a:b], _ = attention_causal(q[a:b], ks, vs, 1.0 / np.sqrt(d))
         o = _bf(o.reshape(N, Hq * d), mode)
-        h = h + o @ W.w_o.T
-        u = _bf(rmsnorm(h, W.mlp_norm, shape.rms_eps), mode)
+        h = h + _aq(o, shape, "o") @ W.w_o.T
+        u = _aq(_bf(rmsnorm(h, W.mlp_norm, shape.rms_eps), mode), shape, "gate_up")
         m = _bf(silu(u @ W.w_gate.T) * (u @ W.w_up.T), mode)
-        h = h + m @ W.w_down.T
+        h = h + _aq(m, shape, "down") @ W.w_down.T
         del W
         if (l + 1) in taps:
             out[l + 1] = head(h[last])

@@ -290,3 +290,45 @@ def test_depth_scaled_residual_projections():
     for w, std in ((lw.w_qkv, 0.02), (lw.w_gate, 0.02), (lw.w_up, 0.02),
                    (lw.w_o, 0.02 / 4.0), (lw.w_down, 0.02 / 4.0)):
         assert abs(np.std(w) / std - 1.0) < 0.15, (np.std(w), std)
+
+
+def _w8a8_case():
+    shape = W.tiny_shape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                         intermediate=384, vocab=64, act_fp8=True)
+    wts = W.model_weights(shape, 31)
+    r = np.random.default_rng(32)
+    pairs = [(r.integers(0, 64, 17), r.integers(0, 64, 6)), ([], r.integers(0, 64, 9)),
+             (r.integers(0, 64, 25), r.integers(0, 64, 3))]
+    return shape, wts, pairs
+
+
+def test_w8a8_batched_and_per_pair_forms_agree():
+    """With act_fp8 the stacked forward and the per-pair forward give the same
+    logits: each token's scale is its own row's, so stacking sequences into
+    one matrix changes nothing. A scale taken over the wrong axis (per column
+    or per matrix) fails here."""
+    shape, wts, pairs = _w8a8_case()
+    seqs = [np.concatenate([np.asarray(a, np.int64), s]) for a, s in pairs]
+    got = M.forward_many(seqs, wts, shape, mode="exact")
+    for i, (a, s) in enumerate(pairs):
+        ref = M.forward_pair(a, s, wts, shape, mode="exact")
+        assert np.max(np.abs(got["logits"][i] - ref["logits"])) <= 1e-12 * np.max(np.abs(ref["logits"]))
+
+
+def test_w8a8_every_quantisation_point_is_applied(monkeypatch):
+    """Dropping any one of the four quantised projection inputs changes the
+    hidden states; all four together move them from the W8A16 result by
+    about what E4M3 rounding (3 mantissa bits, per-token scale) allows: more
+    than 0.1% and less than 5% after two layers."""
+    shape, wts, pairs = _w8a8_case()
+    a, s = pairs[0]
+    full = M.forward_pair(a, s, wts, shape)["h"]
+    import dataclasses
+    w16 = M.forward_pair(a, s, wts, dataclasses.replace(shape, act_fp8=False))["h"]
+    rel = np.max(np.abs(full - w16)) / np.max(np.abs(w16))
+    assert 1e-3 < rel < 5e-2, rel
+    for point in sorted(M.ACT_POINTS):
+        monkeypatch.setattr(M, "ACT_POINTS", M.ACT_POINTS - {point})
+        part = M.forward_pair(a, s, wts, shape)["h"]
+        monkeypatch.undo()
+        assert np.max(np.abs(part - full)) > 1e-6 * np.max(np.abs(full)), point

@@ -64,6 +64,7 @@ class ModelShape:
     kv_fp8: bool = False          # anchor KV stored as OCP E4M3 codes
     k_scale: float = 1.0
     v_scale: float = 1.0
+    act_fp8: bool = False         # projections read per-token E4M3 activations (W8A8)
 
     @property
     def q_dim(self) -> int:
