@@ -66,6 +66,9 @@ Secondary measurements (not the headline line; each prints its own JSON):
                      Logical and computed tokens/min; the oracle leg runs the
                      per-pair definition on a few sampled pairs and compares
                      logits and decisions.
+                     --act-fp8 runs them with per-token E4M3 activations
+                     (W8A8 projections on the fp8 MFMA) against the
+                     oracle's W8A8 reading.
   --workload multiplan36
                      three joins over the join36 anchor table (64 anchors x
                      1024 tokens), 8,192 pairs of 64-token suffixes each, on
@@ -465,6 +468,8 @@ def bench_e2e(args):
     shape = W.QWEN3_4B
     if kind == "multijoin36":
         shape = W.ModelShape(**{**shape.__dict__, "kv_fp8": True})
+    if args.act_fp8:
+        shape = W.ModelShape(**{**shape.__dict__, "act_fp8": True})
     log(f"{kind}: generating the workload")
     if kind == "join36":
         case = W.c3b_case()
@@ -519,6 +524,8 @@ def bench_e2e(args):
     gemm = executed_gemm_flops(shape.n_layers, suffix_tok, n, anchor_tok)
     attn = 16384.0 * shape.n_layers * float(np.sum(s_len * la) + np.sum(s_len * (s_len + 1) / 2))
     attn += 16384.0 * (shape.n_layers - 1) * float(sum(int(a_len[a]) * (int(a_len[a]) + 1) / 2 for a in used))
+    if args.act_fp8:
+        desc += "; W8A8 (per-token E4M3 activations on the fp8 MFMA)"
     res = {"metric": "end-to-end prefill tokens/min (36-layer stack)", "workload": desc, "unit": "tokens/min",
            "ms": ms, "pairs": int(n), "logical_tokens": logical, "computed_tokens": suffix_tok + anchor_tok,
            "logical_tokens_per_min": logical / (ms * 1e-3) * 60.0,
@@ -1259,6 +1266,8 @@ def main():
                                            "traces36", "nested36", "search"],
                     default="join")
     ap.add_argument("--rows", type=int, default=625, help="multijoin36: rows of the 5,000 used")
+    ap.add_argument("--act-fp8", action="store_true",
+                    help="join36 / filter36 / multijoin36: per-token E4M3 activations (W8A8 projections)")
     ap.add_argument("--shared-only", action="store_true", help="shared36: run only the join with prefix nodes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

@@ -84,13 +84,21 @@ typedef int64_t quail_anchor;
  * inverse frequency rope_theta^(-2i/head_dim); RMSNorm is
  * x / sqrt(mean(x^2) + rms_eps) * gamma. Positions: anchor tokens 0..La-1,
  * suffix token j at La + j; La + Ls must not exceed max_anchor_len +
- * max_suffix_len. */
+ * max_suffix_len.
+ * act_dtype selects what the four projections read ([pt] "Como funciona":
+ * the engine's FP8 GEMMs): 0 or QUAIL_DTYPE_BF16 = bf16 activations (W8A16,
+ * the default); QUAIL_DTYPE_FP8_E4M3 = per-token E4M3 activations (W8A8: the
+ * normed inputs, the attention output and the MLP product are quantised per
+ * token as by quail_act_quant_e4m3 and the products run on the fp8 MFMA),
+ * which needs hidden a multiple of 256, intermediate of 128 and an even
+ * n_q_heads. */
 typedef struct {
     int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, vocab;
     float rope_theta, rms_eps;
     int32_t kv_dtype;
     float k_scale, v_scale;
     int32_t max_anchor_len, max_suffix_len;
+    int32_t act_dtype;
 } quail_model_config;
 
 /* One layer's weights (all dev). fp8 matrices are [out, in] E4M3 codes with
@@ -209,8 +217,9 @@ quail_status quail_ctx_check(quail_ctx* ctx, quail_stream stream, int64_t* guard
  * on, every launch of the model path is bracketed by two HIP events on its
  * stream. Kinds: 0 QKV projection (+ RoPE, KV writer), 1 O projection
  * (+ residual), 2 gate/up projection (+ SwiGLU), 3 down projection
- * (+ residual), 4 cascade attention, 5 RMSNorm, 6 other (embedding, head,
- * row copies). quail_ctx_profile(enable) switches it and discards what was
+ * (+ residual), 4 cascade attention, 5 RMSNorm (with fp8 activations also
+ * the per-token quantiser of the attention output and the MLP product),
+ * 6 other (embedding, head, row copies). quail_ctx_profile(enable) switches it and discards what was
  * recorded. quail_ctx_profile_read waits for the recorded launches and
  * returns per kind (host arrays of 7, each nullable): the launch count, the
  * summed launch durations in ms and the summed algorithmic FLOP (GEMMs

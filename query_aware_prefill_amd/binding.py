@@ -36,7 +36,8 @@ class ModelConfig(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("intermediate", C.c_int32),
                 ("vocab", C.c_int32), ("rope_theta", C.c_float), ("rms_eps", C.c_float),
                 ("kv_dtype", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float),
-                ("max_anchor_len", C.c_int32), ("max_suffix_len", C.c_int32)]
+                ("max_anchor_len", C.c_int32), ("max_suffix_len", C.c_int32),
+                ("act_dtype", C.c_int32)]
 
 
 class LayerWeights(C.Structure):

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libquail.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["attn.hip", "gemm.hip", "gemm8.hip", "misc.hip", "host.cpp"]
+SOURCES = ["attn.hip", "gemm.hip", "misc.hip", "host.cpp"]
 # Per-file flags. The attention kernels never see NaN scores (masked keys are
 # -inf), so fmax needs no NaN quieting; without this flag every row-max
 # operand read from an MFMA accumulator costs an extra canonicalizing max.

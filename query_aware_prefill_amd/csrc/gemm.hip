@@ -1,4 +1,5 @@
-// W8A16 GEMM for the decoder projections on gfx950.
+// W8A16 GEMM for the decoder projections on gfx950 (and its W8A8 variant,
+// gemm_a8_kernel, for per-token E4M3 activations).
 //
 // The model runs with FP8 weights and bf16 activations ([it] "Quail, il
 // motore di inferenza ...", second paragraph: Qwen3 4B FP8; [fa] key points:
@@ -417,8 +418,168 @@ gemm_direct_kernel(GemmParams p) {
   epilogue_staged<EPI, MB>(p, acc, lds_addr_of(&smem[0][0]) + wave * 8192, m0 + wm * MW, n_base, o_base, lane);
 }
 
+// ----------------------------------------------------------------------------
+// W8A8 kernel: E4M3 activation codes (one fp32 scale per row) times E4M3
+// weights on the fp8 MFMA, v_mfma_scale_f32_32x32x64_f8f6f4 (twice the bf16
+// rate; scale operands 127 = E8M0 2^0, so a plain product; format selectors
+// 0 = E4M3 for both operands). Same workgroup tile, wave split, tile order
+// and epilogues as gemm_direct_kernel; the k-step is 128 bytes of both
+// operands (the same MFMA time per step as the bf16 kernel's 64), staged over
+// 2 LDS stages of 64 KB. The MFMA operand layout: a lane holds 32 codes of
+// row lane % 32, lanes 0-31 one half of the MFMA's 64 k values and lanes
+// 32-63 the other; the sum over k does not depend on how a lane's values are
+// ordered as long as both operands order them alike: lane half h of MFMA
+// sub-step j holds bytes [64 j + 32 h, 64 j + 32 h + 32) of the k-step for
+// weights and activations both. LDS rows are 128 B with chunk ^= (row/2) % 8.
+// Before the epilogue each lane multiplies its token's accumulators by the
+// token's activation scale; the epilogue then applies the weight scales.
+// ----------------------------------------------------------------------------
+constexpr int kGemmA8GroupM = 2;   // token tiles per group (measured best for this kernel)
+
+// D = W . X^T on one 32x32x64 block: (w0, w1) the 32 weight codes of this
+// lane, (x0, x1) its 32 activation codes
+__device__ __forceinline__ f32x16_t mfma_f8_32x32x64(const uint4& w0, const uint4& w1, const uint4& x0,
+                                                     const uint4& x1, f32x16_t c) {
+  typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
+  const i32x8_t a = {(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+  const i32x8_t b = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(512)
+gemm_a8_kernel(GemmParams p) {
+  constexpr int BM = 256, BN = 256, WM = 4, NW = 8, MB = 2;
+  constexpr int KS = 128;                           // bytes (= k values) per step
+  constexpr int TILE = BM * KS;                     // 32 KB per operand and stage
+  constexpr int PW = TILE / 1024 / NW;              // 1-KB copies per wave per operand
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2 * TILE];
+
+  const int n_tn = (EPI == EPI_SWIGLU) ? p.N / (BN / 2) : p.N / BN;
+  const int n_tm = (p.M + BM - 1) / BM;
+  const int64_t total = (int64_t)n_tn * n_tm;
+  const int64_t wid = xcd_remap(blockIdx.x, total);
+  if (wid < 0) return;
+  const int64_t per_group = (int64_t)kGemmA8GroupM * n_tn;
+  const int64_t grp = wid / per_group;
+  const int64_t rem = wid % per_group;
+  const int gm_rows = (int)min<int64_t>(kGemmA8GroupM, n_tm - grp * kGemmA8GroupM);
+  const int tm = (int)(grp * kGemmA8GroupM + rem % gm_rows);
+  const int tn = (int)(rem / gm_rows);
+  const int m0 = tm * BM;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int wm = wave % WM;
+  const int wn = wave / WM;
+
+  auto wrow = [&](int r) -> int {
+    if (EPI == EPI_SWIGLU) {
+      const int pr = r >> 7, j = r & 63;
+      const int base = tn * (BN / 2) + pr * 64 + j;
+      return (r & 64) ? p.inter + base : base;
+    }
+    return tn * BN + r;
+  };
+  // per-lane copy sources, 8 rows x 128 B per copy (rows past M read row
+  // M - 1; their results are not stored)
+  const uint8_t* a_src[PW];
+  const uint8_t* b_src[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int row = (wave * PW + i) * 8 + (lane >> 3);
+    const int m = min(m0 + row, p.M - 1);
+    const int ma = p.a_map ? p.a_map[m] : m;
+    a_src[i] = p.A8 + (int64_t)ma * p.lda + swz_a(row, lane & 7) * 16;
+    b_src[i] = p.B + (int64_t)wrow(row) * p.K + swz_a(row, lane & 7) * 16;
+  }
+  auto issue = [&](int kt) {
+    uint8_t* st = smem[kt & 1];
+#pragma unroll
+    for (int i = 0; i < PW; ++i) copy16_to_lds(a_src[i] + kt * KS, st + (wave * PW + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < PW; ++i) copy16_to_lds(b_src[i] + kt * KS, st + TILE + (wave * PW + i) * 1024);
+  };
+
+  f32x16_t acc[MB][4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
+
+  const int nk = p.K / KS;
+  issue(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt<0>();
+    raw_barrier();                 // step kt landed everywhere; the other stage is free
+    if (kt + 1 < nk) issue(kt + 1);
+    const uint8_t* st = smem[kt & 1];
+#pragma unroll
+    for (int j = 0; j < KS / 64; ++j) {
+      const int c0 = 4 * j + 2 * hi;
+      uint4 b0[4], b1[4], a0[MB], a1[MB];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const uint8_t* rb = st + TILE + (wn * 128 + nb * 32 + l32) * KS;
+        const int row = wn * 128 + nb * 32 + l32;
+        b0[nb] = *reinterpret_cast<const uint4*>(rb + swz_a(row, c0) * 16);
+        b1[nb] = *reinterpret_cast<const uint4*>(rb + swz_a(row, c0 + 1) * 16);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int row = wm * 64 + mb * 32 + l32;
+        const uint8_t* rb = st + row * KS;
+        a0[mb] = *reinterpret_cast<const uint4*>(rb + swz_a(row, c0) * 16);
+        a1[mb] = *reinterpret_cast<const uint4*>(rb + swz_a(row, c0 + 1) * 16);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[mb][nb] = mfma_f8_32x32x64(b0[nb], b1[nb], a0[mb], a1[mb], acc[mb][nb]);
+    }
+  }
+
+  // the token's activation scale (lane = token within each 32-token block)
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = min(m0 + wm * 64 + mb * 32 + l32, p.M - 1);
+    const float sx = p.a_scale[p.a_map ? p.a_map[m] : m];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][nb][r] *= sx;
+  }
+  const int n_base = tn * BN + wn * 128;
+  const int o_base = tn * (BN / 2) + wn * 64;
+  __syncthreads();   // every wave is done with the stages: they become staging space
+  epilogue_staged<EPI, MB>(p, acc, lds_addr_of(&smem[0][0]) + wave * 8192, m0 + wm * 64, n_base, o_base, lane);
+}
+
 hipError_t launch_gemm(const GemmParams& p, GemmEpi epi, hipStream_t s) {
   if (p.M == 0) return hipSuccess;
+  if (p.A8) {
+    // 256x256 tiles only (SWIGLU: 128 output columns per tile); K in steps of 128
+    if ((epi == EPI_SWIGLU ? p.N % 128 : p.N % 256) || p.K % 128 || !p.a_scale) return hipErrorInvalidValue;
+    const int n_tn = (epi == EPI_SWIGLU) ? p.N / 128 : p.N / 256;
+    const int64_t total = (int64_t)n_tn * ((p.M + 255) / 256);
+    const int64_t grid = (total + 7) / 8 * 8;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const dim3 g((unsigned)grid);
+    switch (epi) {
+      case EPI_STORE: gemm_a8_kernel<EPI_STORE><<<g, dim3(512), 0, s>>>(p); break;
+      case EPI_RESID: gemm_a8_kernel<EPI_RESID><<<g, dim3(512), 0, s>>>(p); break;
+      case EPI_SWIGLU: gemm_a8_kernel<EPI_SWIGLU><<<g, dim3(512), 0, s>>>(p); break;
+      case EPI_QKV: gemm_a8_kernel<EPI_QKV><<<g, dim3(512), 0, s>>>(p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   // 256x256 tiles (8 waves of 64 rows x 128 columns) when the columns allow
   // (SWIGLU: 128 output columns per tile), else 256x128 (4 waves)
   const bool wide = (epi == EPI_SWIGLU) ? (p.N % 128 == 0) : (p.N % 256 == 0);

@@ -31,7 +31,6 @@
 
 #include "../../include/quail.h"
 #include "quail_internal.h"
-#include "w8a8.h"
 
 using namespace quail;
 
@@ -168,8 +167,17 @@ quail_status check_cfg(const quail_model_config* c) {
     return fail(QUAIL_E_UNSUPPORTED, "kv_dtype must be BF16 or FP8_E4M3");
   if (c->kv_dtype == QUAIL_DTYPE_FP8_E4M3 && !(c->k_scale > 0.0f && c->v_scale > 0.0f))
     return fail(QUAIL_E_INVAL, "fp8 KV needs positive k_scale and v_scale");
+  if (c->act_dtype != 0 && c->act_dtype != QUAIL_DTYPE_BF16 && c->act_dtype != QUAIL_DTYPE_FP8_E4M3)
+    return fail(QUAIL_E_UNSUPPORTED, "act_dtype must be 0, BF16 or FP8_E4M3");
+  // W8A8 tiles: 256 output columns (QKV, O, down), 128 SwiGLU columns,
+  // k-steps of 128
+  if (c->act_dtype == QUAIL_DTYPE_FP8_E4M3 && (c->hidden % 256 || c->intermediate % 128 || c->n_q_heads % 2))
+    return fail(QUAIL_E_UNSUPPORTED,
+                "fp8 activations need hidden a multiple of 256, intermediate of 128 and even n_q_heads");
   return QUAIL_OK;
 }
+
+bool act_fp8(const quail_model_config& c) { return c.act_dtype == QUAIL_DTYPE_FP8_E4M3; }
 
 size_t kv_elem_bytes(const quail_model_config& c) {
   return c.kv_dtype == QUAIL_DTYPE_FP8_E4M3 ? 1 : 2;
@@ -193,7 +201,7 @@ int32_t max_pos(const quail_model_config& c) { return c.max_anchor_len + c.max_s
 
 // Workspace carve for a context.
 struct WsLayout {
-  size_t rope, h, u, q, k, v, o, m, hlast, meta, status, guard, total;
+  size_t rope, h, u, q, k, v, o, m, hlast, xq, xs, meta, status, guard, total;
   size_t meta_cap;
 };
 
@@ -225,6 +233,13 @@ WsLayout ws_layout(const quail_model_config& c, int32_t T) {
   w.o = take(Tt * c.n_q_heads * c.head_dim * 2);
   w.m = take(Tt * c.intermediate * 2);
   w.hlast = take(Tt * c.hidden * 2);
+  if (act_fp8(c)) {
+    // per-token E4M3 codes of the widest projection input, and their scales
+    const size_t wmax = std::max<size_t>({(size_t)c.hidden, (size_t)c.n_q_heads * c.head_dim,
+                                          (size_t)c.intermediate});
+    w.xq = take(Tt * wmax);
+    w.xs = take(Tt * 4);
+  }
   w.meta_cap = meta_capacity(T, c.n_layers);
   w.meta = take(w.meta_cap);
   w.status = take(kAlign);                        // debug counters (uint32): guard errors, bad tokens
@@ -783,6 +798,12 @@ quail_status run_batch(quail_ctx* c, const Batch& b, const int32_t* tokens, uint
   const float2* rope = ws_ptr<const float2>(c, c->L.rope);
 
   uint32_t* status = ws_ptr<uint32_t>(c, c->L.status);
+  // W8A8: each projection reads per-token E4M3 codes (xq) and scales (xs) of
+  // its input; the norms write them directly, the attention output and the
+  // MLP product go through the quantiser
+  const bool a8 = act_fp8(cf);
+  uint8_t* xq = a8 ? c->ws + c->L.xq : nullptr;
+  float* xs = a8 ? ws_ptr<float>(c, c->L.xs) : nullptr;
   // A join batch whose only output is each pair's last row (h_last, no
   // h_all) needs, at the last layer, every row's K/V and attention (the last
   // rows attend to them) but the O projection, the MLP and their residual
@@ -798,10 +819,12 @@ quail_status run_batch(quail_ctx* c, const Batch& b, const int32_t* tokens, uint
     NormParams np{};
     np.x = hbuf; np.ldx = H; np.gamma = lw.attn_norm; np.y = ubuf; np.ldy = H;
     np.rows = n; np.H = H; np.eps = cf.rms_eps;
+    np.yq = xq; np.ys = xs;
     TIMED(PK_NORM, 0, launch_rmsnorm(np, s));
 
     GemmParams gp{};
     gp.A = ubuf; gp.lda = H; gp.B = lw.w_qkv; gp.scale = lw.s_qkv;
+    gp.A8 = xq; gp.a_scale = xs;
     gp.M = n; gp.N = (Hq + 2 * Hkv) * kHeadDim; gp.K = H;
     gp.hq = Hq; gp.hkv = Hkv; gp.rope = rope; gp.pos = d_pos; gp.q_out = qbuf;
     gp.layer = l;
@@ -837,8 +860,10 @@ quail_status run_batch(quail_ctx* c, const Batch& b, const int32_t* tokens, uint
     const int32_t m = tail ? n_last : n;
     const int32_t* rmap = tail ? d_last : nullptr;
 
+    if (a8) TIMED(PK_NORM, 0, launch_act_quant_e4m3(n, Hq * kHeadDim, obuf, xq, xs, s));
     GemmParams go{};
     go.A = obuf; go.lda = (int64_t)Hq * kHeadDim; go.B = lw.w_o; go.scale = lw.s_o;
+    go.A8 = xq; go.a_scale = xs;
     go.M = m; go.N = H; go.K = Hq * kHeadDim; go.Yf = hbuf; go.ldy = H;
     go.a_map = rmap; go.y_map = rmap;
     TIMED(PK_O, 2.0 * m * go.N * go.K, launch_gemm(go, EPI_RESID, s));
@@ -849,10 +874,13 @@ quail_status run_batch(quail_ctx* c, const Batch& b, const int32_t* tokens, uint
     GemmParams gg{};
     gg.A = ubuf; gg.lda = H; gg.B = lw.w_gate_up; gg.scale = lw.s_gate_up;
     gg.M = m; gg.N = I; gg.K = H; gg.Y = mbuf; gg.ldy = I; gg.inter = I;
+    gg.A8 = xq; gg.a_scale = xs;
     TIMED(PK_GATE_UP, 2.0 * m * 2.0 * gg.N * gg.K, launch_gemm(gg, EPI_SWIGLU, s));
 
+    if (a8) TIMED(PK_NORM, 0, launch_act_quant_e4m3(m, I, mbuf, xq, xs, s));
     GemmParams gd{};
     gd.A = mbuf; gd.lda = I; gd.B = lw.w_down; gd.scale = lw.s_down;
+    gd.A8 = xq; gd.a_scale = xs;
     gd.M = m; gd.N = H; gd.K = I; gd.Yf = hbuf; gd.ldy = H;
     gd.y_map = rmap;
     TIMED(PK_DOWN, 2.0 * m * gd.N * gd.K, launch_gemm(gd, EPI_RESID, s));
@@ -2474,9 +2502,10 @@ quail_status quail_gemm_w8a8(int32_t M, int32_t N, int32_t K, const uint8_t* xc,
   if (!aligned_to(xc, 16) || !aligned_to(wc, 16) || !aligned_to(y, 16) || !aligned_to(w_scale, 8) ||
       !aligned_to(x_scale, 4))
     return fail(QUAIL_E_UNSUPPORTED, "xc, wc and y must be 16-byte aligned, w_scale 8-byte");
-  W8A8Params p{};
-  p.A = xc; p.a_scale = x_scale; p.B = wc; p.b_scale = w_scale; p.Y = y; p.M = M; p.N = N; p.K = K;
-  HIP_TRY(launch_gemm_w8a8(p, as_stream(stream)));
+  GemmParams p{};
+  p.A8 = xc; p.lda = K; p.a_scale = x_scale; p.B = wc; p.scale = w_scale;
+  p.M = M; p.N = N; p.K = K; p.Y = y; p.ldy = N;
+  HIP_TRY(launch_gemm(p, EPI_STORE, as_stream(stream)));
   return QUAIL_OK;
 }
 

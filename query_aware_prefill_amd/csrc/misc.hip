@@ -135,11 +135,91 @@ hipError_t launch_copy_slab_rows(const uint8_t* src, int64_t src_block, uint8_t*
   return hipGetLastError();
 }
 
+// Per-token E4M3 quantisation of bf16 rows (the W8A8 projections' inputs):
+// amax = the row's largest magnitude, code = E4M3(x * (448 / amax)) with the
+// division and the product single fp32 operations, scale = amax / 448; a row
+// of zeros gets codes 0 and scale 0. Helpers shared by the quantiser and the
+// RMSNorm that emits codes directly.
+__device__ __forceinline__ float absmax_bf16x8(const uint4& v, float m) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    m = fmaxf(m, fmaxf(__uint_as_float((w[e] & 0x7FFFu) << 16), __uint_as_float(w[e] & 0x7FFF0000u)));
+  return m;
+}
+
+// 8 bf16 -> 8 E4M3 codes of x * inv (byte i = element i); inv == 0 (a row of
+// zeros) gives codes 0, also for -0 elements
+__device__ __forceinline__ uint2 quant_bf16x8(const uint4& v, float inv) {
+  if (inv == 0.0f) return make_uint2(0, 0);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t c[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    c[e] = f32_to_e4m3(__uint_as_float(w[e] << 16) * inv) |
+           (f32_to_e4m3(__uint_as_float(w[e] & 0xFFFF0000u) * inv) << 8);
+  return make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16));
+}
+
+__device__ __forceinline__ float quant_inv(float amax) { return amax > 0.0f ? 448.0f / amax : 0.0f; }
+__device__ __forceinline__ float quant_scale(float amax) { return amax > 0.0f ? amax / 448.0f : 0.0f; }
+
+// One wave per row of K bf16 values; rows of up to 64 * 8 * kQuantChunks
+// values stay in registers between the max pass and the encode pass (longer
+// rows are read twice, the second read from the cache).
+constexpr int kQuantChunks = 20;
+
+__global__ void __launch_bounds__(256)
+act_quant_e4m3_kernel(int32_t M, int32_t K, const uint16_t* __restrict__ x, uint8_t* __restrict__ codes,
+                      float* __restrict__ scale) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (int64_t)row * K);
+  uint2* cr = reinterpret_cast<uint2*>(codes + (int64_t)row * K);
+  const int n8 = K / 8;
+  if (n8 <= 64 * kQuantChunks) {
+    uint4 v[kQuantChunks];
+    float m = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kQuantChunks; ++c) {
+      const int i = c * 64 + lane;
+      v[c] = i < n8 ? xr[i] : make_uint4(0, 0, 0, 0);
+      m = absmax_bf16x8(v[c], m);
+    }
+    const float amax = wave_max(m);
+    const float inv = quant_inv(amax);
+#pragma unroll
+    for (int c = 0; c < kQuantChunks; ++c) {
+      const int i = c * 64 + lane;
+      if (i < n8) cr[i] = quant_bf16x8(v[c], inv);
+    }
+    if (lane == 0) scale[row] = quant_scale(amax);
+    return;
+  }
+  float m = 0.0f;
+  for (int i = lane; i < n8; i += 64) m = absmax_bf16x8(xr[i], m);
+  const float amax = wave_max(m);
+  const float inv = quant_inv(amax);
+  for (int i = lane; i < n8; i += 64) cr[i] = quant_bf16x8(xr[i], inv);
+  if (lane == 0) scale[row] = quant_scale(amax);
+}
+
+hipError_t launch_act_quant_e4m3(int32_t M, int32_t K, const uint16_t* x, uint8_t* codes, float* scale,
+                                 hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  act_quant_e4m3_kernel<<<dim3((M + 3) / 4), dim3(256), 0, s>>>(M, K, x, codes, scale);
+  return hipGetLastError();
+}
+
 // y = bf16(x / sqrt(mean(x^2) + eps) * gamma), x an fp32 residual row, one
 // wave per row; 8 columns per lane and chunk (two 16-B loads, one 16-B
 // store). Up to kNormChunks chunks per lane stay in registers: rows of up to
 // 64 * 8 * 8 = 4096 columns are read once, with all their loads in flight
 // together; longer rows are read a second time for the output pass.
+// Q: instead of the bf16 row, its per-token E4M3 codes (yq, row stride H)
+// and scale (ys), quantised from the bf16 values exactly as the standalone
+// quantiser would (long rows recompute the bf16 values for each pass).
 constexpr int kNormChunks = 8;
 
 // bf16(x * inv * gamma) of one 8-column chunk
@@ -155,14 +235,16 @@ __device__ __forceinline__ uint4 norm_chunk(const float4& a, const float4& b, fl
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-__global__ void __launch_bounds__(256) rmsnorm_kernel(NormParams p) {
+template <bool Q>
+__device__ __forceinline__ void rmsnorm_row(const NormParams& p) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= p.rows) return;
   const int src = p.row_map ? p.row_map[r] : r;
   const float4* x = reinterpret_cast<const float4*>(p.x + (int64_t)src * p.ldx);
   const int nc = p.H / 8;
-  uint4* y = reinterpret_cast<uint4*>(p.y + (int64_t)r * p.ldy);
+  uint4* y = Q ? nullptr : reinterpret_cast<uint4*>(p.y + (int64_t)r * p.ldy);
+  uint2* yq = Q ? reinterpret_cast<uint2*>(p.yq + (int64_t)r * p.H) : nullptr;
   const uint4* gm = reinterpret_cast<const uint4*>(p.gamma);
   // per lane, chunks lane, lane + 64, ... in order (the same summation order
   // in both branches)
@@ -184,11 +266,30 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(NormParams p) {
               b[i].y * b[i].y + b[i].z * b[i].z + b[i].w * b[i].w;
     ss = wave_sum(ss);
     const float inv = 1.0f / sqrtf(ss / (float)p.H + p.eps);
+    if (!Q) {
+#pragma unroll
+      for (int i = 0; i < kNormChunks; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nc) y[c] = norm_chunk(a[i], b[i], inv, gm, c);
+      }
+      return;
+    }
+    uint4 yv[kNormChunks];
+    float mx = 0.0f;
 #pragma unroll
     for (int i = 0; i < kNormChunks; ++i) {
       const int c = lane + 64 * i;
-      if (c < nc) y[c] = norm_chunk(a[i], b[i], inv, gm, c);
+      yv[i] = c < nc ? norm_chunk(a[i], b[i], inv, gm, c) : make_uint4(0, 0, 0, 0);
+      mx = absmax_bf16x8(yv[i], mx);
     }
+    const float amax = wave_max(mx);
+    const float qi = quant_inv(amax);
+#pragma unroll
+    for (int i = 0; i < kNormChunks; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nc) yq[c] = quant_bf16x8(yv[i], qi);
+    }
+    if (lane == 0) p.ys[r] = quant_scale(amax);
     return;
   }
   float ss = 0.0f;
@@ -198,12 +299,25 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(NormParams p) {
   }
   ss = wave_sum(ss);
   const float inv = 1.0f / sqrtf(ss / (float)p.H + p.eps);
-  for (int c = lane; c < nc; c += 64) y[c] = norm_chunk(x[2 * c], x[2 * c + 1], inv, gm, c);
+  if (!Q) {
+    for (int c = lane; c < nc; c += 64) y[c] = norm_chunk(x[2 * c], x[2 * c + 1], inv, gm, c);
+    return;
+  }
+  float mx = 0.0f;
+  for (int c = lane; c < nc; c += 64) mx = absmax_bf16x8(norm_chunk(x[2 * c], x[2 * c + 1], inv, gm, c), mx);
+  const float amax = wave_max(mx);
+  const float qi = quant_inv(amax);
+  for (int c = lane; c < nc; c += 64) yq[c] = quant_bf16x8(norm_chunk(x[2 * c], x[2 * c + 1], inv, gm, c), qi);
+  if (lane == 0) p.ys[r] = quant_scale(amax);
 }
+
+__global__ void __launch_bounds__(256) rmsnorm_kernel(NormParams p) { rmsnorm_row<false>(p); }
+__global__ void __launch_bounds__(256) rmsnorm_quant_kernel(NormParams p) { rmsnorm_row<true>(p); }
 
 hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s) {
   if (p.rows == 0) return hipSuccess;
-  rmsnorm_kernel<<<dim3((p.rows + 3) / 4), dim3(256), 0, s>>>(p);
+  if (p.yq) rmsnorm_quant_kernel<<<dim3((p.rows + 3) / 4), dim3(256), 0, s>>>(p);
+  else rmsnorm_kernel<<<dim3((p.rows + 3) / 4), dim3(256), 0, s>>>(p);
   return hipGetLastError();
 }
 

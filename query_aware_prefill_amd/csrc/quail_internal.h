@@ -75,6 +75,8 @@ enum GemmEpi : int32_t {
 
 struct GemmParams {
   const uint16_t* A; int64_t lda;        // bf16 [M][K]
+  const uint8_t* A8;                     // W8A8 (instead of A): E4M3 codes [M][K], row stride lda bytes
+  const float* a_scale;                  // W8A8: one scale per row of A8
   const int32_t* a_map;                  // optional: A row m is row a_map[m] of A
   const int32_t* y_map;                  // optional (RESID): output row m adds into Yf row y_map[m]
   const uint8_t* B;                      // fp8 [N_rows][K]
@@ -102,6 +104,7 @@ struct NormParams {
   const float* x; int64_t ldx;           // fp32 residual rows
   const uint16_t* gamma;                 // bf16 [H] (null: gain 1)
   uint16_t* y; int64_t ldy;
+  uint8_t* yq; float* ys;                // optional (instead of y): per-token E4M3 codes [rows][H] and scales
   const int32_t* row_map;                // optional: y row r reads x row row_map[r]
   int32_t rows, H;
   float eps;
@@ -136,8 +139,13 @@ int attn_tile_tokens(int group, int pack);
 // query tokens per anchor
 int attn_pack_waves(int group, int max_run);
 hipError_t launch_attn_f32(const AttnF32Params& p, hipStream_t s);
+// A8 set: the W8A8 kernel (fp8 MFMA; N a multiple of 256, SWIGLU of 128, K of 128)
 hipError_t launch_gemm(const GemmParams& p, GemmEpi epi, hipStream_t s);
 hipError_t launch_rmsnorm(const NormParams& p, hipStream_t s);
+// codes[m][k] = E4M3(x[m][k] * (448 / amax_m)), scale[m] = amax_m / 448 (x bf16
+// [M][K], K a multiple of 8; a row of zeros: codes 0, scale 0)
+hipError_t launch_act_quant_e4m3(int32_t M, int32_t K, const uint16_t* x, uint8_t* codes, float* scale,
+                                 hipStream_t s);
 // h (fp32) = embedding rows; token ids outside [0, vocab) embed row 0 and are
 // counted in *bad (nullable)
 hipError_t launch_embed(const int32_t* tokens, const int32_t* tok_map, const uint16_t* embed,

@@ -28,7 +28,8 @@ def model_config(shape, max_anchor_len: int, max_suffix_len: int) -> B.ModelConf
         vocab=shape.vocab, rope_theta=shape.rope_theta, rms_eps=shape.rms_eps,
         kv_dtype=B.DTYPE_FP8_E4M3 if shape.kv_fp8 else B.DTYPE_BF16,
         k_scale=shape.k_scale, v_scale=shape.v_scale,
-        max_anchor_len=max_anchor_len, max_suffix_len=max_suffix_len)
+        max_anchor_len=max_anchor_len, max_suffix_len=max_suffix_len,
+        act_dtype=B.DTYPE_FP8_E4M3 if getattr(shape, "act_fp8", False) else B.DTYPE_BF16)
 
 
 class DeviceModel:

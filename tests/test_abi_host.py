@@ -480,3 +480,24 @@ def test_w8a8_argument_checks():
     assert lib.quail_gemm_w8a8(4, 256, 128, fake, fake, None, fake, fake, None) == B.E_INVAL
     assert lib.quail_gemm_w8a8(4, 256, 128, fake, fake, fake, fake + 4, fake, None) == B.E_UNSUPPORTED
     assert lib.quail_gemm_w8a8(0, 256, 128, None, None, None, None, None, None) == B.OK
+
+
+def test_act_dtype_validation_and_workspace():
+    """act_dtype: 0 and BF16 are W8A16, FP8_E4M3 is W8A8 (needs hidden % 256,
+    intermediate % 128 and even n_q_heads); W8A8 workspaces add the codes of
+    the widest projection input and one scale per token."""
+    lib = B.load()
+    out = C.c_size_t()
+    base = {}
+    for a in (0, B.DTYPE_BF16):
+        cfg = _cfg(act_dtype=a)
+        assert lib.quail_workspace_bytes(C.byref(cfg), 64, C.byref(out)) == B.OK
+        base[a] = out.value
+    assert base[0] == base[B.DTYPE_BF16]
+    cfg = _cfg(act_dtype=B.DTYPE_FP8_E4M3)
+    assert lib.quail_workspace_bytes(C.byref(cfg), 64, C.byref(out)) == B.OK
+    assert out.value >= base[0] + 64 * 9728 + 64 * 4
+    for bad in (_cfg(act_dtype=3), _cfg(act_dtype=B.DTYPE_FP8_E4M3, hidden=2560 + 128),
+                _cfg(act_dtype=B.DTYPE_FP8_E4M3, intermediate=9728 + 64),
+                _cfg(act_dtype=B.DTYPE_FP8_E4M3, n_q_heads=1, n_kv_heads=1)):
+        assert lib.quail_workspace_bytes(C.byref(bad), 64, C.byref(out)) == B.E_UNSUPPORTED
