@@ -1028,6 +1028,65 @@ JOIN_ANCHORS, JOIN_SUFFIXES, JOIN_LA, JOIN_LS = 64, 2048, 1024, 64
 ANCHORS_PER_STEP = 2
 
 
+def w8a8_join_field(args, B, shape, dm, inputs, step_inputs, logits, dec, per_step_pairs, logical, T):
+    """The headline join steps again on a context whose projections read
+    per-token E4M3 activations (act_dtype FP8_E4M3), same weights and inputs:
+    ms per step, logical tokens/min, the gate/up launch against the fp8 MFMA
+    peak, and how far its logits and decisions are from the W8A16 run of the
+    last step (the precision this mode gives up)."""
+    import dataclasses
+    import torch
+    from query_aware_prefill_amd.device import model_config
+    shape8 = dataclasses.replace(shape, act_fp8=True)
+    cfg8 = model_config(shape8, JOIN_LA, JOIN_LS)
+    pool = torch.empty(ANCHORS_PER_STEP * B.quail_anchor_bytes(cfg8, JOIN_LA) + (1 << 20), dtype=torch.uint8,
+                       device="cuda")
+    ws = torch.empty(B.quail_workspace_bytes(cfg8, T), dtype=torch.uint8, device="cuda")
+    ctx8 = B.Context(cfg8, dm.weights, pool, ws, T)
+    stream = torch.cuda.current_stream()
+    last = args.warmup + args.steps - 1
+    ref_lg, ref_dec = logits.cpu().numpy().astype(np.float64), dec.cpu().numpy()   # W8A16, step `last`
+    lg8 = torch.empty_like(logits)
+    dec8 = torch.empty_like(dec)
+    n_steps = min(args.steps, 10)
+    ks = list(range(last - n_steps + 1, last + 1))
+
+    def step(k):
+        at, ao, pa, st, so, _, _ = inputs[k]
+        B.quail_join_run(ctx8, at, ao, pa, st, so, 0x0F, lg8, None, dec8, stream=stream)
+
+    for k in range(min(args.warmup, 2)):
+        step(k)
+    torch.cuda.synchronize()
+    B.quail_ctx_profile(ctx8, True)
+    t0 = time.perf_counter()
+    for k in ks:
+        step(k)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    prof = B.quail_ctx_profile_read(ctx8)
+    B.quail_ctx_profile(ctx8, False)
+    ms_step = el * 1000.0 / n_steps
+    gu = prof["gate_up"]
+    gu_ms = gu["ms"] / gu["launches"]
+    gu_tf = gu["flop"] / gu["launches"] / (gu_ms * 1e-3) / 1e12
+    gemm_ms = sum(prof[k]["ms"] for k in ("qkv", "o", "gate_up", "down"))
+    gemm_flop = sum(prof[k]["flop"] for k in ("qkv", "o", "gate_up", "down"))
+    g8 = lg8.cpu().numpy().astype(np.float64)
+    out = {"steps": n_steps, "ms_per_step": ms_step, "logical_tokens_per_min": logical / (ms_step * 1e-3) * 60.0,
+           "gate_up": {"kernel": "quail::gemm_a8_kernel<2>", "launch_ms": gu_ms, "tflops": gu_tf,
+                       "frac_of_fp8_peak": gu_tf / PEAK_FP8_TFLOPS},
+           "gemm_all_tflops": gemm_flop / (gemm_ms * 1e-3) / 1e12, "gemm_share_of_step": gemm_ms / (el * 1000.0),
+           "norm_and_quant_share_of_step": prof["norm"]["ms"] / (el * 1000.0),
+           "vs_w8a16_last_step": {"logits_rel_inf": float(np.max(np.abs(g8 - ref_lg)) / np.max(np.abs(ref_lg))),
+                                  "decisions_equal": float(np.mean(dec8.cpu().numpy() == ref_dec))}}
+    log(f"join w8a8: step {ms_step:.1f} ms, {out['logical_tokens_per_min'] / 1e6:.1f} M logical tok/min; gate/up "
+        f"{gu_ms:.3f} ms, {gu_tf:.1f} TFLOP/s; logits {out['vs_w8a16_last_step']['logits_rel_inf']:.4f} from W8A16, "
+        f"decisions {out['vs_w8a16_last_step']['decisions_equal']:.4f} equal")
+    del ctx8
+    return out
+
+
 def bench_join(args):
     """Headline: the 36-layer join, one step = two anchors with all their pairs."""
     import torch
@@ -1142,6 +1201,11 @@ def bench_join(args):
             "workload": c1["config"]["workload"], "tflops": c1["roofline"]["achieved"],
             "frac": c1["roofline"]["frac"], "launch_ms": c1["roofline"]["launch_ms"],
             "kernel": c1["roofline"]["kernel"], "traffic": c1["roofline"]["traffic"]}
+    # the same steps with per-token E4M3 activations (W8A8 projections on the
+    # fp8 MFMA): an opt-in mode outside the W8A16 contract, timed as a field
+    if not args.no_w8a8:
+        res["config"]["w8a8_same_steps"] = w8a8_join_field(args, B, shape, dm, inputs, step_inputs, logits, dec,
+                                                           per_step_pairs, logical, T)
     if not args.no_cpu_baseline:
         lg = logits.cpu().numpy().astype(np.float64)
         at, ao, pa, st_, so, a0, p0 = inputs[args.warmup + args.steps - 1]
@@ -1266,6 +1330,8 @@ def main():
                                            "traces36", "nested36", "search"],
                     default="join")
     ap.add_argument("--rows", type=int, default=625, help="multijoin36: rows of the 5,000 used")
+    ap.add_argument("--no-w8a8", action="store_true",
+                    help="headline: skip the W8A8 run of the same steps (a field of the line)")
     ap.add_argument("--act-fp8", action="store_true",
                     help="join36 / filter36 / multijoin36: per-token E4M3 activations (W8A8 projections)")
     ap.add_argument("--shared-only", action="store_true", help="shared36: run only the join with prefix nodes")

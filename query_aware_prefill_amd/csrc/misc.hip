@@ -164,14 +164,14 @@ __device__ __forceinline__ uint2 quant_bf16x8(const uint4& v, float inv) {
 __device__ __forceinline__ float quant_inv(float amax) { return amax > 0.0f ? 448.0f / amax : 0.0f; }
 __device__ __forceinline__ float quant_scale(float amax) { return amax > 0.0f ? amax / 448.0f : 0.0f; }
 
-// One wave per row of K bf16 values; rows of up to 64 * 8 * kQuantChunks
-// values stay in registers between the max pass and the encode pass (longer
-// rows are read twice, the second read from the cache).
-constexpr int kQuantChunks = 20;
-
+// One wave per row of K bf16 values; rows of up to 64 * 8 * CH values stay
+// in registers between the max pass and the encode pass (longer rows are read
+// twice, the second read from the cache).
+template <int CH>
 __global__ void __launch_bounds__(256)
 act_quant_e4m3_kernel(int32_t M, int32_t K, const uint16_t* __restrict__ x, uint8_t* __restrict__ codes,
                       float* __restrict__ scale) {
+  constexpr int kQuantChunks = CH;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= M) return;
@@ -205,10 +205,48 @@ act_quant_e4m3_kernel(int32_t M, int32_t K, const uint16_t* __restrict__ x, uint
   if (lane == 0) scale[row] = quant_scale(amax);
 }
 
+// Long rows (up to 256 * 8 * CH values, e.g. the 9728-wide MLP product):
+// one workgroup of 4 waves per row, each thread holding CH 8-value chunks, the
+// row maximum combined across the waves through LDS (a maximum is exact, so
+// the result is the same as the one-wave kernel's).
+template <int CH>
+__global__ void __launch_bounds__(256)
+act_quant_e4m3_row_kernel(int32_t K, const uint16_t* __restrict__ x, uint8_t* __restrict__ codes,
+                          float* __restrict__ scale) {
+  __shared__ float wmax[4];
+  const int row = blockIdx.x;
+  const int t = threadIdx.x;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (int64_t)row * K);
+  uint2* cr = reinterpret_cast<uint2*>(codes + (int64_t)row * K);
+  const int n8 = K / 8;
+  uint4 v[CH];
+  float m = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int i = c * 256 + t;
+    v[c] = i < n8 ? xr[i] : make_uint4(0, 0, 0, 0);
+    m = absmax_bf16x8(v[c], m);
+  }
+  m = wave_max(m);
+  if ((t & 63) == 0) wmax[t >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float inv = quant_inv(amax);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int i = c * 256 + t;
+    if (i < n8) cr[i] = quant_bf16x8(v[c], inv);
+  }
+  if (t == 0) scale[row] = quant_scale(amax);
+}
+
 hipError_t launch_act_quant_e4m3(int32_t M, int32_t K, const uint16_t* x, uint8_t* codes, float* scale,
                                  hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  act_quant_e4m3_kernel<<<dim3((M + 3) / 4), dim3(256), 0, s>>>(M, K, x, codes, scale);
+  if (K > 64 * 8 * 8 && K <= 256 * 8 * 8)
+    act_quant_e4m3_row_kernel<8><<<dim3((unsigned)M), dim3(256), 0, s>>>(K, x, codes, scale);
+  else
+    act_quant_e4m3_kernel<8><<<dim3((M + 3) / 4), dim3(256), 0, s>>>(M, K, x, codes, scale);
   return hipGetLastError();
 }
 

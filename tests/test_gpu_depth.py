@@ -55,13 +55,13 @@ def setup():
     return B, dm, cases, doc, G
 
 
-def _run(B, dm, case, depth, fp8, run):
+def _run(B, dm, case, depth, fp8, run, act_fp8=False):
     """The case through the first `depth` layers by entry point `run`
     (quail_join_run, quail_multijoin_run with a pool for the two largest
     anchors, or quail_join_run_shared); returns logits and decisions."""
     import torch
     from query_aware_prefill_amd.device import model_config, to_device
-    shape = dataclasses.replace(W.QWEN3_4B, n_layers=depth, kv_fp8=fp8)
+    shape = dataclasses.replace(W.QWEN3_4B, n_layers=depth, kv_fp8=fp8, act_fp8=act_fp8)
     cfg = model_config(shape, 128, 64)
     slabs = sorted(B.quail_anchor_bytes(cfg, int(x)) for x in case["a_len"])
     if run == "quail_multijoin_run":
@@ -128,3 +128,49 @@ def test_full_depth_join_against_oracle(setup, name):
         assert agree == n_sure, (name, depth, agree, n_sure)
     if name == "bf16":
         assert rows[-1][2] >= 64, rows[-1]
+
+
+GOLDEN_W8A8 = os.path.join(os.path.dirname(GOLDEN), "depth36_qwen3_w8a8.json")
+SENSITIVITY_W8A8 = os.path.join(os.path.dirname(GOLDEN), "depth36_qwen3_w8a8_sensitivity.json")
+
+
+def w8a8_bars():
+    """Per depth: twice the distance by which the oracle's own W8A8 logits
+    move when one-ulp bf16 disagreements are planted in 1% of its bf16 values
+    (tests/golden/make_w8a8_sensitivity.py), and never below the 2e-2 bar.
+    E4M3 codes are decided from bf16 values, so two correct implementations
+    whose bf16 roundings differ in a few places differ by about that much; the
+    GPU's first-layer K/V bf16 values differ from the oracle's in 0.1% (W8A16)
+    and 1.1% (W8A8) of elements."""
+    doc = json.load(open(SENSITIVITY_W8A8))
+    return {int(d): max(2e-2, 2.0 * v) for d, v in doc["fractions"]["0.01"].items()}
+
+
+def test_full_depth_w8a8_join_against_oracle(setup):
+    """The bf16-KV join through the 36-layer stack with per-token E4M3
+    activations (W8A8) against the oracle's W8A8 reading
+    (tests/golden/depth36_qwen3_w8a8.json, tests/golden/make_depth36_w8a8.py)
+    at depths 1, 4, 12 and 36: logits within the bar above, decisions equal
+    wherever the oracle's margin exceeds the bar times the largest logit
+    (bars from w8a8_bars)."""
+    B, dm, cases, doc, G = setup
+    d8 = json.load(open(GOLDEN_W8A8))
+    assert d8["inputs_sha256_16"] == doc["inputs_sha256_16"]
+    bars = w8a8_bars()
+    case = cases[d8["case"]]
+    rows = []
+    for depth in d8["taps"]:
+        ref = d8["results"][str(depth)]
+        ref_logits = np.array(ref["logits"])
+        say(f"depth36 w8a8: {depth} layers, {len(ref_logits)} pairs")
+        lg, dec = _run(B, dm, case, depth, False, "quail_join_run", act_fp8=True)
+        err = float(np.max(np.abs(lg - ref_logits)) / np.max(np.abs(ref_logits)))
+        sure = np.abs(np.array(ref["margin"])) > bars[depth] * float(np.max(np.abs(ref_logits)))
+        agree = int(np.sum(dec[sure] == np.array(ref["decision"])[sure]))
+        all_agree = int(np.sum(dec == np.array(ref["decision"])))
+        rows.append((depth, err, int(sure.sum()), agree))
+        say(f"  depth {depth:2d}: logits rel err {err:.4f} (bar {bars[depth]:.4f}); decisions beyond the bar "
+            f"{agree}/{int(sure.sum())} agree; all decisions {all_agree}/{len(dec)}")
+    for depth, err, n_sure, agree in rows:
+        assert err <= bars[depth], (depth, err, bars[depth])
+        assert agree == n_sure, (depth, agree, n_sure)

@@ -51,7 +51,9 @@ def _quant(B, x):
     return codes, scale
 
 
-@pytest.mark.parametrize("M,K", [(1, 8), (6, 64), (37, 2560), (9, 4096), (7, 4104), (11, 9728)])
+# one wave per row up to 4096 values; one workgroup per row up to 16384
+# (4104, 9728); beyond that the one-wave kernel reads the row twice (16392)
+@pytest.mark.parametrize("M,K", [(1, 8), (6, 64), (37, 2560), (9, 4096), (7, 4104), (11, 9728), (6, 16392)])
 def test_act_quant_bit_exact(B, M, K):
     say("act quant", M, K)
     r = np.random.default_rng(M * 31 + K)

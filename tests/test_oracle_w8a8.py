@@ -113,3 +113,26 @@ def test_product_within_the_activation_rounding_bound():
     assert np.all(np.abs(y8 - y16) <= bound * (1 + 1e-9) + 1e-12)
     # and the error is not trivially zero (the rows are not representable)
     assert np.abs(y8 - y16).max() > 0
+
+
+def test_w8a8_depth_golden_files_are_consistent():
+    """The full-depth W8A8 golden file and its sensitivity file describe the
+    same inputs as the W8A16 golden file; the W8A8 logits differ from the
+    W8A16 ones (the reading is applied) by a few percent; the oracle's own
+    movement under planted one-ulp disagreements grows with depth."""
+    import json
+    import os
+    gdir = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    base = json.load(open(os.path.join(gdir, "depth36_qwen3.json")))
+    g8 = json.load(open(os.path.join(gdir, "depth36_qwen3_w8a8.json")))
+    sens = json.load(open(os.path.join(gdir, "depth36_qwen3_w8a8_sensitivity.json")))
+    assert g8["inputs_sha256_16"] == base["inputs_sha256_16"] == sens["inputs_sha256_16"]
+    assert g8["taps"] == sens["taps"] == [1, 4, 12, 36]
+    for d in g8["taps"]:
+        a = np.array(g8["results"][str(d)]["logits"])
+        b = np.array(base["results"][g8["case"]][str(d)]["logits"])
+        rel = np.max(np.abs(a - b)) / np.max(np.abs(b))
+        assert 1e-3 < rel < 0.2, (d, rel)
+    for frac, per_depth in sens["fractions"].items():
+        v = [per_depth[str(d)] for d in sens["taps"]]
+        assert all(x > 0 for x in v) and v == sorted(v), (frac, v)
