@@ -4,6 +4,8 @@ forward: anchor prefill + KV writer, join prefill (last and all rows), the
 8-column head and its booleans, the pruned last layer, the whole-join entry
 point, and one Qwen3-4B-shaped layer."""
 import dataclasses
+import json
+import os
 
 import numpy as np
 import pytest
@@ -193,3 +195,60 @@ def test_w8a8_qwen3_shaped_layer(B):
         rms = float(np.sqrt(np.mean((got - h[len(at):]) ** 2) / np.mean(h[len(at):] ** 2)))
         say("  pair", i, "rel", err, "rms rel", rms)
         assert err <= W8A8_LAYER_BAR and rms <= W8A8_LAYER_BAR
+
+
+LAYER_SENSITIVITY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                 "w8a8_layer_sensitivity.json")
+
+
+def test_w8a8_full_size_layer_sampled(B):
+    """The one-layer join workload at full size with fp8 activations, in the
+    launch configuration the bench times (16 anchors x 1024 tokens, 512
+    suffixes x 64 tokens each, 8,192 pairs, 65,536-token batches, Qwen3-4B
+    layer shapes, the pruned last layer): sampled pairs' logits against the
+    oracle's W8A8 per-pair forward stored by
+    tests/golden/make_w8a8_layer_sensitivity.py, within twice the largest
+    movement of those logits under one-ulp bf16 disagreements planted in 1%
+    of the oracle's bf16 values (never below 2e-2); decisions where the
+    margin exceeds that bar; every pair by properties (finite logits,
+    decision = the mask bit of its logits' first argmax, identical bits on a
+    second run)."""
+    import torch
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    gold = json.load(open(LAYER_SENSITIVITY))
+    bar = max(2e-2, 2.0 * max(p["moved_rel"] for p in gold["pairs"].values()))
+    shape = W.ModelShape(n_layers=1, hidden=2560, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                         intermediate=9728, vocab=W.QWEN3_4B.vocab, act_fp8=True)
+    say("w8a8 full size: weights and workload; bar", bar)
+    wts = W.model_weights(shape, 0)
+    case = W.c2_case(seed=2)
+    n = len(case["pair_anchor"])
+    dm = DeviceModel(shape, wts, max_anchor_len=1024, max_suffix_len=64)
+    ctx = dm.context(16 * B.quail_anchor_bytes(dm.cfg, 1024) + (1 << 20), 65536)
+    logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+    dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+    say("w8a8 full size: join_run over", n, "pairs")
+    B.quail_join_run(ctx, to_device(case["a_tok"]), case["a_off"], case["pair_anchor"], to_device(case["s_tok"]),
+                     case["s_off"], 0x0F, logits, None, dec)
+    torch.cuda.synchronize()
+    lg, dg = logits.cpu().numpy(), dec.cpu().numpy()
+    st = B.quail_pool_stats(ctx)
+    assert st["prefills"] == 16 and st["evictions"] == 16 and st["regret_tokens"] == 0
+    for key, ref in gold["pairs"].items():
+        i = int(key)
+        ref_logits = np.array(ref["logits"])
+        err = rel_inf(lg[i], ref_logits)
+        say("  pair", i, "rel", err, "(the oracle's own movement", ref["moved_rel"], ")")
+        assert err <= bar, (i, err, bar)
+        if abs(ref["margin"]) > bar * np.max(np.abs(ref_logits)):
+            assert dg[i] == ref["decision"], i
+    say("w8a8 full size: properties of every pair and a second run")
+    assert np.isfinite(lg).all()
+    assert np.array_equal(dg, ((0x0F >> np.argmax(lg, axis=1)) & 1).astype(np.uint8))
+    logits2 = torch.empty_like(logits)
+    dec2 = torch.empty_like(dec)
+    B.quail_join_run(ctx, to_device(case["a_tok"]), case["a_off"], case["pair_anchor"], to_device(case["s_tok"]),
+                     case["s_off"], 0x0F, logits2, None, dec2)
+    torch.cuda.synchronize()
+    assert np.array_equal(logits2.cpu().numpy().view(np.uint32), lg.view(np.uint32))
+    assert np.array_equal(dec2.cpu().numpy(), dg)

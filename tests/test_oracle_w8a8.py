@@ -136,3 +136,19 @@ def test_w8a8_depth_golden_files_are_consistent():
     for frac, per_depth in sens["fractions"].items():
         v = [per_depth[str(d)] for d in sens["taps"]]
         assert all(x > 0 for x in v) and v == sorted(v), (frac, v)
+
+
+def test_w8a8_layer_sensitivity_file():
+    """The one-layer full-size W8A8 golden file holds the six sampled pairs the
+    GPU test checks, each with 8 finite logits, its decision consistent with
+    its own logits, and a positive planted-disagreement movement."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "w8a8_layer_sensitivity.json")
+    doc = json.load(open(path))
+    assert doc["fraction"] == 0.01 and len(doc["pairs"]) == 6
+    for p in doc["pairs"].values():
+        lg = np.array(p["logits"])
+        assert lg.shape == (8,) and np.isfinite(lg).all()
+        assert p["decision"] == (0x0F >> int(np.argmax(lg))) & 1
+        assert 0 < p["moved_rel"] < 0.5
