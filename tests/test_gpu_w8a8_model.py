@@ -252,3 +252,54 @@ def test_w8a8_full_size_layer_sampled(B):
     torch.cuda.synchronize()
     assert np.array_equal(logits2.cpu().numpy().view(np.uint32), lg.view(np.uint32))
     assert np.array_equal(dec2.cpu().numpy(), dg)
+
+
+def test_w8a8_shared_prefix_nodes_nested(B):
+    """fp8 activations through shared prefix nodes (quail_join_run_shared,
+    nested): under two anchors and among filter rows, suffixes share a prompt
+    and then, in families, a document. The node prefills quantise their rows
+    per token like any batch, so the logits match the oracle's W8A8 per-pair
+    forward; everything is evicted with no regret."""
+    import torch
+    from query_aware_prefill_amd.device import DeviceModel, to_device
+    shape = _tiny()
+    wts = W.model_weights(shape, 19)
+    r = np.random.default_rng(19)
+    a_len = [40, 90]
+    a_tok = r.integers(0, 512, sum(a_len)).astype(np.int32)
+    a_off = np.array([0, 40, 130], np.int32)
+    pairs, seqs = [], []
+    for a in (0, 1, -1):
+        prompt = r.integers(0, 512, 20).astype(np.int32)
+        for f in range(2):
+            doc = r.integers(0, 512, 12 + 4 * f).astype(np.int32)
+            for m in range(3):
+                seqs.append(np.concatenate([prompt, doc, r.integers(0, 512, 2 + m).astype(np.int32)]))
+                pairs.append(a)
+        seqs.append(np.concatenate([prompt, r.integers(0, 512, 6).astype(np.int32)]))
+        pairs.append(a)
+    n = len(seqs)
+    pa = np.array(pairs, np.int32)
+    s_off = np.zeros(n + 1, np.int32)
+    s_off[1:] = np.cumsum([len(x) for x in seqs])
+    s_tok = np.concatenate(seqs).astype(np.int32)
+    dm = DeviceModel(shape, wts, max_anchor_len=1024, max_suffix_len=256)
+    ctx = dm.context(16 << 20, 1024)
+    logits = torch.empty((n, 8), dtype=torch.float32, device="cuda")
+    dec = torch.empty(n, dtype=torch.uint8, device="cuda")
+    say("w8a8 join_run_shared nested", n, "pairs")
+    B.quail_join_run_shared(ctx, to_device(a_tok), a_off, pa, to_device(s_tok), s_off, s_tok, 8, 0x0F,
+                            logits, None, dec, nested=True)
+    torch.cuda.synchronize()
+    st = B.quail_pool_stats(ctx)
+    assert st["prefills"] == 2 + 3 * 3 and st["evictions"] == st["prefills"]
+    assert st["resident"] == 0 and st["regret_tokens"] == 0
+    ref = [OM.forward_pair(a_tok[a_off[a]:a_off[a + 1]] if a >= 0 else [], seqs[i], wts, shape)
+           for i, a in enumerate(pairs)]
+    ref_logits = np.array([x["logits"] for x in ref])
+    err = rel_inf(logits.cpu().numpy(), ref_logits)
+    say("  logits rel err", err)
+    assert err <= 2e-2
+    ok, _ = decisions_agree(dec.cpu().numpy(), [x["decision"] for x in ref], [x["margin"] for x in ref],
+                            2e-2 * np.max(np.abs(ref_logits)))
+    assert ok
