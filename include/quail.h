@@ -548,7 +548,9 @@ quail_status quail_gemm_w8a16(int32_t M, int32_t N, int32_t K, const uint16_t* x
  *                                                ties to the even code)
  *   scale[m]    = amax / 448
  * where 448 / amax, the product and amax / 448 are each one fp32 operation
- * rounded to nearest even. A row of zeros gets codes 0 and scale 0. x dev
+ * rounded to nearest even. A row of zeros gets codes 0 and scale 0. Every
+ * other row must have amax >= 2^-120 so that 448 / amax is finite in fp32
+ * (smaller rows give undefined codes). x dev
  * bf16 [M, K] (row stride K, finite values, 16-byte aligned); codes dev u8
  * [M, K]; scale dev f32 [M]. K a multiple of 8. Caller owns every buffer. */
 quail_status quail_act_quant_e4m3(int32_t M, int32_t K, const uint16_t* x, uint8_t* codes,

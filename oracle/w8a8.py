@@ -11,7 +11,8 @@ the product can run on the fp8 matrix cores.
 Readings where the pages are silent:
   * one scale per token (per row of the activation matrix): s = amax / 448,
     amax = the row's largest magnitude, so the largest element maps to the
-    largest E4M3 magnitude; a row of zeros has s = 0 and codes 0;
+    largest E4M3 magnitude; a row of zeros has s = 0 and codes 0; rows with
+    0 < amax < 2^-120 are outside the domain (448 / amax overflows float32);
   * the code of x is the E4M3 encoding (round to nearest, ties to even,
     saturating) of x * inv, where inv = 448 / amax and both the division and
     the product are single float32 operations (a quantised code is an integer
