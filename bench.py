@@ -66,7 +66,7 @@ Secondary measurements (not the headline line; each prints its own JSON):
                      Logical and computed tokens/min; the oracle leg runs the
                      per-pair definition on a few sampled pairs and compares
                      logits and decisions.
-                     --act-fp8 runs them with per-token E4M3 activations
+                     --act-fp8 runs them (and multijoin36full) with per-token E4M3 activations
                      (W8A8 projections on the fp8 MFMA) against the
                      oracle's W8A8 reading.
   --workload multiplan36
@@ -909,7 +909,7 @@ def bench_multijoin_full(args):
     from query_aware_prefill_amd import binding as B
     from query_aware_prefill_amd.device import DeviceModel, to_device
     B.load()
-    shape = W.ModelShape(**{**W.QWEN3_4B.__dict__, "kv_fp8": True})
+    shape = W.ModelShape(**{**W.QWEN3_4B.__dict__, "kv_fp8": True, "act_fp8": bool(args.act_fp8)})
     log("multijoin36 full: generating the workload")
     case = W.c4_case()
     a_len, a_off, a_tok = case["a_len"], case["a_off"], case["a_tok"]
@@ -958,7 +958,8 @@ def bench_multijoin_full(args):
     attn += 16384.0 * (L - 1) * float(np.sum(a_len.astype(np.float64) * (a_len + 1) / 2))
     res = {"metric": "end-to-end prefill tokens/min (36-layer stack)",
            "workload": "multi-join at full size: 1024 anchors x 768 tokens (E4M3 KV resident), 5,000 rows of "
-                       "U{48..256} tokens x 51 anchors each (255,000 pairs)",
+                       "U{48..256} tokens x 51 anchors each (255,000 pairs)"
+                       + ("; W8A8 (per-token E4M3 activations on the fp8 MFMA)" if args.act_fp8 else ""),
            "unit": "tokens/min", "ms": ms, "anchor_prefill_ms": t_pre * 1e3, "pairs": int(n),
            "logical_tokens": logical, "computed_tokens": suffix_tok + anchor_tok,
            "logical_tokens_per_min": logical / ms * 60e3,
@@ -1333,7 +1334,8 @@ def main():
     ap.add_argument("--no-w8a8", action="store_true",
                     help="headline: skip the W8A8 run of the same steps (a field of the line)")
     ap.add_argument("--act-fp8", action="store_true",
-                    help="join36 / filter36 / multijoin36: per-token E4M3 activations (W8A8 projections)")
+                    help="join36 / filter36 / multijoin36 / multijoin36full: per-token E4M3 activations "
+                         "(W8A8 projections)")
     ap.add_argument("--shared-only", action="store_true", help="shared36: run only the join with prefix nodes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
